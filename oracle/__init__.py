@@ -1,0 +1,34 @@
+"""CPU oracle for the speculative KV coder -- TEST INFRASTRUCTURE ONLY.
+
+This package is the plain, slow reference that the HIP library is checked
+against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` may import it; the product path (``entropy_coding_amd``)
+never imports, calls or links anything here, and the two share no code.
+
+Sources: the wiki page "Speculative KV Coding" (aisparkup.com) and the blog
+post "推测性KV编码：用预测模型实现缓存无损压缩4倍" (blog.hotdry.top).  The pages
+fix the model (a three-part mixture around a predictor mean) and the claim
+(lossless, size close to the model's cross-entropy); they do not fix the coder,
+so every integer detail below follows the written format KVC-1 whose readings
+are listed, with the passages they rest on, in the design notes.
+
+Parity status of each function (what pins it other than itself):
+  order_index / bits_of_order  -- brute force over every bit pattern, torch's
+                                  own bf16 / float8_e4m3fn decoders
+  boundary_positions           -- exact midpoint identity in float64
+  phi_table                    -- scipy.special.ndtr, symmetry, closed values
+  cdf                          -- invariants (C(0)=0, C(N)=M, f>=1) and the
+                                  continuous mixture within a derived bound
+  encode / decode              -- round trip, exact size band, unbounded
+                                  big-integer rANS
+  build_marginal               -- brute-force counting on tiny inputs
+  calibrate_sigma              -- float64 closed form, minimum of the
+                                  Gaussian cost
+  side_hash                    -- parity unpinned (an integrity checksum of
+                                  the side information; its value is a
+                                  convention of the format, not of the pages)
+  model_bits_float             -- closed form for a single Gaussian in a
+                                  constant-ulp region
+"""
+
+from .kvc_oracle import *  # noqa: F401,F403

@@ -1,0 +1,721 @@
+"""Plain CPU oracle of the KVC-1 lossless KV-cache coder (test infrastructure).
+
+Pages cited:
+  [wiki]  "Speculative KV Coding", aisparkup.com wiki
+  [blog]  "推测性KV编码：用预测模型实现缓存无损压缩4倍", blog.hotdry.top
+
+What the pages fix: each KV scalar is coded under a model q built from a
+predictor mean mu and a calibrated per-(kv, head, channel) sigma; q is the
+mixture 0.95 N(mu, sigma^2) + 0.03 N(mu, (3 sigma)^2) + 0.02 p_hat, where p_hat
+is the empirical marginal over the BF16 alphabet ([wiki] § mixture
+distribution; [blog] § engineering choice of predictor).  An arithmetic coder
+emits about -log2 q(KV) bits per scalar and the decoder, holding the same
+(mu, sigma), rebuilds KV exactly ([wiki] § pipeline; [blog] § information
+theory view).  The two sides must agree on the CDF bit for bit ([blog] §
+application scenarios and deployment parameters).
+
+What the pages leave open (coder type, precision, discretisation, stream
+layout) is fixed by the format KVC-1; the numbered steps S-0 .. S-10 below
+follow it in order.  Everything is written for clarity, not speed: NumPy
+vectorises over coder lanes, Python loops over token steps.  Floating point is
+used only where KVC-1 prescribes IEEE float32 steps (S-3); everything after is
+exact integer arithmetic.
+"""
+
+from __future__ import annotations
+
+import functools
+import struct
+
+import numpy as np
+
+__all__ = [
+    "BF16", "E4M3", "F32", "M", "L", "LANES", "HEADER_BYTES", "STATE_BYTES", "StreamError",
+    "alphabet_size", "budgets", "order_index", "bits_of_order", "symbol_value",
+    "boundary_positions", "phi_table", "phi_fx", "mu_to_f32", "cdf",
+    "cdf_table", "build_marginal", "calibrate_sigma", "side_hash", "encode",
+    "decode", "parse_header", "model_bits_int", "model_bits_float",
+    "chunk_layout",
+]
+
+# ---------------------------------------------------------------------------
+# S-0  constants
+# ---------------------------------------------------------------------------
+BF16, E4M3, F32 = 0, 1, 2          # dtype codes shared by the stream header
+LOG2_M = 31
+M = 1 << LOG2_M                    # total of every integer CDF
+LOG2_L = 47
+L = 1 << LOG2_L                    # lower end of the rANS state interval
+WORD_BITS = 16                     # rANS emits / reads 16-bit words
+LANES = 64                         # interleaved rANS lanes per chunk
+HEADER_BYTES = 128
+STATE_BYTES = 8 * LANES            # 64 final states, u64 each
+MAGIC = b"KVC1"
+VERSION = 1
+
+
+class StreamError(ValueError):
+    """Raised by the oracle decoder on a malformed or corrupt stream."""
+
+
+def alphabet_size(dtype: int) -> int:
+    """Number of symbols: every 16-bit BF16 pattern or every 8-bit e4m3fn
+    pattern ([wiki] § core idea: 16 bits per BF16 scalar; [blog] §
+    measured compression: FP8 e4m3 targets)."""
+    if dtype == BF16:
+        return 1 << 16
+    if dtype == E4M3:
+        return 1 << 8
+    raise ValueError(f"bad kv dtype {dtype}")
+
+
+def budgets(dtype: int, w_narrow_bp: int, w_wide_bp: int):
+    """Integer budgets of the three mixture parts.
+
+    The mixture weights are 0.95 / 0.03 / 0.02 ([wiki] § mixture
+    distribution); in basis points (9500, 300).  N units of the total M go to
+    the +1 floor that every symbol gets, the remaining T = M - N are split by
+    the weights with floors, and the escape part gets what is left.
+    """
+    if not (0 <= w_narrow_bp and 0 <= w_wide_bp and w_narrow_bp + w_wide_bp <= 10000):
+        raise ValueError("weights out of range")
+    n = alphabet_size(dtype)
+    t = M - n
+    t_n = t * w_narrow_bp // 10000
+    t_w = t * w_wide_bp // 10000
+    t_e = t - t_n - t_w
+    return t_n, t_w, t_e
+
+
+# ---------------------------------------------------------------------------
+# S-1  ordered alphabet
+# ---------------------------------------------------------------------------
+def order_index(bits, dtype: int) -> np.ndarray:
+    """Map raw bit patterns to the value-ordered symbol index.
+
+    Positive patterns (sign 0) keep their order above the midpoint; negative
+    patterns are reversed below it.  So -NaN < -Inf < ... < -0 < +0 < ... <
+    +Inf < +NaN in index order.
+    """
+    k = 16 if dtype == BF16 else 8
+    u = np.asarray(bits).astype(np.int64) & ((1 << k) - 1)
+    sign = (u >> (k - 1)) & 1
+    return np.where(sign == 0, u ^ (1 << (k - 1)), (~u) & ((1 << k) - 1))
+
+
+def bits_of_order(b, dtype: int) -> np.ndarray:
+    """Inverse of :func:`order_index`."""
+    k = 16 if dtype == BF16 else 8
+    b = np.asarray(b).astype(np.int64)
+    half = 1 << (k - 1)
+    return np.where(b >= half, b ^ half, (~b) & ((1 << k) - 1))
+
+
+def _bf16_bits_to_f64(bits) -> np.ndarray:
+    u = (np.asarray(bits).astype(np.uint32) & 0xFFFF) << 16
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
+
+
+def _e4m3_bits_to_f64(bits) -> np.ndarray:
+    """OCP float8 e4m3fn: 1 sign, 4 exponent (bias 7), 3 mantissa bits;
+    S.1111.111 is NaN and there is no infinity; the largest value is 448."""
+    u = np.asarray(bits).astype(np.int64) & 0xFF
+    sign = np.where(u & 0x80, -1.0, 1.0)
+    e = (u >> 3) & 0xF
+    man = (u & 7).astype(np.float64)
+    normal = (1.0 + man / 8.0) * np.power(2.0, (e - 7).astype(np.float64))
+    sub = man / 8.0 * 2.0 ** -6
+    mag = np.where(e == 0, sub, normal)
+    mag = np.where((u & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+def symbol_value(b, dtype: int) -> np.ndarray:
+    """Real value (float64) of ordered symbol b."""
+    bits = bits_of_order(b, dtype)
+    if dtype == BF16:
+        return _bf16_bits_to_f64(bits)
+    return _e4m3_bits_to_f64(bits)
+
+
+# ---------------------------------------------------------------------------
+# S-2  boundary positions
+# ---------------------------------------------------------------------------
+@functools.lru_cache(maxsize=None)
+def boundary_positions(dtype: int) -> np.ndarray:
+    """pos[b] for b = 0..N: the edge between symbols b-1 and b (float32).
+
+    Reading (the pages write densities, not a discretisation): each finite
+    value owns the round-to-nearest cell around it; the cells of -max and +max
+    extend to -inf / +inf; the edge between -0 and +0 is 0; non-finite symbols
+    get no Gaussian mass, so every edge at or below the lower edge of -max is
+    -inf and every edge at or above the upper edge of +max is +inf.
+    """
+    n = alphabet_size(dtype)
+    b = np.arange(n + 1, dtype=np.int64)
+    vals = symbol_value(np.arange(n), dtype)
+    finite = np.isfinite(vals)
+    lo_sym = int(np.argmax(finite))                 # index of -max
+    hi_sym = int(n - 1 - np.argmax(finite[::-1]))   # index of +max
+    zero_split = int(order_index(0, dtype))         # index of +0
+    pos = np.empty(n + 1, dtype=np.float64)
+    inner = (b > lo_sym) & (b <= hi_sym)
+    bi = b[inner]
+    pos[inner] = (vals[bi - 1] + vals[bi]) / 2.0
+    pos[b <= lo_sym] = -np.inf
+    pos[b > hi_sym] = np.inf
+    pos[zero_split] = 0.0
+    out = pos.astype(np.float32)
+    assert np.array_equal(out.astype(np.float64), pos), "edge not exact in float32"
+    return out
+
+
+# ---------------------------------------------------------------------------
+# S-4  integer standard-normal CDF
+# ---------------------------------------------------------------------------
+PHI_STEPS_PER_UNIT = 256
+PHI_Z_MIN = -8
+
+
+@functools.lru_cache(maxsize=None)
+def phi_table() -> np.ndarray:
+    """T[k] = round(2^31 * Phi(-8 + k/256)) for k = 0..4096, T[4097] = T[4096].
+
+    Phi is the standard normal CDF, written as 1/2 erfc(-x / sqrt 2) and
+    evaluated with mpmath at 50 significant digits.  No entry is a tie: the
+    fractional parts stay well clear of 1/2 (a test checks the margin).
+    """
+    import mpmath
+
+    out = []
+    with mpmath.workdps(50):
+        two31 = mpmath.mpf(2) ** 31
+        half = mpmath.mpf(1) / 2
+        for k in range(4097):
+            x = mpmath.mpf(PHI_Z_MIN) + mpmath.mpf(k) / PHI_STEPS_PER_UNIT
+            phi = mpmath.erfc(-x / mpmath.sqrt(2)) / 2
+            out.append(int(mpmath.floor(two31 * phi + half)))
+    out.append(out[-1])
+    return np.array(out, dtype=np.int64)
+
+
+def phi_fx(q) -> np.ndarray:
+    """Integer Phi of z = q / 2^24 for q in [-2^27, 2^27] (z in [-8, 8]):
+    table lookup at step 1/256 plus integer linear interpolation."""
+    q = np.asarray(q).astype(np.int64)
+    if np.any(np.abs(q) > (1 << 27)):
+        raise ValueError("phi_fx argument out of range")
+    tab = phi_table()
+    u = q + (1 << 27)
+    i = u >> 16
+    r = u & 0xFFFF
+    lo = tab[i]
+    hi = tab[i + 1]
+    return lo + (((hi - lo) * r) >> 16)
+
+
+# ---------------------------------------------------------------------------
+# S-3 / S-5  the mixture CDF
+# ---------------------------------------------------------------------------
+def mu_to_f32(mu, mu_dtype: int) -> np.ndarray:
+    """Predictor mean as float32.  BF16 mu arrives as 16-bit patterns; F32 as
+    float32.  Reading: a non-finite mu carries no location information and is
+    replaced by 0 (both sides do the same, so the code stays lossless)."""
+    if mu_dtype == BF16:
+        m = ((np.asarray(mu).astype(np.uint32) & 0xFFFF) << 16).view(np.float32)
+    elif mu_dtype == F32:
+        m = np.asarray(mu, dtype=np.float32)
+    else:
+        raise ValueError(f"bad mu dtype {mu_dtype}")
+    return np.where(np.isfinite(m), m, np.float32(0.0)).astype(np.float32)
+
+
+def cdf(b, mu32, inv32, dtype: int, t_n: int, t_w: int, prefix=None) -> np.ndarray:
+    """C(b): cumulative frequency below symbol b under the mixture.
+
+    S-3  d = pos(b) - mu and z = d * (1/sigma), each one IEEE float32 operation;
+         z clamped to [-24, 24]; q = round-half-even(z * 2^24).
+    S-5  narrow part uses q clamped to [-2^27, 2^27] (z in [-8, 8]); the wide
+         part (standard deviation 3 sigma) uses floor(q / 3); the escape part
+         is the integer prefix of the marginal, prefix[b].
+         C(b) = b + floor(T_n Phi(q1) / 2^31) + floor(T_w Phi(q3) / 2^31) + prefix[b].
+    """
+    b = np.asarray(b).astype(np.int64)
+    pos = boundary_positions(dtype)[b]
+    mu32 = np.asarray(mu32, dtype=np.float32)
+    inv32 = np.asarray(inv32, dtype=np.float32)
+    with np.errstate(over="ignore", invalid="raise"):
+        d = (pos - mu32).astype(np.float32)
+        z = (d * inv32).astype(np.float32)
+    z = np.clip(z, np.float32(-24.0), np.float32(24.0)).astype(np.float32)
+    q = np.rint(z * np.float32(1 << 24)).astype(np.int64)
+    q1 = np.clip(q, -(1 << 27), 1 << 27)
+    q3 = q // 3                                   # floor division
+    g = ((t_n * phi_fx(q1)) >> 31) + ((t_w * phi_fx(q3)) >> 31)
+    if prefix is not None:
+        g = g + np.asarray(prefix, dtype=np.int64)[b]
+    return b + g
+
+
+def _inv_sigma(sigma) -> np.ndarray:
+    s = np.asarray(sigma, dtype=np.float32)
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        inv = (np.float32(1.0) / s).astype(np.float32)
+    ok = np.isfinite(s) & (s > 0) & np.isfinite(inv)
+    if not np.all(ok):
+        raise ValueError("sigma must be finite, positive, with a finite reciprocal")
+    return inv
+
+
+def cdf_table(mu, sigma, dtype: int, mu_dtype: int, w_narrow_bp: int,
+              w_wide_bp: int, prefix=None) -> np.ndarray:
+    """C(b) for every b = 0..N, for each (mu, sigma) pair: shape [P, N+1]."""
+    t_n, t_w, t_e = budgets(dtype, w_narrow_bp, w_wide_bp)
+    if t_e and prefix is None:
+        raise ValueError("mixture with an escape part needs the marginal prefix")
+    mu32 = mu_to_f32(np.atleast_1d(mu), mu_dtype)
+    inv = _inv_sigma(np.atleast_1d(sigma))
+    n = alphabet_size(dtype)
+    b = np.arange(n + 1, dtype=np.int64)
+    out = np.empty((mu32.size, n + 1), dtype=np.int64)
+    for i in range(mu32.size):
+        out[i] = cdf(b, mu32[i], inv[i], dtype, t_n, t_w, prefix if t_e else None)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# S-6  empirical marginal (the p_hat part)
+# ---------------------------------------------------------------------------
+def build_marginal(samples, dtype: int, w_narrow_bp: int, w_wide_bp: int) -> np.ndarray:
+    """Integer prefix table of the +1-smoothed empirical marginal.
+
+    c[j] = 1 + number of samples whose ordered index is j; cum is its
+    exclusive prefix in index order; prefix[b] = floor(T_e cum[b] / cum[N]).
+    p_hat is the empirical BF16 distribution that catches extreme outliers
+    ([wiki] § mixture distribution; [blog] § engineering choice of predictor).
+    """
+    n = alphabet_size(dtype)
+    _, _, t_e = budgets(dtype, w_narrow_bp, w_wide_bp)
+    idx = order_index(np.asarray(samples).ravel(), dtype)
+    counts = np.bincount(idx, minlength=n).astype(object) + 1
+    cum = [0]
+    for c in counts:
+        cum.append(cum[-1] + int(c))
+    total = cum[-1]
+    return np.array([t_e * c // total for c in cum], dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# S-7  sigma calibration
+# ---------------------------------------------------------------------------
+def _values_f64(x, dtype: int) -> np.ndarray:
+    if dtype == BF16:
+        return _bf16_bits_to_f64(x)
+    if dtype == E4M3:
+        return _e4m3_bits_to_f64(x)
+    if dtype == F32:
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def calibrate_sigma(kv, mu, kv_dtype: int, mu_dtype: int, sigma_floor: float) -> np.ndarray:
+    """sigma[p, d] = max(floor, sqrt(mean over reps and tokens of (kv - mu)^2)).
+
+    Inputs are [reps, planes, tokens, channels].  sigma^2 is the mean squared
+    residual about mu: it minimises the expected Gaussian cost, spread plus
+    miss, of [blog] § information theory view, and the pages calibrate it per
+    (kv, head, channel) on held-out data, then freeze it ([wiki] § predictor
+    choice; [blog] § engineering choice of predictor).  Accumulated in float64,
+    rounded once to float32.
+    """
+    k = _values_f64(kv, kv_dtype)
+    m = _values_f64(mu, mu_dtype)
+    m = np.where(np.isfinite(m), m, 0.0)
+    r = k - m
+    ms = np.mean(r * r, axis=(0, 2))
+    s = np.sqrt(ms).astype(np.float32)
+    return np.maximum(s, np.float32(sigma_floor)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# S-10  side-information checksum
+# ---------------------------------------------------------------------------
+_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+
+
+def _mix64(z: np.ndarray) -> np.ndarray:
+    """splitmix64 output function (Vigna's published constants)."""
+    z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+    z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def _words_hash(words: np.ndarray, tag: int) -> int:
+    w = np.ascontiguousarray(words).view(np.uint32).astype(np.uint64).ravel()
+    i = np.arange(w.size, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = ((i << np.uint64(32)) | w) + np.uint64(tag) * _GOLDEN
+        return int(np.sum(_mix64(z), dtype=np.uint64))
+
+
+def side_hash(sigma, prefix=None) -> int:
+    """64-bit checksum of the side information both ends must share
+    (sum mod 2^64 of mixed (index, word) pairs; sigma words tag 1, prefix
+    words tag 2).  Detects a decoder fed different sigma or p_hat."""
+    h = _words_hash(np.asarray(sigma, dtype=np.float32), 1)
+    if prefix is not None:
+        h += _words_hash(np.asarray(prefix, dtype=np.int64).astype(np.uint32), 2)
+    return h & ((1 << 64) - 1)
+
+
+# ---------------------------------------------------------------------------
+# S-8 .. S-10  rANS coder, interleaving and stream
+# ---------------------------------------------------------------------------
+def chunk_layout(planes: int, tokens: int, channels: int, chunk_tokens: int):
+    """Chunk c = ((g * n_tok_chunks + tc) * (channels / 64) + k) codes tokens
+    [tc*Tc, min((tc+1)*Tc, T)) of channels [64k, 64k+64) of plane g; lane l
+    of the chunk is channel 64k + l."""
+    n_tc = -(-tokens // chunk_tokens)
+    n_k = channels // LANES
+    cid = np.arange(planes * n_tc * n_k, dtype=np.int64)
+    k = cid % n_k
+    tc = (cid // n_k) % n_tc
+    g = cid // (n_k * n_tc)
+    length = np.minimum(chunk_tokens, tokens - tc * chunk_tokens)
+    return g, tc, k, length
+
+
+def _header(kv_dtype, mu_dtype, w_n, w_w, chunk_tokens, planes, tokens, channels,
+            n_chunks, payload_bytes, shash) -> bytes:
+    t_n, t_w, t_e = budgets(kv_dtype, w_n, w_w)
+    h = struct.pack(
+        "<4sHHBBBBBBHIIIIIIQQQQQQ",
+        MAGIC, VERSION, HEADER_BYTES, kv_dtype, mu_dtype, LOG2_M, LOG2_L,
+        WORD_BITS, LANES, 0, w_n, w_w, t_n, t_w, t_e, chunk_tokens,
+        planes, tokens, channels, n_chunks, payload_bytes, shash)
+    return h + bytes(HEADER_BYTES - len(h))
+
+
+def parse_header(stream: bytes) -> dict:
+    if len(stream) < HEADER_BYTES:
+        raise StreamError("stream shorter than its header")
+    f = struct.unpack_from("<4sHHBBBBBBHIIIIIIQQQQQQ", stream, 0)
+    keys = ["magic", "version", "header_bytes", "kv_dtype", "mu_dtype", "log2_m",
+            "log2_l", "word_bits", "lanes", "reserved", "w_narrow_bp", "w_wide_bp",
+            "t_n", "t_w", "t_e", "chunk_tokens", "planes", "tokens", "channels",
+            "n_chunks", "payload_bytes", "side_hash"]
+    h = dict(zip(keys, f))
+    if h["magic"] != MAGIC or h["version"] != VERSION or h["header_bytes"] != HEADER_BYTES:
+        raise StreamError("bad magic/version")
+    if (h["log2_m"], h["log2_l"], h["word_bits"], h["lanes"]) != (LOG2_M, LOG2_L, WORD_BITS, LANES):
+        raise StreamError("unsupported coder parameters")
+    if h["kv_dtype"] not in (BF16, E4M3) or h["mu_dtype"] not in (BF16, F32):
+        raise StreamError("bad dtype")
+    try:
+        bud = budgets(h["kv_dtype"], h["w_narrow_bp"], h["w_wide_bp"])
+    except ValueError as e:
+        raise StreamError(str(e)) from None
+    if bud != (h["t_n"], h["t_w"], h["t_e"]):
+        raise StreamError("budgets do not match weights")
+    if h["chunk_tokens"] < 1 or h["channels"] % LANES or h["channels"] == 0 \
+            or h["planes"] == 0 or h["tokens"] == 0:
+        raise StreamError("bad shape")
+    n_tc = -(-h["tokens"] // h["chunk_tokens"])
+    if h["n_chunks"] != h["planes"] * n_tc * (h["channels"] // LANES):
+        raise StreamError("chunk count does not match shape")
+    return h
+
+
+def _roundup8(x):
+    return (x + 7) // 8 * 8
+
+
+def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int,
+           w_wide_bp: int, chunk_tokens: int, batch_chunks: int = 2048) -> bytes:
+    """Code kv [G, T, D] (raw bit patterns) under the mixture around mu [G, T, D]
+    with sigma [G, D]; return the KVC-1 byte stream.
+
+    Per chunk and lane, tokens are coded last to first so that the decoder
+    runs first to last (rANS is last-in first-out).  Before a symbol with
+    frequency f is pushed, the state x is renormalised down so that
+    x < 2^32 f by emitting its low 16-bit word (count = [x/2^32 >= f] +
+    [x/2^48 >= f] words); then x <- floor(x/f) * M + (x mod f) + start.
+    The words of one token step are laid out in the order the decoder reads
+    them: first, for every lane that emitted at least one word (ascending
+    lane), its last-emitted word; then, for every lane that emitted two,
+    its first-emitted word.
+    """
+    kv = np.asarray(kv)
+    g_n, t_len, d_n = kv.shape
+    if d_n % LANES or d_n == 0 or g_n == 0 or t_len == 0:
+        raise ValueError("channels must be a positive multiple of 64")
+    if chunk_tokens < 1:
+        raise ValueError("chunk_tokens must be >= 1")
+    t_n, t_w, t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)
+    if t_e and prefix is None:
+        raise ValueError("mixture with an escape part needs the marginal prefix")
+    pref = prefix if t_e else None
+    mu32_all = mu_to_f32(mu, mu_dtype)
+    inv_all = _inv_sigma(sigma)
+    sym_all = order_index(kv, kv_dtype)
+
+    g_of, tc_of, k_of, len_of = chunk_layout(g_n, t_len, d_n, chunk_tokens)
+    n_chunks = g_of.size
+    lane = np.arange(LANES, dtype=np.int64)
+    payloads = []
+    for b0 in range(0, n_chunks, batch_chunks):
+        sl = slice(b0, min(n_chunks, b0 + batch_chunks))
+        g, tcid, k, ln = g_of[sl], tc_of[sl], k_of[sl], len_of[sl]
+        nb = g.size
+        d = 64 * k[:, None] + lane[None, :]
+        inv = inv_all[g[:, None], d]
+        x = np.full((nb, LANES), L, dtype=np.uint64)
+        words = np.zeros((nb, chunk_tokens, 2, LANES), dtype=np.uint16)
+        emit = np.zeros((nb, chunk_tokens, 2, LANES), dtype=bool)
+        for t in range(chunk_tokens - 1, -1, -1):
+            active = (t < ln)[:, None]
+            tok = np.minimum(tcid * chunk_tokens + t, t_len - 1)[:, None]
+            s = sym_all[g[:, None], tok, d]
+            mu32 = mu32_all[g[:, None], tok, d]
+            start = cdf(s, mu32, inv, kv_dtype, t_n, t_w, pref)
+            f = cdf(s + 1, mu32, inv, kv_dtype, t_n, t_w, pref) - start
+            fu = f.astype(np.uint64)
+            count = ((x >> np.uint64(32)) >= fu).astype(np.int64) + \
+                    ((x >> np.uint64(48)) >= fu).astype(np.int64)
+            count = np.where(active, count, 0)
+            first = (x & np.uint64(0xFFFF)).astype(np.uint16)
+            second = ((x >> np.uint64(16)) & np.uint64(0xFFFF)).astype(np.uint16)
+            words[:, t, 0, :] = np.where(count == 2, second, first)
+            words[:, t, 1, :] = first
+            emit[:, t, 0, :] = count >= 1
+            emit[:, t, 1, :] = count == 2
+            xs = x >> (np.uint64(16) * count.astype(np.uint64))
+            xn = ((xs // fu) << np.uint64(LOG2_M)) + (xs % fu) + start.astype(np.uint64)
+            x = np.where(active, xn, x)
+        for i in range(nb):
+            body = x[i].astype("<u8").tobytes() + words[i][emit[i]].astype("<u2").tobytes()
+            payloads.append(body + bytes(_roundup8(len(body)) - len(body)))
+
+    sizes = np.array([len(p) for p in payloads], dtype=np.int64)
+    directory = np.concatenate([[0], np.cumsum(sizes)]).astype("<u8")
+    shash = side_hash(sigma, prefix if t_e else None)
+    head = _header(kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp, chunk_tokens,
+                   g_n, t_len, d_n, n_chunks, int(directory[-1]), shash)
+    return head + directory.tobytes() + b"".join(payloads)
+
+
+def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
+           chunk_ids=None):
+    """Rebuild the raw KV bit patterns [G, T, D] from a KVC-1 stream.
+
+    Per token step and lane: target = x mod M; the symbol is the unique s
+    with C(s) <= target < C(s+1) (found here by plain bisection over the
+    alphabet); x <- f * floor(x / M) + target - C(s); then, while x < L, a
+    16-bit word is shifted in (round 1 for every lane that needs one, in lane
+    order, then round 2).  Every lane must end in state L and every chunk
+    must consume exactly its payload, else the stream is corrupt.
+
+    With ``chunk_ids`` only those chunks are decoded; the result is then a
+    dict {chunk id: [length, 64] bit patterns}.
+    """
+    h = parse_header(stream)
+    kv_dtype, mu_dtype = h["kv_dtype"], h["mu_dtype"]
+    g_n, t_len, d_n, tcn = h["planes"], h["tokens"], h["channels"], h["chunk_tokens"]
+    n_chunks = h["n_chunks"]
+    t_n, t_w, t_e = h["t_n"], h["t_w"], h["t_e"]
+    pref = prefix if t_e else None
+    if t_e and prefix is None:
+        raise ValueError("stream uses an escape part; the marginal prefix is needed")
+    if side_hash(sigma, pref) != h["side_hash"]:
+        raise StreamError("side information does not match the stream")
+    dir_off = HEADER_BYTES
+    pay_off = dir_off + 8 * (n_chunks + 1)
+    if len(stream) < pay_off:
+        raise StreamError("stream shorter than its directory")
+    directory = np.frombuffer(stream, dtype="<u8", count=n_chunks + 1, offset=dir_off).astype(np.int64)
+    if directory[0] != 0 or np.any(np.diff(directory) < STATE_BYTES) \
+            or directory[-1] != h["payload_bytes"] or pay_off + directory[-1] != len(stream):
+        raise StreamError("bad chunk directory")
+    if np.any(directory % 8):
+        raise StreamError("misaligned chunk")
+
+    mu32_all = mu_to_f32(mu, mu_dtype)
+    inv_all = _inv_sigma(sigma)
+    g_of, tc_of, k_of, len_of = chunk_layout(g_n, t_len, d_n, tcn)
+    n_sym = alphabet_size(kv_dtype)
+    steps = n_sym.bit_length() - 1
+    lane = np.arange(LANES, dtype=np.int64)
+    ids = np.arange(n_chunks) if chunk_ids is None else np.asarray(chunk_ids, dtype=np.int64)
+    out_full = None
+    out_dict = {}
+    if chunk_ids is None:
+        out_full = np.zeros((g_n, t_len, d_n), dtype=np.uint16 if kv_dtype == BF16 else np.uint8)
+
+    for b0 in range(0, ids.size, batch_chunks):
+        cid = ids[b0:b0 + batch_chunks]
+        g, tcid, k, ln = g_of[cid], tc_of[cid], k_of[cid], len_of[cid]
+        nb = cid.size
+        d = 64 * k[:, None] + lane[None, :]
+        inv = inv_all[g[:, None], d]
+        start_b = pay_off + directory[cid]
+        size_b = directory[cid + 1] - directory[cid]
+        x = np.stack([np.frombuffer(stream, dtype="<u8", count=LANES, offset=int(o)) for o in start_b]).astype(np.uint64)
+        nwords = (size_b - STATE_BYTES) // 2
+        wmax = int(nwords.max()) if nb else 0
+        words = np.zeros((nb, wmax + 1), dtype=np.uint64)
+        for i in range(nb):
+            w = np.frombuffer(stream, dtype="<u2", count=int(nwords[i]), offset=int(start_b[i] + STATE_BYTES))
+            words[i, :w.size] = w
+        ptr = np.zeros(nb, dtype=np.int64)
+        sym = np.zeros((nb, tcn, LANES), dtype=np.int64)
+        for t in range(tcn):
+            active = (t < ln)[:, None]
+            tok = np.minimum(tcid * tcn + t, t_len - 1)[:, None]
+            mu32 = mu32_all[g[:, None], tok, d]
+            target = (x & np.uint64(M - 1)).astype(np.int64)
+            lo = np.zeros((nb, LANES), dtype=np.int64)
+            hi = np.full((nb, LANES), n_sym, dtype=np.int64)
+            c_lo = np.zeros((nb, LANES), dtype=np.int64)
+            c_hi = np.full((nb, LANES), M, dtype=np.int64)
+            for _ in range(steps):
+                mid = (lo + hi) >> 1
+                c_mid = cdf(mid, mu32, inv, kv_dtype, t_n, t_w, pref)
+                go = c_mid <= target
+                lo = np.where(go, mid, lo)
+                c_lo = np.where(go, c_mid, c_lo)
+                hi = np.where(go, hi, mid)
+                c_hi = np.where(go, c_hi, c_mid)
+            f = (c_hi - c_lo).astype(np.uint64)
+            xn = f * (x >> np.uint64(LOG2_M)) + (target - c_lo).astype(np.uint64)
+            x = np.where(active, xn, x)
+            for _round in range(2):
+                need = active & (x < np.uint64(L))
+                rank = np.cumsum(need, axis=1) - need
+                idx = ptr[:, None] + rank
+                if np.any(need & (idx >= nwords[:, None])):
+                    raise StreamError("chunk payload exhausted")
+                w = np.take_along_axis(words, np.minimum(idx, wmax), axis=1)
+                x = np.where(need, (x << np.uint64(16)) | w, x)
+                ptr = ptr + need.sum(axis=1)
+            sym[:, t, :] = lo
+        if np.any(x != np.uint64(L)):
+            raise StreamError("final rANS state is not the initial state")
+        if np.any(_roundup8(STATE_BYTES + 2 * ptr) != size_b):
+            raise StreamError("chunk payload not consumed exactly")
+        for i in range(nb):
+            pad_lo = int(start_b[i] + STATE_BYTES + 2 * ptr[i])
+            if any(stream[pad_lo:int(start_b[i] + size_b[i])]):
+                raise StreamError("nonzero padding")
+        bits = bits_of_order(sym, kv_dtype)
+        for i in range(nb):
+            n_t = int(ln[i])
+            blk = bits[i, :n_t, :]
+            if out_full is not None:
+                t0 = int(tcid[i]) * tcn
+                out_full[g[i], t0:t0 + n_t, 64 * k[i]:64 * k[i] + 64] = blk
+            else:
+                out_dict[int(cid[i])] = blk.astype(out_dict_dtype(kv_dtype))
+    return out_full if out_full is not None else out_dict
+
+
+def out_dict_dtype(kv_dtype):
+    return np.uint16 if kv_dtype == BF16 else np.uint8
+
+
+def chunk_payload(stream: bytes, chunk_id: int) -> bytes:
+    """Bytes of one chunk's payload (states, words, padding)."""
+    h = parse_header(stream)
+    pay_off = HEADER_BYTES + 8 * (h["n_chunks"] + 1)
+    a, b = np.frombuffer(stream, dtype="<u8", count=2, offset=HEADER_BYTES + 8 * chunk_id)
+    return stream[pay_off + int(a):pay_off + int(b)]
+
+
+def encode_chunks(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
+                  chunk_tokens, chunk_ids):
+    """Payloads of selected chunks only (for sampled parity at full size).
+
+    Each chunk depends only on its own slice of kv and mu and on its plane's
+    sigma, so it is coded by running :func:`encode` on a one-plane view."""
+    kv = np.asarray(kv)
+    g_n, t_len, d_n = kv.shape
+    g_of, tc_of, k_of, len_of = chunk_layout(g_n, t_len, d_n, chunk_tokens)
+    out = {}
+    for cid in chunk_ids:
+        g, tc, k, ln = int(g_of[cid]), int(tc_of[cid]), int(k_of[cid]), int(len_of[cid])
+        t0 = tc * chunk_tokens
+        sub_kv = kv[g:g + 1, t0:t0 + ln, 64 * k:64 * k + 64]
+        sub_mu = np.asarray(mu)[g:g + 1, t0:t0 + ln, 64 * k:64 * k + 64]
+        sub_sig = np.asarray(sigma, dtype=np.float32)[g:g + 1, 64 * k:64 * k + 64]
+        s = encode(sub_kv, sub_mu, sub_sig, prefix, kv_dtype, mu_dtype, w_narrow_bp,
+                   w_wide_bp, chunk_tokens)
+        out[int(cid)] = chunk_payload(s, 0)
+    return out
+
+
+__all__ += ["chunk_payload", "encode_chunks"]
+
+
+# ---------------------------------------------------------------------------
+# bits per scalar: the integer model and the continuous mixture
+# ---------------------------------------------------------------------------
+def model_bits_int(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp) -> float:
+    """Mean of -log2(f(s) / M) over all scalars: the ideal code length of the
+    integer model ([wiki] § core idea: bits = cross-entropy of q)."""
+    kv = np.asarray(kv)
+    g_n, t_len, d_n = kv.shape
+    t_n, t_w, t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)
+    pref = prefix if t_e else None
+    inv = np.broadcast_to(_inv_sigma(sigma)[:, None, :], kv.shape)
+    mu32 = mu_to_f32(mu, mu_dtype)
+    s = order_index(kv, kv_dtype)
+    total = 0.0
+    for g in range(g_n):
+        c0 = cdf(s[g], mu32[g], inv[g], kv_dtype, t_n, t_w, pref)
+        c1 = cdf(s[g] + 1, mu32[g], inv[g], kv_dtype, t_n, t_w, pref)
+        total += float(np.sum(LOG2_M - np.log2((c1 - c0).astype(np.float64))))
+    return total / kv.size
+
+
+def _ndtr_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Phi(b) - Phi(a) for a <= b, using the upper-tail form when both are
+    positive so that the difference does not cancel."""
+    from scipy.special import ndtr
+    upper = a > 0
+    return np.where(upper, ndtr(-a) - ndtr(-b), ndtr(b) - ndtr(a))
+
+
+def model_bits_float(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
+                     cap_bits: float = 64.0) -> float:
+    """Mean -log2 q(x) of the continuous mixture over the same cells, float64.
+
+    q(x) = w_n [Phi((hi-mu)/sigma) - Phi((lo-mu)/sigma)]
+         + w_w [same with 3 sigma] + w_e p_hat(x),
+    with p_hat(x) = (prefix[x+1] - prefix[x]) / T_e and the weights in basis
+    points ([wiki] § mixture distribution).  A per-scalar cost is capped at
+    ``cap_bits`` (only reachable without an escape part)."""
+    kv = np.asarray(kv)
+    t_n, t_w, t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)
+    wn, ww = w_narrow_bp / 1e4, w_wide_bp / 1e4
+    we = 1.0 - wn - ww
+    pos = boundary_positions(kv_dtype).astype(np.float64)
+    sig = np.asarray(sigma, dtype=np.float32).astype(np.float64)
+    mu_all = mu_to_f32(mu, mu_dtype).astype(np.float64)
+    s = order_index(kv, kv_dtype)
+    total = 0.0
+    for g in range(kv.shape[0]):
+        lo = pos[s[g]]
+        hi = pos[s[g] + 1]
+        m = mu_all[g]
+        sg = sig[g][None, :]
+        with np.errstate(invalid="ignore"):
+            a1, b1 = (lo - m) / sg, (hi - m) / sg
+            a3, b3 = (lo - m) / (3 * sg), (hi - m) / (3 * sg)
+        q = wn * _ndtr_diff(a1, b1) + ww * _ndtr_diff(a3, b3)
+        if t_e:
+            p = np.asarray(prefix, dtype=np.float64)
+            q = q + we * (p[s[g] + 1] - p[s[g]]) / t_e
+        with np.errstate(divide="ignore"):
+            bits = np.minimum(-np.log2(q), cap_bits)
+        total += float(np.sum(bits))
+    return total / kv.size
