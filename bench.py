@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV coder hot path on one MI355X.
+
+One step = kvc_encode then kvc_decode of the whole Qwen3-8B-shaped bf16 KV
+cache (36 layers x {K,V} x batch 4 x 8 KV heads x 4096 tokens x 128
+channels = 1.21G scalars, 2.42 GB) under the pages' three-part mixture, with
+sigma calibrated per (layer, kv, head, channel) from 128 x 1024 held-out
+tokens and p_hat from 2^20 samples.  Inputs are resident in HBM when timing
+starts; generation, calibration and the marginal are not timed.
+
+Prints one JSON line.  value = raw-KV GB/s of the round trip
+(2 bytes x scalars / (encode + decode time)); encode and decode GB/s,
+bits/scalar three ways, the dominant kernel's HBM roofline fraction and the
+CPU oracle's rate on a bounded sample are reported beside it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (runs before the GPU is touched; plain fork pool)
+# ---------------------------------------------------------------------------
+def _oracle_worker(args):
+    import numpy as np
+    import oracle as O
+    kv, mu, sig, pref, tc, w = args
+    t0 = time.perf_counter()
+    st = O.encode(kv, mu, sig, pref, O.BF16, O.BF16, w[0], w[1], tc)
+    t1 = time.perf_counter()
+    out = O.decode(st, mu, sig, pref)
+    t2 = time.perf_counter()
+    assert np.array_equal(out, kv)
+    return t1 - t0, t2 - t1, len(st)
+
+
+def cpu_baseline(workload, planes_per_worker: int, tokens: int):
+    """The oracle on a bounded sample of the same workload: layer-0 planes
+    drawn with the same recipe on the CPU, split over the host cores; each
+    worker codes and decodes its planes (token chunk of `tokens`)."""
+    import numpy as np
+    import torch
+    import oracle as O
+    from entropy_coding_amd import workloads as W
+
+    cores = len(os.sched_getaffinity(0))
+    kv, mu = W.layer_data(workload, 0, device="cpu", tokens=tokens)
+    sig = W.layer_sigma_true(workload, 0, device="cpu")
+    samples = W.marginal_samples(workload, device="cpu")
+    w = (workload.w_narrow_bp, workload.w_wide_bp)
+    pref = O.build_marginal(W.to_numpy_bits(samples), O.BF16, *w)
+    kvn, mun, sgn = W.to_numpy_bits(kv), W.to_numpy_bits(mu), sig.numpy()
+    g_avail = kvn.shape[0]
+    jobs = []
+    for i in range(cores):
+        sel = [(i * planes_per_worker + j) % g_avail for j in range(planes_per_worker)]
+        jobs.append((kvn[sel], mun[sel], sgn[sel], pref, tokens, w))
+    n = cores * planes_per_worker * tokens * workload.channels
+    torch.set_num_threads(1)
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        res = pool.map(_oracle_worker, jobs)
+    wall = time.perf_counter() - t0
+    enc = max(r[0] for r in res)
+    dec = max(r[1] for r in res)
+    raw = 2.0 * n
+    return {
+        "value": raw / wall / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": f"{n} scalars ({cores} workers x {planes_per_worker} planes x {tokens} tokens x "
+                  f"{workload.channels} channels of layer 0, same recipe drawn on the host); "
+                  f"encode+decode round trip, wall {wall:.2f} s",
+        "encode_gbps": raw / enc / 1e9, "decode_gbps": raw / dec / 1e9,
+    }
+
+
+# ---------------------------------------------------------------------------
+# GPU run
+# ---------------------------------------------------------------------------
+def prepare(workload, dev, calib_reps: int):
+    import torch
+    from entropy_coding_amd import kvc
+    from entropy_coding_amd import workloads as W
+
+    w = workload
+    G, T, D = w.planes, w.tokens, w.channels
+    kv = torch.empty((G, T, D), dtype=torch.bfloat16, device=dev)
+    mu = torch.empty((G, T, D), dtype=torch.bfloat16, device=dev)
+    sigma = torch.empty((G, D), dtype=torch.float32, device=dev)
+    ppl = w.planes_per_layer
+    t0 = time.perf_counter()
+    for l in range(w.layers):
+        k_l, m_l = W.layer_data(w, l, device=dev)
+        kv[l * ppl:(l + 1) * ppl] = k_l
+        mu[l * ppl:(l + 1) * ppl] = m_l
+        del k_l, m_l
+        ck, cm = W.layer_calibration(w, l, reps=calib_reps, device=dev)
+        s_kvh = kvc.kvc_calibrate_sigma(ck, cm)
+        sigma[l * ppl:(l + 1) * ppl] = W.expand_sigma(w, s_kvh)
+        del ck, cm
+    prefix = kvc.kvc_build_marginal(W.marginal_samples(w, device=dev), (w.w_narrow_bp, w.w_wide_bp))
+    torch.cuda.synchronize()
+    log(f"[bench] generated {w.name}: {w.n_scalars} scalars, sigma from {calib_reps}x{w.calib_tokens} "
+        f"tokens per layer, in {time.perf_counter() - t0:.1f} s")
+    return kv, mu, sigma, prefix
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, help="workload id (bench line: 2)")
+    ap.add_argument("--calib-reps", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-planes-per-worker", type=int, default=8)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from entropy_coding_amd import workloads as W
+    w = W.WORKLOADS[args.workload]
+    if w.kv_dtype != W.BF16:
+        raise SystemExit("the bench line is defined on a bf16 workload")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu_baseline: oracle on a host sample ...")
+        cpu = cpu_baseline(w, args.cpu_planes_per_worker, args.cpu_tokens)
+        log(f"[bench] cpu_baseline {cpu['value']:.4f} GB/s on {cpu['cores']} cores")
+
+    import torch
+    from entropy_coding_amd import kvc   # fails loudly if libkvc.so is missing
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    reps = args.calib_reps if args.calib_reps is not None else w.calib_reps
+    kv, mu, sigma, prefix = prepare(w, dev, reps)
+    n = w.n_scalars
+    weights = (w.w_narrow_bp, w.w_wide_bp)
+    p = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, w.planes, w.tokens, w.channels, weights, w.chunk_tokens)
+    enc = kvc.Encoder(p, dev)
+    kv_out = torch.empty((w.planes, w.tokens, w.channels), dtype=torch.int16, device=dev)
+    dws = torch.empty(kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    log(f"[bench] buffers: stream capacity {enc.capacity / 1e9:.2f} GB, workspace {enc.workspace.numel() / 1e9:.2f} GB")
+
+    def step(stats=None):
+        es, ds = [0.0] * kvc.ENCODE_STAGES, [0.0] * kvc.DECODE_STAGES
+        st = enc(kv, mu, sigma, prefix, stage_ms=es)
+        rc = kvc.kvc_decode_into(st, mu, sigma, prefix, kv_out, dws, stage_ms=ds)
+        if rc != kvc.KVC_OK:
+            raise kvc.KvcError(rc, "kvc_decode")
+        if stats is not None:
+            stats.append((es, ds))
+        return st
+
+    for i in range(args.warmup):
+        step()
+        log(f"[bench] warmup {i + 1}/{args.warmup}")
+    torch.cuda.synchronize()
+    stats = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st = step(stats)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"[bench] timed {args.steps} steps in {elapsed:.3f} s")
+    ok = torch.equal(kv_out, kv.view(torch.int16))
+    if not ok:
+        raise SystemExit("decoded KV differs from the input")
+    stream_bytes = st.numel()
+    bits_int, bits_float = kvc.kvc_estimate_bits(kv, mu, sigma, prefix, weights)
+
+    def mean(xs):
+        return sum(xs) / len(xs)
+
+    enc_kernel = mean([s[0][1] for s in stats])
+    enc_total = mean([sum(s[0]) for s in stats])
+    dec_kernel = mean([s[1][1] for s in stats])
+    dec_total = mean([sum(s[1]) for s in stats])
+    ms_per_step = elapsed / args.steps * 1e3
+    raw = 2.0 * n
+    # algorithmic bytes of the coding kernels: KV and mu in, words and states
+    # out (encode); words and states and mu in, KV out (decode)
+    alg = 4.0 * n + stream_bytes
+    dominant = "decode" if dec_kernel >= enc_kernel else "encode"
+    dom_ms = max(dec_kernel, enc_kernel)
+    achieved = alg / (dom_ms * 1e-3) / 1e9
+    res = {
+        "metric": "encode/decode GB/s of raw KV + bits/scalar, Qwen3-8B-shaped bf16 KV",
+        "value": raw / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "shape": [w.layers, 2, w.batch, w.heads, w.tokens, w.channels],
+            "scalars": n, "mixture_bp": list(weights), "chunk_tokens": w.chunk_tokens,
+            "sigma_calibration": f"{reps}x{w.calib_tokens} tokens per layer",
+        },
+        "encode_gbps": raw / (enc_total * 1e-3) / 1e9,
+        "decode_gbps": raw / (dec_total * 1e-3) / 1e9,
+        "encode_ms": enc_total, "decode_ms": dec_total,
+        "encode_stage_ms": {k: mean([s[0][i] for s in stats]) for i, k in
+                            enumerate(["side_hash", "encode_kernel", "scan", "compact"])},
+        "decode_stage_ms": {k: mean([s[1][i] for s in stats]) for i, k in enumerate(["side_hash", "decode_kernel"])},
+        "bits_per_scalar": {"coded": 8.0 * stream_bytes / n, "integer_model": bits_int, "float_model": bits_float},
+        "stream_bytes": stream_bytes,
+        "roundtrip_exact": ok,
+        "roofline": {
+            "bound": "hbm", "kernel": f"k_{dominant}", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+            "algorithmic_bytes": alg, "avg_ms": dom_ms,
+        },
+        "cpu_baseline": cpu,
+        "pages_context": {"bits_per_scalar_qwen3_0.6B_to_32B": [6.74, 5.92],
+                          "fp8_bits_per_element": [2.05, 2.59]},
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,485 @@
+// C ABI of libkvc (declared in include/kvc.h): argument validation, stream
+// header and directory bookkeeping, workspace layout, kernel launches and
+// the single status read-back per call.  Every step of the coder itself
+// runs in the kernels of kvc_kernels.hip.
+#include "kvc.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cfloat>
+#include <cstring>
+
+#include "kvc_internal.hpp"
+
+namespace {
+
+using kvc::ChunkGeom;
+using kvc::Control;
+
+constexpr uint32_t kLog2M = 31;
+constexpr uint32_t kLog2L = 47;
+constexpr uint32_t kWordBits = 16;
+constexpr uint32_t kLanes = 64;
+constexpr uint32_t kVersion = 1;
+constexpr uint32_t kMaxChunkTokens = 1u << 20;
+constexpr int64_t kMaxScalars = int64_t(1) << 40;
+
+uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+bool kv_dtype_ok(int32_t t) { return t == KVC_BF16 || t == KVC_E4M3; }
+bool mu_dtype_ok(int32_t t) { return t == KVC_BF16 || t == KVC_F32; }
+
+uint32_t alphabet(int32_t kv) { return kv == KVC_BF16 ? 65536u : 256u; }
+
+bool budgets(int32_t kv, uint32_t wn, uint32_t ww, uint32_t* tn, uint32_t* tw, uint32_t* te) {
+    if (!kv_dtype_ok(kv) || wn > 10000u || ww > 10000u || wn + ww > 10000u) return false;
+    const uint64_t t = (uint64_t(1) << kLog2M) - alphabet(kv);
+    *tn = static_cast<uint32_t>(t * wn / 10000u);
+    *tw = static_cast<uint32_t>(t * ww / 10000u);
+    *te = static_cast<uint32_t>(t - *tn - *tw);
+    return true;
+}
+
+// Shape rules shared by encoder and decoder.
+bool geometry(int64_t planes, int64_t tokens, int64_t channels, uint32_t chunk_tokens, ChunkGeom* g) {
+    if (planes < 1 || tokens < 1 || channels < 64 || channels % 64) return false;
+    if (planes > kMaxScalars || tokens > kMaxScalars || channels > kMaxScalars) return false;
+    if (planes * channels >= (int64_t(1) << 32)) return false;         // sigma words indexable
+    if (planes * tokens > kMaxScalars / channels) return false;
+    if (chunk_tokens < 1 || chunk_tokens > kMaxChunkTokens) return false;
+    g->planes = planes;
+    g->tokens = tokens;
+    g->channels = channels;
+    g->chunk_tokens = chunk_tokens;
+    g->n_tok_chunks = static_cast<uint32_t>((tokens + chunk_tokens - 1) / chunk_tokens);
+    g->n_groups = static_cast<uint32_t>(channels / 64);
+    g->pad = 0;
+    g->n_chunks = planes * int64_t(g->n_tok_chunks) * int64_t(g->n_groups);
+    return true;
+}
+
+bool params_geometry(const kvc_params* p, ChunkGeom* g) {
+    if (!p || !kv_dtype_ok(p->kv_dtype) || !mu_dtype_ok(p->mu_dtype) || p->reserved != 0) return false;
+    uint32_t tc = p->chunk_tokens;
+    if (tc == 0) tc = static_cast<uint32_t>(p->tokens < 1024 ? (p->tokens > 0 ? p->tokens : 1) : 1024);
+    return geometry(p->planes, p->tokens, p->channels, tc, g);
+}
+
+// Workspace of the encoder: control block, final states, word counts,
+// directory, then one word slot per chunk sized for two words per scalar.
+struct EncodeLayout {
+    uint64_t states, chunk_words, directory, slots, total, slot_words, max_stream;
+};
+
+EncodeLayout encode_layout(const ChunkGeom& g) {
+    EncodeLayout l;
+    const uint64_t n = static_cast<uint64_t>(g.n_chunks);
+    l.slot_words = round_up(2ull * kLanes * g.chunk_tokens, 4);
+    l.states = 256;
+    l.chunk_words = round_up(l.states + n * kLanes * 8, 256);
+    l.directory = round_up(l.chunk_words + n * 4, 256);
+    l.slots = round_up(l.directory + (n + 1) * 8, 256);
+    l.total = l.slots + n * l.slot_words * 2;
+    l.max_stream = KVC_HEADER_BYTES + 8 * (n + 1) + n * (kLanes * 8 + l.slot_words * 2);
+    return l;
+}
+
+void put16(uint8_t* b, int off, uint16_t v) { std::memcpy(b + off, &v, 2); }
+void put32(uint8_t* b, int off, uint32_t v) { std::memcpy(b + off, &v, 4); }
+void put64(uint8_t* b, int off, uint64_t v) { std::memcpy(b + off, &v, 8); }
+uint16_t get16(const uint8_t* b, int off) { uint16_t v; std::memcpy(&v, b + off, 2); return v; }
+uint32_t get32(const uint8_t* b, int off) { uint32_t v; std::memcpy(&v, b + off, 4); return v; }
+uint64_t get64(const uint8_t* b, int off) { uint64_t v; std::memcpy(&v, b + off, 8); return v; }
+
+// KVC-1 header; payload size (offset 72) and side hash (offset 80) are
+// filled in on the device.
+kvc::StreamHeader make_header(const kvc_params* p, const ChunkGeom& g, uint32_t tn, uint32_t tw, uint32_t te) {
+    kvc::StreamHeader h;
+    std::memset(h.bytes, 0, sizeof(h.bytes));
+    std::memcpy(h.bytes, "KVC1", 4);
+    put16(h.bytes, 4, kVersion);
+    put16(h.bytes, 6, KVC_HEADER_BYTES);
+    h.bytes[8] = static_cast<uint8_t>(p->kv_dtype);
+    h.bytes[9] = static_cast<uint8_t>(p->mu_dtype);
+    h.bytes[10] = kLog2M;
+    h.bytes[11] = kLog2L;
+    h.bytes[12] = kWordBits;
+    h.bytes[13] = kLanes;
+    put32(h.bytes, 16, p->w_narrow_bp);
+    put32(h.bytes, 20, p->w_wide_bp);
+    put32(h.bytes, 24, tn);
+    put32(h.bytes, 28, tw);
+    put32(h.bytes, 32, te);
+    put32(h.bytes, 36, g.chunk_tokens);
+    put64(h.bytes, 40, static_cast<uint64_t>(g.planes));
+    put64(h.bytes, 48, static_cast<uint64_t>(g.tokens));
+    put64(h.bytes, 56, static_cast<uint64_t>(g.channels));
+    put64(h.bytes, 64, static_cast<uint64_t>(g.n_chunks));
+    return h;
+}
+
+int parse_header(const uint8_t* b, kvc_params* p, ChunkGeom* g, uint64_t* payload, uint64_t* hash) {
+    if (std::memcmp(b, "KVC1", 4) != 0 || get16(b, 4) != kVersion || get16(b, 6) != KVC_HEADER_BYTES)
+        return KVC_ERR_CORRUPT;
+    if (b[10] != kLog2M || b[11] != kLog2L || b[12] != kWordBits || b[13] != kLanes || get16(b, 14) != 0)
+        return KVC_ERR_CORRUPT;
+    kvc_params q;
+    std::memset(&q, 0, sizeof(q));
+    q.kv_dtype = b[8];
+    q.mu_dtype = b[9];
+    q.w_narrow_bp = get32(b, 16);
+    q.w_wide_bp = get32(b, 20);
+    q.chunk_tokens = get32(b, 36);
+    q.planes = static_cast<int64_t>(get64(b, 40));
+    q.tokens = static_cast<int64_t>(get64(b, 48));
+    q.channels = static_cast<int64_t>(get64(b, 56));
+    uint32_t tn, tw, te;
+    if (!kv_dtype_ok(q.kv_dtype) || !mu_dtype_ok(q.mu_dtype) ||
+        !budgets(q.kv_dtype, q.w_narrow_bp, q.w_wide_bp, &tn, &tw, &te))
+        return KVC_ERR_CORRUPT;
+    if (tn != get32(b, 24) || tw != get32(b, 28) || te != get32(b, 32)) return KVC_ERR_CORRUPT;
+    if (get64(b, 40) > uint64_t(kMaxScalars) || get64(b, 48) > uint64_t(kMaxScalars) ||
+        get64(b, 56) > uint64_t(kMaxScalars))
+        return KVC_ERR_CORRUPT;
+    if (q.chunk_tokens == 0 || !geometry(q.planes, q.tokens, q.channels, q.chunk_tokens, g))
+        return KVC_ERR_CORRUPT;
+    if (get64(b, 64) != static_cast<uint64_t>(g->n_chunks)) return KVC_ERR_CORRUPT;
+    for (int i = 88; i < KVC_HEADER_BYTES; ++i)
+        if (b[i]) return KVC_ERR_CORRUPT;
+    *payload = get64(b, 72);
+    *hash = get64(b, 80);
+    if (p) *p = q;
+    return KVC_OK;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_DEVICE; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Element alignment of KV / mu / sigma / prefix buffers.
+bool data_aligned(int32_t kv_dtype, int32_t mu_dtype, const void* kv, const void* mu, const void* sigma,
+                  const void* prefix) {
+    return aligned(kv, kv_dtype == KVC_BF16 ? 2 : 1) && aligned(mu, mu_dtype == KVC_F32 ? 4 : 2) &&
+           aligned(sigma, 4) && aligned(prefix, 4);
+}
+
+// Optional stage timing with HIP events on the call's stream; inert when
+// the caller passes no output array.
+class StageTimer {
+  public:
+    StageTimer(float* out, int stages, hipStream_t s) : out_(out), n_(stages), s_(s) {
+        if (!out_) return;
+        for (int i = 0; i <= n_ && ok_; ++i) ok_ = hipEventCreate(&ev_[i]) == hipSuccess;
+    }
+    ~StageTimer() {
+        if (!out_) return;
+        for (int i = 0; i <= n_; ++i)
+            if (ev_[i]) (void)hipEventDestroy(ev_[i]);
+    }
+    void mark(int i) {
+        if (out_ && ok_) ok_ = hipEventRecord(ev_[i], s_) == hipSuccess;
+    }
+    // after the stream has been synchronised
+    void read() {
+        if (!out_) return;
+        for (int i = 0; i < n_; ++i) {
+            float ms = -1.0f;
+            if (ok_ && hipEventElapsedTime(&ms, ev_[i], ev_[i + 1]) != hipSuccess) ms = -1.0f;
+            out_[i] = ms;
+        }
+    }
+
+  private:
+    float* out_;
+    int n_;
+    hipStream_t s_;
+    bool ok_ = true;
+    hipEvent_t ev_[8] = {};
+};
+
+}  // namespace
+
+extern "C" {
+
+int kvc_version(void) { return static_cast<int>(kVersion); }
+
+const char* kvc_status_string(int status) {
+    switch (status) {
+        case KVC_OK: return "ok";
+        case KVC_ERR_INVALID: return "invalid argument";
+        case KVC_ERR_CAPACITY: return "buffer too small";
+        case KVC_ERR_CORRUPT: return "corrupt stream";
+        case KVC_ERR_MISMATCH: return "side information does not match the stream";
+        case KVC_ERR_DEVICE: return "device error";
+        default: return "unknown status";
+    }
+}
+
+int kvc_phi_table(uint32_t* h_out) {
+    if (!h_out) return KVC_ERR_INVALID;
+    kvc::host_phi_table(h_out);
+    return KVC_OK;
+}
+
+int kvc_encode_sizes(const kvc_params* p, uint64_t* h_max_stream_bytes, uint64_t* h_workspace_bytes) {
+    ChunkGeom g;
+    if (!params_geometry(p, &g)) return KVC_ERR_INVALID;
+    uint32_t tn, tw, te;
+    if (!budgets(p->kv_dtype, p->w_narrow_bp, p->w_wide_bp, &tn, &tw, &te)) return KVC_ERR_INVALID;
+    const EncodeLayout l = encode_layout(g);
+    if (h_max_stream_bytes) *h_max_stream_bytes = l.max_stream;
+    if (h_workspace_bytes) *h_workspace_bytes = l.total;
+    return KVC_OK;
+}
+
+int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const float* d_sigma,
+               const uint32_t* d_prefix, void* d_out, uint64_t out_capacity, uint64_t* h_out_bytes,
+               void* d_workspace, uint64_t workspace_bytes, void* stream, float* h_stage_ms) {
+    ChunkGeom g;
+    if (!params_geometry(p, &g) || !d_kv || !d_mu || !d_sigma || !d_out || !h_out_bytes || !d_workspace)
+        return KVC_ERR_INVALID;
+    uint32_t tn, tw, te;
+    if (!budgets(p->kv_dtype, p->w_narrow_bp, p->w_wide_bp, &tn, &tw, &te)) return KVC_ERR_INVALID;
+    if (te && !d_prefix) return KVC_ERR_INVALID;
+    if (!data_aligned(p->kv_dtype, p->mu_dtype, d_kv, d_mu, d_sigma, d_prefix) || !aligned(d_out, 8) ||
+        !aligned(d_workspace, 256))
+        return KVC_ERR_INVALID;
+    const EncodeLayout l = encode_layout(g);
+    if (workspace_bytes < l.total) return KVC_ERR_CAPACITY;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    const uint32_t* phi = kvc::device_phi_table(&e);
+    if (e != hipSuccess) return KVC_ERR_DEVICE;
+
+    uint8_t* ws = static_cast<uint8_t*>(d_workspace);
+    Control* ctl = reinterpret_cast<Control*>(ws);
+    const uint32_t* prefix = te ? d_prefix : nullptr;
+    StageTimer timer(h_stage_ms, KVC_ENCODE_STAGES, s);
+    if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    timer.mark(0);
+    if ((e = kvc::launch_side_hash(d_sigma, uint64_t(g.planes) * uint64_t(g.channels), prefix,
+                                   prefix ? alphabet(p->kv_dtype) + 1u : 0u, ctl, s)) != hipSuccess)
+        return KVC_ERR_DEVICE;
+    timer.mark(1);
+
+    kvc::EncodeArgs ea;
+    ea.geom = g;
+    ea.kv = d_kv;
+    ea.mu = d_mu;
+    ea.sigma = d_sigma;
+    ea.prefix = prefix;
+    ea.tn = tn;
+    ea.tw = tw;
+    ea.phi = phi;
+    ea.slots = reinterpret_cast<uint16_t*>(ws + l.slots);
+    ea.slot_words = l.slot_words;
+    ea.states = reinterpret_cast<unsigned long long*>(ws + l.states);
+    ea.chunk_words = reinterpret_cast<uint32_t*>(ws + l.chunk_words);
+    ea.ctl = ctl;
+    if ((e = kvc::launch_encode(ea, p->kv_dtype, p->mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    timer.mark(2);
+
+    unsigned long long* dir = reinterpret_cast<unsigned long long*>(ws + l.directory);
+    if ((e = kvc::launch_scan(ea.chunk_words, g.n_chunks, dir, ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    timer.mark(3);
+
+    kvc::CompactArgs ca;
+    ca.geom = g;
+    ca.slots = ea.slots;
+    ca.slot_words = l.slot_words;
+    ca.states = ea.states;
+    ca.chunk_words = ea.chunk_words;
+    ca.directory = dir;
+    ca.out = static_cast<uint8_t*>(d_out);
+    ca.out_capacity = out_capacity;
+    ca.ctl = ctl;
+    const kvc::StreamHeader h = make_header(p, g, tn, tw, te);
+    if ((e = kvc::launch_compact(ca, h, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    timer.mark(4);
+
+    Control host;
+    if ((e = hipMemcpyAsync(&host, ctl, sizeof(host), hipMemcpyDeviceToHost, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return KVC_ERR_DEVICE;
+    timer.read();
+    *h_out_bytes = KVC_HEADER_BYTES + 8ull * uint64_t(g.n_chunks + 1) + host.total_payload;
+    if (host.flags & kvc::kFlagBadSigma) return KVC_ERR_INVALID;
+    if (host.flags & kvc::kFlagCapacity) return KVC_ERR_CAPACITY;
+    return KVC_OK;
+}
+
+int kvc_stream_info(const void* h_header, uint64_t header_bytes, kvc_params* h_params, uint64_t* h_stream_bytes) {
+    if (!h_header || header_bytes < KVC_HEADER_BYTES) return KVC_ERR_INVALID;
+    ChunkGeom g;
+    uint64_t payload = 0, hash = 0;
+    const int st = parse_header(static_cast<const uint8_t*>(h_header), h_params, &g, &payload, &hash);
+    if (st != KVC_OK) return st;
+    if (h_stream_bytes) *h_stream_bytes = KVC_HEADER_BYTES + 8ull * uint64_t(g.n_chunks + 1) + payload;
+    return KVC_OK;
+}
+
+int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const float* d_sigma,
+               const uint32_t* d_prefix, void* d_kv_out, void* d_workspace, uint64_t workspace_bytes,
+               void* stream, float* h_stage_ms) {
+    if (!d_in || !d_mu || !d_sigma || !d_kv_out || !d_workspace) return KVC_ERR_INVALID;
+    if (workspace_bytes < KVC_DECODE_WORKSPACE_BYTES) return KVC_ERR_CAPACITY;
+    if (!aligned(d_in, 8) || !aligned(d_workspace, 8) || !aligned(d_sigma, 4) || !aligned(d_prefix, 4) ||
+        !aligned(d_kv_out, 2) || !aligned(d_mu, 2))
+        return KVC_ERR_INVALID;
+    if (in_bytes < KVC_HEADER_BYTES) return KVC_ERR_CORRUPT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    const uint32_t* phi = kvc::device_phi_table(&e);
+    if (e != hipSuccess) return KVC_ERR_DEVICE;
+
+    uint8_t hb[KVC_HEADER_BYTES];
+    if ((e = hipMemcpyAsync(hb, d_in, sizeof(hb), hipMemcpyDeviceToHost, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return KVC_ERR_DEVICE;
+    kvc_params p;
+    ChunkGeom g;
+    uint64_t payload = 0, hash = 0;
+    int st = parse_header(hb, &p, &g, &payload, &hash);
+    if (st != KVC_OK) return st;
+    const uint64_t dir_bytes = 8ull * uint64_t(g.n_chunks + 1);
+    if (in_bytes < KVC_HEADER_BYTES + dir_bytes || in_bytes - KVC_HEADER_BYTES - dir_bytes != payload)
+        return KVC_ERR_CORRUPT;
+    uint32_t tn, tw, te;
+    if (!budgets(p.kv_dtype, p.w_narrow_bp, p.w_wide_bp, &tn, &tw, &te)) return KVC_ERR_CORRUPT;
+    if (te && !d_prefix) return KVC_ERR_INVALID;
+    const uint32_t* prefix = te ? d_prefix : nullptr;
+    if (!data_aligned(p.kv_dtype, p.mu_dtype, d_kv_out, d_mu, d_sigma, d_prefix)) return KVC_ERR_INVALID;
+
+    Control* ctl = static_cast<Control*>(d_workspace);
+    StageTimer timer(h_stage_ms, KVC_DECODE_STAGES, s);
+    if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    timer.mark(0);
+    if ((e = kvc::launch_side_hash(d_sigma, uint64_t(g.planes) * uint64_t(g.channels), prefix,
+                                   prefix ? alphabet(p.kv_dtype) + 1u : 0u, ctl, s)) != hipSuccess)
+        return KVC_ERR_DEVICE;
+    timer.mark(1);
+    const uint8_t* in = static_cast<const uint8_t*>(d_in);
+    kvc::DecodeArgs da;
+    da.geom = g;
+    da.directory = reinterpret_cast<const unsigned long long*>(in + KVC_HEADER_BYTES);
+    da.payload = in + KVC_HEADER_BYTES + dir_bytes;
+    da.payload_bytes = payload;
+    da.mu = d_mu;
+    da.sigma = d_sigma;
+    da.prefix = prefix;
+    da.tn = tn;
+    da.tw = tw;
+    da.phi = phi;
+    da.kv_out = d_kv_out;
+    da.ctl = ctl;
+    if ((e = kvc::launch_decode(da, p.kv_dtype, p.mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    timer.mark(2);
+    Control host;
+    if ((e = hipMemcpyAsync(&host, ctl, sizeof(host), hipMemcpyDeviceToHost, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return KVC_ERR_DEVICE;
+    timer.read();
+    if (host.side_hash != hash) return KVC_ERR_MISMATCH;
+    if (host.flags & kvc::kFlagBadSigma) return KVC_ERR_INVALID;
+    if (host.flags & kvc::kFlagCorrupt) return KVC_ERR_CORRUPT;
+    return KVC_OK;
+}
+
+int kvc_calibrate_sigma(const void* d_kv, const void* d_mu, int32_t kv_dtype, int32_t mu_dtype, int64_t reps,
+                        int64_t planes, int64_t tokens, int64_t channels, float sigma_floor, float* d_sigma_out,
+                        void* stream) {
+    if (!d_kv || !d_mu || !d_sigma_out || !kv_dtype_ok(kv_dtype) || !mu_dtype_ok(mu_dtype)) return KVC_ERR_INVALID;
+    if (!data_aligned(kv_dtype, mu_dtype, d_kv, d_mu, d_sigma_out, nullptr)) return KVC_ERR_INVALID;
+    if (reps < 1 || planes < 1 || tokens < 1 || channels < 64 || channels % 64) return KVC_ERR_INVALID;
+    if (reps > kMaxScalars || planes > kMaxScalars || tokens > kMaxScalars || channels > kMaxScalars)
+        return KVC_ERR_INVALID;
+    if (reps * tokens > kMaxScalars / channels || reps * tokens * channels > kMaxScalars / planes)
+        return KVC_ERR_INVALID;
+    if (planes * (channels / 64) > 0x7FFFFFFF) return KVC_ERR_INVALID;
+    if (!(sigma_floor > 0.0f) || !(sigma_floor <= FLT_MAX)) return KVC_ERR_INVALID;
+    return finish(kvc::launch_calibrate(d_kv, d_mu, kv_dtype, mu_dtype, reps, planes, tokens, channels,
+                                        sigma_floor, d_sigma_out, static_cast<hipStream_t>(stream)));
+}
+
+int kvc_build_marginal(const void* d_samples, int32_t dtype, uint64_t n, uint32_t w_narrow_bp,
+                       uint32_t w_wide_bp, uint32_t* d_prefix_out, void* stream) {
+    uint32_t tn, tw, te;
+    if (!d_prefix_out || !budgets(dtype, w_narrow_bp, w_wide_bp, &tn, &tw, &te)) return KVC_ERR_INVALID;
+    if (n > 0 && !d_samples) return KVC_ERR_INVALID;
+    if (!aligned(d_samples, dtype == KVC_BF16 ? 2 : 1) || !aligned(d_prefix_out, 4)) return KVC_ERR_INVALID;
+    if (n >= (uint64_t(1) << 32) - (uint64_t(1) << 16)) return KVC_ERR_INVALID;
+    return finish(kvc::launch_marginal(d_samples, dtype, n, te, d_prefix_out, static_cast<hipStream_t>(stream)));
+}
+
+int kvc_estimate_bits(const kvc_params* p, const void* d_kv, const void* d_mu, const float* d_sigma,
+                      const uint32_t* d_prefix, double* h_bits_out, void* d_workspace, uint64_t workspace_bytes,
+                      void* stream) {
+    ChunkGeom g;
+    if (!params_geometry(p, &g) || !d_kv || !d_mu || !d_sigma || !h_bits_out || !d_workspace)
+        return KVC_ERR_INVALID;
+    if (workspace_bytes < KVC_ESTIMATE_WORKSPACE_BYTES) return KVC_ERR_CAPACITY;
+    if (!data_aligned(p->kv_dtype, p->mu_dtype, d_kv, d_mu, d_sigma, d_prefix) || !aligned(d_workspace, 8))
+        return KVC_ERR_INVALID;
+    uint32_t tn, tw, te;
+    if (!budgets(p->kv_dtype, p->w_narrow_bp, p->w_wide_bp, &tn, &tw, &te)) return KVC_ERR_INVALID;
+    if (te && !d_prefix) return KVC_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    const uint32_t* phi = kvc::device_phi_table(&e);
+    if (e != hipSuccess) return KVC_ERR_DEVICE;
+    Control* ctl = static_cast<Control*>(d_workspace);
+    if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    kvc::EstimateArgs a;
+    a.geom = g;
+    a.kv = d_kv;
+    a.mu = d_mu;
+    a.sigma = d_sigma;
+    a.prefix = te ? d_prefix : nullptr;
+    a.tn = tn;
+    a.tw = tw;
+    a.te = te;
+    a.w_narrow_bp = p->w_narrow_bp;
+    a.w_wide_bp = p->w_wide_bp;
+    a.phi = phi;
+    a.ctl = ctl;
+    if ((e = kvc::launch_estimate(a, p->kv_dtype, p->mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    Control host;
+    if ((e = hipMemcpyAsync(&host, ctl, sizeof(host), hipMemcpyDeviceToHost, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return KVC_ERR_DEVICE;
+    const double n = static_cast<double>(g.planes) * static_cast<double>(g.tokens) * static_cast<double>(g.channels);
+    h_bits_out[0] = host.bits[0] / n;
+    h_bits_out[1] = host.bits[1] / n;
+    return KVC_OK;
+}
+
+int kvc_cdf_table(int32_t kv_dtype, int32_t mu_dtype, uint32_t w_narrow_bp, uint32_t w_wide_bp, const void* d_mu,
+                  const float* d_sigma, int64_t pairs, const uint32_t* d_prefix, uint32_t* d_out, void* stream) {
+    uint32_t tn, tw, te;
+    if (!mu_dtype_ok(mu_dtype) || !budgets(kv_dtype, w_narrow_bp, w_wide_bp, &tn, &tw, &te)) return KVC_ERR_INVALID;
+    if (pairs < 1 || pairs > (int64_t(1) << 24) || !d_mu || !d_sigma || !d_out) return KVC_ERR_INVALID;
+    if (te && !d_prefix) return KVC_ERR_INVALID;
+    if (!data_aligned(kv_dtype, mu_dtype, nullptr, d_mu, d_sigma, d_prefix) || !aligned(d_out, 4))
+        return KVC_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    const uint32_t* phi = kvc::device_phi_table(&e);
+    if (e != hipSuccess) return KVC_ERR_DEVICE;
+    // sigma is checked on the host, a block at a time
+    bool ok = true;
+    float hs[1024];
+    for (int64_t i0 = 0; i0 < pairs && ok; i0 += 1024) {
+        const int64_t m = (pairs - i0 < 1024) ? pairs - i0 : 1024;
+        e = hipMemcpyAsync(hs, d_sigma + i0, sizeof(float) * static_cast<size_t>(m), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return KVC_ERR_DEVICE;
+        for (int64_t i = 0; i < m; ++i) {
+            const float sg = hs[i];
+            const float inv = 1.0f / sg;
+            if (!(sg > 0.0f) || !(sg <= FLT_MAX) || !(inv <= FLT_MAX)) ok = false;
+        }
+    }
+    if (!ok) return KVC_ERR_INVALID;
+    e = kvc::launch_cdf_table(kv_dtype, mu_dtype, tn, tw, d_mu, d_sigma, pairs, te ? d_prefix : nullptr, d_out,
+                              phi, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return finish(e);
+}
+
+}  // extern "C"

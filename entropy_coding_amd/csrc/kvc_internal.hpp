@@ -1,0 +1,118 @@
+// Host-side interface between the C ABI (kvc_api.cpp) and the kernels
+// (kvc_kernels.hip): plain structs of device pointers and sizes, and the
+// launch functions.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace kvc {
+
+// Status bits the kernels raise in the workspace flag word.
+enum : uint32_t {
+    kFlagBadSigma = 1u,
+    kFlagCorrupt = 2u,
+    kFlagCapacity = 4u,
+};
+
+// Control block at the head of every workspace (cleared by a kernel).
+struct Control {
+    uint32_t flags;
+    uint32_t pad;
+    unsigned long long side_hash;       // sum of mixed side-information words
+    unsigned long long total_payload;   // payload bytes of the stream
+    double bits[2];                     // estimate sums (integer model, float model)
+    unsigned long long reserved[3];
+};
+static_assert(sizeof(Control) == 64, "control block size");
+
+struct ChunkGeom {
+    int64_t planes, tokens, channels;
+    uint32_t chunk_tokens;
+    uint32_t n_tok_chunks;              // ceil(tokens / chunk_tokens)
+    uint32_t n_groups;                  // channels / 64
+    uint32_t pad;
+    int64_t n_chunks;
+};
+
+struct EncodeArgs {
+    ChunkGeom geom;
+    const void* kv;
+    const void* mu;
+    const float* sigma;
+    const uint32_t* prefix;             // null when there is no escape part
+    uint32_t tn, tw;
+    const uint32_t* phi;                // device Phi table (kPhiEntries)
+    uint16_t* slots;                    // per-chunk word slots, filled from the end
+    uint64_t slot_words;                // words per slot (2 per scalar, multiple of 4)
+    unsigned long long* states;         // [n_chunks][64] final states
+    uint32_t* chunk_words;              // [n_chunks] words used
+    Control* ctl;
+};
+
+struct StreamHeader {
+    uint8_t bytes[128];
+};
+
+struct CompactArgs {
+    ChunkGeom geom;
+    const uint16_t* slots;
+    uint64_t slot_words;
+    const unsigned long long* states;
+    const uint32_t* chunk_words;
+    const unsigned long long* directory;   // [n_chunks + 1] payload offsets
+    uint8_t* out;
+    uint64_t out_capacity;
+    Control* ctl;
+};
+
+struct DecodeArgs {
+    ChunkGeom geom;
+    const uint8_t* payload;             // first payload byte of the stream
+    const unsigned long long* directory;
+    uint64_t payload_bytes;
+    const void* mu;
+    const float* sigma;
+    const uint32_t* prefix;
+    uint32_t tn, tw;
+    const uint32_t* phi;
+    void* kv_out;
+    Control* ctl;
+};
+
+struct EstimateArgs {
+    ChunkGeom geom;
+    const void* kv;
+    const void* mu;
+    const float* sigma;
+    const uint32_t* prefix;
+    uint32_t tn, tw, te;
+    uint32_t w_narrow_bp, w_wide_bp;
+    const uint32_t* phi;
+    Control* ctl;
+};
+
+// Per-device Phi table: computed once on the host, copied to the device.
+const uint32_t* device_phi_table(hipError_t* err);
+void host_phi_table(uint32_t* out);   // kPhiEntries entries
+
+hipError_t launch_clear_control(Control* ctl, hipStream_t s);
+hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t* prefix,
+                            uint64_t n_prefix, Control* ctl, hipStream_t s);
+hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);
+hipError_t launch_scan(const uint32_t* chunk_words, int64_t n_chunks,
+                       unsigned long long* directory, Control* ctl, hipStream_t s);
+hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);
+hipError_t launch_calibrate(const void* kv, const void* mu, int kv_dtype, int mu_dtype,
+                            int64_t reps, int64_t planes, int64_t tokens, int64_t channels,
+                            float sigma_floor, float* sigma_out, hipStream_t s);
+hipError_t launch_marginal(const void* samples, int dtype, uint64_t n, uint32_t te,
+                           uint32_t* prefix_out, hipStream_t s);
+hipError_t launch_estimate(const EstimateArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);
+hipError_t launch_cdf_table(int kv_dtype, int mu_dtype, uint32_t tn, uint32_t tw,
+                            const void* mu, const float* sigma, int64_t pairs,
+                            const uint32_t* prefix, uint32_t* out, const uint32_t* phi,
+                            hipStream_t s);
+
+}  // namespace kvc

@@ -1,0 +1,652 @@
+// HIP kernels of the KVC-1 coder for gfx950 (MI355X).
+//
+// One 64-lane wavefront owns one chunk: lane l codes channel 64k + l of one
+// plane over a run of tokens, so every token step reads one contiguous
+// 64-element row of KV and mu per wave, and the 64 interleaved rANS states
+// live in registers.  Renormalisation words are placed with two wave ballots
+// and mbcnt ranks.  The Phi table sits in LDS; the escape prefix (256 KB for
+// bf16) is read through L2.  Sources for the model: wiki "Speculative KV
+// Coding" (sections "pipeline", "mixture distribution"); blog post on
+// speculative KV coding (sections "information theory view",
+// "engineering choice of predictor", "deployment parameters").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "kvc_device.hpp"
+#include "kvc_internal.hpp"
+
+namespace kvc {
+
+// ---------------------------------------------------------------------------
+// Phi table: round(2^31 Phi(-8 + k/256)), computed on the host with the C
+// library's erfc in double precision (no entry lies within 1e-6 of a
+// rounding tie, far above double's error) and copied to each device once.
+// ---------------------------------------------------------------------------
+__device__ uint32_t g_phi[kPhiEntries];
+
+void host_phi_table(uint32_t* out) {
+    for (int k = 0; k <= 4096; ++k) {
+        const double x = -8.0 + k / 256.0;
+        const double v = std::ldexp(0.5 * std::erfc(-x * 0.70710678118654752440), 31);
+        out[k] = static_cast<uint32_t>(std::floor(v + 0.5));
+    }
+    out[4097] = out[4096];
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_phi_once[kMaxDevices];
+const uint32_t* g_phi_ptr[kMaxDevices];
+hipError_t g_phi_err[kMaxDevices];
+}  // namespace
+
+const uint32_t* device_phi_table(hipError_t* err) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = (e != hipSuccess) ? e : hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::call_once(g_phi_once[dev], [dev]() {
+        uint32_t host[kPhiEntries];
+        host_phi_table(host);
+        hipError_t r = hipMemcpyToSymbol(HIP_SYMBOL(g_phi), host, sizeof(host), 0, hipMemcpyHostToDevice);
+        void* p = nullptr;
+        if (r == hipSuccess) r = hipGetSymbolAddress(&p, HIP_SYMBOL(g_phi));
+        g_phi_err[dev] = r;
+        g_phi_ptr[dev] = static_cast<const uint32_t*>(p);
+    });
+    *err = g_phi_err[dev];
+    return g_phi_ptr[dev];
+}
+
+// ---------------------------------------------------------------------------
+// helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load_phi_lds(uint32_t* s_phi, const uint32_t* __restrict__ phi) {
+    for (int i = threadIdx.x; i < kPhiEntries; i += blockDim.x) s_phi[i] = phi[i];
+    __syncthreads();
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+struct ChunkPos {
+    int64_t g;
+    uint32_t t0, len, k;
+};
+
+__device__ __forceinline__ ChunkPos chunk_pos(const ChunkGeom& geo, int64_t c) {
+    ChunkPos p;
+    p.k = static_cast<uint32_t>(c % geo.n_groups);
+    const int64_t rest = c / geo.n_groups;
+    const uint32_t tc = static_cast<uint32_t>(rest % geo.n_tok_chunks);
+    p.g = rest / geo.n_tok_chunks;
+    p.t0 = tc * geo.chunk_tokens;
+    const int64_t left = geo.tokens - static_cast<int64_t>(p.t0);
+    p.len = static_cast<uint32_t>(left < geo.chunk_tokens ? left : geo.chunk_tokens);
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// control block and side-information checksum
+// ---------------------------------------------------------------------------
+__global__ void k_clear_control(Control* ctl) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(ctl);
+    if (threadIdx.x < sizeof(Control) / 4) w[threadIdx.x] = 0u;
+}
+
+hipError_t launch_clear_control(Control* ctl, hipStream_t s) {
+    hipLaunchKernelGGL(k_clear_control, dim3(1), dim3(64), 0, s, ctl);
+    return hipGetLastError();
+}
+
+// splitmix64 output function (Vigna's published constants).
+__device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+__global__ void __launch_bounds__(256) k_side_hash(const uint32_t* __restrict__ sigma_words, uint64_t n1,
+                                                   const uint32_t* __restrict__ prefix, uint64_t n2,
+                                                   Control* ctl) {
+    const unsigned long long golden = 0x9E3779B97F4A7C15ull;
+    unsigned long long acc = 0;
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t j = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < n1 + n2; j += stride) {
+        unsigned long long i, w, tag;
+        if (j < n1) { i = j; w = sigma_words[j]; tag = 1; }
+        else { i = j - n1; w = prefix[j - n1]; tag = 2; }
+        acc += mix64(((i << 32) | w) + tag * golden);
+    }
+    acc = wave_sum_u64(acc);
+    if ((threadIdx.x & 63) == 0 && acc) atomicAdd(&ctl->side_hash, acc);
+}
+
+hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t* prefix,
+                            uint64_t n_prefix, Control* ctl, hipStream_t s) {
+    const uint64_t n = n_sigma + n_prefix;
+    uint64_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(k_side_hash, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s,
+                       reinterpret_cast<const uint32_t*>(sigma), n_sigma, prefix, n_prefix, ctl);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// encoder: one wave per chunk, tokens last to first
+// ---------------------------------------------------------------------------
+template <int KV, int MU>
+__global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
+    __shared__ uint32_t s_phi[kPhiEntries];
+    load_phi_lds(s_phi, a.phi);
+
+    const int lane = threadIdx.x & 63;
+    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (chunk >= a.geom.n_chunks) return;
+    const ChunkPos cp = chunk_pos(a.geom, chunk);
+    const int64_t D = a.geom.channels;
+    const int64_t d = static_cast<int64_t>(cp.k) * 64 + lane;
+
+    const float sigma = a.sigma[cp.g * D + d];
+    float inv = __frcp_rn(sigma);
+    const bool ok = sigma_ok(sigma, inv);
+    if (__ballot(!ok)) {
+        if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
+        inv = 1.0f;
+    }
+    const Budgets bud{a.tn, a.tw, a.prefix};
+
+    using KB = typename Alphabet<KV>::Bits;
+    using MT = typename MuT<MU>::T;
+    const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * D + d;
+    const KB* __restrict__ kvp = static_cast<const KB*>(a.kv) + row0;
+    const MT* __restrict__ mup = static_cast<const MT*>(a.mu) + row0;
+
+    uint16_t* __restrict__ slot = a.slots + static_cast<uint64_t>(chunk) * a.slot_words;
+    uint32_t wp = static_cast<uint32_t>(a.slot_words);
+    unsigned long long x = kL;
+
+    for (int t = static_cast<int>(cp.len) - 1; t >= 0; --t) {
+        const int64_t off = static_cast<int64_t>(t) * D;
+        const uint32_t s = order_of_bits<KV>(kvp[off]);
+        const float mu = mu_value<MU>(mup[off]);
+        const uint32_t c0 = cdf_at<KV>(s, mu, inv, s_phi, bud);
+        const uint32_t c1 = cdf_at<KV>(s + 1, mu, inv, s_phi, bud);
+        const uint32_t f = c1 - c0;
+
+        const uint32_t cnt = static_cast<uint32_t>((x >> 32) >= f) + static_cast<uint32_t>((x >> 48) >= f);
+        const uint64_t m1 = __ballot(cnt >= 1u);
+        const uint64_t m2 = __ballot(cnt == 2u);
+        const uint32_t n1 = __popcll(m1), n2 = __popcll(m2);
+        wp -= n1 + n2;
+        if (cnt >= 1u) slot[wp + lane_rank(m1)] = static_cast<uint16_t>(cnt == 2u ? (x >> 16) : x);
+        if (cnt == 2u) slot[wp + n1 + lane_rank(m2)] = static_cast<uint16_t>(x);
+        x >>= 16u * cnt;
+        const unsigned long long qt = x / f;
+        const unsigned long long rm = x - qt * f;
+        x = (qt << kLog2M) + rm + c0;
+    }
+    a.states[chunk * 64 + lane] = x;
+    if (lane == 0) a.chunk_words[chunk] = static_cast<uint32_t>(a.slot_words) - wp;
+}
+
+hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s) {
+    const uint64_t blocks = (static_cast<uint64_t>(a.geom.n_chunks) + 3) / 4;
+    const dim3 grid(static_cast<uint32_t>(blocks)), block(256);
+    if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_encode<kBF16, kBF16>), grid, block, 0, s, a);
+    else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_encode<kBF16, kF32>), grid, block, 0, s, a);
+    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_encode<kE4M3, kBF16>), grid, block, 0, s, a);
+    else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_encode<kE4M3, kF32>), grid, block, 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// stream compaction: exclusive scan of chunk sizes (one workgroup, wave
+// scans), then one workgroup per chunk copies states and words to the
+// chunk's final offset.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned long long chunk_bytes(uint32_t words) {
+    return (static_cast<unsigned long long>(kStateBytes) + 2ull * words + 7ull) & ~7ull;
+}
+
+__device__ __forceinline__ unsigned long long wave_inclusive_scan(unsigned long long v) {
+    const int lane = threadIdx.x & 63;
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long u = __shfl_up(v, off, 64);
+        if (lane >= off) v += u;
+    }
+    return v;
+}
+
+__global__ void __launch_bounds__(1024) k_scan(const uint32_t* __restrict__ words, int64_t n,
+                                               unsigned long long* __restrict__ dir, Control* ctl) {
+    __shared__ unsigned long long s_wave[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t per = (n + 1023) / 1024;
+    const int64_t lo = tid * per;
+    const int64_t hi = (lo + per < n) ? lo + per : n;
+    unsigned long long local = 0;
+    for (int64_t i = lo; i < hi; ++i) local += chunk_bytes(words[i]);
+    const unsigned long long inc = wave_inclusive_scan(local);
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        unsigned long long w = (lane < 16) ? s_wave[lane] : 0ull;
+        const unsigned long long wi = wave_inclusive_scan(w);
+        if (lane < 16) s_wave[lane] = wi - w;      // exclusive over waves
+    }
+    __syncthreads();
+    unsigned long long run = s_wave[wave] + inc - local;
+    for (int64_t i = lo; i < hi; ++i) {
+        dir[i] = run;
+        run += chunk_bytes(words[i]);
+    }
+    if (tid == 1023) {
+        dir[n] = run;
+        ctl->total_payload = run;
+    }
+}
+
+hipError_t launch_scan(const uint32_t* chunk_words, int64_t n_chunks, unsigned long long* directory,
+                       Control* ctl, hipStream_t s) {
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, chunk_words, n_chunks, directory, ctl);
+    return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) k_compact(CompactArgs a, StreamHeader h) {
+    const int64_t n = a.geom.n_chunks;
+    const unsigned long long total = a.ctl->total_payload;
+    const uint64_t dir_off = kHeaderBytes;
+    const uint64_t pay_off = dir_off + 8ull * static_cast<uint64_t>(n + 1);
+    if (pay_off + total > a.out_capacity) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&a.ctl->flags, kFlagCapacity);
+        return;
+    }
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid < kHeaderBytes / 8) {
+        unsigned long long w;
+        __builtin_memcpy(&w, h.bytes + 8 * tid, 8);
+        if (tid == 72 / 8) w = total;
+        if (tid == 80 / 8) w = a.ctl->side_hash;
+        reinterpret_cast<unsigned long long*>(a.out)[tid] = w;
+    }
+    unsigned long long* odir = reinterpret_cast<unsigned long long*>(a.out + dir_off);
+    for (int64_t c = blockIdx.x; c < n; c += gridDim.x) {
+        const unsigned long long beg = a.directory[c];
+        if (tid == 0) {
+            odir[c] = beg;
+            if (c == n - 1) odir[n] = total;
+        }
+        uint8_t* dst = a.out + pay_off + beg;
+        if (tid < 64) reinterpret_cast<unsigned long long*>(dst)[tid] = a.states[c * 64 + tid];
+        const uint32_t nw = a.chunk_words[c];
+        const uint16_t* src = a.slots + static_cast<uint64_t>(c) * a.slot_words + (a.slot_words - nw);
+        uint16_t* dw = reinterpret_cast<uint16_t*>(dst + kStateBytes);
+        const uint32_t padded = static_cast<uint32_t>((chunk_bytes(nw) - kStateBytes) / 2);
+        for (uint32_t i = tid; i < padded; i += blockDim.x) dw[i] = (i < nw) ? src[i] : uint16_t(0);
+    }
+}
+
+hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream_t s) {
+    int64_t blocks = a.geom.n_chunks;
+    if (blocks > 65535) blocks = 65535;
+    hipLaunchKernelGGL(k_compact, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a, h);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// decoder: one wave per chunk, tokens first to last
+// ---------------------------------------------------------------------------
+template <int KV, int MU>
+__global__ void __launch_bounds__(256) k_decode(DecodeArgs a) {
+    __shared__ uint32_t s_phi[kPhiEntries];
+    load_phi_lds(s_phi, a.phi);
+
+    const int lane = threadIdx.x & 63;
+    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (chunk >= a.geom.n_chunks) return;
+    const ChunkPos cp = chunk_pos(a.geom, chunk);
+    const int64_t D = a.geom.channels;
+    const int64_t d = static_cast<int64_t>(cp.k) * 64 + lane;
+
+    // the chunk's directory entry must describe an aligned, in-bounds payload
+    const unsigned long long beg = a.directory[chunk], end = a.directory[chunk + 1];
+    if (beg > end || end > a.payload_bytes || end - beg < kStateBytes || (beg & 7ull) || (end & 7ull)) {
+        if (lane == 0) atomicOr(&a.ctl->flags, kFlagCorrupt);
+        return;
+    }
+    const uint8_t* base = a.payload + beg;
+    unsigned long long x = reinterpret_cast<const unsigned long long*>(base)[lane];
+    const uint16_t* __restrict__ words = reinterpret_cast<const uint16_t*>(base + kStateBytes);
+    const uint32_t avail = static_cast<uint32_t>((end - beg - kStateBytes) / 2);
+
+    const float sigma = a.sigma[cp.g * D + d];
+    float inv = __frcp_rn(sigma);
+    if (__ballot(!sigma_ok(sigma, inv))) {
+        if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
+        inv = 1.0f;
+    }
+    const Budgets bud{a.tn, a.tw, a.prefix};
+
+    using KB = typename Alphabet<KV>::Bits;
+    using MT = typename MuT<MU>::T;
+    const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * D + d;
+    KB* __restrict__ outp = static_cast<KB*>(a.kv_out) + row0;
+    const MT* __restrict__ mup = static_cast<const MT*>(a.mu) + row0;
+
+    uint32_t rp = 0;
+    for (uint32_t t = 0; t < cp.len; ++t) {
+        const int64_t off = static_cast<int64_t>(t) * D;
+        const float mu = mu_value<MU>(mup[off]);
+        const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
+        uint32_t lo = 0, hi = Alphabet<KV>::kSize, clo = 0, chi = kM;
+#pragma unroll 1
+        for (int it = 0; it < Alphabet<KV>::kLog2; ++it) {
+            const uint32_t mid = (lo + hi) >> 1;
+            const uint32_t cm = cdf_at<KV>(mid, mu, inv, s_phi, bud);
+            const bool go = cm <= target;
+            lo = go ? mid : lo;
+            clo = go ? cm : clo;
+            hi = go ? hi : mid;
+            chi = go ? chi : cm;
+        }
+        const uint32_t f = chi - clo;
+        x = static_cast<unsigned long long>(f) * (x >> kLog2M) + (target - clo);
+
+        bool need = x < kL;
+        const uint64_t m1 = __ballot(need);
+        const uint32_t n1 = __popcll(m1);
+        if (need) {
+            const uint32_t i = rp + lane_rank(m1);
+            x = (x << 16) | (i < avail ? words[i] : 0u);
+        }
+        need = x < kL;
+        const uint64_t m2 = __ballot(need);
+        const uint32_t n2 = __popcll(m2);
+        if (need) {
+            const uint32_t i = rp + n1 + lane_rank(m2);
+            x = (x << 16) | (i < avail ? words[i] : 0u);
+        }
+        rp += n1 + n2;
+        outp[off] = static_cast<KB>(bits_of_order<KV>(lo));
+    }
+    // every lane back at the initial state, the payload consumed exactly,
+    // the padding zero
+    bool bad = (x != kL) || (chunk_bytes(rp) != end - beg);
+    if (!bad) {
+        const uint32_t pad_words = avail - rp;        // 0..3
+        if (static_cast<uint32_t>(lane) < pad_words && words[rp + lane] != 0) bad = true;
+    }
+    if (__ballot(bad) && lane == 0) atomicOr(&a.ctl->flags, kFlagCorrupt);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s) {
+    const uint64_t blocks = (static_cast<uint64_t>(a.geom.n_chunks) + 3) / 4;
+    const dim3 grid(static_cast<uint32_t>(blocks)), block(256);
+    if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kBF16, kBF16>), grid, block, 0, s, a);
+    else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_decode<kBF16, kF32>), grid, block, 0, s, a);
+    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kE4M3, kBF16>), grid, block, 0, s, a);
+    else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_decode<kE4M3, kF32>), grid, block, 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// sigma calibration: one workgroup of 16 waves per (plane, 64-channel
+// group); wave w sums rows w, w+16, ... in float64; the 16 partial sums are
+// added in wave order, so the result does not depend on scheduling.
+// ---------------------------------------------------------------------------
+template <int KV>
+__device__ __forceinline__ double kv_value_f64(typename Alphabet<KV>::Bits b) {
+    if constexpr (KV == kBF16) {
+        return static_cast<double>(__uint_as_float(static_cast<uint32_t>(b) << 16));
+    } else {
+        const uint32_t u = b;
+        const uint32_t m = u & 0x7Fu;
+        if (m == 0x7Fu) return __builtin_nan("");
+        const double v = static_cast<double>(e4m3_magnitude(m));
+        return (u & 0x80u) ? -v : v;
+    }
+}
+
+template <int KV, int MU>
+__global__ void __launch_bounds__(1024) k_calibrate(const void* kv_, const void* mu_, int64_t reps,
+                                                    int64_t planes, int64_t tokens, int64_t channels,
+                                                    float floor_, float* __restrict__ out) {
+    __shared__ double s_part[16][64];
+    __shared__ int64_t s_used[16][64];
+    using KB = typename Alphabet<KV>::Bits;
+    using MT = typename MuT<MU>::T;
+    const KB* __restrict__ kv = static_cast<const KB*>(kv_);
+    const MT* __restrict__ mu = static_cast<const MT*>(mu_);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t groups = channels / 64;
+    const int64_t p = blockIdx.x / groups;
+    const int64_t d = (blockIdx.x % groups) * 64 + lane;
+    const int64_t rows = reps * tokens;
+    double acc = 0.0;
+    int64_t used = 0;
+    for (int64_t r = wave; r < rows; r += 16) {
+        const int64_t rep = r / tokens, t = r - rep * tokens;
+        const int64_t off = ((rep * planes + p) * tokens + t) * channels + d;
+        const double e = kv_value_f64<KV>(kv[off]) - static_cast<double>(mu_value<MU>(mu[off]));
+        const double e2 = e * e;
+        if (__builtin_isfinite(e2)) {       // a non-finite residual says nothing about scale
+            acc += e2;
+            ++used;
+        }
+    }
+    s_part[wave][lane] = acc;
+    s_used[wave][lane] = used;
+    __syncthreads();
+    if (wave == 0) {
+        double s = 0.0;
+        int64_t u = 0;
+        for (int w = 0; w < 16; ++w) { s += s_part[w][lane]; u += s_used[w][lane]; }
+        const float sg = u ? static_cast<float>(sqrt(s / static_cast<double>(u))) : 0.0f;
+        out[p * channels + d] = (sg > floor_ && __builtin_isfinite(sg)) ? sg : floor_;
+    }
+}
+
+hipError_t launch_calibrate(const void* kv, const void* mu, int kv_dtype, int mu_dtype, int64_t reps,
+                            int64_t planes, int64_t tokens, int64_t channels, float sigma_floor,
+                            float* sigma_out, hipStream_t s) {
+    const int64_t blocks = planes * (channels / 64);
+    const dim3 grid(static_cast<uint32_t>(blocks)), block(1024);
+    if (kv_dtype == kBF16 && mu_dtype == kBF16)
+        hipLaunchKernelGGL((k_calibrate<kBF16, kBF16>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, sigma_floor, sigma_out);
+    else if (kv_dtype == kBF16 && mu_dtype == kF32)
+        hipLaunchKernelGGL((k_calibrate<kBF16, kF32>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, sigma_floor, sigma_out);
+    else if (kv_dtype == kE4M3 && mu_dtype == kBF16)
+        hipLaunchKernelGGL((k_calibrate<kE4M3, kBF16>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, sigma_floor, sigma_out);
+    else if (kv_dtype == kE4M3 && mu_dtype == kF32)
+        hipLaunchKernelGGL((k_calibrate<kE4M3, kF32>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, sigma_floor, sigma_out);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// empirical marginal: histogram in value order (integer atomics, so the
+// result does not depend on order), then one workgroup turns counts + 1
+// into the scaled prefix in place.
+// ---------------------------------------------------------------------------
+__global__ void k_fill_u32(uint32_t* __restrict__ p, uint64_t n, uint32_t v) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+template <int KV>
+__global__ void __launch_bounds__(256) k_histogram(const void* samples_, uint64_t n, uint32_t* __restrict__ hist) {
+    using KB = typename Alphabet<KV>::Bits;
+    const KB* __restrict__ s = static_cast<const KB*>(samples_);
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+        atomicAdd(&hist[order_of_bits<KV>(s[i])], 1u);
+}
+
+// THREADS * PER = N.  Reads every count into registers before writing.
+template <int THREADS, int PER>
+__global__ void __launch_bounds__(THREADS) k_marginal_prefix(uint32_t* __restrict__ hist, uint32_t te) {
+    __shared__ unsigned long long s_wave[THREADS / 64];
+    constexpr int N = THREADS * PER;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t c[PER];
+    unsigned long long local = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        c[j] = hist[tid * PER + j] + 1u;
+        local += c[j];
+    }
+    const unsigned long long inc = wave_inclusive_scan(local);
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        const unsigned long long w = (lane < THREADS / 64) ? s_wave[lane] : 0ull;
+        const unsigned long long wi = wave_inclusive_scan(w);
+        if (lane < THREADS / 64) s_wave[lane] = wi;          // inclusive over waves
+    }
+    __syncthreads();
+    const unsigned long long total = s_wave[THREADS / 64 - 1];
+    unsigned long long run = (wave ? s_wave[wave - 1] : 0ull) + inc - local;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        hist[tid * PER + j] = static_cast<uint32_t>((static_cast<unsigned long long>(te) * run) / total);
+        run += c[j];
+    }
+    if (tid == THREADS - 1) hist[N] = te;
+}
+
+hipError_t launch_marginal(const void* samples, int dtype, uint64_t n, uint32_t te, uint32_t* prefix_out,
+                           hipStream_t s) {
+    const uint64_t nsym = dtype == kBF16 ? 65536u : 256u;
+    hipLaunchKernelGGL(k_fill_u32, dim3(64), dim3(256), 0, s, prefix_out, nsym + 1, 0u);
+    uint64_t blocks = (n + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks == 0) blocks = 1;
+    if (dtype == kBF16) {
+        hipLaunchKernelGGL(k_histogram<kBF16>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, samples, n, prefix_out);
+        hipLaunchKernelGGL((k_marginal_prefix<1024, 64>), dim3(1), dim3(1024), 0, s, prefix_out, te);
+    } else {
+        hipLaunchKernelGGL(k_histogram<kE4M3>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, samples, n, prefix_out);
+        hipLaunchKernelGGL((k_marginal_prefix<256, 1>), dim3(1), dim3(256), 0, s, prefix_out, te);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// bits estimates: integer model (exact f of the coder) and the continuous
+// mixture over the same cells in float64
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double gauss_mass(double a, double b) {
+    // Phi(b) - Phi(a) for a <= b; the upper-tail form avoids cancellation
+    const double k = 0.70710678118654752440;
+    if (a > 0.0) return 0.5 * (erfc(a * k) - erfc(b * k));
+    return 0.5 * (erfc(-b * k) - erfc(-a * k));
+}
+
+template <int KV, int MU>
+__global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
+    __shared__ uint32_t s_phi[kPhiEntries];
+    __shared__ double s_red[2][4];
+    load_phi_lds(s_phi, a.phi);
+    using KB = typename Alphabet<KV>::Bits;
+    using MT = typename MuT<MU>::T;
+    const KB* __restrict__ kv = static_cast<const KB*>(a.kv);
+    const MT* __restrict__ mup = static_cast<const MT*>(a.mu);
+    const Budgets bud{a.tn, a.tw, a.prefix};
+    const int64_t D = a.geom.channels, T = a.geom.tokens;
+    const int64_t n = a.geom.planes * T * D;
+    const double wn = a.w_narrow_bp / 1e4, ww = a.w_wide_bp / 1e4, we = 1.0 - wn - ww;
+    double acc_i = 0.0, acc_f = 0.0;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const int64_t d = i % D;
+        const int64_t g = i / (T * D);
+        const float sg = a.sigma[g * D + d];
+        const float inv = __frcp_rn(sg);
+        const float mu = mu_value<MU>(mup[i]);
+        const uint32_t s = order_of_bits<KV>(kv[i]);
+        const uint32_t c0 = cdf_at<KV>(s, mu, inv, s_phi, bud);
+        const uint32_t c1 = cdf_at<KV>(s + 1, mu, inv, s_phi, bud);
+        acc_i += 31.0 - log2(static_cast<double>(c1 - c0));
+        const double lo = edge<KV>(s), hi = edge<KV>(s + 1);
+        const double m = mu, sd = sg;
+        double q = wn * gauss_mass((lo - m) / sd, (hi - m) / sd) +
+                   ww * gauss_mass((lo - m) / (3.0 * sd), (hi - m) / (3.0 * sd));
+        if (a.te) q += we * static_cast<double>(a.prefix[s + 1] - a.prefix[s]) / a.te;
+        const double b = -log2(q);
+        acc_f += (b < 64.0) ? b : 64.0;
+    }
+    acc_i = wave_sum_f64(acc_i);
+    acc_f = wave_sum_f64(acc_f);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { s_red[0][wave] = acc_i; s_red[1][wave] = acc_f; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double si = 0.0, sf = 0.0;
+        for (int w = 0; w < 4; ++w) { si += s_red[0][w]; sf += s_red[1][w]; }
+        atomicAdd(&a.ctl->bits[0], si);
+        atomicAdd(&a.ctl->bits[1], sf);
+    }
+}
+
+hipError_t launch_estimate(const EstimateArgs& a, int kv_dtype, int mu_dtype, hipStream_t s) {
+    const dim3 grid(2048), block(256);
+    if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_estimate<kBF16, kBF16>), grid, block, 0, s, a);
+    else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_estimate<kBF16, kF32>), grid, block, 0, s, a);
+    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_estimate<kE4M3, kBF16>), grid, block, 0, s, a);
+    else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_estimate<kE4M3, kF32>), grid, block, 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// the CDF table for given (mu, sigma) pairs
+// ---------------------------------------------------------------------------
+template <int KV, int MU>
+__global__ void __launch_bounds__(256) k_cdf_table(const void* mu_, const float* __restrict__ sigma, int64_t pairs,
+                                                   uint32_t tn, uint32_t tw, const uint32_t* __restrict__ prefix,
+                                                   uint32_t* __restrict__ out, const uint32_t* __restrict__ phi) {
+    __shared__ uint32_t s_phi[kPhiEntries];
+    load_phi_lds(s_phi, phi);
+    using MT = typename MuT<MU>::T;
+    constexpr uint32_t N1 = Alphabet<KV>::kSize + 1;
+    const Budgets bud{tn, tw, prefix};
+    const int64_t total = pairs * N1;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t p = i / N1;
+        const uint32_t b = static_cast<uint32_t>(i - p * N1);
+        const float mu = mu_value<MU>(static_cast<const MT*>(mu_)[p]);
+        const float inv = __frcp_rn(sigma[p]);
+        out[i] = cdf_at<KV>(b, mu, inv, s_phi, bud);
+    }
+}
+
+hipError_t launch_cdf_table(int kv_dtype, int mu_dtype, uint32_t tn, uint32_t tw, const void* mu,
+                            const float* sigma, int64_t pairs, const uint32_t* prefix, uint32_t* out,
+                            const uint32_t* phi, hipStream_t s) {
+    const dim3 grid(1024), block(256);
+    if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_cdf_table<kBF16, kBF16>), grid, block, 0, s, mu, sigma, pairs, tn, tw, prefix, out, phi);
+    else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_cdf_table<kBF16, kF32>), grid, block, 0, s, mu, sigma, pairs, tn, tw, prefix, out, phi);
+    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_cdf_table<kE4M3, kBF16>), grid, block, 0, s, mu, sigma, pairs, tn, tw, prefix, out, phi);
+    else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_cdf_table<kE4M3, kF32>), grid, block, 0, s, mu, sigma, pairs, tn, tw, prefix, out, phi);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,272 @@
+"""ctypes binding over libkvc.so (C ABI in include/kvc.h).
+
+Argument marshalling only: every step of the coder runs in the library's
+HIP kernels.  torch supplies device memory and the current HIP stream.
+Importing this module loads the library and raises ImportError if it has not
+been built (``python -m entropy_coding_amd.build``); there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc.so")
+
+KVC_OK, KVC_ERR_INVALID, KVC_ERR_CAPACITY, KVC_ERR_CORRUPT, KVC_ERR_MISMATCH, KVC_ERR_DEVICE = 0, -1, -2, -3, -4, -5
+KVC_BF16, KVC_E4M3, KVC_F32 = 0, 1, 2
+HEADER_BYTES = 128
+DECODE_WORKSPACE_BYTES = 256
+ESTIMATE_WORKSPACE_BYTES = 256
+ENCODE_STAGES = 4     # side-information checksum, coding kernel, size scan, compaction
+DECODE_STAGES = 2     # side-information checksum, decoding kernel
+
+EXPORTS = [
+    "kvc_version", "kvc_status_string", "kvc_phi_table", "kvc_encode_sizes", "kvc_encode",
+    "kvc_stream_info", "kvc_decode", "kvc_calibrate_sigma", "kvc_build_marginal",
+    "kvc_estimate_bits", "kvc_cdf_table",
+]
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m entropy_coding_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class kvc_params(ctypes.Structure):
+    _fields_ = [
+        ("kv_dtype", ctypes.c_int32), ("mu_dtype", ctypes.c_int32),
+        ("w_narrow_bp", ctypes.c_uint32), ("w_wide_bp", ctypes.c_uint32),
+        ("chunk_tokens", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+        ("planes", ctypes.c_int64), ("tokens", ctypes.c_int64), ("channels", ctypes.c_int64),
+    ]
+
+
+_P = ctypes.c_void_p
+_U64 = ctypes.c_uint64
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_U32 = ctypes.c_uint32
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_lib_version = _sig("kvc_version", ctypes.c_int, [])
+_lib_status_string = _sig("kvc_status_string", ctypes.c_char_p, [ctypes.c_int])
+_lib_phi_table = _sig("kvc_phi_table", ctypes.c_int, [_P])
+_lib_encode_sizes = _sig("kvc_encode_sizes", ctypes.c_int, [ctypes.POINTER(kvc_params), ctypes.POINTER(_U64), ctypes.POINTER(_U64)])
+_lib_encode = _sig("kvc_encode", ctypes.c_int, [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _U64, ctypes.POINTER(_U64), _P, _U64, _P, _P])
+_lib_stream_info = _sig("kvc_stream_info", ctypes.c_int, [_P, _U64, ctypes.POINTER(kvc_params), ctypes.POINTER(_U64)])
+_lib_decode = _sig("kvc_decode", ctypes.c_int, [_P, _U64, _P, _P, _P, _P, _P, _U64, _P, _P])
+_lib_calibrate = _sig("kvc_calibrate_sigma", ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P])
+_lib_marginal = _sig("kvc_build_marginal", ctypes.c_int, [_P, _I32, _U64, _U32, _U32, _P, _P])
+_lib_estimate = _sig("kvc_estimate_bits", ctypes.c_int, [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _P, _U64, _P])
+_lib_cdf_table = _sig("kvc_cdf_table", ctypes.c_int, [_I32, _I32, _U32, _U32, _P, _P, _I64, _P, _P, _P])
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {kvc_status_string(status)} ({status})")
+
+
+def _check(st: int, where: str):
+    if st != KVC_OK:
+        raise KvcError(st, where)
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _kv_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16 or t.dtype == torch.int16:
+        return KVC_BF16
+    if t.dtype == torch.float8_e4m3fn or t.dtype == torch.uint8:
+        return KVC_E4M3
+    raise TypeError(f"KV must be bf16 (or int16 patterns) or e4m3 (or uint8 patterns), got {t.dtype}")
+
+
+def _mu_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16 or t.dtype == torch.int16:
+        return KVC_BF16
+    if t.dtype == torch.float32:
+        return KVC_F32
+    raise TypeError(f"mu must be bf16 or float32, got {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def kvc_version() -> int:
+    return _lib_version()
+
+
+def kvc_status_string(status: int) -> str:
+    return _lib_status_string(status).decode()
+
+
+def kvc_phi_table() -> np.ndarray:
+    out = np.zeros(4098, dtype=np.uint32)
+    _check(_lib_phi_table(out.ctypes.data), "kvc_phi_table")
+    return out
+
+
+def make_params(kv_dtype, mu_dtype, planes, tokens, channels, weights=(9500, 300), chunk_tokens=0) -> kvc_params:
+    return kvc_params(kv_dtype, mu_dtype, weights[0], weights[1], chunk_tokens, 0, planes, tokens, channels)
+
+
+def kvc_encode_sizes(p: kvc_params):
+    a, b = _U64(), _U64()
+    _check(_lib_encode_sizes(ctypes.byref(p), ctypes.byref(a), ctypes.byref(b)), "kvc_encode_sizes")
+    return a.value, b.value
+
+
+class Encoder:
+    """Holds the output and workspace buffers of one shape so that repeated
+    calls allocate nothing."""
+
+    def __init__(self, p: kvc_params, device="cuda", out_capacity: int | None = None):
+        self.p = p
+        max_stream, ws = kvc_encode_sizes(p)
+        self.capacity = max_stream if out_capacity is None else out_capacity
+        self.out = torch.empty(self.capacity, dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+
+    def __call__(self, kv, mu, sigma, prefix=None, stream=None, stage_ms: list | None = None) -> torch.Tensor:
+        n = _U64(0)
+        ms = (ctypes.c_float * ENCODE_STAGES)() if stage_ms is not None else None
+        st = _lib_encode(ctypes.byref(self.p), _ptr(kv), _ptr(mu), _ptr(sigma), _ptr(prefix),
+                         _ptr(self.out), self.capacity, ctypes.byref(n), _ptr(self.workspace),
+                         self.workspace.numel(), _stream(stream), ms)
+        _check(st, "kvc_encode")
+        if ms is not None:
+            stage_ms[:] = list(ms)
+        return self.out[: n.value]
+
+
+def kvc_encode(kv: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, prefix: torch.Tensor | None = None,
+               weights=(9500, 300), chunk_tokens: int = 0, stream=None) -> torch.Tensor:
+    """Encode KV [G, T, D] under the mixture around mu with sigma [G, D];
+    returns the stream as a uint8 device tensor."""
+    for t, nm in ((kv, "kv"), (mu, "mu"), (sigma, "sigma")):
+        _need(t, nm)
+    if prefix is not None:
+        _need(prefix, "prefix")
+    g, t, d = kv.shape
+    if tuple(mu.shape) != (g, t, d) or tuple(sigma.shape) != (g, d) or sigma.dtype != torch.float32:
+        raise ValueError("shapes: kv and mu [G, T, D], sigma [G, D] float32")
+    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens)
+    return Encoder(p, kv.device)(kv, mu, sigma, prefix, stream).clone()
+
+
+def kvc_stream_info(header: bytes | np.ndarray):
+    h = np.frombuffer(bytes(header[:HEADER_BYTES]), dtype=np.uint8).copy()
+    p = kvc_params()
+    total = _U64()
+    _check(_lib_stream_info(h.ctypes.data, h.size, ctypes.byref(p), ctypes.byref(total)), "kvc_stream_info")
+    return p, total.value
+
+
+def kvc_decode(stream_bytes: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor,
+               prefix: torch.Tensor | None = None, kv_out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode a KVC-1 stream (uint8 device tensor) back to KV bit patterns
+    (int16 for bf16, uint8 for e4m3), shape [G, T, D]."""
+    _need(stream_bytes, "stream")
+    for t, nm in ((mu, "mu"), (sigma, "sigma")):
+        _need(t, nm)
+    if stream_bytes.numel() < HEADER_BYTES:
+        raise KvcError(KVC_ERR_CORRUPT, "kvc_decode")
+    p, _ = kvc_stream_info(stream_bytes[:HEADER_BYTES].cpu().numpy().tobytes())
+    shape = (p.planes, p.tokens, p.channels)
+    if kv_out is None:
+        kv_out = torch.empty(shape, dtype=torch.int16 if p.kv_dtype == KVC_BF16 else torch.uint8,
+                             device=stream_bytes.device)
+    if workspace is None:
+        workspace = torch.empty(DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=stream_bytes.device)
+    st = _lib_decode(_ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _ptr(sigma), _ptr(prefix),
+                     _ptr(kv_out), _ptr(workspace), workspace.numel(), _stream(stream), None)
+    _check(st, "kvc_decode")
+    return kv_out
+
+
+def kvc_decode_into(stream_bytes, mu, sigma, prefix, kv_out, workspace, stream=None,
+                    stage_ms: list | None = None) -> int:
+    """Decode without reading the header on the Python side; returns the
+    status instead of raising (for timing loops and error-path tests)."""
+    ms = (ctypes.c_float * DECODE_STAGES)() if stage_ms is not None else None
+    st = _lib_decode(_ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _ptr(sigma), _ptr(prefix),
+                     _ptr(kv_out), _ptr(workspace), workspace.numel(), _stream(stream), ms)
+    if ms is not None:
+        stage_ms[:] = list(ms)
+    return st
+
+
+def kvc_calibrate_sigma(kv: torch.Tensor, mu: torch.Tensor, sigma_floor: float = 2.0 ** -30,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kv, mu: [reps, planes, tokens, channels] -> sigma [planes, channels]."""
+    _need(kv, "kv")
+    _need(mu, "mu")
+    r, g, t, d = kv.shape
+    if out is None:
+        out = torch.empty((g, d), dtype=torch.float32, device=kv.device)
+    st = _lib_calibrate(_ptr(kv), _ptr(mu), _kv_dtype(kv), _mu_dtype(mu), r, g, t, d, sigma_floor,
+                        _ptr(out), _stream(stream))
+    _check(st, "kvc_calibrate_sigma")
+    return out
+
+
+def kvc_build_marginal(samples: torch.Tensor, weights=(9500, 300), stream=None) -> torch.Tensor:
+    """Prefix table of the +1-smoothed marginal; returned as int32 (all
+    values are below 2^31) with N + 1 entries."""
+    _need(samples, "samples")
+    dt = _kv_dtype(samples)
+    n_sym = 65536 if dt == KVC_BF16 else 256
+    out = torch.empty(n_sym + 1, dtype=torch.int32, device=samples.device)
+    st = _lib_marginal(_ptr(samples), dt, samples.numel(), weights[0], weights[1], _ptr(out), _stream(stream))
+    _check(st, "kvc_build_marginal")
+    return out
+
+
+def kvc_estimate_bits(kv, mu, sigma, prefix=None, weights=(9500, 300), stream=None):
+    """(integer-model bits/scalar, float-model bits/scalar)."""
+    g, t, d = kv.shape
+    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, 0)
+    ws = torch.empty(ESTIMATE_WORKSPACE_BYTES, dtype=torch.uint8, device=kv.device)
+    out = (ctypes.c_double * 2)()
+    st = _lib_estimate(ctypes.byref(p), _ptr(kv), _ptr(mu), _ptr(sigma), _ptr(prefix), ctypes.addressof(out),
+                       _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "kvc_estimate_bits")
+    return out[0], out[1]
+
+
+def kvc_cdf_table(kv_dtype: int, mu: torch.Tensor, sigma: torch.Tensor, prefix=None, weights=(9500, 300),
+                  stream=None) -> torch.Tensor:
+    """C(b) for b = 0..N for each (mu, sigma) pair; int32 storage of uint32
+    values (reinterpret as uint32 on the host)."""
+    _need(mu, "mu")
+    _need(sigma, "sigma")
+    n_sym = 65536 if kv_dtype == KVC_BF16 else 256
+    pairs = mu.numel()
+    out = torch.empty((pairs, n_sym + 1), dtype=torch.int32, device=mu.device)
+    st = _lib_cdf_table(kv_dtype, _mu_dtype(mu), weights[0], weights[1], _ptr(mu), _ptr(sigma), pairs,
+                        _ptr(prefix), _ptr(out), _stream(stream))
+    _check(st, "kvc_cdf_table")
+    return out

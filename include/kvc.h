@@ -1,0 +1,192 @@
+/*
+ * kvc.h -- C ABI of libkvc, a lossless KV-cache entropy coder for MI355X (gfx950).
+ *
+ * The method ("speculative KV coding"): both ends of a KV transfer rebuild a
+ * predictor mean mu and a frozen, calibrated per-(kv, head, channel) sigma;
+ * every KV scalar is arithmetic-coded under the mixture
+ *     q = 0.95 N(mu, sigma^2) + 0.03 N(mu, (3 sigma)^2) + 0.02 p_hat,
+ * p_hat being the empirical marginal over the BF16 (or e4m3) alphabet, and
+ * the decoder rebuilds KV exactly from the bits and (mu, sigma).
+ * Sources: wiki page "Speculative KV Coding" (aisparkup.com), sections
+ * "pipeline", "predictor choice" and "mixture distribution"; blog post
+ * "推测性KV编码：用预测模型实现缓存无损压缩4倍" (blog.hotdry.top), sections
+ * "engineering choice of predictor" and "application scenarios and
+ * deployment parameters".
+ *
+ * The byte stream is format KVC-1: integer mixture CDF with total 2^31 and
+ * every frequency >= 1, 64-bit-state rANS with 16-bit words, 64 interleaved
+ * lanes (one per channel) per chunk of up to chunk_tokens tokens, a chunk
+ * directory for random access, and a checksum of the side information.
+ *
+ * Conventions for every call:
+ *   - Pointers named d_* are DEVICE pointers owned by the caller; pointers
+ *     named h_* are HOST pointers.  The library never allocates memory and
+ *     never frees caller memory; scratch comes from a caller workspace.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is queued on it; calls that return a host value synchronise
+ *     that stream once before returning.
+ *   - Layouts are row-major: KV and mu are [planes][tokens][channels] with
+ *     channels fastest; sigma is [planes][channels] float32; the marginal
+ *     prefix is uint32[N + 1] (N = 65536 for bf16, 256 for e4m3).
+ *   - Every call returns a kvc_status; no exception crosses the ABI.  On an
+ *     error, outputs are undefined (but never written out of bounds).
+ *   - Concurrent calls on different streams are safe; the only state the
+ *     library keeps is a read-only per-device table, set up on first use.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvc_status {
+    KVC_OK = 0,
+    KVC_ERR_INVALID = -1,   /* bad argument, shape, dtype, weights or sigma   */
+    KVC_ERR_CAPACITY = -2,  /* output buffer or workspace too small           */
+    KVC_ERR_CORRUPT = -3,   /* stream malformed or damaged                    */
+    KVC_ERR_MISMATCH = -4,  /* sigma / prefix differ from the encoder's       */
+    KVC_ERR_DEVICE = -5     /* a HIP call failed                              */
+} kvc_status;
+
+enum { KVC_BF16 = 0, KVC_E4M3 = 1, KVC_F32 = 2 };   /* E4M3 = OCP float8 e4m3fn */
+
+#define KVC_HEADER_BYTES 128
+#define KVC_DECODE_WORKSPACE_BYTES 256
+#define KVC_ESTIMATE_WORKSPACE_BYTES 256
+#define KVC_ENCODE_STAGES 4
+#define KVC_DECODE_STAGES 2
+
+typedef struct kvc_params {
+    int32_t kv_dtype;        /* KVC_BF16 or KVC_E4M3                               */
+    int32_t mu_dtype;        /* KVC_BF16 or KVC_F32                                */
+    uint32_t w_narrow_bp;    /* weight of N(mu, sigma^2), basis points: 9500        */
+    uint32_t w_wide_bp;      /* weight of N(mu, (3 sigma)^2), basis points: 300     */
+                             /* the escape part p_hat gets 10000 - both; (10000, 0)
+                                is a single Gaussian and needs no prefix table     */
+    uint32_t chunk_tokens;   /* tokens per chunk; 0 = min(tokens, 1024)            */
+    uint32_t reserved;       /* must be 0                                          */
+    int64_t planes;          /* G = layers * 2 * batch * kv_heads                  */
+    int64_t tokens;          /* T                                                  */
+    int64_t channels;        /* D, a positive multiple of 64                       */
+} kvc_params;
+
+/* Library version (KVC-1 stream format = 1). */
+int kvc_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* kvc_status_string(int status);
+
+/*
+ * Integer standard-normal CDF table of the format, computed on the host:
+ * h_out[k] = round(2^31 * Phi(-8 + k/256)) for k = 0..4096, h_out[4097] =
+ * h_out[4096].  Needs no GPU.  Returns KVC_ERR_INVALID for a NULL pointer.
+ */
+int kvc_phi_table(uint32_t* h_out /* [4098] */);
+
+/*
+ * Sizes for kvc_encode: the largest stream the call can produce (every
+ * scalar at two 16-bit words, the worst case of the coder) and the workspace
+ * it needs.  Host only; returns KVC_ERR_INVALID for bad parameters.
+ */
+int kvc_encode_sizes(const kvc_params* p, uint64_t* h_max_stream_bytes,
+                     uint64_t* h_workspace_bytes);
+
+/*
+ * Encoder ([wiki] "pipeline": KV_full and (mu, sigma) go into the arithmetic
+ * coder, which emits the bits).  Codes d_kv (bf16 or e4m3 bit patterns) under
+ * the mixture around d_mu with d_sigma and the marginal prefix d_prefix
+ * (NULL allowed when w_narrow_bp + w_wide_bp == 10000).  Writes the stream
+ * to d_out and its length to *h_out_bytes.  sigma must be finite and
+ * positive with a finite reciprocal, else KVC_ERR_INVALID.  If the stream
+ * does not fit out_capacity the call returns KVC_ERR_CAPACITY and sets
+ * *h_out_bytes to the size it needed.  Synchronises `stream` once.
+ * h_stage_ms: NULL, or KVC_ENCODE_STAGES floats that receive the GPU time in
+ * milliseconds of each stage (side-information checksum, coding kernel,
+ * size scan, compaction), measured with HIP events on `stream`.
+ */
+int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu,
+               const float* d_sigma, const uint32_t* d_prefix, void* d_out,
+               uint64_t out_capacity, uint64_t* h_out_bytes, void* d_workspace,
+               uint64_t workspace_bytes, void* stream, float* h_stage_ms);
+
+/*
+ * Parse the 128-byte stream header held in HOST memory into *h_params and
+ * the total stream length *h_stream_bytes.  Host only; KVC_ERR_CORRUPT if
+ * the header is not a valid KVC-1 header.
+ */
+int kvc_stream_info(const void* h_header, uint64_t header_bytes, kvc_params* h_params,
+                    uint64_t* h_stream_bytes);
+
+/*
+ * Decoder ([wiki] "pipeline": the bitstream plus (mu, sigma) give back
+ * KV_full exactly).  d_in holds in_bytes of a KVC-1 stream; shape and
+ * parameters come from its header.  d_mu, d_sigma, d_prefix must be the
+ * encoder's (checked through the stream's checksum: KVC_ERR_MISMATCH).
+ * Writes KV bit patterns to d_kv_out ([planes][tokens][channels]).  Returns
+ * KVC_ERR_CORRUPT if the stream is malformed, truncated or damaged (every
+ * lane must end in the initial state and consume exactly its chunk).
+ * Workspace: KVC_DECODE_WORKSPACE_BYTES.  Synchronises `stream` twice
+ * (header read, status read).  h_stage_ms: NULL, or KVC_DECODE_STAGES
+ * floats (side-information checksum, decoding kernel), as for kvc_encode.
+ */
+int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu,
+               const float* d_sigma, const uint32_t* d_prefix, void* d_kv_out,
+               void* d_workspace, uint64_t workspace_bytes, void* stream,
+               float* h_stage_ms);
+
+/*
+ * Sigma calibration ([wiki] "predictor choice": per-(kv, head, channel)
+ * variance calibrated on data, then frozen; [blog] "deployment parameters":
+ * 128 sequences of 1024 tokens).  d_kv and d_mu are [reps][planes][tokens]
+ * [channels]; writes d_sigma_out[planes][channels] = max(sigma_floor,
+ * sqrt(mean over reps and tokens of (kv - mu)^2)), accumulated in float64
+ * in a fixed order (deterministic).  Returns KVC_ERR_INVALID for bad shapes
+ * or a non-positive floor.  Does not synchronise.
+ */
+int kvc_calibrate_sigma(const void* d_kv, const void* d_mu, int32_t kv_dtype,
+                        int32_t mu_dtype, int64_t reps, int64_t planes, int64_t tokens,
+                        int64_t channels, float sigma_floor, float* d_sigma_out,
+                        void* stream);
+
+/*
+ * Empirical marginal ([wiki] "mixture distribution": an empirical BF16
+ * distribution catches extreme outliers).  d_samples holds n bit patterns
+ * (bf16 or e4m3); writes the integer prefix d_prefix_out[b] =
+ * floor(T_e * cum[b] / cum[N]) of the +1-smoothed histogram in value order,
+ * with T_e the escape budget of the weights.  n < 2^32 - 2^16.  Does not
+ * synchronise.
+ */
+int kvc_build_marginal(const void* d_samples, int32_t dtype, uint64_t n,
+                       uint32_t w_narrow_bp, uint32_t w_wide_bp,
+                       uint32_t* d_prefix_out, void* stream);
+
+/*
+ * Bits per scalar ([wiki] "core idea": the rate is the cross-entropy of the
+ * model).  h_bits_out[0] = mean of -log2(f/2^31) under the integer model the
+ * coder uses; h_bits_out[1] = mean -log2 q under the continuous mixture over
+ * the same cells (float64, per-scalar cost capped at 64 bits).  Workspace:
+ * KVC_ESTIMATE_WORKSPACE_BYTES.  Synchronises `stream` once.
+ */
+int kvc_estimate_bits(const kvc_params* p, const void* d_kv, const void* d_mu,
+                      const float* d_sigma, const uint32_t* d_prefix, double* h_bits_out,
+                      void* d_workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * The shared CDF itself ([blog] "deployment parameters": encoder and decoder
+ * must agree on it bit for bit).  For each of `pairs` (mu, sigma) pairs,
+ * writes C(b) for b = 0..N to d_out[pair][N + 1].  d_mu holds `pairs`
+ * values of mu_dtype, d_sigma `pairs` floats.  Synchronises `stream` once
+ * (to report an invalid sigma).
+ */
+int kvc_cdf_table(int32_t kv_dtype, int32_t mu_dtype, uint32_t w_narrow_bp,
+                  uint32_t w_wide_bp, const void* d_mu, const float* d_sigma, int64_t pairs,
+                  const uint32_t* d_prefix, uint32_t* d_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -327,15 +327,22 @@ def calibrate_sigma(kv, mu, kv_dtype: int, mu_dtype: int, sigma_floor: float) ->
     miss, of [blog] § information theory view, and the pages calibrate it per
     (kv, head, channel) on held-out data, then freeze it ([wiki] § predictor
     choice; [blog] § engineering choice of predictor).  Accumulated in float64,
-    rounded once to float32.
+    rounded once to float32.  Residuals that are not finite (a NaN or Inf in
+    the calibration data) are left out of the mean; a channel with none left
+    gets the floor.
     """
     k = _values_f64(kv, kv_dtype)
     m = _values_f64(mu, mu_dtype)
     m = np.where(np.isfinite(m), m, 0.0)
-    r = k - m
-    ms = np.mean(r * r, axis=(0, 2))
-    s = np.sqrt(ms).astype(np.float32)
-    return np.maximum(s, np.float32(sigma_floor)).astype(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        r2 = (k - m) ** 2
+    ok = np.isfinite(r2)                  # non-finite residuals are skipped
+    used = ok.sum(axis=(0, 2))
+    total = np.where(ok, r2, 0.0).sum(axis=(0, 2))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        s = np.sqrt(total / used).astype(np.float32)
+    fl = np.float32(sigma_floor)
+    return np.where((used > 0) & np.isfinite(s) & (s > fl), s, fl).astype(np.float32)
 
 
 # ---------------------------------------------------------------------------
@@ -653,7 +660,20 @@ def encode_chunks(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide
     return out
 
 
-__all__ += ["chunk_payload", "encode_chunks"]
+def wrap_chunk(payload: bytes, sigma_sub, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
+               chunk_tokens, tokens) -> bytes:
+    """A one-chunk stream around one chunk's payload (64 channels, `tokens`
+    tokens of one plane, its 64 sigmas), so that :func:`decode` can check a
+    chunk cut out of a large stream on its own."""
+    t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)[2]
+    shash = side_hash(np.asarray(sigma_sub, dtype=np.float32).reshape(1, LANES), prefix if t_e else None)
+    head = _header(kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp, chunk_tokens, 1, tokens, LANES, 1,
+                   len(payload), shash)
+    directory = np.array([0, len(payload)], dtype="<u8")
+    return head + directory.tobytes() + payload
+
+
+__all__ += ["chunk_payload", "encode_chunks", "wrap_chunk"]
 
 
 # ---------------------------------------------------------------------------

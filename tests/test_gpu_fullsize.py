@@ -1,0 +1,147 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times.  The GPU round trip is checked on every scalar; the oracle
+codes and decodes a sample of chunks cut from the GPU's stream (each chunk
+depends only on its own slice of KV and mu, its 64 sigmas and p_hat), and
+the smaller workload is checked byte for byte in full."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from entropy_coding_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_inputs(kvc, w, dev, layers=None, reps=None):
+    layers = list(range(w.layers)) if layers is None else layers
+    ppl = w.planes_per_layer
+    G = len(layers) * ppl
+    kv_dt = torch.bfloat16 if w.kv_dtype == W.BF16 else torch.uint8
+    mu_dt = torch.bfloat16 if w.mu_dtype == W.BF16 else torch.float32
+    kv = torch.empty((G, w.tokens, w.channels), dtype=kv_dt, device=dev)
+    mu = torch.empty((G, w.tokens, w.channels), dtype=mu_dt, device=dev)
+    sig = torch.empty((G, w.channels), dtype=torch.float32, device=dev)
+    reps = w.calib_reps if reps is None else reps
+    for i, l in enumerate(layers):
+        k, m = W.layer_data(w, l, device=dev)
+        kv[i * ppl:(i + 1) * ppl] = k
+        mu[i * ppl:(i + 1) * ppl] = m
+        if reps:
+            ck, cm = W.layer_calibration(w, l, reps=reps, device=dev)
+            sig[i * ppl:(i + 1) * ppl] = W.expand_sigma(w, kvc.kvc_calibrate_sigma(ck, cm))
+        else:
+            sig[i * ppl:(i + 1) * ppl] = W.layer_sigma_true(w, l, device=dev)
+    samples = W.marginal_samples(w, device=dev)
+    prefix = kvc.kvc_build_marginal(samples, (w.w_narrow_bp, w.w_wide_bp))
+    return kv, mu, sig, prefix
+
+
+def sampled_chunk_parity(kvc, w, kv, mu, sig, prefix, stream, n_sample=6, seed=0):
+    g_n, t_n, d_n = kv.shape
+    tc = w.chunk_tokens
+    gof, tcof, kof, lnof = O.chunk_layout(g_n, t_n, d_n, tc)
+    n_chunks = gof.size
+    rng = np.random.default_rng(seed)
+    ids = sorted(set([0, n_chunks - 1] + rng.integers(0, n_chunks, n_sample - 2).tolist()))
+    pref = prefix.cpu().numpy().astype(np.int64)
+    head = stream[:128 + 8 * (n_chunks + 1)].cpu().numpy()
+    directory = head[128:].view("<u8")
+    pay_off = 128 + 8 * (n_chunks + 1)
+    w_ = (w.w_narrow_bp, w.w_wide_bp)
+    for cid in ids:
+        g, tci, k, ln = int(gof[cid]), int(tcof[cid]), int(kof[cid]), int(lnof[cid])
+        t0 = tci * tc
+        sl = (slice(g, g + 1), slice(t0, t0 + ln), slice(64 * k, 64 * k + 64))
+        kvs = W.to_numpy_bits(kv[sl].contiguous())
+        mus = W.to_numpy_bits(mu[sl].contiguous())
+        sgs = sig[g:g + 1, 64 * k:64 * k + 64].cpu().numpy()
+        gpu_payload = stream[pay_off + int(directory[cid]):pay_off + int(directory[cid + 1])].cpu().numpy().tobytes()
+        want = O.encode_chunks(kvs, mus, sgs, pref, w.kv_dtype, w.mu_dtype, *w_, tc, [0])[0]
+        assert gpu_payload == want, f"chunk {cid} (plane {g}, tokens {t0}+{ln}, group {k}) differs"
+        back = O.decode(O.wrap_chunk(gpu_payload, sgs, pref, w.kv_dtype, w.mu_dtype, *w_, tc, ln), mus, sgs, pref)
+        assert np.array_equal(back, kvs)
+    say(f"sampled chunks {ids} of {n_chunks} identical to the oracle")
+
+
+@pytest.mark.parametrize("wid,layers", [(2, None), (3, None), (4, [0, 63])])
+def test_full_size_round_trip_and_sampled_parity(kvc, cuda, wid, layers):
+    w = W.WORKLOADS[wid]
+    say(f"workload {wid}: {w.name}, layers {layers or 'all'}")
+    kv, mu, sig, prefix = build_inputs(kvc, w, cuda, layers, reps=16)
+    torch.cuda.synchronize()
+    g, t, d = kv.shape
+    p = kvc.make_params(kvc._kv_dtype(kv), kvc._mu_dtype(mu), g, t, d, (w.w_narrow_bp, w.w_wide_bp), w.chunk_tokens)
+    enc = kvc.Encoder(p, cuda)
+    st = enc(kv, mu, sig, prefix)
+    say(f"encoded {kv.numel()} scalars -> {st.numel()} bytes ({8.0 * st.numel() / kv.numel():.4f} bits/scalar)")
+    out = kvc.kvc_decode(st, mu, sig, prefix)
+    assert torch.equal(out.view(kv.dtype) if kv.dtype != torch.uint8 else out, kv)
+    sampled_chunk_parity(kvc, w, kv, mu, sig, prefix, st)
+    # the encoder is deterministic: a second call gives the same bytes
+    st2 = enc(kv, mu, sig, prefix)
+    assert torch.equal(st2, st)
+
+
+def test_qwen3_0p6b_shaped_full_parity(kvc, cuda):
+    """The 58.7M-scalar workload byte for byte against the oracle, sigma
+    calibrated on the device from 8 x 1024 held-out tokens per layer."""
+    w = W.WORKLOADS[1]
+    kv, mu, sig, prefix = build_inputs(kvc, w, cuda)
+    st = kvc.kvc_encode(kv, mu, sig, prefix, (w.w_narrow_bp, w.w_wide_bp), w.chunk_tokens)
+    kvn, mun, sgn = W.to_numpy_bits(kv), W.to_numpy_bits(mu), sig.cpu().numpy()
+    pref = prefix.cpu().numpy().astype(np.int64)
+    say("oracle encoding 58.7M scalars ...")
+    want = O.encode(kvn, mun, sgn, pref, O.BF16, O.BF16, w.w_narrow_bp, w.w_wide_bp, w.chunk_tokens)
+    assert st.cpu().numpy().tobytes() == want
+    out = kvc.kvc_decode(st, mu, sig, prefix)
+    assert torch.equal(out, kv.view(torch.int16))
+
+
+@pytest.mark.parametrize("case", ["perfect_predictor", "all_nan", "constant", "noise_predictor", "huge_sigma"])
+def test_degenerate_inputs(kvc, cuda, case):
+    w = W.WORKLOADS[0]
+    kv, mu = W.layer_data(w, 0, tokens=130)
+    sig = W.layer_sigma_true(w, 0)
+    if case == "perfect_predictor":
+        mu = kv.clone()
+        sig = torch.full_like(sig, 2.0 ** -30)
+    elif case == "all_nan":
+        kv = torch.full_like(kv, float("nan"))
+    elif case == "constant":
+        kv = torch.full_like(kv, 1.0)
+        mu = torch.full_like(mu, 1.0)
+    elif case == "noise_predictor":
+        mu = W.noise_predictor(w, tuple(kv.shape))
+        sig = torch.full_like(sig, 2.0 ** -30)
+    elif case == "huge_sigma":
+        sig = torch.full_like(sig, 1e30)
+    samples = W.marginal_samples(w)
+    wts = (9500, 300)
+    pref = O.build_marginal(W.to_numpy_bits(samples), O.BF16, *wts)
+    kvn, mun, sgn = W.to_numpy_bits(kv), W.to_numpy_bits(mu), sig.numpy()
+    want = O.encode(kvn, mun, sgn, pref, O.BF16, O.BF16, *wts, 64)
+    pref_d = torch.from_numpy(pref.astype(np.int32)).to(cuda)
+    kv_d, mu_d, sig_d = kv.to(cuda), mu.to(cuda), sig.to(cuda)
+    st = kvc.kvc_encode(kv_d, mu_d, sig_d, pref_d, wts, 64)
+    assert st.cpu().numpy().tobytes() == want
+    out = kvc.kvc_decode(st, mu_d, sig_d, pref_d)
+    assert torch.equal(out, kv_d.view(torch.int16))
+    say(f"{case}: {8.0 * len(want) / kv.numel():.4f} bits/scalar")
+
+
+def test_empty_and_oversized_shapes_are_rejected(kvc, cuda):
+    for shape in [(0, 5, 64), (2, 0, 64), (2, 5, 0), (2, 5, 32)]:
+        p = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, *shape)
+        with pytest.raises(kvc.KvcError) as e:
+            kvc.kvc_encode_sizes(p)
+        assert e.value.status == kvc.KVC_ERR_INVALID
+    p = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, 1 << 27, 1, 64)   # sigma words beyond 2^32
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_encode_sizes(p)

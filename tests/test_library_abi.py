@@ -1,0 +1,84 @@
+"""The C ABI library without a GPU: it loads, exports every call declared
+in include/kvc.h, and its host-side logic (Phi table, sizes, header
+parsing, argument validation) behaves."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from entropy_coding_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_calls():
+    with open(os.path.join(ROOT, "include", "kvc.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(kvc_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_call_is_exported(kvc):
+    names = declared_calls()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(kvc.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(kvc.EXPORTS) == names
+
+
+def test_version_and_status_strings(kvc):
+    assert kvc.kvc_version() == 1
+    assert kvc.kvc_status_string(0) == "ok"
+    assert "corrupt" in kvc.kvc_status_string(-3)
+
+
+def test_host_phi_table_equals_oracle(kvc):
+    # libm erfc in double on the library side, mpmath at 50 digits in the oracle
+    assert np.array_equal(kvc.kvc_phi_table().astype(np.int64), O.phi_table())
+
+
+def test_encode_sizes(kvc):
+    w = W.WORKLOADS[2]
+    p = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, w.planes, w.tokens, w.channels, (9500, 300), 1024)
+    max_stream, ws = kvc.kvc_encode_sizes(p)
+    n_chunks = w.planes * 4 * 2
+    assert max_stream == 128 + 8 * (n_chunks + 1) + n_chunks * (512 + 2 * 2 * 64 * 1024)
+    assert ws >= n_chunks * (512 + 4 + 8 + 4 * 64 * 1024)
+    for bad in [dict(channels=96), dict(planes=0), dict(tokens=0), dict(reserved=1), dict(kv_dtype=2),
+                dict(mu_dtype=1), dict(w_narrow_bp=9000, w_wide_bp=1001), dict(chunk_tokens=1 << 21)]:
+        q = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, 4, 100, 128)
+        for k, v in bad.items():
+            setattr(q, k, v)
+        with pytest.raises(kvc.KvcError) as e:
+            kvc.kvc_encode_sizes(q)
+        assert e.value.status == kvc.KVC_ERR_INVALID
+
+
+def oracle_stream(kv_dtype=O.BF16, w=(9500, 300), tc=16):
+    kv, mu, sig, samples = W.tiny_case(7, kv_dtype=kv_dtype)
+    mu_dtype = O.BF16 if kv_dtype == O.BF16 else O.F32
+    pref = O.build_marginal(W.to_numpy_bits(samples), kv_dtype, *w)
+    return O.encode(W.to_numpy_bits(kv), W.to_numpy_bits(mu), sig.numpy(), pref, kv_dtype, mu_dtype, *w, tc)
+
+
+def test_stream_info_reads_oracle_headers(kvc):
+    for kv_dtype, w, tc in [(O.BF16, (9500, 300), 16), (O.E4M3, (9500, 300), 7), (O.BF16, (10000, 0), 64)]:
+        st = oracle_stream(kv_dtype, w, tc)
+        p, total = kvc.kvc_stream_info(st[:128])
+        h = O.parse_header(st)
+        assert total == len(st)
+        assert (p.kv_dtype, p.mu_dtype, p.w_narrow_bp, p.w_wide_bp, p.chunk_tokens) == \
+               (h["kv_dtype"], h["mu_dtype"], h["w_narrow_bp"], h["w_wide_bp"], h["chunk_tokens"])
+        assert (p.planes, p.tokens, p.channels) == (h["planes"], h["tokens"], h["channels"])
+
+
+@pytest.mark.parametrize("offset", [0, 4, 8, 10, 13, 16, 24, 36, 56, 64, 100])
+def test_stream_info_rejects_damaged_headers(kvc, offset):
+    st = bytearray(oracle_stream()[:128])
+    st[offset] ^= 0x41
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_stream_info(bytes(st))
+    assert e.value.status == kvc.KVC_ERR_CORRUPT
