@@ -160,14 +160,17 @@ def main():
     dws = torch.empty(kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     log(f"[bench] buffers: stream capacity {enc.capacity / 1e9:.2f} GB, workspace {enc.workspace.numel() / 1e9:.2f} GB")
 
+    fallback = [0]
+
     def step(stats=None):
-        es, ds = [0.0] * kvc.ENCODE_STAGES, [0.0] * kvc.DECODE_STAGES
-        st = enc(kv, mu, sigma, prefix, stage_ms=es)
-        rc = kvc.kvc_decode_into(st, mu, sigma, prefix, kv_out, dws, stage_ms=ds)
+        ei, di = {}, {}
+        st = enc(kv, mu, sigma, prefix, info=ei)
+        rc = kvc.kvc_decode_into(st, mu, sigma, prefix, kv_out, dws, info=di)
         if rc != kvc.KVC_OK:
             raise kvc.KvcError(rc, "kvc_decode")
+        fallback[0] = di["fallback_symbols"]
         if stats is not None:
-            stats.append((es, ds))
+            stats.append((ei["stage_ms"], di["stage_ms"]))
         return st
 
     for i in range(args.warmup):
@@ -228,6 +231,7 @@ def main():
         "decode_stage_ms": {k: mean([s[1][i] for s in stats]) for i, k in enumerate(["side_hash", "decode_kernel"])},
         "bits_per_scalar": {"coded": 8.0 * stream_bytes / n, "integer_model": bits_int, "float_model": bits_float},
         "stream_bytes": stream_bytes,
+        "decode_fallback_share": fallback[0] / n,
         "roundtrip_exact": ok,
         "roofline": {
             "bound": "hbm", "kernel": f"k_{dominant}", "achieved": achieved, "peak": HBM_PEAK_GBPS,

@@ -47,6 +47,7 @@ bool geometry(int64_t planes, int64_t tokens, int64_t channels, uint32_t chunk_t
     if (planes * channels >= (int64_t(1) << 32)) return false;         // sigma words indexable
     if (planes * tokens > kMaxScalars / channels) return false;
     if (chunk_tokens < 1 || chunk_tokens > kMaxChunkTokens) return false;
+    if (int64_t(chunk_tokens) * channels >= (int64_t(1) << 31)) return false;   // in-chunk offsets fit 31 bits
     g->planes = planes;
     g->tokens = tokens;
     g->channels = channels;
@@ -215,9 +216,9 @@ const char* kvc_status_string(int status) {
     }
 }
 
-int kvc_phi_table(uint32_t* h_out) {
-    if (!h_out) return KVC_ERR_INVALID;
-    kvc::host_phi_table(h_out);
+int kvc_phi_tables(uint32_t* h_narrow, uint32_t* h_wide) {
+    if (!h_narrow || !h_wide) return KVC_ERR_INVALID;
+    kvc::host_phi_tables(h_narrow, h_wide);
     return KVC_OK;
 }
 
@@ -234,7 +235,7 @@ int kvc_encode_sizes(const kvc_params* p, uint64_t* h_max_stream_bytes, uint64_t
 
 int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const float* d_sigma,
                const uint32_t* d_prefix, void* d_out, uint64_t out_capacity, uint64_t* h_out_bytes,
-               void* d_workspace, uint64_t workspace_bytes, void* stream, float* h_stage_ms) {
+               void* d_workspace, uint64_t workspace_bytes, void* stream, kvc_encode_info* h_info) {
     ChunkGeom g;
     if (!params_geometry(p, &g) || !d_kv || !d_mu || !d_sigma || !d_out || !h_out_bytes || !d_workspace)
         return KVC_ERR_INVALID;
@@ -248,13 +249,13 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     if (workspace_bytes < l.total) return KVC_ERR_CAPACITY;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    const uint32_t* phi = kvc::device_phi_table(&e);
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
     if (e != hipSuccess) return KVC_ERR_DEVICE;
 
     uint8_t* ws = static_cast<uint8_t*>(d_workspace);
     Control* ctl = reinterpret_cast<Control*>(ws);
     const uint32_t* prefix = te ? d_prefix : nullptr;
-    StageTimer timer(h_stage_ms, KVC_ENCODE_STAGES, s);
+    StageTimer timer(h_info ? h_info->stage_ms : nullptr, KVC_ENCODE_STAGES, s);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(0);
     if ((e = kvc::launch_side_hash(d_sigma, uint64_t(g.planes) * uint64_t(g.channels), prefix,
@@ -319,7 +320,7 @@ int kvc_stream_info(const void* h_header, uint64_t header_bytes, kvc_params* h_p
 
 int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const float* d_sigma,
                const uint32_t* d_prefix, void* d_kv_out, void* d_workspace, uint64_t workspace_bytes,
-               void* stream, float* h_stage_ms) {
+               void* stream, kvc_decode_info* h_info) {
     if (!d_in || !d_mu || !d_sigma || !d_kv_out || !d_workspace) return KVC_ERR_INVALID;
     if (workspace_bytes < KVC_DECODE_WORKSPACE_BYTES) return KVC_ERR_CAPACITY;
     if (!aligned(d_in, 8) || !aligned(d_workspace, 8) || !aligned(d_sigma, 4) || !aligned(d_prefix, 4) ||
@@ -328,7 +329,7 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     if (in_bytes < KVC_HEADER_BYTES) return KVC_ERR_CORRUPT;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    const uint32_t* phi = kvc::device_phi_table(&e);
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
     if (e != hipSuccess) return KVC_ERR_DEVICE;
 
     uint8_t hb[KVC_HEADER_BYTES];
@@ -349,7 +350,7 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     if (!data_aligned(p.kv_dtype, p.mu_dtype, d_kv_out, d_mu, d_sigma, d_prefix)) return KVC_ERR_INVALID;
 
     Control* ctl = static_cast<Control*>(d_workspace);
-    StageTimer timer(h_stage_ms, KVC_DECODE_STAGES, s);
+    StageTimer timer(h_info ? h_info->stage_ms : nullptr, KVC_DECODE_STAGES, s);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(0);
     if ((e = kvc::launch_side_hash(d_sigma, uint64_t(g.planes) * uint64_t(g.channels), prefix,
@@ -376,6 +377,7 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     if ((e = hipMemcpyAsync(&host, ctl, sizeof(host), hipMemcpyDeviceToHost, s)) != hipSuccess) return KVC_ERR_DEVICE;
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.read();
+    if (h_info) h_info->fallback_symbols = host.misses;
     if (host.side_hash != hash) return KVC_ERR_MISMATCH;
     if (host.flags & kvc::kFlagBadSigma) return KVC_ERR_INVALID;
     if (host.flags & kvc::kFlagCorrupt) return KVC_ERR_CORRUPT;
@@ -422,7 +424,7 @@ int kvc_estimate_bits(const kvc_params* p, const void* d_kv, const void* d_mu, c
     if (te && !d_prefix) return KVC_ERR_INVALID;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    const uint32_t* phi = kvc::device_phi_table(&e);
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
     if (e != hipSuccess) return KVC_ERR_DEVICE;
     Control* ctl = static_cast<Control*>(d_workspace);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
@@ -459,7 +461,7 @@ int kvc_cdf_table(int32_t kv_dtype, int32_t mu_dtype, uint32_t w_narrow_bp, uint
         return KVC_ERR_INVALID;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    const uint32_t* phi = kvc::device_phi_table(&e);
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
     if (e != hipSuccess) return KVC_ERR_DEVICE;
     // sigma is checked on the host, a block at a time
     bool ok = true;
@@ -471,8 +473,7 @@ int kvc_cdf_table(int32_t kv_dtype, int32_t mu_dtype, uint32_t w_narrow_bp, uint
         if (e != hipSuccess) return KVC_ERR_DEVICE;
         for (int64_t i = 0; i < m; ++i) {
             const float sg = hs[i];
-            const float inv = 1.0f / sg;
-            if (!(sg > 0.0f) || !(sg <= FLT_MAX) || !(inv <= FLT_MAX)) ok = false;
+            if (!(sg >= 0x1p-96f && sg <= 0x1p96f)) ok = false;
         }
     }
     if (!ok) return KVC_ERR_INVALID;

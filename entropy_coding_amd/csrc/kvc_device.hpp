@@ -1,8 +1,9 @@
 // Device-side building blocks of the KVC-1 coder for gfx950: the ordered
-// alphabet, cell edges, the integer Phi and the mixture CDF.  Every
-// floating-point step is a single IEEE float32 operation with round to
-// nearest (no contraction, denormals kept), so the CDF is bit-identical to
-// the host-side specification; everything after the argument is integer.
+// alphabet, cell edges, the integer mixture CDF and the rANS arithmetic.
+// Every floating-point step of the CDF is a single IEEE float32 operation
+// with round to nearest (no contraction, denormals kept), so the CDF is
+// bit-identical to the host-side specification; everything after the
+// argument is integer.
 //
 // Model: q = 0.95 N(mu, sigma^2) + 0.03 N(mu, (3 sigma)^2) + 0.02 p_hat
 // (wiki "Speculative KV Coding", section "mixture distribution"); encoder
@@ -22,20 +23,31 @@ constexpr int kF32 = 2;
 constexpr uint32_t kLog2M = 31;
 constexpr uint32_t kM = 1u << kLog2M;         // total of every CDF
 constexpr uint64_t kL = 1ull << 47;           // lower end of the rANS state interval
+constexpr uint32_t kLHi = 1u << 15;           // kL >> 32
 constexpr int kLanes = 64;                    // rANS lanes per chunk = one wavefront
 constexpr int kStateBytes = 8 * kLanes;       // final states at the head of a chunk
-constexpr int kPhiEntries = 4098;             // Phi(-8 + k/256), k = 0..4096, plus a copy
 constexpr int kHeaderBytes = 128;
+
+// Mixture table: z grid -24 .. 24 at step 1/256, plus one repeated entry.
+constexpr int kTableZMax = 24;
+constexpr int kTablePoints = 2 * kTableZMax * 256 + 1;      // 12289
+constexpr int kTableEntries = kTablePoints + 1;             // 12290
+constexpr int32_t kQMax = kTableZMax << 24;                 // |q| <= 24 * 2^24
+constexpr float kQMaxF = static_cast<float>(kQMax);
 
 template <int KV> struct Alphabet;
 template <> struct Alphabet<kBF16> {
     static constexpr uint32_t kSize = 65536;
     static constexpr int kLog2 = 16;
+    static constexpr uint32_t kLoFinite = 128;      // index of -max
+    static constexpr uint32_t kHiFinite = 65407;    // index of +max
     using Bits = uint16_t;
 };
 template <> struct Alphabet<kE4M3> {
     static constexpr uint32_t kSize = 256;
     static constexpr int kLog2 = 8;
+    static constexpr uint32_t kLoFinite = 1;
+    static constexpr uint32_t kHiFinite = 254;
     using Bits = uint8_t;
 };
 
@@ -92,6 +104,41 @@ __device__ __forceinline__ float edge(uint32_t b) {
     else return edge_e4m3(b);
 }
 
+// Value of a finite ordered symbol.
+template <int KV>
+__device__ __forceinline__ float symbol_value(uint32_t b) {
+    const uint32_t u = bits_of_order<KV>(b);
+    if constexpr (KV == kBF16) {
+        return __uint_as_float(u << 16);
+    } else {
+        const float v = e4m3_magnitude(u & 0x7Fu);
+        return (u & 0x80u) ? -v : v;
+    }
+}
+
+// Ordered index of the finite symbol nearest to x (ties to even), clamped to
+// the finite range.  Used only to aim the decoder's search.
+template <int KV>
+__device__ __forceinline__ uint32_t nearest_symbol(float x) {
+    if constexpr (KV == kBF16) {
+        const uint32_t u = __float_as_uint(x);
+        const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+        uint32_t b = order_of_bits<kBF16>(r & 0xFFFFu);
+        b = b < Alphabet<kBF16>::kLoFinite ? Alphabet<kBF16>::kLoFinite : b;
+        return b > Alphabet<kBF16>::kHiFinite ? Alphabet<kBF16>::kHiFinite : b;
+    } else {
+        // bisection over the 254 finite e4m3 cells (8 steps, no memory)
+        uint32_t lo = 1, hi = 255;
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t mid = (lo + hi) >> 1;
+            const bool up = x >= edge_e4m3(mid);
+            lo = up ? mid : lo;
+            hi = up ? hi : mid;
+        }
+        return lo;
+    }
+}
+
 // Predictor mean as float32; a non-finite mean is replaced by 0.
 template <int MU> struct MuT;
 template <> struct MuT<kBF16> { using T = uint16_t; };
@@ -105,35 +152,37 @@ __device__ __forceinline__ float mu_value(typename MuT<MU>::T v) {
     return __builtin_isfinite(m) ? m : 0.0f;
 }
 
-// Integer Phi of z = q / 2^24, q in [-2^27, 2^27]: table step 1/256 with
-// integer linear interpolation over the 16 low bits.
-__device__ __forceinline__ uint32_t phi_fx(int32_t q, const uint32_t* __restrict__ phi) {
-    const uint32_t u = static_cast<uint32_t>(q + (1 << 27));
-    const uint32_t i = u >> 16, r = u & 0xFFFFu;
-    const uint32_t a = phi[i], c = phi[i + 1];
-    return a + static_cast<uint32_t>((static_cast<uint64_t>(c - a) * r) >> 16);
+// q = rint(clamp(d * inv, +-24) * 2^24) computed as rint(clamp(d * inv24,
+// +-24 * 2^24)) with inv24 = inv * 2^24: identical for every sigma in the
+// accepted range [2^-96, 2^96] (the power-of-two scaling is exact there and
+// both forms saturate together).
+__device__ __forceinline__ int32_t z_fixed(float edge_pos, float mu, float inv24) {
+    const float d = __fsub_rn(edge_pos, mu);
+    float zq = __fmul_rn(d, inv24);
+    zq = __builtin_amdgcn_fmed3f(zq, -kQMaxF, kQMaxF);
+    return static_cast<int32_t>(__builtin_rintf(zq));
 }
 
-struct Budgets {
-    uint32_t tn, tw;                  // narrow and wide Gaussian budgets
-    const uint32_t* __restrict__ prefix;  // escape prefix (N + 1 entries) or null
+// Integer mixture CDF of z = q / 2^24: table step 1/256 with integer linear
+// interpolation over the 16 low bits of q (table steps are below 2^22, so the
+// product fits 24-bit multiplies).
+__device__ __forceinline__ uint32_t h_fx(int32_t q, const uint32_t* __restrict__ tab) {
+    const uint32_t u = static_cast<uint32_t>(q + kQMax);
+    const uint32_t i = u >> 16, r = u & 0xFFFFu;
+    const uint32_t a = tab[i], c = tab[i + 1];
+    const uint32_t dlt = (c - a) & 0x3FFFFFu;
+    return a + static_cast<uint32_t>((static_cast<uint64_t>(dlt) * r) >> 16);
+}
+
+struct Model {
+    const uint32_t* __restrict__ tab;      // mixture table in LDS
+    const uint32_t* __restrict__ prefix;   // escape prefix (N + 1 entries) or null
 };
 
-// C(b) = b + floor(T_n Phi(q1) / 2^31) + floor(T_w Phi(floor(q/3)) / 2^31) + prefix[b]
-// with q = rint(clamp((edge(b) - mu) * inv, +-24) * 2^24) and q1 = clamp(q, +-2^27).
+// C(b) = b + h_fx(q(b)) + prefix[b].
 template <int KV>
-__device__ __forceinline__ uint32_t cdf_at(uint32_t b, float mu, float inv,
-                                           const uint32_t* __restrict__ phi, const Budgets& m) {
-    const float d = __fsub_rn(edge<KV>(b), mu);
-    float z = __fmul_rn(d, inv);
-    z = fminf(fmaxf(z, -24.0f), 24.0f);
-    const int32_t q = __float2int_rn(z * 16777216.0f);
-    const int32_t q1 = min(max(q, -(1 << 27)), 1 << 27);
-    // floor(q / 3): shift q by 3 * 2^28 so the dividend is non-negative
-    const int32_t q3 = static_cast<int32_t>(static_cast<uint32_t>(q + 3 * (1 << 28)) / 3u) - (1 << 28);
-    const uint32_t g1 = static_cast<uint32_t>((static_cast<uint64_t>(m.tn) * phi_fx(q1, phi)) >> 31);
-    const uint32_t g3 = static_cast<uint32_t>((static_cast<uint64_t>(m.tw) * phi_fx(q3, phi)) >> 31);
-    uint32_t g = b + g1 + g3;
+__device__ __forceinline__ uint32_t cdf_at(uint32_t b, float mu, float inv24, const Model& m) {
+    uint32_t g = b + h_fx(z_fixed(edge<KV>(b), mu, inv24), m.tab);
     if (m.prefix) g += m.prefix[b];
     return g;
 }
@@ -144,11 +193,32 @@ __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
-__device__ __forceinline__ bool sigma_ok(float s, float inv) {
-    return __builtin_isfinite(s) && s > 0.0f && __builtin_isfinite(inv);
+// Accepted sigma: finite, within [2^-96, 2^96].
+__device__ __forceinline__ bool sigma_ok(float s) {
+    return s >= 0x1p-96f && s <= 0x1p96f;
 }
 
-// Bits per element of a KV dtype.
-__host__ __device__ constexpr int kv_bytes(int kv) { return kv == kBF16 ? 2 : 1; }
+// floor(x / f) and x mod f for x < 2^32 f (the quotient fits 32 bits),
+// without a hardware divider: a float32 estimate, one float32 correction of
+// the remainder, and a final integer adjustment by at most one.
+__device__ __forceinline__ void divmod_q32(uint64_t x, uint32_t f, uint32_t& q, uint32_t& r) {
+    const float rf = __builtin_amdgcn_rcpf(static_cast<float>(f));
+    const uint32_t xh = static_cast<uint32_t>(x >> 32), xl = static_cast<uint32_t>(x);
+    const float fx = __fmaf_rn(static_cast<float>(xh), 4294967296.0f, static_cast<float>(xl));
+    const uint32_t q0 = static_cast<uint32_t>(__builtin_amdgcn_fmed3f(fx * rf, 0.0f, 4294967040.0f));
+    const int64_t r0 = static_cast<int64_t>(x - static_cast<uint64_t>(q0) * f);   // |r0| < 2^42
+    // r0 as float32 from two parts that are exact in float32 (a split at bit
+    // 32 would cancel catastrophically for small negative r0)
+    const float fr0 = __fmaf_rn(static_cast<float>(static_cast<int32_t>(r0 >> 21)), 2097152.0f,
+                                static_cast<float>(static_cast<uint32_t>(r0) & 0x1FFFFFu));
+    // floor of the corrected estimate is within one of floor(r0 / f)
+    const int64_t qs = static_cast<int64_t>(q0) + static_cast<int32_t>(__builtin_floorf(fr0 * rf));
+    uint32_t q1 = static_cast<uint32_t>(qs > 0xFFFFFFFFll ? 0xFFFFFFFFll : qs);
+    int64_t r1 = static_cast<int64_t>(x - static_cast<uint64_t>(q1) * f);     // in [-f, 2f)
+    if (r1 < 0) { q1 -= 1u; r1 += f; }
+    if (r1 >= static_cast<int64_t>(f)) { q1 += 1u; r1 -= f; }
+    q = q1;
+    r = static_cast<uint32_t>(r1);
+}
 
 }  // namespace kvc

@@ -22,7 +22,8 @@ struct Control {
     unsigned long long side_hash;       // sum of mixed side-information words
     unsigned long long total_payload;   // payload bytes of the stream
     double bits[2];                     // estimate sums (integer model, float model)
-    unsigned long long reserved[3];
+    unsigned long long misses;          // decoder: symbols found by the fallback search
+    unsigned long long reserved[2];
 };
 static_assert(sizeof(Control) == 64, "control block size");
 
@@ -35,6 +36,12 @@ struct ChunkGeom {
     int64_t n_chunks;
 };
 
+// Per-device Phi base tables (kTablePoints entries each).
+struct PhiTables {
+    const uint32_t* a;                  // round(2^31 Phi(z_k))
+    const uint32_t* b;                  // round(2^31 Phi(z_k / 3))
+};
+
 struct EncodeArgs {
     ChunkGeom geom;
     const void* kv;
@@ -42,7 +49,7 @@ struct EncodeArgs {
     const float* sigma;
     const uint32_t* prefix;             // null when there is no escape part
     uint32_t tn, tw;
-    const uint32_t* phi;                // device Phi table (kPhiEntries)
+    PhiTables phi;
     uint16_t* slots;                    // per-chunk word slots, filled from the end
     uint64_t slot_words;                // words per slot (2 per scalar, multiple of 4)
     unsigned long long* states;         // [n_chunks][64] final states
@@ -75,7 +82,7 @@ struct DecodeArgs {
     const float* sigma;
     const uint32_t* prefix;
     uint32_t tn, tw;
-    const uint32_t* phi;
+    PhiTables phi;
     void* kv_out;
     Control* ctl;
 };
@@ -88,13 +95,14 @@ struct EstimateArgs {
     const uint32_t* prefix;
     uint32_t tn, tw, te;
     uint32_t w_narrow_bp, w_wide_bp;
-    const uint32_t* phi;
+    PhiTables phi;
     Control* ctl;
 };
 
-// Per-device Phi table: computed once on the host, copied to the device.
-const uint32_t* device_phi_table(hipError_t* err);
-void host_phi_table(uint32_t* out);   // kPhiEntries entries
+// Phi base tables: computed once on the host, copied to each device.
+constexpr int kPhiPoints = 12289;
+PhiTables device_phi_tables(hipError_t* err);
+void host_phi_tables(uint32_t* a, uint32_t* b);   // kPhiPoints entries each
 
 hipError_t launch_clear_control(Control* ctl, hipStream_t s);
 hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t* prefix,
@@ -112,7 +120,7 @@ hipError_t launch_marginal(const void* samples, int dtype, uint64_t n, uint32_t 
 hipError_t launch_estimate(const EstimateArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);
 hipError_t launch_cdf_table(int kv_dtype, int mu_dtype, uint32_t tn, uint32_t tw,
                             const void* mu, const float* sigma, int64_t pairs,
-                            const uint32_t* prefix, uint32_t* out, const uint32_t* phi,
+                            const uint32_t* prefix, uint32_t* out, PhiTables phi,
                             hipStream_t s);
 
 }  // namespace kvc

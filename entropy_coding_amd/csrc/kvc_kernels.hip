@@ -4,11 +4,12 @@
 // plane over a run of tokens, so every token step reads one contiguous
 // 64-element row of KV and mu per wave, and the 64 interleaved rANS states
 // live in registers.  Renormalisation words are placed with two wave ballots
-// and mbcnt ranks.  The Phi table sits in LDS; the escape prefix (256 KB for
-// bf16) is read through L2.  Sources for the model: wiki "Speculative KV
-// Coding" (sections "pipeline", "mixture distribution"); blog post on
-// speculative KV coding (sections "information theory view",
-// "engineering choice of predictor", "deployment parameters").
+// and mbcnt ranks.  Each workgroup builds the mixture table (and, for the
+// decoder, its inverse index) in LDS from two per-device Phi tables; the
+// escape prefix (256 KB for bf16) is read through L2.  Sources for the
+// model: wiki "Speculative KV Coding" (sections "pipeline", "mixture
+// distribution"); blog post on speculative KV coding (sections "information
+// theory view", "engineering choice of predictor", "deployment parameters").
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -21,53 +22,81 @@
 namespace kvc {
 
 // ---------------------------------------------------------------------------
-// Phi table: round(2^31 Phi(-8 + k/256)), computed on the host with the C
-// library's erfc in double precision (no entry lies within 1e-6 of a
-// rounding tie, far above double's error) and copied to each device once.
+// Phi base tables: A[k] = round(2^31 Phi(z_k)), B[k] = round(2^31 Phi(z_k/3))
+// on z_k = -24 + k/256, computed on the host with the C library's erfc in
+// double precision (no entry lies within 4e-6 of a rounding tie, far above
+// double's error) and copied to each device once.
 // ---------------------------------------------------------------------------
-__device__ uint32_t g_phi[kPhiEntries];
+__device__ uint32_t g_phi_a[kTablePoints];
+__device__ uint32_t g_phi_b[kTablePoints];
 
-void host_phi_table(uint32_t* out) {
-    for (int k = 0; k <= 4096; ++k) {
-        const double x = -8.0 + k / 256.0;
-        const double v = std::ldexp(0.5 * std::erfc(-x * 0.70710678118654752440), 31);
-        out[k] = static_cast<uint32_t>(std::floor(v + 0.5));
+void host_phi_tables(uint32_t* a, uint32_t* b) {
+    for (int k = 0; k < kTablePoints; ++k) {
+        const double z = -24.0 + k / 256.0;
+        const double s = 0.70710678118654752440;
+        a[k] = static_cast<uint32_t>(std::floor(std::ldexp(0.5 * std::erfc(-z * s), 31) + 0.5));
+        b[k] = static_cast<uint32_t>(std::floor(std::ldexp(0.5 * std::erfc(-(z / 3.0) * s), 31) + 0.5));
     }
-    out[4097] = out[4096];
 }
 
 namespace {
 constexpr int kMaxDevices = 64;
 std::once_flag g_phi_once[kMaxDevices];
-const uint32_t* g_phi_ptr[kMaxDevices];
+PhiTables g_phi_dev[kMaxDevices];
 hipError_t g_phi_err[kMaxDevices];
 }  // namespace
 
-const uint32_t* device_phi_table(hipError_t* err) {
+PhiTables device_phi_tables(hipError_t* err) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
         *err = (e != hipSuccess) ? e : hipErrorInvalidDevice;
-        return nullptr;
+        return PhiTables{nullptr, nullptr};
     }
     std::call_once(g_phi_once[dev], [dev]() {
-        uint32_t host[kPhiEntries];
-        host_phi_table(host);
-        hipError_t r = hipMemcpyToSymbol(HIP_SYMBOL(g_phi), host, sizeof(host), 0, hipMemcpyHostToDevice);
-        void* p = nullptr;
-        if (r == hipSuccess) r = hipGetSymbolAddress(&p, HIP_SYMBOL(g_phi));
+        static uint32_t ha[kTablePoints], hb[kTablePoints];
+        host_phi_tables(ha, hb);
+        hipError_t r = hipMemcpyToSymbol(HIP_SYMBOL(g_phi_a), ha, sizeof(ha), 0, hipMemcpyHostToDevice);
+        if (r == hipSuccess) r = hipMemcpyToSymbol(HIP_SYMBOL(g_phi_b), hb, sizeof(hb), 0, hipMemcpyHostToDevice);
+        void* pa = nullptr;
+        void* pb = nullptr;
+        if (r == hipSuccess) r = hipGetSymbolAddress(&pa, HIP_SYMBOL(g_phi_a));
+        if (r == hipSuccess) r = hipGetSymbolAddress(&pb, HIP_SYMBOL(g_phi_b));
         g_phi_err[dev] = r;
-        g_phi_ptr[dev] = static_cast<const uint32_t*>(p);
+        g_phi_dev[dev] = PhiTables{static_cast<const uint32_t*>(pa), static_cast<const uint32_t*>(pb)};
     });
     *err = g_phi_err[dev];
-    return g_phi_ptr[dev];
+    return g_phi_dev[dev];
 }
 
 // ---------------------------------------------------------------------------
 // helpers
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void load_phi_lds(uint32_t* s_phi, const uint32_t* __restrict__ phi) {
-    for (int i = threadIdx.x; i < kPhiEntries; i += blockDim.x) s_phi[i] = phi[i];
+// H[k] = floor(T_n A[k] / 2^31) + floor(T_w B[k] / 2^31), H[12289] = H[12288].
+__device__ __forceinline__ void build_table_lds(uint32_t* s_tab, const PhiTables& phi, uint32_t tn, uint32_t tw) {
+    for (int k = threadIdx.x; k < kTableEntries; k += blockDim.x) {
+        const int kk = k < kTablePoints ? k : kTablePoints - 1;
+        const uint32_t h = static_cast<uint32_t>((static_cast<uint64_t>(tn) * phi.a[kk]) >> 31) +
+                           static_cast<uint32_t>((static_cast<uint64_t>(tw) * phi.b[kk]) >> 31);
+        s_tab[k] = h;
+    }
+    __syncthreads();
+}
+
+// Inverse index of the mixture table for the decoder's aim: inv[j] is the
+// largest k with H[k] <= floor(j * (T_n + T_w) / kInvSteps).
+constexpr int kInvSteps = 4096;
+__device__ __forceinline__ void build_inverse_lds(uint16_t* s_inv, const uint32_t* s_tab, uint32_t htot) {
+    for (int j = threadIdx.x; j <= kInvSteps; j += blockDim.x) {
+        const uint32_t thr = static_cast<uint32_t>((static_cast<uint64_t>(htot) * j) / kInvSteps);
+        uint32_t lo = 0, hi = kTablePoints;          // H[lo] <= thr, search in [lo, hi)
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (s_tab[mid] <= thr) lo = mid;
+            else hi = mid;
+        }
+        s_inv[j] = static_cast<uint16_t>(lo);
+    }
     __syncthreads();
 }
 
@@ -138,7 +167,7 @@ hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t
                             uint64_t n_prefix, Control* ctl, hipStream_t s) {
     const uint64_t n = n_sigma + n_prefix;
     uint64_t blocks = (n + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
+    if (blocks > 512) blocks = 512;
     if (blocks == 0) blocks = 1;
     hipLaunchKernelGGL(k_side_hash, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s,
                        reinterpret_cast<const uint32_t*>(sigma), n_sigma, prefix, n_prefix, ctl);
@@ -146,66 +175,104 @@ hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t
 }
 
 // ---------------------------------------------------------------------------
-// encoder: one wave per chunk, tokens last to first
+// encoder: one wave per chunk, tokens last to first.  The model side of a
+// batch of tokens (loads, symbol, both CDF edges) does not depend on the
+// coder state, so it runs ahead of the serial rANS pushes.
 // ---------------------------------------------------------------------------
+constexpr int kEncodeBlock = 1024;
+constexpr int kEncodeBatch = 8;
+
+struct PushState {
+    uint32_t xl, xh;                 // 64-bit rANS state
+    uint32_t wp;                     // words left free in the slot (wave-uniform)
+};
+
+// Push one symbol (start c0, frequency f) onto the 64 lane states; emitted
+// words go to the slot block of this token step, in decoder read order.
+__device__ __forceinline__ void rans_push(PushState& st, uint32_t c0, uint32_t f, uint16_t* __restrict__ slot) {
+    const bool e1 = st.xh >= f;               // x / 2^32 >= f: one word out
+    const bool e2 = (st.xh >> 16) >= f;       // x / 2^48 >= f: two words out
+    const uint64_t m1 = __ballot(e1);
+    const uint64_t m2 = __ballot(e2);
+    const uint32_t n1 = __popcll(m1), n2 = __popcll(m2);
+    st.wp -= n1 + n2;
+    if (e1) slot[st.wp + lane_rank(m1)] = static_cast<uint16_t>(e2 ? (st.xl >> 16) : st.xl);
+    if (e2) slot[st.wp + n1 + lane_rank(m2)] = static_cast<uint16_t>(st.xl);
+    uint32_t lo = e1 ? __builtin_amdgcn_alignbit(st.xh, st.xl, 16) : st.xl;
+    uint32_t hi = e1 ? (st.xh >> 16) : st.xh;
+    lo = e2 ? st.xh : lo;
+    hi = e2 ? 0u : hi;
+    uint32_t q, r;
+    divmod_q32((static_cast<uint64_t>(hi) << 32) | lo, f, q, r);
+    // x = q * 2^31 + r + c0 with r + c0 < 2^31: no carry into bit 31
+    st.xh = q >> 1;
+    st.xl = (q << 31) | (r + c0);
+}
+
+template <int KV, int MU, int U>
+__device__ __forceinline__ void encode_batch(int t, PushState& st, const typename Alphabet<KV>::Bits* __restrict__ kvp,
+                                             const typename MuT<MU>::T* __restrict__ mup, uint32_t D, float inv24,
+                                             const Model& m, uint16_t* __restrict__ slot) {
+    typename Alphabet<KV>::Bits kb[U];
+    typename MuT<MU>::T mb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t off = static_cast<uint32_t>(t - u) * D;
+        kb[u] = kvp[off];
+        mb[u] = mup[off];
+    }
+    uint32_t c0[U], fr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t s = order_of_bits<KV>(kb[u]);
+        const float mu = mu_value<MU>(mb[u]);
+        c0[u] = cdf_at<KV>(s, mu, inv24, m);
+        fr[u] = cdf_at<KV>(s + 1, mu, inv24, m) - c0[u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) rans_push(st, c0[u], fr[u], slot);
+}
+
 template <int KV, int MU>
-__global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
-    __shared__ uint32_t s_phi[kPhiEntries];
-    load_phi_lds(s_phi, a.phi);
+__global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
+    __shared__ uint32_t s_tab[kTableEntries];
+    build_table_lds(s_tab, a.phi, a.tn, a.tw);
 
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (kEncodeBlock / 64) + (threadIdx.x >> 6);
     if (chunk >= a.geom.n_chunks) return;
     const ChunkPos cp = chunk_pos(a.geom, chunk);
-    const int64_t D = a.geom.channels;
-    const int64_t d = static_cast<int64_t>(cp.k) * 64 + lane;
+    const uint32_t D = static_cast<uint32_t>(a.geom.channels);
 
-    const float sigma = a.sigma[cp.g * D + d];
-    float inv = __frcp_rn(sigma);
-    const bool ok = sigma_ok(sigma, inv);
-    if (__ballot(!ok)) {
+    const float sigma = a.sigma[cp.g * D + cp.k * 64 + lane];
+    float inv24 = __frcp_rn(sigma) * 16777216.0f;
+    if (__ballot(!sigma_ok(sigma))) {
         if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
-        inv = 1.0f;
+        inv24 = 16777216.0f;
     }
-    const Budgets bud{a.tn, a.tw, a.prefix};
+    const Model m{s_tab, a.prefix};
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
-    const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * D + d;
-    const KB* __restrict__ kvp = static_cast<const KB*>(a.kv) + row0;
-    const MT* __restrict__ mup = static_cast<const MT*>(a.mu) + row0;
-
+    const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * static_cast<int64_t>(D) + cp.k * 64;
+    const KB* __restrict__ kvp = static_cast<const KB*>(a.kv) + row0 + lane;
+    const MT* __restrict__ mup = static_cast<const MT*>(a.mu) + row0 + lane;
     uint16_t* __restrict__ slot = a.slots + static_cast<uint64_t>(chunk) * a.slot_words;
-    uint32_t wp = static_cast<uint32_t>(a.slot_words);
-    unsigned long long x = kL;
 
-    for (int t = static_cast<int>(cp.len) - 1; t >= 0; --t) {
-        const int64_t off = static_cast<int64_t>(t) * D;
-        const uint32_t s = order_of_bits<KV>(kvp[off]);
-        const float mu = mu_value<MU>(mup[off]);
-        const uint32_t c0 = cdf_at<KV>(s, mu, inv, s_phi, bud);
-        const uint32_t c1 = cdf_at<KV>(s + 1, mu, inv, s_phi, bud);
-        const uint32_t f = c1 - c0;
+    PushState st{static_cast<uint32_t>(kL), kLHi, static_cast<uint32_t>(a.slot_words)};
+    int t = static_cast<int>(cp.len) - 1;
+    for (; t >= kEncodeBatch - 1; t -= kEncodeBatch)
+        encode_batch<KV, MU, kEncodeBatch>(t, st, kvp, mup, D, inv24, m, slot);
+    for (; t >= 0; --t) encode_batch<KV, MU, 1>(t, st, kvp, mup, D, inv24, m, slot);
 
-        const uint32_t cnt = static_cast<uint32_t>((x >> 32) >= f) + static_cast<uint32_t>((x >> 48) >= f);
-        const uint64_t m1 = __ballot(cnt >= 1u);
-        const uint64_t m2 = __ballot(cnt == 2u);
-        const uint32_t n1 = __popcll(m1), n2 = __popcll(m2);
-        wp -= n1 + n2;
-        if (cnt >= 1u) slot[wp + lane_rank(m1)] = static_cast<uint16_t>(cnt == 2u ? (x >> 16) : x);
-        if (cnt == 2u) slot[wp + n1 + lane_rank(m2)] = static_cast<uint16_t>(x);
-        x >>= 16u * cnt;
-        const unsigned long long qt = x / f;
-        const unsigned long long rm = x - qt * f;
-        x = (qt << kLog2M) + rm + c0;
-    }
-    a.states[chunk * 64 + lane] = x;
-    if (lane == 0) a.chunk_words[chunk] = static_cast<uint32_t>(a.slot_words) - wp;
+    a.states[chunk * 64 + lane] = (static_cast<unsigned long long>(st.xh) << 32) | st.xl;
+    if (lane == 0) a.chunk_words[chunk] = static_cast<uint32_t>(a.slot_words) - st.wp;
 }
 
 hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s) {
-    const uint64_t blocks = (static_cast<uint64_t>(a.geom.n_chunks) + 3) / 4;
-    const dim3 grid(static_cast<uint32_t>(blocks)), block(256);
+    constexpr int waves = kEncodeBlock / 64;
+    const uint64_t blocks = (static_cast<uint64_t>(a.geom.n_chunks) + waves - 1) / waves;
+    const dim3 grid(static_cast<uint32_t>(blocks)), block(kEncodeBlock);
     if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_encode<kBF16, kBF16>), grid, block, 0, s, a);
     else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_encode<kBF16, kF32>), grid, block, 0, s, a);
     else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_encode<kE4M3, kBF16>), grid, block, 0, s, a);
@@ -217,7 +284,7 @@ hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStr
 // ---------------------------------------------------------------------------
 // stream compaction: exclusive scan of chunk sizes (one workgroup, wave
 // scans), then one workgroup per chunk copies states and words to the
-// chunk's final offset.
+// chunk's final offset with 16-byte stores.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ unsigned long long chunk_bytes(uint32_t words) {
     return (static_cast<unsigned long long>(kStateBytes) + 2ull * words + 7ull) & ~7ull;
@@ -293,11 +360,34 @@ __global__ void __launch_bounds__(256) k_compact(CompactArgs a, StreamHeader h) 
         }
         uint8_t* dst = a.out + pay_off + beg;
         if (tid < 64) reinterpret_cast<unsigned long long*>(dst)[tid] = a.states[c * 64 + tid];
+        // words [w0, w0 + nw) of the slot -> dst + 512, zero padded to 8 bytes;
+        // the slot is 8-byte aligned, so read aligned dwords and realign by
+        // half a dword when w0 is odd
         const uint32_t nw = a.chunk_words[c];
-        const uint16_t* src = a.slots + static_cast<uint64_t>(c) * a.slot_words + (a.slot_words - nw);
-        uint16_t* dw = reinterpret_cast<uint16_t*>(dst + kStateBytes);
-        const uint32_t padded = static_cast<uint32_t>((chunk_bytes(nw) - kStateBytes) / 2);
-        for (uint32_t i = tid; i < padded; i += blockDim.x) dw[i] = (i < nw) ? src[i] : uint16_t(0);
+        const uint64_t w0 = a.slot_words - nw;
+        const uint32_t* src32 = reinterpret_cast<const uint32_t*>(a.slots + static_cast<uint64_t>(c) * a.slot_words);
+        const uint32_t s_dw = static_cast<uint32_t>(w0 >> 1);                    // first source dword
+        const bool odd = (w0 & 1) != 0;
+        const uint32_t out_dw = static_cast<uint32_t>((chunk_bytes(nw) - kStateBytes) / 4);   // multiple of 2
+        const uint32_t src_end_dw = static_cast<uint32_t>(a.slot_words >> 1);   // exclusive
+        uint32_t* d32 = reinterpret_cast<uint32_t*>(dst + kStateBytes);
+        for (uint32_t i = 2 * tid; i < out_dw; i += 2 * blockDim.x) {
+            uint32_t v[3];
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const uint32_t sd = s_dw + i + j;
+                v[j] = sd < src_end_dw ? src32[sd] : 0u;
+            }
+            uint32_t o0 = odd ? __builtin_amdgcn_alignbit(v[1], v[0], 16) : v[0];
+            uint32_t o1 = odd ? __builtin_amdgcn_alignbit(v[2], v[1], 16) : v[1];
+            // words past nw are padding
+            const uint32_t wi = 2 * i;                     // first word of o0
+            if (wi + 0 >= nw) o0 = 0u;
+            else if (wi + 1 >= nw) o0 &= 0xFFFFu;
+            if (wi + 2 >= nw) o1 = 0u;
+            else if (wi + 3 >= nw) o1 &= 0xFFFFu;
+            *reinterpret_cast<uint2*>(d32 + i) = make_uint2(o0, o1);
+        }
     }
 }
 
@@ -309,19 +399,98 @@ hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream
 }
 
 // ---------------------------------------------------------------------------
-// decoder: one wave per chunk, tokens first to last
+// decoder: one wave per chunk, tokens first to last.  The symbol is aimed
+// at through the inverse of the mixture table (the escape and floor terms
+// taken at the predictor's own symbol), the nearest cell edge E and one of
+// its neighbours are evaluated, and a bisection inside the known bracket
+// handles the rare misses; the search result is checked exactly either way.
 // ---------------------------------------------------------------------------
+constexpr int kDecodeBlock = 1024;
+
+template <int KV>
+struct DecodeModel {
+    Model m;
+    const uint16_t* __restrict__ inv;      // inverse index in LDS
+    uint32_t htot;                         // T_n + T_w
+    float inv_scale;                       // kInvSteps / htot
+};
+
+// Find s with C(s) <= target < C(s + 1); returns s, start and frequency.
+template <int KV>
+__device__ __forceinline__ uint32_t decode_symbol(uint32_t target, float mu, float sg, float inv24, uint32_t bias,
+                                                  const DecodeModel<KV>& dm, uint32_t& start, uint32_t& freq,
+                                                  uint32_t& misses) {
+    constexpr uint32_t N = Alphabet<KV>::kSize;
+    uint32_t E;
+    if (dm.htot) {
+        // aim: e = target minus the floor and escape mass below mu's symbol
+        int32_t e = static_cast<int32_t>(target) - static_cast<int32_t>(bias);
+        e = e < 0 ? 0 : e;
+        const uint32_t eu = static_cast<uint32_t>(e) < dm.htot ? static_cast<uint32_t>(e) : dm.htot - 1u;
+        int j = static_cast<int>(static_cast<float>(eu) * dm.inv_scale);
+        const int jl = j > 0 ? j - 1 : 0;
+        const int jh = j + 2 < kInvSteps ? j + 2 : kInvSteps;
+        uint32_t lo = dm.inv[jl];
+        uint32_t hi = static_cast<uint32_t>(dm.inv[jh]) + 1u;
+        hi = hi < static_cast<uint32_t>(kTablePoints - 1) ? hi : static_cast<uint32_t>(kTablePoints - 1);
+        while (hi - lo > 1) {                       // H[lo] <= eu < H[hi]
+            const uint32_t mid = (lo + hi) >> 1;
+            if (dm.m.tab[mid] <= eu) lo = mid;
+            else hi = mid;
+        }
+        const uint32_t h0 = dm.m.tab[lo], h1 = dm.m.tab[lo + 1];
+        const float frac = static_cast<float>(eu - h0) * __builtin_amdgcn_rcpf(static_cast<float>(h1 - h0));
+        const float zf = (static_cast<float>(lo) + frac) * (1.0f / 256.0f) - static_cast<float>(kTableZMax);
+        const float pos = __fmaf_rn(zf, sg, mu);
+        const uint32_t jb = nearest_symbol<KV>(pos);
+        E = jb + (pos > symbol_value<KV>(jb) ? 1u : 0u);
+    } else {
+        E = nearest_symbol<KV>(mu);
+    }
+    const uint32_t cE = cdf_at<KV>(E, mu, inv24, dm.m);
+    const bool up = target >= cE;
+    const uint32_t E2 = up ? E + 1u : E - 1u;
+    const uint32_t c2 = cdf_at<KV>(E2, mu, inv24, dm.m);
+    const bool ok = up ? (target < c2) : (target >= c2);
+    uint32_t s = up ? E : E2;
+    start = up ? cE : c2;
+    freq = up ? c2 - cE : cE - c2;
+    if (__ballot(!ok)) {
+        // bracket [lo, hi) with C(lo) <= target < C(hi) from what is known
+        uint32_t lo = up ? E2 : 0u, hi = up ? N : E2;
+        uint32_t clo = up ? c2 : 0u, chi = up ? kM : c2;
+        bool need = !ok;
+        misses += need ? 1u : 0u;
+        for (int it = 0; it <= Alphabet<KV>::kLog2 && __ballot(need && hi - lo > 1); ++it) {
+            if (need && hi - lo > 1) {
+                const uint32_t mid = (lo + hi) >> 1;
+                const uint32_t cm = cdf_at<KV>(mid, mu, inv24, dm.m);
+                if (cm <= target) { lo = mid; clo = cm; }
+                else { hi = mid; chi = cm; }
+            }
+        }
+        if (need) {
+            s = lo;
+            start = clo;
+            freq = chi - clo;
+        }
+    }
+    return s;
+}
+
 template <int KV, int MU>
-__global__ void __launch_bounds__(256) k_decode(DecodeArgs a) {
-    __shared__ uint32_t s_phi[kPhiEntries];
-    load_phi_lds(s_phi, a.phi);
+__global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
+    __shared__ uint32_t s_tab[kTableEntries];
+    __shared__ uint16_t s_inv[kInvSteps + 1];
+    build_table_lds(s_tab, a.phi, a.tn, a.tw);
+    const uint32_t htot = a.tn + a.tw;
+    if (htot) build_inverse_lds(s_inv, s_tab, htot);
 
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (kDecodeBlock / 64) + (threadIdx.x >> 6);
     if (chunk >= a.geom.n_chunks) return;
     const ChunkPos cp = chunk_pos(a.geom, chunk);
-    const int64_t D = a.geom.channels;
-    const int64_t d = static_cast<int64_t>(cp.k) * 64 + lane;
+    const uint32_t D = static_cast<uint32_t>(a.geom.channels);
 
     // the chunk's directory entry must describe an aligned, in-bounds payload
     const unsigned long long beg = a.directory[chunk], end = a.directory[chunk + 1];
@@ -334,38 +503,33 @@ __global__ void __launch_bounds__(256) k_decode(DecodeArgs a) {
     const uint16_t* __restrict__ words = reinterpret_cast<const uint16_t*>(base + kStateBytes);
     const uint32_t avail = static_cast<uint32_t>((end - beg - kStateBytes) / 2);
 
-    const float sigma = a.sigma[cp.g * D + d];
-    float inv = __frcp_rn(sigma);
-    if (__ballot(!sigma_ok(sigma, inv))) {
+    const float sigma = a.sigma[cp.g * D + cp.k * 64 + lane];
+    float inv24 = __frcp_rn(sigma) * 16777216.0f;
+    float sg = sigma;
+    if (__ballot(!sigma_ok(sigma))) {
         if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
-        inv = 1.0f;
+        inv24 = 16777216.0f;
+        sg = 1.0f;
     }
-    const Budgets bud{a.tn, a.tw, a.prefix};
+    DecodeModel<KV> dm{Model{s_tab, a.prefix}, s_inv, htot,
+                       htot ? static_cast<float>(kInvSteps) / static_cast<float>(htot) : 0.0f};
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
-    const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * D + d;
-    KB* __restrict__ outp = static_cast<KB*>(a.kv_out) + row0;
-    const MT* __restrict__ mup = static_cast<const MT*>(a.mu) + row0;
+    const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * static_cast<int64_t>(D) + cp.k * 64;
+    KB* __restrict__ outp = static_cast<KB*>(a.kv_out) + row0 + lane;
+    const MT* __restrict__ mup = static_cast<const MT*>(a.mu) + row0 + lane;
 
-    uint32_t rp = 0;
+    uint32_t rp = 0, misses = 0;
     for (uint32_t t = 0; t < cp.len; ++t) {
-        const int64_t off = static_cast<int64_t>(t) * D;
+        const uint32_t off = t * D;
         const float mu = mu_value<MU>(mup[off]);
+        const uint32_t gm = nearest_symbol<KV>(mu);
+        const uint32_t bias = gm + (a.prefix ? a.prefix[gm] : 0u);
         const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
-        uint32_t lo = 0, hi = Alphabet<KV>::kSize, clo = 0, chi = kM;
-#pragma unroll 1
-        for (int it = 0; it < Alphabet<KV>::kLog2; ++it) {
-            const uint32_t mid = (lo + hi) >> 1;
-            const uint32_t cm = cdf_at<KV>(mid, mu, inv, s_phi, bud);
-            const bool go = cm <= target;
-            lo = go ? mid : lo;
-            clo = go ? cm : clo;
-            hi = go ? hi : mid;
-            chi = go ? chi : cm;
-        }
-        const uint32_t f = chi - clo;
-        x = static_cast<unsigned long long>(f) * (x >> kLog2M) + (target - clo);
+        uint32_t start, freq;
+        const uint32_t s = decode_symbol<KV>(target, mu, sg, inv24, bias, dm, start, freq, misses);
+        x = static_cast<unsigned long long>(freq) * (x >> kLog2M) + (target - start);
 
         bool need = x < kL;
         const uint64_t m1 = __ballot(need);
@@ -382,7 +546,7 @@ __global__ void __launch_bounds__(256) k_decode(DecodeArgs a) {
             x = (x << 16) | (i < avail ? words[i] : 0u);
         }
         rp += n1 + n2;
-        outp[off] = static_cast<KB>(bits_of_order<KV>(lo));
+        outp[off] = static_cast<KB>(bits_of_order<KV>(s));
     }
     // every lane back at the initial state, the payload consumed exactly,
     // the padding zero
@@ -392,11 +556,14 @@ __global__ void __launch_bounds__(256) k_decode(DecodeArgs a) {
         if (static_cast<uint32_t>(lane) < pad_words && words[rp + lane] != 0) bad = true;
     }
     if (__ballot(bad) && lane == 0) atomicOr(&a.ctl->flags, kFlagCorrupt);
+    const unsigned long long mw = wave_sum_u64(misses);
+    if (lane == 0 && mw) atomicAdd(&a.ctl->misses, mw);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s) {
-    const uint64_t blocks = (static_cast<uint64_t>(a.geom.n_chunks) + 3) / 4;
-    const dim3 grid(static_cast<uint32_t>(blocks)), block(256);
+    constexpr int waves = kDecodeBlock / 64;
+    const uint64_t blocks = (static_cast<uint64_t>(a.geom.n_chunks) + waves - 1) / waves;
+    const dim3 grid(static_cast<uint32_t>(blocks)), block(kDecodeBlock);
     if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kBF16, kBF16>), grid, block, 0, s, a);
     else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_decode<kBF16, kF32>), grid, block, 0, s, a);
     else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kE4M3, kBF16>), grid, block, 0, s, a);
@@ -409,6 +576,7 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStr
 // sigma calibration: one workgroup of 16 waves per (plane, 64-channel
 // group); wave w sums rows w, w+16, ... in float64; the 16 partial sums are
 // added in wave order, so the result does not depend on scheduling.
+// Non-finite residuals carry no scale information and are skipped.
 // ---------------------------------------------------------------------------
 template <int KV>
 __device__ __forceinline__ double kv_value_f64(typename Alphabet<KV>::Bits b) {
@@ -445,7 +613,7 @@ __global__ void __launch_bounds__(1024) k_calibrate(const void* kv_, const void*
         const int64_t off = ((rep * planes + p) * tokens + t) * channels + d;
         const double e = kv_value_f64<KV>(kv[off]) - static_cast<double>(mu_value<MU>(mu[off]));
         const double e2 = e * e;
-        if (__builtin_isfinite(e2)) {       // a non-finite residual says nothing about scale
+        if (__builtin_isfinite(e2)) {
             acc += e2;
             ++used;
         }
@@ -560,14 +728,14 @@ __device__ __forceinline__ double gauss_mass(double a, double b) {
 
 template <int KV, int MU>
 __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
-    __shared__ uint32_t s_phi[kPhiEntries];
+    __shared__ uint32_t s_tab[kTableEntries];
     __shared__ double s_red[2][4];
-    load_phi_lds(s_phi, a.phi);
+    build_table_lds(s_tab, a.phi, a.tn, a.tw);
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
     const KB* __restrict__ kv = static_cast<const KB*>(a.kv);
     const MT* __restrict__ mup = static_cast<const MT*>(a.mu);
-    const Budgets bud{a.tn, a.tw, a.prefix};
+    const Model model{s_tab, a.prefix};
     const int64_t D = a.geom.channels, T = a.geom.tokens;
     const int64_t n = a.geom.planes * T * D;
     const double wn = a.w_narrow_bp / 1e4, ww = a.w_wide_bp / 1e4, we = 1.0 - wn - ww;
@@ -577,11 +745,11 @@ __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
         const int64_t d = i % D;
         const int64_t g = i / (T * D);
         const float sg = a.sigma[g * D + d];
-        const float inv = __frcp_rn(sg);
+        const float inv24 = __frcp_rn(sg) * 16777216.0f;
         const float mu = mu_value<MU>(mup[i]);
         const uint32_t s = order_of_bits<KV>(kv[i]);
-        const uint32_t c0 = cdf_at<KV>(s, mu, inv, s_phi, bud);
-        const uint32_t c1 = cdf_at<KV>(s + 1, mu, inv, s_phi, bud);
+        const uint32_t c0 = cdf_at<KV>(s, mu, inv24, model);
+        const uint32_t c1 = cdf_at<KV>(s + 1, mu, inv24, model);
         acc_i += 31.0 - log2(static_cast<double>(c1 - c0));
         const double lo = edge<KV>(s), hi = edge<KV>(s + 1);
         const double m = mu, sd = sg;
@@ -605,7 +773,7 @@ __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
 }
 
 hipError_t launch_estimate(const EstimateArgs& a, int kv_dtype, int mu_dtype, hipStream_t s) {
-    const dim3 grid(2048), block(256);
+    const dim3 grid(1024), block(256);
     if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_estimate<kBF16, kBF16>), grid, block, 0, s, a);
     else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_estimate<kBF16, kF32>), grid, block, 0, s, a);
     else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_estimate<kE4M3, kBF16>), grid, block, 0, s, a);
@@ -620,27 +788,27 @@ hipError_t launch_estimate(const EstimateArgs& a, int kv_dtype, int mu_dtype, hi
 template <int KV, int MU>
 __global__ void __launch_bounds__(256) k_cdf_table(const void* mu_, const float* __restrict__ sigma, int64_t pairs,
                                                    uint32_t tn, uint32_t tw, const uint32_t* __restrict__ prefix,
-                                                   uint32_t* __restrict__ out, const uint32_t* __restrict__ phi) {
-    __shared__ uint32_t s_phi[kPhiEntries];
-    load_phi_lds(s_phi, phi);
+                                                   uint32_t* __restrict__ out, PhiTables phi) {
+    __shared__ uint32_t s_tab[kTableEntries];
+    build_table_lds(s_tab, phi, tn, tw);
     using MT = typename MuT<MU>::T;
     constexpr uint32_t N1 = Alphabet<KV>::kSize + 1;
-    const Budgets bud{tn, tw, prefix};
+    const Model model{s_tab, prefix};
     const int64_t total = pairs * N1;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
         const int64_t p = i / N1;
         const uint32_t b = static_cast<uint32_t>(i - p * N1);
         const float mu = mu_value<MU>(static_cast<const MT*>(mu_)[p]);
-        const float inv = __frcp_rn(sigma[p]);
-        out[i] = cdf_at<KV>(b, mu, inv, s_phi, bud);
+        const float inv24 = __frcp_rn(sigma[p]) * 16777216.0f;
+        out[i] = cdf_at<KV>(b, mu, inv24, model);
     }
 }
 
 hipError_t launch_cdf_table(int kv_dtype, int mu_dtype, uint32_t tn, uint32_t tw, const void* mu,
                             const float* sigma, int64_t pairs, const uint32_t* prefix, uint32_t* out,
-                            const uint32_t* phi, hipStream_t s) {
-    const dim3 grid(1024), block(256);
+                            PhiTables phi, hipStream_t s) {
+    const dim3 grid(512), block(256);
     if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_cdf_table<kBF16, kBF16>), grid, block, 0, s, mu, sigma, pairs, tn, tw, prefix, out, phi);
     else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_cdf_table<kBF16, kF32>), grid, block, 0, s, mu, sigma, pairs, tn, tw, prefix, out, phi);
     else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_cdf_table<kE4M3, kBF16>), grid, block, 0, s, mu, sigma, pairs, tn, tw, prefix, out, phi);

@@ -26,7 +26,7 @@ ENCODE_STAGES = 4     # side-information checksum, coding kernel, size scan, com
 DECODE_STAGES = 2     # side-information checksum, decoding kernel
 
 EXPORTS = [
-    "kvc_version", "kvc_status_string", "kvc_phi_table", "kvc_encode_sizes", "kvc_encode",
+    "kvc_version", "kvc_status_string", "kvc_phi_tables", "kvc_encode_sizes", "kvc_encode",
     "kvc_stream_info", "kvc_decode", "kvc_calibrate_sigma", "kvc_build_marginal",
     "kvc_estimate_bits", "kvc_cdf_table",
 ]
@@ -45,6 +45,15 @@ class kvc_params(ctypes.Structure):
     ]
 
 
+class kvc_encode_info(ctypes.Structure):
+    _fields_ = [("stage_ms", ctypes.c_float * 4)]
+
+
+class kvc_decode_info(ctypes.Structure):
+    _fields_ = [("stage_ms", ctypes.c_float * 2), ("reserved", ctypes.c_uint32),
+                ("fallback_symbols", ctypes.c_uint64)]
+
+
 _P = ctypes.c_void_p
 _U64 = ctypes.c_uint64
 _I64 = ctypes.c_int64
@@ -61,7 +70,7 @@ def _sig(name, res, args):
 
 _lib_version = _sig("kvc_version", ctypes.c_int, [])
 _lib_status_string = _sig("kvc_status_string", ctypes.c_char_p, [ctypes.c_int])
-_lib_phi_table = _sig("kvc_phi_table", ctypes.c_int, [_P])
+_lib_phi_tables = _sig("kvc_phi_tables", ctypes.c_int, [_P, _P])
 _lib_encode_sizes = _sig("kvc_encode_sizes", ctypes.c_int, [ctypes.POINTER(kvc_params), ctypes.POINTER(_U64), ctypes.POINTER(_U64)])
 _lib_encode = _sig("kvc_encode", ctypes.c_int, [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _U64, ctypes.POINTER(_U64), _P, _U64, _P, _P])
 _lib_stream_info = _sig("kvc_stream_info", ctypes.c_int, [_P, _U64, ctypes.POINTER(kvc_params), ctypes.POINTER(_U64)])
@@ -122,10 +131,12 @@ def kvc_status_string(status: int) -> str:
     return _lib_status_string(status).decode()
 
 
-def kvc_phi_table() -> np.ndarray:
-    out = np.zeros(4098, dtype=np.uint32)
-    _check(_lib_phi_table(out.ctypes.data), "kvc_phi_table")
-    return out
+def kvc_phi_tables():
+    """(narrow, wide) base tables of the library, computed on the host."""
+    a = np.zeros(12289, dtype=np.uint32)
+    b = np.zeros(12289, dtype=np.uint32)
+    _check(_lib_phi_tables(a.ctypes.data, b.ctypes.data), "kvc_phi_tables")
+    return a, b
 
 
 def make_params(kv_dtype, mu_dtype, planes, tokens, channels, weights=(9500, 300), chunk_tokens=0) -> kvc_params:
@@ -149,15 +160,15 @@ class Encoder:
         self.out = torch.empty(self.capacity, dtype=torch.uint8, device=device)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
 
-    def __call__(self, kv, mu, sigma, prefix=None, stream=None, stage_ms: list | None = None) -> torch.Tensor:
+    def __call__(self, kv, mu, sigma, prefix=None, stream=None, info: dict | None = None) -> torch.Tensor:
         n = _U64(0)
-        ms = (ctypes.c_float * ENCODE_STAGES)() if stage_ms is not None else None
+        inf = kvc_encode_info() if info is not None else None
         st = _lib_encode(ctypes.byref(self.p), _ptr(kv), _ptr(mu), _ptr(sigma), _ptr(prefix),
                          _ptr(self.out), self.capacity, ctypes.byref(n), _ptr(self.workspace),
-                         self.workspace.numel(), _stream(stream), ms)
+                         self.workspace.numel(), _stream(stream), ctypes.byref(inf) if inf is not None else None)
         _check(st, "kvc_encode")
-        if ms is not None:
-            stage_ms[:] = list(ms)
+        if inf is not None:
+            info["stage_ms"] = list(inf.stage_ms)
         return self.out[: n.value]
 
 
@@ -208,14 +219,16 @@ def kvc_decode(stream_bytes: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor
 
 
 def kvc_decode_into(stream_bytes, mu, sigma, prefix, kv_out, workspace, stream=None,
-                    stage_ms: list | None = None) -> int:
+                    info: dict | None = None) -> int:
     """Decode without reading the header on the Python side; returns the
     status instead of raising (for timing loops and error-path tests)."""
-    ms = (ctypes.c_float * DECODE_STAGES)() if stage_ms is not None else None
+    inf = kvc_decode_info() if info is not None else None
     st = _lib_decode(_ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _ptr(sigma), _ptr(prefix),
-                     _ptr(kv_out), _ptr(workspace), workspace.numel(), _stream(stream), ms)
-    if ms is not None:
-        stage_ms[:] = list(ms)
+                     _ptr(kv_out), _ptr(workspace), workspace.numel(), _stream(stream),
+                     ctypes.byref(inf) if inf is not None else None)
+    if inf is not None:
+        info["stage_ms"] = list(inf.stage_ms)
+        info["fallback_symbols"] = inf.fallback_symbols
     return st
 
 

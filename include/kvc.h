@@ -59,6 +59,20 @@ enum { KVC_BF16 = 0, KVC_E4M3 = 1, KVC_F32 = 2 };   /* E4M3 = OCP float8 e4m3fn 
 #define KVC_ENCODE_STAGES 4
 #define KVC_DECODE_STAGES 2
 
+/* Optional per-call measurements (pass NULL to skip; costs a few events). */
+typedef struct kvc_encode_info {
+    float stage_ms[KVC_ENCODE_STAGES];  /* GPU time of: side-information checksum,
+                                           coding kernel, size scan, compaction   */
+} kvc_encode_info;
+
+typedef struct kvc_decode_info {
+    float stage_ms[KVC_DECODE_STAGES];  /* GPU time of: side-information checksum,
+                                           decoding kernel                        */
+    uint32_t reserved;
+    uint64_t fallback_symbols;          /* symbols the decoder's aimed search
+                                           missed and found by bisection          */
+} kvc_decode_info;
+
 typedef struct kvc_params {
     int32_t kv_dtype;        /* KVC_BF16 or KVC_E4M3                               */
     int32_t mu_dtype;        /* KVC_BF16 or KVC_F32                                */
@@ -66,7 +80,8 @@ typedef struct kvc_params {
     uint32_t w_wide_bp;      /* weight of N(mu, (3 sigma)^2), basis points: 300     */
                              /* the escape part p_hat gets 10000 - both; (10000, 0)
                                 is a single Gaussian and needs no prefix table     */
-    uint32_t chunk_tokens;   /* tokens per chunk; 0 = min(tokens, 1024)            */
+    uint32_t chunk_tokens;   /* tokens per chunk; 0 = min(tokens, 1024);
+                                chunk_tokens * channels < 2^31                  */
     uint32_t reserved;       /* must be 0                                          */
     int64_t planes;          /* G = layers * 2 * batch * kv_heads                  */
     int64_t tokens;          /* T                                                  */
@@ -80,11 +95,13 @@ int kvc_version(void);
 const char* kvc_status_string(int status);
 
 /*
- * Integer standard-normal CDF table of the format, computed on the host:
- * h_out[k] = round(2^31 * Phi(-8 + k/256)) for k = 0..4096, h_out[4097] =
- * h_out[4096].  Needs no GPU.  Returns KVC_ERR_INVALID for a NULL pointer.
+ * The format's two standard-normal CDF tables on the grid z_k = -24 + k/256,
+ * k = 0..12288, computed on the host: h_narrow[k] = round(2^31 Phi(z_k)) and
+ * h_wide[k] = round(2^31 Phi(z_k / 3)).  The mixture table the coder uses is
+ * floor(T_n h_narrow[k] / 2^31) + floor(T_w h_wide[k] / 2^31).  Needs no GPU.
+ * Returns KVC_ERR_INVALID for a NULL pointer.
  */
-int kvc_phi_table(uint32_t* h_out /* [4098] */);
+int kvc_phi_tables(uint32_t* h_narrow /* [12289] */, uint32_t* h_wide /* [12289] */);
 
 /*
  * Sizes for kvc_encode: the largest stream the call can produce (every
@@ -99,18 +116,17 @@ int kvc_encode_sizes(const kvc_params* p, uint64_t* h_max_stream_bytes,
  * coder, which emits the bits).  Codes d_kv (bf16 or e4m3 bit patterns) under
  * the mixture around d_mu with d_sigma and the marginal prefix d_prefix
  * (NULL allowed when w_narrow_bp + w_wide_bp == 10000).  Writes the stream
- * to d_out and its length to *h_out_bytes.  sigma must be finite and
- * positive with a finite reciprocal, else KVC_ERR_INVALID.  If the stream
+ * to d_out and its length to *h_out_bytes.  Every sigma must lie in
+ * [2^-96, 2^96], else KVC_ERR_INVALID.  If the stream
  * does not fit out_capacity the call returns KVC_ERR_CAPACITY and sets
  * *h_out_bytes to the size it needed.  Synchronises `stream` once.
- * h_stage_ms: NULL, or KVC_ENCODE_STAGES floats that receive the GPU time in
- * milliseconds of each stage (side-information checksum, coding kernel,
- * size scan, compaction), measured with HIP events on `stream`.
+ * h_info: NULL, or receives the GPU time of each stage, measured with HIP
+ * events on `stream`.
  */
 int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu,
                const float* d_sigma, const uint32_t* d_prefix, void* d_out,
                uint64_t out_capacity, uint64_t* h_out_bytes, void* d_workspace,
-               uint64_t workspace_bytes, void* stream, float* h_stage_ms);
+               uint64_t workspace_bytes, void* stream, kvc_encode_info* h_info);
 
 /*
  * Parse the 128-byte stream header held in HOST memory into *h_params and
@@ -129,13 +145,13 @@ int kvc_stream_info(const void* h_header, uint64_t header_bytes, kvc_params* h_p
  * KVC_ERR_CORRUPT if the stream is malformed, truncated or damaged (every
  * lane must end in the initial state and consume exactly its chunk).
  * Workspace: KVC_DECODE_WORKSPACE_BYTES.  Synchronises `stream` twice
- * (header read, status read).  h_stage_ms: NULL, or KVC_DECODE_STAGES
- * floats (side-information checksum, decoding kernel), as for kvc_encode.
+ * (header read, status read).  h_info: NULL, or receives the stage times
+ * and the number of symbols found by the fallback search.
  */
 int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu,
                const float* d_sigma, const uint32_t* d_prefix, void* d_kv_out,
                void* d_workspace, uint64_t workspace_bytes, void* stream,
-               float* h_stage_ms);
+               kvc_decode_info* h_info);
 
 /*
  * Sigma calibration ([wiki] "predictor choice": per-(kv, head, channel)

@@ -16,8 +16,9 @@ Parity status of each function (what pins it other than itself):
   order_index / bits_of_order  -- brute force over every bit pattern, torch's
                                   own bf16 / float8_e4m3fn decoders
   boundary_positions           -- exact midpoint identity in float64
-  phi_table                    -- scipy.special.ndtr, symmetry, closed values
-  cdf                          -- invariants (C(0)=0, C(N)=M, f>=1) and the
+  phi_tables / mixture_table  -- scipy.special.ndtr, symmetry, closed values,
+                                  the wide table against the narrow one at z/3
+  h_fx / cdf                   -- invariants (C(0)=0, C(N)=M, f>=1) and the
                                   continuous mixture within a derived bound
   encode / decode              -- round trip, exact size band, unbounded
                                   big-integer rANS

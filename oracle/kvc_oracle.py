@@ -32,7 +32,7 @@ import numpy as np
 __all__ = [
     "BF16", "E4M3", "F32", "M", "L", "LANES", "HEADER_BYTES", "STATE_BYTES", "StreamError",
     "alphabet_size", "budgets", "order_index", "bits_of_order", "symbol_value",
-    "boundary_positions", "phi_table", "phi_fx", "mu_to_f32", "cdf",
+    "boundary_positions", "phi_tables", "mixture_table", "h_fx", "mu_to_f32", "cdf",
     "cdf_table", "build_marginal", "calibrate_sigma", "side_hash", "encode",
     "decode", "parse_header", "model_bits_int", "model_bits_float",
     "chunk_layout",
@@ -172,46 +172,58 @@ def boundary_positions(dtype: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# S-4  integer standard-normal CDF
+# S-4  integer mixture table
 # ---------------------------------------------------------------------------
-PHI_STEPS_PER_UNIT = 256
-PHI_Z_MIN = -8
+TABLE_STEPS_PER_UNIT = 256          # z grid step 1/256
+TABLE_Z_MAX = 24                    # z grid covers [-24, 24]
+TABLE_POINTS = 2 * TABLE_Z_MAX * TABLE_STEPS_PER_UNIT + 1    # 12289
 
 
 @functools.lru_cache(maxsize=None)
-def phi_table() -> np.ndarray:
-    """T[k] = round(2^31 * Phi(-8 + k/256)) for k = 0..4096, T[4097] = T[4096].
-
-    Phi is the standard normal CDF, written as 1/2 erfc(-x / sqrt 2) and
-    evaluated with mpmath at 50 significant digits.  No entry is a tie: the
-    fractional parts stay well clear of 1/2 (a test checks the margin).
-    """
+def phi_tables():
+    """Base tables of the standard normal CDF Phi on the z grid
+    z_k = -24 + k/256, k = 0..12288:
+      A[k] = round(2^31 Phi(z_k))      (the N(mu, sigma^2) part),
+      B[k] = round(2^31 Phi(z_k / 3))  (the N(mu, (3 sigma)^2) part).
+    Phi(x) = erfc(-x / sqrt 2) / 2, evaluated with mpmath at 50 digits; no
+    entry lies near a rounding tie (a test checks the margin)."""
     import mpmath
 
-    out = []
+    a, b = [], []
     with mpmath.workdps(50):
         two31 = mpmath.mpf(2) ** 31
         half = mpmath.mpf(1) / 2
-        for k in range(4097):
-            x = mpmath.mpf(PHI_Z_MIN) + mpmath.mpf(k) / PHI_STEPS_PER_UNIT
-            phi = mpmath.erfc(-x / mpmath.sqrt(2)) / 2
-            out.append(int(mpmath.floor(two31 * phi + half)))
-    out.append(out[-1])
-    return np.array(out, dtype=np.int64)
+        r2 = mpmath.sqrt(2)
+        for k in range(TABLE_POINTS):
+            z = mpmath.mpf(-TABLE_Z_MAX) + mpmath.mpf(k) / TABLE_STEPS_PER_UNIT
+            a.append(int(mpmath.floor(two31 * mpmath.erfc(-z / r2) / 2 + half)))
+            b.append(int(mpmath.floor(two31 * mpmath.erfc(-(z / 3) / r2) / 2 + half)))
+    return np.array(a, dtype=np.int64), np.array(b, dtype=np.int64)
 
 
-def phi_fx(q) -> np.ndarray:
-    """Integer Phi of z = q / 2^24 for q in [-2^27, 2^27] (z in [-8, 8]):
-    table lookup at step 1/256 plus integer linear interpolation."""
+@functools.lru_cache(maxsize=None)
+def mixture_table(t_n: int, t_w: int) -> np.ndarray:
+    """H[k] = floor(T_n A[k] / 2^31) + floor(T_w B[k] / 2^31): the two
+    Gaussian parts of the mixture, in integer budget units, on the z grid;
+    H[12289] repeats H[12288] so that interpolation may read one past the
+    end."""
+    a, b = phi_tables()
+    h = ((t_n * a) >> 31) + ((t_w * b) >> 31)
+    return np.concatenate([h, h[-1:]])
+
+
+def h_fx(q, table) -> np.ndarray:
+    """Integer mixture CDF of z = q / 2^24, q in [-24 2^24, 24 2^24]: table
+    lookup at step 1/256 with integer linear interpolation over the 16 low
+    bits."""
     q = np.asarray(q).astype(np.int64)
-    if np.any(np.abs(q) > (1 << 27)):
-        raise ValueError("phi_fx argument out of range")
-    tab = phi_table()
-    u = q + (1 << 27)
+    if np.any(np.abs(q) > TABLE_Z_MAX << 24):
+        raise ValueError("h_fx argument out of range")
+    u = q + (TABLE_Z_MAX << 24)
     i = u >> 16
     r = u & 0xFFFF
-    lo = tab[i]
-    hi = tab[i + 1]
+    lo = table[i]
+    hi = table[i + 1]
     return lo + (((hi - lo) * r) >> 16)
 
 
@@ -236,10 +248,9 @@ def cdf(b, mu32, inv32, dtype: int, t_n: int, t_w: int, prefix=None) -> np.ndarr
 
     S-3  d = pos(b) - mu and z = d * (1/sigma), each one IEEE float32 operation;
          z clamped to [-24, 24]; q = round-half-even(z * 2^24).
-    S-5  narrow part uses q clamped to [-2^27, 2^27] (z in [-8, 8]); the wide
-         part (standard deviation 3 sigma) uses floor(q / 3); the escape part
-         is the integer prefix of the marginal, prefix[b].
-         C(b) = b + floor(T_n Phi(q1) / 2^31) + floor(T_w Phi(q3) / 2^31) + prefix[b].
+    S-5  C(b) = b + h_fx(q) + prefix[b]: the +1 floor of every symbol below b,
+         both Gaussian parts through the mixture table, and the escape part
+         as the integer prefix of the marginal.
     """
     b = np.asarray(b).astype(np.int64)
     pos = boundary_positions(dtype)[b]
@@ -248,24 +259,26 @@ def cdf(b, mu32, inv32, dtype: int, t_n: int, t_w: int, prefix=None) -> np.ndarr
     with np.errstate(over="ignore", invalid="raise"):
         d = (pos - mu32).astype(np.float32)
         z = (d * inv32).astype(np.float32)
-    z = np.clip(z, np.float32(-24.0), np.float32(24.0)).astype(np.float32)
+    z = np.clip(z, np.float32(-TABLE_Z_MAX), np.float32(TABLE_Z_MAX)).astype(np.float32)
     q = np.rint(z * np.float32(1 << 24)).astype(np.int64)
-    q1 = np.clip(q, -(1 << 27), 1 << 27)
-    q3 = q // 3                                   # floor division
-    g = ((t_n * phi_fx(q1)) >> 31) + ((t_w * phi_fx(q3)) >> 31)
+    g = h_fx(q, mixture_table(t_n, t_w))
     if prefix is not None:
         g = g + np.asarray(prefix, dtype=np.int64)[b]
     return b + g
 
 
+SIGMA_MIN = np.float32(2.0 ** -96)
+SIGMA_MAX = np.float32(2.0 ** 96)
+
+
 def _inv_sigma(sigma) -> np.ndarray:
+    """float32 1/sigma.  Reading: sigma must lie in [2^-96, 2^96] (a KV
+    residual scale far outside that range is not a calibration result)."""
     s = np.asarray(sigma, dtype=np.float32)
-    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
-        inv = (np.float32(1.0) / s).astype(np.float32)
-    ok = np.isfinite(s) & (s > 0) & np.isfinite(inv)
+    ok = (s >= SIGMA_MIN) & (s <= SIGMA_MAX)
     if not np.all(ok):
-        raise ValueError("sigma must be finite, positive, with a finite reciprocal")
-    return inv
+        raise ValueError("sigma must lie in [2^-96, 2^96]")
+    return (np.float32(1.0) / s).astype(np.float32)
 
 
 def cdf_table(mu, sigma, dtype: int, mu_dtype: int, w_narrow_bp: int,

@@ -1,0 +1,44 @@
+"""A float32 model of the encoder's division routine (floor(x / f) and
+x mod f for x < 2^32 f without a hardware divider): a float estimate of the
+quotient, one float correction from the remainder, and one integer
+adjustment.  The model runs the same steps with NumPy float32 and checks
+them against exact integer division at the extremes of f and x, with the
+reciprocal perturbed by up to two ulps (the hardware reciprocal is not
+correctly rounded)."""
+import numpy as np
+import pytest
+
+f32 = np.float32
+
+
+def divmod_model(x: int, f: int, ulps: int):
+    rf = f32(1.0) / f32(f)
+    for _ in range(abs(ulps)):
+        rf = np.nextafter(rf, f32(np.inf if ulps > 0 else -np.inf))
+    xh, xl = x >> 32, x & 0xFFFFFFFF
+    fx = f32(float(f32(xh)) * 4294967296.0 + float(f32(xl)))          # one fma rounding
+    q0 = int(min(max(f32(fx * rf), f32(0.0)), f32(4294967040.0)))
+    r0 = x - q0 * f
+    assert abs(r0) < 2 ** 42
+    hi, lo = r0 >> 21, r0 & 0x1FFFFF                                    # both exact in float32
+    fr0 = f32(float(f32(hi)) * 2097152.0 + float(f32(lo)))
+    q1 = min(q0 + int(np.floor(f32(fr0 * rf))), 0xFFFFFFFF)
+    r1 = x - q1 * f
+    assert -f <= r1 < 2 * f
+    if r1 < 0:
+        q1, r1 = q1 - 1, r1 + f
+    if r1 >= f:
+        q1, r1 = q1 + 1, r1 - f
+    return q1, r1
+
+
+@pytest.mark.parametrize("ulps", [-2, 0, 2])
+def test_division_model_is_exact(ulps):
+    rng = np.random.default_rng(3 + ulps)
+    fs = [1, 2, 3, 5, 40, 255, 256, 257, 65535, 65536, 2 ** 24 - 1, 2 ** 24 + 1, 2 ** 31 - 65535,
+          2 ** 31 - 1] + [int(v) for v in rng.integers(1, 2 ** 31, 24)]
+    for f in fs:
+        lo, hi = 2 ** 16 * f, min(2 ** 32 * f, 2 ** 63)        # the coder's range of x
+        xs = [lo, lo + 1, hi - 1, hi - 2] + [int(v) for v in rng.integers(lo, hi, 300, dtype=np.uint64)]
+        for x in xs:
+            assert divmod_model(x, f, ulps) == divmod(x, f), (x, f)

@@ -51,7 +51,7 @@ def tiny(kv_dtype, seed=7, planes=3, tokens=45, channels=128):
 def adversarial_pairs(rng, n_random):
     mus = [0.0, -0.0, 1e-40, -1e-40, 3.0e38, -3.0e38, 1.5, -2.75, 0.001, 1e4, np.nan, np.inf, -np.inf,
            0.998046875, 448.0, -448.0, 0.0, 2.0 ** -133, 0.5 * (1 + 2 ** -8)]
-    sig = [1e-3, 2.0 ** -30, 2.0 ** -30, 1e-38, 1.0, 1e30, 2.0 ** -4, 0.37, 10.0, 2.0 ** -7, 0.5, 0.5, 0.5,
+    sig = [1e-3, 2.0 ** -30, 2.0 ** -30, 2.0 ** -96, 1.0, 2.0 ** 96, 2.0 ** -4, 0.37, 10.0, 2.0 ** -7, 0.5, 0.5, 0.5,
            2.0 ** -12, 2.0, 0.01, 1e4, 2.0 ** -20, 2.0 ** -9]
     m = np.concatenate([np.float32(mus), (rng.standard_normal(n_random) * np.exp(rng.normal(0, 2, n_random))).astype(np.float32)])
     s = np.concatenate([np.float32(sig), np.exp2(rng.uniform(-30, 8, n_random)).astype(np.float32)])
@@ -87,7 +87,7 @@ def test_cdf_table_bf16_mu(kvc, cuda):
 
 
 def test_cdf_table_rejects_bad_sigma(kvc, cuda):
-    for bad in [0.0, -1.0, float("inf"), float("nan"), 1e-45]:
+    for bad in [0.0, -1.0, float("inf"), float("nan"), 1e-45, 1e-30, 1e30]:
         with pytest.raises(kvc.KvcError) as e:
             kvc.kvc_cdf_table(kvc.KVC_E4M3, torch.zeros(2, device=cuda), torch.tensor([1.0, bad], device=cuda),
                               None, (10000, 0))
@@ -247,7 +247,7 @@ def test_error_statuses(kvc, cuda):
     assert dec(st[:-8]) == kvc.KVC_ERR_CORRUPT
     assert dec(st[:100]) == kvc.KVC_ERR_CORRUPT
     # bad sigma on encode
-    for v in [0.0, float("nan"), float("inf"), -1.0]:
+    for v in [0.0, float("nan"), float("inf"), -1.0, 1e-30, 1e30]:
         s3 = sig_d.clone()
         s3[1, 5] = v
         with pytest.raises(kvc.KvcError) as e:

@@ -104,8 +104,11 @@ def test_qwen3_0p6b_shaped_full_parity(kvc, cuda):
     assert torch.equal(out, kv.view(torch.int16))
 
 
+@pytest.mark.parametrize("wts", [(9500, 300), (10000, 0)])
 @pytest.mark.parametrize("case", ["perfect_predictor", "all_nan", "constant", "noise_predictor", "huge_sigma"])
-def test_degenerate_inputs(kvc, cuda, case):
+def test_degenerate_inputs(kvc, cuda, case, wts):
+    """Frequencies at both extremes: 1 (NaN under a single Gaussian) and
+    about 2^31 (a perfect predictor)."""
     w = W.WORKLOADS[0]
     kv, mu = W.layer_data(w, 0, tokens=130)
     sig = W.layer_sigma_true(w, 0)
@@ -121,13 +124,12 @@ def test_degenerate_inputs(kvc, cuda, case):
         mu = W.noise_predictor(w, tuple(kv.shape))
         sig = torch.full_like(sig, 2.0 ** -30)
     elif case == "huge_sigma":
-        sig = torch.full_like(sig, 1e30)
+        sig = torch.full_like(sig, 2.0 ** 96)
     samples = W.marginal_samples(w)
-    wts = (9500, 300)
-    pref = O.build_marginal(W.to_numpy_bits(samples), O.BF16, *wts)
+    pref = O.build_marginal(W.to_numpy_bits(samples), O.BF16, *wts) if wts[1] else None
     kvn, mun, sgn = W.to_numpy_bits(kv), W.to_numpy_bits(mu), sig.numpy()
     want = O.encode(kvn, mun, sgn, pref, O.BF16, O.BF16, *wts, 64)
-    pref_d = torch.from_numpy(pref.astype(np.int32)).to(cuda)
+    pref_d = torch.from_numpy(pref.astype(np.int32)).to(cuda) if pref is not None else None
     kv_d, mu_d, sig_d = kv.to(cuda), mu.to(cuda), sig.to(cuda)
     st = kvc.kvc_encode(kv_d, mu_d, sig_d, pref_d, wts, 64)
     assert st.cpu().numpy().tobytes() == want

@@ -35,9 +35,11 @@ def test_version_and_status_strings(kvc):
     assert "corrupt" in kvc.kvc_status_string(-3)
 
 
-def test_host_phi_table_equals_oracle(kvc):
+def test_host_phi_tables_equal_oracle(kvc):
     # libm erfc in double on the library side, mpmath at 50 digits in the oracle
-    assert np.array_equal(kvc.kvc_phi_table().astype(np.int64), O.phi_table())
+    a, b = kvc.kvc_phi_tables()
+    oa, ob = O.phi_tables()
+    assert np.array_equal(a.astype(np.int64), oa) and np.array_equal(b.astype(np.int64), ob)
 
 
 def test_encode_sizes(kvc):
@@ -48,7 +50,8 @@ def test_encode_sizes(kvc):
     assert max_stream == 128 + 8 * (n_chunks + 1) + n_chunks * (512 + 2 * 2 * 64 * 1024)
     assert ws >= n_chunks * (512 + 4 + 8 + 4 * 64 * 1024)
     for bad in [dict(channels=96), dict(planes=0), dict(tokens=0), dict(reserved=1), dict(kv_dtype=2),
-                dict(mu_dtype=1), dict(w_narrow_bp=9000, w_wide_bp=1001), dict(chunk_tokens=1 << 21)]:
+                dict(mu_dtype=1), dict(w_narrow_bp=9000, w_wide_bp=1001), dict(chunk_tokens=1 << 21),
+                dict(channels=1 << 21, chunk_tokens=1024)]:
         q = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, 4, 100, 128)
         for k, v in bad.items():
             setattr(q, k, v)

@@ -10,8 +10,8 @@ import oracle as O
 
 ADVERSARIAL = [
     # (mu, sigma)
-    (0.0, 1e-3), (-0.0, 2.0 ** -30), (1e-40, 2.0 ** -30), (-1e-40, 1e-38),
-    (3.0e38, 1.0), (-3.0e38, 1e30), (1.5, 2.0 ** -4), (-2.75, 0.37),
+    (0.0, 1e-3), (-0.0, 2.0 ** -30), (1e-40, 2.0 ** -30), (-1e-40, 2.0 ** -96),
+    (3.0e38, 1.0), (-3.0e38, 2.0 ** 96), (1.5, 2.0 ** -4), (-2.75, 0.37),
     (0.001, 10.0), (1e4, 2.0 ** -7), (np.nan, 0.5), (np.inf, 0.5),
     (0.998046875, 2.0 ** -12), (448.0, 2.0), (-448.0, 0.01), (0.0, 1e4),
 ]
@@ -86,7 +86,7 @@ def test_nonfinite_mu_is_treated_as_zero():
     assert np.array_equal(a, np.repeat(b, 3, axis=0))
 
 
-@pytest.mark.parametrize("bad", [0.0, -1.0, np.inf, np.nan, 1e-45])
+@pytest.mark.parametrize("bad", [0.0, -1.0, np.inf, np.nan, 1e-45, 1e-30, 1e30])
 def test_bad_sigma_rejected(bad):
     with pytest.raises(ValueError):
         O.cdf_table(np.float32([0.0]), np.float32([bad]), O.E4M3, O.F32, 10000, 0)
