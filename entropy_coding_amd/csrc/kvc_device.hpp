@@ -116,8 +116,8 @@ __device__ __forceinline__ float symbol_value(uint32_t b) {
     }
 }
 
-// Ordered index of the finite symbol nearest to x (ties to even), clamped to
-// the finite range.  Used only to aim the decoder's search.
+// Ordered index of a finite symbol near x, clamped to the finite range.
+// Used only to aim the decoder's search, so rounding details do not matter.
 template <int KV>
 __device__ __forceinline__ uint32_t nearest_symbol(float x) {
     if constexpr (KV == kBF16) {
@@ -127,15 +127,38 @@ __device__ __forceinline__ uint32_t nearest_symbol(float x) {
         b = b < Alphabet<kBF16>::kLoFinite ? Alphabet<kBF16>::kLoFinite : b;
         return b > Alphabet<kBF16>::kHiFinite ? Alphabet<kBF16>::kHiFinite : b;
     } else {
-        // bisection over the 254 finite e4m3 cells (8 steps, no memory)
-        uint32_t lo = 1, hi = 255;
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t mid = (lo + hi) >> 1;
-            const bool up = x >= edge_e4m3(mid);
-            lo = up ? mid : lo;
-            hi = up ? hi : mid;
+        // round |x| to 3 mantissa bits (normal range) or to a multiple of
+        // 2^-9 (subnormal range), saturating at 448
+        const float ax = fminf(fabsf(x), 448.0f);
+        uint32_t m;
+        if (ax < 0x1p-6f) {
+            m = static_cast<uint32_t>(__builtin_rintf(ax * 512.0f));     // 0..8 (8 = 2^-6)
+        } else {
+            const uint32_t u = __float_as_uint(ax);
+            const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;    // 8-bit exponent, 3-bit mantissa
+            m = r - (120u << 3);
         }
-        return lo;
+        m = m > 126u ? 126u : m;
+        const uint32_t bits = m | (x < 0.0f ? 0x80u : 0u);
+        return order_of_bits<kE4M3>(bits);
+    }
+}
+
+// Index of the cell edge nearest to x (within one cell; the decoder only
+// aims with it), clamped so that it and both neighbours are valid indices.
+// bf16 edges sit at fp32 patterns m * 2^16 + 2^15, so the nearest is m =
+// pattern >> 16 on either sign.
+template <int KV>
+__device__ __forceinline__ uint32_t nearest_edge(float x) {
+    if constexpr (KV == kBF16) {
+        const uint32_t u = __float_as_uint(x);
+        const uint32_t m = (u & 0x7FFFFFFFu) >> 16;
+        uint32_t e = (u >> 31) ? 32767u - m : 32769u + m;
+        e = e < Alphabet<kBF16>::kLoFinite ? Alphabet<kBF16>::kLoFinite : e;
+        return e > Alphabet<kBF16>::kHiFinite + 1u ? Alphabet<kBF16>::kHiFinite + 1u : e;
+    } else {
+        const uint32_t jb = nearest_symbol<kE4M3>(x);
+        return jb + (x > symbol_value<kE4M3>(jb) ? 1u : 0u);
     }
 }
 

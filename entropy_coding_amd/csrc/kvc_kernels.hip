@@ -83,23 +83,6 @@ __device__ __forceinline__ void build_table_lds(uint32_t* s_tab, const PhiTables
     __syncthreads();
 }
 
-// Inverse index of the mixture table for the decoder's aim: inv[j] is the
-// largest k with H[k] <= floor(j * (T_n + T_w) / kInvSteps).
-constexpr int kInvSteps = 4096;
-__device__ __forceinline__ void build_inverse_lds(uint16_t* s_inv, const uint32_t* s_tab, uint32_t htot) {
-    for (int j = threadIdx.x; j <= kInvSteps; j += blockDim.x) {
-        const uint32_t thr = static_cast<uint32_t>((static_cast<uint64_t>(htot) * j) / kInvSteps);
-        uint32_t lo = 0, hi = kTablePoints;          // H[lo] <= thr, search in [lo, hi)
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (s_tab[mid] <= thr) lo = mid;
-            else hi = mid;
-        }
-        s_inv[j] = static_cast<uint16_t>(lo);
-    }
-    __syncthreads();
-}
-
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;
@@ -399,95 +382,181 @@ hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream
 }
 
 // ---------------------------------------------------------------------------
-// decoder: one wave per chunk, tokens first to last.  The symbol is aimed
-// at through the inverse of the mixture table (the escape and floor terms
-// taken at the predictor's own symbol), the nearest cell edge E and one of
-// its neighbours are evaluated, and a bisection inside the known bracket
-// handles the rare misses; the search result is checked exactly either way.
+// decoder: one wave per chunk, tokens first to last.
+//
+// Finding the symbol s with C(s) <= target < C(s+1): C(b) = Q(b) + H(z_b)
+// with Q(b) = b + prefix[b] (floor and escape mass) and H the mixture
+// table.  The aim inverts H through a float table of z at evenly spaced
+// values of H, once with Q taken at the predictor's own symbol and once
+// with Q at the first guess; the edge E nearest the aimed position and one
+// neighbour are evaluated exactly.  Lanes that still miss (tail symbols,
+// under one in a hundred) are resolved one at a time by the whole wave: 63
+// lanes probe the missing lane's bracket at once (geometrically spaced from
+// the known end first, then evenly), so any miss takes two or three rounds.
+// The result is exact whatever the aim; the aim only sets the cost.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeBlock = 1024;
+constexpr int kDecodeBatch = 4;
+constexpr int kZinvSteps = 4096;
 
-template <int KV>
-struct DecodeModel {
-    Model m;
-    const uint16_t* __restrict__ inv;      // inverse index in LDS
-    uint32_t htot;                         // T_n + T_w
-    float inv_scale;                       // kInvSteps / htot
-};
-
-// Find s with C(s) <= target < C(s + 1); returns s, start and frequency.
-template <int KV>
-__device__ __forceinline__ uint32_t decode_symbol(uint32_t target, float mu, float sg, float inv24, uint32_t bias,
-                                                  const DecodeModel<KV>& dm, uint32_t& start, uint32_t& freq,
-                                                  uint32_t& misses) {
-    constexpr uint32_t N = Alphabet<KV>::kSize;
-    uint32_t E;
-    if (dm.htot) {
-        // aim: e = target minus the floor and escape mass below mu's symbol
-        int32_t e = static_cast<int32_t>(target) - static_cast<int32_t>(bias);
-        e = e < 0 ? 0 : e;
-        const uint32_t eu = static_cast<uint32_t>(e) < dm.htot ? static_cast<uint32_t>(e) : dm.htot - 1u;
-        int j = static_cast<int>(static_cast<float>(eu) * dm.inv_scale);
-        const int jl = j > 0 ? j - 1 : 0;
-        const int jh = j + 2 < kInvSteps ? j + 2 : kInvSteps;
-        uint32_t lo = dm.inv[jl];
-        uint32_t hi = static_cast<uint32_t>(dm.inv[jh]) + 1u;
-        hi = hi < static_cast<uint32_t>(kTablePoints - 1) ? hi : static_cast<uint32_t>(kTablePoints - 1);
-        while (hi - lo > 1) {                       // H[lo] <= eu < H[hi]
+// zinv[j] = z at which the (interpolated) mixture table reaches
+// floor(j * htot / kZinvSteps).
+__device__ __forceinline__ void build_zinv_lds(float* s_zinv, const uint32_t* s_tab, uint32_t htot) {
+    for (int j = threadIdx.x; j <= kZinvSteps; j += blockDim.x) {
+        const uint32_t e = static_cast<uint32_t>((static_cast<uint64_t>(htot) * j) / kZinvSteps);
+        uint32_t lo = 0, hi = kTablePoints;           // largest k with H[k] <= e
+        while (hi - lo > 1) {
             const uint32_t mid = (lo + hi) >> 1;
-            if (dm.m.tab[mid] <= eu) lo = mid;
+            if (s_tab[mid] <= e) lo = mid;
             else hi = mid;
         }
-        const uint32_t h0 = dm.m.tab[lo], h1 = dm.m.tab[lo + 1];
-        const float frac = static_cast<float>(eu - h0) * __builtin_amdgcn_rcpf(static_cast<float>(h1 - h0));
-        const float zf = (static_cast<float>(lo) + frac) * (1.0f / 256.0f) - static_cast<float>(kTableZMax);
-        const float pos = __fmaf_rn(zf, sg, mu);
-        const uint32_t jb = nearest_symbol<KV>(pos);
-        E = jb + (pos > symbol_value<KV>(jb) ? 1u : 0u);
-    } else {
-        E = nearest_symbol<KV>(mu);
-    }
-    const uint32_t cE = cdf_at<KV>(E, mu, inv24, dm.m);
-    const bool up = target >= cE;
-    const uint32_t E2 = up ? E + 1u : E - 1u;
-    const uint32_t c2 = cdf_at<KV>(E2, mu, inv24, dm.m);
-    const bool ok = up ? (target < c2) : (target >= c2);
-    uint32_t s = up ? E : E2;
-    start = up ? cE : c2;
-    freq = up ? c2 - cE : cE - c2;
-    if (__ballot(!ok)) {
-        // bracket [lo, hi) with C(lo) <= target < C(hi) from what is known
-        uint32_t lo = up ? E2 : 0u, hi = up ? N : E2;
-        uint32_t clo = up ? c2 : 0u, chi = up ? kM : c2;
-        bool need = !ok;
-        misses += need ? 1u : 0u;
-        for (int it = 0; it <= Alphabet<KV>::kLog2 && __ballot(need && hi - lo > 1); ++it) {
-            if (need && hi - lo > 1) {
-                const uint32_t mid = (lo + hi) >> 1;
-                const uint32_t cm = cdf_at<KV>(mid, mu, inv24, dm.m);
-                if (cm <= target) { lo = mid; clo = cm; }
-                else { hi = mid; chi = cm; }
-            }
+        float z;
+        if (lo >= static_cast<uint32_t>(kTablePoints - 1)) {
+            z = static_cast<float>(kTableZMax);
+        } else {
+            const float fr = static_cast<float>(e - s_tab[lo]) / static_cast<float>(s_tab[lo + 1] - s_tab[lo]);
+            z = (static_cast<float>(lo) + fr) * (1.0f / 256.0f) - static_cast<float>(kTableZMax);
         }
-        if (need) {
-            s = lo;
-            start = clo;
-            freq = chi - clo;
-        }
+        s_zinv[j] = z;
     }
-    return s;
+    __syncthreads();
 }
+
+struct Aim {
+    const float* __restrict__ zinv;    // LDS
+    float scale;                       // kZinvSteps / htot (0 when there is no Gaussian part)
+    int32_t htot;
+};
+
+// Nearest cell edge to the position where H reaches `e`.
+template <int KV>
+__device__ __forceinline__ uint32_t aim_edge(int32_t e, float mu, float sg, const Aim& a) {
+    e = e < 0 ? 0 : (e > a.htot ? a.htot : e);
+    const float ef = static_cast<float>(e) * a.scale;
+    const float jf = fminf(__builtin_floorf(ef), static_cast<float>(kZinvSteps - 1));
+    const int j = static_cast<int>(jf);
+    const float fr = ef - jf;
+    const float z0 = a.zinv[j], z1 = a.zinv[j + 1];
+    const float z = __fmaf_rn(fr, z1 - z0, z0);
+    return nearest_edge<KV>(__fmaf_rn(z, sg, mu));
+}
+
+// Probe offsets for the first cooperative round: 1, 2, 3, ... then growing
+// geometrically to 65535 over the 63 probing lanes.
+__device__ __forceinline__ uint32_t geo_offset(int lane) {
+    const float g = __builtin_amdgcn_exp2f(static_cast<float>(lane) * (16.0f / 62.0f));
+    const uint32_t o = static_cast<uint32_t>(g);
+    return o > static_cast<uint32_t>(lane + 1) ? o : static_cast<uint32_t>(lane + 1);
+}
+
+struct Found {
+    uint32_t s, start, freq;
+};
+
+// The whole wave resolves every lane with `need` set, one lane at a time.
+// [lo, hi) brackets the lane's symbol with C(lo) = clo <= target < C(hi) = chi;
+// `up` tells which end is the known near one (lo if up).
+template <int KV>
+__device__ __forceinline__ void coop_search(bool need, uint32_t target, float mu, float inv24, bool up, uint32_t lo,
+                                            uint32_t hi, uint32_t clo, uint32_t chi, const Model& m, uint32_t geo,
+                                            Found& out) {
+    const int lane = threadIdx.x & 63;
+    uint64_t pend = __ballot(need);
+    while (pend) {
+        const int L = __builtin_ctzll(pend);
+        pend &= pend - 1;
+        const uint32_t t = __builtin_amdgcn_readlane(target, L);
+        const float mL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mu), L));
+        const float iL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv24), L));
+        const bool upL = __builtin_amdgcn_readlane(static_cast<int>(up), L) != 0;
+        uint32_t a = __builtin_amdgcn_readlane(lo, L), b = __builtin_amdgcn_readlane(hi, L);
+        uint32_t ca = __builtin_amdgcn_readlane(clo, L), cb = __builtin_amdgcn_readlane(chi, L);
+        bool first = true;
+        for (int round = 0; round < 8 && b - a > 1; ++round) {
+            const uint32_t span = b - a;
+            const bool geometric = first && span > 64u;
+            uint32_t p;
+            if (geometric) {
+                const uint32_t off = geo < span - 1u ? geo : span - 1u;
+                p = upL ? a + off : b - off;
+            } else {
+                p = a + static_cast<uint32_t>((static_cast<uint64_t>(lane + 1) * span) >> 6);
+            }
+            const bool valid = lane < 63 && p > a && p < b;
+            const uint32_t c = cdf_at<KV>(valid ? p : a, mL, iL, m);
+            const uint64_t mle = __ballot(valid && c <= t);
+            const uint64_t mgt = __ballot(valid && c > t);
+            // probe positions increase with the lane, except geometric probes
+            // taken down from the upper end
+            const bool rising = !(geometric && !upL);
+            if (mle) {
+                const int k = rising ? 63 - __builtin_clzll(mle) : __builtin_ctzll(mle);
+                a = __builtin_amdgcn_readlane(p, k);
+                ca = __builtin_amdgcn_readlane(c, k);
+            }
+            if (mgt) {
+                const int k = rising ? __builtin_ctzll(mgt) : 63 - __builtin_clzll(mgt);
+                b = __builtin_amdgcn_readlane(p, k);
+                cb = __builtin_amdgcn_readlane(c, k);
+            }
+            first = false;
+        }
+        if (lane == L) {
+            out.s = a;
+            out.start = ca;
+            out.freq = cb - ca;
+        }
+    }
+}
+
+// Stream words of a chunk, held two 128-word blocks at a time across the
+// wave's registers (one dword of each block per lane) and read with a lane
+// permute; the next block is loaded as soon as the current one is entered,
+// so no memory read sits on the serial decode chain.
+struct WordWindow {
+    const uint32_t* __restrict__ dw;   // chunk words as dwords (8-byte aligned)
+    uint32_t n_dw;                     // dwords in the chunk's word area
+    uint32_t base;                     // first word of the current block
+    uint32_t cur, nxt;                 // this lane's dword of the current / next block
+
+    __device__ __forceinline__ uint32_t load(uint32_t block, int lane) const {
+        const uint32_t d = block * 64u + static_cast<uint32_t>(lane);
+        return d < n_dw ? dw[d] : 0u;
+    }
+    __device__ __forceinline__ void init(int lane) {
+        base = 0;
+        cur = load(0, lane);
+        nxt = load(1, lane);
+    }
+    // word p, base <= p < base + 256; called with the whole wave active
+    __device__ __forceinline__ uint32_t word(uint32_t p) const {
+        const uint32_t rel = p - base;
+        const int src = static_cast<int>((rel >> 1) & 63u) << 2;
+        const uint32_t v0 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(cur)));
+        const uint32_t v1 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(nxt)));
+        const uint32_t v = (rel & 128u) ? v1 : v0;
+        return (rel & 1u) ? (v >> 16) : (v & 0xFFFFu);
+    }
+    __device__ __forceinline__ void advance(uint32_t rp, int lane) {
+        if (rp >= base + 128u) {                       // wave-uniform
+            cur = nxt;
+            base += 128u;
+            nxt = load((base >> 7) + 1u, lane);
+        }
+    }
+};
 
 template <int KV, int MU>
 __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
     __shared__ uint32_t s_tab[kTableEntries];
-    __shared__ uint16_t s_inv[kInvSteps + 1];
+    __shared__ float s_zinv[kZinvSteps + 1];
     build_table_lds(s_tab, a.phi, a.tn, a.tw);
     const uint32_t htot = a.tn + a.tw;
-    if (htot) build_inverse_lds(s_inv, s_tab, htot);
+    if (htot) build_zinv_lds(s_zinv, s_tab, htot);
 
     const int lane = threadIdx.x & 63;
-    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (kDecodeBlock / 64) + (threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (kDecodeBlock / 64) + wave;
     if (chunk >= a.geom.n_chunks) return;
     const ChunkPos cp = chunk_pos(a.geom, chunk);
     const uint32_t D = static_cast<uint32_t>(a.geom.channels);
@@ -500,8 +569,9 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
     }
     const uint8_t* base = a.payload + beg;
     unsigned long long x = reinterpret_cast<const unsigned long long*>(base)[lane];
-    const uint16_t* __restrict__ words = reinterpret_cast<const uint16_t*>(base + kStateBytes);
-    const uint32_t avail = static_cast<uint32_t>((end - beg - kStateBytes) / 2);
+    const uint32_t avail = static_cast<uint32_t>((end - beg - kStateBytes) / 2);     // a multiple of 4
+    WordWindow win{reinterpret_cast<const uint32_t*>(base + kStateBytes), avail / 2u, 0u, 0u, 0u};
+    win.init(lane);
 
     const float sigma = a.sigma[cp.g * D + cp.k * 64 + lane];
     float inv24 = __frcp_rn(sigma) * 16777216.0f;
@@ -511,48 +581,91 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
         inv24 = 16777216.0f;
         sg = 1.0f;
     }
-    DecodeModel<KV> dm{Model{s_tab, a.prefix}, s_inv, htot,
-                       htot ? static_cast<float>(kInvSteps) / static_cast<float>(htot) : 0.0f};
+    const Model m{s_tab, a.prefix};
+    const Aim aim{s_zinv, htot ? static_cast<float>(kZinvSteps) / static_cast<float>(htot) : 0.0f,
+                  static_cast<int32_t>(htot)};
+    const uint32_t geo = geo_offset(lane);
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
     const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * static_cast<int64_t>(D) + cp.k * 64;
-    KB* __restrict__ outp = static_cast<KB*>(a.kv_out) + row0 + lane;
-    const MT* __restrict__ mup = static_cast<const MT*>(a.mu) + row0 + lane;
+    KB* __restrict__ outp = static_cast<KB*>(a.kv_out) + row0;
+    const MT* __restrict__ mup = static_cast<const MT*>(a.mu) + row0;
 
     uint32_t rp = 0, misses = 0;
-    for (uint32_t t = 0; t < cp.len; ++t) {
-        const uint32_t off = t * D;
-        const float mu = mu_value<MU>(mup[off]);
-        const uint32_t gm = nearest_symbol<KV>(mu);
-        const uint32_t bias = gm + (a.prefix ? a.prefix[gm] : 0u);
-        const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
-        uint32_t start, freq;
-        const uint32_t s = decode_symbol<KV>(target, mu, sg, inv24, bias, dm, start, freq, misses);
-        x = static_cast<unsigned long long>(freq) * (x >> kLog2M) + (target - start);
+    for (uint32_t t0 = 0; t0 < cp.len; t0 += kDecodeBatch) {
+        // model side of the batch: predictor means and their escape bias
+        float mus[kDecodeBatch];
+        uint32_t bias[kDecodeBatch];
+#pragma unroll
+        for (int u = 0; u < kDecodeBatch; ++u) {
+            const uint32_t t = t0 + u < cp.len ? t0 + u : cp.len - 1;
+            mus[u] = mu_value<MU>(mup[t * D + lane]);
+        }
+#pragma unroll
+        for (int u = 0; u < kDecodeBatch; ++u) {
+            const uint32_t gm = nearest_symbol<KV>(mus[u]);
+            bias[u] = gm + (m.prefix ? m.prefix[gm] : 0u);
+        }
+        const uint32_t nb = cp.len - t0 < kDecodeBatch ? cp.len - t0 : kDecodeBatch;
+        for (uint32_t u = 0; u < nb; ++u) {
+            float mu = mus[0];
+            uint32_t bs = bias[0];
+#pragma unroll
+            for (int v = 1; v < kDecodeBatch; ++v) {
+                mu = (u == static_cast<uint32_t>(v)) ? mus[v] : mu;
+                bs = (u == static_cast<uint32_t>(v)) ? bias[v] : bs;
+            }
+            const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
+            // aim twice (escape and floor mass taken at mu's symbol, then at
+            // the first guess), then check the nearest edge and a neighbour
+            uint32_t E = aim_edge<KV>(static_cast<int32_t>(target - bs), mu, sg, aim);
+            const uint32_t qE = E + (m.prefix ? m.prefix[E] : 0u);
+            E = aim_edge<KV>(static_cast<int32_t>(target - qE), mu, sg, aim);
+            uint32_t p0 = 0, p1 = 0, p2 = 0;
+            if (m.prefix) {
+                p0 = m.prefix[E - 1u];
+                p1 = m.prefix[E];
+                p2 = m.prefix[E + 1u];
+            }
+            const uint32_t cE = E + h_fx(z_fixed(edge<KV>(E), mu, inv24), m.tab) + p1;
+            const bool up = target >= cE;
+            const uint32_t E2 = up ? E + 1u : E - 1u;
+            const uint32_t c2 = E2 + h_fx(z_fixed(edge<KV>(E2), mu, inv24), m.tab) + (up ? p2 : p0);
+            const bool ok = up ? (target < c2) : (target >= c2);
+            Found fd;
+            fd.s = up ? E : E2;
+            fd.start = up ? cE : c2;
+            fd.freq = up ? c2 - cE : cE - c2;
+            if (__ballot(!ok)) {
+                misses += ok ? 0u : 1u;
+                coop_search<KV>(!ok, target, mu, inv24, up, up ? E2 : 0u, up ? Alphabet<KV>::kSize : E2,
+                                up ? c2 : 0u, up ? kM : c2, m, geo, fd);
+            }
+            x = static_cast<unsigned long long>(fd.freq) * (x >> kLog2M) + (target - fd.start);
 
-        bool need = x < kL;
-        const uint64_t m1 = __ballot(need);
-        const uint32_t n1 = __popcll(m1);
-        if (need) {
-            const uint32_t i = rp + lane_rank(m1);
-            x = (x << 16) | (i < avail ? words[i] : 0u);
+            // refill: up to two words per lane, in lane order per round
+            bool need = x < kL;
+            const uint64_t m1 = __ballot(need);
+            const uint32_t n1 = __popcll(m1);
+            const uint32_t w1 = win.word(rp + lane_rank(m1));
+            if (need) x = (x << 16) | w1;
+            need = x < kL;
+            const uint64_t m2 = __ballot(need);
+            const uint32_t n2 = __popcll(m2);
+            const uint32_t w2 = win.word(rp + n1 + lane_rank(m2));
+            if (need) x = (x << 16) | w2;
+            rp += n1 + n2;
+            win.advance(rp, lane);
+            outp[(t0 + u) * D + lane] = static_cast<KB>(bits_of_order<KV>(fd.s));
         }
-        need = x < kL;
-        const uint64_t m2 = __ballot(need);
-        const uint32_t n2 = __popcll(m2);
-        if (need) {
-            const uint32_t i = rp + n1 + lane_rank(m2);
-            x = (x << 16) | (i < avail ? words[i] : 0u);
-        }
-        rp += n1 + n2;
-        outp[off] = static_cast<KB>(bits_of_order<KV>(s));
     }
     // every lane back at the initial state, the payload consumed exactly,
     // the padding zero
     bool bad = (x != kL) || (chunk_bytes(rp) != end - beg);
     if (!bad) {
         const uint32_t pad_words = avail - rp;        // 0..3
+        const uint16_t* words = reinterpret_cast<const uint16_t*>(base + kStateBytes);
         if (static_cast<uint32_t>(lane) < pad_words && words[rp + lane] != 0) bad = true;
     }
     if (__ballot(bad) && lane == 0) atomicOr(&a.ctl->flags, kFlagCorrupt);
