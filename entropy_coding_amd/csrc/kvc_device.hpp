@@ -221,27 +221,41 @@ __device__ __forceinline__ bool sigma_ok(float s) {
     return s >= 0x1p-96f && s <= 0x1p96f;
 }
 
-// floor(x / f) and x mod f for x < 2^32 f (the quotient fits 32 bits),
-// without a hardware divider: a float32 estimate, one float32 correction of
-// the remainder, and a final integer adjustment by at most one.
-__device__ __forceinline__ void divmod_q32(uint64_t x, uint32_t f, uint32_t& q, uint32_t& r) {
-    const float rf = __builtin_amdgcn_rcpf(static_cast<float>(f));
-    const uint32_t xh = static_cast<uint32_t>(x >> 32), xl = static_cast<uint32_t>(x);
-    const float fx = __fmaf_rn(static_cast<float>(xh), 4294967296.0f, static_cast<float>(xl));
-    const uint32_t q0 = static_cast<uint32_t>(__builtin_amdgcn_fmed3f(fx * rf, 0.0f, 4294967040.0f));
-    const int64_t r0 = static_cast<int64_t>(x - static_cast<uint64_t>(q0) * f);   // |r0| < 2^42
-    // r0 as float32 from two parts that are exact in float32 (a split at bit
-    // 32 would cancel catastrophically for small negative r0)
-    const float fr0 = __fmaf_rn(static_cast<float>(static_cast<int32_t>(r0 >> 21)), 2097152.0f,
-                                static_cast<float>(static_cast<uint32_t>(r0) & 0x1FFFFFu));
-    // floor of the corrected estimate is within one of floor(r0 / f)
-    const int64_t qs = static_cast<int64_t>(q0) + static_cast<int32_t>(__builtin_floorf(fr0 * rf));
-    uint32_t q1 = static_cast<uint32_t>(qs > 0xFFFFFFFFll ? 0xFFFFFFFFll : qs);
-    int64_t r1 = static_cast<int64_t>(x - static_cast<uint64_t>(q1) * f);     // in [-f, 2f)
-    if (r1 < 0) { q1 -= 1u; r1 += f; }
-    if (r1 >= static_cast<int64_t>(f)) { q1 += 1u; r1 -= f; }
-    q = q1;
-    r = static_cast<uint32_t>(r1);
+// floor(x / f) and x mod f for x = xh * 2^32 + xl < 2^32 f (the quotient
+// fits 32 bits), without a hardware divider: a float64 quotient from the
+// hardware reciprocal refined by one Newton step is within one of the
+// truth; one integer adjustment makes it exact.
+__device__ __forceinline__ void divmod_q32(uint32_t xh, uint32_t xl, uint32_t f, uint32_t& q, uint32_t& r) {
+    const double fd = static_cast<double>(f);
+    double rc = __builtin_amdgcn_rcp(fd);
+    rc = __fma_rn(rc, __fma_rn(-fd, rc, 1.0), rc);
+    const double xd = __fma_rn(static_cast<double>(xh), 4294967296.0, static_cast<double>(xl));
+    const uint32_t q0 = static_cast<uint32_t>(__builtin_fmin(xd * rc, 4294967295.0));
+    // rem = x - q0 f lies in [-f, 2f): its high word is 0 or all ones
+    const uint64_t p = static_cast<uint64_t>(q0) * f;
+    const uint32_t rl = xl - static_cast<uint32_t>(p);
+    const uint32_t rh = xh - static_cast<uint32_t>(p >> 32) - (xl < static_cast<uint32_t>(p) ? 1u : 0u);
+    const bool neg = rh != 0u;
+    const bool big = !neg && rl >= f;
+    q = neg ? q0 - 1u : (big ? q0 + 1u : q0);
+    r = neg ? rl + f : (big ? rl - f : rl);
+}
+
+// Both cell edges of the bf16 symbol with bit pattern u: the inner edge
+// (towards zero) is the midpoint below the magnitude, the outer edge the
+// midpoint above; the -max / +max cells open to -inf / +inf, Inf and NaN
+// patterns get two infinite edges, and the edge between -0 and +0 is 0.
+__device__ __forceinline__ void bf16_cell_edges(uint32_t u, float& lo, float& hi) {
+    const uint32_t m = u & 0x7FFFu;
+    uint32_t ob = (m << 16) | 0x8000u;
+    uint32_t ib = ob - 0x10000u;
+    ob = m >= 0x7F7Fu ? 0x7F800000u : ob;
+    ib = m >= 0x7F80u ? 0x7F800000u : ib;
+    ib = m == 0u ? 0u : ib;
+    const uint32_t sb = (u & 0x8000u) << 16;
+    const bool neg = sb != 0u;
+    lo = __uint_as_float((neg ? ob : ib) | sb);
+    hi = __uint_as_float((neg ? ib : ob) | sb);
 }
 
 }  // namespace kvc

@@ -186,32 +186,49 @@ __device__ __forceinline__ void rans_push(PushState& st, uint32_t c0, uint32_t f
     lo = e2 ? st.xh : lo;
     hi = e2 ? 0u : hi;
     uint32_t q, r;
-    divmod_q32((static_cast<uint64_t>(hi) << 32) | lo, f, q, r);
+    divmod_q32(hi, lo, f, q, r);
     // x = q * 2^31 + r + c0 with r + c0 < 2^31: no carry into bit 31
     st.xh = q >> 1;
     st.xl = (q << 31) | (r + c0);
 }
 
+// Start and frequency of the symbol with bit pattern kb under the mixture.
+template <int KV>
+__device__ __forceinline__ void symbol_range(uint32_t kb, float mu, float inv24, const Model& m, uint32_t& c0,
+                                             uint32_t& f) {
+    const uint32_t s = order_of_bits<KV>(kb);
+    float lo, hi;
+    if constexpr (KV == kBF16) {
+        bf16_cell_edges(kb, lo, hi);
+    } else {
+        lo = edge<KV>(s);
+        hi = edge<KV>(s + 1);
+    }
+    uint32_t a = s + h_fx(z_fixed(lo, mu, inv24), m.tab);
+    uint32_t b = s + 1u + h_fx(z_fixed(hi, mu, inv24), m.tab);
+    if (m.prefix) {
+        a += m.prefix[s];
+        b += m.prefix[s + 1];
+    }
+    c0 = a;
+    f = b - a;
+}
+
 template <int KV, int MU, int U>
-__device__ __forceinline__ void encode_batch(int t, PushState& st, const typename Alphabet<KV>::Bits* __restrict__ kvp,
-                                             const typename MuT<MU>::T* __restrict__ mup, uint32_t D, float inv24,
-                                             const Model& m, uint16_t* __restrict__ slot) {
-    typename Alphabet<KV>::Bits kb[U];
+__device__ __forceinline__ void encode_batch(int t, PushState& st, const typename Alphabet<KV>::Bits* __restrict__ kvb,
+                                             const typename MuT<MU>::T* __restrict__ mub, uint32_t D, uint32_t lane,
+                                             float inv24, const Model& m, uint16_t* __restrict__ slot) {
+    uint32_t kb[U];
     typename MuT<MU>::T mb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint32_t off = static_cast<uint32_t>(t - u) * D;
-        kb[u] = kvp[off];
-        mb[u] = mup[off];
+        const uint32_t off = static_cast<uint32_t>(t - u) * D + lane;
+        kb[u] = kvb[off];
+        mb[u] = mub[off];
     }
     uint32_t c0[U], fr[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const uint32_t s = order_of_bits<KV>(kb[u]);
-        const float mu = mu_value<MU>(mb[u]);
-        c0[u] = cdf_at<KV>(s, mu, inv24, m);
-        fr[u] = cdf_at<KV>(s + 1, mu, inv24, m) - c0[u];
-    }
+    for (int u = 0; u < U; ++u) symbol_range<KV>(kb[u], mu_value<MU>(mb[u]), inv24, m, c0[u], fr[u]);
 #pragma unroll
     for (int u = 0; u < U; ++u) rans_push(st, c0[u], fr[u], slot);
 }
@@ -221,8 +238,9 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
     __shared__ uint32_t s_tab[kTableEntries];
     build_table_lds(s_tab, a.phi, a.tn, a.tw);
 
-    const int lane = threadIdx.x & 63;
-    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (kEncodeBlock / 64) + (threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63u;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (kEncodeBlock / 64) + wave;
     if (chunk >= a.geom.n_chunks) return;
     const ChunkPos cp = chunk_pos(a.geom, chunk);
     const uint32_t D = static_cast<uint32_t>(a.geom.channels);
@@ -237,16 +255,17 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
+    // wave-uniform bases; lanes index them with 32-bit offsets
     const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * static_cast<int64_t>(D) + cp.k * 64;
-    const KB* __restrict__ kvp = static_cast<const KB*>(a.kv) + row0 + lane;
-    const MT* __restrict__ mup = static_cast<const MT*>(a.mu) + row0 + lane;
+    const KB* __restrict__ kvb = static_cast<const KB*>(a.kv) + row0;
+    const MT* __restrict__ mub = static_cast<const MT*>(a.mu) + row0;
     uint16_t* __restrict__ slot = a.slots + static_cast<uint64_t>(chunk) * a.slot_words;
 
     PushState st{static_cast<uint32_t>(kL), kLHi, static_cast<uint32_t>(a.slot_words)};
     int t = static_cast<int>(cp.len) - 1;
     for (; t >= kEncodeBatch - 1; t -= kEncodeBatch)
-        encode_batch<KV, MU, kEncodeBatch>(t, st, kvp, mup, D, inv24, m, slot);
-    for (; t >= 0; --t) encode_batch<KV, MU, 1>(t, st, kvp, mup, D, inv24, m, slot);
+        encode_batch<KV, MU, kEncodeBatch>(t, st, kvb, mub, D, lane, inv24, m, slot);
+    for (; t >= 0; --t) encode_batch<KV, MU, 1>(t, st, kvb, mub, D, lane, inv24, m, slot);
 
     a.states[chunk * 64 + lane] = (static_cast<unsigned long long>(st.xh) << 32) | st.xl;
     if (lane == 0) a.chunk_words[chunk] = static_cast<uint32_t>(a.slot_words) - st.wp;
@@ -607,15 +626,11 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
             const uint32_t gm = nearest_symbol<KV>(mus[u]);
             bias[u] = gm + (m.prefix ? m.prefix[gm] : 0u);
         }
-        const uint32_t nb = cp.len - t0 < kDecodeBatch ? cp.len - t0 : kDecodeBatch;
-        for (uint32_t u = 0; u < nb; ++u) {
-            float mu = mus[0];
-            uint32_t bs = bias[0];
 #pragma unroll
-            for (int v = 1; v < kDecodeBatch; ++v) {
-                mu = (u == static_cast<uint32_t>(v)) ? mus[v] : mu;
-                bs = (u == static_cast<uint32_t>(v)) ? bias[v] : bs;
-            }
+        for (int u = 0; u < kDecodeBatch; ++u) {
+            if (t0 + u >= cp.len) break;                 // wave-uniform
+            const float mu = mus[u];
+            const uint32_t bs = bias[u];
             const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
             // aim twice (escape and floor mass taken at mu's symbol, then at
             // the first guess), then check the nearest edge and a neighbour

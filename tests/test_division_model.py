@@ -42,3 +42,38 @@ def test_division_model_is_exact(ulps):
         xs = [lo, lo + 1, hi - 1, hi - 2] + [int(v) for v in rng.integers(lo, hi, 300, dtype=np.uint64)]
         for x in xs:
             assert divmod_model(x, f, ulps) == divmod(x, f), (x, f)
+
+
+def divmod_f64_model(x: int, f: int, rcp_rel_err: float):
+    """The fp64 variant: x as a double (one rounding), a hardware reciprocal
+    with relative error up to `rcp_rel_err`, one Newton step, a truncated
+    quotient within one of the truth, and a two-sided integer fix."""
+    xh, xl = x >> 32, x & 0xFFFFFFFF
+    xd = float(xh) * 4294967296.0 + float(xl)              # fma: exact product, one rounding
+    fd = float(f)
+    r = (1.0 / fd) * (1.0 + rcp_rel_err)
+    e = 1.0 - fd * r                                         # fma
+    r = r + r * e                                            # fma
+    q = int(xd * r)                                          # truncation of a positive value
+    q = min(q, 0xFFFFFFFF)
+    rem = x - q * f
+    assert -f <= rem < 2 * f
+    if rem < 0:
+        q, rem = q - 1, rem + f
+    elif rem >= f:
+        q, rem = q + 1, rem - f
+    return q, rem
+
+
+@pytest.mark.parametrize("err", [-2.0 ** -20, 0.0, 2.0 ** -20])
+def test_division_f64_model_is_exact(err):
+    rng = np.random.default_rng(11)
+    fs = [1, 2, 3, 40, 255, 256, 65535, 65536, 2 ** 24 + 1, 2 ** 31 - 65535, 2 ** 31 - 1] + \
+         [int(v) for v in rng.integers(1, 2 ** 31, 24)]
+    for f in fs:
+        lo, hi = 2 ** 16 * f, min(2 ** 32 * f, 2 ** 63)
+        xs = [lo, lo + 1, hi - 1, hi - 2] + [int(v) for v in rng.integers(lo, hi, 300, dtype=np.uint64)]
+        xs += [q * f for q in (2 ** 16, 2 ** 31, 2 ** 32 - 1) if lo <= q * f < hi]
+        xs += [q * f - 1 for q in (2 ** 16 + 1, 2 ** 31, 2 ** 32 - 1) if lo <= q * f - 1 < hi]
+        for x in xs:
+            assert divmod_f64_model(x, f, err) == divmod(x, f), (x, f)
