@@ -127,6 +127,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-planes-per-worker", type=int, default=8)
     ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--chunk-tokens", type=int, default=None, help="override the workload's chunk length")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -154,7 +155,8 @@ def main():
     kv, mu, sigma, prefix = prepare(w, dev, reps)
     n = w.n_scalars
     weights = (w.w_narrow_bp, w.w_wide_bp)
-    p = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, w.planes, w.tokens, w.channels, weights, w.chunk_tokens)
+    tc = args.chunk_tokens if args.chunk_tokens else w.chunk_tokens
+    p = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, w.planes, w.tokens, w.channels, weights, tc)
     enc = kvc.Encoder(p, dev)
     kv_out = torch.empty((w.planes, w.tokens, w.channels), dtype=torch.int16, device=dev)
     dws = torch.empty(kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
@@ -220,7 +222,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "shape": [w.layers, 2, w.batch, w.heads, w.tokens, w.channels],
-            "scalars": n, "mixture_bp": list(weights), "chunk_tokens": w.chunk_tokens,
+            "scalars": n, "mixture_bp": list(weights), "chunk_tokens": tc,
             "sigma_calibration": f"{reps}x{w.calib_tokens} tokens per layer",
         },
         "encode_gbps": raw / (enc_total * 1e-3) / 1e9,

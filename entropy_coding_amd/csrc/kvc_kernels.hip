@@ -528,47 +528,58 @@ __device__ __forceinline__ void coop_search(bool need, uint32_t target, float mu
     }
 }
 
-// Stream words of a chunk, held two 128-word blocks at a time across the
-// wave's registers (one dword of each block per lane) and read with a lane
-// permute; the next block is loaded as soon as the current one is entered,
-// so no memory read sits on the serial decode chain.
-struct WordWindow {
+// Stream words of a chunk, staged through a per-wave LDS ring of two
+// 128-word blocks.  The block after next is loaded into registers (one
+// dword per lane) as soon as a block is entered and written to the ring
+// when the one before it is left, so no global read sits on the serial
+// decode chain; a refill read is one LDS access.
+struct WordRing {
     const uint32_t* __restrict__ dw;   // chunk words as dwords (8-byte aligned)
     uint32_t n_dw;                     // dwords in the chunk's word area
-    uint32_t base;                     // first word of the current block
-    uint32_t cur, nxt;                 // this lane's dword of the current / next block
+    uint32_t* ring;                    // this wave's 128 dwords of LDS
+    uint32_t base;                     // first word of the block being read
+    uint32_t ahead;                    // this lane's dword of block base/128 + 2
 
-    __device__ __forceinline__ uint32_t load(uint32_t block, int lane) const {
-        const uint32_t d = block * 64u + static_cast<uint32_t>(lane);
+    __device__ __forceinline__ uint32_t load(uint32_t block, uint32_t lane) const {
+        const uint32_t d = block * 64u + lane;
         return d < n_dw ? dw[d] : 0u;
     }
-    __device__ __forceinline__ void init(int lane) {
+    __device__ __forceinline__ void init(uint32_t lane) {
         base = 0;
-        cur = load(0, lane);
-        nxt = load(1, lane);
+        ring[lane] = load(0, lane);
+        ring[64u + lane] = load(1, lane);
+        ahead = load(2, lane);
     }
-    // word p, base <= p < base + 256; called with the whole wave active
+    // word p, base <= p < base + 256
     __device__ __forceinline__ uint32_t word(uint32_t p) const {
-        const uint32_t rel = p - base;
-        const int src = static_cast<int>((rel >> 1) & 63u) << 2;
-        const uint32_t v0 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(cur)));
-        const uint32_t v1 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(nxt)));
-        const uint32_t v = (rel & 128u) ? v1 : v0;
-        return (rel & 1u) ? (v >> 16) : (v & 0xFFFFu);
+        return reinterpret_cast<const uint16_t*>(ring)[p & 255u];
     }
-    __device__ __forceinline__ void advance(uint32_t rp, int lane) {
+    __device__ __forceinline__ void advance(uint32_t rp, uint32_t lane) {
         if (rp >= base + 128u) {                       // wave-uniform
-            cur = nxt;
+            // the block just left (slot of base) takes the block after next
+            ring[((base >> 7) & 1u) * 64u + lane] = ahead;
             base += 128u;
-            nxt = load((base >> 7) + 1u, lane);
+            ahead = load((base >> 7) + 2u, lane);
         }
     }
 };
+
+// Ordered index of mu's own symbol (exact for a bf16 mean, nearest otherwise).
+template <int KV, int MU>
+__device__ __forceinline__ uint32_t mean_symbol(typename MuT<MU>::T raw, float mu) {
+    if constexpr (KV == kBF16 && MU == kBF16) {
+        const uint32_t u = raw;
+        return (u & 0x7F80u) == 0x7F80u ? 32768u : order_of_bits<kBF16>(u);   // non-finite mean counts as 0
+    } else {
+        return nearest_symbol<KV>(mu);
+    }
+}
 
 template <int KV, int MU>
 __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
     __shared__ uint32_t s_tab[kTableEntries];
     __shared__ float s_zinv[kZinvSteps + 1];
+    __shared__ uint32_t s_ring[kDecodeBlock / 64][128];
     build_table_lds(s_tab, a.phi, a.tn, a.tw);
     const uint32_t htot = a.tn + a.tw;
     if (htot) build_zinv_lds(s_zinv, s_tab, htot);
@@ -589,8 +600,8 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
     const uint8_t* base = a.payload + beg;
     unsigned long long x = reinterpret_cast<const unsigned long long*>(base)[lane];
     const uint32_t avail = static_cast<uint32_t>((end - beg - kStateBytes) / 2);     // a multiple of 4
-    WordWindow win{reinterpret_cast<const uint32_t*>(base + kStateBytes), avail / 2u, 0u, 0u, 0u};
-    win.init(lane);
+    WordRing win{reinterpret_cast<const uint32_t*>(base + kStateBytes), avail / 2u, s_ring[wave], 0u, 0u};
+    win.init(static_cast<uint32_t>(lane));
 
     const float sigma = a.sigma[cp.g * D + cp.k * 64 + lane];
     float inv24 = __frcp_rn(sigma) * 16777216.0f;
@@ -616,14 +627,16 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
         // model side of the batch: predictor means and their escape bias
         float mus[kDecodeBatch];
         uint32_t bias[kDecodeBatch];
+        MT raw[kDecodeBatch];
 #pragma unroll
         for (int u = 0; u < kDecodeBatch; ++u) {
             const uint32_t t = t0 + u < cp.len ? t0 + u : cp.len - 1;
-            mus[u] = mu_value<MU>(mup[t * D + lane]);
+            raw[u] = mup[t * D + lane];
         }
 #pragma unroll
         for (int u = 0; u < kDecodeBatch; ++u) {
-            const uint32_t gm = nearest_symbol<KV>(mus[u]);
+            mus[u] = mu_value<MU>(raw[u]);
+            const uint32_t gm = mean_symbol<KV, MU>(raw[u], mus[u]);
             bias[u] = gm + (m.prefix ? m.prefix[gm] : 0u);
         }
 #pragma unroll
@@ -671,7 +684,7 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
             const uint32_t w2 = win.word(rp + n1 + lane_rank(m2));
             if (need) x = (x << 16) | w2;
             rp += n1 + n2;
-            win.advance(rp, lane);
+            win.advance(rp, static_cast<uint32_t>(lane));
             outp[(t0 + u) * D + lane] = static_cast<KB>(bits_of_order<KV>(fd.s));
         }
     }
