@@ -419,10 +419,12 @@ constexpr int kDecodeBatch = 4;
 constexpr int kZinvSteps = 4096;
 
 // zinv[j] = z at which the (interpolated) mixture table reaches
-// floor(j * htot / kZinvSteps).
+// floor(j * htot / kZinvSteps); one repeated entry past the end lets the aim
+// truncate without a bound check.
 __device__ __forceinline__ void build_zinv_lds(float* s_zinv, const uint32_t* s_tab, uint32_t htot) {
-    for (int j = threadIdx.x; j <= kZinvSteps; j += blockDim.x) {
-        const uint32_t e = static_cast<uint32_t>((static_cast<uint64_t>(htot) * j) / kZinvSteps);
+    for (int j = threadIdx.x; j <= kZinvSteps + 1; j += blockDim.x) {
+        const int jj = j > kZinvSteps ? kZinvSteps : j;
+        const uint32_t e = static_cast<uint32_t>((static_cast<uint64_t>(htot) * jj) / kZinvSteps);
         uint32_t lo = 0, hi = kTablePoints;           // largest k with H[k] <= e
         while (hi - lo > 1) {
             const uint32_t mid = (lo + hi) >> 1;
@@ -447,17 +449,55 @@ struct Aim {
     int32_t htot;
 };
 
-// Nearest cell edge to the position where H reaches `e`.
-template <int KV>
-__device__ __forceinline__ uint32_t aim_edge(int32_t e, float mu, float sg, const Aim& a) {
-    e = e < 0 ? 0 : (e > a.htot ? a.htot : e);
-    const float ef = static_cast<float>(e) * a.scale;
-    const float jf = fminf(__builtin_floorf(ef), static_cast<float>(kZinvSteps - 1));
-    const int j = static_cast<int>(jf);
-    const float fr = ef - jf;
+// Position where H reaches `e` (clamped to [0, htot]).
+__device__ __forceinline__ float aim_pos(int32_t e, float mu, float sg, const Aim& a) {
+    const float ef = __builtin_amdgcn_fmed3f(static_cast<float>(e) * a.scale, 0.0f, static_cast<float>(kZinvSteps));
+    const int j = static_cast<int>(ef);                // ef >= 0: truncation is floor
+    const float fr = ef - static_cast<float>(j);
     const float z0 = a.zinv[j], z1 = a.zinv[j + 1];
     const float z = __fmaf_rn(fr, z1 - z0, z0);
-    return nearest_edge<KV>(__fmaf_rn(z, sg, mu));
+    return __fmaf_rn(z, sg, mu);
+}
+
+template <int KV>
+__device__ __forceinline__ uint32_t aim_edge(int32_t e, float mu, float sg, const Aim& a) {
+    return nearest_edge<KV>(aim_pos(e, mu, sg, a));
+}
+
+// bf16 edge nearest to x, as its index and the magnitude pattern of its
+// position.  x is first clamped to the outer edges of -max / +max, so the
+// edge is m * 2^16 + 2^15 with m the upper half of x's magnitude pattern.
+// The outermost edges come out finite (the midpoints above +max and below
+// -max); edge_pattern() turns them into the infinities of the format.
+struct Bf16Edge {
+    uint32_t e;      // edge index, kLoFinite .. kHiFinite + 1
+    uint32_t mag;    // m * 2^16 + 2^15, at most 0x7F7F8000
+    uint32_t sign;   // 0x80000000 when x < 0
+};
+constexpr uint32_t kBf16OuterMag = 0x7F7F8000u;    // midpoint above +max
+
+__device__ __forceinline__ Bf16Edge nearest_edge_bf16(float x) {
+    const float lim = __uint_as_float(kBf16OuterMag);
+    const uint32_t u = __float_as_uint(__builtin_amdgcn_fmed3f(x, -lim, lim));
+    const uint32_t m = (u >> 16) & 0x7FFFu;
+    Bf16Edge r;
+    r.sign = u & 0x80000000u;
+    r.e = r.sign ? 32767u - m : 32769u + m;
+    r.mag = (u & 0x7FFF0000u) | 0x8000u;
+    return r;
+}
+
+// Position of the edge with magnitude pattern `mag` (at most one step past
+// kBf16OuterMag, or 0 for the edge between -0 and +0).  With a bf16 mean the
+// outer edge itself may stay finite: the mean lies inside [-max, max], at
+// least half a bf16 step from it, so z saturates at +-24 exactly as it does
+// for an infinite edge (sigma <= 2^96).  An fp32 mean can sit beyond it, so
+// there the edge becomes infinite as the format defines.
+template <int MU>
+__device__ __forceinline__ float edge_pattern(uint32_t mag, uint32_t sign) {
+    if constexpr (MU == kBF16) mag = mag < 0x7F800000u ? mag : 0x7F800000u;
+    else mag = mag < kBf16OuterMag ? mag : 0x7F800000u;
+    return __uint_as_float(mag | sign);
 }
 
 // Probe offsets for the first cooperative round: 1, 2, 3, ... then growing
@@ -564,6 +604,39 @@ struct WordRing {
     }
 };
 
+// Escape prefix for aiming only: every 2^shift-th entry in LDS (all of it
+// for e4m3), read back with linear interpolation.  The aim is a guess; the
+// symbol is then settled with the exact prefix, so this table only moves
+// cost, never results.
+constexpr int kCoarseEntries = 1026;             // 65536 / 64 + 1, plus one repeat
+
+template <int KV>
+struct Coarse {
+    static constexpr int kShift = KV == kBF16 ? 6 : 0;
+    static constexpr uint32_t kLast = Alphabet<KV>::kSize >> kShift;     // index of the entry for b = N
+};
+
+template <int KV>
+__device__ __forceinline__ void build_coarse_lds(uint32_t* s_pc, const uint32_t* __restrict__ prefix) {
+    constexpr uint32_t last = Coarse<KV>::kLast;
+    for (uint32_t j = threadIdx.x; j <= last + 1u; j += blockDim.x) {
+        const uint32_t jj = j > last ? last : j;
+        s_pc[j] = prefix ? prefix[jj << Coarse<KV>::kShift] : 0u;
+    }
+}
+
+template <int KV>
+__device__ __forceinline__ uint32_t coarse_prefix(const uint32_t* s_pc, uint32_t b) {
+    if constexpr (Coarse<KV>::kShift == 0) {
+        return s_pc[b];
+    } else {
+        constexpr int sh = Coarse<KV>::kShift;
+        const uint32_t j = b >> sh, r = b & ((1u << sh) - 1u);
+        const uint32_t lo = s_pc[j], hi = s_pc[j + 1];
+        return lo + (((hi - lo) * r) >> sh);     // hi - lo <= T_e < 2^26
+    }
+}
+
 // Ordered index of mu's own symbol (exact for a bf16 mean, nearest otherwise).
 template <int KV, int MU>
 __device__ __forceinline__ uint32_t mean_symbol(typename MuT<MU>::T raw, float mu) {
@@ -578,11 +651,13 @@ __device__ __forceinline__ uint32_t mean_symbol(typename MuT<MU>::T raw, float m
 template <int KV, int MU>
 __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
     __shared__ uint32_t s_tab[kTableEntries];
-    __shared__ float s_zinv[kZinvSteps + 1];
+    __shared__ float s_zinv[kZinvSteps + 2];
     __shared__ uint32_t s_ring[kDecodeBlock / 64][128];
+    __shared__ uint32_t s_pc[kCoarseEntries];
+    build_coarse_lds<KV>(s_pc, a.prefix);
     build_table_lds(s_tab, a.phi, a.tn, a.tw);
     const uint32_t htot = a.tn + a.tw;
-    if (htot) build_zinv_lds(s_zinv, s_tab, htot);
+    build_zinv_lds(s_zinv, s_tab, htot);              // all z = 24 when htot = 0
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -599,6 +674,12 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
     }
     const uint8_t* base = a.payload + beg;
     unsigned long long x = reinterpret_cast<const unsigned long long*>(base)[lane];
+    // an encoder leaves every state in [L, 2^63); decoding keeps it there,
+    // which the step below relies on (x >> 31 fits 32 bits)
+    if (__ballot(x < kL || (x >> 63) != 0ull)) {
+        if (lane == 0) atomicOr(&a.ctl->flags, kFlagCorrupt);
+        return;
+    }
     const uint32_t avail = static_cast<uint32_t>((end - beg - kStateBytes) / 2);     // a multiple of 4
     WordRing win{reinterpret_cast<const uint32_t*>(base + kStateBytes), avail / 2u, s_ring[wave], 0u, 0u};
     win.init(static_cast<uint32_t>(lane));
@@ -637,7 +718,7 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
         for (int u = 0; u < kDecodeBatch; ++u) {
             mus[u] = mu_value<MU>(raw[u]);
             const uint32_t gm = mean_symbol<KV, MU>(raw[u], mus[u]);
-            bias[u] = gm + (m.prefix ? m.prefix[gm] : 0u);
+            bias[u] = gm + coarse_prefix<KV>(s_pc, gm);
         }
 #pragma unroll
         for (int u = 0; u < kDecodeBatch; ++u) {
@@ -647,19 +728,44 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
             const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
             // aim twice (escape and floor mass taken at mu's symbol, then at
             // the first guess), then check the nearest edge and a neighbour
-            uint32_t E = aim_edge<KV>(static_cast<int32_t>(target - bs), mu, sg, aim);
-            const uint32_t qE = E + (m.prefix ? m.prefix[E] : 0u);
-            E = aim_edge<KV>(static_cast<int32_t>(target - qE), mu, sg, aim);
-            uint32_t p0 = 0, p1 = 0, p2 = 0;
-            if (m.prefix) {
-                p0 = m.prefix[E - 1u];
-                p1 = m.prefix[E];
-                p2 = m.prefix[E + 1u];
+            uint32_t E, E2, cE, c2;
+            bool up;
+            if constexpr (KV == kBF16) {
+                const uint32_t E1 = nearest_edge_bf16(aim_pos(static_cast<int32_t>(target - bs), mu, sg, aim)).e;
+                const uint32_t qE = E1 + coarse_prefix<KV>(s_pc, E1);
+                const Bf16Edge ed = nearest_edge_bf16(aim_pos(static_cast<int32_t>(target - qE), mu, sg, aim));
+                E = ed.e;
+                uint32_t p0 = 0, p1 = 0, p2 = 0;
+                if (m.prefix) {
+                    const uint32_t* pp = m.prefix + (E - 1u);     // E >= 1: one 12-byte read
+                    p0 = pp[0];
+                    p1 = pp[1];
+                    p2 = pp[2];
+                }
+                cE = E + h_fx(z_fixed(edge_pattern<MU>(ed.mag, ed.sign), mu, inv24), m.tab) + p1;
+                up = target >= cE;
+                // the neighbour one step away from zero (up on the positive
+                // side) or towards it; towards zero from m = 0 is the edge 0
+                const bool outward = up != (ed.sign != 0u);
+                const uint32_t mag2 = outward ? ed.mag + 0x10000u : __builtin_elementwise_sub_sat(ed.mag, 0x10000u);
+                E2 = up ? E + 1u : E - 1u;
+                c2 = E2 + h_fx(z_fixed(edge_pattern<MU>(mag2, ed.sign), mu, inv24), m.tab) + (up ? p2 : p0);
+            } else {
+                E = aim_edge<KV>(static_cast<int32_t>(target - bs), mu, sg, aim);
+                const uint32_t qE = E + coarse_prefix<KV>(s_pc, E);
+                E = aim_edge<KV>(static_cast<int32_t>(target - qE), mu, sg, aim);
+                uint32_t p0 = 0, p1 = 0, p2 = 0;
+                if (m.prefix) {
+                    const uint32_t* pp = m.prefix + (E - 1u);     // E >= 1: one 12-byte read
+                    p0 = pp[0];
+                    p1 = pp[1];
+                    p2 = pp[2];
+                }
+                cE = E + h_fx(z_fixed(edge<KV>(E), mu, inv24), m.tab) + p1;
+                up = target >= cE;
+                E2 = up ? E + 1u : E - 1u;
+                c2 = E2 + h_fx(z_fixed(edge<KV>(E2), mu, inv24), m.tab) + (up ? p2 : p0);
             }
-            const uint32_t cE = E + h_fx(z_fixed(edge<KV>(E), mu, inv24), m.tab) + p1;
-            const bool up = target >= cE;
-            const uint32_t E2 = up ? E + 1u : E - 1u;
-            const uint32_t c2 = E2 + h_fx(z_fixed(edge<KV>(E2), mu, inv24), m.tab) + (up ? p2 : p0);
             const bool ok = up ? (target < c2) : (target >= c2);
             Found fd;
             fd.s = up ? E : E2;
@@ -670,20 +776,27 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
                 coop_search<KV>(!ok, target, mu, inv24, up, up ? E2 : 0u, up ? Alphabet<KV>::kSize : E2,
                                 up ? c2 : 0u, up ? kM : c2, m, geo, fd);
             }
-            x = static_cast<unsigned long long>(fd.freq) * (x >> kLog2M) + (target - fd.start);
+            // x < 2^63, so x >> 31 fits 32 bits: one 32 x 32 -> 64 multiply-add
+            x = static_cast<unsigned long long>(fd.freq) * static_cast<uint32_t>(x >> kLog2M) + (target - fd.start);
 
-            // refill: up to two words per lane, in lane order per round
-            bool need = x < kL;
-            const uint64_t m1 = __ballot(need);
+            // refill: a lane takes one word when x < 2^47 and a second one
+            // when x < 2^31 (then x << 16 is still below 2^47); round one
+            // holds one word per taking lane in lane order, round two the
+            // second words, so both reads are placed before either is used
+            const uint32_t xh = static_cast<uint32_t>(x >> 32), xl = static_cast<uint32_t>(x);
+            const bool take1 = xh < kLHi;
+            const bool take2 = xh == 0u && xl < 0x80000000u;
+            const uint64_t m1 = __ballot(take1), m2 = __ballot(take2);
             const uint32_t n1 = __popcll(m1);
             const uint32_t w1 = win.word(rp + lane_rank(m1));
-            if (need) x = (x << 16) | w1;
-            need = x < kL;
-            const uint64_t m2 = __ballot(need);
-            const uint32_t n2 = __popcll(m2);
             const uint32_t w2 = win.word(rp + n1 + lane_rank(m2));
-            if (need) x = (x << 16) | w2;
-            rp += n1 + n2;
+            const uint32_t hi1 = __builtin_amdgcn_alignbit(xh, xl, 16);     // (x << 16) >> 32
+            const uint32_t lo1 = (xl << 16) | w1;
+            const uint32_t lo2 = (w1 << 16) | w2;
+            const uint32_t nh = take2 ? xl : (take1 ? hi1 : xh);
+            const uint32_t nl = take2 ? lo2 : (take1 ? lo1 : xl);
+            x = (static_cast<unsigned long long>(nh) << 32) | nl;
+            rp += n1 + __popcll(m2);
             win.advance(rp, static_cast<uint32_t>(lane));
             outp[(t0 + u) * D + lane] = static_cast<KB>(bits_of_order<KV>(fd.s));
         }

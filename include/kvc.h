@@ -143,7 +143,8 @@ int kvc_stream_info(const void* h_header, uint64_t header_bytes, kvc_params* h_p
  * encoder's (checked through the stream's checksum: KVC_ERR_MISMATCH).
  * Writes KV bit patterns to d_kv_out ([planes][tokens][channels]).  Returns
  * KVC_ERR_CORRUPT if the stream is malformed, truncated or damaged (every
- * lane must end in the initial state and consume exactly its chunk).
+ * lane must start from a state in [2^47, 2^63), end in the initial state
+ * and consume exactly its chunk).
  * Workspace: KVC_DECODE_WORKSPACE_BYTES.  Synchronises `stream` twice
  * (header read, status read).  h_info: NULL, or receives the stage times
  * and the number of symbols found by the fallback search.

@@ -581,6 +581,9 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
         start_b = pay_off + directory[cid]
         size_b = directory[cid + 1] - directory[cid]
         x = np.stack([np.frombuffer(stream, dtype="<u8", count=LANES, offset=int(o)) for o in start_b]).astype(np.uint64)
+        # an encoder's final state lies in the state interval [L, 2^16 L)
+        if np.any((x < np.uint64(L)) | (x >= np.uint64(L << 16))):
+            raise StreamError("initial rANS state outside [L, 2^16 L)")
         nwords = (size_b - STATE_BYTES) // 2
         wmax = int(nwords.max()) if nb else 0
         words = np.zeros((nb, wmax + 1), dtype=np.uint64)

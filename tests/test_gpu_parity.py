@@ -239,6 +239,9 @@ def test_error_statuses(kvc, cuda):
         bad[i] ^= 1 << int(rng.integers(0, 8))
         assert dec(bad) == kvc.KVC_ERR_CORRUPT
     bad = st.clone()
+    bad[pay + 7] ^= 0x80                    # top bit of lane 0's state
+    assert dec(bad) == kvc.KVC_ERR_CORRUPT
+    bad = st.clone()
     bad[128 + 8 * 2] ^= 8
     assert dec(bad) == kvc.KVC_ERR_CORRUPT
     bad = st.clone()

@@ -122,6 +122,12 @@ def test_damaged_streams_are_rejected():
         bad[i] ^= 1 << int(rng.integers(0, 8))
         with pytest.raises(O.StreamError):
             O.decode(bytes(bad), mu, sig, pref)
+    # the top bit of a state is outside the state interval [L, 2^16 L) even
+    # where the rest of the decode would not notice it
+    bad = bytearray(st)
+    bad[pay + 7] ^= 0x80
+    with pytest.raises(O.StreamError, match="initial rANS state"):
+        O.decode(bytes(bad), mu, sig, pref)
     with pytest.raises(O.StreamError):
         O.decode(st[:-8], mu, sig, pref)
     with pytest.raises(O.StreamError):
