@@ -187,13 +187,16 @@ __device__ __forceinline__ int32_t z_fixed(float edge_pos, float mu, float inv24
 }
 
 // Integer mixture CDF of z = q / 2^24: table step 1/256 with integer linear
-// interpolation over the 16 low bits of q (table steps are below 2^22, so the
-// product fits 24-bit multiplies).
+// interpolation over the 16 low bits of q.  Every step of the table is below
+// 2^22 (the largest step of round(2^31 Phi) on this grid is 3,346,562 and the
+// two weighted parts add to at most that), so the product fits the 24-bit
+// multiplier.
 __device__ __forceinline__ uint32_t h_fx(int32_t q, const uint32_t* __restrict__ tab) {
     const uint32_t u = static_cast<uint32_t>(q + kQMax);
     const uint32_t i = u >> 16, r = u & 0xFFFFu;
     const uint32_t a = tab[i], c = tab[i + 1];
-    const uint32_t dlt = (c - a) & 0x3FFFFFu;
+    const uint32_t dlt = c - a;
+    __builtin_assume(dlt < (1u << 22));
     return a + static_cast<uint32_t>((static_cast<uint64_t>(dlt) * r) >> 16);
 }
 
@@ -223,22 +226,21 @@ __device__ __forceinline__ bool sigma_ok(float s) {
 
 // floor(x / f) and x mod f for x = xh * 2^32 + xl < 2^32 f (the quotient
 // fits 32 bits), without a hardware divider: a float64 quotient from the
-// hardware reciprocal refined by one Newton step is within one of the
-// truth; one integer adjustment makes it exact.
+// hardware reciprocal refined by one Newton step is within 2^-16 of x / f;
+// truncating it plus one half gives the quotient or one above it, which one
+// borrow test settles.
 __device__ __forceinline__ void divmod_q32(uint32_t xh, uint32_t xl, uint32_t f, uint32_t& q, uint32_t& r) {
     const double fd = static_cast<double>(f);
     double rc = __builtin_amdgcn_rcp(fd);
     rc = __fma_rn(rc, __fma_rn(-fd, rc, 1.0), rc);
     const double xd = __fma_rn(static_cast<double>(xh), 4294967296.0, static_cast<double>(xl));
-    const uint32_t q0 = static_cast<uint32_t>(__builtin_fmin(xd * rc, 4294967295.0));
-    // rem = x - q0 f lies in [-f, 2f): its high word is 0 or all ones
+    const uint32_t q0 = static_cast<uint32_t>(__builtin_fmin(__fma_rn(xd, rc, 0.5), 4294967295.0));
+    // rem = x - q0 f lies in [-f, f): negative exactly when the high word borrows
     const uint64_t p = static_cast<uint64_t>(q0) * f;
-    const uint32_t rl = xl - static_cast<uint32_t>(p);
-    const uint32_t rh = xh - static_cast<uint32_t>(p >> 32) - (xl < static_cast<uint32_t>(p) ? 1u : 0u);
-    const bool neg = rh != 0u;
-    const bool big = !neg && rl >= f;
-    q = neg ? q0 - 1u : (big ? q0 + 1u : q0);
-    r = neg ? rl + f : (big ? rl - f : rl);
+    const uint64_t rem = ((static_cast<uint64_t>(xh) << 32) | xl) - p;
+    const bool neg = static_cast<int64_t>(rem) < 0;
+    q = q0 - (neg ? 1u : 0u);
+    r = static_cast<uint32_t>(rem) + (neg ? f : 0u);
 }
 
 // Both cell edges of the bf16 symbol with bit pattern u: the inner edge
@@ -252,6 +254,22 @@ __device__ __forceinline__ void bf16_cell_edges(uint32_t u, float& lo, float& hi
     ob = m >= 0x7F7Fu ? 0x7F800000u : ob;
     ib = m >= 0x7F80u ? 0x7F800000u : ib;
     ib = m == 0u ? 0u : ib;
+    const uint32_t sb = (u & 0x8000u) << 16;
+    const bool neg = sb != 0u;
+    lo = __uint_as_float((neg ? ob : ib) | sb);
+    hi = __uint_as_float((neg ? ib : ob) | sb);
+}
+
+// The same edges where the mean is a bf16 value: the edges beyond +-max may
+// stay finite (the midpoint past max), because a bf16 mean lies at least half
+// a bf16 step inside them and z saturates at +-24 exactly as for an infinite
+// edge (sigma <= 2^96).  Inf and NaN patterns are taken as +-Inf.
+__device__ __forceinline__ void bf16_cell_edges_bf16_mean(uint32_t u, float& lo, float& hi) {
+    uint32_t m = u & 0x7FFFu;
+    m = m < 0x7F80u ? m : 0x7F80u;
+    const uint32_t ob0 = (m << 16) | 0x8000u;
+    const uint32_t ib = __builtin_elementwise_sub_sat(ob0, 0x10000u);   // 0 for +-0
+    const uint32_t ob = ob0 < 0x7F800000u ? ob0 : 0x7F800000u;
     const uint32_t sb = (u & 0x8000u) << 16;
     const bool neg = sb != 0u;
     lo = __uint_as_float((neg ? ob : ib) | sb);

@@ -193,12 +193,14 @@ __device__ __forceinline__ void rans_push(PushState& st, uint32_t c0, uint32_t f
 }
 
 // Start and frequency of the symbol with bit pattern kb under the mixture.
-template <int KV>
+template <int KV, int MU>
 __device__ __forceinline__ void symbol_range(uint32_t kb, float mu, float inv24, const Model& m, uint32_t& c0,
                                              uint32_t& f) {
     const uint32_t s = order_of_bits<KV>(kb);
     float lo, hi;
-    if constexpr (KV == kBF16) {
+    if constexpr (KV == kBF16 && MU == kBF16) {
+        bf16_cell_edges_bf16_mean(kb, lo, hi);
+    } else if constexpr (KV == kBF16) {
         bf16_cell_edges(kb, lo, hi);
     } else {
         lo = edge<KV>(s);
@@ -214,6 +216,13 @@ __device__ __forceinline__ void symbol_range(uint32_t kb, float mu, float inv24,
     f = b - a;
 }
 
+// Element `lane` of a row whose base is wave-uniform: the base stays in
+// scalar registers and the lane adds a 32-bit byte offset.
+template <typename T>
+__device__ __forceinline__ const T& row_elem(const T* __restrict__ row, uint32_t lane) {
+    return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(row) + lane * static_cast<uint32_t>(sizeof(T)));
+}
+
 template <int KV, int MU, int U>
 __device__ __forceinline__ void encode_batch(int t, PushState& st, const typename Alphabet<KV>::Bits* __restrict__ kvb,
                                              const typename MuT<MU>::T* __restrict__ mub, uint32_t D, uint32_t lane,
@@ -222,13 +231,13 @@ __device__ __forceinline__ void encode_batch(int t, PushState& st, const typenam
     typename MuT<MU>::T mb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint32_t off = static_cast<uint32_t>(t - u) * D + lane;
-        kb[u] = kvb[off];
-        mb[u] = mub[off];
+        const uint64_t row = static_cast<uint64_t>(t - u) * D;
+        kb[u] = row_elem(kvb + row, lane);
+        mb[u] = row_elem(mub + row, lane);
     }
     uint32_t c0[U], fr[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) symbol_range<KV>(kb[u], mu_value<MU>(mb[u]), inv24, m, c0[u], fr[u]);
+    for (int u = 0; u < U; ++u) symbol_range<KV, MU>(kb[u], mu_value<MU>(mb[u]), inv24, m, c0[u], fr[u]);
 #pragma unroll
     for (int u = 0; u < U; ++u) rans_push(st, c0[u], fr[u], slot);
 }
@@ -712,7 +721,7 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < kDecodeBatch; ++u) {
             const uint32_t t = t0 + u < cp.len ? t0 + u : cp.len - 1;
-            raw[u] = mup[t * D + lane];
+            raw[u] = row_elem(mup + static_cast<uint64_t>(t) * D, static_cast<uint32_t>(lane));
         }
 #pragma unroll
         for (int u = 0; u < kDecodeBatch; ++u) {
@@ -798,7 +807,9 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
             x = (static_cast<unsigned long long>(nh) << 32) | nl;
             rp += n1 + __popcll(m2);
             win.advance(rp, static_cast<uint32_t>(lane));
-            outp[(t0 + u) * D + lane] = static_cast<KB>(bits_of_order<KV>(fd.s));
+            KB* orow = outp + static_cast<uint64_t>(t0 + u) * D;
+            *reinterpret_cast<KB*>(reinterpret_cast<char*>(orow) + static_cast<uint32_t>(lane) * sizeof(KB)) =
+                static_cast<KB>(bits_of_order<KV>(fd.s));
         }
     }
     // every lane back at the initial state, the payload consumed exactly,
