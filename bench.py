@@ -24,6 +24,39 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["entropy_coding_amd/csrc/kvc_kernels.hip", "entropy_coding_amd/csrc/kvc_device.hpp",
+                  "entropy_coding_amd/csrc/kvc_internal.hpp"]
+TRAFFIC_FILE = "profiles/traffic_qwen3-8b_bf16.txt"
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of each coding kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by what the same
+    counter reads for a copy of known size), or {} when the summary is
+    missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return {}
+    out, sha = {}, None
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and parts[0] == "kernel_sources_sha256":
+                sha = parts[1]
+            elif len(parts) >= 3 and parts[0] == "traffic":
+                kv = dict(p.split("=", 1) for p in parts[2:])
+                out[parts[1]] = {k: float(v) for k, v in kv.items()}
+    return out if sha == kernel_sources_sha256() else {}
 
 
 def log(*a):
@@ -128,6 +161,8 @@ def main():
     ap.add_argument("--cpu-planes-per-worker", type=int, default=8)
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--chunk-tokens", type=int, default=None, help="override the workload's chunk length")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="after the timed steps, copy 1 GiB once (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -186,6 +221,13 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {elapsed:.3f} s")
+    if args.traffic_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] traffic probe: copied 1 GiB")
     ok = torch.equal(kv_out, kv.view(torch.int16))
     if not ok:
         raise SystemExit("decoded KV differs from the input")
@@ -204,9 +246,16 @@ def main():
     # algorithmic bytes of the coding kernels: KV and mu in, words and states
     # out (encode); words and states and mu in, KV out (decode)
     alg = 4.0 * n + stream_bytes
-    dominant = "decode" if dec_kernel >= enc_kernel else "encode"
-    dom_ms = max(dec_kernel, enc_kernel)
-    achieved = alg / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+
+    def roofline(kernel, avg_ms):
+        a = alg / (avg_ms * 1e-3) / 1e9
+        t = traffic.get(kernel, {}).get("total")
+        return {"bound": "hbm", "kernel": kernel, "achieved": a, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": a / HBM_PEAK_GBPS, "traffic": t, "algorithmic_bytes": alg, "avg_ms": avg_ms}
+
+    rl = {"k_encode": roofline("k_encode", enc_kernel), "k_decode": roofline("k_decode", dec_kernel)}
+    dominant = "k_decode" if dec_kernel >= enc_kernel else "k_encode"
     res = {
         "metric": "encode/decode GB/s of raw KV + bits/scalar, Qwen3-8B-shaped bf16 KV",
         "value": raw / (ms_per_step * 1e-3) / 1e9,
@@ -235,11 +284,8 @@ def main():
         "stream_bytes": stream_bytes,
         "decode_fallback_share": fallback[0] / n,
         "roundtrip_exact": ok,
-        "roofline": {
-            "bound": "hbm", "kernel": f"k_{dominant}", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-            "algorithmic_bytes": alg, "avg_ms": dom_ms,
-        },
+        "roofline": rl[dominant],
+        "rooflines": rl,
         "cpu_baseline": cpu,
         "pages_context": {"bits_per_scalar_qwen3_0.6B_to_32B": [6.74, 5.92],
                           "fp8_bits_per_element": [2.05, 2.59]},

@@ -462,7 +462,7 @@ struct Aim {
 __device__ __forceinline__ float aim_pos(int32_t e, float mu, float sg, const Aim& a) {
     const float ef = __builtin_amdgcn_fmed3f(static_cast<float>(e) * a.scale, 0.0f, static_cast<float>(kZinvSteps));
     const int j = static_cast<int>(ef);                // ef >= 0: truncation is floor
-    const float fr = ef - static_cast<float>(j);
+    const float fr = __builtin_amdgcn_fractf(ef);
     const float z0 = a.zinv[j], z1 = a.zinv[j + 1];
     const float z = __fmaf_rn(fr, z1 - z0, z0);
     return __fmaf_rn(z, sg, mu);
@@ -488,10 +488,10 @@ constexpr uint32_t kBf16OuterMag = 0x7F7F8000u;    // midpoint above +max
 __device__ __forceinline__ Bf16Edge nearest_edge_bf16(float x) {
     const float lim = __uint_as_float(kBf16OuterMag);
     const uint32_t u = __float_as_uint(__builtin_amdgcn_fmed3f(x, -lim, lim));
-    const uint32_t m = (u >> 16) & 0x7FFFu;
+    const uint32_t h = u >> 16;                      // bf16 pattern below x's magnitude
     Bf16Edge r;
     r.sign = u & 0x80000000u;
-    r.e = r.sign ? 32767u - m : 32769u + m;
+    r.e = r.sign ? (h ^ 0xFFFFu) : h + 32769u;       // 32767 - m or 32769 + m
     r.mag = (u & 0x7FFF0000u) | 0x8000u;
     return r;
 }
@@ -642,7 +642,11 @@ __device__ __forceinline__ uint32_t coarse_prefix(const uint32_t* s_pc, uint32_t
         constexpr int sh = Coarse<KV>::kShift;
         const uint32_t j = b >> sh, r = b & ((1u << sh) - 1u);
         const uint32_t lo = s_pc[j], hi = s_pc[j + 1];
-        return lo + (((hi - lo) * r) >> sh);     // hi - lo <= T_e < 2^26
+        // (hi - lo) >> sh < 2^20: a 24-bit multiply; the dropped low bits move
+        // the guess by under 2^sh slots
+        const uint32_t step = (hi - lo) >> sh;
+        __builtin_assume(step < (1u << 20));
+        return lo + step * r;
     }
 }
 
