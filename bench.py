@@ -129,8 +129,8 @@ def prepare(workload, dev, calib_reps: int):
 
     w = workload
     G, T, D = w.planes, w.tokens, w.channels
-    kv = torch.empty((G, T, D), dtype=torch.bfloat16, device=dev)
-    mu = torch.empty((G, T, D), dtype=torch.bfloat16, device=dev)
+    kv = torch.empty((G, T, D), dtype=torch.bfloat16 if w.kv_dtype == W.BF16 else torch.uint8, device=dev)
+    mu = torch.empty((G, T, D), dtype=torch.bfloat16 if w.mu_dtype == W.BF16 else torch.float32, device=dev)
     sigma = torch.empty((G, D), dtype=torch.float32, device=dev)
     ppl = w.planes_per_layer
     t0 = time.perf_counter()
@@ -155,7 +155,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, help="workload id (bench line: 2)")
+    ap.add_argument("--workload", type=int, default=2,
+                    help="workload id: 2 = the bench line; 1 and 3 code the whole cache in one call, 4 one layer per call")
     ap.add_argument("--calib-reps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-planes-per-worker", type=int, default=8)
@@ -172,11 +173,12 @@ def main():
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from entropy_coding_amd import workloads as W
     w = W.WORKLOADS[args.workload]
-    if w.kv_dtype != W.BF16:
-        raise SystemExit("the bench line is defined on a bf16 workload")
+    if args.workload == 0:
+        raise SystemExit("workload 0 is a parity case (1M scalars), not a bench line")
+    per_layer = args.workload == 4            # streamed one layer per call
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and w.kv_dtype == W.BF16:
         log("[bench] cpu_baseline: oracle on a host sample ...")
         cpu = cpu_baseline(w, args.cpu_planes_per_worker, args.cpu_tokens)
         log(f"[bench] cpu_baseline {cpu['value']:.4f} GB/s on {cpu['cores']} cores")
@@ -191,24 +193,41 @@ def main():
     n = w.n_scalars
     weights = (w.w_narrow_bp, w.w_wide_bp)
     tc = args.chunk_tokens if args.chunk_tokens else w.chunk_tokens
-    p = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, w.planes, w.tokens, w.channels, weights, tc)
+    kv_code = kvc.KVC_BF16 if w.kv_dtype == W.BF16 else kvc.KVC_E4M3
+    mu_code = kvc.KVC_BF16 if w.mu_dtype == W.BF16 else kvc.KVC_F32
+    kv_size = 2 if w.kv_dtype == W.BF16 else 1
+    mu_size = 2 if w.mu_dtype == W.BF16 else 4
+    # one call over the whole cache, or one call per layer
+    parts = ([slice(l * w.planes_per_layer, (l + 1) * w.planes_per_layer) for l in range(w.layers)]
+             if per_layer else [slice(0, w.planes)])
+    g_part = parts[0].stop - parts[0].start
+    p = kvc.make_params(kv_code, mu_code, g_part, w.tokens, w.channels, weights, tc)
     enc = kvc.Encoder(p, dev)
-    kv_out = torch.empty((w.planes, w.tokens, w.channels), dtype=torch.int16, device=dev)
+    kv_out = torch.empty((w.planes, w.tokens, w.channels), dtype=torch.int16 if kv_size == 2 else torch.uint8,
+                         device=dev)
     dws = torch.empty(kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
-    log(f"[bench] buffers: stream capacity {enc.capacity / 1e9:.2f} GB, workspace {enc.workspace.numel() / 1e9:.2f} GB")
+    log(f"[bench] buffers: stream capacity {enc.capacity / 1e9:.2f} GB, workspace {enc.workspace.numel() / 1e9:.2f} GB,"
+        f" {len(parts)} call(s) per step")
 
     fallback = [0]
+    stream_total = [0]
 
     def step(stats=None):
-        ei, di = {}, {}
-        st = enc(kv, mu, sigma, prefix, info=ei)
-        rc = kvc.kvc_decode_into(st, mu, sigma, prefix, kv_out, dws, info=di)
-        if rc != kvc.KVC_OK:
-            raise kvc.KvcError(rc, "kvc_decode")
-        fallback[0] = di["fallback_symbols"]
+        e_ms, d_ms = [0.0] * 4, [0.0] * 2
+        fb, nbytes = 0, 0
+        for sl in parts:
+            ei, di = {}, {}
+            st = enc(kv[sl], mu[sl], sigma[sl], prefix, info=ei)
+            rc = kvc.kvc_decode_into(st, mu[sl], sigma[sl], prefix, kv_out[sl], dws, info=di)
+            if rc != kvc.KVC_OK:
+                raise kvc.KvcError(rc, "kvc_decode")
+            e_ms = [a + b for a, b in zip(e_ms, ei["stage_ms"])]
+            d_ms = [a + b for a, b in zip(d_ms, di["stage_ms"])]
+            fb += di["fallback_symbols"]
+            nbytes += st.numel()
+        fallback[0], stream_total[0] = fb, nbytes
         if stats is not None:
-            stats.append((ei["stage_ms"], di["stage_ms"]))
-        return st
+            stats.append((e_ms, d_ms))
 
     for i in range(args.warmup):
         step()
@@ -217,7 +236,7 @@ def main():
     stats = []
     t0 = time.perf_counter()
     for i in range(args.steps):
-        st = step(stats)
+        step(stats)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {elapsed:.3f} s")
@@ -228,11 +247,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("[bench] traffic probe: copied 1 GiB")
-    ok = torch.equal(kv_out, kv.view(torch.int16))
+    ok = torch.equal(kv_out, kv.view(torch.int16) if kv_size == 2 else kv)
     if not ok:
         raise SystemExit("decoded KV differs from the input")
-    stream_bytes = st.numel()
-    bits_int, bits_float = kvc.kvc_estimate_bits(kv, mu, sigma, prefix, weights)
+    stream_bytes = stream_total[0]
+    bits_int, bits_float = 0.0, 0.0
+    for sl in parts:
+        bi, bf = kvc.kvc_estimate_bits(kv[sl], mu[sl], sigma[sl], prefix, weights)
+        frac = (sl.stop - sl.start) / w.planes
+        bits_int += bi * frac
+        bits_float += bf * frac
 
     def mean(xs):
         return sum(xs) / len(xs)
@@ -242,11 +266,11 @@ def main():
     dec_kernel = mean([s[1][1] for s in stats])
     dec_total = mean([sum(s[1]) for s in stats])
     ms_per_step = elapsed / args.steps * 1e3
-    raw = 2.0 * n
+    raw = float(kv_size) * n
     # algorithmic bytes of the coding kernels: KV and mu in, words and states
     # out (encode); words and states and mu in, KV out (decode)
-    alg = 4.0 * n + stream_bytes
-    traffic = measured_traffic()
+    alg = float(kv_size + mu_size) * n + stream_bytes
+    traffic = measured_traffic() if args.workload == 2 and tc == w.chunk_tokens else {}
 
     def roofline(kernel, avg_ms):
         a = alg / (avg_ms * 1e-3) / 1e9
@@ -257,7 +281,8 @@ def main():
     rl = {"k_encode": roofline("k_encode", enc_kernel), "k_decode": roofline("k_decode", dec_kernel)}
     dominant = "k_decode" if dec_kernel >= enc_kernel else "k_encode"
     res = {
-        "metric": "encode/decode GB/s of raw KV + bits/scalar, Qwen3-8B-shaped bf16 KV",
+        "metric": "encode/decode GB/s of raw KV + bits/scalar, Qwen3-8B-shaped bf16 KV" if args.workload == 2
+                  else f"encode/decode GB/s of raw KV + bits/scalar, {w.name}",
         "value": raw / (ms_per_step * 1e-3) / 1e9,
         "unit": "GB/s",
         "n_gpus": 1,
@@ -267,12 +292,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if kv_size == 2 else "e4m3",
         "data": "synthetic",
         "config": {
             "workload": w.name, "shape": [w.layers, 2, w.batch, w.heads, w.tokens, w.channels],
             "scalars": n, "mixture_bp": list(weights), "chunk_tokens": tc,
             "sigma_calibration": f"{reps}x{w.calib_tokens} tokens per layer",
+            "mu_dtype": "bf16" if mu_size == 2 else "fp32", "calls_per_step": len(parts),
         },
         "encode_gbps": raw / (enc_total * 1e-3) / 1e9,
         "decode_gbps": raw / (dec_total * 1e-3) / 1e9,

@@ -59,10 +59,24 @@ bool geometry(int64_t planes, int64_t tokens, int64_t channels, uint32_t chunk_t
     return true;
 }
 
+// Default chunk length: 1024 tokens (at most the sequence), halved down to
+// 256 while the call has fewer chunks than MI355X has wave slots (256 CUs x
+// 32 waves), since each chunk is one wave.  Shorter chunks cost about 47 bits
+// per lane of final state, so they are used only where they add waves.
+constexpr int64_t kWaveSlots = 256 * 32;
+
+uint32_t default_chunk_tokens(int64_t planes, int64_t tokens, int64_t channels) {
+    int64_t tc = tokens < 1024 ? (tokens > 0 ? tokens : 1) : 1024;
+    if (planes <= 0 || channels < 64) return static_cast<uint32_t>(tc);
+    auto chunks = [&](int64_t c) { return planes * ((tokens + c - 1) / c) * (channels / 64); };
+    while (tc > 256 && chunks(tc) < kWaveSlots) tc = (tc + 1) / 2;
+    return static_cast<uint32_t>(tc);
+}
+
 bool params_geometry(const kvc_params* p, ChunkGeom* g) {
     if (!p || !kv_dtype_ok(p->kv_dtype) || !mu_dtype_ok(p->mu_dtype) || p->reserved != 0) return false;
     uint32_t tc = p->chunk_tokens;
-    if (tc == 0) tc = static_cast<uint32_t>(p->tokens < 1024 ? (p->tokens > 0 ? p->tokens : 1) : 1024);
+    if (tc == 0) tc = default_chunk_tokens(p->planes, p->tokens, p->channels);
     return geometry(p->planes, p->tokens, p->channels, tc, g);
 }
 
@@ -386,7 +400,7 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
 
 int kvc_calibrate_sigma(const void* d_kv, const void* d_mu, int32_t kv_dtype, int32_t mu_dtype, int64_t reps,
                         int64_t planes, int64_t tokens, int64_t channels, float sigma_floor, float* d_sigma_out,
-                        void* stream) {
+                        void* d_workspace, uint64_t workspace_bytes, void* stream) {
     if (!d_kv || !d_mu || !d_sigma_out || !kv_dtype_ok(kv_dtype) || !mu_dtype_ok(mu_dtype)) return KVC_ERR_INVALID;
     if (!data_aligned(kv_dtype, mu_dtype, d_kv, d_mu, d_sigma_out, nullptr)) return KVC_ERR_INVALID;
     if (reps < 1 || planes < 1 || tokens < 1 || channels < 64 || channels % 64) return KVC_ERR_INVALID;
@@ -396,8 +410,14 @@ int kvc_calibrate_sigma(const void* d_kv, const void* d_mu, int32_t kv_dtype, in
         return KVC_ERR_INVALID;
     if (planes * (channels / 64) > 0x7FFFFFFF) return KVC_ERR_INVALID;
     if (!(sigma_floor > 0.0f) || !(sigma_floor <= FLT_MAX)) return KVC_ERR_INVALID;
+    // partial sums: one CalibPart per (split, plane, channel), at most 64 splits
+    static_assert(sizeof(kvc::CalibPart) * kvc::kCalibSplitsMax == 1024, "workspace formula");
+    if (!d_workspace || !aligned(d_workspace, 256) || planes * channels > kMaxScalars / 1024 ||
+        workspace_bytes < KVC_CALIBRATE_WORKSPACE_BYTES(planes, channels))
+        return KVC_ERR_INVALID;
     return finish(kvc::launch_calibrate(d_kv, d_mu, kv_dtype, mu_dtype, reps, planes, tokens, channels,
-                                        sigma_floor, d_sigma_out, static_cast<hipStream_t>(stream)));
+                                        sigma_floor, d_sigma_out, static_cast<kvc::CalibPart*>(d_workspace),
+                                        static_cast<hipStream_t>(stream)));
 }
 
 int kvc_build_marginal(const void* d_samples, int32_t dtype, uint64_t n, uint32_t w_narrow_bp,

@@ -112,9 +112,16 @@ hipError_t launch_scan(const uint32_t* chunk_words, int64_t n_chunks,
                        unsigned long long* directory, Control* ctl, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);
-hipError_t launch_calibrate(const void* kv, const void* mu, int kv_dtype, int mu_dtype,
-                            int64_t reps, int64_t planes, int64_t tokens, int64_t channels,
-                            float sigma_floor, float* sigma_out, hipStream_t s);
+// sigma calibration: float64 partial sums per (split, plane, channel)
+struct CalibPart {
+    double sum;
+    unsigned long long used;
+};
+constexpr int64_t kCalibSplitsMax = 64;
+int64_t calibrate_splits(int64_t reps, int64_t planes, int64_t tokens, int64_t channels);
+hipError_t launch_calibrate(const void* kv, const void* mu, int kv_dtype, int mu_dtype, int64_t reps,
+                            int64_t planes, int64_t tokens, int64_t channels, float sigma_floor,
+                            float* sigma_out, CalibPart* part, hipStream_t s);
 hipError_t launch_marginal(const void* samples, int dtype, uint64_t n, uint32_t te,
                            uint32_t* prefix_out, hipStream_t s);
 hipError_t launch_estimate(const EstimateArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);

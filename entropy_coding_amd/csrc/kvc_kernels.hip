@@ -860,59 +860,121 @@ __device__ __forceinline__ double kv_value_f64(typename Alphabet<KV>::Bits b) {
     }
 }
 
+// Pass 1: block (plane and 64-channel group, split) sums the squared
+// residuals of a contiguous range of the reps x tokens rows.  Its 4 waves
+// take every 4th row; each lane keeps one channel's float64 sum in row order
+// and the waves are added in wave order, so the partial does not depend on
+// scheduling.  Rows are loaded 4 at a time to keep loads in flight.
+constexpr int kCalibBlock = 256;
+constexpr int kCalibWaves = kCalibBlock / 64;
+constexpr int kCalibUnroll = 4;
+
 template <int KV, int MU>
-__global__ void __launch_bounds__(1024) k_calibrate(const void* kv_, const void* mu_, int64_t reps,
-                                                    int64_t planes, int64_t tokens, int64_t channels,
-                                                    float floor_, float* __restrict__ out) {
-    __shared__ double s_part[16][64];
-    __shared__ int64_t s_used[16][64];
+__global__ void __launch_bounds__(kCalibBlock) k_calibrate_part(const void* kv_, const void* mu_, int64_t reps,
+                                                                int64_t planes, int64_t tokens, int64_t channels,
+                                                                CalibPart* __restrict__ part) {
+    __shared__ double s_sum[kCalibWaves][64];
+    __shared__ unsigned long long s_used[kCalibWaves][64];
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
     const KB* __restrict__ kv = static_cast<const KB*>(kv_);
     const MT* __restrict__ mu = static_cast<const MT*>(mu_);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int64_t groups = channels / 64;
     const int64_t p = blockIdx.x / groups;
     const int64_t d = (blockIdx.x % groups) * 64 + lane;
+    const int64_t splits = gridDim.y, s = blockIdx.y;
     const int64_t rows = reps * tokens;
+    const int64_t r1 = rows * (s + 1) / splits;
+    int64_t r = rows * s / splits + wave;
+    int64_t rep = r / tokens, t = r - rep * tokens;      // advanced by carries below
     double acc = 0.0;
-    int64_t used = 0;
-    for (int64_t r = wave; r < rows; r += 16) {
-        const int64_t rep = r / tokens, t = r - rep * tokens;
-        const int64_t off = ((rep * planes + p) * tokens + t) * channels + d;
-        const double e = kv_value_f64<KV>(kv[off]) - static_cast<double>(mu_value<MU>(mu[off]));
-        const double e2 = e * e;
-        if (__builtin_isfinite(e2)) {
-            acc += e2;
-            ++used;
+    unsigned long long used = 0;
+    while (r < r1) {                                     // wave-uniform
+        KB kb[kCalibUnroll];
+        MT mb[kCalibUnroll];
+        bool live[kCalibUnroll];
+#pragma unroll
+        for (int u = 0; u < kCalibUnroll; ++u) {
+            live[u] = r < r1;
+            if (live[u]) {
+                const int64_t off = ((rep * planes + p) * tokens + t) * channels + d;
+                kb[u] = kv[off];
+                mb[u] = mu[off];
+            }
+            r += kCalibWaves;
+            t += kCalibWaves;
+            while (t >= tokens) {
+                t -= tokens;
+                ++rep;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCalibUnroll; ++u) {
+            if (!live[u]) continue;
+            const double e = kv_value_f64<KV>(kb[u]) - static_cast<double>(mu_value<MU>(mb[u]));
+            const double e2 = e * e;
+            if (__builtin_isfinite(e2)) {
+                acc += e2;
+                ++used;
+            }
         }
     }
-    s_part[wave][lane] = acc;
+    s_sum[wave][lane] = acc;
     s_used[wave][lane] = used;
     __syncthreads();
     if (wave == 0) {
-        double s = 0.0;
-        int64_t u = 0;
-        for (int w = 0; w < 16; ++w) { s += s_part[w][lane]; u += s_used[w][lane]; }
-        const float sg = u ? static_cast<float>(sqrt(s / static_cast<double>(u))) : 0.0f;
-        out[p * channels + d] = (sg > floor_ && __builtin_isfinite(sg)) ? sg : floor_;
+        double sum = 0.0;
+        unsigned long long u = 0;
+        for (int w = 0; w < kCalibWaves; ++w) {
+            sum += s_sum[w][lane];
+            u += s_used[w][lane];
+        }
+        part[s * planes * channels + p * channels + d] = CalibPart{sum, u};
     }
+}
+
+// Pass 2: one thread per (plane, channel) adds the splits in order.
+__global__ void k_calibrate_final(const CalibPart* __restrict__ part, int64_t splits, int64_t n, float floor_,
+                                  float* __restrict__ out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    double sum = 0.0;
+    unsigned long long u = 0;
+    for (int64_t s = 0; s < splits; ++s) {
+        sum += part[s * n + i].sum;
+        u += part[s * n + i].used;
+    }
+    const float sg = u ? static_cast<float>(sqrt(sum / static_cast<double>(u))) : 0.0f;
+    out[i] = (sg > floor_ && __builtin_isfinite(sg)) ? sg : floor_;
+}
+
+int64_t calibrate_splits(int64_t reps, int64_t planes, int64_t tokens, int64_t channels) {
+    const int64_t pairs = planes * (channels / 64);
+    int64_t sp = (4096 + pairs - 1) / pairs;             // about 4096 blocks in all
+    sp = sp < 1 ? 1 : (sp > kCalibSplitsMax ? kCalibSplitsMax : sp);
+    const int64_t rows = reps * tokens;
+    return sp > rows ? rows : sp;
 }
 
 hipError_t launch_calibrate(const void* kv, const void* mu, int kv_dtype, int mu_dtype, int64_t reps,
                             int64_t planes, int64_t tokens, int64_t channels, float sigma_floor,
-                            float* sigma_out, hipStream_t s) {
-    const int64_t blocks = planes * (channels / 64);
-    const dim3 grid(static_cast<uint32_t>(blocks)), block(1024);
+                            float* sigma_out, CalibPart* part, hipStream_t s) {
+    const int64_t splits = calibrate_splits(reps, planes, tokens, channels);
+    const dim3 grid(static_cast<uint32_t>(planes * (channels / 64)), static_cast<uint32_t>(splits)), block(kCalibBlock);
     if (kv_dtype == kBF16 && mu_dtype == kBF16)
-        hipLaunchKernelGGL((k_calibrate<kBF16, kBF16>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, sigma_floor, sigma_out);
+        hipLaunchKernelGGL((k_calibrate_part<kBF16, kBF16>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, part);
     else if (kv_dtype == kBF16 && mu_dtype == kF32)
-        hipLaunchKernelGGL((k_calibrate<kBF16, kF32>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, sigma_floor, sigma_out);
+        hipLaunchKernelGGL((k_calibrate_part<kBF16, kF32>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, part);
     else if (kv_dtype == kE4M3 && mu_dtype == kBF16)
-        hipLaunchKernelGGL((k_calibrate<kE4M3, kBF16>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, sigma_floor, sigma_out);
+        hipLaunchKernelGGL((k_calibrate_part<kE4M3, kBF16>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, part);
     else if (kv_dtype == kE4M3 && mu_dtype == kF32)
-        hipLaunchKernelGGL((k_calibrate<kE4M3, kF32>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, sigma_floor, sigma_out);
+        hipLaunchKernelGGL((k_calibrate_part<kE4M3, kF32>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, part);
     else return hipErrorInvalidValue;
+    const int64_t n = planes * channels;
+    hipLaunchKernelGGL(k_calibrate_final, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s, part, splits,
+                       n, sigma_floor, sigma_out);
     return hipGetLastError();
 }
 

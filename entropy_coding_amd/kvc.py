@@ -75,7 +75,8 @@ _lib_encode_sizes = _sig("kvc_encode_sizes", ctypes.c_int, [ctypes.POINTER(kvc_p
 _lib_encode = _sig("kvc_encode", ctypes.c_int, [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _U64, ctypes.POINTER(_U64), _P, _U64, _P, _P])
 _lib_stream_info = _sig("kvc_stream_info", ctypes.c_int, [_P, _U64, ctypes.POINTER(kvc_params), ctypes.POINTER(_U64)])
 _lib_decode = _sig("kvc_decode", ctypes.c_int, [_P, _U64, _P, _P, _P, _P, _P, _U64, _P, _P])
-_lib_calibrate = _sig("kvc_calibrate_sigma", ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P])
+_lib_calibrate = _sig("kvc_calibrate_sigma", ctypes.c_int,
+                      [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _U64, _P])
 _lib_marginal = _sig("kvc_build_marginal", ctypes.c_int, [_P, _I32, _U64, _U32, _U32, _P, _P])
 _lib_estimate = _sig("kvc_estimate_bits", ctypes.c_int, [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _P, _U64, _P])
 _lib_cdf_table = _sig("kvc_cdf_table", ctypes.c_int, [_I32, _I32, _U32, _U32, _P, _P, _I64, _P, _P, _P])
@@ -232,16 +233,23 @@ def kvc_decode_into(stream_bytes, mu, sigma, prefix, kv_out, workspace, stream=N
     return st
 
 
+def calibrate_workspace_bytes(planes: int, channels: int) -> int:
+    return planes * channels * 1024
+
+
 def kvc_calibrate_sigma(kv: torch.Tensor, mu: torch.Tensor, sigma_floor: float = 2.0 ** -30,
-                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
     """kv, mu: [reps, planes, tokens, channels] -> sigma [planes, channels]."""
     _need(kv, "kv")
     _need(mu, "mu")
     r, g, t, d = kv.shape
     if out is None:
         out = torch.empty((g, d), dtype=torch.float32, device=kv.device)
+    if workspace is None:
+        workspace = torch.empty(calibrate_workspace_bytes(g, d), dtype=torch.uint8, device=kv.device)
     st = _lib_calibrate(_ptr(kv), _ptr(mu), _kv_dtype(kv), _mu_dtype(mu), r, g, t, d, sigma_floor,
-                        _ptr(out), _stream(stream))
+                        _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "kvc_calibrate_sigma")
     return out
 

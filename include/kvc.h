@@ -80,7 +80,9 @@ typedef struct kvc_params {
     uint32_t w_wide_bp;      /* weight of N(mu, (3 sigma)^2), basis points: 300     */
                              /* the escape part p_hat gets 10000 - both; (10000, 0)
                                 is a single Gaussian and needs no prefix table     */
-    uint32_t chunk_tokens;   /* tokens per chunk; 0 = min(tokens, 1024);
+    uint32_t chunk_tokens;   /* tokens per chunk; 0 = min(tokens, 1024),
+                                halved down to 256 while the call has fewer
+                                than 8192 chunks (one per wave slot);
                                 chunk_tokens * channels < 2^31                  */
     uint32_t reserved;       /* must be 0                                          */
     int64_t planes;          /* G = layers * 2 * batch * kv_heads                  */
@@ -160,13 +162,19 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu,
  * 128 sequences of 1024 tokens).  d_kv and d_mu are [reps][planes][tokens]
  * [channels]; writes d_sigma_out[planes][channels] = max(sigma_floor,
  * sqrt(mean over reps and tokens of (kv - mu)^2)), accumulated in float64
- * in a fixed order (deterministic).  Returns KVC_ERR_INVALID for bad shapes
- * or a non-positive floor.  Does not synchronise.
+ * in a fixed order (deterministic); residuals that are not finite are left
+ * out, and a channel with none left gets the floor.  d_workspace (256-byte
+ * aligned) holds the float64 partial sums: at least
+ * KVC_CALIBRATE_WORKSPACE_BYTES(planes, channels) bytes.  Returns
+ * KVC_ERR_INVALID for bad shapes, a non-positive floor or a short
+ * workspace.  Does not synchronise.
  */
+#define KVC_CALIBRATE_WORKSPACE_BYTES(planes, channels) \
+    ((uint64_t)(planes) * (uint64_t)(channels) * 1024u)
 int kvc_calibrate_sigma(const void* d_kv, const void* d_mu, int32_t kv_dtype,
                         int32_t mu_dtype, int64_t reps, int64_t planes, int64_t tokens,
                         int64_t channels, float sigma_floor, float* d_sigma_out,
-                        void* stream);
+                        void* d_workspace, uint64_t workspace_bytes, void* stream);
 
 /*
  * Empirical marginal ([wiki] "mixture distribution": an empirical BF16

@@ -207,6 +207,30 @@ def test_calibrate_matches_oracle(kvc, cuda):
     assert ulp3.max() <= 1
 
 
+@pytest.mark.parametrize("reps,planes,tokens,channels", [
+    (1, 1, 1, 64),          # one row: one split
+    (3, 2, 1, 128),         # rows step over several reps at once (tokens < waves per block)
+    (5, 3, 3, 64),          # 15 rows in 15 splits, ragged carries
+    (7, 1, 333, 192),       # many splits of uneven length, three channel groups
+])
+def test_calibrate_odd_shapes(kvc, cuda, reps, planes, tokens, channels):
+    g = torch.Generator(device="cpu").manual_seed(reps * 1000 + tokens)
+    mu = (torch.randn((reps, planes, tokens, channels), generator=g) * 0.5).to(torch.bfloat16)
+    kv = (mu.float() + 0.05 * torch.randn(mu.shape, generator=g)).to(torch.bfloat16)
+    got = kvc.kvc_calibrate_sigma(kv.to(cuda), mu.to(cuda)).cpu().numpy()
+    expect = O.calibrate_sigma(W.to_numpy_bits(kv), W.to_numpy_bits(mu), O.BF16, O.BF16, 2.0 ** -30)
+    ulp = np.abs(got.view(np.int32).astype(np.int64) - expect.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1
+
+
+def test_calibrate_rejects_short_workspace(kvc, cuda):
+    kv = torch.zeros((2, 3, 8, 64), dtype=torch.bfloat16, device=cuda)
+    ws = torch.empty(kvc.calibrate_workspace_bytes(3, 64) - 1, dtype=torch.uint8, device=cuda)
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_calibrate_sigma(kv, kv, workspace=ws)
+    assert e.value.status == kvc.KVC_ERR_INVALID
+
+
 # ---------------------------------------------------------------------------
 # error paths
 # ---------------------------------------------------------------------------

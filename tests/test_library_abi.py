@@ -60,6 +60,28 @@ def test_encode_sizes(kvc):
         assert e.value.status == kvc.KVC_ERR_INVALID
 
 
+@pytest.mark.parametrize("planes,tokens,channels,expect", [
+    (2304, 4096, 128, 1024),     # 18,432 chunks at 1024 tokens: already one per wave slot and more
+    (448, 1024, 128, 256),       # 896 chunks at 1024 -> 3,584 at 256 (the floor)
+    (16, 32768, 128, 256),       # one 32K-token layer: 1,024 -> 4,096 chunks
+    (576, 8192, 128, 1024),      # 9,216 chunks at 1024
+    (64, 4096, 128, 256),        # 512 -> 1,024 -> 2,048 chunks: the floor comes first
+    (512, 4096, 128, 512),       # 4,096 -> 8,192 chunks at 512: enough
+    (3, 45, 128, 45),            # short sequences keep one chunk per plane and group
+])
+def test_default_chunk_length(kvc, planes, tokens, channels, expect):
+    """chunk_tokens = 0 picks 1024 tokens, halved down to 256 while the call
+    has fewer chunks than the chip's 8,192 wave slots."""
+    auto = kvc.kvc_encode_sizes(kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, planes, tokens, channels, (9500, 300), 0))
+    fixed = kvc.kvc_encode_sizes(kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, planes, tokens, channels, (9500, 300),
+                                                 expect))
+    assert auto == fixed
+    if expect > 256:
+        other = kvc.kvc_encode_sizes(kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, planes, tokens, channels,
+                                                     (9500, 300), expect // 2))
+        assert other != auto
+
+
 def oracle_stream(kv_dtype=O.BF16, w=(9500, 300), tc=16):
     kv, mu, sig, samples = W.tiny_case(7, kv_dtype=kv_dtype)
     mu_dtype = O.BF16 if kv_dtype == O.BF16 else O.F32
