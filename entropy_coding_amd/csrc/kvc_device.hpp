@@ -260,20 +260,4 @@ __device__ __forceinline__ void bf16_cell_edges(uint32_t u, float& lo, float& hi
     hi = __uint_as_float((neg ? ib : ob) | sb);
 }
 
-// The same edges where the mean is a bf16 value: the edges beyond +-max may
-// stay finite (the midpoint past max), because a bf16 mean lies at least half
-// a bf16 step inside them and z saturates at +-24 exactly as for an infinite
-// edge (sigma <= 2^96).  Inf and NaN patterns are taken as +-Inf.
-__device__ __forceinline__ void bf16_cell_edges_bf16_mean(uint32_t u, float& lo, float& hi) {
-    uint32_t m = u & 0x7FFFu;
-    m = m < 0x7F80u ? m : 0x7F80u;
-    const uint32_t ob0 = (m << 16) | 0x8000u;
-    const uint32_t ib = __builtin_elementwise_sub_sat(ob0, 0x10000u);   // 0 for +-0
-    const uint32_t ob = ob0 < 0x7F800000u ? ob0 : 0x7F800000u;
-    const uint32_t sb = (u & 0x8000u) << 16;
-    const bool neg = sb != 0u;
-    lo = __uint_as_float((neg ? ob : ib) | sb);
-    hi = __uint_as_float((neg ? ib : ob) | sb);
-}
-
 }  // namespace kvc

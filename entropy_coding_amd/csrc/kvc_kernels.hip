@@ -179,8 +179,11 @@ __device__ __forceinline__ void rans_push(PushState& st, uint32_t c0, uint32_t f
     const uint64_t m2 = __ballot(e2);
     const uint32_t n1 = __popcll(m1), n2 = __popcll(m2);
     st.wp -= n1 + n2;
-    if (e1) slot[st.wp + lane_rank(m1)] = static_cast<uint16_t>(e2 ? (st.xl >> 16) : st.xl);
-    if (e2) slot[st.wp + n1 + lane_rank(m2)] = static_cast<uint16_t>(st.xl);
+    // wave-uniform bases in scalar registers, 32-bit lane offsets
+    char* r1 = reinterpret_cast<char*>(slot + st.wp);
+    char* r2 = reinterpret_cast<char*>(slot + st.wp + n1);
+    if (e1) *reinterpret_cast<uint16_t*>(r1 + 2u * lane_rank(m1)) = static_cast<uint16_t>(e2 ? (st.xl >> 16) : st.xl);
+    if (e2) *reinterpret_cast<uint16_t*>(r2 + 2u * lane_rank(m2)) = static_cast<uint16_t>(st.xl);
     uint32_t lo = e1 ? __builtin_amdgcn_alignbit(st.xh, st.xl, 16) : st.xl;
     uint32_t hi = e1 ? (st.xh >> 16) : st.xh;
     lo = e2 ? st.xh : lo;
@@ -196,11 +199,32 @@ __device__ __forceinline__ void rans_push(PushState& st, uint32_t c0, uint32_t f
 template <int KV, int MU>
 __device__ __forceinline__ void symbol_range(uint32_t kb, float mu, float inv24, const Model& m, uint32_t& c0,
                                              uint32_t& f) {
+    if constexpr (KV == kBF16 && MU == kBF16) {
+        // ord(u): u ^ 0x8000 for a positive pattern, u ^ 0xFFFF for a negative one
+        const uint32_t s = (kb ^ 0x8000u) ^ (static_cast<uint32_t>(static_cast<int32_t>(kb << 16) >> 31) & 0x7FFFu);
+        // both cell edges carry the value's sign; h is monotone in the
+        // position, so the lower edge's h is the smaller one on either side
+        uint32_t mg = kb & 0x7FFFu;
+        mg = __builtin_elementwise_min(mg, 0x7F80u);                  // Inf and NaN as Inf
+        const uint32_t ob0 = (mg << 16) | 0x8000u;
+        const uint32_t ib = __builtin_elementwise_sub_sat(ob0, 0x10000u);  // 0 for +-0
+        const uint32_t ob = __builtin_elementwise_min(ob0, 0x7F800000u);
+        const uint32_t sb = (kb & 0x8000u) << 16;
+        const uint32_t ha = h_fx(z_fixed(__uint_as_float(ib | sb), mu, inv24), m.tab);
+        const uint32_t hb = h_fx(z_fixed(__uint_as_float(ob | sb), mu, inv24), m.tab);
+        uint32_t a = s + __builtin_elementwise_min(ha, hb);
+        uint32_t b = s + 1u + __builtin_elementwise_max(ha, hb);
+        if (m.prefix) {
+            a += m.prefix[s];
+            b += m.prefix[s + 1];
+        }
+        c0 = a;
+        f = b - a;
+        return;
+    }
     const uint32_t s = order_of_bits<KV>(kb);
     float lo, hi;
-    if constexpr (KV == kBF16 && MU == kBF16) {
-        bf16_cell_edges_bf16_mean(kb, lo, hi);
-    } else if constexpr (KV == kBF16) {
+    if constexpr (KV == kBF16) {
         bf16_cell_edges(kb, lo, hi);
     } else {
         lo = edge<KV>(s);
@@ -509,6 +533,29 @@ __device__ __forceinline__ float edge_pattern(uint32_t mag, uint32_t sign) {
     return __uint_as_float(mag | sign);
 }
 
+// Position of bf16 edge b (any b in 0..N) through edge_pattern: magnitude
+// |b - 32768| * 2^16 - 2^15 (0 for the edge between -0 and +0), negative
+// below b = 32768; beyond the outer edges the pattern is pinned to Inf.
+template <int MU>
+__device__ __forceinline__ float edge_from_index_bf16(uint32_t b) {
+    const uint32_t a = b >= 32768u ? b - 32768u : 32768u - b;
+    const uint32_t mag = __builtin_elementwise_sub_sat(a << 16, 0x8000u);    // a <= 32768
+    return edge_pattern<MU>(mag, b < 32768u ? 0x80000000u : 0u);
+}
+
+// C(b) for the wave-cooperative search: the exact CDF, with the bf16 edge
+// taken through edge_from_index_bf16.
+template <int KV, int MU>
+__device__ __forceinline__ uint32_t cdf_probe(uint32_t b, float mu, float inv24, const Model& m) {
+    if constexpr (KV == kBF16) {
+        uint32_t g = b + h_fx(z_fixed(edge_from_index_bf16<MU>(b), mu, inv24), m.tab);
+        if (m.prefix) g += m.prefix[b];
+        return g;
+    } else {
+        return cdf_at<KV>(b, mu, inv24, m);
+    }
+}
+
 // Probe offsets for the first cooperative round: 1, 2, 3, ... then growing
 // geometrically to 65535 over the 63 probing lanes.
 __device__ __forceinline__ uint32_t geo_offset(int lane) {
@@ -524,7 +571,7 @@ struct Found {
 // The whole wave resolves every lane with `need` set, one lane at a time.
 // [lo, hi) brackets the lane's symbol with C(lo) = clo <= target < C(hi) = chi;
 // `up` tells which end is the known near one (lo if up).
-template <int KV>
+template <int KV, int MU>
 __device__ __forceinline__ void coop_search(bool need, uint32_t target, float mu, float inv24, bool up, uint32_t lo,
                                             uint32_t hi, uint32_t clo, uint32_t chi, const Model& m, uint32_t geo,
                                             Found& out) {
@@ -548,10 +595,11 @@ __device__ __forceinline__ void coop_search(bool need, uint32_t target, float mu
                 const uint32_t off = geo < span - 1u ? geo : span - 1u;
                 p = upL ? a + off : b - off;
             } else {
-                p = a + static_cast<uint32_t>((static_cast<uint64_t>(lane + 1) * span) >> 6);
+                __builtin_assume(span <= Alphabet<KV>::kSize);      // (lane + 1) * span < 2^23
+                p = a + ((static_cast<uint32_t>(lane + 1) * span) >> 6);
             }
             const bool valid = lane < 63 && p > a && p < b;
-            const uint32_t c = cdf_at<KV>(valid ? p : a, mL, iL, m);
+            const uint32_t c = cdf_probe<KV, MU>(valid ? p : a, mL, iL, m);
             const uint64_t mle = __ballot(valid && c <= t);
             const uint64_t mgt = __ballot(valid && c > t);
             // probe positions increase with the lane, except geometric probes
@@ -731,7 +779,7 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
         for (int u = 0; u < kDecodeBatch; ++u) {
             mus[u] = mu_value<MU>(raw[u]);
             const uint32_t gm = mean_symbol<KV, MU>(raw[u], mus[u]);
-            bias[u] = gm + coarse_prefix<KV>(s_pc, gm);
+            bias[u] = gm + s_pc[gm >> Coarse<KV>::kShift];        // first aim: the step is close enough
         }
 #pragma unroll
         for (int u = 0; u < kDecodeBatch; ++u) {
@@ -786,7 +834,7 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
             fd.freq = up ? c2 - cE : cE - c2;
             if (__ballot(!ok)) {
                 misses += ok ? 0u : 1u;
-                coop_search<KV>(!ok, target, mu, inv24, up, up ? E2 : 0u, up ? Alphabet<KV>::kSize : E2,
+                coop_search<KV, MU>(!ok, target, mu, inv24, up, up ? E2 : 0u, up ? Alphabet<KV>::kSize : E2,
                                 up ? c2 : 0u, up ? kM : c2, m, geo, fd);
             }
             // x < 2^63, so x >> 31 fits 32 bits: one 32 x 32 -> 64 multiply-add
