@@ -184,10 +184,10 @@ __device__ __forceinline__ void rans_push(PushState& st, uint32_t c0, uint32_t f
     char* r2 = reinterpret_cast<char*>(slot + st.wp + n1);
     if (e1) *reinterpret_cast<uint16_t*>(r1 + 2u * lane_rank(m1)) = static_cast<uint16_t>(e2 ? (st.xl >> 16) : st.xl);
     if (e2) *reinterpret_cast<uint16_t*>(r2 + 2u * lane_rank(m2)) = static_cast<uint16_t>(st.xl);
-    uint32_t lo = e1 ? __builtin_amdgcn_alignbit(st.xh, st.xl, 16) : st.xl;
-    uint32_t hi = e1 ? (st.xh >> 16) : st.xh;
-    lo = e2 ? st.xh : lo;
-    hi = e2 ? 0u : hi;
+    // drop the emitted words: x >> 16 per word (e2 implies e1)
+    const uint32_t sh = e2 ? 32u : (e1 ? 16u : 0u);
+    const unsigned long long xs = ((static_cast<unsigned long long>(st.xh) << 32) | st.xl) >> sh;
+    const uint32_t lo = static_cast<uint32_t>(xs), hi = static_cast<uint32_t>(xs >> 32);
     uint32_t q, r;
     divmod_q32(hi, lo, f, q, r);
     // x = q * 2^31 + r + c0 with r + c0 < 2^31: no carry into bit 31
@@ -492,6 +492,14 @@ __device__ __forceinline__ float aim_pos(int32_t e, float mu, float sg, const Ai
     return __fmaf_rn(z, sg, mu);
 }
 
+// The same without interpolation (the nearest table entry): the first of
+// the two aims only has to land near enough to pick the escape bias.
+__device__ __forceinline__ float aim_pos_near(int32_t e, float mu, float sg, const Aim& a) {
+    const float ef = __builtin_amdgcn_fmed3f(static_cast<float>(e) * a.scale, 0.0f, static_cast<float>(kZinvSteps));
+    const int j = static_cast<int>(ef + 0.5f);
+    return __fmaf_rn(a.zinv[j], sg, mu);
+}
+
 template <int KV>
 __device__ __forceinline__ uint32_t aim_edge(int32_t e, float mu, float sg, const Aim& a) {
     return nearest_edge<KV>(aim_pos(e, mu, sg, a));
@@ -792,7 +800,7 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
             uint32_t E, E2, cE, c2;
             bool up;
             if constexpr (KV == kBF16) {
-                const uint32_t E1 = nearest_edge_bf16(aim_pos(static_cast<int32_t>(target - bs), mu, sg, aim)).e;
+                const uint32_t E1 = nearest_edge_bf16(aim_pos_near(static_cast<int32_t>(target - bs), mu, sg, aim)).e;
                 const uint32_t qE = E1 + coarse_prefix<KV>(s_pc, E1);
                 const Bf16Edge ed = nearest_edge_bf16(aim_pos(static_cast<int32_t>(target - qE), mu, sg, aim));
                 E = ed.e;
@@ -812,7 +820,7 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
                 E2 = up ? E + 1u : E - 1u;
                 c2 = E2 + h_fx(z_fixed(edge_pattern<MU>(mag2, ed.sign), mu, inv24), m.tab) + (up ? p2 : p0);
             } else {
-                E = aim_edge<KV>(static_cast<int32_t>(target - bs), mu, sg, aim);
+                E = nearest_edge<KV>(aim_pos_near(static_cast<int32_t>(target - bs), mu, sg, aim));
                 const uint32_t qE = E + coarse_prefix<KV>(s_pc, E);
                 E = aim_edge<KV>(static_cast<int32_t>(target - qE), mu, sg, aim);
                 uint32_t p0 = 0, p1 = 0, p2 = 0;
