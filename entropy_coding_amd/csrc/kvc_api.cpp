@@ -282,7 +282,7 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     ea.kv = d_kv;
     ea.mu = d_mu;
     ea.sigma = d_sigma;
-    ea.prefix = prefix;
+    ea.prefix = prefix ? prefix : phi.zero;          // kernels read a prefix unconditionally
     ea.tn = tn;
     ea.tw = tw;
     ea.phi = phi;
@@ -379,7 +379,7 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     da.payload_bytes = payload;
     da.mu = d_mu;
     da.sigma = d_sigma;
-    da.prefix = prefix;
+    da.prefix = prefix ? prefix : phi.zero;
     da.tn = tn;
     da.tw = tw;
     da.phi = phi;
@@ -453,7 +453,7 @@ int kvc_estimate_bits(const kvc_params* p, const void* d_kv, const void* d_mu, c
     a.kv = d_kv;
     a.mu = d_mu;
     a.sigma = d_sigma;
-    a.prefix = te ? d_prefix : nullptr;
+    a.prefix = te ? d_prefix : phi.zero;
     a.tn = tn;
     a.tw = tw;
     a.te = te;
@@ -497,7 +497,7 @@ int kvc_cdf_table(int32_t kv_dtype, int32_t mu_dtype, uint32_t w_narrow_bp, uint
         }
     }
     if (!ok) return KVC_ERR_INVALID;
-    e = kvc::launch_cdf_table(kv_dtype, mu_dtype, tn, tw, d_mu, d_sigma, pairs, te ? d_prefix : nullptr, d_out,
+    e = kvc::launch_cdf_table(kv_dtype, mu_dtype, tn, tw, d_mu, d_sigma, pairs, te ? d_prefix : phi.zero, d_out,
                               phi, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     return finish(e);

@@ -202,14 +202,14 @@ __device__ __forceinline__ uint32_t h_fx(int32_t q, const uint32_t* __restrict__
 
 struct Model {
     const uint32_t* __restrict__ tab;      // mixture table in LDS
-    const uint32_t* __restrict__ prefix;   // escape prefix (N + 1 entries) or null
+    const uint32_t* __restrict__ prefix;   // escape prefix (N + 1 entries; zeros without an escape part)
 };
 
 // C(b) = b + h_fx(q(b)) + prefix[b].
 template <int KV>
 __device__ __forceinline__ uint32_t cdf_at(uint32_t b, float mu, float inv24, const Model& m) {
     uint32_t g = b + h_fx(z_fixed(edge<KV>(b), mu, inv24), m.tab);
-    if (m.prefix) g += m.prefix[b];
+    g += m.prefix[b];
     return g;
 }
 

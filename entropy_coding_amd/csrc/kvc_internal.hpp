@@ -40,6 +40,7 @@ struct ChunkGeom {
 struct PhiTables {
     const uint32_t* a;                  // round(2^31 Phi(z_k))
     const uint32_t* b;                  // round(2^31 Phi(z_k / 3))
+    const uint32_t* zero;               // 65,537 zeros: the escape prefix of a model without one
 };
 
 struct EncodeArgs {
@@ -47,7 +48,7 @@ struct EncodeArgs {
     const void* kv;
     const void* mu;
     const float* sigma;
-    const uint32_t* prefix;             // null when there is no escape part
+    const uint32_t* prefix;             // escape prefix; the zero table when there is no escape part
     uint32_t tn, tw;
     PhiTables phi;
     uint16_t* slots;                    // per-chunk word slots, filled from the end

@@ -29,6 +29,10 @@ namespace kvc {
 // ---------------------------------------------------------------------------
 __device__ uint32_t g_phi_a[kTablePoints];
 __device__ uint32_t g_phi_b[kTablePoints];
+// Stands in for the escape prefix when the weights leave no escape part, so
+// that the kernels read a prefix unconditionally (zero-initialised, never
+// written).
+__device__ uint32_t g_zero_prefix[65537];
 
 void host_phi_tables(uint32_t* a, uint32_t* b) {
     for (int k = 0; k < kTablePoints; ++k) {
@@ -51,7 +55,7 @@ PhiTables device_phi_tables(hipError_t* err) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
         *err = (e != hipSuccess) ? e : hipErrorInvalidDevice;
-        return PhiTables{nullptr, nullptr};
+        return PhiTables{nullptr, nullptr, nullptr};
     }
     std::call_once(g_phi_once[dev], [dev]() {
         static uint32_t ha[kTablePoints], hb[kTablePoints];
@@ -60,10 +64,13 @@ PhiTables device_phi_tables(hipError_t* err) {
         if (r == hipSuccess) r = hipMemcpyToSymbol(HIP_SYMBOL(g_phi_b), hb, sizeof(hb), 0, hipMemcpyHostToDevice);
         void* pa = nullptr;
         void* pb = nullptr;
+        void* pz = nullptr;
         if (r == hipSuccess) r = hipGetSymbolAddress(&pa, HIP_SYMBOL(g_phi_a));
         if (r == hipSuccess) r = hipGetSymbolAddress(&pb, HIP_SYMBOL(g_phi_b));
+        if (r == hipSuccess) r = hipGetSymbolAddress(&pz, HIP_SYMBOL(g_zero_prefix));
         g_phi_err[dev] = r;
-        g_phi_dev[dev] = PhiTables{static_cast<const uint32_t*>(pa), static_cast<const uint32_t*>(pb)};
+        g_phi_dev[dev] = PhiTables{static_cast<const uint32_t*>(pa), static_cast<const uint32_t*>(pb),
+                                   static_cast<const uint32_t*>(pz)};
     });
     *err = g_phi_err[dev];
     return g_phi_dev[dev];
@@ -163,7 +170,7 @@ hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t
 // coder state, so it runs ahead of the serial rANS pushes.
 // ---------------------------------------------------------------------------
 constexpr int kEncodeBlock = 1024;
-constexpr int kEncodeBatch = 8;
+constexpr int kEncodeBatch = 6;
 
 struct PushState {
     uint32_t xl, xh;                 // 64-bit rANS state
@@ -214,10 +221,8 @@ __device__ __forceinline__ void symbol_range(uint32_t kb, float mu, float inv24,
         const uint32_t hb = h_fx(z_fixed(__uint_as_float(ob | sb), mu, inv24), m.tab);
         uint32_t a = s + __builtin_elementwise_min(ha, hb);
         uint32_t b = s + 1u + __builtin_elementwise_max(ha, hb);
-        if (m.prefix) {
-            a += m.prefix[s];
-            b += m.prefix[s + 1];
-        }
+        a += m.prefix[s];
+        b += m.prefix[s + 1];
         c0 = a;
         f = b - a;
         return;
@@ -232,10 +237,8 @@ __device__ __forceinline__ void symbol_range(uint32_t kb, float mu, float inv24,
     }
     uint32_t a = s + h_fx(z_fixed(lo, mu, inv24), m.tab);
     uint32_t b = s + 1u + h_fx(z_fixed(hi, mu, inv24), m.tab);
-    if (m.prefix) {
-        a += m.prefix[s];
-        b += m.prefix[s + 1];
-    }
+    a += m.prefix[s];
+    b += m.prefix[s + 1];
     c0 = a;
     f = b - a;
 }
@@ -557,7 +560,7 @@ template <int KV, int MU>
 __device__ __forceinline__ uint32_t cdf_probe(uint32_t b, float mu, float inv24, const Model& m) {
     if constexpr (KV == kBF16) {
         uint32_t g = b + h_fx(z_fixed(edge_from_index_bf16<MU>(b), mu, inv24), m.tab);
-        if (m.prefix) g += m.prefix[b];
+        g += m.prefix[b];
         return g;
     } else {
         return cdf_at<KV>(b, mu, inv24, m);
@@ -686,7 +689,7 @@ __device__ __forceinline__ void build_coarse_lds(uint32_t* s_pc, const uint32_t*
     constexpr uint32_t last = Coarse<KV>::kLast;
     for (uint32_t j = threadIdx.x; j <= last + 1u; j += blockDim.x) {
         const uint32_t jj = j > last ? last : j;
-        s_pc[j] = prefix ? prefix[jj << Coarse<KV>::kShift] : 0u;
+        s_pc[j] = prefix[jj << Coarse<KV>::kShift];
     }
 }
 
@@ -804,13 +807,8 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
                 const uint32_t qE = E1 + coarse_prefix<KV>(s_pc, E1);
                 const Bf16Edge ed = nearest_edge_bf16(aim_pos(static_cast<int32_t>(target - qE), mu, sg, aim));
                 E = ed.e;
-                uint32_t p0 = 0, p1 = 0, p2 = 0;
-                if (m.prefix) {
-                    const uint32_t* pp = m.prefix + (E - 1u);     // E >= 1: one 12-byte read
-                    p0 = pp[0];
-                    p1 = pp[1];
-                    p2 = pp[2];
-                }
+                const uint32_t* pp = m.prefix + (E - 1u);         // E >= 1: one 12-byte read
+                const uint32_t p0 = pp[0], p1 = pp[1], p2 = pp[2];
                 cE = E + h_fx(z_fixed(edge_pattern<MU>(ed.mag, ed.sign), mu, inv24), m.tab) + p1;
                 up = target >= cE;
                 // the neighbour one step away from zero (up on the positive
@@ -823,13 +821,8 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
                 E = nearest_edge<KV>(aim_pos_near(static_cast<int32_t>(target - bs), mu, sg, aim));
                 const uint32_t qE = E + coarse_prefix<KV>(s_pc, E);
                 E = aim_edge<KV>(static_cast<int32_t>(target - qE), mu, sg, aim);
-                uint32_t p0 = 0, p1 = 0, p2 = 0;
-                if (m.prefix) {
-                    const uint32_t* pp = m.prefix + (E - 1u);     // E >= 1: one 12-byte read
-                    p0 = pp[0];
-                    p1 = pp[1];
-                    p2 = pp[2];
-                }
+                const uint32_t* pp = m.prefix + (E - 1u);         // E >= 1: one 12-byte read
+                const uint32_t p0 = pp[0], p1 = pp[1], p2 = pp[2];
                 cE = E + h_fx(z_fixed(edge<KV>(E), mu, inv24), m.tab) + p1;
                 up = target >= cE;
                 E2 = up ? E + 1u : E - 1u;
