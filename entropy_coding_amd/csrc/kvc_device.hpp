@@ -203,6 +203,7 @@ __device__ __forceinline__ uint32_t h_fx(int32_t q, const uint32_t* __restrict__
 struct Model {
     const uint32_t* __restrict__ tab;      // mixture table in LDS
     const uint32_t* __restrict__ prefix;   // escape prefix (N + 1 entries; zeros without an escape part)
+    const uint32_t* small = nullptr;       // e4m3 only: prefix and edges in LDS
 };
 
 // C(b) = b + h_fx(q(b)) + prefix[b].

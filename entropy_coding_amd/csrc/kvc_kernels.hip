@@ -165,6 +165,44 @@ hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t
 }
 
 // ---------------------------------------------------------------------------
+// e4m3: the 257 cell edges and the 257-entry escape prefix fit in LDS, so the
+// small alphabet's CDF needs no global reads and no edge arithmetic.
+// Layout of a block's table: prefix[0..256], then edges (fp32) at
+// kE4EdgeOff .. kE4EdgeOff + 256.
+// ---------------------------------------------------------------------------
+constexpr int kE4EdgeOff = 260;
+constexpr int kE4Words = kE4EdgeOff + 257;
+
+__device__ __forceinline__ void build_e4_lds(uint32_t* t, const uint32_t* __restrict__ prefix) {
+    for (int j = threadIdx.x; j <= 256; j += blockDim.x) {
+        t[j] = prefix[j];
+        t[kE4EdgeOff + j] = __float_as_uint(edge_e4m3(static_cast<uint32_t>(j)));
+    }
+}
+
+__device__ __forceinline__ float e4_edge(const uint32_t* t, uint32_t b) {
+    return __uint_as_float(t[kE4EdgeOff + b]);
+}
+
+// C(b) for e4m3 from the LDS table: b + h(q_b) + prefix[b].
+__device__ __forceinline__ uint32_t e4_cdf(const uint32_t* t, const uint32_t* tab, uint32_t b, float mu,
+                                           float inv24) {
+    return b + h_fx(z_fixed(e4_edge(t, b), mu, inv24), tab) + t[b];
+}
+
+// Nearest e4m3 cell edge to x, for aiming only: the magnitude pattern h of
+// |x| truncated to the e4m3 grid (3 mantissa bits; steps of 2^-9 below 2^-6)
+// puts |x| between symbols h and h + 1, whose midpoint is the nearest edge.
+__device__ __forceinline__ uint32_t nearest_edge_e4m3(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const float ax = __builtin_fabsf(x);
+    int32_t h = ax < 0x1p-6f ? static_cast<int32_t>(ax * 512.0f)
+                             : static_cast<int32_t>((u & 0x7FFFFFFFu) >> 20) - (120 << 3);
+    h = h < 126 ? h : 126;
+    return (u >> 31) ? static_cast<uint32_t>(127 - h) : static_cast<uint32_t>(129 + h);
+}
+
+// ---------------------------------------------------------------------------
 // encoder: one wave per chunk, tokens last to first.  The model side of a
 // batch of tokens (loads, symbol, both CDF edges) does not depend on the
 // coder state, so it runs ahead of the serial rANS pushes.
@@ -228,6 +266,13 @@ __device__ __forceinline__ void symbol_range(uint32_t kb, float mu, float inv24,
         return;
     }
     const uint32_t s = order_of_bits<KV>(kb);
+    if constexpr (KV == kE4M3) {
+        const uint32_t a = e4_cdf(m.small, m.tab, s, mu, inv24);
+        const uint32_t b = e4_cdf(m.small, m.tab, s + 1u, mu, inv24);
+        c0 = a;
+        f = b - a;
+        return;
+    }
     float lo, hi;
     if constexpr (KV == kBF16) {
         bf16_cell_edges(kb, lo, hi);
@@ -272,6 +317,8 @@ __device__ __forceinline__ void encode_batch(int t, PushState& st, const typenam
 template <int KV, int MU>
 __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
     __shared__ uint32_t s_tab[kTableEntries];
+    __shared__ uint32_t s_small[KV == kE4M3 ? kE4Words : 1];
+    if constexpr (KV == kE4M3) build_e4_lds(s_small, a.prefix);
     build_table_lds(s_tab, a.phi, a.tn, a.tw);
 
     const uint32_t lane = threadIdx.x & 63u;
@@ -287,7 +334,7 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
         if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
         inv24 = 16777216.0f;
     }
-    const Model m{s_tab, a.prefix};
+    const Model m{s_tab, a.prefix, s_small};
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
@@ -563,7 +610,7 @@ __device__ __forceinline__ uint32_t cdf_probe(uint32_t b, float mu, float inv24,
         g += m.prefix[b];
         return g;
     } else {
-        return cdf_at<KV>(b, mu, inv24, m);
+        return e4_cdf(m.small, m.tab, b, mu, inv24);
     }
 }
 
@@ -726,7 +773,9 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
     __shared__ float s_zinv[kZinvSteps + 2];
     __shared__ uint32_t s_ring[kDecodeBlock / 64][128];
     __shared__ uint32_t s_pc[kCoarseEntries];
-    build_coarse_lds<KV>(s_pc, a.prefix);
+    static_assert(kE4Words <= kCoarseEntries, "e4m3 tables share the coarse-prefix array");
+    if constexpr (KV == kE4M3) build_e4_lds(s_pc, a.prefix);      // exact prefix + edges
+    else build_coarse_lds<KV>(s_pc, a.prefix);
     build_table_lds(s_tab, a.phi, a.tn, a.tw);
     const uint32_t htot = a.tn + a.tw;
     build_zinv_lds(s_zinv, s_tab, htot);              // all z = 24 when htot = 0
@@ -764,7 +813,7 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
         inv24 = 16777216.0f;
         sg = 1.0f;
     }
-    const Model m{s_tab, a.prefix};
+    const Model m{s_tab, a.prefix, s_pc};
     const Aim aim{s_zinv, htot ? static_cast<float>(kZinvSteps) / static_cast<float>(htot) : 0.0f,
                   static_cast<int32_t>(htot)};
     const uint32_t geo = geo_offset(lane);
@@ -818,15 +867,13 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
                 E2 = up ? E + 1u : E - 1u;
                 c2 = E2 + h_fx(z_fixed(edge_pattern<MU>(mag2, ed.sign), mu, inv24), m.tab) + (up ? p2 : p0);
             } else {
-                E = nearest_edge<KV>(aim_pos_near(static_cast<int32_t>(target - bs), mu, sg, aim));
-                const uint32_t qE = E + coarse_prefix<KV>(s_pc, E);
-                E = aim_edge<KV>(static_cast<int32_t>(target - qE), mu, sg, aim);
-                const uint32_t* pp = m.prefix + (E - 1u);         // E >= 1: one 12-byte read
-                const uint32_t p0 = pp[0], p1 = pp[1], p2 = pp[2];
-                cE = E + h_fx(z_fixed(edge<KV>(E), mu, inv24), m.tab) + p1;
+                // e4m3: edges and the exact prefix come from LDS
+                E = nearest_edge_e4m3(aim_pos_near(static_cast<int32_t>(target - bs), mu, sg, aim));
+                E = nearest_edge_e4m3(aim_pos(static_cast<int32_t>(target - (E + s_pc[E])), mu, sg, aim));
+                cE = e4_cdf(s_pc, m.tab, E, mu, inv24);
                 up = target >= cE;
                 E2 = up ? E + 1u : E - 1u;
-                c2 = E2 + h_fx(z_fixed(edge<KV>(E2), mu, inv24), m.tab) + (up ? p2 : p0);
+                c2 = e4_cdf(s_pc, m.tab, E2, mu, inv24);
             }
             const bool ok = up ? (target < c2) : (target >= c2);
             Found fd;
