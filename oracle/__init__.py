@@ -20,6 +20,8 @@ Parity status of each function (what pins it other than itself):
                                   the wide table against the narrow one at z/3
   h_fx / cdf                   -- invariants (C(0)=0, C(N)=M, f>=1) and the
                                   continuous mixture within a derived bound
+  gauss_cum / escape_cum       -- the slot ranges tile the coder range and
+                                  add up to the mixture frequencies
   encode / decode              -- round trip, exact size band, unbounded
                                   big-integer rANS
   build_marginal               -- brute-force counting on tiny inputs

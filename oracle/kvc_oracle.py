@@ -33,6 +33,7 @@ __all__ = [
     "BF16", "E4M3", "F32", "M", "L", "LANES", "HEADER_BYTES", "STATE_BYTES", "StreamError",
     "alphabet_size", "budgets", "order_index", "bits_of_order", "symbol_value",
     "boundary_positions", "phi_tables", "mixture_table", "h_fx", "mu_to_f32", "cdf",
+    "gauss_cum", "escape_cum",
     "cdf_table", "build_marginal", "calibrate_sigma", "side_hash", "encode",
     "decode", "parse_header", "model_bits_int", "model_bits_float",
     "chunk_layout",
@@ -51,7 +52,7 @@ LANES = 64                         # interleaved rANS lanes per chunk
 HEADER_BYTES = 128
 STATE_BYTES = 8 * LANES            # 64 final states, u64 each
 MAGIC = b"KVC1"
-VERSION = 1
+VERSION = 2
 
 
 class StreamError(ValueError):
@@ -267,6 +268,18 @@ def cdf(b, mu32, inv32, dtype: int, t_n: int, t_w: int, prefix=None) -> np.ndarr
     return b + g
 
 
+def gauss_cum(b, mu32, inv32, dtype: int, t_n: int, t_w: int) -> np.ndarray:
+    """G(b) = h(q_b): the two Gaussian parts of C below symbol b, 0 .. T_n + T_w."""
+    return cdf(b, mu32, inv32, dtype, t_n, t_w, None) - np.asarray(b).astype(np.int64)
+
+
+def escape_cum(b, prefix=None) -> np.ndarray:
+    """Q(b) = b + prefix[b]: the +1 floor and the escape part of C below
+    symbol b, 0 .. N + T_e.  C(b) = G(b) + Q(b)."""
+    b = np.asarray(b).astype(np.int64)
+    return b if prefix is None else b + np.asarray(prefix, dtype=np.int64)[b]
+
+
 SIGMA_MIN = np.float32(2.0 ** -96)
 SIGMA_MAX = np.float32(2.0 ** 96)
 
@@ -458,9 +471,13 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
 
     Per chunk and lane, tokens are coded last to first so that the decoder
     runs first to last (rANS is last-in first-out).  Before a symbol with
-    frequency f is pushed, the state x is renormalised down so that
-    x < 2^32 f by emitting its low 16-bit word (count = [x/2^32 >= f] +
-    [x/2^48 >= f] words); then x <- floor(x/f) * M + (x mod f) + start.
+    frequency f = C(s+1) - C(s) is pushed, the state x is renormalised down
+    so that x < 2^32 f by emitting its low 16-bit word (count = [x/2^32 >= f]
+    + [x/2^48 >= f] words); then x <- floor(x/f) * M + slot(s, x mod f).
+    The symbol's f slots are its Gaussian slots [G(s), G(s+1)) in the range
+    [0, T_n + T_w), then its floor-and-escape slots [Q(s), Q(s+1)) shifted
+    by T_n + T_w: slot(s, r) = G(s) + r for r < f_G, else
+    T_n + T_w + Q(s) + (r - f_G).
     The words of one token step are laid out in the order the decoder reads
     them: first, for every lane that emitted at least one word (ascending
     lane), its last-emitted word; then, for every lane that emitted two,
@@ -498,8 +515,10 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
             tok = np.minimum(tcid * chunk_tokens + t, t_len - 1)[:, None]
             s = sym_all[g[:, None], tok, d]
             mu32 = mu32_all[g[:, None], tok, d]
-            start = cdf(s, mu32, inv, kv_dtype, t_n, t_w, pref)
-            f = cdf(s + 1, mu32, inv, kv_dtype, t_n, t_w, pref) - start
+            g0 = gauss_cum(s, mu32, inv, kv_dtype, t_n, t_w)
+            fg = gauss_cum(s + 1, mu32, inv, kv_dtype, t_n, t_w) - g0
+            q0 = escape_cum(s, pref)
+            f = fg + escape_cum(s + 1, pref) - q0
             fu = f.astype(np.uint64)
             count = ((x >> np.uint64(32)) >= fu).astype(np.int64) + \
                     ((x >> np.uint64(48)) >= fu).astype(np.int64)
@@ -511,7 +530,9 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
             emit[:, t, 0, :] = count >= 1
             emit[:, t, 1, :] = count == 2
             xs = x >> (np.uint64(16) * count.astype(np.uint64))
-            xn = ((xs // fu) << np.uint64(LOG2_M)) + (xs % fu) + start.astype(np.uint64)
+            r = (xs % fu).astype(np.int64)
+            slot = np.where(r < fg, g0 + r, (t_n + t_w) + q0 + (r - fg))
+            xn = ((xs // fu) << np.uint64(LOG2_M)) + slot.astype(np.uint64)
             x = np.where(active, xn, x)
         for i in range(nb):
             body = x[i].astype("<u8").tobytes() + words[i][emit[i]].astype("<u2").tobytes()
@@ -529,9 +550,12 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
            chunk_ids=None):
     """Rebuild the raw KV bit patterns [G, T, D] from a KVC-1 stream.
 
-    Per token step and lane: target = x mod M; the symbol is the unique s
-    with C(s) <= target < C(s+1) (found here by plain bisection over the
-    alphabet); x <- f * floor(x / M) + target - C(s); then, while x < L, a
+    Per token step and lane: target = x mod M.  A target below T_n + T_w is
+    a Gaussian slot: the symbol is the unique s with G(s) <= target <
+    G(s+1) and its rank r = target - G(s); otherwise y = target - T_n - T_w
+    is a floor-and-escape slot: s is the unique symbol with Q(s) <= y <
+    Q(s+1) and r = f_G(s) + y - Q(s) (both found here by plain bisection
+    over the alphabet).  Then x <- f * floor(x / M) + r; then, while x < L, a
     16-bit word is shifted in (round 1 for every lane that needs one, in lane
     order, then round 2).  Every lane must end in state L and every chunk
     must consume exactly its payload, else the stream is corrupt.
@@ -597,20 +621,28 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
             tok = np.minimum(tcid * tcn + t, t_len - 1)[:, None]
             mu32 = mu32_all[g[:, None], tok, d]
             target = (x & np.uint64(M - 1)).astype(np.int64)
-            lo = np.zeros((nb, LANES), dtype=np.int64)
-            hi = np.full((nb, LANES), n_sym, dtype=np.int64)
-            c_lo = np.zeros((nb, LANES), dtype=np.int64)
-            c_hi = np.full((nb, LANES), M, dtype=np.int64)
+            htot = t_n + t_w
+            in_g = target < htot
+            y = target - htot
+            # bisection: largest b with G(b) <= target, and with Q(b) <= y
+            lo_g = np.zeros((nb, LANES), dtype=np.int64)
+            hi_g = np.full((nb, LANES), n_sym, dtype=np.int64)
+            lo_q = np.zeros((nb, LANES), dtype=np.int64)
+            hi_q = np.full((nb, LANES), n_sym, dtype=np.int64)
             for _ in range(steps):
-                mid = (lo + hi) >> 1
-                c_mid = cdf(mid, mu32, inv, kv_dtype, t_n, t_w, pref)
-                go = c_mid <= target
-                lo = np.where(go, mid, lo)
-                c_lo = np.where(go, c_mid, c_lo)
-                hi = np.where(go, hi, mid)
-                c_hi = np.where(go, c_hi, c_mid)
-            f = (c_hi - c_lo).astype(np.uint64)
-            xn = f * (x >> np.uint64(LOG2_M)) + (target - c_lo).astype(np.uint64)
+                mid = (lo_g + hi_g) >> 1
+                go = gauss_cum(mid, mu32, inv, kv_dtype, t_n, t_w) <= target
+                lo_g, hi_g = np.where(go, mid, lo_g), np.where(go, hi_g, mid)
+                mid = (lo_q + hi_q) >> 1
+                go = escape_cum(mid, pref) <= y
+                lo_q, hi_q = np.where(go, mid, lo_q), np.where(go, hi_q, mid)
+            lo = np.where(in_g, lo_g, lo_q)
+            g0 = gauss_cum(lo, mu32, inv, kv_dtype, t_n, t_w)
+            fg = gauss_cum(lo + 1, mu32, inv, kv_dtype, t_n, t_w) - g0
+            q0 = escape_cum(lo, pref)
+            f = (fg + escape_cum(lo + 1, pref) - q0).astype(np.uint64)
+            r = np.where(in_g, target - g0, fg + (y - q0)).astype(np.uint64)
+            xn = f * (x >> np.uint64(LOG2_M)) + r
             x = np.where(active, xn, x)
             for _round in range(2):
                 need = active & (x < np.uint64(L))

@@ -42,6 +42,30 @@ def test_whole_alphabet_invariants(dtype, mode):
     assert np.all(f >= 1)                     # every symbol stays codable
 
 
+@pytest.mark.parametrize("dtype", [O.BF16, O.E4M3])
+@pytest.mark.parametrize("mode", ["single", "mixture"])
+def test_slot_ranges_tile_the_coder_range(dtype, mode):
+    """The coder's slots: the Gaussian ranges [G(b), G(b+1)) tile
+    [0, T_n + T_w) and the floor-and-escape ranges [Q(b), Q(b+1)) tile
+    [0, N + T_e) (placed after them), and each symbol's two ranges add up to
+    its mixture frequency C(b+1) - C(b): a bijection between slots and
+    (symbol, rank) pairs with the mixture's frequencies."""
+    w = (10000, 0) if mode == "single" else (9500, 300)
+    t_n, t_w, t_e = O.budgets(dtype, *w)
+    pref = marginal(dtype) if mode == "mixture" else None
+    n = O.alphabet_size(dtype)
+    b = np.arange(n + 1, dtype=np.int64)
+    q = O.escape_cum(b, pref)
+    assert q[0] == 0 and q[-1] == n + t_e and np.all(np.diff(q) >= 1)
+    for mu, sg in ADVERSARIAL:
+        mu32 = O.mu_to_f32(np.array([mu], dtype=np.float32), O.F32)[0]
+        inv = (np.float32(1.0) / np.float32(sg)).astype(np.float32)
+        g = O.gauss_cum(b, mu32, inv, dtype, t_n, t_w)
+        assert g[0] == 0 and g[-1] == t_n + t_w and np.all(np.diff(g) >= 0)
+        c = O.cdf(b, mu32, inv, dtype, t_n, t_w, pref)
+        assert np.array_equal(np.diff(g) + np.diff(q), np.diff(c))
+
+
 def test_single_gaussian_floor_symbol_costs_31_bits():
     tab = O.cdf_table(np.float32([1.0]), np.float32([0.01]), O.BF16, O.F32, 10000, 0)[0]
     nan_sym = int(O.order_index(0x7FC0, O.BF16))
