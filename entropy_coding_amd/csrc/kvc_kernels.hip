@@ -208,16 +208,25 @@ __device__ __forceinline__ uint32_t nearest_edge_e4m3(float x) {
 // coder state, so it runs ahead of the serial rANS pushes.
 // ---------------------------------------------------------------------------
 constexpr int kEncodeBlock = 1024;
-constexpr int kEncodeBatch = 6;
+constexpr int kEncodeBatch = 5;
 
 struct PushState {
     uint32_t xl, xh;                 // 64-bit rANS state
     uint32_t wp;                     // words left free in the slot (wave-uniform)
 };
 
-// Push one symbol (start c0, frequency f) onto the 64 lane states; emitted
-// words go to the slot block of this token step, in decoder read order.
-__device__ __forceinline__ void rans_push(PushState& st, uint32_t c0, uint32_t f, uint16_t* __restrict__ slot) {
+// A symbol's f slots: its Gaussian slots G(s) .. G(s+1) - 1 in
+// [0, T_n + T_w), then its floor-and-escape slots T_n + T_w + Q(s) ..
+// (Q(s) = s + prefix[s]).  slot(r) = g0 + r for r < fg, else qb + r with
+// qb = T_n + T_w + Q(s) - fg.
+struct SymSlots {
+    uint32_t g0, fg, qb, f;
+};
+
+// Push one symbol onto the 64 lane states; emitted words go to the slot
+// block of this token step, in decoder read order.
+__device__ __forceinline__ void rans_push(PushState& st, const SymSlots& y, uint16_t* __restrict__ slot) {
+    const uint32_t f = y.f;
     const bool e1 = st.xh >= f;               // x / 2^32 >= f: one word out
     const bool e2 = (st.xh >> 16) >= f;       // x / 2^48 >= f: two words out
     const uint64_t m1 = __ballot(e1);
@@ -235,15 +244,28 @@ __device__ __forceinline__ void rans_push(PushState& st, uint32_t c0, uint32_t f
     const uint32_t lo = static_cast<uint32_t>(xs), hi = static_cast<uint32_t>(xs >> 32);
     uint32_t q, r;
     divmod_q32(hi, lo, f, q, r);
-    // x = q * 2^31 + r + c0 with r + c0 < 2^31: no carry into bit 31
+    // x = q * 2^31 + slot(r), slot < 2^31: no carry into bit 31
+    const uint32_t sl = r + (r < y.fg ? y.g0 : y.qb);
     st.xh = q >> 1;
-    st.xl = (q << 31) | (r + c0);
+    st.xl = (q << 31) | sl;
 }
 
-// Start and frequency of the symbol with bit pattern kb under the mixture.
+// Slots of the symbol with bit pattern kb under the mixture: ga, gb are the
+// mixture-table values at its two cell edges (in either order), s its index.
+__device__ __forceinline__ SymSlots make_slots(uint32_t s, uint32_t ga, uint32_t gb, const Model& m, uint32_t htot) {
+    const uint32_t g0 = __builtin_elementwise_min(ga, gb);
+    const uint32_t fg = __builtin_elementwise_max(ga, gb) - g0;
+    const uint32_t p0 = m.prefix[s], p1 = m.prefix[s + 1];
+    SymSlots y;
+    y.g0 = g0;
+    y.fg = fg;
+    y.qb = htot + s + p0 - fg;
+    y.f = fg + 1u + (p1 - p0);
+    return y;
+}
+
 template <int KV, int MU>
-__device__ __forceinline__ void symbol_range(uint32_t kb, float mu, float inv24, const Model& m, uint32_t& c0,
-                                             uint32_t& f) {
+__device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float inv24, const Model& m, uint32_t htot) {
     if constexpr (KV == kBF16 && MU == kBF16) {
         // ord(u): u ^ 0x8000 for a positive pattern, u ^ 0xFFFF for a negative one
         const uint32_t s = (kb ^ 0x8000u) ^ (static_cast<uint32_t>(static_cast<int32_t>(kb << 16) >> 31) & 0x7FFFu);
@@ -257,35 +279,25 @@ __device__ __forceinline__ void symbol_range(uint32_t kb, float mu, float inv24,
         const uint32_t sb = (kb & 0x8000u) << 16;
         const uint32_t ha = h_fx(z_fixed(__uint_as_float(ib | sb), mu, inv24), m.tab);
         const uint32_t hb = h_fx(z_fixed(__uint_as_float(ob | sb), mu, inv24), m.tab);
-        uint32_t a = s + __builtin_elementwise_min(ha, hb);
-        uint32_t b = s + 1u + __builtin_elementwise_max(ha, hb);
-        a += m.prefix[s];
-        b += m.prefix[s + 1];
-        c0 = a;
-        f = b - a;
-        return;
+        return make_slots(s, ha, hb, m, htot);
     }
     const uint32_t s = order_of_bits<KV>(kb);
     if constexpr (KV == kE4M3) {
-        const uint32_t a = e4_cdf(m.small, m.tab, s, mu, inv24);
-        const uint32_t b = e4_cdf(m.small, m.tab, s + 1u, mu, inv24);
-        c0 = a;
-        f = b - a;
-        return;
+        const uint32_t ha = h_fx(z_fixed(e4_edge(m.small, s), mu, inv24), m.tab);
+        const uint32_t hb = h_fx(z_fixed(e4_edge(m.small, s + 1u), mu, inv24), m.tab);
+        const uint32_t p0 = m.small[s], p1 = m.small[s + 1u];
+        SymSlots y;
+        y.g0 = ha;
+        y.fg = hb - ha;
+        y.qb = htot + s + p0 - y.fg;
+        y.f = y.fg + 1u + (p1 - p0);
+        return y;
     }
     float lo, hi;
-    if constexpr (KV == kBF16) {
-        bf16_cell_edges(kb, lo, hi);
-    } else {
-        lo = edge<KV>(s);
-        hi = edge<KV>(s + 1);
-    }
-    uint32_t a = s + h_fx(z_fixed(lo, mu, inv24), m.tab);
-    uint32_t b = s + 1u + h_fx(z_fixed(hi, mu, inv24), m.tab);
-    a += m.prefix[s];
-    b += m.prefix[s + 1];
-    c0 = a;
-    f = b - a;
+    bf16_cell_edges(kb, lo, hi);
+    const uint32_t ha = h_fx(z_fixed(lo, mu, inv24), m.tab);
+    const uint32_t hb = h_fx(z_fixed(hi, mu, inv24), m.tab);
+    return make_slots(s, ha, hb, m, htot);
 }
 
 // Element `lane` of a row whose base is wave-uniform: the base stays in
@@ -298,7 +310,7 @@ __device__ __forceinline__ const T& row_elem(const T* __restrict__ row, uint32_t
 template <int KV, int MU, int U>
 __device__ __forceinline__ void encode_batch(int t, PushState& st, const typename Alphabet<KV>::Bits* __restrict__ kvb,
                                              const typename MuT<MU>::T* __restrict__ mub, uint32_t D, uint32_t lane,
-                                             float inv24, const Model& m, uint16_t* __restrict__ slot) {
+                                             float inv24, const Model& m, uint32_t htot, uint16_t* __restrict__ slot) {
     uint32_t kb[U];
     typename MuT<MU>::T mb[U];
 #pragma unroll
@@ -307,11 +319,11 @@ __device__ __forceinline__ void encode_batch(int t, PushState& st, const typenam
         kb[u] = row_elem(kvb + row, lane);
         mb[u] = row_elem(mub + row, lane);
     }
-    uint32_t c0[U], fr[U];
+    SymSlots y[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) symbol_range<KV, MU>(kb[u], mu_value<MU>(mb[u]), inv24, m, c0[u], fr[u]);
+    for (int u = 0; u < U; ++u) y[u] = symbol_slots<KV, MU>(kb[u], mu_value<MU>(mb[u]), inv24, m, htot);
 #pragma unroll
-    for (int u = 0; u < U; ++u) rans_push(st, c0[u], fr[u], slot);
+    for (int u = 0; u < U; ++u) rans_push(st, y[u], slot);
 }
 
 template <int KV, int MU>
@@ -346,9 +358,10 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
 
     PushState st{static_cast<uint32_t>(kL), kLHi, static_cast<uint32_t>(a.slot_words)};
     int t = static_cast<int>(cp.len) - 1;
+    const uint32_t htot = a.tn + a.tw;
     for (; t >= kEncodeBatch - 1; t -= kEncodeBatch)
-        encode_batch<KV, MU, kEncodeBatch>(t, st, kvb, mub, D, lane, inv24, m, slot);
-    for (; t >= 0; --t) encode_batch<KV, MU, 1>(t, st, kvb, mub, D, lane, inv24, m, slot);
+        encode_batch<KV, MU, kEncodeBatch>(t, st, kvb, mub, D, lane, inv24, m, htot, slot);
+    for (; t >= 0; --t) encode_batch<KV, MU, 1>(t, st, kvb, mub, D, lane, inv24, m, htot, slot);
 
     a.states[chunk * 64 + lane] = (static_cast<unsigned long long>(st.xh) << 32) | st.xl;
     if (lane == 0) a.chunk_words[chunk] = static_cast<uint32_t>(a.slot_words) - st.wp;
@@ -601,17 +614,12 @@ __device__ __forceinline__ float edge_from_index_bf16(uint32_t b) {
     return edge_pattern<MU>(mag, b < 32768u ? 0x80000000u : 0u);
 }
 
-// C(b) for the wave-cooperative search: the exact CDF, with the bf16 edge
-// taken through edge_from_index_bf16.
+// G(b), the mixture-table term of the CDF at edge b, for the
+// wave-cooperative search (bf16 edge from the index; e4m3 edge from LDS).
 template <int KV, int MU>
-__device__ __forceinline__ uint32_t cdf_probe(uint32_t b, float mu, float inv24, const Model& m) {
-    if constexpr (KV == kBF16) {
-        uint32_t g = b + h_fx(z_fixed(edge_from_index_bf16<MU>(b), mu, inv24), m.tab);
-        g += m.prefix[b];
-        return g;
-    } else {
-        return e4_cdf(m.small, m.tab, b, mu, inv24);
-    }
+__device__ __forceinline__ uint32_t gauss_probe(uint32_t b, float mu, float inv24, const Model& m) {
+    if constexpr (KV == kBF16) return h_fx(z_fixed(edge_from_index_bf16<MU>(b), mu, inv24), m.tab);
+    else return h_fx(z_fixed(e4_edge(m.small, b), mu, inv24), m.tab);
 }
 
 // Probe offsets for the first cooperative round: 1, 2, 3, ... then growing
@@ -622,17 +630,14 @@ __device__ __forceinline__ uint32_t geo_offset(int lane) {
     return o > static_cast<uint32_t>(lane + 1) ? o : static_cast<uint32_t>(lane + 1);
 }
 
-struct Found {
-    uint32_t s, start, freq;
-};
-
-// The whole wave resolves every lane with `need` set, one lane at a time.
-// [lo, hi) brackets the lane's symbol with C(lo) = clo <= target < C(hi) = chi;
-// `up` tells which end is the known near one (lo if up).
+// Gaussian-range slot not bracketed by the aim: the whole wave resolves
+// every lane with `need` set, one lane at a time.  [lo, hi) brackets the
+// lane's symbol with G(lo) = glo <= target < G(hi) = ghi; `up` tells which
+// end is the known near one (lo if up).  Returns s, G(s), G(s+1) - G(s).
 template <int KV, int MU>
-__device__ __forceinline__ void coop_search(bool need, uint32_t target, float mu, float inv24, bool up, uint32_t lo,
-                                            uint32_t hi, uint32_t clo, uint32_t chi, const Model& m, uint32_t geo,
-                                            Found& out) {
+__device__ __forceinline__ void coop_gauss(bool need, uint32_t target, float mu, float inv24, bool up, uint32_t lo,
+                                           uint32_t hi, uint32_t glo, uint32_t ghi, const Model& m, uint32_t geo,
+                                           uint32_t& s_out, uint32_t& g0_out, uint32_t& fg_out) {
     const int lane = threadIdx.x & 63;
     uint64_t pend = __ballot(need);
     while (pend) {
@@ -643,7 +648,7 @@ __device__ __forceinline__ void coop_search(bool need, uint32_t target, float mu
         const float iL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv24), L));
         const bool upL = __builtin_amdgcn_readlane(static_cast<int>(up), L) != 0;
         uint32_t a = __builtin_amdgcn_readlane(lo, L), b = __builtin_amdgcn_readlane(hi, L);
-        uint32_t ca = __builtin_amdgcn_readlane(clo, L), cb = __builtin_amdgcn_readlane(chi, L);
+        uint32_t ga = __builtin_amdgcn_readlane(glo, L), gb = __builtin_amdgcn_readlane(ghi, L);
         bool first = true;
         for (int round = 0; round < 8 && b - a > 1; ++round) {
             const uint32_t span = b - a;
@@ -657,7 +662,7 @@ __device__ __forceinline__ void coop_search(bool need, uint32_t target, float mu
                 p = a + ((static_cast<uint32_t>(lane + 1) * span) >> 6);
             }
             const bool valid = lane < 63 && p > a && p < b;
-            const uint32_t c = cdf_probe<KV, MU>(valid ? p : a, mL, iL, m);
+            const uint32_t c = gauss_probe<KV, MU>(valid ? p : a, mL, iL, m);
             const uint64_t mle = __ballot(valid && c <= t);
             const uint64_t mgt = __ballot(valid && c > t);
             // probe positions increase with the lane, except geometric probes
@@ -666,19 +671,73 @@ __device__ __forceinline__ void coop_search(bool need, uint32_t target, float mu
             if (mle) {
                 const int k = rising ? 63 - __builtin_clzll(mle) : __builtin_ctzll(mle);
                 a = __builtin_amdgcn_readlane(p, k);
-                ca = __builtin_amdgcn_readlane(c, k);
+                ga = __builtin_amdgcn_readlane(c, k);
             }
             if (mgt) {
                 const int k = rising ? __builtin_ctzll(mgt) : 63 - __builtin_clzll(mgt);
                 b = __builtin_amdgcn_readlane(p, k);
-                cb = __builtin_amdgcn_readlane(c, k);
+                gb = __builtin_amdgcn_readlane(c, k);
             }
             first = false;
         }
         if (lane == L) {
-            out.s = a;
-            out.start = ca;
-            out.freq = cb - ca;
+            s_out = a;
+            g0_out = ga;
+            fg_out = gb - ga;
+        }
+    }
+}
+
+// Floor-and-escape slot y: the symbol s with Q(s) <= y < Q(s+1), Q(b) = b +
+// prefix[b], which does not depend on the lane's model.  The whole wave
+// looks each such lane up: bf16 in three ballot rounds (every 16th entry of
+// the every-64th-entry LDS copy, then the 16 entries after the match, then
+// the 64 exact entries of that segment, one contiguous read); e4m3 in two
+// rounds over the exact LDS copy.  Returns s, Q(s), Q(s+1) - Q(s).  Lane 0
+// always matches for a valid prefix (Q(0) = 0 <= y); it is counted as a
+// match regardless, so a damaged prefix still keeps every index in range
+// (the decode then fails its checks).
+template <int KV>
+__device__ __forceinline__ void escape_search(bool need, uint32_t y, const uint32_t* s_pc,
+                                              const uint32_t* __restrict__ prefix, uint32_t& s_out,
+                                              uint32_t& q_out, uint32_t& fq_out) {
+    const uint32_t lane = threadIdx.x & 63u;
+    uint64_t pend = __ballot(need);
+    while (pend) {
+        const int L = __builtin_ctzll(pend);
+        pend &= pend - 1;
+        const uint32_t yl = __builtin_amdgcn_readlane(y, L);
+        uint32_t sv, q0, q1;
+        if constexpr (KV == kBF16) {
+            // Qc(j) = Q(64 j) = 64 j + s_pc[j], j = 0 .. 1024; Qc(0) = 0 <= y < Qc(1024)
+            uint32_t j = 16u * lane;                                        // 0 .. 1008
+            uint64_t le = __ballot(64u * j + s_pc[j] <= yl);
+            const uint32_t k = 63u - __builtin_clzll(le | 1ull);
+            j = 16u * k + (lane & 15u);                                     // <= 1023
+            le = __ballot(lane < 16u && 64u * j + s_pc[j] <= yl);
+            const uint32_t jj = 16u * k + (63u - __builtin_clzll(le | 1ull));
+            const uint32_t b = 64u * jj + lane;                            // <= 65535
+            const uint32_t qb = b + prefix[b];
+            le = __ballot(qb <= yl);
+            const uint32_t kk = 63u - __builtin_clzll(le | 1ull);
+            sv = 64u * jj + kk;
+            q0 = __builtin_amdgcn_readlane(qb, kk);
+            q1 = kk < 63u ? __builtin_amdgcn_readlane(qb, kk + 1u) : 64u * (jj + 1u) + s_pc[jj + 1u];
+        } else {
+            // s_pc[b] = prefix[b], b = 0 .. 256
+            uint32_t b = 4u * lane;                                         // 0 .. 252
+            uint64_t le = __ballot(b + s_pc[b] <= yl);
+            const uint32_t k = 63u - __builtin_clzll(le | 1ull);
+            b = 4u * k + (lane & 3u);                                       // <= 255
+            le = __ballot(lane < 4u && b + s_pc[b] <= yl);
+            sv = 4u * k + (63u - __builtin_clzll(le | 1ull));
+            q0 = sv + s_pc[sv];
+            q1 = sv + 1u + s_pc[sv + 1u];
+        }
+        if (lane == static_cast<uint32_t>(L)) {
+            s_out = sv;
+            q_out = q0;
+            fq_out = q1 - q0;
         }
     }
 }
@@ -719,10 +778,8 @@ struct WordRing {
     }
 };
 
-// Escape prefix for aiming only: every 2^shift-th entry in LDS (all of it
-// for e4m3), read back with linear interpolation.  The aim is a guess; the
-// symbol is then settled with the exact prefix, so this table only moves
-// cost, never results.
+// Every 64th escape-prefix entry in LDS, for the lookup of floor-and-escape
+// slots (e4m3 keeps its whole prefix there instead).
 constexpr int kCoarseEntries = 1026;             // 65536 / 64 + 1, plus one repeat
 
 template <int KV>
@@ -737,33 +794,6 @@ __device__ __forceinline__ void build_coarse_lds(uint32_t* s_pc, const uint32_t*
     for (uint32_t j = threadIdx.x; j <= last + 1u; j += blockDim.x) {
         const uint32_t jj = j > last ? last : j;
         s_pc[j] = prefix[jj << Coarse<KV>::kShift];
-    }
-}
-
-template <int KV>
-__device__ __forceinline__ uint32_t coarse_prefix(const uint32_t* s_pc, uint32_t b) {
-    if constexpr (Coarse<KV>::kShift == 0) {
-        return s_pc[b];
-    } else {
-        constexpr int sh = Coarse<KV>::kShift;
-        const uint32_t j = b >> sh, r = b & ((1u << sh) - 1u);
-        const uint32_t lo = s_pc[j], hi = s_pc[j + 1];
-        // (hi - lo) >> sh < 2^20: a 24-bit multiply; the dropped low bits move
-        // the guess by under 2^sh slots
-        const uint32_t step = (hi - lo) >> sh;
-        __builtin_assume(step < (1u << 20));
-        return lo + step * r;
-    }
-}
-
-// Ordered index of mu's own symbol (exact for a bf16 mean, nearest otherwise).
-template <int KV, int MU>
-__device__ __forceinline__ uint32_t mean_symbol(typename MuT<MU>::T raw, float mu) {
-    if constexpr (KV == kBF16 && MU == kBF16) {
-        const uint32_t u = raw;
-        return (u & 0x7F80u) == 0x7F80u ? 32768u : order_of_bits<kBF16>(u);   // non-finite mean counts as 0
-    } else {
-        return nearest_symbol<KV>(mu);
     }
 }
 
@@ -826,9 +856,8 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
 
     uint32_t rp = 0, misses = 0;
     for (uint32_t t0 = 0; t0 < cp.len; t0 += kDecodeBatch) {
-        // model side of the batch: predictor means and their escape bias
+        // model side of the batch: predictor means
         float mus[kDecodeBatch];
-        uint32_t bias[kDecodeBatch];
         MT raw[kDecodeBatch];
 #pragma unroll
         for (int u = 0; u < kDecodeBatch; ++u) {
@@ -836,57 +865,89 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
             raw[u] = row_elem(mup + static_cast<uint64_t>(t) * D, static_cast<uint32_t>(lane));
         }
 #pragma unroll
-        for (int u = 0; u < kDecodeBatch; ++u) {
-            mus[u] = mu_value<MU>(raw[u]);
-            const uint32_t gm = mean_symbol<KV, MU>(raw[u], mus[u]);
-            bias[u] = gm + s_pc[gm >> Coarse<KV>::kShift];        // first aim: the step is close enough
-        }
+        for (int u = 0; u < kDecodeBatch; ++u) mus[u] = mu_value<MU>(raw[u]);
 #pragma unroll
         for (int u = 0; u < kDecodeBatch; ++u) {
             if (t0 + u >= cp.len) break;                 // wave-uniform
             const float mu = mus[u];
-            const uint32_t bs = bias[u];
             const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
-            // aim twice (escape and floor mass taken at mu's symbol, then at
-            // the first guess), then check the nearest edge and a neighbour
-            uint32_t E, E2, cE, c2;
+            const bool in_g = target < htot;             // a Gaussian slot
+            // Gaussian slots: aim through the inverse table, check the nearest
+            // edge and one neighbour.  Floor-and-escape slots: look the symbol
+            // up (it does not depend on the model) and evaluate its two edges.
+            uint32_t E, qe = 0, fqe = 0;
+            uint32_t mag = 0, sgn = 0;                   // bf16: E's edge as magnitude pattern and sign
+            if constexpr (KV == kBF16) {
+                const Bf16Edge ed = nearest_edge_bf16(aim_pos(static_cast<int32_t>(target), mu, sg, aim));
+                E = ed.e;
+                mag = ed.mag;
+                sgn = ed.sign;
+            } else {
+                E = nearest_edge_e4m3(aim_pos(static_cast<int32_t>(target), mu, sg, aim));
+            }
+            if (__ballot(!in_g)) {
+                uint32_t se = 0;
+                escape_search<KV>(!in_g, target - htot, s_pc, m.prefix, se, qe, fqe);
+                if (!in_g) {
+                    E = se;
+                    if constexpr (KV == kBF16) {
+                        const uint32_t ad = se >= 32768u ? se - 32768u : 32768u - se;
+                        mag = __builtin_elementwise_sub_sat(ad << 16, 0x8000u);     // 0 for the edge 0
+                        sgn = se < 32768u ? 0x80000000u : 0u;
+                    }
+                }
+                misses += in_g ? 0u : 1u;
+            }
+            uint32_t gE, gE2, E2, p0, p1, p2;
             bool up;
             if constexpr (KV == kBF16) {
-                const uint32_t E1 = nearest_edge_bf16(aim_pos_near(static_cast<int32_t>(target - bs), mu, sg, aim)).e;
-                const uint32_t qE = E1 + coarse_prefix<KV>(s_pc, E1);
-                const Bf16Edge ed = nearest_edge_bf16(aim_pos(static_cast<int32_t>(target - qE), mu, sg, aim));
-                E = ed.e;
-                const uint32_t* pp = m.prefix + (E - 1u);         // E >= 1: one 12-byte read
-                const uint32_t p0 = pp[0], p1 = pp[1], p2 = pp[2];
-                cE = E + h_fx(z_fixed(edge_pattern<MU>(ed.mag, ed.sign), mu, inv24), m.tab) + p1;
-                up = target >= cE;
+                // prefix at E-1, E, E+1 (one 12-byte read; escape lanes use
+                // their lookup instead, so their base is only kept in range)
+                const uint32_t pb = E - 1u < 65535u ? E - 1u : 0u;          // reads pb .. pb + 2 <= N
+                const uint32_t* pp = m.prefix + pb;
+                p0 = pp[0];
+                p1 = pp[1];
+                p2 = pp[2];
+                gE = h_fx(z_fixed(edge_pattern<MU>(mag, sgn), mu, inv24), m.tab);
+                up = !in_g || target >= gE;
                 // the neighbour one step away from zero (up on the positive
-                // side) or towards it; towards zero from m = 0 is the edge 0
-                const bool outward = up != (ed.sign != 0u);
-                const uint32_t mag2 = outward ? ed.mag + 0x10000u : __builtin_elementwise_sub_sat(ed.mag, 0x10000u);
+                // side) or towards it; away from the edge 0 is 2^15
+                const bool outward = up != (sgn != 0u);
+                const uint32_t mag2 = outward ? ((mag + 0x8000u) | 0x8000u) : __builtin_elementwise_sub_sat(mag, 0x10000u);
                 E2 = up ? E + 1u : E - 1u;
-                c2 = E2 + h_fx(z_fixed(edge_pattern<MU>(mag2, ed.sign), mu, inv24), m.tab) + (up ? p2 : p0);
+                gE2 = h_fx(z_fixed(edge_pattern<MU>(mag2, sgn), mu, inv24), m.tab);
             } else {
-                // e4m3: edges and the exact prefix come from LDS
-                E = nearest_edge_e4m3(aim_pos_near(static_cast<int32_t>(target - bs), mu, sg, aim));
-                E = nearest_edge_e4m3(aim_pos(static_cast<int32_t>(target - (E + s_pc[E])), mu, sg, aim));
-                cE = e4_cdf(s_pc, m.tab, E, mu, inv24);
-                up = target >= cE;
+                const uint32_t pb = E - 1u < 255u ? E - 1u : 0u;            // reads pb .. pb + 2 <= N
+                p0 = s_pc[pb];
+                p1 = s_pc[pb + 1u];
+                p2 = s_pc[pb + 2u];
+                gE = h_fx(z_fixed(e4_edge(s_pc, E), mu, inv24), m.tab);
+                up = !in_g || target >= gE;
                 E2 = up ? E + 1u : E - 1u;
-                c2 = e4_cdf(s_pc, m.tab, E2, mu, inv24);
+                gE2 = h_fx(z_fixed(e4_edge(s_pc, E2), mu, inv24), m.tab);
             }
-            const bool ok = up ? (target < c2) : (target >= c2);
-            Found fd;
-            fd.s = up ? E : E2;
-            fd.start = up ? cE : c2;
-            fd.freq = up ? c2 - cE : cE - c2;
-            if (__ballot(!ok)) {
-                misses += ok ? 0u : 1u;
-                coop_search<KV, MU>(!ok, target, mu, inv24, up, up ? E2 : 0u, up ? Alphabet<KV>::kSize : E2,
-                                up ? c2 : 0u, up ? kM : c2, m, geo, fd);
+            uint32_t sym = up ? E : E2;
+            uint32_t g0 = up ? gE : gE2;
+            uint32_t fg = up ? gE2 - gE : gE - gE2;
+            uint32_t qs = in_g ? sym + (up ? p1 : p0) : qe;              // Q(s)
+            uint32_t fq = in_g ? 1u + (up ? p2 - p1 : p1 - p0) : fqe;    // Q(s+1) - Q(s)
+            const bool need = in_g && (up ? target >= gE2 : target < gE2);
+            if (__ballot(need)) {
+                misses += need ? 1u : 0u;
+                coop_gauss<KV, MU>(need, target, mu, inv24, up, up ? E2 : 0u, up ? Alphabet<KV>::kSize : E2,
+                                   up ? gE2 : 0u, up ? htot : gE2, m, geo, sym, g0, fg);
+                if (need) {
+                    const uint32_t* pq = KV == kBF16 ? m.prefix : s_pc;
+                    const uint32_t a0 = pq[sym], a1 = pq[sym + 1u];
+                    qs = sym + a0;
+                    fq = 1u + (a1 - a0);
+                }
             }
+            // rank within the symbol's f = fg + fq slots
+            const uint32_t f = fg + fq;
+            const uint32_t r = in_g ? target - g0 : fg + (target - htot - qs);
             // x < 2^63, so x >> 31 fits 32 bits: one 32 x 32 -> 64 multiply-add
-            x = static_cast<unsigned long long>(fd.freq) * static_cast<uint32_t>(x >> kLog2M) + (target - fd.start);
+            x = static_cast<unsigned long long>(f) * static_cast<uint32_t>(x >> kLog2M) + r;
 
             // refill: a lane takes one word when x < 2^47 and a second one
             // when x < 2^31 (then x << 16 is still below 2^47); round one
@@ -909,7 +970,7 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
             win.advance(rp, static_cast<uint32_t>(lane));
             KB* orow = outp + static_cast<uint64_t>(t0 + u) * D;
             *reinterpret_cast<KB*>(reinterpret_cast<char*>(orow) + static_cast<uint32_t>(lane) * sizeof(KB)) =
-                static_cast<KB>(bits_of_order<KV>(fd.s));
+                static_cast<KB>(bits_of_order<KV>(sym));
         }
     }
     // every lane back at the initial state, the payload consumed exactly,

@@ -90,7 +90,8 @@ typedef struct kvc_params {
     int64_t channels;        /* D, a positive multiple of 64                       */
 } kvc_params;
 
-/* Library version (KVC-1 stream format = 1). */
+/* Stream format version written and accepted: 2 (Gaussian and floor-and-escape
+   slots in separate ranges of the coder). */
 int kvc_version(void);
 
 /* Human-readable name of a status code (static string). */

@@ -30,7 +30,7 @@ import struct
 import numpy as np
 
 __all__ = [
-    "BF16", "E4M3", "F32", "M", "L", "LANES", "HEADER_BYTES", "STATE_BYTES", "StreamError",
+    "BF16", "E4M3", "F32", "M", "L", "LANES", "HEADER_BYTES", "STATE_BYTES", "VERSION", "StreamError",
     "alphabet_size", "budgets", "order_index", "bits_of_order", "symbol_value",
     "boundary_positions", "phi_tables", "mixture_table", "h_fx", "mu_to_f32", "cdf",
     "gauss_cum", "escape_cum",
