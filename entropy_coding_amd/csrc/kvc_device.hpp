@@ -234,7 +234,8 @@ __device__ __forceinline__ void divmod_q32(uint32_t xh, uint32_t xl, uint32_t f,
     const double fd = static_cast<double>(f);
     double rc = __builtin_amdgcn_rcp(fd);
     rc = __fma_rn(rc, __fma_rn(-fd, rc, 1.0), rc);
-    const double xd = __fma_rn(static_cast<double>(xh), 4294967296.0, static_cast<double>(xl));
+    // xh < 2^31 (x < 2^63): a signed conversion is exact and cheaper
+    const double xd = __fma_rn(static_cast<double>(static_cast<int32_t>(xh)), 4294967296.0, static_cast<double>(xl));
     const uint32_t q0 = static_cast<uint32_t>(__builtin_fmin(__fma_rn(xd, rc, 0.5), 4294967295.0));
     // rem = x - q0 f lies in [-f, f): negative exactly when the high word borrows
     const uint64_t p = static_cast<uint64_t>(q0) * f;

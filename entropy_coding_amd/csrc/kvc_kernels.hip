@@ -931,7 +931,8 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
             uint32_t fg = up ? gE2 - gE : gE - gE2;
             uint32_t qs = in_g ? sym + (up ? p1 : p0) : qe;              // Q(s)
             uint32_t fq = in_g ? 1u + (up ? p2 - p1 : p1 - p0) : fqe;    // Q(s+1) - Q(s)
-            const bool need = in_g && (up ? target >= gE2 : target < gE2);
+            // bracketed: target < G(E+1) going up, target >= G(E-1) going down
+            const bool need = in_g && ((target < gE2) != up);
             if (__ballot(need)) {
                 misses += need ? 1u : 0u;
                 coop_gauss<KV, MU>(need, target, mu, inv24, up, up ? E2 : 0u, up ? Alphabet<KV>::kSize : E2,
