@@ -127,6 +127,26 @@ def test_stream_matches_oracle_and_round_trips(kvc, cuda, kv_dtype, w, tc, g, t,
     assert np.array_equal(out2.cpu().numpy().view(kv.dtype), kv)
 
 
+@pytest.mark.parametrize("kv_dtype", [O.BF16, O.E4M3])
+@pytest.mark.parametrize("w", [(0, 0), (0, 10000), (5000, 0), (9999, 0)])
+@pytest.mark.parametrize("marg", ["data", "peaked"])
+def test_escape_heavy_and_escape_free_mixtures(kvc, cuda, kv_dtype, w, marg):
+    """Weights that put every slot in the floor-and-escape range (0, 0), none
+    there but the floor (0, 10000), half of them (5000, 0) or a sliver
+    (9999, 0), with the marginal of the data or one concentrated on a single
+    symbol: streams identical to the oracle's, and they decode."""
+    kv, mu, sig, samples, mu_dtype = tiny(kv_dtype, planes=2, tokens=40, channels=128)
+    if marg == "peaked":
+        samples = np.full_like(samples, samples[0])
+    pref = O.build_marginal(samples, kv_dtype, *w) if w[0] + w[1] < 10000 else None
+    expect = O.encode(kv, mu, sig, pref, kv_dtype, mu_dtype, *w, 16)
+    kv_d, mu_d, sig_d, pref_d = dev_bits(kv, cuda), dev_bits(mu, cuda), torch.from_numpy(sig).to(cuda), dev_prefix(pref, cuda)
+    st = kvc.kvc_encode(kv_d, mu_d, sig_d, pref_d, w, 16)
+    assert host_bytes(st) == expect
+    out = kvc.kvc_decode(st, mu_d, sig_d, pref_d)
+    assert np.array_equal(out.cpu().numpy().view(kv.dtype), kv)
+
+
 def test_golden_streams(kvc, cuda):
     with open(os.path.join(ROOT, "tests", "golden", "tiny_streams.txt")) as f:
         lines = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
