@@ -104,64 +104,6 @@ __device__ __forceinline__ float edge(uint32_t b) {
     else return edge_e4m3(b);
 }
 
-// Value of a finite ordered symbol.
-template <int KV>
-__device__ __forceinline__ float symbol_value(uint32_t b) {
-    const uint32_t u = bits_of_order<KV>(b);
-    if constexpr (KV == kBF16) {
-        return __uint_as_float(u << 16);
-    } else {
-        const float v = e4m3_magnitude(u & 0x7Fu);
-        return (u & 0x80u) ? -v : v;
-    }
-}
-
-// Ordered index of a finite symbol near x, clamped to the finite range.
-// Used only to aim the decoder's search, so rounding details do not matter.
-template <int KV>
-__device__ __forceinline__ uint32_t nearest_symbol(float x) {
-    if constexpr (KV == kBF16) {
-        const uint32_t u = __float_as_uint(x);
-        const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-        uint32_t b = order_of_bits<kBF16>(r & 0xFFFFu);
-        b = b < Alphabet<kBF16>::kLoFinite ? Alphabet<kBF16>::kLoFinite : b;
-        return b > Alphabet<kBF16>::kHiFinite ? Alphabet<kBF16>::kHiFinite : b;
-    } else {
-        // round |x| to 3 mantissa bits (normal range) or to a multiple of
-        // 2^-9 (subnormal range), saturating at 448
-        const float ax = fminf(fabsf(x), 448.0f);
-        uint32_t m;
-        if (ax < 0x1p-6f) {
-            m = static_cast<uint32_t>(__builtin_rintf(ax * 512.0f));     // 0..8 (8 = 2^-6)
-        } else {
-            const uint32_t u = __float_as_uint(ax);
-            const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;    // 8-bit exponent, 3-bit mantissa
-            m = r - (120u << 3);
-        }
-        m = m > 126u ? 126u : m;
-        const uint32_t bits = m | (x < 0.0f ? 0x80u : 0u);
-        return order_of_bits<kE4M3>(bits);
-    }
-}
-
-// Index of the cell edge nearest to x (within one cell; the decoder only
-// aims with it), clamped so that it and both neighbours are valid indices.
-// bf16 edges sit at fp32 patterns m * 2^16 + 2^15, so the nearest is m =
-// pattern >> 16 on either sign.
-template <int KV>
-__device__ __forceinline__ uint32_t nearest_edge(float x) {
-    if constexpr (KV == kBF16) {
-        const uint32_t u = __float_as_uint(x);
-        const uint32_t m = (u & 0x7FFFFFFFu) >> 16;
-        uint32_t e = (u >> 31) ? 32767u - m : 32769u + m;
-        e = e < Alphabet<kBF16>::kLoFinite ? Alphabet<kBF16>::kLoFinite : e;
-        return e > Alphabet<kBF16>::kHiFinite + 1u ? Alphabet<kBF16>::kHiFinite + 1u : e;
-    } else {
-        const uint32_t jb = nearest_symbol<kE4M3>(x);
-        return jb + (x > symbol_value<kE4M3>(jb) ? 1u : 0u);
-    }
-}
-
 // Predictor mean as float32; a non-finite mean is replaced by 0.
 template <int MU> struct MuT;
 template <> struct MuT<kBF16> { using T = uint16_t; };

@@ -5,8 +5,9 @@
 // 64-element row of KV and mu per wave, and the 64 interleaved rANS states
 // live in registers.  Renormalisation words are placed with two wave ballots
 // and mbcnt ranks.  Each workgroup builds the mixture table (and, for the
-// decoder, its inverse index) in LDS from two per-device Phi tables; the
-// escape prefix (256 KB for bf16) is read through L2.  Sources for the
+// decoder, its inverse index and every 64th escape-prefix entry) in LDS
+// from two per-device Phi tables; the escape prefix itself (256 KB for bf16)
+// is read through L2 (e4m3's 1 KB prefix sits in LDS).  Sources for the
 // model: wiki "Speculative KV Coding" (sections "pipeline", "mixture
 // distribution"); blog post on speculative KV coding (sections "information
 // theory view", "engineering choice of predictor", "deployment parameters").
@@ -182,12 +183,6 @@ __device__ __forceinline__ void build_e4_lds(uint32_t* t, const uint32_t* __rest
 
 __device__ __forceinline__ float e4_edge(const uint32_t* t, uint32_t b) {
     return __uint_as_float(t[kE4EdgeOff + b]);
-}
-
-// C(b) for e4m3 from the LDS table: b + h(q_b) + prefix[b].
-__device__ __forceinline__ uint32_t e4_cdf(const uint32_t* t, const uint32_t* tab, uint32_t b, float mu,
-                                           float inv24) {
-    return b + h_fx(z_fixed(e4_edge(t, b), mu, inv24), tab) + t[b];
 }
 
 // Nearest e4m3 cell edge to x, for aiming only: the magnitude pattern h of
@@ -382,7 +377,7 @@ hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStr
 // ---------------------------------------------------------------------------
 // stream compaction: exclusive scan of chunk sizes (one workgroup, wave
 // scans), then one workgroup per chunk copies states and words to the
-// chunk's final offset with 16-byte stores.
+// chunk's final offset with 8-byte stores.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ unsigned long long chunk_bytes(uint32_t words) {
     return (static_cast<unsigned long long>(kStateBytes) + 2ull * words + 7ull) & ~7ull;
@@ -499,16 +494,18 @@ hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream
 // ---------------------------------------------------------------------------
 // decoder: one wave per chunk, tokens first to last.
 //
-// Finding the symbol s with C(s) <= target < C(s+1): C(b) = Q(b) + H(z_b)
-// with Q(b) = b + prefix[b] (floor and escape mass) and H the mixture
-// table.  The aim inverts H through a float table of z at evenly spaced
-// values of H, once with Q taken at the predictor's own symbol and once
-// with Q at the first guess; the edge E nearest the aimed position and one
-// neighbour are evaluated exactly.  Lanes that still miss (tail symbols,
-// under one in a hundred) are resolved one at a time by the whole wave: 63
-// lanes probe the missing lane's bracket at once (geometrically spaced from
-// the known end first, then evenly), so any miss takes two or three rounds.
-// The result is exact whatever the aim; the aim only sets the cost.
+// A target below T_n + T_w is a Gaussian slot: the symbol s has
+// G(s) <= target < G(s+1) with G the mixture-table term alone.  The aim
+// inverts G through a float table of z at evenly spaced values of it; the
+// edge E nearest the aimed position and one neighbour are evaluated
+// exactly.  Lanes the aim misses (0.07% of symbols on the 8B-shaped
+// workload) are resolved one at a time by the whole wave: 63 lanes probe
+// the missing lane's bracket at once (geometrically spaced from the known end
+// first, then evenly).  A target above is a floor-and-escape slot, whose
+// symbol depends only on the static prefix: the wave looks it up (three
+// ballot rounds), then evaluates G at the symbol's two edges for its
+// frequency.  The result is exact whatever the aim; the aim only sets the
+// cost.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeBlock = 1024;
 constexpr int kDecodeBatch = 4;
@@ -542,7 +539,6 @@ __device__ __forceinline__ void build_zinv_lds(float* s_zinv, const uint32_t* s_
 struct Aim {
     const float* __restrict__ zinv;    // LDS
     float scale;                       // kZinvSteps / htot (0 when there is no Gaussian part)
-    int32_t htot;
 };
 
 // Position where H reaches `e` (clamped to [0, htot]).
@@ -553,19 +549,6 @@ __device__ __forceinline__ float aim_pos(int32_t e, float mu, float sg, const Ai
     const float z0 = a.zinv[j], z1 = a.zinv[j + 1];
     const float z = __fmaf_rn(fr, z1 - z0, z0);
     return __fmaf_rn(z, sg, mu);
-}
-
-// The same without interpolation (the nearest table entry): the first of
-// the two aims only has to land near enough to pick the escape bias.
-__device__ __forceinline__ float aim_pos_near(int32_t e, float mu, float sg, const Aim& a) {
-    const float ef = __builtin_amdgcn_fmed3f(static_cast<float>(e) * a.scale, 0.0f, static_cast<float>(kZinvSteps));
-    const int j = static_cast<int>(ef + 0.5f);
-    return __fmaf_rn(a.zinv[j], sg, mu);
-}
-
-template <int KV>
-__device__ __forceinline__ uint32_t aim_edge(int32_t e, float mu, float sg, const Aim& a) {
-    return nearest_edge<KV>(aim_pos(e, mu, sg, a));
 }
 
 // bf16 edge nearest to x, as its index and the magnitude pattern of its
@@ -844,8 +827,7 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
         sg = 1.0f;
     }
     const Model m{s_tab, a.prefix, s_pc};
-    const Aim aim{s_zinv, htot ? static_cast<float>(kZinvSteps) / static_cast<float>(htot) : 0.0f,
-                  static_cast<int32_t>(htot)};
+    const Aim aim{s_zinv, htot ? static_cast<float>(kZinvSteps) / static_cast<float>(htot) : 0.0f};
     const uint32_t geo = geo_offset(lane);
 
     using KB = typename Alphabet<KV>::Bits;

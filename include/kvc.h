@@ -69,8 +69,10 @@ typedef struct kvc_decode_info {
     float stage_ms[KVC_DECODE_STAGES];  /* GPU time of: side-information checksum,
                                            decoding kernel                        */
     uint32_t reserved;
-    uint64_t fallback_symbols;          /* symbols the decoder's aimed search
-                                           missed and found by bisection          */
+    uint64_t fallback_symbols;          /* symbols not found by the aim: slots in
+                                           the floor-and-escape range (looked up
+                                           by the wave) plus Gaussian slots the
+                                           aim missed (searched by the wave)      */
 } kvc_decode_info;
 
 typedef struct kvc_params {
@@ -150,7 +152,7 @@ int kvc_stream_info(const void* h_header, uint64_t header_bytes, kvc_params* h_p
  * and consume exactly its chunk).
  * Workspace: KVC_DECODE_WORKSPACE_BYTES.  Synchronises `stream` twice
  * (header read, status read).  h_info: NULL, or receives the stage times
- * and the number of symbols found by the fallback search.
+ * and the number of symbols the aim did not find.
  */
 int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu,
                const float* d_sigma, const uint32_t* d_prefix, void* d_kv_out,
