@@ -23,6 +23,12 @@ constexpr uint32_t kLanes = 64;
 constexpr uint32_t kVersion = 2;   // stream format version (split slot ranges)
 constexpr uint32_t kMaxChunkTokens = 1u << 20;
 constexpr int64_t kMaxScalars = int64_t(1) << 40;
+// decode workspace: control block, the start of the prefix's hot window
+// (one u32), then the escape bucket table (u16)
+constexpr uint64_t kDecodeHotOffset = 64;
+constexpr uint64_t kDecodeBucketOffset = 256;
+static_assert(kDecodeBucketOffset + 2 * kvc::kEscapeBucketsMax <= KVC_DECODE_WORKSPACE_BYTES,
+              "decode workspace holds the control block and the bucket table");
 
 uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -47,7 +53,8 @@ bool geometry(int64_t planes, int64_t tokens, int64_t channels, uint32_t chunk_t
     if (planes * channels >= (int64_t(1) << 32)) return false;         // sigma words indexable
     if (planes * tokens > kMaxScalars / channels) return false;
     if (chunk_tokens < 1 || chunk_tokens > kMaxChunkTokens) return false;
-    if (int64_t(chunk_tokens) * channels >= (int64_t(1) << 31)) return false;   // in-chunk offsets fit 31 bits
+    // a chunk's rows span chunk_tokens * channels scalars of up to 4 bytes: byte offsets fit 31 bits
+    if (int64_t(chunk_tokens) * channels >= (int64_t(1) << 29)) return false;
     g->planes = planes;
     g->tokens = tokens;
     g->channels = channels;
@@ -364,11 +371,25 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     if (!data_aligned(p.kv_dtype, p.mu_dtype, d_kv_out, d_mu, d_sigma, d_prefix)) return KVC_ERR_INVALID;
 
     Control* ctl = static_cast<Control*>(d_workspace);
+    // escape bucket table after the control block: the smallest shift that
+    // keeps ((N + T_e - 1) >> shift) + 2 entries within the table
+    const uint32_t n_sym = alphabet(p.kv_dtype);
+    const uint64_t q_total = uint64_t(n_sym) + te;
+    uint32_t shift = 0;
+    while (((q_total - 1) >> shift) + 2 > kvc::kEscapeBucketsMax) ++shift;
+    const uint32_t n_buckets = static_cast<uint32_t>(((q_total - 1) >> shift) + 2);
+    uint16_t* buckets = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(d_workspace) + kDecodeBucketOffset);
     StageTimer timer(h_info ? h_info->stage_ms : nullptr, KVC_DECODE_STAGES, s);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(0);
     if ((e = kvc::launch_side_hash(d_sigma, uint64_t(g.planes) * uint64_t(g.channels), prefix,
-                                   prefix ? alphabet(p.kv_dtype) + 1u : 0u, ctl, s)) != hipSuccess)
+                                   prefix ? n_sym + 1u : 0u, ctl, s)) != hipSuccess)
+        return KVC_ERR_DEVICE;
+    if ((e = kvc::launch_escape_buckets(prefix ? prefix : phi.zero, n_sym, shift, n_buckets, buckets, s)) !=
+        hipSuccess)
+        return KVC_ERR_DEVICE;
+    uint32_t* hot_lo = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d_workspace) + kDecodeHotOffset);
+    if (p.kv_dtype == KVC_BF16 && (e = kvc::launch_hot_window(prefix ? prefix : phi.zero, hot_lo, s)) != hipSuccess)
         return KVC_ERR_DEVICE;
     timer.mark(1);
     const uint8_t* in = static_cast<const uint8_t*>(d_in);
@@ -383,6 +404,10 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     da.tn = tn;
     da.tw = tw;
     da.phi = phi;
+    da.buckets = buckets;
+    da.bucket_shift = shift;
+    da.te = te;
+    da.hot_lo = hot_lo;
     da.kv_out = d_kv_out;
     da.ctl = ctl;
     if ((e = kvc::launch_decode(da, p.kv_dtype, p.mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;

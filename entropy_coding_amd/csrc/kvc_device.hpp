@@ -142,11 +142,28 @@ __device__ __forceinline__ uint32_t h_fx(int32_t q, const uint32_t* __restrict__
     return a + static_cast<uint32_t>((static_cast<uint64_t>(dlt) * r) >> 16);
 }
 
+// Raw buffer resource over `bytes` bytes at p (gfx9 layout: no stride,
+// dword 3 = 0x00020000).  An access through it takes a per-lane byte offset
+// in a vector register and a wave-uniform one in a scalar register, so the
+// address costs no vector arithmetic; reads beyond the range return 0 and
+// writes beyond it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+
 struct Model {
     const uint32_t* __restrict__ tab;      // mixture table in LDS
     const uint32_t* __restrict__ prefix;   // escape prefix (N + 1 entries; zeros without an escape part)
-    const uint32_t* small = nullptr;       // e4m3 only: prefix and edges in LDS
+    const uint32_t* small;                 // e4m3 only: prefix and edges in LDS
+    __amdgpu_buffer_rsrc_t pre;            // the escape prefix as a buffer
 };
+
+// prefix[s] and prefix[s + 1] in one 8-byte read
+__device__ __forceinline__ void prefix_pair(const Model& m, uint32_t s, uint32_t& p0, uint32_t& p1) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(m.pre, s << 2, 0, 0);
+    p0 = v[0];
+    p1 = v[1];
+}
 
 // C(b) = b + h_fx(q(b)) + prefix[b].
 template <int KV>

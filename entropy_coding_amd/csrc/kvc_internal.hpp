@@ -84,6 +84,10 @@ struct DecodeArgs {
     const uint32_t* prefix;
     uint32_t tn, tw;
     PhiTables phi;
+    const uint16_t* buckets;            // escape bucket table (launch_escape_buckets)
+    uint32_t bucket_shift;
+    uint32_t te;                        // escape budget (0: no escape part)
+    const uint32_t* hot_lo;             // bf16: start of the prefix's hot window (launch_hot_window)
     void* kv_out;
     Control* ctl;
 };
@@ -113,6 +117,13 @@ hipError_t launch_scan(const uint32_t* chunk_words, int64_t n_chunks,
                        unsigned long long* directory, Control* ctl, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);
+// Bucket table of Q(b) = b + prefix[b] for the decoder's floor-and-escape
+// lookup: bucket[j] = largest s < n_sym with Q(s) <= j << shift.
+constexpr uint32_t kEscapeBucketsMax = 65538;
+hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_t shift, uint32_t n_entries,
+                                 uint16_t* bucket, hipStream_t s);
+// bf16: the start of the decoder's hot window of the prefix, one u32.
+hipError_t launch_hot_window(const uint32_t* prefix, uint32_t* out, hipStream_t s);
 // sigma calibration: float64 partial sums per (split, plane, channel)
 struct CalibPart {
     double sum;

@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "kvc_device.hpp"
 #include "kvc_internal.hpp"
@@ -185,18 +186,6 @@ __device__ __forceinline__ float e4_edge(const uint32_t* t, uint32_t b) {
     return __uint_as_float(t[kE4EdgeOff + b]);
 }
 
-// Nearest e4m3 cell edge to x, for aiming only: the magnitude pattern h of
-// |x| truncated to the e4m3 grid (3 mantissa bits; steps of 2^-9 below 2^-6)
-// puts |x| between symbols h and h + 1, whose midpoint is the nearest edge.
-__device__ __forceinline__ uint32_t nearest_edge_e4m3(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const float ax = __builtin_fabsf(x);
-    int32_t h = ax < 0x1p-6f ? static_cast<int32_t>(ax * 512.0f)
-                             : static_cast<int32_t>((u & 0x7FFFFFFFu) >> 20) - (120 << 3);
-    h = h < 126 ? h : 126;
-    return (u >> 31) ? static_cast<uint32_t>(127 - h) : static_cast<uint32_t>(129 + h);
-}
-
 // ---------------------------------------------------------------------------
 // encoder: one wave per chunk, tokens last to first.  The model side of a
 // batch of tokens (loads, symbol, both CDF edges) does not depend on the
@@ -250,7 +239,8 @@ __device__ __forceinline__ void rans_push(PushState& st, const SymSlots& y, uint
 __device__ __forceinline__ SymSlots make_slots(uint32_t s, uint32_t ga, uint32_t gb, const Model& m, uint32_t htot) {
     const uint32_t g0 = __builtin_elementwise_min(ga, gb);
     const uint32_t fg = __builtin_elementwise_max(ga, gb) - g0;
-    const uint32_t p0 = m.prefix[s], p1 = m.prefix[s + 1];
+    uint32_t p0, p1;
+    prefix_pair(m, s, p0, p1);
     SymSlots y;
     y.g0 = g0;
     y.fg = fg;
@@ -341,7 +331,7 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
         if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
         inv24 = 16777216.0f;
     }
-    const Model m{s_tab, a.prefix, s_small};
+    const Model m{s_tab, a.prefix, s_small, buffer_rsrc(a.prefix, (Alphabet<KV>::kSize + 1u) * 4u)};
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
@@ -494,107 +484,196 @@ hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream
 // ---------------------------------------------------------------------------
 // decoder: one wave per chunk, tokens first to last.
 //
-// A target below T_n + T_w is a Gaussian slot: the symbol s has
-// G(s) <= target < G(s+1) with G the mixture-table term alone.  The aim
-// inverts G through a float table of z at evenly spaced values of it; the
-// edge E nearest the aimed position and one neighbour are evaluated
-// exactly.  Lanes the aim misses (0.07% of symbols on the 8B-shaped
-// workload) are resolved one at a time by the whole wave: 63 lanes probe
-// the missing lane's bracket at once (geometrically spaced from the known end
-// first, then evenly).  A target above is a floor-and-escape slot, whose
-// symbol depends only on the static prefix: the wave looks it up (three
-// ballot rounds), then evaluates G at the symbol's two edges for its
-// frequency.  The result is exact whatever the aim; the aim only sets the
-// cost.
+// The rANS target t = x mod 2^31 lies either in the Gaussian range
+// [0, T_n + T_w), where the symbol s is the one with G(s) <= t < G(s+1), or
+// in the floor-and-escape range above it, where s is the one with
+// Q(s) <= t - T_n - T_w < Q(s+1); Q does not depend on the lane's model.
+//
+// Gaussian range: the aim inverts the mixture table through a table of z at
+// log-spaced distances of t from the nearer end of the range (so the tails,
+// where G is flat in z, are resolved as finely as the bulk), takes the cell
+// the aimed position mu + z sigma falls in, and evaluates G exactly at that
+// cell's two edges, as the encoder does.  A cell that does not bracket t is
+// moved one symbol towards it and checked again; what still misses is
+// searched by the whole wave.  Floor-and-escape range: a bucket table of Q
+// (built per call from the prefix) brackets s, and a per-lane binary search
+// over the exact prefix finishes it.  The symbol found never depends on the
+// aim, only the cost of finding it.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeBlock = 1024;
 constexpr int kDecodeBatch = 4;
-constexpr int kZinvSteps = 4096;
 
-// zinv[j] = z at which the (interpolated) mixture table reaches
-// floor(j * htot / kZinvSteps); one repeated entry past the end lets the aim
-// truncate without a bound check.
-__device__ __forceinline__ void build_zinv_lds(float* s_zinv, const uint32_t* s_tab, uint32_t htot) {
-    for (int j = threadIdx.x; j <= kZinvSteps + 1; j += blockDim.x) {
-        const int jj = j > kZinvSteps ? kZinvSteps : j;
-        const uint32_t e = static_cast<uint32_t>((static_cast<uint64_t>(htot) * jj) / kZinvSteps);
-        uint32_t lo = 0, hi = kTablePoints;           // largest k with H[k] <= e
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (s_tab[mid] <= e) lo = mid;
-            else hi = mid;
-        }
-        float z;
-        if (lo >= static_cast<uint32_t>(kTablePoints - 1)) {
-            z = static_cast<float>(kTableZMax);
-        } else {
-            const float fr = static_cast<float>(e - s_tab[lo]) / static_cast<float>(s_tab[lo + 1] - s_tab[lo]);
-            z = (static_cast<float>(lo) + fr) * (1.0f / 256.0f) - static_cast<float>(kTableZMax);
-        }
-        s_zinv[j] = z;
+// Aim table: z(d), the position at which the interpolated mixture table
+// reaches d, is linear between the knots d_j = 2^(j >> 6) (1 + (j & 63) / 64);
+// entry j holds the line's intercept and slope (z = c_j + k_j d on
+// [d_j, d_{j+1})), so that the float32 bits of d give the entry (exponent
+// and top mantissa bits) and one fused multiply-add gives z.  Distances
+// stay below 2^31 (one entry at 2^31 takes float rounding).
+constexpr int kAimMantBits = 5;
+constexpr uint32_t kAimFracBits = 23 - kAimMantBits;
+constexpr int kAimEntries = (31 << kAimMantBits) + 1;
+
+__device__ __forceinline__ double table_inverse(const uint32_t* s_tab, double d) {
+    uint32_t lo = 0, hi = kTablePoints;                 // largest k with H[k] <= d
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (static_cast<double>(s_tab[mid]) <= d) lo = mid;
+        else hi = mid;
+    }
+    if (lo >= static_cast<uint32_t>(kTablePoints - 1)) return kTableZMax;
+    const double fr = (d - s_tab[lo]) / static_cast<double>(s_tab[lo + 1] - s_tab[lo]);
+    return (lo + fr) / 256.0 - kTableZMax;
+}
+
+__device__ __forceinline__ double aim_knot(int j) {
+    return ldexp(1.0 + static_cast<double>(j & ((1 << kAimMantBits) - 1)) / (1 << kAimMantBits), j >> kAimMantBits);
+}
+
+__device__ __forceinline__ void build_aim_lds(float2* s_aim, const uint32_t* s_tab) {
+    for (int j = threadIdx.x; j < kAimEntries; j += blockDim.x) {
+        const double d0 = aim_knot(j), d1 = aim_knot(j + 1);
+        const double z0 = table_inverse(s_tab, d0), z1 = table_inverse(s_tab, d1);
+        const double k = (z1 - z0) / (d1 - d0);
+        s_aim[j] = make_float2(static_cast<float>(z0 - k * d0), static_cast<float>(k));
     }
     __syncthreads();
 }
 
-struct Aim {
-    const float* __restrict__ zinv;    // LDS
-    float scale;                       // kZinvSteps / htot (0 when there is no Gaussian part)
-};
-
-// Position where H reaches `e` (clamped to [0, htot]).
-__device__ __forceinline__ float aim_pos(int32_t e, float mu, float sg, const Aim& a) {
-    const float ef = __builtin_amdgcn_fmed3f(static_cast<float>(e) * a.scale, 0.0f, static_cast<float>(kZinvSteps));
-    const int j = static_cast<int>(ef);                // ef >= 0: truncation is floor
-    const float fr = __builtin_amdgcn_fractf(ef);
-    const float z0 = a.zinv[j], z1 = a.zinv[j + 1];
-    const float z = __fmaf_rn(fr, z1 - z0, z0);
-    return __fmaf_rn(z, sg, mu);
+// z where the mixture table reaches t (t < htot), from the distance to the
+// nearer end of the range; the upper half mirrors the lower one (the table
+// is symmetric to within 2 units).
+__device__ __forceinline__ float aim_z(uint32_t t, uint32_t htot, const float2* s_aim) {
+    const uint32_t u = htot - t;
+    const bool upper = u < t;
+    // the distance to the nearer end, at least 1 (med3 of t, u and 1)
+    const uint32_t d = __builtin_elementwise_max(__builtin_elementwise_min(t, u), 1u);
+    const float df = static_cast<float>(d);
+    // d >= 1: the exponent field starts at 127; the table is addressed from
+    // a base biased by that many octaves (the LDS address wraps back)
+    const float2 e = (s_aim - (127u << kAimMantBits))[__float_as_uint(df) >> kAimFracBits];
+    const float z = __fmaf_rn(df, e.y, e.x);
+    return upper ? -z : z;
 }
 
-// bf16 edge nearest to x, as its index and the magnitude pattern of its
-// position.  x is first clamped to the outer edges of -max / +max, so the
-// edge is m * 2^16 + 2^15 with m the upper half of x's magnitude pattern.
-// The outermost edges come out finite (the midpoints above +max and below
-// -max); edge_pattern() turns them into the infinities of the format.
-struct Bf16Edge {
-    uint32_t e;      // edge index, kLoFinite .. kHiFinite + 1
-    uint32_t mag;    // m * 2^16 + 2^15, at most 0x7F7F8000
-    uint32_t sign;   // 0x80000000 when x < 0
-};
-constexpr uint32_t kBf16OuterMag = 0x7F7F8000u;    // midpoint above +max
-
-__device__ __forceinline__ Bf16Edge nearest_edge_bf16(float x) {
-    const float lim = __uint_as_float(kBf16OuterMag);
+// bf16 pattern of the value nearest x (round to nearest even), x clamped
+// to [-max, max].
+__device__ __forceinline__ uint32_t nearest_bf16(float x) {
+    const float lim = __uint_as_float(0x7F7F0000u);
     const uint32_t u = __float_as_uint(__builtin_amdgcn_fmed3f(x, -lim, lim));
-    const uint32_t h = u >> 16;                      // bf16 pattern below x's magnitude
-    Bf16Edge r;
-    r.sign = u & 0x80000000u;
-    r.e = r.sign ? (h ^ 0xFFFFu) : h + 32769u;       // 32767 - m or 32769 + m
-    r.mag = (u & 0x7FFF0000u) | 0x8000u;
-    return r;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Position of the edge with magnitude pattern `mag` (at most one step past
-// kBf16OuterMag, or 0 for the edge between -0 and +0).  With a bf16 mean the
-// outer edge itself may stay finite: the mean lies inside [-max, max], at
-// least half a bf16 step from it, so z saturates at +-24 exactly as it does
-// for an infinite edge (sigma <= 2^96).  An fp32 mean can sit beyond it, so
-// there the edge becomes infinite as the format defines.
+// e4m3fn pattern of the value nearest x, x clamped to [-448, 448]:
+// subnormal steps of 2^-9 below 2^-6, three mantissa bits above.
+__device__ __forceinline__ uint32_t nearest_e4m3(float x) {
+    const float c = __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f);
+    const uint32_t u = __float_as_uint(c);
+    const uint32_t a = u & 0x7FFFFFFFu;
+    const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(__builtin_fabsf(c) * 512.0f));
+    const uint32_t nrm = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    return (a < 0x3C800000u ? sub : nrm) | ((u >> 24) & 0x80u);
+}
+
+template <int KV>
+__device__ __forceinline__ uint32_t nearest_symbol_bits(float x) {
+    if constexpr (KV == kBF16) return nearest_bf16(x);
+    else return nearest_e4m3(x);
+}
+
+// Hot window of the escape prefix in LDS: for magnitude patterns m_lo ..
+// m_lo + kHotHalf - 1 of both signs, P-hat at the symbol and its successor,
+// so that a cell in the window takes its escape terms from one LDS read
+// instead of a gather over the 256 KB prefix.  Layout (kHotHalf + 1 entries
+// per sign): hot[i] = P-hat[0x8000 - m_lo - kHotHalf + i] (negative values,
+// i = 0 .. kHotHalf), hot[kHotHalf + 1 + i] = P-hat[0x8000 + m_lo + i].  The
+// window start maximises the marginal mass it holds (k_hot_window).
+constexpr uint32_t kHotHalf = 2048;
+constexpr int kHotEntries = 2 * (kHotHalf + 1);
+
+__device__ __forceinline__ void build_hot_lds(uint32_t* s_hot, const uint32_t* __restrict__ prefix, uint32_t m_lo) {
+    for (uint32_t i = threadIdx.x; i <= kHotHalf; i += blockDim.x) {
+        s_hot[i] = prefix[0x8000u - m_lo - kHotHalf + i];
+        s_hot[kHotHalf + 1u + i] = prefix[0x8000u + m_lo + i];
+    }
+}
+
+// A candidate symbol with its exact CDF terms: G at both cell edges, and
+// the escape prefix at s and s + 1.
+struct Cell {
+    uint32_t s, g0, g1, p0, p1;
+};
+
+// Cell of the bf16 pattern kb.  The outer edge (away from zero) is the
+// pattern's magnitude plus half a step, the inner edge the magnitude minus
+// half a step (0 for +-0).  With a bf16 mean the +-max cells may keep
+// their finite outer edge (the mean lies at least half a step inside it, so
+// z saturates at +-24 as for an infinite edge, sigma <= 2^96); with an fp32
+// mean it becomes infinite, as the format defines.  Inf and NaN patterns
+// reach here only from the escape lookup, and their G terms are replaced
+// by the caller (every edge of theirs is infinite).
+// The escape terms come from the hot window when `hot` is given and the
+// magnitude lies in it (`inside` tells; the caller reads the prefix for
+// lanes outside), else from the prefix in global memory.
 template <int MU>
-__device__ __forceinline__ float edge_pattern(uint32_t mag, uint32_t sign) {
-    if constexpr (MU == kBF16) mag = mag < 0x7F800000u ? mag : 0x7F800000u;
-    else mag = mag < kBf16OuterMag ? mag : 0x7F800000u;
-    return __uint_as_float(mag | sign);
+__device__ __forceinline__ Cell eval_bf16(uint32_t kb, float mu, float inv24, const Model& m,
+                                          const uint32_t* hot = nullptr, uint32_t m_lo = 0, bool* inside = nullptr) {
+    const uint32_t kbs = kb << 16;
+    const uint32_t sign = kbs & 0x80000000u;
+    uint32_t ob = kbs | 0x8000u;
+    const uint32_t ib = __builtin_elementwise_max(__builtin_elementwise_sub_sat(ob, 0x10000u), sign);
+    if constexpr (MU == kF32) ob = (kbs & 0x7FFFFFFFu) == 0x7F7F0000u ? (sign | 0x7F800000u) : ob;
+    const uint32_t ha = h_fx(z_fixed(__uint_as_float(ib), mu, inv24), m.tab);
+    const uint32_t hb = h_fx(z_fixed(__uint_as_float(ob), mu, inv24), m.tab);
+    Cell c;
+    c.g0 = __builtin_elementwise_min(ha, hb);
+    c.g1 = __builtin_elementwise_max(ha, hb);
+    // ordered index: 0x8000 + m for a positive pattern, 0x7FFF - m for a negative one
+    const uint32_t neg = static_cast<uint32_t>(static_cast<int32_t>(kbs) >> 31);
+    const uint32_t mag = kb & 0x7FFFu;
+    c.s = (mag ^ neg) + 0x8000u;
+    if (hot) {
+        // negative: P-hat[s] at kHotHalf - 1 - d; positive: at kHotHalf + 1 + d
+        const uint32_t d = mag - m_lo;
+        *inside = d < kHotHalf;
+        const uint32_t dc = __builtin_elementwise_min(d, kHotHalf - 1u);
+        const uint32_t* h = hot + ((dc ^ neg) + neg + (kHotHalf + 1u));
+        c.p0 = h[0];
+        c.p1 = h[1];
+    } else {
+        prefix_pair(m, c.s, c.p0, c.p1);
+    }
+    return c;
 }
 
-// Position of bf16 edge b (any b in 0..N) through edge_pattern: magnitude
-// |b - 32768| * 2^16 - 2^15 (0 for the edge between -0 and +0), negative
-// below b = 32768; beyond the outer edges the pattern is pinned to Inf.
+// Cell of the e4m3 pattern kb: edges and prefix from the LDS copies.
+__device__ __forceinline__ Cell eval_e4m3(uint32_t kb, float mu, float inv24, const Model& m) {
+    Cell c;
+    c.s = order_of_bits<kE4M3>(kb);
+    c.g0 = h_fx(z_fixed(e4_edge(m.small, c.s), mu, inv24), m.tab);
+    c.g1 = h_fx(z_fixed(e4_edge(m.small, c.s + 1u), mu, inv24), m.tab);
+    c.p0 = m.small[c.s];
+    c.p1 = m.small[c.s + 1u];
+    return c;
+}
+
+template <int KV, int MU>
+__device__ __forceinline__ Cell eval_cell(uint32_t kb, float mu, float inv24, const Model& m) {
+    if constexpr (KV == kBF16) return eval_bf16<MU>(kb, mu, inv24, m);
+    else return eval_e4m3(kb, mu, inv24, m);
+}
+
+// bf16 edge b (any b in 0..N) as a position: magnitude |b - 32768| * 2^16 -
+// 2^15 (0 for the edge between -0 and +0), negative below b = 32768; at
+// and beyond the outer edges of -max / +max the position is infinite for
+// an fp32 mean; a bf16 mean may keep the finite outer edge (see eval_bf16),
+// beyond which the pattern is pinned to Inf.
 template <int MU>
 __device__ __forceinline__ float edge_from_index_bf16(uint32_t b) {
     const uint32_t a = b >= 32768u ? b - 32768u : 32768u - b;
-    const uint32_t mag = __builtin_elementwise_sub_sat(a << 16, 0x8000u);    // a <= 32768
-    return edge_pattern<MU>(mag, b < 32768u ? 0x80000000u : 0u);
+    uint32_t mag = __builtin_elementwise_sub_sat(a << 16, 0x8000u);    // a <= 32768
+    if constexpr (MU == kBF16) mag = mag < 0x7F800000u ? mag : 0x7F800000u;
+    else mag = mag < 0x7F7F8000u ? mag : 0x7F800000u;
+    return __uint_as_float(mag | (b < 32768u ? 0x80000000u : 0u));
 }
 
 // G(b), the mixture-table term of the CDF at edge b, for the
@@ -613,15 +692,16 @@ __device__ __forceinline__ uint32_t geo_offset(int lane) {
     return o > static_cast<uint32_t>(lane + 1) ? o : static_cast<uint32_t>(lane + 1);
 }
 
-// Gaussian-range slot not bracketed by the aim: the whole wave resolves
+// Gaussian-range slot the aim did not bracket: the whole wave resolves
 // every lane with `need` set, one lane at a time.  [lo, hi) brackets the
 // lane's symbol with G(lo) = glo <= target < G(hi) = ghi; `up` tells which
-// end is the known near one (lo if up).  Returns s, G(s), G(s+1) - G(s).
+// end is the known near one (lo if up).  Returns s.
 template <int KV, int MU>
-__device__ __forceinline__ void coop_gauss(bool need, uint32_t target, float mu, float inv24, bool up, uint32_t lo,
-                                           uint32_t hi, uint32_t glo, uint32_t ghi, const Model& m, uint32_t geo,
-                                           uint32_t& s_out, uint32_t& g0_out, uint32_t& fg_out) {
+__device__ __forceinline__ uint32_t coop_gauss(bool need, uint32_t target, float mu, float inv24, bool up, uint32_t lo,
+                                               uint32_t hi, uint32_t glo, uint32_t ghi, const Model& m, uint32_t geo,
+                                               uint32_t s_in) {
     const int lane = threadIdx.x & 63;
+    uint32_t s_out = s_in;
     uint64_t pend = __ballot(need);
     while (pend) {
         const int L = __builtin_ctzll(pend);
@@ -663,66 +743,64 @@ __device__ __forceinline__ void coop_gauss(bool need, uint32_t target, float mu,
             }
             first = false;
         }
-        if (lane == L) {
-            s_out = a;
-            g0_out = ga;
-            fg_out = gb - ga;
-        }
+        (void)ga;
+        (void)gb;
+        if (lane == L) s_out = a;
     }
+    return s_out;
 }
 
-// Floor-and-escape slot y: the symbol s with Q(s) <= y < Q(s+1), Q(b) = b +
-// prefix[b], which does not depend on the lane's model.  The whole wave
-// looks each such lane up: bf16 in three ballot rounds (every 16th entry of
-// the every-64th-entry LDS copy, then the 16 entries after the match, then
-// the 64 exact entries of that segment, one contiguous read); e4m3 in two
-// rounds over the exact LDS copy.  Returns s, Q(s), Q(s+1) - Q(s).  Lane 0
-// always matches for a valid prefix (Q(0) = 0 <= y); it is counted as a
-// match regardless, so a damaged prefix still keeps every index in range
-// (the decode then fails its checks).
+// Bucket table of the static part Q(b) = b + prefix[b] of the CDF:
+// bucket[j] = the largest s < N with Q(s) <= j * 2^shift.  A slot y in the
+// floor-and-escape range then has its symbol in [bucket[y >> shift],
+// bucket[(y >> shift) + 1]].  The shift is the smallest that keeps the
+// table within kEscapeBucketsMax entries.
+__global__ void __launch_bounds__(256) k_escape_buckets(const uint32_t* __restrict__ prefix, uint32_t n_sym,
+                                                        uint32_t shift, uint32_t n_entries,
+                                                        uint16_t* __restrict__ bucket) {
+    const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= n_entries) return;
+    const unsigned long long y = static_cast<unsigned long long>(j) << shift;
+    uint32_t lo = 0, hi = n_sym - 1;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1u) >> 1;
+        if (static_cast<unsigned long long>(mid) + prefix[mid] <= y) lo = mid;
+        else hi = mid - 1u;
+    }
+    bucket[j] = static_cast<uint16_t>(lo);
+}
+
+hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_t shift, uint32_t n_entries,
+                                 uint16_t* bucket, hipStream_t s) {
+    hipLaunchKernelGGL(k_escape_buckets, dim3((n_entries + 255) / 256), dim3(256), 0, s, prefix, n_sym, shift,
+                       n_entries, bucket);
+    return hipGetLastError();
+}
+
+// Symbol of the floor-and-escape slot y for every lane with `need` set:
+// the bucket table narrows it to [lo, hi], a per-lane binary search over
+// Q(b) = b + prefix[b] finishes it.  Indices stay in [0, N) whatever the
+// prefix holds.
 template <int KV>
-__device__ __forceinline__ void escape_search(bool need, uint32_t y, const uint32_t* s_pc,
-                                              const uint32_t* __restrict__ prefix, uint32_t& s_out,
-                                              uint32_t& q_out, uint32_t& fq_out) {
-    const uint32_t lane = threadIdx.x & 63u;
-    uint64_t pend = __ballot(need);
-    while (pend) {
-        const int L = __builtin_ctzll(pend);
-        pend &= pend - 1;
-        const uint32_t yl = __builtin_amdgcn_readlane(y, L);
-        uint32_t sv, q0, q1;
-        if constexpr (KV == kBF16) {
-            // Qc(j) = Q(64 j) = 64 j + s_pc[j], j = 0 .. 1024; Qc(0) = 0 <= y < Qc(1024)
-            uint32_t j = 16u * lane;                                        // 0 .. 1008
-            uint64_t le = __ballot(64u * j + s_pc[j] <= yl);
-            const uint32_t k = 63u - __builtin_clzll(le | 1ull);
-            j = 16u * k + (lane & 15u);                                     // <= 1023
-            le = __ballot(lane < 16u && 64u * j + s_pc[j] <= yl);
-            const uint32_t jj = 16u * k + (63u - __builtin_clzll(le | 1ull));
-            const uint32_t b = 64u * jj + lane;                            // <= 65535
-            const uint32_t qb = b + prefix[b];
-            le = __ballot(qb <= yl);
-            const uint32_t kk = 63u - __builtin_clzll(le | 1ull);
-            sv = 64u * jj + kk;
-            q0 = __builtin_amdgcn_readlane(qb, kk);
-            q1 = kk < 63u ? __builtin_amdgcn_readlane(qb, kk + 1u) : 64u * (jj + 1u) + s_pc[jj + 1u];
-        } else {
-            // s_pc[b] = prefix[b], b = 0 .. 256
-            uint32_t b = 4u * lane;                                         // 0 .. 252
-            uint64_t le = __ballot(b + s_pc[b] <= yl);
-            const uint32_t k = 63u - __builtin_clzll(le | 1ull);
-            b = 4u * k + (lane & 3u);                                       // <= 255
-            le = __ballot(lane < 4u && b + s_pc[b] <= yl);
-            sv = 4u * k + (63u - __builtin_clzll(le | 1ull));
-            q0 = sv + s_pc[sv];
-            q1 = sv + 1u + s_pc[sv + 1u];
-        }
-        if (lane == static_cast<uint32_t>(L)) {
-            s_out = sv;
-            q_out = q0;
-            fq_out = q1 - q0;
+__device__ __forceinline__ uint32_t escape_symbol(bool need, uint32_t y, __amdgpu_buffer_rsrc_t bucket,
+                                                  uint32_t shift, const Model& m) {
+    uint32_t lo = 0, hi = 0;
+    if (need) {
+        const uint32_t j = y >> shift;
+        lo = __builtin_amdgcn_raw_buffer_load_b16(bucket, j << 1, 0, 0);
+        hi = __builtin_amdgcn_raw_buffer_load_b16(bucket, (j << 1) + 2u, 0, 0);
+    }
+    while (__ballot(lo < hi)) {
+        if (lo < hi) {
+            const uint32_t mid = (lo + hi + 1u) >> 1;
+            uint32_t pm;
+            if constexpr (KV == kBF16) pm = __builtin_amdgcn_raw_buffer_load_b32(m.pre, mid << 2, 0, 0);
+            else pm = m.small[mid];
+            if (mid + pm <= y) lo = mid;
+            else hi = mid - 1u;
         }
     }
+    return lo;
 }
 
 // Stream words of a chunk, staged through a per-wave LDS ring of two
@@ -730,10 +808,11 @@ __device__ __forceinline__ void escape_search(bool need, uint32_t y, const uint3
 // dword per lane) as soon as a block is entered and written to the ring
 // when the one before it is left, so no global read sits on the serial
 // decode chain; a refill read is one LDS access.
+constexpr int kRingDwords = 128;
 struct WordRing {
     const uint32_t* __restrict__ dw;   // chunk words as dwords (8-byte aligned)
     uint32_t n_dw;                     // dwords in the chunk's word area
-    uint32_t* ring;                    // this wave's 128 dwords of LDS
+    uint32_t* ring;                    // this wave's kRingDwords dwords of LDS
     uint32_t base;                     // first word of the block being read
     uint32_t ahead;                    // this lane's dword of block base/128 + 2
 
@@ -761,37 +840,51 @@ struct WordRing {
     }
 };
 
-// Every 64th escape-prefix entry in LDS, for the lookup of floor-and-escape
-// slots (e4m3 keeps its whole prefix there instead).
-constexpr int kCoarseEntries = 1026;             // 65536 / 64 + 1, plus one repeat
-
-template <int KV>
-struct Coarse {
-    static constexpr int kShift = KV == kBF16 ? 6 : 0;
-    static constexpr uint32_t kLast = Alphabet<KV>::kSize >> kShift;     // index of the entry for b = N
-};
-
-template <int KV>
-__device__ __forceinline__ void build_coarse_lds(uint32_t* s_pc, const uint32_t* __restrict__ prefix) {
-    constexpr uint32_t last = Coarse<KV>::kLast;
-    for (uint32_t j = threadIdx.x; j <= last + 1u; j += blockDim.x) {
-        const uint32_t jj = j > last ? last : j;
-        s_pc[j] = prefix[jj << Coarse<KV>::kShift];
+// Window start: the m_lo in [0, 0x8000 - kHotHalf] whose window holds the
+// most escape mass (ties to the smallest), from prefix differences.  One
+// workgroup.
+__global__ void __launch_bounds__(1024) k_hot_window(const uint32_t* __restrict__ prefix, uint32_t* __restrict__ out) {
+    __shared__ unsigned long long s_best[16];
+    constexpr uint32_t last = 0x8000u - kHotHalf;
+    unsigned long long best = 0;                  // mass << 32 | (0xFFFFFFFF - m_lo): max picks the smallest m_lo
+    for (uint32_t c = threadIdx.x; c <= last; c += blockDim.x) {
+        const uint32_t mass = (prefix[0x8000u + c + kHotHalf] - prefix[0x8000u + c]) +
+                              (prefix[0x8000u - c] - prefix[0x8000u - c - kHotHalf]);
+        const unsigned long long key = (static_cast<unsigned long long>(mass) << 32) | (0xFFFFFFFFu - c);
+        best = key > best ? key : best;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        const unsigned long long o = __shfl_xor(best, off, 64);
+        best = o > best ? o : best;
+    }
+    if ((threadIdx.x & 63) == 0) s_best[threadIdx.x >> 6] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 16; ++w) best = s_best[w] > best ? s_best[w] : best;
+        best = s_best[0] > best ? s_best[0] : best;
+        const uint32_t c = 0xFFFFFFFFu - static_cast<uint32_t>(best);
+        out[0] = c <= last ? c : 0u;
     }
 }
 
+hipError_t launch_hot_window(const uint32_t* prefix, uint32_t* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_hot_window, dim3(1), dim3(1024), 0, s, prefix, out);
+    return hipGetLastError();
+}
+
 template <int KV, int MU>
-__global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
+__global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(64))) k_decode(DecodeArgs a) {
     __shared__ uint32_t s_tab[kTableEntries];
-    __shared__ float s_zinv[kZinvSteps + 2];
-    __shared__ uint32_t s_ring[kDecodeBlock / 64][128];
-    __shared__ uint32_t s_pc[kCoarseEntries];
-    static_assert(kE4Words <= kCoarseEntries, "e4m3 tables share the coarse-prefix array");
-    if constexpr (KV == kE4M3) build_e4_lds(s_pc, a.prefix);      // exact prefix + edges
-    else build_coarse_lds<KV>(s_pc, a.prefix);
+    __shared__ float2 s_aim[kAimEntries];
+    __shared__ uint32_t s_ring[kDecodeBlock / 64][kRingDwords];
+    __shared__ uint32_t s_small[KV == kE4M3 ? kE4Words : 1];
+    __shared__ uint32_t s_hot[KV == kBF16 ? kHotEntries : 1];
+    const uint32_t m_lo = KV == kBF16 ? __builtin_elementwise_min(a.hot_lo[0], 0x8000u - kHotHalf) : 0u;
+    if constexpr (KV == kE4M3) build_e4_lds(s_small, a.prefix);      // exact prefix + edges
+    else build_hot_lds(s_hot, a.prefix, m_lo);
     build_table_lds(s_tab, a.phi, a.tn, a.tw);
     const uint32_t htot = a.tn + a.tw;
-    build_zinv_lds(s_zinv, s_tab, htot);              // all z = 24 when htot = 0
+    build_aim_lds(s_aim, s_tab);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -826,135 +919,163 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
         inv24 = 16777216.0f;
         sg = 1.0f;
     }
-    const Model m{s_tab, a.prefix, s_pc};
-    const Aim aim{s_zinv, htot ? static_cast<float>(kZinvSteps) / static_cast<float>(htot) : 0.0f};
+    constexpr uint32_t kN = Alphabet<KV>::kSize;
+    const Model m{s_tab, a.prefix, s_small, buffer_rsrc(a.prefix, (kN + 1u) * 4u)};
     const uint32_t geo = geo_offset(lane);
+    // without an escape part the prefix (and so the window) is all zero
+    const uint64_t has_escape = a.te ? ~0ull : 0ull;
+    const __amdgpu_buffer_rsrc_t bucket = buffer_rsrc(a.buckets, kEscapeBucketsMax * 2u);
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
+    // this chunk's rows of mu and of the output as buffers: lane offset in a
+    // vector register, row offset in a scalar one
     const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * static_cast<int64_t>(D) + cp.k * 64;
-    KB* __restrict__ outp = static_cast<KB*>(a.kv_out) + row0;
-    const MT* __restrict__ mup = static_cast<const MT*>(a.mu) + row0;
+    const uint32_t rows_bytes = cp.len * D * static_cast<uint32_t>(sizeof(MT));
+    const __amdgpu_buffer_rsrc_t mub = buffer_rsrc(static_cast<const MT*>(a.mu) + row0, rows_bytes);
+    const __amdgpu_buffer_rsrc_t outb =
+        buffer_rsrc(static_cast<KB*>(a.kv_out) + row0, cp.len * D * static_cast<uint32_t>(sizeof(KB)));
+    const uint32_t mu_lane = static_cast<uint32_t>(lane) * static_cast<uint32_t>(sizeof(MT));
+    const uint32_t kv_lane = static_cast<uint32_t>(lane) * static_cast<uint32_t>(sizeof(KB));
 
-    uint32_t rp = 0, misses = 0;
-    for (uint32_t t0 = 0; t0 < cp.len; t0 += kDecodeBatch) {
-        // model side of the batch: predictor means
-        float mus[kDecodeBatch];
-        MT raw[kDecodeBatch];
-#pragma unroll
-        for (int u = 0; u < kDecodeBatch; ++u) {
-            const uint32_t t = t0 + u < cp.len ? t0 + u : cp.len - 1;
-            raw[u] = row_elem(mup + static_cast<uint64_t>(t) * D, static_cast<uint32_t>(lane));
+    uint32_t rp = 0;
+    unsigned long long misses = 0;                   // wave-uniform
+
+    // One symbol of every lane: row t of the chunk, predictor mean mu.
+    auto step = [&](uint32_t t, float mu) {
+        const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
+        // candidate: the cell the aim lands in, with its exact CDF terms
+        uint32_t kb = nearest_symbol_bits<KV>(__fmaf_rn(aim_z(target, htot, s_aim), sg, mu));
+        Cell c;
+        uint64_t far = 0;
+        if constexpr (KV == kBF16) {
+            bool inside;
+            c = eval_bf16<MU>(kb, mu, inv24, m, s_hot, m_lo, &inside);
+            far = __ballot(!inside) & has_escape;
+        } else {
+            c = eval_cell<KV, MU>(kb, mu, inv24, m);
         }
-#pragma unroll
-        for (int u = 0; u < kDecodeBatch; ++u) mus[u] = mu_value<MU>(raw[u]);
-#pragma unroll
-        for (int u = 0; u < kDecodeBatch; ++u) {
-            if (t0 + u >= cp.len) break;                 // wave-uniform
-            const float mu = mus[u];
-            const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
-            const bool in_g = target < htot;             // a Gaussian slot
-            // Gaussian slots: aim through the inverse table, check the nearest
-            // edge and one neighbour.  Floor-and-escape slots: look the symbol
-            // up (it does not depend on the model) and evaluate its two edges.
-            uint32_t E, qe = 0, fqe = 0;
-            uint32_t mag = 0, sgn = 0;                   // bf16: E's edge as magnitude pattern and sign
-            if constexpr (KV == kBF16) {
-                const Bf16Edge ed = nearest_edge_bf16(aim_pos(static_cast<int32_t>(target), mu, sg, aim));
-                E = ed.e;
-                mag = ed.mag;
-                sgn = ed.sign;
-            } else {
-                E = nearest_edge_e4m3(aim_pos(static_cast<int32_t>(target), mu, sg, aim));
+        const uint64_t esc = __ballot(target >= htot);
+        uint64_t need = (__ballot(target < c.g0) | __ballot(target >= c.g1)) & ~esc;
+        if (esc | need | far) {
+            if (far) {
+                // cells outside the hot window: escape terms from the prefix
+                if ((far >> lane) & 1ull) prefix_pair(m, c.s, c.p0, c.p1);
             }
-            if (__ballot(!in_g)) {
-                uint32_t se = 0;
-                escape_search<KV>(!in_g, target - htot, s_pc, m.prefix, se, qe, fqe);
-                if (!in_g) {
-                    E = se;
+            if (esc) {
+                // floor-and-escape slots: look the symbol up; its rank is
+                // f_G(s) + (y - Q(s)), so its slots are taken to start at
+                // T_n + T_w + Q(s) - f_G(s) (G terms of Inf and NaN, whose
+                // edges are all infinite, set first)
+                misses += __popcll(esc);
+                const bool e = target >= htot;
+                const uint32_t se = escape_symbol<KV>(e, target - htot, bucket, a.bucket_shift, m);
+                if (e) {
+                    kb = bits_of_order<KV>(se);
+                    c = eval_cell<KV, MU>(kb, mu, inv24, m);
                     if constexpr (KV == kBF16) {
-                        const uint32_t ad = se >= 32768u ? se - 32768u : 32768u - se;
-                        mag = __builtin_elementwise_sub_sat(ad << 16, 0x8000u);     // 0 for the edge 0
-                        sgn = se < 32768u ? 0x80000000u : 0u;
+                        if ((kb & 0x7FFFu) >= 0x7F80u) c.g0 = c.g1 = (kb & 0x8000u) ? 0u : htot;
+                    }
+                    const uint32_t fg = c.g1 - c.g0;
+                    c.g0 = htot + c.s + c.p0 - fg;
+                    c.g1 = c.g0 + fg;
+                }
+            }
+            if (need) {
+                // Gaussian slots outside the aimed cell: one symbol towards
+                // the target first (G(0) = 0 <= target < G(N) = htot), then
+                // the wave-cooperative search
+                misses += __popcll(need);
+                bool hit = ((need >> lane) & 1ull) == 0ull;
+                if (!hit) {
+                    kb = bits_of_order<KV>(target < c.g0 ? c.s - 1u : c.s + 1u);
+                    c = eval_cell<KV, MU>(kb, mu, inv24, m);
+                    hit = target >= c.g0 && target < c.g1;
+                }
+                need = __ballot(!hit);
+                if (need) {
+                    const bool up = target >= c.g1;
+                    const uint32_t sym = coop_gauss<KV, MU>(!hit, target, mu, inv24, up, up ? c.s + 1u : 0u,
+                                                            up ? kN : c.s, up ? c.g1 : 0u, up ? htot : c.g0, m, geo,
+                                                            c.s);
+                    if (!hit) {
+                        kb = bits_of_order<KV>(sym);
+                        c = eval_cell<KV, MU>(kb, mu, inv24, m);
                     }
                 }
-                misses += in_g ? 0u : 1u;
             }
-            uint32_t gE, gE2, E2, p0, p1, p2;
-            bool up;
-            if constexpr (KV == kBF16) {
-                // prefix at E-1, E, E+1 (one 12-byte read; escape lanes use
-                // their lookup instead, so their base is only kept in range)
-                const uint32_t pb = E - 1u < 65535u ? E - 1u : 0u;          // reads pb .. pb + 2 <= N
-                const uint32_t* pp = m.prefix + pb;
-                p0 = pp[0];
-                p1 = pp[1];
-                p2 = pp[2];
-                gE = h_fx(z_fixed(edge_pattern<MU>(mag, sgn), mu, inv24), m.tab);
-                up = !in_g || target >= gE;
-                // the neighbour one step away from zero (up on the positive
-                // side) or towards it; away from the edge 0 is 2^15
-                const bool outward = up != (sgn != 0u);
-                const uint32_t mag2 = outward ? ((mag + 0x8000u) | 0x8000u) : __builtin_elementwise_sub_sat(mag, 0x10000u);
-                E2 = up ? E + 1u : E - 1u;
-                gE2 = h_fx(z_fixed(edge_pattern<MU>(mag2, sgn), mu, inv24), m.tab);
-            } else {
-                const uint32_t pb = E - 1u < 255u ? E - 1u : 0u;            // reads pb .. pb + 2 <= N
-                p0 = s_pc[pb];
-                p1 = s_pc[pb + 1u];
-                p2 = s_pc[pb + 2u];
-                gE = h_fx(z_fixed(e4_edge(s_pc, E), mu, inv24), m.tab);
-                up = !in_g || target >= gE;
-                E2 = up ? E + 1u : E - 1u;
-                gE2 = h_fx(z_fixed(e4_edge(s_pc, E2), mu, inv24), m.tab);
-            }
-            uint32_t sym = up ? E : E2;
-            uint32_t g0 = up ? gE : gE2;
-            uint32_t fg = up ? gE2 - gE : gE - gE2;
-            uint32_t qs = in_g ? sym + (up ? p1 : p0) : qe;              // Q(s)
-            uint32_t fq = in_g ? 1u + (up ? p2 - p1 : p1 - p0) : fqe;    // Q(s+1) - Q(s)
-            // bracketed: target < G(E+1) going up, target >= G(E-1) going down
-            const bool need = in_g && ((target < gE2) != up);
-            if (__ballot(need)) {
-                misses += need ? 1u : 0u;
-                coop_gauss<KV, MU>(need, target, mu, inv24, up, up ? E2 : 0u, up ? Alphabet<KV>::kSize : E2,
-                                   up ? gE2 : 0u, up ? htot : gE2, m, geo, sym, g0, fg);
-                if (need) {
-                    const uint32_t* pq = KV == kBF16 ? m.prefix : s_pc;
-                    const uint32_t a0 = pq[sym], a1 = pq[sym + 1u];
-                    qs = sym + a0;
-                    fq = 1u + (a1 - a0);
-                }
-            }
-            // rank within the symbol's f = fg + fq slots
-            const uint32_t f = fg + fq;
-            const uint32_t r = in_g ? target - g0 : fg + (target - htot - qs);
-            // x < 2^63, so x >> 31 fits 32 bits: one 32 x 32 -> 64 multiply-add
-            x = static_cast<unsigned long long>(f) * static_cast<uint32_t>(x >> kLog2M) + r;
-
-            // refill: a lane takes one word when x < 2^47 and a second one
-            // when x < 2^31 (then x << 16 is still below 2^47); round one
-            // holds one word per taking lane in lane order, round two the
-            // second words, so both reads are placed before either is used
-            const uint32_t xh = static_cast<uint32_t>(x >> 32), xl = static_cast<uint32_t>(x);
-            const bool take1 = xh < kLHi;
-            const bool take2 = xh == 0u && xl < 0x80000000u;
-            const uint64_t m1 = __ballot(take1), m2 = __ballot(take2);
-            const uint32_t n1 = __popcll(m1);
-            const uint32_t w1 = win.word(rp + lane_rank(m1));
-            const uint32_t w2 = win.word(rp + n1 + lane_rank(m2));
-            const uint32_t hi1 = __builtin_amdgcn_alignbit(xh, xl, 16);     // (x << 16) >> 32
-            const uint32_t lo1 = (xl << 16) | w1;
-            const uint32_t lo2 = (w1 << 16) | w2;
-            const uint32_t nh = take2 ? xl : (take1 ? hi1 : xh);
-            const uint32_t nl = take2 ? lo2 : (take1 ? lo1 : xl);
-            x = (static_cast<unsigned long long>(nh) << 32) | nl;
-            rp += n1 + __popcll(m2);
-            win.advance(rp, static_cast<uint32_t>(lane));
-            KB* orow = outp + static_cast<uint64_t>(t0 + u) * D;
-            *reinterpret_cast<KB*>(reinterpret_cast<char*>(orow) + static_cast<uint32_t>(lane) * sizeof(KB)) =
-                static_cast<KB>(bits_of_order<KV>(sym));
         }
+        // x = f (x >> 31) + rank, f = f_G + 1 + (prefix[s + 1] - prefix[s]);
+        // x < 2^63, so x >> 31 fits 32 bits
+        const uint32_t f = (c.g1 - c.g0) + 1u + (c.p1 - c.p0);
+        x = static_cast<unsigned long long>(f) * static_cast<uint32_t>(x >> kLog2M) + (target - c.g0);
+
+        // refill: a lane takes one word when x < 2^47 and a second one when
+        // it is still below 2^47 after that (x < 2^31 before); round one
+        // holds one word per taking lane in lane order, round two the second
+        // words
+        uint32_t xh = static_cast<uint32_t>(x >> 32), xl = static_cast<uint32_t>(x);
+        const bool take1 = xh < kLHi;
+        const uint64_t m1 = __ballot(take1);
+        const uint32_t w1 = win.word(rp + lane_rank(m1));
+        const uint32_t sh = __builtin_amdgcn_alignbit(xh, xl, 16);
+        xl = take1 ? (xl << 16) | w1 : xl;
+        xh = take1 ? sh : xh;
+        rp += __popcll(m1);
+        const uint64_t m2 = __ballot(xh < kLHi);
+        if (m2) {
+            const bool take2 = xh < kLHi;
+            const uint32_t w2 = win.word(rp + lane_rank(m2));
+            const uint32_t sh2 = __builtin_amdgcn_alignbit(xh, xl, 16);
+            xl = take2 ? (xl << 16) | w2 : xl;
+            xh = take2 ? sh2 : xh;
+            rp += __popcll(m2);
+        }
+        x = (static_cast<unsigned long long>(xh) << 32) | xl;
+        win.advance(rp, static_cast<uint32_t>(lane));
+        const uint32_t ooff = t * D * static_cast<uint32_t>(sizeof(KB));
+        if constexpr (KV == kBF16) __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(kb), outb, kv_lane, ooff, 0);
+        else __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(kb), outb, kv_lane, ooff, 0);
+    };
+    // predictor-mean rows as raw bits (the last row stands in for rows past
+    // the chunk's end, which are not decoded; the buffer does not
+    // range-check the row offset)
+    using MRaw = typename std::conditional<MU == kBF16, uint16_t, uint32_t>::type;
+    auto load_mu = [&](uint32_t t) -> MRaw {
+        const uint32_t roff = (t < cp.len ? t : cp.len - 1) * D * static_cast<uint32_t>(sizeof(MT));
+        if constexpr (MU == kBF16) return __builtin_amdgcn_raw_buffer_load_b16(mub, mu_lane, roff, 0);
+        else return __builtin_amdgcn_raw_buffer_load_b32(mub, mu_lane, roff, 0);
+    };
+    auto mu_of = [](MRaw r) -> float {
+        return MU == kBF16 ? __uint_as_float(static_cast<uint32_t>(r) << 16) : __uint_as_float(static_cast<uint32_t>(r));
+    };
+
+    // full batches: the means of the next batch are loaded while this one
+    // decodes, so no HBM read sits on the serial chain; a non-finite mean
+    // counts as 0
+    const uint32_t full = cp.len - cp.len % kDecodeBatch;
+    MRaw nxt[kDecodeBatch];
+#pragma unroll
+    for (int u = 0; u < kDecodeBatch; ++u) nxt[u] = load_mu(u);
+    for (uint32_t t0 = 0; t0 < full; t0 += kDecodeBatch) {
+        float mus[kDecodeBatch];
+#pragma unroll
+        for (int u = 0; u < kDecodeBatch; ++u) mus[u] = mu_of(nxt[u]);
+#pragma unroll
+        for (int u = 0; u < kDecodeBatch; ++u) nxt[u] = load_mu(t0 + kDecodeBatch + u);
+        uint64_t odd = 0;
+#pragma unroll
+        for (int u = 0; u < kDecodeBatch; ++u) odd |= __ballot(!__builtin_isfinite(mus[u]));
+        if (odd) {
+#pragma unroll
+            for (int u = 0; u < kDecodeBatch; ++u) mus[u] = __builtin_isfinite(mus[u]) ? mus[u] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kDecodeBatch; ++u) step(t0 + u, mus[u]);
+    }
+    for (uint32_t t = full; t < cp.len; ++t) {
+        const float mu = mu_of(load_mu(t));
+        step(t, __builtin_isfinite(mu) ? mu : 0.0f);
     }
     // every lane back at the initial state, the payload consumed exactly,
     // the padding zero
@@ -965,8 +1086,7 @@ __global__ void __launch_bounds__(kDecodeBlock) k_decode(DecodeArgs a) {
         if (static_cast<uint32_t>(lane) < pad_words && words[rp + lane] != 0) bad = true;
     }
     if (__ballot(bad) && lane == 0) atomicOr(&a.ctl->flags, kFlagCorrupt);
-    const unsigned long long mw = wave_sum_u64(misses);
-    if (lane == 0 && mw) atomicAdd(&a.ctl->misses, mw);
+    if (lane == 0 && misses) atomicAdd(&a.ctl->misses, misses);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s) {
@@ -1206,7 +1326,7 @@ __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
     using MT = typename MuT<MU>::T;
     const KB* __restrict__ kv = static_cast<const KB*>(a.kv);
     const MT* __restrict__ mup = static_cast<const MT*>(a.mu);
-    const Model model{s_tab, a.prefix};
+    const Model model{s_tab, a.prefix, nullptr, buffer_rsrc(a.prefix, (Alphabet<KV>::kSize + 1u) * 4u)};
     const int64_t D = a.geom.channels, T = a.geom.tokens;
     const int64_t n = a.geom.planes * T * D;
     const double wn = a.w_narrow_bp / 1e4, ww = a.w_wide_bp / 1e4, we = 1.0 - wn - ww;
@@ -1264,7 +1384,7 @@ __global__ void __launch_bounds__(256) k_cdf_table(const void* mu_, const float*
     build_table_lds(s_tab, phi, tn, tw);
     using MT = typename MuT<MU>::T;
     constexpr uint32_t N1 = Alphabet<KV>::kSize + 1;
-    const Model model{s_tab, prefix};
+    const Model model{s_tab, prefix, nullptr, buffer_rsrc(prefix, (Alphabet<KV>::kSize + 1u) * 4u)};
     const int64_t total = pairs * N1;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {

@@ -54,7 +54,7 @@ typedef enum kvc_status {
 enum { KVC_BF16 = 0, KVC_E4M3 = 1, KVC_F32 = 2 };   /* E4M3 = OCP float8 e4m3fn */
 
 #define KVC_HEADER_BYTES 128
-#define KVC_DECODE_WORKSPACE_BYTES 256
+#define KVC_DECODE_WORKSPACE_BYTES 131584   /* control block + escape bucket table */
 #define KVC_ESTIMATE_WORKSPACE_BYTES 256
 #define KVC_ENCODE_STAGES 4
 #define KVC_DECODE_STAGES 2
@@ -66,13 +66,15 @@ typedef struct kvc_encode_info {
 } kvc_encode_info;
 
 typedef struct kvc_decode_info {
-    float stage_ms[KVC_DECODE_STAGES];  /* GPU time of: side-information checksum,
-                                           decoding kernel                        */
+    float stage_ms[KVC_DECODE_STAGES];  /* GPU time of: side-information checksum
+                                           and escape bucket table, decoding
+                                           kernel                                 */
     uint32_t reserved;
     uint64_t fallback_symbols;          /* symbols not found by the aim: slots in
                                            the floor-and-escape range (looked up
-                                           by the wave) plus Gaussian slots the
-                                           aim missed (searched by the wave)      */
+                                           through the bucket table) plus
+                                           Gaussian slots whose aimed cell did not
+                                           hold the target                        */
 } kvc_decode_info;
 
 typedef struct kvc_params {
@@ -85,7 +87,7 @@ typedef struct kvc_params {
     uint32_t chunk_tokens;   /* tokens per chunk; 0 = min(tokens, 1024),
                                 halved down to 256 while the call has fewer
                                 than 8192 chunks (one per wave slot);
-                                chunk_tokens * channels < 2^31                  */
+                                chunk_tokens * channels < 2^29                  */
     uint32_t reserved;       /* must be 0                                          */
     int64_t planes;          /* G = layers * 2 * batch * kv_heads                  */
     int64_t tokens;          /* T                                                  */
