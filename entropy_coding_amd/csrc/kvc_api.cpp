@@ -23,9 +23,7 @@ constexpr uint32_t kLanes = 64;
 constexpr uint32_t kVersion = 2;   // stream format version (split slot ranges)
 constexpr uint32_t kMaxChunkTokens = 1u << 20;
 constexpr int64_t kMaxScalars = int64_t(1) << 40;
-// decode workspace: control block, the start of the prefix's hot window
-// (one u32), then the escape bucket table (u16)
-constexpr uint64_t kDecodeHotOffset = 64;
+// decode workspace: control block, then the escape bucket table (u16)
 constexpr uint64_t kDecodeBucketOffset = 256;
 static_assert(kDecodeBucketOffset + 2 * kvc::kEscapeBucketsMax <= KVC_DECODE_WORKSPACE_BYTES,
               "decode workspace holds the control block and the bucket table");
@@ -66,18 +64,34 @@ bool geometry(int64_t planes, int64_t tokens, int64_t channels, uint32_t chunk_t
     return true;
 }
 
-// Default chunk length: 1024 tokens (at most the sequence), halved down to
-// 256 while the call has fewer chunks than MI355X has wave slots (256 CUs x
-// 32 waves), since each chunk is one wave.  Shorter chunks cost about 47 bits
-// per lane of final state, so they are used only where they add waves.
+// Default chunk length.  Each chunk is one wave and MI355X holds 8,192 of
+// them at once (256 CUs x 32 waves), so a call runs in rounds of 8,192
+// chunks, each round as long as one chunk.  Among the lengths
+// ceil(T / k) from at most 1024 tokens down to 256 (or T when shorter), the
+// default takes the one with the least rounds x (length + 9): the time of
+// the call, plus a per-chunk allowance for the final states (about 47 bits
+// per lane) and the per-chunk set-up.  Ties go to the longer chunk; of the
+// lengths that give the same chunks per plane, the shortest costs least,
+// so the choice is always some ceil(T / k).
 constexpr int64_t kWaveSlots = 256 * 32;
+constexpr int64_t kChunkMax = 1024, kChunkFloor = 256, kChunkAllowance = 9;
 
 uint32_t default_chunk_tokens(int64_t planes, int64_t tokens, int64_t channels) {
-    int64_t tc = tokens < 1024 ? (tokens > 0 ? tokens : 1) : 1024;
-    if (planes <= 0 || channels < 64) return static_cast<uint32_t>(tc);
-    auto chunks = [&](int64_t c) { return planes * ((tokens + c - 1) / c) * (channels / 64); };
-    while (tc > 256 && chunks(tc) < kWaveSlots) tc = (tc + 1) / 2;
-    return static_cast<uint32_t>(tc);
+    if (tokens <= 0) return 1;
+    if (planes <= 0 || channels < 64) return static_cast<uint32_t>(tokens < kChunkMax ? tokens : kChunkMax);
+    const int64_t groups = channels / 64;
+    const int64_t top = tokens < kChunkMax ? tokens : kChunkMax;
+    const int64_t floor_len = tokens < kChunkFloor ? tokens : kChunkFloor;
+    int64_t best_len = top, best_cost = -1;
+    for (int64_t len = top; len >= floor_len; --len) {          // at most 769 lengths
+        const int64_t chunks = planes * ((tokens + len - 1) / len) * groups;
+        const int64_t cost = ((chunks + kWaveSlots - 1) / kWaveSlots) * (len + kChunkAllowance);
+        if (best_cost < 0 || cost < best_cost) {
+            best_len = len;
+            best_cost = cost;
+        }
+    }
+    return static_cast<uint32_t>(best_len);
 }
 
 bool params_geometry(const kvc_params* p, ChunkGeom* g) {
@@ -388,9 +402,6 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     if ((e = kvc::launch_escape_buckets(prefix ? prefix : phi.zero, n_sym, shift, n_buckets, buckets, s)) !=
         hipSuccess)
         return KVC_ERR_DEVICE;
-    uint32_t* hot_lo = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d_workspace) + kDecodeHotOffset);
-    if (p.kv_dtype == KVC_BF16 && (e = kvc::launch_hot_window(prefix ? prefix : phi.zero, hot_lo, s)) != hipSuccess)
-        return KVC_ERR_DEVICE;
     timer.mark(1);
     const uint8_t* in = static_cast<const uint8_t*>(d_in);
     kvc::DecodeArgs da;
@@ -406,8 +417,6 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     da.phi = phi;
     da.buckets = buckets;
     da.bucket_shift = shift;
-    da.te = te;
-    da.hot_lo = hot_lo;
     da.kv_out = d_kv_out;
     da.ctl = ctl;
     if ((e = kvc::launch_decode(da, p.kv_dtype, p.mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;

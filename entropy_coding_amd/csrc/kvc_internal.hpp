@@ -86,8 +86,6 @@ struct DecodeArgs {
     PhiTables phi;
     const uint16_t* buckets;            // escape bucket table (launch_escape_buckets)
     uint32_t bucket_shift;
-    uint32_t te;                        // escape budget (0: no escape part)
-    const uint32_t* hot_lo;             // bf16: start of the prefix's hot window (launch_hot_window)
     void* kv_out;
     Control* ctl;
 };
@@ -122,8 +120,6 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStr
 constexpr uint32_t kEscapeBucketsMax = 65538;
 hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_t shift, uint32_t n_entries,
                                  uint16_t* bucket, hipStream_t s);
-// bf16: the start of the decoder's hot window of the prefix, one u32.
-hipError_t launch_hot_window(const uint32_t* prefix, uint32_t* out, hipStream_t s);
 // sigma calibration: float64 partial sums per (split, plane, channel)
 struct CalibPart {
     double sum;

@@ -509,7 +509,7 @@ constexpr int kDecodeBatch = 4;
 // [d_j, d_{j+1})), so that the float32 bits of d give the entry (exponent
 // and top mantissa bits) and one fused multiply-add gives z.  Distances
 // stay below 2^31 (one entry at 2^31 takes float rounding).
-constexpr int kAimMantBits = 5;
+constexpr int kAimMantBits = 6;
 constexpr uint32_t kAimFracBits = 23 - kAimMantBits;
 constexpr int kAimEntries = (31 << kAimMantBits) + 1;
 
@@ -545,12 +545,15 @@ __device__ __forceinline__ void build_aim_lds(float2* s_aim, const uint32_t* s_t
 __device__ __forceinline__ float aim_z(uint32_t t, uint32_t htot, const float2* s_aim) {
     const uint32_t u = htot - t;
     const bool upper = u < t;
-    // the distance to the nearer end, at least 1 (med3 of t, u and 1)
-    const uint32_t d = __builtin_elementwise_max(__builtin_elementwise_min(t, u), 1u);
+    // the distance to the nearer end, at least 1: the median of t, u and 1
+    uint32_t d;
+    __asm__("v_med3_u32 %0, %1, %2, 1" : "=v"(d) : "v"(t), "v"(u));
     const float df = static_cast<float>(d);
     // d >= 1: the exponent field starts at 127; the table is addressed from
     // a base biased by that many octaves (the LDS address wraps back)
-    const float2 e = (s_aim - (127u << kAimMantBits))[__float_as_uint(df) >> kAimFracBits];
+    uint32_t j;
+    __asm__("v_bfe_u32 %0, %1, %2, 15" : "=v"(j) : "v"(__float_as_uint(df)), "i"(kAimFracBits));
+    const float2 e = (s_aim - (127u << kAimMantBits))[j];
     const float z = __fmaf_rn(df, e.y, e.x);
     return upper ? -z : z;
 }
@@ -580,23 +583,6 @@ __device__ __forceinline__ uint32_t nearest_symbol_bits(float x) {
     else return nearest_e4m3(x);
 }
 
-// Hot window of the escape prefix in LDS: for magnitude patterns m_lo ..
-// m_lo + kHotHalf - 1 of both signs, P-hat at the symbol and its successor,
-// so that a cell in the window takes its escape terms from one LDS read
-// instead of a gather over the 256 KB prefix.  Layout (kHotHalf + 1 entries
-// per sign): hot[i] = P-hat[0x8000 - m_lo - kHotHalf + i] (negative values,
-// i = 0 .. kHotHalf), hot[kHotHalf + 1 + i] = P-hat[0x8000 + m_lo + i].  The
-// window start maximises the marginal mass it holds (k_hot_window).
-constexpr uint32_t kHotHalf = 2048;
-constexpr int kHotEntries = 2 * (kHotHalf + 1);
-
-__device__ __forceinline__ void build_hot_lds(uint32_t* s_hot, const uint32_t* __restrict__ prefix, uint32_t m_lo) {
-    for (uint32_t i = threadIdx.x; i <= kHotHalf; i += blockDim.x) {
-        s_hot[i] = prefix[0x8000u - m_lo - kHotHalf + i];
-        s_hot[kHotHalf + 1u + i] = prefix[0x8000u + m_lo + i];
-    }
-}
-
 // A candidate symbol with its exact CDF terms: G at both cell edges, and
 // the escape prefix at s and s + 1.
 struct Cell {
@@ -611,12 +597,8 @@ struct Cell {
 // mean it becomes infinite, as the format defines.  Inf and NaN patterns
 // reach here only from the escape lookup, and their G terms are replaced
 // by the caller (every edge of theirs is infinite).
-// The escape terms come from the hot window when `hot` is given and the
-// magnitude lies in it (`inside` tells; the caller reads the prefix for
-// lanes outside), else from the prefix in global memory.
 template <int MU>
-__device__ __forceinline__ Cell eval_bf16(uint32_t kb, float mu, float inv24, const Model& m,
-                                          const uint32_t* hot = nullptr, uint32_t m_lo = 0, bool* inside = nullptr) {
+__device__ __forceinline__ Cell eval_bf16(uint32_t kb, float mu, float inv24, const Model& m) {
     const uint32_t kbs = kb << 16;
     const uint32_t sign = kbs & 0x80000000u;
     uint32_t ob = kbs | 0x8000u;
@@ -629,19 +611,8 @@ __device__ __forceinline__ Cell eval_bf16(uint32_t kb, float mu, float inv24, co
     c.g1 = __builtin_elementwise_max(ha, hb);
     // ordered index: 0x8000 + m for a positive pattern, 0x7FFF - m for a negative one
     const uint32_t neg = static_cast<uint32_t>(static_cast<int32_t>(kbs) >> 31);
-    const uint32_t mag = kb & 0x7FFFu;
-    c.s = (mag ^ neg) + 0x8000u;
-    if (hot) {
-        // negative: P-hat[s] at kHotHalf - 1 - d; positive: at kHotHalf + 1 + d
-        const uint32_t d = mag - m_lo;
-        *inside = d < kHotHalf;
-        const uint32_t dc = __builtin_elementwise_min(d, kHotHalf - 1u);
-        const uint32_t* h = hot + ((dc ^ neg) + neg + (kHotHalf + 1u));
-        c.p0 = h[0];
-        c.p1 = h[1];
-    } else {
-        prefix_pair(m, c.s, c.p0, c.p1);
-    }
+    c.s = ((kb & 0x7FFFu) ^ neg) + 0x8000u;
+    prefix_pair(m, c.s, c.p0, c.p1);
     return c;
 }
 
@@ -804,11 +775,13 @@ __device__ __forceinline__ uint32_t escape_symbol(bool need, uint32_t y, __amdgp
 }
 
 // Stream words of a chunk, staged through a per-wave LDS ring of two
-// 128-word blocks.  The block after next is loaded into registers (one
-// dword per lane) as soon as a block is entered and written to the ring
-// when the one before it is left, so no global read sits on the serial
-// decode chain; a refill read is one LDS access.
-constexpr int kRingDwords = 128;
+// 128-word blocks plus a copy of the first block after the second, so that
+// the 128 words from any position of the ring on are contiguous.  The
+// block after next is loaded into registers (one dword per lane) as soon as
+// a block is entered and written to the ring when the one before it is
+// left, so no global read sits on the serial decode chain.  A refill read
+// is one LDS access at a wave-uniform base plus the lane's rank.
+constexpr int kRingDwords = 192;
 struct WordRing {
     const uint32_t* __restrict__ dw;   // chunk words as dwords (8-byte aligned)
     uint32_t n_dw;                     // dwords in the chunk's word area
@@ -822,55 +795,30 @@ struct WordRing {
     }
     __device__ __forceinline__ void init(uint32_t lane) {
         base = 0;
-        ring[lane] = load(0, lane);
+        const uint32_t b0 = load(0, lane);
+        ring[lane] = b0;
+        ring[128u + lane] = b0;
         ring[64u + lane] = load(1, lane);
         ahead = load(2, lane);
     }
-    // word p, base <= p < base + 256
-    __device__ __forceinline__ uint32_t word(uint32_t p) const {
-        return reinterpret_cast<const uint16_t*>(ring)[p & 255u];
+    // words p .. p + 127 start here (base <= p < base + 128; p wave-uniform)
+    __device__ __forceinline__ const uint16_t* at(uint32_t p) const {
+        return reinterpret_cast<const uint16_t*>(ring) + (p & 255u);
     }
     __device__ __forceinline__ void advance(uint32_t rp, uint32_t lane) {
         if (rp >= base + 128u) {                       // wave-uniform
             // the block just left (slot of base) takes the block after next
-            ring[((base >> 7) & 1u) * 64u + lane] = ahead;
+            if ((base >> 7) & 1u) {
+                ring[64u + lane] = ahead;
+            } else {
+                ring[lane] = ahead;
+                ring[128u + lane] = ahead;
+            }
             base += 128u;
             ahead = load((base >> 7) + 2u, lane);
         }
     }
 };
-
-// Window start: the m_lo in [0, 0x8000 - kHotHalf] whose window holds the
-// most escape mass (ties to the smallest), from prefix differences.  One
-// workgroup.
-__global__ void __launch_bounds__(1024) k_hot_window(const uint32_t* __restrict__ prefix, uint32_t* __restrict__ out) {
-    __shared__ unsigned long long s_best[16];
-    constexpr uint32_t last = 0x8000u - kHotHalf;
-    unsigned long long best = 0;                  // mass << 32 | (0xFFFFFFFF - m_lo): max picks the smallest m_lo
-    for (uint32_t c = threadIdx.x; c <= last; c += blockDim.x) {
-        const uint32_t mass = (prefix[0x8000u + c + kHotHalf] - prefix[0x8000u + c]) +
-                              (prefix[0x8000u - c] - prefix[0x8000u - c - kHotHalf]);
-        const unsigned long long key = (static_cast<unsigned long long>(mass) << 32) | (0xFFFFFFFFu - c);
-        best = key > best ? key : best;
-    }
-    for (int off = 32; off > 0; off >>= 1) {
-        const unsigned long long o = __shfl_xor(best, off, 64);
-        best = o > best ? o : best;
-    }
-    if ((threadIdx.x & 63) == 0) s_best[threadIdx.x >> 6] = best;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 1; w < 16; ++w) best = s_best[w] > best ? s_best[w] : best;
-        best = s_best[0] > best ? s_best[0] : best;
-        const uint32_t c = 0xFFFFFFFFu - static_cast<uint32_t>(best);
-        out[0] = c <= last ? c : 0u;
-    }
-}
-
-hipError_t launch_hot_window(const uint32_t* prefix, uint32_t* out, hipStream_t s) {
-    hipLaunchKernelGGL(k_hot_window, dim3(1), dim3(1024), 0, s, prefix, out);
-    return hipGetLastError();
-}
 
 template <int KV, int MU>
 __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(64))) k_decode(DecodeArgs a) {
@@ -878,10 +826,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
     __shared__ float2 s_aim[kAimEntries];
     __shared__ uint32_t s_ring[kDecodeBlock / 64][kRingDwords];
     __shared__ uint32_t s_small[KV == kE4M3 ? kE4Words : 1];
-    __shared__ uint32_t s_hot[KV == kBF16 ? kHotEntries : 1];
-    const uint32_t m_lo = KV == kBF16 ? __builtin_elementwise_min(a.hot_lo[0], 0x8000u - kHotHalf) : 0u;
     if constexpr (KV == kE4M3) build_e4_lds(s_small, a.prefix);      // exact prefix + edges
-    else build_hot_lds(s_hot, a.prefix, m_lo);
     build_table_lds(s_tab, a.phi, a.tn, a.tw);
     const uint32_t htot = a.tn + a.tw;
     build_aim_lds(s_aim, s_tab);
@@ -922,8 +867,6 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
     constexpr uint32_t kN = Alphabet<KV>::kSize;
     const Model m{s_tab, a.prefix, s_small, buffer_rsrc(a.prefix, (kN + 1u) * 4u)};
     const uint32_t geo = geo_offset(lane);
-    // without an escape part the prefix (and so the window) is all zero
-    const uint64_t has_escape = a.te ? ~0ull : 0ull;
     const __amdgpu_buffer_rsrc_t bucket = buffer_rsrc(a.buckets, kEscapeBucketsMax * 2u);
 
     using KB = typename Alphabet<KV>::Bits;
@@ -946,62 +889,49 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
         // candidate: the cell the aim lands in, with its exact CDF terms
         uint32_t kb = nearest_symbol_bits<KV>(__fmaf_rn(aim_z(target, htot, s_aim), sg, mu));
-        Cell c;
-        uint64_t far = 0;
-        if constexpr (KV == kBF16) {
-            bool inside;
-            c = eval_bf16<MU>(kb, mu, inv24, m, s_hot, m_lo, &inside);
-            far = __ballot(!inside) & has_escape;
-        } else {
-            c = eval_cell<KV, MU>(kb, mu, inv24, m);
-        }
         const uint64_t esc = __ballot(target >= htot);
+        if (esc) {
+            // floor-and-escape slots: the symbol comes from the lookup
+            misses += __popcll(esc);
+            const bool e = target >= htot;
+            const uint32_t se = escape_symbol<KV>(e, target - htot, bucket, a.bucket_shift, m);
+            if (e) kb = bits_of_order<KV>(se);
+        }
+        Cell c = eval_cell<KV, MU>(kb, mu, inv24, m);
+        if (esc) {
+            // a floor-and-escape slot has rank f_G(s) + (y - Q(s)): the
+            // symbol's slots are taken to start at T_n + T_w + Q(s) - f_G(s)
+            // (G terms of Inf and NaN, whose edges are all infinite, set first)
+            if (target >= htot) {
+                __asm__ volatile("");                    // keep this a branch (rarely taken)
+                if constexpr (KV == kBF16) {
+                    if ((kb & 0x7FFFu) >= 0x7F80u) c.g0 = c.g1 = (kb & 0x8000u) ? 0u : htot;
+                }
+                const uint32_t fg = c.g1 - c.g0;
+                c.g0 = htot + c.s + c.p0 - fg;
+                c.g1 = c.g0 + fg;
+            }
+        }
         uint64_t need = (__ballot(target < c.g0) | __ballot(target >= c.g1)) & ~esc;
-        if (esc | need | far) {
-            if (far) {
-                // cells outside the hot window: escape terms from the prefix
-                if ((far >> lane) & 1ull) prefix_pair(m, c.s, c.p0, c.p1);
+        if (need) {
+            // Gaussian slots outside the aimed cell: one symbol towards the
+            // target first (G(0) = 0 <= target < G(N) = htot), then the
+            // wave-cooperative search
+            misses += __popcll(need);
+            bool hit = ((need >> lane) & 1ull) == 0ull;
+            if (!hit) {
+                kb = bits_of_order<KV>(target < c.g0 ? c.s - 1u : c.s + 1u);
+                c = eval_cell<KV, MU>(kb, mu, inv24, m);
+                hit = target >= c.g0 && target < c.g1;
             }
-            if (esc) {
-                // floor-and-escape slots: look the symbol up; its rank is
-                // f_G(s) + (y - Q(s)), so its slots are taken to start at
-                // T_n + T_w + Q(s) - f_G(s) (G terms of Inf and NaN, whose
-                // edges are all infinite, set first)
-                misses += __popcll(esc);
-                const bool e = target >= htot;
-                const uint32_t se = escape_symbol<KV>(e, target - htot, bucket, a.bucket_shift, m);
-                if (e) {
-                    kb = bits_of_order<KV>(se);
-                    c = eval_cell<KV, MU>(kb, mu, inv24, m);
-                    if constexpr (KV == kBF16) {
-                        if ((kb & 0x7FFFu) >= 0x7F80u) c.g0 = c.g1 = (kb & 0x8000u) ? 0u : htot;
-                    }
-                    const uint32_t fg = c.g1 - c.g0;
-                    c.g0 = htot + c.s + c.p0 - fg;
-                    c.g1 = c.g0 + fg;
-                }
-            }
+            need = __ballot(!hit);
             if (need) {
-                // Gaussian slots outside the aimed cell: one symbol towards
-                // the target first (G(0) = 0 <= target < G(N) = htot), then
-                // the wave-cooperative search
-                misses += __popcll(need);
-                bool hit = ((need >> lane) & 1ull) == 0ull;
+                const bool up = target >= c.g1;
+                const uint32_t sym = coop_gauss<KV, MU>(!hit, target, mu, inv24, up, up ? c.s + 1u : 0u,
+                                                        up ? kN : c.s, up ? c.g1 : 0u, up ? htot : c.g0, m, geo, c.s);
                 if (!hit) {
-                    kb = bits_of_order<KV>(target < c.g0 ? c.s - 1u : c.s + 1u);
+                    kb = bits_of_order<KV>(sym);
                     c = eval_cell<KV, MU>(kb, mu, inv24, m);
-                    hit = target >= c.g0 && target < c.g1;
-                }
-                need = __ballot(!hit);
-                if (need) {
-                    const bool up = target >= c.g1;
-                    const uint32_t sym = coop_gauss<KV, MU>(!hit, target, mu, inv24, up, up ? c.s + 1u : 0u,
-                                                            up ? kN : c.s, up ? c.g1 : 0u, up ? htot : c.g0, m, geo,
-                                                            c.s);
-                    if (!hit) {
-                        kb = bits_of_order<KV>(sym);
-                        c = eval_cell<KV, MU>(kb, mu, inv24, m);
-                    }
                 }
             }
         }
@@ -1017,7 +947,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         uint32_t xh = static_cast<uint32_t>(x >> 32), xl = static_cast<uint32_t>(x);
         const bool take1 = xh < kLHi;
         const uint64_t m1 = __ballot(take1);
-        const uint32_t w1 = win.word(rp + lane_rank(m1));
+        const uint32_t w1 = win.at(rp)[lane_rank(m1)];
         const uint32_t sh = __builtin_amdgcn_alignbit(xh, xl, 16);
         xl = take1 ? (xl << 16) | w1 : xl;
         xh = take1 ? sh : xh;
@@ -1025,7 +955,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         const uint64_t m2 = __ballot(xh < kLHi);
         if (m2) {
             const bool take2 = xh < kLHi;
-            const uint32_t w2 = win.word(rp + lane_rank(m2));
+            const uint32_t w2 = win.at(rp)[lane_rank(m2)];
             const uint32_t sh2 = __builtin_amdgcn_alignbit(xh, xl, 16);
             xl = take2 ? (xl << 16) | w2 : xl;
             xh = take2 ? sh2 : xh;

@@ -65,9 +65,9 @@ WORKLOADS = {
     1: Workload(1, "Qwen3-0.6B-shaped bf16 KV (28 layers, 1024 tokens)", 28, 1, 8, 1024, 128,
                 BF16, BF16, 9500, 300, True, False, 8, 1024, 256),
     2: Workload(2, "Qwen3-8B-shaped bf16 KV (36 layers, batch 4, 4096 tokens)", 36, 4, 8, 4096, 128,
-                BF16, BF16, 9500, 300, True, True, 128, 1024, 1024),
+                BF16, BF16, 9500, 300, True, True, 128, 1024, 586),
     3: Workload(3, "FP8 e4m3 KV (36 layers, 8192 tokens, fp32 predictor)", 36, 1, 8, 8192, 128,
-                E4M3, F32, 9500, 300, False, False, 128, 1024, 1024),
+                E4M3, F32, 9500, 300, False, False, 128, 1024, 586),
     4: Workload(4, "Qwen3-32B-shaped long-context bf16 KV (64 layers, 32768 tokens)", 64, 1, 8, 32768, 128,
                 BF16, BF16, 9500, 300, True, True, 128, 1024, 256),
 }

@@ -84,9 +84,11 @@ typedef struct kvc_params {
     uint32_t w_wide_bp;      /* weight of N(mu, (3 sigma)^2), basis points: 300     */
                              /* the escape part p_hat gets 10000 - both; (10000, 0)
                                 is a single Gaussian and needs no prefix table     */
-    uint32_t chunk_tokens;   /* tokens per chunk; 0 = min(tokens, 1024),
-                                halved down to 256 while the call has fewer
-                                than 8192 chunks (one per wave slot);
+    uint32_t chunk_tokens;   /* tokens per chunk; 0 = the library's default:
+                                of the lengths ceil(tokens / k) between 1024
+                                and 256 (or tokens, if fewer), the one with
+                                the least rounds x (length + 9), a round being
+                                8,192 chunks (one wave each) at once;
                                 chunk_tokens * channels < 2^29                  */
     uint32_t reserved;       /* must be 0                                          */
     int64_t planes;          /* G = layers * 2 * batch * kv_heads                  */

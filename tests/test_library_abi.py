@@ -61,17 +61,18 @@ def test_encode_sizes(kvc):
 
 
 @pytest.mark.parametrize("planes,tokens,channels,expect", [
-    (2304, 4096, 128, 1024),     # 18,432 chunks at 1024 tokens: already one per wave slot and more
-    (448, 1024, 128, 256),       # 896 chunks at 1024 -> 3,584 at 256 (the floor)
-    (16, 32768, 128, 256),       # one 32K-token layer: 1,024 -> 4,096 chunks
-    (576, 8192, 128, 1024),      # 9,216 chunks at 1024
-    (64, 4096, 128, 256),        # 512 -> 1,024 -> 2,048 chunks: the floor comes first
-    (512, 4096, 128, 512),       # 4,096 -> 8,192 chunks at 512: enough
+    (2304, 4096, 128, 586),      # 7 chunks per plane and group: 32,256 chunks, 3.94 rounds of 8,192
+                                 # (1024 tokens: 18,432 chunks in 3 rounds, the last a quarter full)
+    (448, 1024, 128, 256),       # 3,584 chunks: one round at any length, so the floor
+    (16, 32768, 128, 256),       # one 32K-token layer: 4,096 chunks at the floor
+    (576, 8192, 128, 586),       # 16,128 chunks, 1.97 rounds (1024 tokens: 9,216 chunks, 2 rounds)
+    (64, 4096, 128, 256),        # 2,048 chunks
+    (512, 4096, 128, 512),       # exactly one round of 8,192 chunks
     (3, 45, 128, 45),            # short sequences keep one chunk per plane and group
 ])
 def test_default_chunk_length(kvc, planes, tokens, channels, expect):
-    """chunk_tokens = 0 picks 1024 tokens, halved down to 256 while the call
-    has fewer chunks than the chip's 8,192 wave slots."""
+    """chunk_tokens = 0 picks, among lengths from 1024 down to 256 tokens,
+    the one with the least (rounds of 8,192 chunks) x (length + 9)."""
     auto = kvc.kvc_encode_sizes(kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, planes, tokens, channels, (9500, 300), 0))
     fixed = kvc.kvc_encode_sizes(kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, planes, tokens, channels, (9500, 300),
                                                  expect))
