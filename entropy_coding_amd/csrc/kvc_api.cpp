@@ -20,7 +20,7 @@ constexpr uint32_t kLog2M = 31;
 constexpr uint32_t kLog2L = 47;
 constexpr uint32_t kWordBits = 16;
 constexpr uint32_t kLanes = 64;
-constexpr uint32_t kVersion = 2;   // stream format version (split slot ranges)
+constexpr uint32_t kVersion = 3;   // stream format version (split slot ranges, floor of z * 2^24)
 constexpr uint32_t kMaxChunkTokens = 1u << 20;
 constexpr int64_t kMaxScalars = int64_t(1) << 40;
 // decode workspace: control block, then the escape bucket table (u16)

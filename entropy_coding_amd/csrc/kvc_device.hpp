@@ -117,15 +117,18 @@ __device__ __forceinline__ float mu_value(typename MuT<MU>::T v) {
     return __builtin_isfinite(m) ? m : 0.0f;
 }
 
-// q = rint(clamp(d * inv, +-24) * 2^24) computed as rint(clamp(d * inv24,
+// q = floor(clamp(d * inv, +-24) * 2^24) computed as floor(clamp(d * inv24,
 // +-24 * 2^24)) with inv24 = inv * 2^24: identical for every sigma in the
 // accepted range [2^-96, 2^96] (the power-of-two scaling is exact there and
-// both forms saturate together).
+// both forms saturate together).  Floor and conversion are one instruction
+// (v_cvt_flr_i32_f32).
 __device__ __forceinline__ int32_t z_fixed(float edge_pos, float mu, float inv24) {
     const float d = __fsub_rn(edge_pos, mu);
     float zq = __fmul_rn(d, inv24);
     zq = __builtin_amdgcn_fmed3f(zq, -kQMaxF, kQMaxF);
-    return static_cast<int32_t>(__builtin_rintf(zq));
+    int32_t q;
+    __asm__("v_cvt_flr_i32_f32 %0, %1" : "=v"(q) : "v"(zq));
+    return q;
 }
 
 // Integer mixture CDF of z = q / 2^24: table step 1/256 with integer linear

@@ -96,8 +96,8 @@ typedef struct kvc_params {
     int64_t channels;        /* D, a positive multiple of 64                       */
 } kvc_params;
 
-/* Stream format version written and accepted: 2 (Gaussian and floor-and-escape
-   slots in separate ranges of the coder). */
+/* Stream format version written and accepted: 3 (Gaussian and floor-and-escape
+   slots in separate ranges of the coder; the CDF argument q = floor(z * 2^24)). */
 int kvc_version(void);
 
 /* Human-readable name of a status code (static string). */

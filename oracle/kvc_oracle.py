@@ -52,7 +52,7 @@ LANES = 64                         # interleaved rANS lanes per chunk
 HEADER_BYTES = 128
 STATE_BYTES = 8 * LANES            # 64 final states, u64 each
 MAGIC = b"KVC1"
-VERSION = 2
+VERSION = 3
 
 
 class StreamError(ValueError):
@@ -247,8 +247,11 @@ def mu_to_f32(mu, mu_dtype: int) -> np.ndarray:
 def cdf(b, mu32, inv32, dtype: int, t_n: int, t_w: int, prefix=None) -> np.ndarray:
     """C(b): cumulative frequency below symbol b under the mixture.
 
-    S-3  d = pos(b) - mu and z = d * (1/sigma), each one IEEE float32 operation;
-         z clamped to [-24, 24]; q = round-half-even(z * 2^24).
+    S-3  d = pos(b) - mu and z' = d * (2^24/sigma), each one IEEE float32
+         operation, where 2^24/sigma is the float32 1/sigma times 2^24 (exact
+         for sigma in [2^-96, 2^96]); z' clamped to [-24 * 2^24, 24 * 2^24];
+         q = floor(z').  (q / 2^24 is z; the fixed-point scale is applied
+         before the product so that a tiny z keeps its sign through floor.)
     S-5  C(b) = b + h_fx(q) + prefix[b]: the +1 floor of every symbol below b,
          both Gaussian parts through the mixture table, and the escape part
          as the integer prefix of the marginal.
@@ -257,11 +260,12 @@ def cdf(b, mu32, inv32, dtype: int, t_n: int, t_w: int, prefix=None) -> np.ndarr
     pos = boundary_positions(dtype)[b]
     mu32 = np.asarray(mu32, dtype=np.float32)
     inv32 = np.asarray(inv32, dtype=np.float32)
-    with np.errstate(over="ignore", invalid="raise"):
+    inv24 = (inv32 * np.float32(1 << 24)).astype(np.float32)
+    qmax = np.float32(TABLE_Z_MAX << 24)
+    with np.errstate(over="ignore", under="ignore", invalid="raise"):
         d = (pos - mu32).astype(np.float32)
-        z = (d * inv32).astype(np.float32)
-    z = np.clip(z, np.float32(-TABLE_Z_MAX), np.float32(TABLE_Z_MAX)).astype(np.float32)
-    q = np.rint(z * np.float32(1 << 24)).astype(np.int64)
+        z24 = (d * inv24).astype(np.float32)
+    q = np.floor(np.clip(z24, -qmax, qmax)).astype(np.int64)
     g = h_fx(q, mixture_table(t_n, t_w))
     if prefix is not None:
         g = g + np.asarray(prefix, dtype=np.int64)[b]

@@ -49,10 +49,14 @@ def tiny(kv_dtype, seed=7, planes=3, tokens=45, channels=128):
 # the CDF
 # ---------------------------------------------------------------------------
 def adversarial_pairs(rng, n_random):
+    # the last four put z * 2^24 at subnormal magnitudes of either sign for the edges next to mu
+    # (floor of a negative subnormal is -1)
     mus = [0.0, -0.0, 1e-40, -1e-40, 3.0e38, -3.0e38, 1.5, -2.75, 0.001, 1e4, np.nan, np.inf, -np.inf,
-           0.998046875, 448.0, -448.0, 0.0, 2.0 ** -133, 0.5 * (1 + 2 ** -8)]
+           0.998046875, 448.0, -448.0, 0.0, 2.0 ** -133, 0.5 * (1 + 2 ** -8),
+           2.0 ** -60, -2.0 ** -60, 1e-20, -3e-20]
     sig = [1e-3, 2.0 ** -30, 2.0 ** -30, 2.0 ** -96, 1.0, 2.0 ** 96, 2.0 ** -4, 0.37, 10.0, 2.0 ** -7, 0.5, 0.5, 0.5,
-           2.0 ** -12, 2.0, 0.01, 1e4, 2.0 ** -20, 2.0 ** -9]
+           2.0 ** -12, 2.0, 0.01, 1e4, 2.0 ** -20, 2.0 ** -9,
+           2.0 ** 96, 2.0 ** 96, 2.0 ** 96, 2.0 ** 90]
     m = np.concatenate([np.float32(mus), (rng.standard_normal(n_random) * np.exp(rng.normal(0, 2, n_random))).astype(np.float32)])
     s = np.concatenate([np.float32(sig), np.exp2(rng.uniform(-30, 8, n_random)).astype(np.float32)])
     return m.astype(np.float32), s.astype(np.float32)

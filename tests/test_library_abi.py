@@ -30,7 +30,7 @@ def test_every_declared_call_is_exported(kvc):
 
 
 def test_version_and_status_strings(kvc):
-    assert kvc.kvc_version() == O.VERSION == 2
+    assert kvc.kvc_version() == O.VERSION == 3
     assert kvc.kvc_status_string(0) == "ok"
     assert "corrupt" in kvc.kvc_status_string(-3)
 
