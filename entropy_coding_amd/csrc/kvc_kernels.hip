@@ -558,12 +558,14 @@ __device__ __forceinline__ float aim_z(uint32_t t, uint32_t htot, const float2* 
     return upper ? -z : z;
 }
 
-// bf16 pattern of the value nearest x (round to nearest even), x clamped
-// to [-max, max].
+// A decoder candidate is held as a word whose upper half is the bf16
+// pattern (the lower half is ignored) and, for e4m3, as the pattern itself.
+// Nearest bf16 value to x (round to nearest even), x clamped to
+// [-max, max]: the rounded float32 bits, whose upper half is the pattern.
 __device__ __forceinline__ uint32_t nearest_bf16(float x) {
     const float lim = __uint_as_float(0x7F7F0000u);
     const uint32_t u = __float_as_uint(__builtin_amdgcn_fmed3f(x, -lim, lim));
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return u + 0x7FFFu + ((u >> 16) & 1u);
 }
 
 // e4m3fn pattern of the value nearest x, x clamped to [-448, 448]:
@@ -578,9 +580,27 @@ __device__ __forceinline__ uint32_t nearest_e4m3(float x) {
 }
 
 template <int KV>
-__device__ __forceinline__ uint32_t nearest_symbol_bits(float x) {
+__device__ __forceinline__ uint32_t nearest_candidate(float x) {
     if constexpr (KV == kBF16) return nearest_bf16(x);
     else return nearest_e4m3(x);
+}
+
+// Candidate of the ordered index s, and the bit pattern of a candidate.
+template <int KV>
+__device__ __forceinline__ uint32_t candidate_of_index(uint32_t s) {
+    if constexpr (KV == kBF16) {
+        // s >= 0x8000: pattern s ^ 0x8000; below: 0xFFFF - s = s ^ 0xFFFF
+        const uint32_t below = ((s >> 15) & 1u) - 1u;
+        return (s ^ 0x8000u ^ (below & 0x7FFFu)) << 16;
+    } else {
+        return bits_of_order<KV>(s);
+    }
+}
+
+template <int KV>
+__device__ __forceinline__ uint32_t candidate_bits(uint32_t cand) {
+    if constexpr (KV == kBF16) return cand >> 16;
+    else return cand;
 }
 
 // A candidate symbol with its exact CDF terms: G at both cell edges, and
@@ -589,7 +609,7 @@ struct Cell {
     uint32_t s, g0, g1, p0, p1;
 };
 
-// Cell of the bf16 pattern kb.  The outer edge (away from zero) is the
+// Cell of the bf16 candidate kw (pattern in the upper half).  The outer edge (away from zero) is the
 // pattern's magnitude plus half a step, the inner edge the magnitude minus
 // half a step (0 for +-0).  With a bf16 mean the +-max cells may keep
 // their finite outer edge (the mean lies at least half a step inside it, so
@@ -598,20 +618,19 @@ struct Cell {
 // reach here only from the escape lookup, and their G terms are replaced
 // by the caller (every edge of theirs is infinite).
 template <int MU>
-__device__ __forceinline__ Cell eval_bf16(uint32_t kb, float mu, float inv24, const Model& m) {
-    const uint32_t kbs = kb << 16;
-    const uint32_t sign = kbs & 0x80000000u;
-    uint32_t ob = kbs | 0x8000u;
+__device__ __forceinline__ Cell eval_bf16(uint32_t kw, float mu, float inv24, const Model& m) {
+    const uint32_t neg = static_cast<uint32_t>(static_cast<int32_t>(kw) >> 31);
+    const uint32_t sign = kw & 0x80000000u;
+    uint32_t ob = (kw & 0xFFFF0000u) | 0x8000u;
     const uint32_t ib = __builtin_elementwise_max(__builtin_elementwise_sub_sat(ob, 0x10000u), sign);
-    if constexpr (MU == kF32) ob = (kbs & 0x7FFFFFFFu) == 0x7F7F0000u ? (sign | 0x7F800000u) : ob;
+    if constexpr (MU == kF32) ob = (kw & 0x7FFF0000u) == 0x7F7F0000u ? (sign | 0x7F800000u) : ob;
     const uint32_t ha = h_fx(z_fixed(__uint_as_float(ib), mu, inv24), m.tab);
     const uint32_t hb = h_fx(z_fixed(__uint_as_float(ob), mu, inv24), m.tab);
     Cell c;
     c.g0 = __builtin_elementwise_min(ha, hb);
     c.g1 = __builtin_elementwise_max(ha, hb);
     // ordered index: 0x8000 + m for a positive pattern, 0x7FFF - m for a negative one
-    const uint32_t neg = static_cast<uint32_t>(static_cast<int32_t>(kbs) >> 31);
-    c.s = ((kb & 0x7FFFu) ^ neg) + 0x8000u;
+    c.s = (((kw >> 16) & 0x7FFFu) ^ neg) + 0x8000u;
     prefix_pair(m, c.s, c.p0, c.p1);
     return c;
 }
@@ -783,15 +802,14 @@ __device__ __forceinline__ uint32_t escape_symbol(bool need, uint32_t y, __amdgp
 // is one LDS access at a wave-uniform base plus the lane's rank.
 constexpr int kRingDwords = 192;
 struct WordRing {
-    const uint32_t* __restrict__ dw;   // chunk words as dwords (8-byte aligned)
-    uint32_t n_dw;                     // dwords in the chunk's word area
+    __amdgpu_buffer_rsrc_t words;      // the chunk's word area (reads past its end give 0)
     uint32_t* ring;                    // this wave's kRingDwords dwords of LDS
     uint32_t base;                     // first word of the block being read
     uint32_t ahead;                    // this lane's dword of block base/128 + 2
 
     __device__ __forceinline__ uint32_t load(uint32_t block, uint32_t lane) const {
-        const uint32_t d = block * 64u + lane;
-        return d < n_dw ? dw[d] : 0u;
+        // the whole offset in the vector operand, where the range check applies
+        return __builtin_amdgcn_raw_buffer_load_b32(words, (block * 64u + lane) * 4u, 0, 0);
     }
     __device__ __forceinline__ void init(uint32_t lane) {
         base = 0;
@@ -853,7 +871,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         return;
     }
     const uint32_t avail = static_cast<uint32_t>((end - beg - kStateBytes) / 2);     // a multiple of 4
-    WordRing win{reinterpret_cast<const uint32_t*>(base + kStateBytes), avail / 2u, s_ring[wave], 0u, 0u};
+    WordRing win{buffer_rsrc(base + kStateBytes, avail * 2u), s_ring[wave], 0u, 0u};
     win.init(static_cast<uint32_t>(lane));
 
     const float sigma = a.sigma[cp.g * D + cp.k * 64 + lane];
@@ -888,14 +906,14 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
     auto step = [&](uint32_t t, float mu) {
         const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
         // candidate: the cell the aim lands in, with its exact CDF terms
-        uint32_t kb = nearest_symbol_bits<KV>(__fmaf_rn(aim_z(target, htot, s_aim), sg, mu));
+        uint32_t kb = nearest_candidate<KV>(__fmaf_rn(aim_z(target, htot, s_aim), sg, mu));
         const uint64_t esc = __ballot(target >= htot);
         if (esc) {
             // floor-and-escape slots: the symbol comes from the lookup
             misses += __popcll(esc);
             const bool e = target >= htot;
             const uint32_t se = escape_symbol<KV>(e, target - htot, bucket, a.bucket_shift, m);
-            if (e) kb = bits_of_order<KV>(se);
+            if (e) kb = candidate_of_index<KV>(se);
         }
         Cell c = eval_cell<KV, MU>(kb, mu, inv24, m);
         if (esc) {
@@ -905,7 +923,10 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
             if (target >= htot) {
                 __asm__ volatile("");                    // keep this a branch (rarely taken)
                 if constexpr (KV == kBF16) {
-                    if ((kb & 0x7FFFu) >= 0x7F80u) c.g0 = c.g1 = (kb & 0x8000u) ? 0u : htot;
+                    const bool special = (kb & 0x7F800000u) == 0x7F800000u;    // Inf, NaN
+                    if (__ballot(special)) {
+                        if (special) c.g0 = c.g1 = (kb & 0x80000000u) ? 0u : htot;
+                    }
                 }
                 const uint32_t fg = c.g1 - c.g0;
                 c.g0 = htot + c.s + c.p0 - fg;
@@ -920,7 +941,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
             misses += __popcll(need);
             bool hit = ((need >> lane) & 1ull) == 0ull;
             if (!hit) {
-                kb = bits_of_order<KV>(target < c.g0 ? c.s - 1u : c.s + 1u);
+                kb = candidate_of_index<KV>(target < c.g0 ? c.s - 1u : c.s + 1u);
                 c = eval_cell<KV, MU>(kb, mu, inv24, m);
                 hit = target >= c.g0 && target < c.g1;
             }
@@ -930,7 +951,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
                 const uint32_t sym = coop_gauss<KV, MU>(!hit, target, mu, inv24, up, up ? c.s + 1u : 0u,
                                                         up ? kN : c.s, up ? c.g1 : 0u, up ? htot : c.g0, m, geo, c.s);
                 if (!hit) {
-                    kb = bits_of_order<KV>(sym);
+                    kb = candidate_of_index<KV>(sym);
                     c = eval_cell<KV, MU>(kb, mu, inv24, m);
                 }
             }
@@ -964,7 +985,8 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         x = (static_cast<unsigned long long>(xh) << 32) | xl;
         win.advance(rp, static_cast<uint32_t>(lane));
         const uint32_t ooff = t * D * static_cast<uint32_t>(sizeof(KB));
-        if constexpr (KV == kBF16) __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(kb), outb, kv_lane, ooff, 0);
+        if constexpr (KV == kBF16)
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(candidate_bits<KV>(kb)), outb, kv_lane, ooff, 0);
         else __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(kb), outb, kv_lane, ooff, 0);
     };
     // predictor-mean rows as raw bits (the last row stands in for rows past
