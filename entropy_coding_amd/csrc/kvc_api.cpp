@@ -23,10 +23,15 @@ constexpr uint32_t kLanes = 64;
 constexpr uint32_t kVersion = 3;   // stream format version (split slot ranges, floor of z * 2^24)
 constexpr uint32_t kMaxChunkTokens = 1u << 20;
 constexpr int64_t kMaxScalars = int64_t(1) << 40;
-// decode workspace: control block, then the escape bucket table (u16)
+// decode workspace: control block, the escape bucket table (u16), the
+// mixture table and the aim table
 constexpr uint64_t kDecodeBucketOffset = 256;
-static_assert(kDecodeBucketOffset + 2 * kvc::kEscapeBucketsMax <= KVC_DECODE_WORKSPACE_BYTES,
-              "decode workspace holds the control block and the bucket table");
+constexpr uint64_t kDecodeTableOffset = 131584;
+constexpr uint64_t kDecodeAimOffset = kDecodeTableOffset + 49408;
+static_assert(kDecodeBucketOffset + 2 * kvc::kEscapeBucketsMax <= kDecodeTableOffset &&
+                  kDecodeTableOffset + kvc::kTableBytes <= kDecodeAimOffset &&
+                  kDecodeAimOffset + kvc::kAimBytes <= KVC_DECODE_WORKSPACE_BYTES,
+              "decode workspace layout");
 
 uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
@@ -102,9 +107,10 @@ bool params_geometry(const kvc_params* p, ChunkGeom* g) {
 }
 
 // Workspace of the encoder: control block, final states, word counts,
-// directory, then one word slot per chunk sized for two words per scalar.
+// directory, one word slot per chunk sized for two words per scalar, then
+// the per-call mixture table.
 struct EncodeLayout {
-    uint64_t states, chunk_words, directory, slots, total, slot_words, max_stream;
+    uint64_t states, chunk_words, directory, slots, table, total, slot_words, max_stream;
 };
 
 EncodeLayout encode_layout(const ChunkGeom& g) {
@@ -115,7 +121,8 @@ EncodeLayout encode_layout(const ChunkGeom& g) {
     l.chunk_words = round_up(l.states + n * kLanes * 8, 256);
     l.directory = round_up(l.chunk_words + n * 4, 256);
     l.slots = round_up(l.directory + (n + 1) * 8, 256);
-    l.total = l.slots + n * l.slot_words * 2;
+    l.table = round_up(l.slots + n * l.slot_words * 2, 256);
+    l.total = l.table + kvc::kTableBytes;
     l.max_stream = KVC_HEADER_BYTES + 8 * (n + 1) + n * (kLanes * 8 + l.slot_words * 2);
     return l;
 }
@@ -306,12 +313,15 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     ea.prefix = prefix ? prefix : phi.zero;          // kernels read a prefix unconditionally
     ea.tn = tn;
     ea.tw = tw;
-    ea.phi = phi;
+    ea.table = reinterpret_cast<const uint32_t*>(ws + l.table);
     ea.slots = reinterpret_cast<uint16_t*>(ws + l.slots);
     ea.slot_words = l.slot_words;
     ea.states = reinterpret_cast<unsigned long long*>(ws + l.states);
     ea.chunk_words = reinterpret_cast<uint32_t*>(ws + l.chunk_words);
     ea.ctl = ctl;
+    if ((e = kvc::launch_coder_tables(phi, tn, tw, reinterpret_cast<uint32_t*>(ws + l.table), nullptr, s)) !=
+        hipSuccess)
+        return KVC_ERR_DEVICE;
     if ((e = kvc::launch_encode(ea, p->kv_dtype, p->mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(2);
 
@@ -358,7 +368,7 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
                void* stream, kvc_decode_info* h_info) {
     if (!d_in || !d_mu || !d_sigma || !d_kv_out || !d_workspace) return KVC_ERR_INVALID;
     if (workspace_bytes < KVC_DECODE_WORKSPACE_BYTES) return KVC_ERR_CAPACITY;
-    if (!aligned(d_in, 8) || !aligned(d_workspace, 8) || !aligned(d_sigma, 4) || !aligned(d_prefix, 4) ||
+    if (!aligned(d_in, 8) || !aligned(d_workspace, 256) || !aligned(d_sigma, 4) || !aligned(d_prefix, 4) ||
         !aligned(d_kv_out, 2) || !aligned(d_mu, 2))
         return KVC_ERR_INVALID;
     if (in_bytes < KVC_HEADER_BYTES) return KVC_ERR_CORRUPT;
@@ -402,6 +412,10 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     if ((e = kvc::launch_escape_buckets(prefix ? prefix : phi.zero, n_sym, shift, n_buckets, buckets, s)) !=
         hipSuccess)
         return KVC_ERR_DEVICE;
+    uint8_t* ws = static_cast<uint8_t*>(d_workspace);
+    if ((e = kvc::launch_coder_tables(phi, tn, tw, reinterpret_cast<uint32_t*>(ws + kDecodeTableOffset),
+                                      reinterpret_cast<float*>(ws + kDecodeAimOffset), s)) != hipSuccess)
+        return KVC_ERR_DEVICE;
     timer.mark(1);
     const uint8_t* in = static_cast<const uint8_t*>(d_in);
     kvc::DecodeArgs da;
@@ -414,7 +428,8 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     da.prefix = prefix ? prefix : phi.zero;
     da.tn = tn;
     da.tw = tw;
-    da.phi = phi;
+    da.table = reinterpret_cast<const uint32_t*>(ws + kDecodeTableOffset);
+    da.aim = reinterpret_cast<const float*>(ws + kDecodeAimOffset);
     da.buckets = buckets;
     da.bucket_shift = shift;
     da.kv_out = d_kv_out;

@@ -43,6 +43,14 @@ struct PhiTables {
     const uint32_t* zero;               // 65,537 zeros: the escape prefix of a model without one
 };
 
+// Per-call coder tables in global memory (launch_coder_tables), copied into
+// LDS by every workgroup of the coding kernels: the mixture table (12,290
+// words, padded to 12,292) and the decoder's aim table (float pairs).
+constexpr uint32_t kTableWordsPadded = 12292;
+constexpr uint64_t kTableBytes = 4ull * kTableWordsPadded;
+constexpr uint32_t kAimFloats = 2 * 1986;          // 1985 pairs and a zero pair
+constexpr uint64_t kAimBytes = 4ull * kAimFloats;
+
 struct EncodeArgs {
     ChunkGeom geom;
     const void* kv;
@@ -50,7 +58,7 @@ struct EncodeArgs {
     const float* sigma;
     const uint32_t* prefix;             // escape prefix; the zero table when there is no escape part
     uint32_t tn, tw;
-    PhiTables phi;
+    const uint32_t* table;              // the mixture table (launch_coder_tables)
     uint16_t* slots;                    // per-chunk word slots, filled from the end
     uint64_t slot_words;                // words per slot (2 per scalar, multiple of 4)
     unsigned long long* states;         // [n_chunks][64] final states
@@ -83,7 +91,8 @@ struct DecodeArgs {
     const float* sigma;
     const uint32_t* prefix;
     uint32_t tn, tw;
-    PhiTables phi;
+    const uint32_t* table;              // the mixture table (launch_coder_tables)
+    const float* aim;                   // the aim table, kAimFloats floats
     const uint16_t* buckets;            // escape bucket table (launch_escape_buckets)
     uint32_t bucket_shift;
     void* kv_out;
@@ -108,6 +117,10 @@ PhiTables device_phi_tables(hipError_t* err);
 void host_phi_tables(uint32_t* a, uint32_t* b);   // kPhiPoints entries each
 
 hipError_t launch_clear_control(Control* ctl, hipStream_t s);
+// The mixture table for budgets (tn, tw) into `table` (kTableBytes) and,
+// when `aim` is not null, the decoder's aim table (kAimBytes).
+hipError_t launch_coder_tables(const PhiTables& phi, uint32_t tn, uint32_t tw, uint32_t* table, float* aim,
+                               hipStream_t s);
 hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t* prefix,
                             uint64_t n_prefix, Control* ctl, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);

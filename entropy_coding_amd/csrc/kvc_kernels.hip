@@ -92,6 +92,15 @@ __device__ __forceinline__ void build_table_lds(uint32_t* s_tab, const PhiTables
     __syncthreads();
 }
 
+// Copy of a per-call table from global memory into LDS, 16 bytes per
+// thread and step (n16 = bytes / 16); ends with a barrier.
+__device__ __forceinline__ void copy_to_lds(void* dst, const void* __restrict__ src, uint32_t n16) {
+    uint4* d = static_cast<uint4*>(dst);
+    const uint4* __restrict__ q = static_cast<const uint4*>(src);
+    for (uint32_t k = threadIdx.x; k < n16; k += blockDim.x) d[k] = q[k];
+    __syncthreads();
+}
+
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;
@@ -313,10 +322,10 @@ __device__ __forceinline__ void encode_batch(int t, PushState& st, const typenam
 
 template <int KV, int MU>
 __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
-    __shared__ uint32_t s_tab[kTableEntries];
+    __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
     __shared__ uint32_t s_small[KV == kE4M3 ? kE4Words : 1];
     if constexpr (KV == kE4M3) build_e4_lds(s_small, a.prefix);
-    build_table_lds(s_tab, a.phi, a.tn, a.tw);
+    copy_to_lds(s_tab, a.table, static_cast<uint32_t>(kTableBytes / 16));
 
     const uint32_t lane = threadIdx.x & 63u;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -537,6 +546,33 @@ __device__ __forceinline__ void build_aim_lds(float2* s_aim, const uint32_t* s_t
         s_aim[j] = make_float2(static_cast<float>(z0 - k * d0), static_cast<float>(k));
     }
     __syncthreads();
+}
+
+static_assert(kTableEntries <= static_cast<int>(kTableWordsPadded) && kTableWordsPadded % 4 == 0, "table padding");
+static_assert(2 * (kAimEntries + 1) == static_cast<int>(kAimFloats) && kAimFloats % 4 == 0, "aim table size");
+
+// One workgroup: the mixture table for (tn, tw), padded with its last
+// entry, and (when aim is given) the aim table built from it, plus one
+// zero pair that pads it to 16 bytes.
+__global__ void __launch_bounds__(1024) k_coder_tables(PhiTables phi, uint32_t tn, uint32_t tw,
+                                                       uint32_t* __restrict__ table, float* __restrict__ aim) {
+    __shared__ uint32_t s_tab[kTableEntries];
+    __shared__ float2 s_aim[kAimEntries];
+    build_table_lds(s_tab, phi, tn, tw);
+    for (int k = threadIdx.x; k < static_cast<int>(kTableWordsPadded); k += blockDim.x)
+        table[k] = s_tab[k < kTableEntries ? k : kTableEntries - 1];
+    if (aim == nullptr) return;
+    build_aim_lds(s_aim, s_tab);
+    for (int k = threadIdx.x; k <= kAimEntries; k += blockDim.x) {
+        aim[2 * k] = k < kAimEntries ? s_aim[k].x : 0.0f;
+        aim[2 * k + 1] = k < kAimEntries ? s_aim[k].y : 0.0f;
+    }
+}
+
+hipError_t launch_coder_tables(const PhiTables& phi, uint32_t tn, uint32_t tw, uint32_t* table, float* aim,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(k_coder_tables, dim3(1), dim3(1024), 0, s, phi, tn, tw, table, aim);
+    return hipGetLastError();
 }
 
 // z where the mixture table reaches t (t < htot), from the distance to the
@@ -840,14 +876,14 @@ struct WordRing {
 
 template <int KV, int MU>
 __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(64))) k_decode(DecodeArgs a) {
-    __shared__ uint32_t s_tab[kTableEntries];
-    __shared__ float2 s_aim[kAimEntries];
+    __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
+    __shared__ __align__(16) float2 s_aim[kAimEntries + 1];
     __shared__ uint32_t s_ring[kDecodeBlock / 64][kRingDwords];
     __shared__ uint32_t s_small[KV == kE4M3 ? kE4Words : 1];
     if constexpr (KV == kE4M3) build_e4_lds(s_small, a.prefix);      // exact prefix + edges
-    build_table_lds(s_tab, a.phi, a.tn, a.tw);
+    copy_to_lds(s_tab, a.table, static_cast<uint32_t>(kTableBytes / 16));
+    copy_to_lds(s_aim, a.aim, static_cast<uint32_t>(kAimBytes / 16));
     const uint32_t htot = a.tn + a.tw;
-    build_aim_lds(s_aim, s_tab);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -956,6 +992,14 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
                 }
             }
         }
+        // the symbol is final: store it now, so that the store is issued
+        // after this step's prefix read and before the next one (the vector
+        // memory counter is in order, so a store issued later would hold up
+        // the wait for the next step's prefix read until it completes)
+        const uint32_t ooff = t * D * static_cast<uint32_t>(sizeof(KB));
+        if constexpr (KV == kBF16)
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(candidate_bits<KV>(kb)), outb, kv_lane, ooff, 0);
+        else __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(kb), outb, kv_lane, ooff, 0);
         // x = f (x >> 31) + rank, f = f_G + 1 + (prefix[s + 1] - prefix[s]);
         // x < 2^63, so x >> 31 fits 32 bits
         const uint32_t f = (c.g1 - c.g0) + 1u + (c.p1 - c.p0);
@@ -984,10 +1028,6 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         }
         x = (static_cast<unsigned long long>(xh) << 32) | xl;
         win.advance(rp, static_cast<uint32_t>(lane));
-        const uint32_t ooff = t * D * static_cast<uint32_t>(sizeof(KB));
-        if constexpr (KV == kBF16)
-            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(candidate_bits<KV>(kb)), outb, kv_lane, ooff, 0);
-        else __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(kb), outb, kv_lane, ooff, 0);
     };
     // predictor-mean rows as raw bits (the last row stands in for rows past
     // the chunk's end, which are not decoded; the buffer does not

@@ -54,7 +54,7 @@ typedef enum kvc_status {
 enum { KVC_BF16 = 0, KVC_E4M3 = 1, KVC_F32 = 2 };   /* E4M3 = OCP float8 e4m3fn */
 
 #define KVC_HEADER_BYTES 128
-#define KVC_DECODE_WORKSPACE_BYTES 131584   /* control block + escape bucket table */
+#define KVC_DECODE_WORKSPACE_BYTES 262144   /* control block, escape bucket table, coder tables */
 #define KVC_ESTIMATE_WORKSPACE_BYTES 256
 #define KVC_ENCODE_STAGES 4
 #define KVC_DECODE_STAGES 2
@@ -154,7 +154,7 @@ int kvc_stream_info(const void* h_header, uint64_t header_bytes, kvc_params* h_p
  * KVC_ERR_CORRUPT if the stream is malformed, truncated or damaged (every
  * lane must start from a state in [2^47, 2^63), end in the initial state
  * and consume exactly its chunk).
- * Workspace: KVC_DECODE_WORKSPACE_BYTES.  Synchronises `stream` twice
+ * Workspace: KVC_DECODE_WORKSPACE_BYTES, 256-byte aligned.  Synchronises `stream` twice
  * (header read, status read).  h_info: NULL, or receives the stage times
  * and the number of symbols the aim did not find.
  */
