@@ -23,12 +23,12 @@ constexpr uint32_t kLanes = 64;
 constexpr uint32_t kVersion = 3;   // stream format version (split slot ranges, floor of z * 2^24)
 constexpr uint32_t kMaxChunkTokens = 1u << 20;
 constexpr int64_t kMaxScalars = int64_t(1) << 40;
-// decode workspace: control block, the escape bucket table (u16), the
+// decode workspace: control block, the escape bucket table (u32), the
 // mixture table and the aim table
 constexpr uint64_t kDecodeBucketOffset = 256;
-constexpr uint64_t kDecodeTableOffset = 131584;
+constexpr uint64_t kDecodeTableOffset = 262656;
 constexpr uint64_t kDecodeAimOffset = kDecodeTableOffset + 49408;
-static_assert(kDecodeBucketOffset + 2 * kvc::kEscapeBucketsMax <= kDecodeTableOffset &&
+static_assert(kDecodeBucketOffset + 4 * kvc::kEscapeBucketsMax <= kDecodeTableOffset &&
                   kDecodeTableOffset + kvc::kTableBytes <= kDecodeAimOffset &&
                   kDecodeAimOffset + kvc::kAimBytes <= KVC_DECODE_WORKSPACE_BYTES,
               "decode workspace layout");
@@ -402,14 +402,14 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     uint32_t shift = 0;
     while (((q_total - 1) >> shift) + 2 > kvc::kEscapeBucketsMax) ++shift;
     const uint32_t n_buckets = static_cast<uint32_t>(((q_total - 1) >> shift) + 2);
-    uint16_t* buckets = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(d_workspace) + kDecodeBucketOffset);
+    uint32_t* buckets = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d_workspace) + kDecodeBucketOffset);
     StageTimer timer(h_info ? h_info->stage_ms : nullptr, KVC_DECODE_STAGES, s);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(0);
     if ((e = kvc::launch_side_hash(d_sigma, uint64_t(g.planes) * uint64_t(g.channels), prefix,
                                    prefix ? n_sym + 1u : 0u, ctl, s)) != hipSuccess)
         return KVC_ERR_DEVICE;
-    if ((e = kvc::launch_escape_buckets(prefix ? prefix : phi.zero, n_sym, shift, n_buckets, buckets, s)) !=
+    if ((e = kvc::launch_escape_buckets(prefix ? prefix : phi.zero, n_sym, shift, n_buckets, p.kv_dtype, buckets, s)) !=
         hipSuccess)
         return KVC_ERR_DEVICE;
     uint8_t* ws = static_cast<uint8_t*>(d_workspace);

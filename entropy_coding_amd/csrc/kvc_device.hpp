@@ -158,14 +158,22 @@ struct Model {
     const uint32_t* __restrict__ tab;      // mixture table in LDS
     const uint32_t* __restrict__ prefix;   // escape prefix (N + 1 entries; zeros without an escape part)
     const uint32_t* small;                 // e4m3 only: prefix and edges in LDS
-    __amdgpu_buffer_rsrc_t pre;            // the escape prefix as a buffer
 };
 
-// prefix[s] and prefix[s + 1] in one 8-byte read
+// Two consecutive u32 at byte offset `off` of `base` in one 8-byte read
+// (4-byte aligned), addressed as a scalar base plus a 32-bit lane offset.
+struct alignas(4) U32Pair {
+    uint32_t a, b;
+};
+__device__ __forceinline__ U32Pair load_pair(const uint32_t* base, uint32_t off) {
+    return *reinterpret_cast<const U32Pair*>(reinterpret_cast<const char*>(base) + off);
+}
+
+// prefix[s] and prefix[s + 1] (s < N)
 __device__ __forceinline__ void prefix_pair(const Model& m, uint32_t s, uint32_t& p0, uint32_t& p1) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(m.pre, s << 2, 0, 0);
-    p0 = v[0];
-    p1 = v[1];
+    const U32Pair v = load_pair(m.prefix, s << 2);
+    p0 = v.a;
+    p1 = v.b;
 }
 
 // C(b) = b + h_fx(q(b)) + prefix[b].

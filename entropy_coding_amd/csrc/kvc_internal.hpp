@@ -93,7 +93,7 @@ struct DecodeArgs {
     uint32_t tn, tw;
     const uint32_t* table;              // the mixture table (launch_coder_tables)
     const float* aim;                   // the aim table, kAimFloats floats
-    const uint16_t* buckets;            // escape bucket table (launch_escape_buckets)
+    const uint32_t* buckets;            // escape bucket table (launch_escape_buckets)
     uint32_t bucket_shift;
     void* kv_out;
     Control* ctl;
@@ -129,10 +129,11 @@ hipError_t launch_scan(const uint32_t* chunk_words, int64_t n_chunks,
 hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);
 // Bucket table of Q(b) = b + prefix[b] for the decoder's floor-and-escape
-// lookup: bucket[j] = largest s < n_sym with Q(s) <= j << shift.
+// lookup: entry j = (s_j << 16) | pattern of s_j, where s_j is the largest
+// s < n_sym with Q(s) <= j << shift (entries order as their symbols).
 constexpr uint32_t kEscapeBucketsMax = 65538;
 hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_t shift, uint32_t n_entries,
-                                 uint16_t* bucket, hipStream_t s);
+                                 int kv_dtype, uint32_t* bucket, hipStream_t s);
 // sigma calibration: float64 partial sums per (split, plane, channel)
 struct CalibPart {
     double sum;

@@ -340,7 +340,7 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
         if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
         inv24 = 16777216.0f;
     }
-    const Model m{s_tab, a.prefix, s_small, buffer_rsrc(a.prefix, (Alphabet<KV>::kSize + 1u) * 4u)};
+    const Model m{s_tab, a.prefix, s_small};
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
@@ -510,7 +510,7 @@ hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream
 // aim, only the cost of finding it.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeBlock = 1024;
-constexpr int kDecodeBatch = 4;
+constexpr int kDecodeBatch = 8;
 
 // Aim table: z(d), the position at which the interpolated mixture table
 // reaches d, is linear between the knots d_j = 2^(j >> 6) (1 + (j & 63) / 64);
@@ -776,14 +776,17 @@ __device__ __forceinline__ uint32_t coop_gauss(bool need, uint32_t target, float
     return s_out;
 }
 
-// Bucket table of the static part Q(b) = b + prefix[b] of the CDF:
-// bucket[j] = the largest s < N with Q(s) <= j * 2^shift.  A slot y in the
-// floor-and-escape range then has its symbol in [bucket[y >> shift],
-// bucket[(y >> shift) + 1]].  The shift is the smallest that keeps the
-// table within kEscapeBucketsMax entries.
+// Bucket table of the static part Q(b) = b + prefix[b] of the CDF: with
+// s_j the largest s < N with Q(s) <= j * 2^shift, entry j holds s_j in its
+// high 16 bits and s_j's bit pattern in its low 16 (so entries order as
+// their symbols, and an entry gives the decoder's candidate word of s_j
+// at once).  A slot y in the floor-and-escape range has its symbol in
+// [s_(y >> shift), s_((y >> shift) + 1)].  The shift is the smallest that
+// keeps the table within kEscapeBucketsMax entries.
+template <int KV>
 __global__ void __launch_bounds__(256) k_escape_buckets(const uint32_t* __restrict__ prefix, uint32_t n_sym,
                                                         uint32_t shift, uint32_t n_entries,
-                                                        uint16_t* __restrict__ bucket) {
+                                                        uint32_t* __restrict__ bucket) {
     const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= n_entries) return;
     const unsigned long long y = static_cast<unsigned long long>(j) << shift;
@@ -793,40 +796,60 @@ __global__ void __launch_bounds__(256) k_escape_buckets(const uint32_t* __restri
         if (static_cast<unsigned long long>(mid) + prefix[mid] <= y) lo = mid;
         else hi = mid - 1u;
     }
-    bucket[j] = static_cast<uint16_t>(lo);
+    bucket[j] = (lo << 16) | candidate_bits<KV>(candidate_of_index<KV>(lo));
 }
 
 hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_t shift, uint32_t n_entries,
-                                 uint16_t* bucket, hipStream_t s) {
-    hipLaunchKernelGGL(k_escape_buckets, dim3((n_entries + 255) / 256), dim3(256), 0, s, prefix, n_sym, shift,
-                       n_entries, bucket);
+                                 int kv_dtype, uint32_t* bucket, hipStream_t s) {
+    const dim3 grid((n_entries + 255) / 256), block(256);
+    if (kv_dtype == kBF16)
+        hipLaunchKernelGGL(k_escape_buckets<kBF16>, grid, block, 0, s, prefix, n_sym, shift, n_entries, bucket);
+    else hipLaunchKernelGGL(k_escape_buckets<kE4M3>, grid, block, 0, s, prefix, n_sym, shift, n_entries, bucket);
     return hipGetLastError();
 }
 
-// Symbol of the floor-and-escape slot y for every lane with `need` set:
-// the bucket table narrows it to [lo, hi], a per-lane binary search over
-// Q(b) = b + prefix[b] finishes it.  Indices stay in [0, N) whatever the
-// prefix holds.
+// The symbol of escape offset y within [lo, hi]: binary search for the
+// largest s with s + prefix[s] <= y.
 template <int KV>
-__device__ __forceinline__ uint32_t escape_symbol(bool need, uint32_t y, __amdgpu_buffer_rsrc_t bucket,
-                                                  uint32_t shift, const Model& m) {
-    uint32_t lo = 0, hi = 0;
-    if (need) {
-        const uint32_t j = y >> shift;
-        lo = __builtin_amdgcn_raw_buffer_load_b16(bucket, j << 1, 0, 0);
-        hi = __builtin_amdgcn_raw_buffer_load_b16(bucket, (j << 1) + 2u, 0, 0);
-    }
+__device__ __forceinline__ uint32_t escape_symbol(uint32_t lo, uint32_t hi, uint32_t y, const Model& m) {
     while (__ballot(lo < hi)) {
         if (lo < hi) {
             const uint32_t mid = (lo + hi + 1u) >> 1;
             uint32_t pm;
-            if constexpr (KV == kBF16) pm = __builtin_amdgcn_raw_buffer_load_b32(m.pre, mid << 2, 0, 0);
+            if constexpr (KV == kBF16)
+                pm = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(m.prefix) + (mid << 2));
             else pm = m.small[mid];
             if (mid + pm <= y) lo = mid;
             else hi = mid - 1u;
         }
     }
     return lo;
+}
+
+// Candidate word of the floor-and-escape slot y for every lane with `need`
+// set: the bucket table narrows the symbol to [lo, hi] and, when lo = hi,
+// gives the candidate word itself; a per-lane binary search over
+// Q(b) = b + prefix[b] finishes the rest.  Indices stay in [0, N) whatever
+// the prefix holds.
+template <int KV>
+__device__ __forceinline__ uint32_t escape_candidate(bool need, uint32_t y, const uint32_t* bucket, uint32_t shift,
+                                                     const Model& m) {
+    // entries j and j + 1 (j <= the last bucket but one) in one read; a
+    // lane without `need` keeps them equal.  Entries order as their symbols.
+    uint32_t e0 = 0, e1 = 0;
+    if (need) {
+        const U32Pair v = load_pair(bucket, (y >> shift) << 2);
+        e0 = v.a;
+        e1 = v.b;
+    }
+    if (__ballot(e0 < e1)) {
+        // a bucket that starts within a run of symbols: search it
+        const bool search = e0 < e1;
+        const uint32_t s = escape_symbol<KV>(e0 >> 16, e1 >> 16, y, m);
+        if (search) e0 = (s << 16) | candidate_bits<KV>(candidate_of_index<KV>(s));
+    }
+    if constexpr (KV == kBF16) return e0 << 16;
+    else return e0 & 0xFFFFu;
 }
 
 // Stream words of a chunk, staged through a per-wave LDS ring of two
@@ -919,9 +942,8 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         sg = 1.0f;
     }
     constexpr uint32_t kN = Alphabet<KV>::kSize;
-    const Model m{s_tab, a.prefix, s_small, buffer_rsrc(a.prefix, (kN + 1u) * 4u)};
+    const Model m{s_tab, a.prefix, s_small};
     const uint32_t geo = geo_offset(lane);
-    const __amdgpu_buffer_rsrc_t bucket = buffer_rsrc(a.buckets, kEscapeBucketsMax * 2u);
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
@@ -932,35 +954,59 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
     const __amdgpu_buffer_rsrc_t mub = buffer_rsrc(static_cast<const MT*>(a.mu) + row0, rows_bytes);
     const __amdgpu_buffer_rsrc_t outb =
         buffer_rsrc(static_cast<KB*>(a.kv_out) + row0, cp.len * D * static_cast<uint32_t>(sizeof(KB)));
+    const uint64_t out_base = reinterpret_cast<uint64_t>(static_cast<KB*>(a.kv_out) + row0);
     const uint32_t mu_lane = static_cast<uint32_t>(lane) * static_cast<uint32_t>(sizeof(MT));
     const uint32_t kv_lane = static_cast<uint32_t>(lane) * static_cast<uint32_t>(sizeof(KB));
 
     uint32_t rp = 0;
     unsigned long long misses = 0;                   // wave-uniform
 
-    // One symbol of every lane: row t of the chunk, predictor mean mu.
-    auto step = [&](uint32_t t, float mu) {
+    // predictor-mean rows as raw bits (the last row stands in for rows past
+    // the chunk's end, which are not decoded; the buffer does not
+    // range-check the row offset)
+    using MRaw = typename std::conditional<MU == kBF16, uint16_t, uint32_t>::type;
+    auto load_mu = [&](uint32_t t) -> MRaw {
+        const uint32_t roff = (t < cp.len ? t : cp.len - 1) * D * static_cast<uint32_t>(sizeof(MT));
+        if constexpr (MU == kBF16) return __builtin_amdgcn_raw_buffer_load_b16(mub, mu_lane, roff, 0);
+        else return __builtin_amdgcn_raw_buffer_load_b32(mub, mu_lane, roff, 0);
+    };
+    auto mu_of = [](MRaw r) -> float {
+        return MU == kBF16 ? __uint_as_float(static_cast<uint32_t>(r) << 16) : __uint_as_float(static_cast<uint32_t>(r));
+    };
+    MRaw nxt[kDecodeBatch];
+
+    // One symbol of every lane: row t of the chunk, predictor mean mu.  The
+    // first step of a batch loads the means of the next batch right after
+    // its prefix read: the vector memory counter is in order, so this step's
+    // wait for the prefix does not include them and the next step's does.
+    auto step = [&](uint32_t t, float mu, bool first) {
         const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
         // candidate: the cell the aim lands in, with its exact CDF terms
         uint32_t kb = nearest_candidate<KV>(__fmaf_rn(aim_z(target, htot, s_aim), sg, mu));
-        const uint64_t esc = __ballot(target >= htot);
+        const bool is_esc = target >= htot;
+        const uint64_t esc = __ballot(is_esc);
         if (esc) {
             // floor-and-escape slots: the symbol comes from the lookup
             misses += __popcll(esc);
-            const bool e = target >= htot;
-            const uint32_t se = escape_symbol<KV>(e, target - htot, bucket, a.bucket_shift, m);
-            if (e) kb = candidate_of_index<KV>(se);
+            const uint32_t ce = escape_candidate<KV>(is_esc, target - htot, a.buckets, a.bucket_shift, m);
+            if (is_esc) kb = ce;
         }
         Cell c = eval_cell<KV, MU>(kb, mu, inv24, m);
+        if (first) {
+            __asm__ volatile("" : : : "memory");
+#pragma unroll
+            for (int u = 0; u < kDecodeBatch; ++u) nxt[u] = load_mu(t + kDecodeBatch + u);
+        }
         if (esc) {
             // a floor-and-escape slot has rank f_G(s) + (y - Q(s)): the
             // symbol's slots are taken to start at T_n + T_w + Q(s) - f_G(s)
             // (G terms of Inf and NaN, whose edges are all infinite, set first)
-            if (target >= htot) {
+            if (is_esc) {
                 __asm__ volatile("");                    // keep this a branch (rarely taken)
                 if constexpr (KV == kBF16) {
                     const bool special = (kb & 0x7F800000u) == 0x7F800000u;    // Inf, NaN
                     if (__ballot(special)) {
+                        __asm__ volatile("");            // a branch: Inf and NaN are rare
                         if (special) c.g0 = c.g1 = (kb & 0x80000000u) ? 0u : htot;
                     }
                 }
@@ -969,7 +1015,8 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
                 c.g1 = c.g0 + fg;
             }
         }
-        uint64_t need = (__ballot(target < c.g0) | __ballot(target >= c.g1)) & ~esc;
+        // in the cell when target - G0 < G1 - G0 (unsigned: below G0 wraps)
+        uint64_t need = __ballot(target - c.g0 >= c.g1 - c.g0) & ~esc;
         if (need) {
             // Gaussian slots outside the aimed cell: one symbol towards the
             // target first (G(0) = 0 <= target < G(N) = htot), then the
@@ -979,7 +1026,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
             if (!hit) {
                 kb = candidate_of_index<KV>(target < c.g0 ? c.s - 1u : c.s + 1u);
                 c = eval_cell<KV, MU>(kb, mu, inv24, m);
-                hit = target >= c.g0 && target < c.g1;
+                hit = target - c.g0 < c.g1 - c.g0;
             }
             need = __ballot(!hit);
             if (need) {
@@ -998,7 +1045,12 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         // the wait for the next step's prefix read until it completes)
         const uint32_t ooff = t * D * static_cast<uint32_t>(sizeof(KB));
         if constexpr (KV == kBF16)
-            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(candidate_bits<KV>(kb)), outb, kv_lane, ooff, 0);
+        {
+            // the pattern is the high half of the candidate word: a high-half
+            // store from a scalar row address and the lane's offset
+            const uint64_t row = out_base + ooff;
+            __asm__ volatile("global_store_short_d16_hi %0, %1, %2" : : "v"(kv_lane), "v"(kb), "s"(row));
+        }
         else __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(kb), outb, kv_lane, ooff, 0);
         // x = f (x >> 31) + rank, f = f_G + 1 + (prefix[s + 1] - prefix[s]);
         // x < 2^63, so x >> 31 fits 32 bits
@@ -1029,32 +1081,17 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         x = (static_cast<unsigned long long>(xh) << 32) | xl;
         win.advance(rp, static_cast<uint32_t>(lane));
     };
-    // predictor-mean rows as raw bits (the last row stands in for rows past
-    // the chunk's end, which are not decoded; the buffer does not
-    // range-check the row offset)
-    using MRaw = typename std::conditional<MU == kBF16, uint16_t, uint32_t>::type;
-    auto load_mu = [&](uint32_t t) -> MRaw {
-        const uint32_t roff = (t < cp.len ? t : cp.len - 1) * D * static_cast<uint32_t>(sizeof(MT));
-        if constexpr (MU == kBF16) return __builtin_amdgcn_raw_buffer_load_b16(mub, mu_lane, roff, 0);
-        else return __builtin_amdgcn_raw_buffer_load_b32(mub, mu_lane, roff, 0);
-    };
-    auto mu_of = [](MRaw r) -> float {
-        return MU == kBF16 ? __uint_as_float(static_cast<uint32_t>(r) << 16) : __uint_as_float(static_cast<uint32_t>(r));
-    };
 
     // full batches: the means of the next batch are loaded while this one
     // decodes, so no HBM read sits on the serial chain; a non-finite mean
     // counts as 0
     const uint32_t full = cp.len - cp.len % kDecodeBatch;
-    MRaw nxt[kDecodeBatch];
 #pragma unroll
     for (int u = 0; u < kDecodeBatch; ++u) nxt[u] = load_mu(u);
     for (uint32_t t0 = 0; t0 < full; t0 += kDecodeBatch) {
         float mus[kDecodeBatch];
 #pragma unroll
         for (int u = 0; u < kDecodeBatch; ++u) mus[u] = mu_of(nxt[u]);
-#pragma unroll
-        for (int u = 0; u < kDecodeBatch; ++u) nxt[u] = load_mu(t0 + kDecodeBatch + u);
         uint64_t odd = 0;
 #pragma unroll
         for (int u = 0; u < kDecodeBatch; ++u) odd |= __ballot(!__builtin_isfinite(mus[u]));
@@ -1063,11 +1100,11 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
             for (int u = 0; u < kDecodeBatch; ++u) mus[u] = __builtin_isfinite(mus[u]) ? mus[u] : 0.0f;
         }
 #pragma unroll
-        for (int u = 0; u < kDecodeBatch; ++u) step(t0 + u, mus[u]);
+        for (int u = 0; u < kDecodeBatch; ++u) step(t0 + u, mus[u], u == 0);
     }
     for (uint32_t t = full; t < cp.len; ++t) {
         const float mu = mu_of(load_mu(t));
-        step(t, __builtin_isfinite(mu) ? mu : 0.0f);
+        step(t, __builtin_isfinite(mu) ? mu : 0.0f, false);
     }
     // every lane back at the initial state, the payload consumed exactly,
     // the padding zero
@@ -1318,7 +1355,7 @@ __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
     using MT = typename MuT<MU>::T;
     const KB* __restrict__ kv = static_cast<const KB*>(a.kv);
     const MT* __restrict__ mup = static_cast<const MT*>(a.mu);
-    const Model model{s_tab, a.prefix, nullptr, buffer_rsrc(a.prefix, (Alphabet<KV>::kSize + 1u) * 4u)};
+    const Model model{s_tab, a.prefix, nullptr};
     const int64_t D = a.geom.channels, T = a.geom.tokens;
     const int64_t n = a.geom.planes * T * D;
     const double wn = a.w_narrow_bp / 1e4, ww = a.w_wide_bp / 1e4, we = 1.0 - wn - ww;
@@ -1376,7 +1413,7 @@ __global__ void __launch_bounds__(256) k_cdf_table(const void* mu_, const float*
     build_table_lds(s_tab, phi, tn, tw);
     using MT = typename MuT<MU>::T;
     constexpr uint32_t N1 = Alphabet<KV>::kSize + 1;
-    const Model model{s_tab, prefix, nullptr, buffer_rsrc(prefix, (Alphabet<KV>::kSize + 1u) * 4u)};
+    const Model model{s_tab, prefix, nullptr};
     const int64_t total = pairs * N1;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {

@@ -54,7 +54,7 @@ typedef enum kvc_status {
 enum { KVC_BF16 = 0, KVC_E4M3 = 1, KVC_F32 = 2 };   /* E4M3 = OCP float8 e4m3fn */
 
 #define KVC_HEADER_BYTES 128
-#define KVC_DECODE_WORKSPACE_BYTES 262144   /* control block, escape bucket table, coder tables */
+#define KVC_DECODE_WORKSPACE_BYTES 393216   /* control block, escape bucket table, coder tables */
 #define KVC_ESTIMATE_WORKSPACE_BYTES 256
 #define KVC_ENCODE_STAGES 4
 #define KVC_DECODE_STAGES 2

@@ -29,6 +29,15 @@ def test_every_declared_call_is_exported(kvc):
     assert sorted(kvc.EXPORTS) == names
 
 
+def test_binding_constants_match_header(kvc):
+    with open(os.path.join(ROOT, "include", "kvc.h")) as f:
+        text = f.read()
+    ws = int(re.search(r"#define KVC_DECODE_WORKSPACE_BYTES (\d+)", text).group(1))
+    hb = int(re.search(r"#define KVC_HEADER_BYTES (\d+)", text).group(1))
+    assert kvc.DECODE_WORKSPACE_BYTES == ws and ws % 256 == 0
+    assert kvc.HEADER_BYTES == hb
+
+
 def test_version_and_status_strings(kvc):
     assert kvc.kvc_version() == O.VERSION == 3
     assert kvc.kvc_status_string(0) == "ok"
