@@ -20,6 +20,11 @@ follow it in order.  Everything is written for clarity, not speed: NumPy
 vectorises over coder lanes, Python loops over token steps.  Floating point is
 used only where KVC-1 prescribes IEEE float32 steps (S-3); everything after is
 exact integer arithmetic.
+
+Position-aware sigma ([blog] § limitations and future directions: a static
+per-channel sigma ignores how the residual varies with position; [wiki] §
+future directions: better residual models) is the optional S-11: sigma per
+(plane, block of B tokens, channel) instead of per (plane, channel).
 """
 
 from __future__ import annotations
@@ -36,7 +41,7 @@ __all__ = [
     "gauss_cum", "escape_cum",
     "cdf_table", "build_marginal", "calibrate_sigma", "side_hash", "encode",
     "decode", "parse_header", "model_bits_int", "model_bits_float",
-    "chunk_layout",
+    "chunk_layout", "sigma_blocks",
 ]
 
 # ---------------------------------------------------------------------------
@@ -298,6 +303,35 @@ def _inv_sigma(sigma) -> np.ndarray:
     return (np.float32(1.0) / s).astype(np.float32)
 
 
+def sigma_blocks(sigma, tokens: int, sigma_block_tokens: int = 0):
+    """S-11  sigma as [G, n_blocks, D] and the block length in tokens.
+
+    sigma_block_tokens = 0: one sigma per (plane, channel), sigma [G, D], one
+    block covering every token.  B > 0: sigma [G, ceil(T / B), D]; token t
+    of plane g, channel d uses sigma[g, t // B, d].  Reading ([blog] §
+    limitations and future directions name position-aware sigma without a
+    form): blocks of B consecutive tokens, the plainest position dependence
+    that stays per (kv, head, channel)."""
+    sg = np.asarray(sigma, dtype=np.float32)
+    if sigma_block_tokens == 0:
+        if sg.ndim != 2:
+            raise ValueError("sigma must be [planes, channels] without sigma blocks")
+        return sg[:, None, :], max(int(tokens), 1)
+    nb = -(-int(tokens) // int(sigma_block_tokens))
+    if sg.ndim != 3 or sg.shape[1] != nb:
+        raise ValueError("sigma must be [planes, ceil(tokens / B), channels]")
+    return sg, int(sigma_block_tokens)
+
+
+def _check_sigma_blocks(tokens: int, chunk_tokens: int, sigma_block_tokens: int) -> None:
+    """A chunk must see one sigma: B is a multiple of the chunk length, or a
+    single block covers every token."""
+    if sigma_block_tokens < 0:
+        raise ValueError("sigma_block_tokens must be >= 0")
+    if sigma_block_tokens and sigma_block_tokens < tokens and sigma_block_tokens % chunk_tokens:
+        raise ValueError("sigma_block_tokens must be a multiple of chunk_tokens")
+
+
 def cdf_table(mu, sigma, dtype: int, mu_dtype: int, w_narrow_bp: int,
               w_wide_bp: int, prefix=None) -> np.ndarray:
     """C(b) for every b = 0..N, for each (mu, sigma) pair: shape [P, N+1]."""
@@ -349,8 +383,12 @@ def _values_f64(x, dtype: int) -> np.ndarray:
     raise ValueError(dtype)
 
 
-def calibrate_sigma(kv, mu, kv_dtype: int, mu_dtype: int, sigma_floor: float) -> np.ndarray:
+def calibrate_sigma(kv, mu, kv_dtype: int, mu_dtype: int, sigma_floor: float,
+                    block_tokens: int = 0) -> np.ndarray:
     """sigma[p, d] = max(floor, sqrt(mean over reps and tokens of (kv - mu)^2)).
+
+    With block_tokens = B > 0 (S-11), sigma[p, j, d] takes the mean over reps
+    and the tokens [jB, min((j+1)B, T)) only.
 
     Inputs are [reps, planes, tokens, channels].  sigma^2 is the mean squared
     residual about mu: it minimises the expected Gaussian cost, spread plus
@@ -367,12 +405,17 @@ def calibrate_sigma(kv, mu, kv_dtype: int, mu_dtype: int, sigma_floor: float) ->
     with np.errstate(invalid="ignore", over="ignore"):
         r2 = (k - m) ** 2
     ok = np.isfinite(r2)                  # non-finite residuals are skipped
-    used = ok.sum(axis=(0, 2))
-    total = np.where(ok, r2, 0.0).sum(axis=(0, 2))
+    r2 = np.where(ok, r2, 0.0)
+    t_len = r2.shape[2]
+    bounds = [(0, t_len)] if block_tokens == 0 else \
+        [(j, min(j + block_tokens, t_len)) for j in range(0, t_len, block_tokens)]
+    used = np.stack([ok[:, :, a:b].sum(axis=(0, 2)) for a, b in bounds], axis=1)
+    total = np.stack([r2[:, :, a:b].sum(axis=(0, 2)) for a, b in bounds], axis=1)
     with np.errstate(invalid="ignore", divide="ignore"):
         s = np.sqrt(total / used).astype(np.float32)
     fl = np.float32(sigma_floor)
-    return np.where((used > 0) & np.isfinite(s) & (s > fl), s, fl).astype(np.float32)
+    out = np.where((used > 0) & np.isfinite(s) & (s > fl), s, fl).astype(np.float32)
+    return out[:, 0, :] if block_tokens == 0 else out
 
 
 # ---------------------------------------------------------------------------
@@ -423,29 +466,33 @@ def chunk_layout(planes: int, tokens: int, channels: int, chunk_tokens: int):
     return g, tc, k, length
 
 
+_HEADER_FMT = "<4sHHBBBBBBHIIIIIIQQQQQQI"
+
+
 def _header(kv_dtype, mu_dtype, w_n, w_w, chunk_tokens, planes, tokens, channels,
-            n_chunks, payload_bytes, shash) -> bytes:
+            n_chunks, payload_bytes, shash, sigma_block_tokens=0) -> bytes:
     t_n, t_w, t_e = budgets(kv_dtype, w_n, w_w)
     h = struct.pack(
-        "<4sHHBBBBBBHIIIIIIQQQQQQ",
+        _HEADER_FMT,
         MAGIC, VERSION, HEADER_BYTES, kv_dtype, mu_dtype, LOG2_M, LOG2_L,
         WORD_BITS, LANES, 0, w_n, w_w, t_n, t_w, t_e, chunk_tokens,
-        planes, tokens, channels, n_chunks, payload_bytes, shash)
+        planes, tokens, channels, n_chunks, payload_bytes, shash, sigma_block_tokens)
     return h + bytes(HEADER_BYTES - len(h))
 
 
 def parse_header(stream: bytes) -> dict:
     if len(stream) < HEADER_BYTES:
         raise StreamError("stream shorter than its header")
-    f = struct.unpack_from("<4sHHBBBBBBHIIIIIIQQQQQQ", stream, 0)
+    f = struct.unpack_from(_HEADER_FMT, stream, 0)
     keys = ["magic", "version", "header_bytes", "kv_dtype", "mu_dtype", "log2_m",
             "log2_l", "word_bits", "lanes", "reserved", "w_narrow_bp", "w_wide_bp",
             "t_n", "t_w", "t_e", "chunk_tokens", "planes", "tokens", "channels",
-            "n_chunks", "payload_bytes", "side_hash"]
+            "n_chunks", "payload_bytes", "side_hash", "sigma_block_tokens"]
     h = dict(zip(keys, f))
     if h["magic"] != MAGIC or h["version"] != VERSION or h["header_bytes"] != HEADER_BYTES:
         raise StreamError("bad magic/version")
-    if (h["log2_m"], h["log2_l"], h["word_bits"], h["lanes"]) != (LOG2_M, LOG2_L, WORD_BITS, LANES):
+    if (h["log2_m"], h["log2_l"], h["word_bits"], h["lanes"]) != (LOG2_M, LOG2_L, WORD_BITS, LANES) \
+            or h["reserved"] != 0 or any(stream[struct.calcsize(_HEADER_FMT):HEADER_BYTES]):
         raise StreamError("unsupported coder parameters")
     if h["kv_dtype"] not in (BF16, E4M3) or h["mu_dtype"] not in (BF16, F32):
         raise StreamError("bad dtype")
@@ -461,6 +508,10 @@ def parse_header(stream: bytes) -> dict:
     n_tc = -(-h["tokens"] // h["chunk_tokens"])
     if h["n_chunks"] != h["planes"] * n_tc * (h["channels"] // LANES):
         raise StreamError("chunk count does not match shape")
+    try:
+        _check_sigma_blocks(h["tokens"], h["chunk_tokens"], h["sigma_block_tokens"])
+    except ValueError as e:
+        raise StreamError(str(e)) from None
     return h
 
 
@@ -469,9 +520,11 @@ def _roundup8(x):
 
 
 def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int,
-           w_wide_bp: int, chunk_tokens: int, batch_chunks: int = 2048) -> bytes:
+           w_wide_bp: int, chunk_tokens: int, batch_chunks: int = 2048,
+           sigma_block_tokens: int = 0) -> bytes:
     """Code kv [G, T, D] (raw bit patterns) under the mixture around mu [G, T, D]
-    with sigma [G, D]; return the KVC-1 byte stream.
+    with sigma [G, D] (or, with sigma_block_tokens = B > 0, sigma
+    [G, ceil(T / B), D]: S-11); return the KVC-1 byte stream.
 
     Per chunk and lane, tokens are coded last to first so that the decoder
     runs first to last (rANS is last-in first-out).  Before a symbol with
@@ -493,12 +546,14 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
         raise ValueError("channels must be a positive multiple of 64")
     if chunk_tokens < 1:
         raise ValueError("chunk_tokens must be >= 1")
+    _check_sigma_blocks(t_len, chunk_tokens, sigma_block_tokens)
     t_n, t_w, t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)
     if t_e and prefix is None:
         raise ValueError("mixture with an escape part needs the marginal prefix")
     pref = prefix if t_e else None
     mu32_all = mu_to_f32(mu, mu_dtype)
-    inv_all = _inv_sigma(sigma)
+    sig3, blk = sigma_blocks(sigma, t_len, sigma_block_tokens)
+    inv_all = _inv_sigma(sig3)
     sym_all = order_index(kv, kv_dtype)
 
     g_of, tc_of, k_of, len_of = chunk_layout(g_n, t_len, d_n, chunk_tokens)
@@ -510,7 +565,7 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
         g, tcid, k, ln = g_of[sl], tc_of[sl], k_of[sl], len_of[sl]
         nb = g.size
         d = 64 * k[:, None] + lane[None, :]
-        inv = inv_all[g[:, None], d]
+        inv = inv_all[g[:, None], (tcid * chunk_tokens // blk)[:, None], d]
         x = np.full((nb, LANES), L, dtype=np.uint64)
         words = np.zeros((nb, chunk_tokens, 2, LANES), dtype=np.uint16)
         emit = np.zeros((nb, chunk_tokens, 2, LANES), dtype=bool)
@@ -546,7 +601,7 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
     directory = np.concatenate([[0], np.cumsum(sizes)]).astype("<u8")
     shash = side_hash(sigma, prefix if t_e else None)
     head = _header(kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp, chunk_tokens,
-                   g_n, t_len, d_n, n_chunks, int(directory[-1]), shash)
+                   g_n, t_len, d_n, n_chunks, int(directory[-1]), shash, sigma_block_tokens)
     return head + directory.tobytes() + b"".join(payloads)
 
 
@@ -589,7 +644,11 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
         raise StreamError("misaligned chunk")
 
     mu32_all = mu_to_f32(mu, mu_dtype)
-    inv_all = _inv_sigma(sigma)
+    try:
+        sig3, blk = sigma_blocks(sigma, t_len, h["sigma_block_tokens"])
+    except ValueError as e:
+        raise StreamError(str(e)) from None
+    inv_all = _inv_sigma(sig3)
     g_of, tc_of, k_of, len_of = chunk_layout(g_n, t_len, d_n, tcn)
     n_sym = alphabet_size(kv_dtype)
     steps = n_sym.bit_length() - 1
@@ -605,7 +664,7 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
         g, tcid, k, ln = g_of[cid], tc_of[cid], k_of[cid], len_of[cid]
         nb = cid.size
         d = 64 * k[:, None] + lane[None, :]
-        inv = inv_all[g[:, None], d]
+        inv = inv_all[g[:, None], (tcid * tcn // blk)[:, None], d]
         start_b = pay_off + directory[cid]
         size_b = directory[cid + 1] - directory[cid]
         x = np.stack([np.frombuffer(stream, dtype="<u8", count=LANES, offset=int(o)) for o in start_b]).astype(np.uint64)
@@ -691,13 +750,15 @@ def chunk_payload(stream: bytes, chunk_id: int) -> bytes:
 
 
 def encode_chunks(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
-                  chunk_tokens, chunk_ids):
+                  chunk_tokens, chunk_ids, sigma_block_tokens=0):
     """Payloads of selected chunks only (for sampled parity at full size).
 
-    Each chunk depends only on its own slice of kv and mu and on its plane's
-    sigma, so it is coded by running :func:`encode` on a one-plane view."""
+    Each chunk depends only on its own slice of kv and mu and on the sigma
+    its tokens use, so it is coded by running :func:`encode` on a one-plane
+    view."""
     kv = np.asarray(kv)
     g_n, t_len, d_n = kv.shape
+    sig3, blk = sigma_blocks(sigma, t_len, sigma_block_tokens)
     g_of, tc_of, k_of, len_of = chunk_layout(g_n, t_len, d_n, chunk_tokens)
     out = {}
     for cid in chunk_ids:
@@ -705,7 +766,7 @@ def encode_chunks(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide
         t0 = tc * chunk_tokens
         sub_kv = kv[g:g + 1, t0:t0 + ln, 64 * k:64 * k + 64]
         sub_mu = np.asarray(mu)[g:g + 1, t0:t0 + ln, 64 * k:64 * k + 64]
-        sub_sig = np.asarray(sigma, dtype=np.float32)[g:g + 1, 64 * k:64 * k + 64]
+        sub_sig = sig3[g:g + 1, t0 // blk, 64 * k:64 * k + 64]
         s = encode(sub_kv, sub_mu, sub_sig, prefix, kv_dtype, mu_dtype, w_narrow_bp,
                    w_wide_bp, chunk_tokens)
         out[int(cid)] = chunk_payload(s, 0)
@@ -731,14 +792,21 @@ __all__ += ["chunk_payload", "encode_chunks", "wrap_chunk"]
 # ---------------------------------------------------------------------------
 # bits per scalar: the integer model and the continuous mixture
 # ---------------------------------------------------------------------------
-def model_bits_int(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp) -> float:
+def sigma_per_token(sigma, tokens: int, sigma_block_tokens: int = 0) -> np.ndarray:
+    """sigma of every (plane, token, channel): [G, T, D] (S-11)."""
+    sig3, blk = sigma_blocks(sigma, tokens, sigma_block_tokens)
+    return np.repeat(sig3, blk, axis=1)[:, :tokens, :]
+
+
+def model_bits_int(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
+                   sigma_block_tokens: int = 0) -> float:
     """Mean of -log2(f(s) / M) over all scalars: the ideal code length of the
     integer model ([wiki] § core idea: bits = cross-entropy of q)."""
     kv = np.asarray(kv)
     g_n, t_len, d_n = kv.shape
     t_n, t_w, t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)
     pref = prefix if t_e else None
-    inv = np.broadcast_to(_inv_sigma(sigma)[:, None, :], kv.shape)
+    inv = _inv_sigma(sigma_per_token(sigma, t_len, sigma_block_tokens))
     mu32 = mu_to_f32(mu, mu_dtype)
     s = order_index(kv, kv_dtype)
     total = 0.0
@@ -758,7 +826,7 @@ def _ndtr_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 
 
 def model_bits_float(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
-                     cap_bits: float = 64.0) -> float:
+                     cap_bits: float = 64.0, sigma_block_tokens: int = 0) -> float:
     """Mean -log2 q(x) of the continuous mixture over the same cells, float64.
 
     q(x) = w_n [Phi((hi-mu)/sigma) - Phi((lo-mu)/sigma)]
@@ -771,7 +839,7 @@ def model_bits_float(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_w
     wn, ww = w_narrow_bp / 1e4, w_wide_bp / 1e4
     we = 1.0 - wn - ww
     pos = boundary_positions(kv_dtype).astype(np.float64)
-    sig = np.asarray(sigma, dtype=np.float32).astype(np.float64)
+    sig = sigma_per_token(sigma, kv.shape[1], sigma_block_tokens).astype(np.float64)
     mu_all = mu_to_f32(mu, mu_dtype).astype(np.float64)
     s = order_index(kv, kv_dtype)
     total = 0.0
@@ -779,7 +847,7 @@ def model_bits_float(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_w
         lo = pos[s[g]]
         hi = pos[s[g] + 1]
         m = mu_all[g]
-        sg = sig[g][None, :]
+        sg = sig[g]
         with np.errstate(invalid="ignore"):
             a1, b1 = (lo - m) / sg, (hi - m) / sg
             a3, b3 = (lo - m) / (3 * sg), (hi - m) / (3 * sg)
