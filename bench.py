@@ -122,7 +122,7 @@ def cpu_baseline(workload, planes_per_worker: int, tokens: int):
 # ---------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------
-def prepare(workload, dev, calib_reps: int):
+def prepare(workload, dev, calib_reps: int, sigma_block: int = 0):
     import torch
     from entropy_coding_amd import kvc
     from entropy_coding_amd import workloads as W
@@ -131,7 +131,9 @@ def prepare(workload, dev, calib_reps: int):
     G, T, D = w.planes, w.tokens, w.channels
     kv = torch.empty((G, T, D), dtype=torch.bfloat16 if w.kv_dtype == W.BF16 else torch.uint8, device=dev)
     mu = torch.empty((G, T, D), dtype=torch.bfloat16 if w.mu_dtype == W.BF16 else torch.float32, device=dev)
-    sigma = torch.empty((G, D), dtype=torch.float32, device=dev)
+    if sigma_block and w.calib_tokens < T:
+        raise SystemExit("sigma blocks need calibration data over every position (calib_tokens = tokens)")
+    sigma = torch.empty(kvc.sigma_shape(G, T, D, sigma_block), dtype=torch.float32, device=dev)
     ppl = w.planes_per_layer
     t0 = time.perf_counter()
     for l in range(w.layers):
@@ -140,7 +142,7 @@ def prepare(workload, dev, calib_reps: int):
         mu[l * ppl:(l + 1) * ppl] = m_l
         del k_l, m_l
         ck, cm = W.layer_calibration(w, l, reps=calib_reps, device=dev)
-        s_kvh = kvc.kvc_calibrate_sigma(ck, cm)
+        s_kvh = kvc.kvc_calibrate_sigma(ck, cm, block_tokens=sigma_block)
         sigma[l * ppl:(l + 1) * ppl] = W.expand_sigma(w, s_kvh)
         del ck, cm
     prefix = kvc.kvc_build_marginal(W.marginal_samples(w, device=dev), (w.w_narrow_bp, w.w_wide_bp))
@@ -236,6 +238,8 @@ def main():
     ap.add_argument("--chunk-tokens", type=int, default=None, help="override the workload's chunk length")
     ap.add_argument("--offload", action="store_true",
                     help="(per-layer workload 4) also time the host-offload reload: pinned streams, copies overlapped with decode")
+    ap.add_argument("--sigma-block", type=int, default=0,
+                    help="position-aware sigma: one sigma per block of this many tokens (0 = per plane)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="after the timed steps, copy 1 GiB once (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -263,10 +267,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     reps = args.calib_reps if args.calib_reps is not None else w.calib_reps
-    kv, mu, sigma, prefix = prepare(w, dev, reps)
+    kv, mu, sigma, prefix = prepare(w, dev, reps, args.sigma_block)
     n = w.n_scalars
     weights = (w.w_narrow_bp, w.w_wide_bp)
-    tc = args.chunk_tokens if args.chunk_tokens else w.chunk_tokens
+    # with sigma blocks the library's default picks a divisor of the block length
+    tc = args.chunk_tokens if args.chunk_tokens else (0 if args.sigma_block else w.chunk_tokens)
     kv_code = kvc.KVC_BF16 if w.kv_dtype == W.BF16 else kvc.KVC_E4M3
     mu_code = kvc.KVC_BF16 if w.mu_dtype == W.BF16 else kvc.KVC_F32
     kv_size = 2 if w.kv_dtype == W.BF16 else 1
@@ -275,8 +280,11 @@ def main():
     parts = ([slice(l * w.planes_per_layer, (l + 1) * w.planes_per_layer) for l in range(w.layers)]
              if per_layer else [slice(0, w.planes)])
     g_part = parts[0].stop - parts[0].start
-    p = kvc.make_params(kv_code, mu_code, g_part, w.tokens, w.channels, weights, tc)
+    p = kvc.make_params(kv_code, mu_code, g_part, w.tokens, w.channels, weights, tc, args.sigma_block)
     enc = kvc.Encoder(p, dev)
+    if tc == 0:
+        tc = kvc.kvc_stream_info(enc(kv[parts[0]], mu[parts[0]], sigma[parts[0]], prefix)[:128].cpu().numpy())[0] \
+            .chunk_tokens
     kv_out = torch.empty((w.planes, w.tokens, w.channels), dtype=torch.int16 if kv_size == 2 else torch.uint8,
                          device=dev)
     dws = torch.empty(kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
@@ -327,7 +335,8 @@ def main():
     stream_bytes = stream_total[0]
     bits_int, bits_float = 0.0, 0.0
     for sl in parts:
-        bi, bf = kvc.kvc_estimate_bits(kv[sl], mu[sl], sigma[sl], prefix, weights)
+        bi, bf = kvc.kvc_estimate_bits(kv[sl], mu[sl], sigma[sl], prefix, weights,
+                                       sigma_block_tokens=args.sigma_block, chunk_tokens=tc)
         frac = (sl.stop - sl.start) / w.planes
         bits_int += bi * frac
         bits_float += bf * frac
@@ -370,7 +379,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "shape": [w.layers, 2, w.batch, w.heads, w.tokens, w.channels],
-            "scalars": n, "mixture_bp": list(weights), "chunk_tokens": tc,
+            "scalars": n, "mixture_bp": list(weights), "chunk_tokens": tc, "sigma_block_tokens": args.sigma_block,
             "sigma_calibration": f"{reps}x{w.calib_tokens} tokens per layer",
             "mu_dtype": "bf16" if mu_size == 2 else "fp32", "calls_per_step": len(parts),
         },

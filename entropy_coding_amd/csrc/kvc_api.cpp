@@ -49,13 +49,20 @@ bool budgets(int32_t kv, uint32_t wn, uint32_t ww, uint32_t* tn, uint32_t* tw, u
     return true;
 }
 
-// Shape rules shared by encoder and decoder.
-bool geometry(int64_t planes, int64_t tokens, int64_t channels, uint32_t chunk_tokens, ChunkGeom* g) {
+// Shape rules shared by encoder and decoder.  sigma_block_tokens: 0 (one
+// sigma per plane and channel) or B, one sigma per block of B tokens; a
+// chunk must lie within one block, so B is a multiple of the chunk length
+// unless one block covers every token.
+bool geometry(int64_t planes, int64_t tokens, int64_t channels, uint32_t chunk_tokens, uint32_t sigma_block_tokens,
+              ChunkGeom* g) {
     if (planes < 1 || tokens < 1 || channels < 64 || channels % 64) return false;
     if (planes > kMaxScalars || tokens > kMaxScalars || channels > kMaxScalars) return false;
-    if (planes * channels >= (int64_t(1) << 32)) return false;         // sigma words indexable
     if (planes * tokens > kMaxScalars / channels) return false;
     if (chunk_tokens < 1 || chunk_tokens > kMaxChunkTokens) return false;
+    const bool blocks = sigma_block_tokens != 0 && int64_t(sigma_block_tokens) < tokens;
+    if (blocks && sigma_block_tokens % chunk_tokens) return false;
+    const int64_t n_blocks = blocks ? (tokens + sigma_block_tokens - 1) / sigma_block_tokens : 1;
+    if (planes * n_blocks * channels >= (int64_t(1) << 32)) return false;   // sigma words indexable
     // a chunk's rows span chunk_tokens * channels scalars of up to 4 bytes: byte offsets fit 31 bits
     if (int64_t(chunk_tokens) * channels >= (int64_t(1) << 29)) return false;
     g->planes = planes;
@@ -64,9 +71,15 @@ bool geometry(int64_t planes, int64_t tokens, int64_t channels, uint32_t chunk_t
     g->chunk_tokens = chunk_tokens;
     g->n_tok_chunks = static_cast<uint32_t>((tokens + chunk_tokens - 1) / chunk_tokens);
     g->n_groups = static_cast<uint32_t>(channels / 64);
-    g->pad = 0;
+    g->sigma_tc = blocks ? sigma_block_tokens / chunk_tokens : 0u;
     g->n_chunks = planes * int64_t(g->n_tok_chunks) * int64_t(g->n_groups);
+    g->sigma_blocks = n_blocks;
     return true;
+}
+
+// Words of sigma: [planes][sigma blocks][channels].
+uint64_t sigma_words(const ChunkGeom& g) {
+    return uint64_t(g.planes) * uint64_t(g.sigma_blocks) * uint64_t(g.channels);
 }
 
 // Default chunk length.  Each chunk is one wave and MI355X holds 8,192 of
@@ -81,14 +94,25 @@ bool geometry(int64_t planes, int64_t tokens, int64_t channels, uint32_t chunk_t
 constexpr int64_t kWaveSlots = 256 * 32;
 constexpr int64_t kChunkMax = 1024, kChunkFloor = 256, kChunkAllowance = 9;
 
-uint32_t default_chunk_tokens(int64_t planes, int64_t tokens, int64_t channels) {
+uint32_t default_chunk_tokens(int64_t planes, int64_t tokens, int64_t channels, uint32_t sigma_block_tokens) {
     if (tokens <= 0) return 1;
     if (planes <= 0 || channels < 64) return static_cast<uint32_t>(tokens < kChunkMax ? tokens : kChunkMax);
     const int64_t groups = channels / 64;
-    const int64_t top = tokens < kChunkMax ? tokens : kChunkMax;
-    const int64_t floor_len = tokens < kChunkFloor ? tokens : kChunkFloor;
-    int64_t best_len = top, best_cost = -1;
-    for (int64_t len = top; len >= floor_len; --len) {          // at most 769 lengths
+    // with sigma blocks shorter than the tokens, only divisors of the block
+    // length (so that no chunk straddles two blocks)
+    const int64_t blk = (sigma_block_tokens != 0 && int64_t(sigma_block_tokens) < tokens) ? sigma_block_tokens : 0;
+    const int64_t span = blk ? blk : tokens;
+    const int64_t top = span < kChunkMax ? span : kChunkMax;
+    int64_t floor_len = span < kChunkFloor ? span : kChunkFloor;
+    if (blk) {
+        // no divisor of B in [floor, top]: the largest divisor below
+        bool any = false;
+        for (int64_t len = top; len >= floor_len && !any; --len) any = blk % len == 0;
+        if (!any) floor_len = 1;
+    }
+    int64_t best_len = 0, best_cost = -1;
+    for (int64_t len = top; len >= floor_len; --len) {          // at most 1024 lengths
+        if (blk && blk % len) continue;
         const int64_t chunks = planes * ((tokens + len - 1) / len) * groups;
         const int64_t cost = ((chunks + kWaveSlots - 1) / kWaveSlots) * (len + kChunkAllowance);
         if (best_cost < 0 || cost < best_cost) {
@@ -100,10 +124,10 @@ uint32_t default_chunk_tokens(int64_t planes, int64_t tokens, int64_t channels) 
 }
 
 bool params_geometry(const kvc_params* p, ChunkGeom* g) {
-    if (!p || !kv_dtype_ok(p->kv_dtype) || !mu_dtype_ok(p->mu_dtype) || p->reserved != 0) return false;
+    if (!p || !kv_dtype_ok(p->kv_dtype) || !mu_dtype_ok(p->mu_dtype)) return false;
     uint32_t tc = p->chunk_tokens;
-    if (tc == 0) tc = default_chunk_tokens(p->planes, p->tokens, p->channels);
-    return geometry(p->planes, p->tokens, p->channels, tc, g);
+    if (tc == 0) tc = default_chunk_tokens(p->planes, p->tokens, p->channels, p->sigma_block_tokens);
+    return geometry(p->planes, p->tokens, p->channels, tc, p->sigma_block_tokens, g);
 }
 
 // Workspace of the encoder: control block, final states, word counts,
@@ -158,6 +182,7 @@ kvc::StreamHeader make_header(const kvc_params* p, const ChunkGeom& g, uint32_t 
     put64(h.bytes, 48, static_cast<uint64_t>(g.tokens));
     put64(h.bytes, 56, static_cast<uint64_t>(g.channels));
     put64(h.bytes, 64, static_cast<uint64_t>(g.n_chunks));
+    put32(h.bytes, 88, p->sigma_block_tokens);
     return h;
 }
 
@@ -176,6 +201,7 @@ int parse_header(const uint8_t* b, kvc_params* p, ChunkGeom* g, uint64_t* payloa
     q.planes = static_cast<int64_t>(get64(b, 40));
     q.tokens = static_cast<int64_t>(get64(b, 48));
     q.channels = static_cast<int64_t>(get64(b, 56));
+    q.sigma_block_tokens = get32(b, 88);
     uint32_t tn, tw, te;
     if (!kv_dtype_ok(q.kv_dtype) || !mu_dtype_ok(q.mu_dtype) ||
         !budgets(q.kv_dtype, q.w_narrow_bp, q.w_wide_bp, &tn, &tw, &te))
@@ -184,10 +210,10 @@ int parse_header(const uint8_t* b, kvc_params* p, ChunkGeom* g, uint64_t* payloa
     if (get64(b, 40) > uint64_t(kMaxScalars) || get64(b, 48) > uint64_t(kMaxScalars) ||
         get64(b, 56) > uint64_t(kMaxScalars))
         return KVC_ERR_CORRUPT;
-    if (q.chunk_tokens == 0 || !geometry(q.planes, q.tokens, q.channels, q.chunk_tokens, g))
+    if (q.chunk_tokens == 0 || !geometry(q.planes, q.tokens, q.channels, q.chunk_tokens, q.sigma_block_tokens, g))
         return KVC_ERR_CORRUPT;
     if (get64(b, 64) != static_cast<uint64_t>(g->n_chunks)) return KVC_ERR_CORRUPT;
-    for (int i = 88; i < KVC_HEADER_BYTES; ++i)
+    for (int i = 92; i < KVC_HEADER_BYTES; ++i)
         if (b[i]) return KVC_ERR_CORRUPT;
     *payload = get64(b, 72);
     *hash = get64(b, 80);
@@ -300,8 +326,8 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     StageTimer timer(h_info ? h_info->stage_ms : nullptr, KVC_ENCODE_STAGES, s);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(0);
-    if ((e = kvc::launch_side_hash(d_sigma, uint64_t(g.planes) * uint64_t(g.channels), prefix,
-                                   prefix ? alphabet(p->kv_dtype) + 1u : 0u, ctl, s)) != hipSuccess)
+    if ((e = kvc::launch_side_hash(d_sigma, sigma_words(g), prefix, prefix ? alphabet(p->kv_dtype) + 1u : 0u, ctl,
+                                   s)) != hipSuccess)
         return KVC_ERR_DEVICE;
     timer.mark(1);
 
@@ -406,8 +432,8 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     StageTimer timer(h_info ? h_info->stage_ms : nullptr, KVC_DECODE_STAGES, s);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(0);
-    if ((e = kvc::launch_side_hash(d_sigma, uint64_t(g.planes) * uint64_t(g.channels), prefix,
-                                   prefix ? n_sym + 1u : 0u, ctl, s)) != hipSuccess)
+    if ((e = kvc::launch_side_hash(d_sigma, sigma_words(g), prefix, prefix ? n_sym + 1u : 0u, ctl, s)) !=
+        hipSuccess)
         return KVC_ERR_DEVICE;
     if ((e = kvc::launch_escape_buckets(prefix ? prefix : phi.zero, n_sym, shift, n_buckets, p.kv_dtype, buckets, s)) !=
         hipSuccess)
@@ -450,23 +476,33 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
 int kvc_calibrate_sigma(const void* d_kv, const void* d_mu, int32_t kv_dtype, int32_t mu_dtype, int64_t reps,
                         int64_t planes, int64_t tokens, int64_t channels, float sigma_floor, float* d_sigma_out,
                         void* d_workspace, uint64_t workspace_bytes, void* stream) {
+    return kvc_calibrate_sigma_blocks(d_kv, d_mu, kv_dtype, mu_dtype, reps, planes, tokens, channels, 0, sigma_floor,
+                                      d_sigma_out, d_workspace, workspace_bytes, stream);
+}
+
+int kvc_calibrate_sigma_blocks(const void* d_kv, const void* d_mu, int32_t kv_dtype, int32_t mu_dtype, int64_t reps,
+                               int64_t planes, int64_t tokens, int64_t channels, int64_t block_tokens,
+                               float sigma_floor, float* d_sigma_out, void* d_workspace, uint64_t workspace_bytes,
+                               void* stream) {
     if (!d_kv || !d_mu || !d_sigma_out || !kv_dtype_ok(kv_dtype) || !mu_dtype_ok(mu_dtype)) return KVC_ERR_INVALID;
+    if (block_tokens < 0) return KVC_ERR_INVALID;
     if (!data_aligned(kv_dtype, mu_dtype, d_kv, d_mu, d_sigma_out, nullptr)) return KVC_ERR_INVALID;
     if (reps < 1 || planes < 1 || tokens < 1 || channels < 64 || channels % 64) return KVC_ERR_INVALID;
     if (reps > kMaxScalars || planes > kMaxScalars || tokens > kMaxScalars || channels > kMaxScalars)
         return KVC_ERR_INVALID;
     if (reps * tokens > kMaxScalars / channels || reps * tokens * channels > kMaxScalars / planes)
         return KVC_ERR_INVALID;
-    if (planes * (channels / 64) > 0x7FFFFFFF) return KVC_ERR_INVALID;
+    const int64_t n_blocks = (block_tokens == 0 || block_tokens >= tokens) ? 1 : (tokens + block_tokens - 1) / block_tokens;
+    if (planes * n_blocks * (channels / 64) > 0x7FFFFFFF) return KVC_ERR_INVALID;
     if (!(sigma_floor > 0.0f) || !(sigma_floor <= FLT_MAX)) return KVC_ERR_INVALID;
-    // partial sums: one CalibPart per (split, plane, channel), at most 64 splits
+    // partial sums: one CalibPart per (split, plane, block, channel), at most 64 splits
     static_assert(sizeof(kvc::CalibPart) * kvc::kCalibSplitsMax == 1024, "workspace formula");
-    if (!d_workspace || !aligned(d_workspace, 256) || planes * channels > kMaxScalars / 1024 ||
-        workspace_bytes < KVC_CALIBRATE_WORKSPACE_BYTES(planes, channels))
+    if (!d_workspace || !aligned(d_workspace, 256) || planes * n_blocks * channels > kMaxScalars / 1024 ||
+        workspace_bytes < KVC_CALIBRATE_WORKSPACE_BYTES(planes * n_blocks, channels))
         return KVC_ERR_INVALID;
     return finish(kvc::launch_calibrate(d_kv, d_mu, kv_dtype, mu_dtype, reps, planes, tokens, channels,
-                                        sigma_floor, d_sigma_out, static_cast<kvc::CalibPart*>(d_workspace),
-                                        static_cast<hipStream_t>(stream)));
+                                        n_blocks == 1 ? 0 : block_tokens, sigma_floor, d_sigma_out,
+                                        static_cast<kvc::CalibPart*>(d_workspace), static_cast<hipStream_t>(stream)));
 }
 
 int kvc_build_marginal(const void* d_samples, int32_t dtype, uint64_t n, uint32_t w_narrow_bp,

@@ -32,8 +32,9 @@ struct ChunkGeom {
     uint32_t chunk_tokens;
     uint32_t n_tok_chunks;              // ceil(tokens / chunk_tokens)
     uint32_t n_groups;                  // channels / 64
-    uint32_t pad;
+    uint32_t sigma_tc;                  // token chunks per sigma block; 0: one sigma block per plane
     int64_t n_chunks;
+    int64_t sigma_blocks;               // sigma blocks per plane (sigma is [planes][sigma_blocks][channels])
 };
 
 // Per-device Phi base tables (kTablePoints entries each).
@@ -140,10 +141,12 @@ struct CalibPart {
     unsigned long long used;
 };
 constexpr int64_t kCalibSplitsMax = 64;
-int64_t calibrate_splits(int64_t reps, int64_t planes, int64_t tokens, int64_t channels);
+int64_t calibrate_splits(int64_t reps, int64_t pairs, int64_t block);
+// sigma per (plane, block of block_tokens tokens, channel); block_tokens = 0
+// (or >= tokens): one block of every token
 hipError_t launch_calibrate(const void* kv, const void* mu, int kv_dtype, int mu_dtype, int64_t reps,
-                            int64_t planes, int64_t tokens, int64_t channels, float sigma_floor,
-                            float* sigma_out, CalibPart* part, hipStream_t s);
+                            int64_t planes, int64_t tokens, int64_t channels, int64_t block_tokens,
+                            float sigma_floor, float* sigma_out, CalibPart* part, hipStream_t s);
 hipError_t launch_marginal(const void* samples, int dtype, uint64_t n, uint32_t te,
                            uint32_t* prefix_out, hipStream_t s);
 hipError_t launch_estimate(const EstimateArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);

@@ -113,6 +113,7 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 struct ChunkPos {
     int64_t g;
+    int64_t srow;                       // row of sigma: [planes][sigma_blocks] flattened
     uint32_t t0, len, k;
 };
 
@@ -122,6 +123,9 @@ __device__ __forceinline__ ChunkPos chunk_pos(const ChunkGeom& geo, int64_t c) {
     const int64_t rest = c / geo.n_groups;
     const uint32_t tc = static_cast<uint32_t>(rest % geo.n_tok_chunks);
     p.g = rest / geo.n_tok_chunks;
+    // a chunk lies within one sigma block (the block length is a multiple
+    // of the chunk length)
+    p.srow = p.g * geo.sigma_blocks + (geo.sigma_tc ? tc / geo.sigma_tc : 0u);
     p.t0 = tc * geo.chunk_tokens;
     const int64_t left = geo.tokens - static_cast<int64_t>(p.t0);
     p.len = static_cast<uint32_t>(left < geo.chunk_tokens ? left : geo.chunk_tokens);
@@ -334,7 +338,7 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
     const ChunkPos cp = chunk_pos(a.geom, chunk);
     const uint32_t D = static_cast<uint32_t>(a.geom.channels);
 
-    const float sigma = a.sigma[cp.g * D + cp.k * 64 + lane];
+    const float sigma = a.sigma[cp.srow * D + cp.k * 64 + lane];
     float inv24 = __frcp_rn(sigma) * 16777216.0f;
     if (__ballot(!sigma_ok(sigma))) {
         if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
@@ -933,7 +937,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
     WordRing win{buffer_rsrc(base + kStateBytes, avail * 2u), s_ring[wave], 0u, 0u};
     win.init(static_cast<uint32_t>(lane));
 
-    const float sigma = a.sigma[cp.g * D + cp.k * 64 + lane];
+    const float sigma = a.sigma[cp.srow * D + cp.k * 64 + lane];
     float inv24 = __frcp_rn(sigma) * 16777216.0f;
     float sg = sigma;
     if (__ballot(!sigma_ok(sigma))) {
@@ -1131,10 +1135,11 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStr
 }
 
 // ---------------------------------------------------------------------------
-// sigma calibration: one workgroup of 16 waves per (plane, 64-channel
-// group); wave w sums rows w, w+16, ... in float64; the 16 partial sums are
-// added in wave order, so the result does not depend on scheduling.
-// Non-finite residuals carry no scale information and are skipped.
+// sigma calibration: workgroups of 4 waves per (plane, sigma block, 64-channel
+// group), each over a contiguous split of the block's reps x tokens rows;
+// float64 sums in a fixed order, so the result does not depend on
+// scheduling.  Non-finite residuals carry no scale information and are
+// skipped.
 // ---------------------------------------------------------------------------
 template <int KV>
 __device__ __forceinline__ double kv_value_f64(typename Alphabet<KV>::Bits b) {
@@ -1149,8 +1154,9 @@ __device__ __forceinline__ double kv_value_f64(typename Alphabet<KV>::Bits b) {
     }
 }
 
-// Pass 1: block (plane and 64-channel group, split) sums the squared
-// residuals of a contiguous range of the reps x tokens rows.  Its 4 waves
+// Pass 1: block (plane, sigma block and 64-channel group, split) sums the
+// squared residuals of a contiguous range of the block's reps x tokens rows
+// (rep-major; a sigma block of `block` tokens, the last one shorter).  Its 4 waves
 // take every 4th row; each lane keeps one channel's float64 sum in row order
 // and the waves are added in wave order, so the partial does not depend on
 // scheduling.  Rows are loaded 4 at a time to keep loads in flight.
@@ -1161,6 +1167,7 @@ constexpr int kCalibUnroll = 4;
 template <int KV, int MU>
 __global__ void __launch_bounds__(kCalibBlock) k_calibrate_part(const void* kv_, const void* mu_, int64_t reps,
                                                                 int64_t planes, int64_t tokens, int64_t channels,
+                                                                int64_t block, int64_t nb,
                                                                 CalibPart* __restrict__ part) {
     __shared__ double s_sum[kCalibWaves][64];
     __shared__ unsigned long long s_used[kCalibWaves][64];
@@ -1171,13 +1178,17 @@ __global__ void __launch_bounds__(kCalibBlock) k_calibrate_part(const void* kv_,
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int64_t groups = channels / 64;
-    const int64_t p = blockIdx.x / groups;
+    // (plane, sigma block) pair: the block's tokens [t_lo, t_lo + len)
+    const int64_t vp = blockIdx.x / groups;
+    const int64_t p = vp / nb;
+    const int64_t t_lo = (vp - p * nb) * block;
+    const int64_t len = tokens - t_lo < block ? tokens - t_lo : block;
     const int64_t d = (blockIdx.x % groups) * 64 + lane;
     const int64_t splits = gridDim.y, s = blockIdx.y;
-    const int64_t rows = reps * tokens;
+    const int64_t rows = reps * len;
     const int64_t r1 = rows * (s + 1) / splits;
     int64_t r = rows * s / splits + wave;
-    int64_t rep = r / tokens, t = r - rep * tokens;      // advanced by carries below
+    int64_t rep = r / len, t = r - rep * len;            // advanced by carries below
     double acc = 0.0;
     unsigned long long used = 0;
     while (r < r1) {                                     // wave-uniform
@@ -1188,14 +1199,14 @@ __global__ void __launch_bounds__(kCalibBlock) k_calibrate_part(const void* kv_,
         for (int u = 0; u < kCalibUnroll; ++u) {
             live[u] = r < r1;
             if (live[u]) {
-                const int64_t off = ((rep * planes + p) * tokens + t) * channels + d;
+                const int64_t off = ((rep * planes + p) * tokens + t_lo + t) * channels + d;
                 kb[u] = kv[off];
                 mb[u] = mu[off];
             }
             r += kCalibWaves;
             t += kCalibWaves;
-            while (t >= tokens) {
-                t -= tokens;
+            while (t >= len) {
+                t -= len;
                 ++rep;
             }
         }
@@ -1220,7 +1231,7 @@ __global__ void __launch_bounds__(kCalibBlock) k_calibrate_part(const void* kv_,
             sum += s_sum[w][lane];
             u += s_used[w][lane];
         }
-        part[s * planes * channels + p * channels + d] = CalibPart{sum, u};
+        part[s * planes * nb * channels + vp * channels + d] = CalibPart{sum, u};
     }
 }
 
@@ -1239,29 +1250,36 @@ __global__ void k_calibrate_final(const CalibPart* __restrict__ part, int64_t sp
     out[i] = (sg > floor_ && __builtin_isfinite(sg)) ? sg : floor_;
 }
 
-int64_t calibrate_splits(int64_t reps, int64_t planes, int64_t tokens, int64_t channels) {
-    const int64_t pairs = planes * (channels / 64);
+int64_t calibrate_splits(int64_t reps, int64_t pairs, int64_t block) {
     int64_t sp = (4096 + pairs - 1) / pairs;             // about 4096 blocks in all
     sp = sp < 1 ? 1 : (sp > kCalibSplitsMax ? kCalibSplitsMax : sp);
-    const int64_t rows = reps * tokens;
+    const int64_t rows = reps * block;
     return sp > rows ? rows : sp;
 }
 
 hipError_t launch_calibrate(const void* kv, const void* mu, int kv_dtype, int mu_dtype, int64_t reps,
-                            int64_t planes, int64_t tokens, int64_t channels, float sigma_floor,
-                            float* sigma_out, CalibPart* part, hipStream_t s) {
-    const int64_t splits = calibrate_splits(reps, planes, tokens, channels);
-    const dim3 grid(static_cast<uint32_t>(planes * (channels / 64)), static_cast<uint32_t>(splits)), block(kCalibBlock);
+                            int64_t planes, int64_t tokens, int64_t channels, int64_t block_tokens,
+                            float sigma_floor, float* sigma_out, CalibPart* part, hipStream_t s) {
+    // block_tokens = 0 or >= tokens: one block of every token
+    const int64_t blk = (block_tokens == 0 || block_tokens > tokens) ? tokens : block_tokens;
+    const int64_t nb = (tokens + blk - 1) / blk;
+    const int64_t pairs = planes * nb * (channels / 64);
+    const int64_t splits = calibrate_splits(reps, pairs, blk);
+    const dim3 grid(static_cast<uint32_t>(pairs), static_cast<uint32_t>(splits)), block(kCalibBlock);
     if (kv_dtype == kBF16 && mu_dtype == kBF16)
-        hipLaunchKernelGGL((k_calibrate_part<kBF16, kBF16>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, part);
+        hipLaunchKernelGGL((k_calibrate_part<kBF16, kBF16>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels,
+                           blk, nb, part);
     else if (kv_dtype == kBF16 && mu_dtype == kF32)
-        hipLaunchKernelGGL((k_calibrate_part<kBF16, kF32>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, part);
+        hipLaunchKernelGGL((k_calibrate_part<kBF16, kF32>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels,
+                           blk, nb, part);
     else if (kv_dtype == kE4M3 && mu_dtype == kBF16)
-        hipLaunchKernelGGL((k_calibrate_part<kE4M3, kBF16>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, part);
+        hipLaunchKernelGGL((k_calibrate_part<kE4M3, kBF16>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels,
+                           blk, nb, part);
     else if (kv_dtype == kE4M3 && mu_dtype == kF32)
-        hipLaunchKernelGGL((k_calibrate_part<kE4M3, kF32>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, part);
+        hipLaunchKernelGGL((k_calibrate_part<kE4M3, kF32>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels,
+                           blk, nb, part);
     else return hipErrorInvalidValue;
-    const int64_t n = planes * channels;
+    const int64_t n = planes * nb * channels;
     hipLaunchKernelGGL(k_calibrate_final, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s, part, splits,
                        n, sigma_floor, sigma_out);
     return hipGetLastError();
@@ -1364,7 +1382,8 @@ __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
         const int64_t d = i % D;
         const int64_t g = i / (T * D);
-        const float sg = a.sigma[g * D + d];
+        const int64_t tc = (i / D - g * T) / a.geom.chunk_tokens;
+        const float sg = a.sigma[(g * a.geom.sigma_blocks + (a.geom.sigma_tc ? tc / a.geom.sigma_tc : 0)) * D + d];
         const float inv24 = __frcp_rn(sg) * 16777216.0f;
         const float mu = mu_value<MU>(mup[i]);
         const uint32_t s = order_of_bits<KV>(kv[i]);

@@ -27,8 +27,8 @@ DECODE_STAGES = 2     # side-information checksum + escape bucket table, decodin
 
 EXPORTS = [
     "kvc_version", "kvc_status_string", "kvc_phi_tables", "kvc_encode_sizes", "kvc_encode",
-    "kvc_stream_info", "kvc_decode", "kvc_calibrate_sigma", "kvc_build_marginal",
-    "kvc_estimate_bits", "kvc_cdf_table",
+    "kvc_stream_info", "kvc_decode", "kvc_calibrate_sigma", "kvc_calibrate_sigma_blocks",
+    "kvc_build_marginal", "kvc_estimate_bits", "kvc_cdf_table",
 ]
 
 if not os.path.exists(LIB_PATH):
@@ -40,7 +40,7 @@ class kvc_params(ctypes.Structure):
     _fields_ = [
         ("kv_dtype", ctypes.c_int32), ("mu_dtype", ctypes.c_int32),
         ("w_narrow_bp", ctypes.c_uint32), ("w_wide_bp", ctypes.c_uint32),
-        ("chunk_tokens", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+        ("chunk_tokens", ctypes.c_uint32), ("sigma_block_tokens", ctypes.c_uint32),
         ("planes", ctypes.c_int64), ("tokens", ctypes.c_int64), ("channels", ctypes.c_int64),
     ]
 
@@ -77,6 +77,8 @@ _lib_stream_info = _sig("kvc_stream_info", ctypes.c_int, [_P, _U64, ctypes.POINT
 _lib_decode = _sig("kvc_decode", ctypes.c_int, [_P, _U64, _P, _P, _P, _P, _P, _U64, _P, _P])
 _lib_calibrate = _sig("kvc_calibrate_sigma", ctypes.c_int,
                       [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _U64, _P])
+_lib_calibrate_blocks = _sig("kvc_calibrate_sigma_blocks", ctypes.c_int,
+                             [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _U64, _P])
 _lib_marginal = _sig("kvc_build_marginal", ctypes.c_int, [_P, _I32, _U64, _U32, _U32, _P, _P])
 _lib_estimate = _sig("kvc_estimate_bits", ctypes.c_int, [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _P, _U64, _P])
 _lib_cdf_table = _sig("kvc_cdf_table", ctypes.c_int, [_I32, _I32, _U32, _U32, _P, _P, _I64, _P, _P, _P])
@@ -140,8 +142,17 @@ def kvc_phi_tables():
     return a, b
 
 
-def make_params(kv_dtype, mu_dtype, planes, tokens, channels, weights=(9500, 300), chunk_tokens=0) -> kvc_params:
-    return kvc_params(kv_dtype, mu_dtype, weights[0], weights[1], chunk_tokens, 0, planes, tokens, channels)
+def make_params(kv_dtype, mu_dtype, planes, tokens, channels, weights=(9500, 300), chunk_tokens=0,
+                sigma_block_tokens=0) -> kvc_params:
+    return kvc_params(kv_dtype, mu_dtype, weights[0], weights[1], chunk_tokens, sigma_block_tokens,
+                      planes, tokens, channels)
+
+
+def sigma_shape(planes: int, tokens: int, channels: int, sigma_block_tokens: int = 0):
+    """Shape of sigma: [G, D], or [G, ceil(T / B), D] with sigma blocks."""
+    if sigma_block_tokens == 0:
+        return (planes, channels)
+    return (planes, -(-tokens // sigma_block_tokens), channels)
 
 
 def kvc_encode_sizes(p: kvc_params):
@@ -174,17 +185,20 @@ class Encoder:
 
 
 def kvc_encode(kv: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, prefix: torch.Tensor | None = None,
-               weights=(9500, 300), chunk_tokens: int = 0, stream=None) -> torch.Tensor:
-    """Encode KV [G, T, D] under the mixture around mu with sigma [G, D];
-    returns the stream as a uint8 device tensor."""
+               weights=(9500, 300), chunk_tokens: int = 0, stream=None,
+               sigma_block_tokens: int = 0) -> torch.Tensor:
+    """Encode KV [G, T, D] under the mixture around mu with sigma [G, D] (or
+    [G, ceil(T / B), D] with sigma_block_tokens = B); returns the stream as
+    a uint8 device tensor."""
     for t, nm in ((kv, "kv"), (mu, "mu"), (sigma, "sigma")):
         _need(t, nm)
     if prefix is not None:
         _need(prefix, "prefix")
     g, t, d = kv.shape
-    if tuple(mu.shape) != (g, t, d) or tuple(sigma.shape) != (g, d) or sigma.dtype != torch.float32:
-        raise ValueError("shapes: kv and mu [G, T, D], sigma [G, D] float32")
-    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens)
+    if tuple(mu.shape) != (g, t, d) or tuple(sigma.shape) != sigma_shape(g, t, d, sigma_block_tokens) \
+            or sigma.dtype != torch.float32:
+        raise ValueError("shapes: kv and mu [G, T, D], sigma [G, D] (or [G, ceil(T / B), D]) float32")
+    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens, sigma_block_tokens)
     return Encoder(p, kv.device)(kv, mu, sigma, prefix, stream).clone()
 
 
@@ -239,17 +253,25 @@ def calibrate_workspace_bytes(planes: int, channels: int) -> int:
 
 def kvc_calibrate_sigma(kv: torch.Tensor, mu: torch.Tensor, sigma_floor: float = 2.0 ** -30,
                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                        stream=None) -> torch.Tensor:
-    """kv, mu: [reps, planes, tokens, channels] -> sigma [planes, channels]."""
+                        stream=None, block_tokens: int = 0) -> torch.Tensor:
+    """kv, mu: [reps, planes, tokens, channels] -> sigma [planes, channels],
+    or with block_tokens = B > 0 sigma [planes, ceil(tokens / B), channels]
+    (one sigma per block of B tokens)."""
     _need(kv, "kv")
     _need(mu, "mu")
     r, g, t, d = kv.shape
+    shape = sigma_shape(g, t, d, block_tokens)
+    n_rows = g if block_tokens == 0 else g * shape[1]
     if out is None:
-        out = torch.empty((g, d), dtype=torch.float32, device=kv.device)
+        out = torch.empty(shape, dtype=torch.float32, device=kv.device)
     if workspace is None:
-        workspace = torch.empty(calibrate_workspace_bytes(g, d), dtype=torch.uint8, device=kv.device)
-    st = _lib_calibrate(_ptr(kv), _ptr(mu), _kv_dtype(kv), _mu_dtype(mu), r, g, t, d, sigma_floor,
-                        _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+        workspace = torch.empty(calibrate_workspace_bytes(n_rows, d), dtype=torch.uint8, device=kv.device)
+    if block_tokens == 0:
+        st = _lib_calibrate(_ptr(kv), _ptr(mu), _kv_dtype(kv), _mu_dtype(mu), r, g, t, d, sigma_floor,
+                            _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    else:
+        st = _lib_calibrate_blocks(_ptr(kv), _ptr(mu), _kv_dtype(kv), _mu_dtype(mu), r, g, t, d, block_tokens,
+                                   sigma_floor, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "kvc_calibrate_sigma")
     return out
 
@@ -266,10 +288,11 @@ def kvc_build_marginal(samples: torch.Tensor, weights=(9500, 300), stream=None) 
     return out
 
 
-def kvc_estimate_bits(kv, mu, sigma, prefix=None, weights=(9500, 300), stream=None):
+def kvc_estimate_bits(kv, mu, sigma, prefix=None, weights=(9500, 300), stream=None, sigma_block_tokens: int = 0,
+                      chunk_tokens: int = 0):
     """(integer-model bits/scalar, float-model bits/scalar)."""
     g, t, d = kv.shape
-    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, 0)
+    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens, sigma_block_tokens)
     ws = torch.empty(ESTIMATE_WORKSPACE_BYTES, dtype=torch.uint8, device=kv.device)
     out = (ctypes.c_double * 2)()
     st = _lib_estimate(ctypes.byref(p), _ptr(kv), _ptr(mu), _ptr(sigma), _ptr(prefix), ctypes.addressof(out),

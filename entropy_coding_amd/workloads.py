@@ -8,7 +8,8 @@ predictor mean plus a long-tailed residual ([wiki] 'Speculative KV Coding',
 § mixture distribution; [blog] § engineering choice of predictor).
 
 Layout: KV and mu are [G, T, D] with G = layers * 2 (K, V) * batch * heads
-planes in that order, channel fastest.  sigma is [G, D].  Everything is drawn
+planes in that order, channel fastest.  sigma is [G, D] (or [G, blocks, D]
+with one sigma per block of tokens).  Everything is drawn
 with torch generators on the requested device, one seed per (purpose, layer),
 so a long configuration can be produced one layer at a time.
 """
@@ -41,6 +42,7 @@ class Workload:
     calib_reps: int           # 0: use the generating sigma directly
     calib_tokens: int
     chunk_tokens: int         # the library's default for the call shape (one layer per call for id 4)
+    position_scale: bool = False   # residual scale varies with token position (see position_factor)
 
     @property
     def planes_per_layer(self) -> int:
@@ -70,9 +72,11 @@ WORKLOADS = {
                 E4M3, F32, 9500, 300, False, False, 128, 1024, 586),
     4: Workload(4, "Qwen3-32B-shaped long-context bf16 KV (64 layers, 32768 tokens)", 64, 1, 8, 32768, 128,
                 BF16, BF16, 9500, 300, True, True, 128, 1024, 256),
+    5: Workload(5, "Qwen3-8B-shaped bf16 KV with position-varying residual scale (36 layers, batch 4, 4096 tokens)",
+                36, 4, 8, 4096, 128, BF16, BF16, 9500, 300, True, True, 32, 4096, 586, True),
 }
 
-PURPOSE = {"params": 0, "data": 1, "calib": 2, "marginal": 3, "noise": 4}
+PURPOSE = {"params": 0, "data": 1, "calib": 2, "marginal": 3, "noise": 4, "position": 5}
 
 
 def seed_for(cid: int, purpose: str, layer: int = 0) -> int:
@@ -120,8 +124,30 @@ def _e4m3_ulp(x: torch.Tensor) -> torch.Tensor:
     return torch.exp2(e - 3.0)
 
 
-def _draw(w: Workload, s, sig, reps: int, tokens: int, g, device):
-    """KV and mu draws shaped [reps, 2, heads, tokens, D]."""
+def position_factor(w: Workload, layer: int, tokens: int, device="cpu"):
+    """Residual scale by position, [2, heads, tokens, D] (ones unless the
+    workload has position_scale).  A stand-in for position structure the
+    pages point at ([blog] § limitations and future directions): on the upper
+    64 K channels (the slowly rotating RoPE pairs) the scale follows
+    1 + 0.75 sin(2 pi t / P + phi) with a period P = 2^U(10, 13) tokens and a
+    phase phi ~ U(0, 2 pi) per (head, channel); the first 4 tokens of every
+    channel (attention sinks) have 4x the residual scale."""
+    f = torch.ones((2, w.heads, tokens, w.channels), device=device)
+    if not w.position_scale:
+        return f
+    g = _gen(device, seed_for(w.cid, "position", layer))
+    half = w.channels // 2
+    period = torch.exp2(torch.empty((w.heads, half), device=device).uniform_(10.0, 13.0, generator=g))
+    phase = torch.empty((w.heads, half), device=device).uniform_(0.0, 2.0 * math.pi, generator=g)
+    t = torch.arange(tokens, device=device, dtype=torch.float32)[None, :, None]
+    f[0, :, :, half:] = 1.0 + 0.75 * torch.sin(2.0 * math.pi * t / period[:, None, :] + phase[:, None, :])
+    f[:, :, :4, :] *= 4.0
+    return f
+
+
+def _draw(w: Workload, s, sig, reps: int, tokens: int, g, device, pos=None):
+    """KV and mu draws shaped [reps, 2, heads, tokens, D]; pos: the residual
+    scale by position [2, heads, tokens, D] (None: 1)."""
     shape = (reps, 2, w.heads, tokens, w.channels)
     s_b = s[None, :, :, None, :]
     if w.kv_dtype == E4M3:
@@ -131,6 +157,8 @@ def _draw(w: Workload, s, sig, reps: int, tokens: int, g, device):
         return kv.view(torch.uint8), mu.float()
     mu = (torch.randn(shape, generator=g, device=device) * s_b).to(torch.bfloat16)
     eps = _residual(w, shape, g, device)
+    if pos is not None:
+        eps = eps * pos[None]
     kv = (mu.float() + sig[None, :, :, None, :] * eps).to(torch.bfloat16)
     return kv, mu
 
@@ -142,7 +170,8 @@ def layer_data(w: Workload, layer: int, device="cpu", tokens: int | None = None)
     t = w.tokens if tokens is None else tokens
     s, sig = layer_params(w, layer, device)
     g = _gen(device, seed_for(w.cid, "data", layer))
-    kv, mu = _draw(w, s, sig, w.batch, t, g, device)
+    pos = position_factor(w, layer, t, device) if w.position_scale else None
+    kv, mu = _draw(w, s, sig, w.batch, t, g, device, pos)
     # [B, 2, H, T, D] -> [2, B, H, T, D]
     kv = kv.transpose(0, 1).reshape(w.planes_per_layer, t, w.channels).contiguous()
     mu = mu.transpose(0, 1).reshape(w.planes_per_layer, t, w.channels).contiguous()
@@ -160,14 +189,17 @@ def layer_calibration(w: Workload, layer: int, reps: int, device="cpu", tokens: 
     t = w.calib_tokens if tokens is None else tokens
     s, sig = layer_params(w, layer, device)
     g = _gen(device, seed_for(w.cid, "calib", layer))
-    kv, mu = _draw(w, s, sig, reps, t, g, device)
+    pos = position_factor(w, layer, t, device) if w.position_scale else None
+    kv, mu = _draw(w, s, sig, reps, t, g, device, pos)
     return kv.reshape(reps, 2 * w.heads, t, w.channels), mu.reshape(reps, 2 * w.heads, t, w.channels)
 
 
 def expand_sigma(w: Workload, sigma_kvh: torch.Tensor) -> torch.Tensor:
-    """sigma [2*H, D] per (kv, head) -> [2*B*H, D] per plane of one layer."""
-    return sigma_kvh.reshape(2, 1, w.heads, w.channels).expand(2, w.batch, w.heads, w.channels) \
-        .reshape(-1, w.channels).contiguous()
+    """sigma [2*H, ..., D] per (kv, head) -> [2*B*H, ..., D] per plane of one
+    layer (the middle dimension, if any, is the sigma block)."""
+    rest = tuple(sigma_kvh.shape[1:])
+    return sigma_kvh.reshape((2, 1, w.heads) + rest).expand((2, w.batch, w.heads) + rest) \
+        .reshape((-1,) + rest).contiguous()
 
 
 def marginal_samples(w: Workload, n: int = 1 << 20, device="cpu"):

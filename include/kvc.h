@@ -88,9 +88,20 @@ typedef struct kvc_params {
                                 of the lengths ceil(tokens / k) between 1024
                                 and 256 (or tokens, if fewer), the one with
                                 the least rounds x (length + 9), a round being
-                                8,192 chunks (one wave each) at once;
-                                chunk_tokens * channels < 2^29                  */
-    uint32_t reserved;       /* must be 0                                          */
+                                8,192 chunks (one wave each) at once (with
+                                sigma blocks: of the divisors of the block
+                                length in that range, else the largest
+                                divisor below it); chunk_tokens * channels
+                                < 2^29                                           */
+    uint32_t sigma_block_tokens; /* position-aware sigma ([blog] "limitations and
+                                future directions"): 0 = one sigma per (plane,
+                                channel), d_sigma [planes][channels]; B > 0 =
+                                one sigma per (plane, block of B tokens,
+                                channel), d_sigma [planes][ceil(tokens / B)]
+                                [channels], token t using block t / B.  B must
+                                be a multiple of chunk_tokens unless B >=
+                                tokens (KVC_ERR_INVALID).  Recorded in the
+                                stream header.                                 */
     int64_t planes;          /* G = layers * 2 * batch * kv_heads                  */
     int64_t tokens;          /* T                                                  */
     int64_t channels;        /* D, a positive multiple of 64                       */
@@ -182,6 +193,22 @@ int kvc_calibrate_sigma(const void* d_kv, const void* d_mu, int32_t kv_dtype,
                         int32_t mu_dtype, int64_t reps, int64_t planes, int64_t tokens,
                         int64_t channels, float sigma_floor, float* d_sigma_out,
                         void* d_workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * Position-aware sigma calibration ([blog] "limitations and future
+ * directions": a static per-channel sigma ignores how the residual changes
+ * with position).  As kvc_calibrate_sigma, per block of block_tokens
+ * tokens: d_sigma_out[planes][n_blocks][channels] with n_blocks =
+ * ceil(tokens / block_tokens), block j taking the mean over reps and the
+ * tokens [j * block_tokens, min((j + 1) * block_tokens, tokens)).
+ * block_tokens = 0 or >= tokens gives one block (the per-plane sigma).
+ * Workspace: KVC_CALIBRATE_WORKSPACE_BYTES(planes * n_blocks, channels).
+ */
+int kvc_calibrate_sigma_blocks(const void* d_kv, const void* d_mu, int32_t kv_dtype,
+                               int32_t mu_dtype, int64_t reps, int64_t planes, int64_t tokens,
+                               int64_t channels, int64_t block_tokens, float sigma_floor,
+                               float* d_sigma_out, void* d_workspace, uint64_t workspace_bytes,
+                               void* stream);
 
 /*
  * Empirical marginal ([wiki] "mixture distribution": an empirical BF16

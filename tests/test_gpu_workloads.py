@@ -19,7 +19,7 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_inputs(kvc, w, dev, layers=None, reps=None):
+def build_inputs(kvc, w, dev, layers=None, reps=None, sigma_block=0):
     layers = list(range(w.layers)) if layers is None else layers
     ppl = w.planes_per_layer
     G = len(layers) * ppl
@@ -27,7 +27,7 @@ def build_inputs(kvc, w, dev, layers=None, reps=None):
     mu_dt = torch.bfloat16 if w.mu_dtype == W.BF16 else torch.float32
     kv = torch.empty((G, w.tokens, w.channels), dtype=kv_dt, device=dev)
     mu = torch.empty((G, w.tokens, w.channels), dtype=mu_dt, device=dev)
-    sig = torch.empty((G, w.channels), dtype=torch.float32, device=dev)
+    sig = torch.empty(kvc.sigma_shape(G, w.tokens, w.channels, sigma_block), dtype=torch.float32, device=dev)
     reps = w.calib_reps if reps is None else reps
     for i, l in enumerate(layers):
         k, m = W.layer_data(w, l, device=dev)
@@ -35,7 +35,7 @@ def build_inputs(kvc, w, dev, layers=None, reps=None):
         mu[i * ppl:(i + 1) * ppl] = m
         if reps:
             ck, cm = W.layer_calibration(w, l, reps=reps, device=dev)
-            sig[i * ppl:(i + 1) * ppl] = W.expand_sigma(w, kvc.kvc_calibrate_sigma(ck, cm))
+            sig[i * ppl:(i + 1) * ppl] = W.expand_sigma(w, kvc.kvc_calibrate_sigma(ck, cm, block_tokens=sigma_block))
         else:
             sig[i * ppl:(i + 1) * ppl] = W.layer_sigma_true(w, l, device=dev)
     samples = W.marginal_samples(w, device=dev)
@@ -43,9 +43,9 @@ def build_inputs(kvc, w, dev, layers=None, reps=None):
     return kv, mu, sig, prefix
 
 
-def sampled_chunk_parity(kvc, w, kv, mu, sig, prefix, stream, n_sample=6, seed=0):
+def sampled_chunk_parity(kvc, w, kv, mu, sig, prefix, stream, n_sample=6, seed=0, tc=None, sigma_block=0):
     g_n, t_n, d_n = kv.shape
-    tc = w.chunk_tokens
+    tc = w.chunk_tokens if tc is None else tc
     gof, tcof, kof, lnof = O.chunk_layout(g_n, t_n, d_n, tc)
     n_chunks = gof.size
     rng = np.random.default_rng(seed)
@@ -61,7 +61,10 @@ def sampled_chunk_parity(kvc, w, kv, mu, sig, prefix, stream, n_sample=6, seed=0
         sl = (slice(g, g + 1), slice(t0, t0 + ln), slice(64 * k, 64 * k + 64))
         kvs = W.to_numpy_bits(kv[sl].contiguous())
         mus = W.to_numpy_bits(mu[sl].contiguous())
-        sgs = sig[g:g + 1, 64 * k:64 * k + 64].cpu().numpy()
+        if sigma_block:
+            sgs = sig[g:g + 1, t0 // sigma_block, 64 * k:64 * k + 64].cpu().numpy()
+        else:
+            sgs = sig[g:g + 1, 64 * k:64 * k + 64].cpu().numpy()
         gpu_payload = stream[pay_off + int(directory[cid]):pay_off + int(directory[cid + 1])].cpu().numpy().tobytes()
         want = O.encode_chunks(kvs, mus, sgs, pref, w.kv_dtype, w.mu_dtype, *w_, tc, [0])[0]
         assert gpu_payload == want, f"chunk {cid} (plane {g}, tokens {t0}+{ln}, group {k}) differs"
@@ -87,6 +90,37 @@ def test_full_size_round_trip_and_sampled_parity(kvc, cuda, wid, layers):
     # the encoder is deterministic: a second call gives the same bytes
     st2 = enc(kv, mu, sig, prefix)
     assert torch.equal(st2, st)
+
+
+def test_position_aware_sigma_full_size(kvc, cuda):
+    """The position-varying workload at full size with one sigma per 512
+    tokens, calibrated per block on the device, in the configuration the
+    benchmark times (the library's default chunk length): round trip,
+    sampled chunks against the oracle, and fewer bits than one sigma per
+    plane."""
+    w = W.WORKLOADS[5]
+    blk = 512
+    say(f"workload 5: {w.name}, sigma blocks of {blk} tokens")
+    kv, mu, sig, prefix = build_inputs(kvc, w, cuda, reps=8, sigma_block=blk)
+    torch.cuda.synchronize()
+    g, t, d = kv.shape
+    wts = (w.w_narrow_bp, w.w_wide_bp)
+    enc = kvc.Encoder(kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, g, t, d, wts, 0, blk), cuda)
+    st = enc(kv, mu, sig, prefix)
+    p, _ = kvc.kvc_stream_info(st[:128].cpu().numpy())
+    assert p.sigma_block_tokens == blk and blk % p.chunk_tokens == 0
+    say(f"encoded {kv.numel()} scalars at {p.chunk_tokens}-token chunks -> {8.0 * st.numel() / kv.numel():.4f} bits/scalar")
+    out = kvc.kvc_decode(st, mu, sig, prefix)
+    assert torch.equal(out, kv.view(torch.int16))
+    sampled_chunk_parity(kvc, w, kv, mu, sig, prefix, st, tc=p.chunk_tokens, sigma_block=blk)
+    # one sigma per plane over the same calibration draws costs more
+    _, _, sig1, _ = build_inputs(kvc, w, cuda, layers=[0], reps=8)
+    ppl = w.planes_per_layer
+    b_plane = kvc.kvc_estimate_bits(kv[:ppl], mu[:ppl], sig1, prefix, wts)[0]
+    b_block = kvc.kvc_estimate_bits(kv[:ppl], mu[:ppl], sig[:ppl], prefix, wts, sigma_block_tokens=blk,
+                                    chunk_tokens=p.chunk_tokens)[0]
+    say(f"layer 0 model bits: per plane {b_plane:.4f}, per {blk}-token block {b_block:.4f}")
+    assert b_block < b_plane
 
 
 def test_qwen3_0p6b_shaped_full_parity(kvc, cuda):

@@ -58,7 +58,8 @@ def test_encode_sizes(kvc):
     n_chunks = w.planes * 4 * 2
     assert max_stream == 128 + 8 * (n_chunks + 1) + n_chunks * (512 + 2 * 2 * 64 * 1024)
     assert ws >= n_chunks * (512 + 4 + 8 + 4 * 64 * 1024)
-    for bad in [dict(channels=96), dict(planes=0), dict(tokens=0), dict(reserved=1), dict(kv_dtype=2),
+    for bad in [dict(channels=96), dict(planes=0), dict(tokens=0), dict(sigma_block_tokens=30, chunk_tokens=20),
+                dict(sigma_block_tokens=1, chunk_tokens=0, planes=1 << 30, tokens=1 << 10), dict(kv_dtype=2),
                 dict(mu_dtype=1), dict(w_narrow_bp=9000, w_wide_bp=1001), dict(chunk_tokens=1 << 21),
                 dict(channels=1 << 21, chunk_tokens=1024)]:
         q = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, 4, 100, 128)
@@ -92,6 +93,20 @@ def test_default_chunk_length(kvc, planes, tokens, channels, expect):
         assert other != auto
 
 
+@pytest.mark.parametrize("planes,tokens,block,expect", [
+    (2304, 4096, 1024, 256),     # divisors 1024, 512, 256: 3, 5, 9 rounds of 1033, 521, 265
+    (448, 1024, 300, 300),       # the only divisor of 300 in [256, 1024]
+    (3, 45, 16, 16),             # blocks shorter than the floor: the block itself
+    (3, 45, 100, 45),            # one block covers every token: the rule without blocks
+    (4, 2000, 1031, 1),          # a prime block length above 1024: its divisor 1
+])
+def test_default_chunk_length_with_sigma_blocks(kvc, planes, tokens, block, expect):
+    """With sigma blocks shorter than the tokens, the default chunk length is
+    the best divisor of the block length (no chunk straddles two blocks)."""
+    mk = lambda tc: kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, planes, tokens, 128, (9500, 300), tc, block)
+    assert kvc.kvc_encode_sizes(mk(0)) == kvc.kvc_encode_sizes(mk(expect))
+
+
 def oracle_stream(kv_dtype=O.BF16, w=(9500, 300), tc=16):
     kv, mu, sig, samples = W.tiny_case(7, kv_dtype=kv_dtype)
     mu_dtype = O.BF16 if kv_dtype == O.BF16 else O.F32
@@ -110,7 +125,21 @@ def test_stream_info_reads_oracle_headers(kvc):
         assert (p.planes, p.tokens, p.channels) == (h["planes"], h["tokens"], h["channels"])
 
 
-@pytest.mark.parametrize("offset", [0, 4, 8, 10, 13, 16, 24, 36, 56, 64, 100])
+def test_stream_info_reads_the_sigma_block_field(kvc):
+    kv, mu, sig, samples = W.tiny_case(3, 2, 45, 128, O.BF16)
+    kv, mu, sig, samples = W.to_numpy_bits(kv), W.to_numpy_bits(mu), sig.numpy(), W.to_numpy_bits(samples)
+    pref = O.build_marginal(samples, O.BF16, 9500, 300)
+    sig3 = np.repeat(sig[:, None, :], 3, axis=1)
+    st = O.encode(kv, mu, sig3, pref, O.BF16, O.BF16, 9500, 300, 8, sigma_block_tokens=16)
+    p, total = kvc.kvc_stream_info(st[:128])
+    assert p.sigma_block_tokens == 16 and p.chunk_tokens == 8 and total == len(st)
+    bad = bytearray(st[:128])
+    bad[88] = 20                                       # 20 is not a multiple of the 8-token chunks
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_stream_info(bytes(bad))
+
+
+@pytest.mark.parametrize("offset", [0, 4, 8, 10, 13, 16, 24, 36, 56, 64, 92, 100])
 def test_stream_info_rejects_damaged_headers(kvc, offset):
     st = bytearray(oracle_stream()[:128])
     st[offset] ^= 0x41
