@@ -240,6 +240,8 @@ def main():
                     help="(per-layer workload 4) also time the host-offload reload: pinned streams, copies overlapped with decode")
     ap.add_argument("--sigma-block", type=int, default=0,
                     help="position-aware sigma: one sigma per block of this many tokens (0 = per plane)")
+    ap.add_argument("--paged", type=int, default=0,
+                    help="decode straight into a paged KV cache with pages of this many tokens (shuffled table)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="after the timed steps, copy 1 GiB once (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -293,6 +295,19 @@ def main():
 
     fallback = [0]
     stream_total = [0]
+    paged = None
+    if args.paged:
+        if per_layer or w.kv_dtype != W.BF16:
+            raise SystemExit("--paged is defined on the one-call bf16 workloads")
+        pt = args.paged
+        max_pages = -(-w.tokens // pt)
+        num_pages = w.batch * max_pages
+        gen = torch.Generator(device="cpu").manual_seed(11)
+        table = torch.randperm(num_pages, generator=gen).to(torch.int32).reshape(w.batch, max_pages).to(dev)
+        pools = [torch.empty((num_pages, pt, w.heads, w.channels), dtype=torch.int16, device=dev)
+                 for _ in range(2 * w.layers)]
+        paged = kvc.PagedKV(pools, table, pt)
+        log(f"[bench] paged output: {len(pools)} pools of {num_pages} x {pt}-token pages, shuffled table")
 
     def step(stats=None):
         e_ms, d_ms = [0.0] * 4, [0.0] * 2
@@ -300,7 +315,10 @@ def main():
         for sl in parts:
             ei, di = {}, {}
             st = enc(kv[sl], mu[sl], sigma[sl], prefix, info=ei)
-            rc = kvc.kvc_decode_into(st, mu[sl], sigma[sl], prefix, kv_out[sl], dws, info=di)
+            if paged is not None:
+                rc = kvc.kvc_decode_paged(st, mu[sl], sigma[sl], prefix, paged, dws, info=di)
+            else:
+                rc = kvc.kvc_decode_into(st, mu[sl], sigma[sl], prefix, kv_out[sl], dws, info=di)
             if rc != kvc.KVC_OK:
                 raise kvc.KvcError(rc, "kvc_decode")
             e_ms = [a + b for a, b in zip(e_ms, ei["stage_ms"])]
@@ -329,6 +347,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("[bench] traffic probe: copied 1 GiB")
+    scatter_ms = None
+    if paged is not None:
+        # read the pages back through the table into the contiguous layout
+        tl = paged.block_table.long()
+        bh = w.batch * w.heads
+        for lk, pool in enumerate(paged.pools):
+            kv_out[lk * bh:(lk + 1) * bh] = pool[tl].reshape(w.batch, -1, w.heads, w.channels)[:, :w.tokens] \
+                .permute(0, 2, 1, 3).reshape(bh, w.tokens, w.channels)
+        # the unfused alternative needs a second pass over the decoded KV
+        # (read and write every byte once): at least one device copy of it
+        dst = torch.empty_like(kv_out)
+        dst.copy_(kv_out)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(3):
+            dst.copy_(kv_out)
+        ev1.record()
+        torch.cuda.synchronize()
+        scatter_ms = ev0.elapsed_time(ev1) / 3
+        del dst
     ok = torch.equal(kv_out, kv.view(torch.int16) if kv_size == 2 else kv)
     if not ok:
         raise SystemExit("decoded KV differs from the input")
@@ -353,7 +391,8 @@ def main():
     # algorithmic bytes of the coding kernels: KV and mu in, words and states
     # out (encode); words and states and mu in, KV out (decode)
     alg = float(kv_size + mu_size) * n + stream_bytes
-    traffic = measured_traffic() if args.workload == 2 and tc == w.chunk_tokens else {}
+    traffic = measured_traffic() if args.workload == 2 and tc == w.chunk_tokens and not args.paged \
+        and not args.sigma_block else {}
 
     def roofline(kernel, avg_ms):
         a = alg / (avg_ms * 1e-3) / 1e9
@@ -382,6 +421,8 @@ def main():
             "scalars": n, "mixture_bp": list(weights), "chunk_tokens": tc, "sigma_block_tokens": args.sigma_block,
             "sigma_calibration": f"{reps}x{w.calib_tokens} tokens per layer",
             "mu_dtype": "bf16" if mu_size == 2 else "fp32", "calls_per_step": len(parts),
+            "decode_output": f"paged, {args.paged}-token pages" if args.paged else "contiguous",
+            "second_pass_copy_ms": scatter_ms,
         },
         "encode_gbps": raw / (enc_total * 1e-3) / 1e9,
         "decode_gbps": raw / (dec_total * 1e-3) / 1e9,

@@ -389,14 +389,28 @@ int kvc_stream_info(const void* h_header, uint64_t header_bytes, kvc_params* h_p
     return KVC_OK;
 }
 
-int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const float* d_sigma,
-               const uint32_t* d_prefix, void* d_kv_out, void* d_workspace, uint64_t workspace_bytes,
-               void* stream, kvc_decode_info* h_info) {
-    if (!d_in || !d_mu || !d_sigma || !d_kv_out || !d_workspace) return KVC_ERR_INVALID;
+}  // extern "C"
+
+namespace {
+
+// kvc_decode and kvc_decode_paged: the output is d_kv_out, or the paged
+// pools when `paged` is not null.
+int decode_common(const void* d_in, uint64_t in_bytes, const void* d_mu, const float* d_sigma,
+                  const uint32_t* d_prefix, void* d_kv_out, const kvc_paged_kv* paged, void* d_workspace,
+                  uint64_t workspace_bytes, void* stream, kvc_decode_info* h_info) {
+    if (!d_in || !d_mu || !d_sigma || (!d_kv_out && !paged) || !d_workspace) return KVC_ERR_INVALID;
     if (workspace_bytes < KVC_DECODE_WORKSPACE_BYTES) return KVC_ERR_CAPACITY;
     if (!aligned(d_in, 8) || !aligned(d_workspace, 256) || !aligned(d_sigma, 4) || !aligned(d_prefix, 4) ||
         !aligned(d_kv_out, 2) || !aligned(d_mu, 2))
         return KVC_ERR_INVALID;
+    if (paged) {
+        if (!paged->d_pools || !paged->d_block_table || !aligned(paged->d_pools, 8) ||
+            !aligned(paged->d_block_table, 4) || paged->reserved != 0 || paged->page_tokens < 1 ||
+            paged->batch < 1 || paged->heads < 1 || paged->batch > 0x7FFFFFFF || paged->heads > 0x7FFFFFFF ||
+            paged->num_pages < 1 || paged->num_pages > 0x7FFFFFFF || paged->max_pages < 1 ||
+            paged->max_pages > kMaxScalars || paged->batch * paged->max_pages > kMaxScalars)
+            return KVC_ERR_INVALID;
+    }
     if (in_bytes < KVC_HEADER_BYTES) return KVC_ERR_CORRUPT;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
@@ -419,6 +433,24 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     if (te && !d_prefix) return KVC_ERR_INVALID;
     const uint32_t* prefix = te ? d_prefix : nullptr;
     if (!data_aligned(p.kv_dtype, p.mu_dtype, d_kv_out, d_mu, d_sigma, d_prefix)) return KVC_ERR_INVALID;
+    kvc::PagedOut po{};
+    if (paged) {
+        // planes ordered (layer, kv, batch, head); every token's page inside the table's rows
+        const int64_t per_layer = 2 * paged->batch * paged->heads;
+        if (g.planes % per_layer != 0) return KVC_ERR_INVALID;
+        if (paged->max_pages < (g.tokens + paged->page_tokens - 1) / paged->page_tokens) return KVC_ERR_INVALID;
+        // a page's bytes fit 32 bits
+        const int64_t esize = p.kv_dtype == KVC_BF16 ? 2 : 1;
+        if (paged->heads * g.channels * esize * int64_t(paged->page_tokens) >= (int64_t(1) << 32))
+            return KVC_ERR_INVALID;
+        po.pools = paged->d_pools;
+        po.block_table = paged->d_block_table;
+        po.max_pages = paged->max_pages;
+        po.num_pages = paged->num_pages;
+        po.page_tokens = paged->page_tokens;
+        po.heads = static_cast<uint32_t>(paged->heads);
+        po.batch = static_cast<uint32_t>(paged->batch);
+    }
 
     Control* ctl = static_cast<Control*>(d_workspace);
     // escape bucket table after the control block: the smallest shift that
@@ -434,6 +466,9 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     timer.mark(0);
     if ((e = kvc::launch_side_hash(d_sigma, sigma_words(g), prefix, prefix ? n_sym + 1u : 0u, ctl, s)) !=
         hipSuccess)
+        return KVC_ERR_DEVICE;
+    if (paged && (e = kvc::launch_check_pages(po, (g.tokens + po.page_tokens - 1) / po.page_tokens, ctl, s)) !=
+                     hipSuccess)
         return KVC_ERR_DEVICE;
     if ((e = kvc::launch_escape_buckets(prefix ? prefix : phi.zero, n_sym, shift, n_buckets, p.kv_dtype, buckets, s)) !=
         hipSuccess)
@@ -459,8 +494,9 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     da.buckets = buckets;
     da.bucket_shift = shift;
     da.kv_out = d_kv_out;
+    da.paged = po;
     da.ctl = ctl;
-    if ((e = kvc::launch_decode(da, p.kv_dtype, p.mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    if ((e = kvc::launch_decode(da, p.kv_dtype, p.mu_dtype, paged != nullptr, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(2);
     Control host;
     if ((e = hipMemcpyAsync(&host, ctl, sizeof(host), hipMemcpyDeviceToHost, s)) != hipSuccess) return KVC_ERR_DEVICE;
@@ -468,9 +504,29 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const floa
     timer.read();
     if (h_info) h_info->fallback_symbols = host.misses;
     if (host.side_hash != hash) return KVC_ERR_MISMATCH;
-    if (host.flags & kvc::kFlagBadSigma) return KVC_ERR_INVALID;
+    if (host.flags & (kvc::kFlagBadSigma | kvc::kFlagBadPage)) return KVC_ERR_INVALID;
     if (host.flags & kvc::kFlagCorrupt) return KVC_ERR_CORRUPT;
     return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const float* d_sigma,
+               const uint32_t* d_prefix, void* d_kv_out, void* d_workspace, uint64_t workspace_bytes,
+               void* stream, kvc_decode_info* h_info) {
+    if (!d_kv_out) return KVC_ERR_INVALID;
+    return decode_common(d_in, in_bytes, d_mu, d_sigma, d_prefix, d_kv_out, nullptr, d_workspace, workspace_bytes,
+                         stream, h_info);
+}
+
+int kvc_decode_paged(const void* d_in, uint64_t in_bytes, const void* d_mu, const float* d_sigma,
+                     const uint32_t* d_prefix, const kvc_paged_kv* h_paged, void* d_workspace,
+                     uint64_t workspace_bytes, void* stream, kvc_decode_info* h_info) {
+    if (!h_paged) return KVC_ERR_INVALID;
+    return decode_common(d_in, in_bytes, d_mu, d_sigma, d_prefix, nullptr, h_paged, d_workspace, workspace_bytes,
+                         stream, h_info);
 }
 
 int kvc_calibrate_sigma(const void* d_kv, const void* d_mu, int32_t kv_dtype, int32_t mu_dtype, int64_t reps,

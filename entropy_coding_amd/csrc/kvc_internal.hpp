@@ -13,6 +13,7 @@ enum : uint32_t {
     kFlagBadSigma = 1u,
     kFlagCorrupt = 2u,
     kFlagCapacity = 4u,
+    kFlagBadPage = 8u,                  // a block-table entry outside the page pool
 };
 
 // Control block at the head of every workspace (cleared by a kernel).
@@ -83,6 +84,18 @@ struct CompactArgs {
     Control* ctl;
 };
 
+// Decoded rows written straight into paged KV pools: pool (layer, kv) is
+// [num_pages][page_tokens][heads][channels]; plane g = ((layer * 2 + kv) *
+// batch + b) * heads + h keeps token t at page block_table[b][t /
+// page_tokens], row t % page_tokens.
+struct PagedOut {
+    void* const* pools;                 // [layers * 2] pool base pointers
+    const int32_t* block_table;         // [batch][max_pages]
+    int64_t max_pages, num_pages;
+    uint32_t page_tokens, heads;
+    uint32_t batch, pad;
+};
+
 struct DecodeArgs {
     ChunkGeom geom;
     const uint8_t* payload;             // first payload byte of the stream
@@ -96,7 +109,8 @@ struct DecodeArgs {
     const float* aim;                   // the aim table, kAimFloats floats
     const uint32_t* buckets;            // escape bucket table (launch_escape_buckets)
     uint32_t bucket_shift;
-    void* kv_out;
+    void* kv_out;                       // contiguous output [planes][tokens][channels], or
+    PagedOut paged;                     // the paged output (launch_decode with paged = true)
     Control* ctl;
 };
 
@@ -128,7 +142,9 @@ hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStr
 hipError_t launch_scan(const uint32_t* chunk_words, int64_t n_chunks,
                        unsigned long long* directory, Control* ctl, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, bool paged, hipStream_t s);
+// Sets kFlagBadPage if a block-table entry of columns [0, used) lies outside the pool.
+hipError_t launch_check_pages(const PagedOut& p, int64_t used, Control* ctl, hipStream_t s);
 // Bucket table of Q(b) = b + prefix[b] for the decoder's floor-and-escape
 // lookup: entry j = (s_j << 16) | pattern of s_j, where s_j is the largest
 // s < n_sym with Q(s) <= j << shift (entries order as their symbols).

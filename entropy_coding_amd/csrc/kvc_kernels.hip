@@ -901,7 +901,7 @@ struct WordRing {
     }
 };
 
-template <int KV, int MU>
+template <int KV, int MU, bool PAGED>
 __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(64))) k_decode(DecodeArgs a) {
     __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
     __shared__ __align__(16) float2 s_aim[kAimEntries + 1];
@@ -961,6 +961,40 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
     const uint64_t out_base = reinterpret_cast<uint64_t>(static_cast<KB*>(a.kv_out) + row0);
     const uint32_t mu_lane = static_cast<uint32_t>(lane) * static_cast<uint32_t>(sizeof(MT));
     const uint32_t kv_lane = static_cast<uint32_t>(lane) * static_cast<uint32_t>(sizeof(KB));
+
+    // paged output: page_row is the byte address of the current token's row
+    // (this chunk's 64 channels of head h), a token further each step; at a
+    // page boundary the next entry of the sequence's table row names the
+    // page.  Every entry the call reads was checked before the launch
+    // (k_check_pages; the decode does nothing when one is bad).  Reads of
+    // the pool pointer and of table entries come back in vector registers
+    // and are moved to scalar ones, where the stores take their base address.
+    uint64_t page_row = 0, page_base = 0;
+    const int32_t* page_entry = nullptr;
+    uint32_t page_left = 0, tok_bytes = 0, page_bytes = 0;
+    auto page_at = [&](uint32_t row) -> uint64_t {
+        const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(*page_entry));
+        return page_base + uint64_t(e) * page_bytes + uint64_t(row) * tok_bytes;
+    };
+    if constexpr (PAGED) {
+        if (a.ctl->flags & kFlagBadPage) return;                // the same in every wave of the launch
+        const int64_t per_kv = int64_t(a.paged.batch) * a.paged.heads;
+        const int64_t lk = cp.g / per_kv;                       // layer * 2 + kv
+        const uint32_t bh = static_cast<uint32_t>(cp.g - lk * per_kv);
+        const uint32_t b = bh / a.paged.heads, h = bh - b * a.paged.heads;
+        const uint64_t pool = reinterpret_cast<uint64_t>(a.paged.pools[lk]);
+        // (the builtin returns int: each half is taken as unsigned before widening)
+        const uint32_t pool_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pool)));
+        const uint32_t pool_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(pool >> 32)));
+        tok_bytes = a.paged.heads * D * static_cast<uint32_t>(sizeof(KB));      // below 2^32 (checked by the caller)
+        page_bytes = a.paged.page_tokens * tok_bytes;
+        page_base = ((uint64_t(pool_hi) << 32) | pool_lo) + (h * D + cp.k * 64u) * static_cast<uint32_t>(sizeof(KB));
+        const uint32_t page_i = cp.t0 / a.paged.page_tokens;
+        const uint32_t in_page = cp.t0 - page_i * a.paged.page_tokens;
+        page_entry = a.paged.block_table + int64_t(b) * a.paged.max_pages + page_i;
+        page_left = a.paged.page_tokens - in_page;
+        page_row = page_at(in_page);
+    }
 
     uint32_t rp = 0;
     unsigned long long misses = 0;                   // wave-uniform
@@ -1043,22 +1077,36 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
                 }
             }
         }
-        // the symbol is final: store it now, so that the store is issued
-        // after this step's prefix read and before the next one (the vector
-        // memory counter is in order, so a store issued later would hold up
-        // the wait for the next step's prefix read until it completes)
+        // x = f (x >> 31) + rank, f = f_G + 1 + (prefix[s + 1] - prefix[s]);
+        // x < 2^63, so x >> 31 fits 32 bits
+        const uint32_t f = (c.g1 - c.g0) + 1u + (c.p1 - c.p0);
+        // the symbol is final: store it right after this step's wait for its
+        // prefix read (f is an input of the store only to hold it there).
+        // The vector memory counter is in order and counts stores: a store
+        // issued before that wait would be waited for too, and one issued
+        // in the next step would hold up the next wait.
         const uint32_t ooff = t * D * static_cast<uint32_t>(sizeof(KB));
-        if constexpr (KV == kBF16)
+        if constexpr (PAGED) {
+            if constexpr (KV == kBF16)
+                __asm__ volatile("global_store_short_d16_hi %0, %1, %2" : : "v"(kv_lane), "v"(kb), "s"(page_row), "v"(f));
+            else __asm__ volatile("global_store_byte %0, %1, %2" : : "v"(kv_lane), "v"(kb), "s"(page_row), "v"(f));
+            page_row += tok_bytes;
+            if (--page_left == 0 && t + 1u < cp.len) {  // the next token starts a page
+                ++page_entry;
+                page_left = a.paged.page_tokens;
+                page_row = page_at(0);
+            }
+        } else if constexpr (KV == kBF16)
         {
             // the pattern is the high half of the candidate word: a high-half
             // store from a scalar row address and the lane's offset
             const uint64_t row = out_base + ooff;
-            __asm__ volatile("global_store_short_d16_hi %0, %1, %2" : : "v"(kv_lane), "v"(kb), "s"(row));
+            __asm__ volatile("global_store_short_d16_hi %0, %1, %2" : : "v"(kv_lane), "v"(kb), "s"(row), "v"(f));
         }
-        else __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(kb), outb, kv_lane, ooff, 0);
-        // x = f (x >> 31) + rank, f = f_G + 1 + (prefix[s + 1] - prefix[s]);
-        // x < 2^63, so x >> 31 fits 32 bits
-        const uint32_t f = (c.g1 - c.g0) + 1u + (c.p1 - c.p0);
+        else {
+            __asm__ volatile("" : : "v"(f));
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(kb), outb, kv_lane, ooff, 0);
+        }
         x = static_cast<unsigned long long>(f) * static_cast<uint32_t>(x >> kLog2M) + (target - c.g0);
 
         // refill: a lane takes one word when x < 2^47 and a second one when
@@ -1122,16 +1170,41 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
     if (lane == 0 && misses) atomicAdd(&a.ctl->misses, misses);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s) {
+// Every block-table entry a paged decode reads (rows 0..batch-1, columns
+// 0..used-1) must name a page of the pool; one that does not sets the flag
+// the decoder reads before its first store.
+__global__ void __launch_bounds__(256) k_check_pages(const int32_t* __restrict__ table, int64_t batch,
+                                                     int64_t max_pages, int64_t used, int64_t num_pages,
+                                                     Control* __restrict__ ctl) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= batch * used) return;
+    const int32_t e = table[(i / used) * max_pages + i % used];
+    if (e < 0 || int64_t(e) >= num_pages) atomicOr(&ctl->flags, kFlagBadPage);
+}
+
+hipError_t launch_check_pages(const PagedOut& p, int64_t used, Control* ctl, hipStream_t s) {
+    const int64_t n = int64_t(p.batch) * used;
+    hipLaunchKernelGGL(k_check_pages, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s, p.block_table,
+                       int64_t(p.batch), p.max_pages, used, p.num_pages, ctl);
+    return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t launch_decode_as(const DecodeArgs& a, int kv_dtype, int mu_dtype, dim3 grid, dim3 block, hipStream_t s) {
+    if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kBF16, kBF16, PAGED>), grid, block, 0, s, a);
+    else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_decode<kBF16, kF32, PAGED>), grid, block, 0, s, a);
+    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kE4M3, kBF16, PAGED>), grid, block, 0, s, a);
+    else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_decode<kE4M3, kF32, PAGED>), grid, block, 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, bool paged, hipStream_t s) {
     constexpr int waves = kDecodeBlock / 64;
     const uint64_t blocks = (static_cast<uint64_t>(a.geom.n_chunks) + waves - 1) / waves;
     const dim3 grid(static_cast<uint32_t>(blocks)), block(kDecodeBlock);
-    if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kBF16, kBF16>), grid, block, 0, s, a);
-    else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_decode<kBF16, kF32>), grid, block, 0, s, a);
-    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kE4M3, kBF16>), grid, block, 0, s, a);
-    else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_decode<kE4M3, kF32>), grid, block, 0, s, a);
-    else return hipErrorInvalidValue;
-    return hipGetLastError();
+    return paged ? launch_decode_as<true>(a, kv_dtype, mu_dtype, grid, block, s)
+                 : launch_decode_as<false>(a, kv_dtype, mu_dtype, grid, block, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -27,7 +27,7 @@ DECODE_STAGES = 2     # side-information checksum + escape bucket table, decodin
 
 EXPORTS = [
     "kvc_version", "kvc_status_string", "kvc_phi_tables", "kvc_encode_sizes", "kvc_encode",
-    "kvc_stream_info", "kvc_decode", "kvc_calibrate_sigma", "kvc_calibrate_sigma_blocks",
+    "kvc_stream_info", "kvc_decode", "kvc_decode_paged", "kvc_calibrate_sigma", "kvc_calibrate_sigma_blocks",
     "kvc_build_marginal", "kvc_estimate_bits", "kvc_cdf_table",
 ]
 
@@ -42,6 +42,14 @@ class kvc_params(ctypes.Structure):
         ("w_narrow_bp", ctypes.c_uint32), ("w_wide_bp", ctypes.c_uint32),
         ("chunk_tokens", ctypes.c_uint32), ("sigma_block_tokens", ctypes.c_uint32),
         ("planes", ctypes.c_int64), ("tokens", ctypes.c_int64), ("channels", ctypes.c_int64),
+    ]
+
+
+class kvc_paged_kv(ctypes.Structure):
+    _fields_ = [
+        ("d_pools", ctypes.c_void_p), ("d_block_table", ctypes.c_void_p),
+        ("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("max_pages", ctypes.c_int64),
+        ("num_pages", ctypes.c_int64), ("page_tokens", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
     ]
 
 
@@ -75,6 +83,8 @@ _lib_encode_sizes = _sig("kvc_encode_sizes", ctypes.c_int, [ctypes.POINTER(kvc_p
 _lib_encode = _sig("kvc_encode", ctypes.c_int, [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _U64, ctypes.POINTER(_U64), _P, _U64, _P, _P])
 _lib_stream_info = _sig("kvc_stream_info", ctypes.c_int, [_P, _U64, ctypes.POINTER(kvc_params), ctypes.POINTER(_U64)])
 _lib_decode = _sig("kvc_decode", ctypes.c_int, [_P, _U64, _P, _P, _P, _P, _P, _U64, _P, _P])
+_lib_decode_paged = _sig("kvc_decode_paged", ctypes.c_int,
+                         [_P, _U64, _P, _P, _P, ctypes.POINTER(kvc_paged_kv), _P, _U64, _P, _P])
 _lib_calibrate = _sig("kvc_calibrate_sigma", ctypes.c_int,
                       [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _U64, _P])
 _lib_calibrate_blocks = _sig("kvc_calibrate_sigma_blocks", ctypes.c_int,
@@ -241,6 +251,42 @@ def kvc_decode_into(stream_bytes, mu, sigma, prefix, kv_out, workspace, stream=N
     st = _lib_decode(_ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _ptr(sigma), _ptr(prefix),
                      _ptr(kv_out), _ptr(workspace), workspace.numel(), _stream(stream),
                      ctypes.byref(inf) if inf is not None else None)
+    if inf is not None:
+        info["stage_ms"] = list(inf.stage_ms)
+        info["fallback_symbols"] = inf.fallback_symbols
+    return st
+
+
+class PagedKV:
+    """A paged KV cache as the library sees it: one pool per (layer, kv),
+    each [num_pages, page_tokens, heads, channels], and a block table
+    [batch, max_pages] of int32 page numbers shared by every pool.  Holds
+    the device array of pool pointers that the call reads."""
+
+    def __init__(self, pools, block_table: torch.Tensor, page_tokens: int):
+        pools = list(pools)
+        for t in pools:
+            _need(t, "pool")
+        _need(block_table, "block_table")
+        if block_table.dtype != torch.int32 or block_table.dim() != 2:
+            raise ValueError("block_table must be int32 [batch, max_pages]")
+        n_pages, pt, heads, _ = pools[0].shape
+        if pt != page_tokens or any(tuple(t.shape) != tuple(pools[0].shape) for t in pools):
+            raise ValueError("pools must all be [num_pages, page_tokens, heads, channels]")
+        self.pools = pools
+        self.block_table = block_table
+        self.ptrs = torch.tensor([t.data_ptr() for t in pools], dtype=torch.int64, device=block_table.device)
+        self.desc = kvc_paged_kv(self.ptrs.data_ptr(), block_table.data_ptr(), block_table.shape[0], heads,
+                                 block_table.shape[1], n_pages, page_tokens, 0)
+
+
+def kvc_decode_paged(stream_bytes, mu, sigma, prefix, paged: PagedKV, workspace, stream=None,
+                     info: dict | None = None) -> int:
+    """Decode straight into a paged KV cache; returns the status."""
+    inf = kvc_decode_info() if info is not None else None
+    st = _lib_decode_paged(_ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _ptr(sigma), _ptr(prefix),
+                           ctypes.byref(paged.desc), _ptr(workspace), workspace.numel(), _stream(stream),
+                           ctypes.byref(inf) if inf is not None else None)
     if inf is not None:
         info["stage_ms"] = list(inf.stage_ms)
         info["fallback_symbols"] = inf.fallback_symbols

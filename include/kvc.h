@@ -175,6 +175,45 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu,
                kvc_decode_info* h_info);
 
 /*
+ * Paged output for kvc_decode_paged: the serving engine's KV cache as page
+ * pools.  Pool p = 2 * layer + kv (K then V of each layer) is laid out
+ * [num_pages][page_tokens][heads][channels] in the stream's KV dtype; the
+ * stream's planes are ordered (layer, kv, batch, head), so planes = layers *
+ * 2 * batch * heads; token t of sequence b lives in page
+ * block_table[b * max_pages + t / page_tokens], row t % page_tokens.
+ */
+typedef struct kvc_paged_kv {
+    void* const* d_pools;          /* device array of layers * 2 pool base pointers  */
+    const int32_t* d_block_table;  /* device [batch][max_pages] physical page numbers */
+    int64_t batch;                 /* sequences                                       */
+    int64_t heads;                 /* KV heads per pool row                           */
+    int64_t max_pages;             /* row stride of the table, >= ceil(tokens /
+                                      page_tokens)                                    */
+    int64_t num_pages;             /* pages in every pool, < 2^31                    */
+    uint32_t page_tokens;          /* tokens per page                                 */
+    uint32_t reserved;             /* must be 0                                       */
+} kvc_paged_kv;
+
+/*
+ * Decoder fused into the consumer's layout ([blog] "application scenarios
+ * and deployment parameters": a compressed prefix-cache entry is
+ * decompressed when it is hit, and decoding has to keep up with the rate
+ * at which the cache is consumed).  As kvc_decode, but every decoded row
+ * goes straight to its page of the paged KV cache described by *h_paged
+ * (host struct; its pointers are device pointers) instead of a contiguous
+ * [planes][tokens][channels] array: no second pass over the KV.  Rows of
+ * pages the table does not name are left untouched.  KVC_ERR_INVALID if the
+ * planes are not a multiple of 2 * batch * heads, the table is too narrow,
+ * a page holds 2^32 bytes or more, or (checked on the device before the
+ * decode) an entry of the columns the tokens use lies outside
+ * [0, num_pages): then nothing is written.
+ */
+int kvc_decode_paged(const void* d_in, uint64_t in_bytes, const void* d_mu,
+                     const float* d_sigma, const uint32_t* d_prefix, const kvc_paged_kv* h_paged,
+                     void* d_workspace, uint64_t workspace_bytes, void* stream,
+                     kvc_decode_info* h_info);
+
+/*
  * Sigma calibration ([wiki] "predictor choice": per-(kv, head, channel)
  * variance calibrated on data, then frozen; [blog] "deployment parameters":
  * 128 sequences of 1024 tokens).  d_kv and d_mu are [reps][planes][tokens]

@@ -790,6 +790,39 @@ __all__ += ["chunk_payload", "encode_chunks", "wrap_chunk"]
 
 
 # ---------------------------------------------------------------------------
+# Paged output: decoded rows placed in a paged KV cache
+# ---------------------------------------------------------------------------
+def scatter_to_pages(kv, batch: int, heads: int, block_table, page_tokens: int, num_pages: int,
+                     fill: int = 0) -> np.ndarray:
+    """The decoder's output placed in page pools, as a serving engine keeps
+    its cache ([blog] § application scenarios and deployment parameters:
+    a compressed cache entry is decompressed where it is consumed).
+
+    kv is [G, T, D] with planes ordered (layer, kv, batch, head); the result
+    is [layers * 2, num_pages, page_tokens, heads, D], pool 2 * layer + kv,
+    with kv[g, t] at page block_table[b, t // page_tokens], row
+    t % page_tokens, head h; entries no token maps to keep `fill`."""
+    kv = np.asarray(kv)
+    g_n, t_len, d_n = kv.shape
+    per_layer = 2 * batch * heads
+    if g_n % per_layer:
+        raise ValueError("planes must be layers * 2 * batch * heads")
+    table = np.asarray(block_table, dtype=np.int64)
+    pools = np.full((g_n // per_layer * 2, num_pages, page_tokens, heads, d_n), fill, dtype=kv.dtype)
+    g = np.arange(g_n)
+    pool_of, b_of, h_of = g // (batch * heads), (g // heads) % batch, g % heads
+    t = np.arange(t_len)
+    page = table[b_of[:, None], t[None, :] // page_tokens]          # [G, T]
+    if np.any((page < 0) | (page >= num_pages)):
+        raise ValueError("block table entry outside the pool")
+    pools[pool_of[:, None], page, (t % page_tokens)[None, :], h_of[:, None]] = kv
+    return pools
+
+
+__all__ += ["scatter_to_pages"]
+
+
+# ---------------------------------------------------------------------------
 # bits per scalar: the integer model and the continuous mixture
 # ---------------------------------------------------------------------------
 def sigma_per_token(sigma, tokens: int, sigma_block_tokens: int = 0) -> np.ndarray:

@@ -84,3 +84,25 @@ def test_side_hash_sensitivity():
     p2[[3, 4]] = p2[[4, 3]]
     assert O.side_hash(sig, p2) != h0
     assert O.side_hash(sig, None) != h0
+
+
+def test_scatter_to_pages_brute_force():
+    """The paged placement against plain loops over every (plane, token)."""
+    rng = np.random.default_rng(3)
+    layers, batch, heads, t_len, d, pt = 2, 3, 2, 11, 64, 4
+    g_n = layers * 2 * batch * heads
+    kv = rng.integers(0, 1 << 16, size=(g_n, t_len, d)).astype(np.uint16)
+    max_pages, num_pages = 3, 20
+    table = rng.permutation(num_pages)[:batch * max_pages].reshape(batch, max_pages).astype(np.int32)
+    got = O.scatter_to_pages(kv, batch, heads, table, pt, num_pages, fill=0xABCD)
+    want = np.full((layers * 2, num_pages, pt, heads, d), 0xABCD, dtype=np.uint16)
+    for g in range(g_n):
+        lk, rest = divmod(g, batch * heads)
+        b, h = divmod(rest, heads)
+        for t in range(t_len):
+            want[lk, table[b, t // pt], t % pt, h, :] = kv[g, t, :]
+    assert np.array_equal(got, want)
+    # every token lands somewhere distinct: the pages hold all of kv
+    assert np.sum(got != 0xABCD) == np.sum(kv != 0xABCD)
+    with pytest.raises(ValueError):
+        O.scatter_to_pages(kv, batch, heads, np.full((batch, max_pages), num_pages, np.int32), pt, num_pages)
