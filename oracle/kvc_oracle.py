@@ -419,6 +419,87 @@ def calibrate_sigma(kv, mu, kv_dtype: int, mu_dtype: int, sigma_floor: float,
 
 
 # ---------------------------------------------------------------------------
+# S-12  rate-fitted sigma (an optional calibration)
+# ---------------------------------------------------------------------------
+RATE_STEPS = 25                    # candidate multipliers k_j = 1 - j/32, j = 0..24
+LOG2_TABLE_BITS = 8
+
+
+@functools.lru_cache(maxsize=None)
+def log2_table_q16() -> np.ndarray:
+    """round(2^16 log2(1 + m/256)) for m = 0..255."""
+    m = np.arange(1 << LOG2_TABLE_BITS, dtype=np.float64)
+    return np.floor(65536.0 * np.log2(1.0 + m / 256.0) + 0.5).astype(np.int64)
+
+
+def code_len_q16(f) -> np.ndarray:
+    """An integer stand-in for 2^16 (31 - log2 f), the code length of a
+    symbol of frequency f in 2^-16 bits: with e the position of f's top bit
+    and m the 8 bits below it, 2^16 (31 - e) - LOG2[m].  Exact at powers of
+    two; high by less than 2^16 log2(1 + 1/256) (0.0056 bits) elsewhere
+    (the bits of f below those 8 are dropped)."""
+    f = np.asarray(f, dtype=np.int64)
+    if np.any(f < 1) or np.any(f > M):
+        raise ValueError("frequency outside [1, M]")
+    e = np.floor(np.log2(f.astype(np.float64))).astype(np.int64)
+    e = np.where((np.int64(1) << (e + 1)) <= f, e + 1, e)      # exact bit length - 1
+    e = np.where((np.int64(1) << e) > f, e - 1, e)
+    norm = (f << (31 - e)) & 0x7FFFFFFF                       # the bits below the top one, at 30..0
+    m = norm >> 23
+    return (31 - e) * 65536 - log2_table_q16()[m]
+
+
+def calibrate_sigma_rate(kv, mu, kv_dtype: int, mu_dtype: int, sigma_floor: float, prefix,
+                         w_narrow_bp: int, w_wide_bp: int, block_tokens: int = 0, base=None,
+                         return_costs: bool = False):
+    """S-12: the sigma among sigma_j = max(floor, fp32(base * k_j)), k_j =
+    1 - j/32, j = 0..24, that gives the held-out data the least integer code
+    length sum(code_len_q16(f)) under the format's CDF, f = C(s+1) - C(s);
+    the first j on a tie.  base defaults to the RMS calibration (S-7).
+
+    Reading ([blog] § limitations and future directions: better residual
+    models; § engineering choice of predictor: sigma calibrated once on
+    held-out data): the RMS is the variance estimate the pages name, but one
+    outlier in a few hundred inflates it; fitting the scale to the code
+    length the coder will actually spend is the plainest better estimate
+    that keeps the pages' mixture.  The cost is an integer sum, so the
+    choice does not depend on the order of summation."""
+    if base is None:
+        base = calibrate_sigma(kv, mu, kv_dtype, mu_dtype, sigma_floor, block_tokens)
+    base = np.asarray(base, dtype=np.float32)
+    kv = np.asarray(kv)
+    reps, planes, t_len, ch = kv.shape
+    base3 = base[:, None, :] if block_tokens == 0 else base
+    blk = t_len if block_tokens == 0 else block_tokens
+    t_n, t_w, t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)
+    pref = prefix if t_e else None
+    s = order_index(kv, kv_dtype).astype(np.int64)
+    m32 = mu_to_f32(mu, mu_dtype)
+    fl = np.float32(sigma_floor)
+    tok_block = np.arange(t_len) // blk
+    costs = np.zeros((RATE_STEPS,) + base3.shape, dtype=np.int64)
+    cands = []
+    for j in range(RATE_STEPS):
+        k = np.float32(1.0 - j / 32.0)
+        sj = np.maximum((base3 * k).astype(np.float32), fl).astype(np.float32)
+        cands.append(sj)
+        inv = _inv_sigma(sj)[:, tok_block, :]                 # [planes, T, D]
+        for r in range(reps):
+            c0 = cdf(s[r], m32[r], inv, kv_dtype, t_n, t_w, pref)
+            c1 = cdf(s[r] + 1, m32[r], inv, kv_dtype, t_n, t_w, pref)
+            cl = code_len_q16(c1 - c0)                        # [planes, T, D]
+            for b in range(base3.shape[1]):
+                costs[j, :, b, :] += cl[:, b * blk:(b + 1) * blk, :].sum(axis=1)
+    pick = np.argmin(costs, axis=0)                           # the first minimum
+    out = np.take_along_axis(np.stack(cands), pick[None], axis=0)[0]
+    out = out[:, 0, :] if block_tokens == 0 else out
+    return (out, costs) if return_costs else out
+
+
+__all__ += ["RATE_STEPS", "log2_table_q16", "code_len_q16", "calibrate_sigma_rate"]
+
+
+# ---------------------------------------------------------------------------
 # S-10  side-information checksum
 # ---------------------------------------------------------------------------
 _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
