@@ -561,6 +561,40 @@ int kvc_calibrate_sigma_blocks(const void* d_kv, const void* d_mu, int32_t kv_dt
                                         static_cast<kvc::CalibPart*>(d_workspace), static_cast<hipStream_t>(stream)));
 }
 
+int kvc_calibrate_sigma_rate(const void* d_kv, const void* d_mu, int32_t kv_dtype, int32_t mu_dtype, int64_t reps,
+                             int64_t planes, int64_t tokens, int64_t channels, int64_t block_tokens, float sigma_floor,
+                             uint32_t w_narrow_bp, uint32_t w_wide_bp, const uint32_t* d_prefix, float* d_sigma_out,
+                             void* d_workspace, uint64_t workspace_bytes, void* stream) {
+    uint32_t tn, tw, te;
+    if (!budgets(kv_dtype, w_narrow_bp, w_wide_bp, &tn, &tw, &te) || (te && !d_prefix) || !aligned(d_prefix, 4))
+        return KVC_ERR_INVALID;
+    // every candidate sigma must be a valid sigma of the format
+    if (!(sigma_floor >= 0x1p-96f) || !(sigma_floor <= 0x1p96f)) return KVC_ERR_INVALID;
+    if (block_tokens < 0 || tokens < 1 || planes < 1 || channels < 64) return KVC_ERR_INVALID;
+    const int64_t n_blocks = (block_tokens == 0 || block_tokens >= tokens) ? 1 : (tokens + block_tokens - 1) / block_tokens;
+    if (planes > kMaxScalars / n_blocks || planes * n_blocks > kMaxScalars / channels) return KVC_ERR_INVALID;
+    const uint64_t n = uint64_t(planes * n_blocks) * uint64_t(channels);
+    const uint64_t rms_bytes = KVC_CALIBRATE_WORKSPACE_BYTES(planes * n_blocks, channels);
+    const uint64_t cost_bytes = n * uint64_t(kvc::kRateSteps) * uint64_t(kvc::kCalibSplitsMax) * 8u;
+    if (!d_workspace || workspace_bytes < KVC_CALIBRATE_RATE_WORKSPACE_BYTES(planes * n_blocks, channels))
+        return KVC_ERR_INVALID;
+    static_assert(kvc::kRateSteps * kvc::kCalibSplitsMax * 8 == 12800, "workspace formula");
+    int st = kvc_calibrate_sigma_blocks(d_kv, d_mu, kv_dtype, mu_dtype, reps, planes, tokens, channels, block_tokens,
+                                        sigma_floor, d_sigma_out, d_workspace, rms_bytes, stream);
+    if (st != KVC_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
+    if (e != hipSuccess) return KVC_ERR_DEVICE;
+    uint8_t* ws = static_cast<uint8_t*>(d_workspace);
+    auto* part = reinterpret_cast<unsigned long long*>(ws + rms_bytes);
+    auto* table = reinterpret_cast<uint32_t*>(ws + round_up(rms_bytes + cost_bytes, 256));
+    if ((e = kvc::launch_coder_tables(phi, tn, tw, table, nullptr, s)) != hipSuccess) return KVC_ERR_DEVICE;
+    return finish(kvc::launch_rate_fit(d_kv, d_mu, kv_dtype, mu_dtype, reps, planes, tokens, channels,
+                                       n_blocks == 1 ? 0 : block_tokens, sigma_floor, table,
+                                       te ? d_prefix : phi.zero, d_sigma_out, part, s));
+}
+
 int kvc_build_marginal(const void* d_samples, int32_t dtype, uint64_t n, uint32_t w_narrow_bp,
                        uint32_t w_wide_bp, uint32_t* d_prefix_out, void* stream) {
     uint32_t tn, tw, te;

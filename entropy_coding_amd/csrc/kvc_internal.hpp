@@ -163,6 +163,16 @@ int64_t calibrate_splits(int64_t reps, int64_t pairs, int64_t block);
 hipError_t launch_calibrate(const void* kv, const void* mu, int kv_dtype, int mu_dtype, int64_t reps,
                             int64_t planes, int64_t tokens, int64_t channels, int64_t block_tokens,
                             float sigma_floor, float* sigma_out, CalibPart* part, hipStream_t s);
+// Rate-fitted sigma: sigma_io (the base on entry) becomes, per (plane,
+// block, channel), the candidate max(floor, base (1 - j/32)), j < kRateSteps,
+// with the least integer code length under the mixture table `table`
+// (launch_coder_tables) and the escape prefix.  part: kRateSteps x splits x
+// (planes x blocks x channels) u64.
+constexpr int kRateSteps = 25;
+hipError_t launch_rate_fit(const void* kv, const void* mu, int kv_dtype, int mu_dtype, int64_t reps, int64_t planes,
+                           int64_t tokens, int64_t channels, int64_t block_tokens, float sigma_floor,
+                           const uint32_t* table, const uint32_t* prefix, float* sigma_io, unsigned long long* part,
+                           hipStream_t s);
 hipError_t launch_marginal(const void* samples, int dtype, uint64_t n, uint32_t te,
                            uint32_t* prefix_out, hipStream_t s);
 hipError_t launch_estimate(const EstimateArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);

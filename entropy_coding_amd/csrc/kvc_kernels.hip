@@ -1359,6 +1359,116 @@ hipError_t launch_calibrate(const void* kv, const void* mu, int kv_dtype, int mu
 }
 
 // ---------------------------------------------------------------------------
+// rate-fitted sigma: for each candidate sigma_j = max(floor, base * (1 - j/32)),
+// the integer code length of the held-out data under the coder's own CDF,
+// sum of 2^16 (31 - e) - LOG2[m] over f = C(s+1) - C(s) (e the top bit of f,
+// m the 8 bits below it); the least sum wins, the first j on a tie.  Sums of
+// integers: the result does not depend on the order of summation.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t code_len_q16(uint32_t f, const uint32_t* log2_tab) {
+    const uint32_t lz = __builtin_clz(f);                    // f >= 1: 31 - top bit
+    const uint32_t m = ((f << lz) >> 23) & 0xFFu;
+    return lz * 65536u - log2_tab[m];
+}
+
+template <int KV, int MU>
+__global__ void __launch_bounds__(kCalibBlock) k_rate_cost(const void* kv_, const void* mu_, int64_t reps,
+                                                           int64_t planes, int64_t tokens, int64_t channels,
+                                                           int64_t block, int64_t nb, const float* __restrict__ base,
+                                                           float sigma_floor, const uint32_t* __restrict__ table,
+                                                           const uint32_t* __restrict__ prefix,
+                                                           unsigned long long* __restrict__ part) {
+    __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
+    __shared__ uint32_t s_log[256];
+    __shared__ unsigned long long s_sum[kCalibWaves][64];
+    for (uint32_t i = threadIdx.x; i < 256u; i += blockDim.x)
+        s_log[i] = static_cast<uint32_t>(floor(65536.0 * log2(1.0 + i / 256.0) + 0.5));
+    copy_to_lds(s_tab, table, static_cast<uint32_t>(kTableBytes / 16));     // and the barrier
+    using KB = typename Alphabet<KV>::Bits;
+    using MT = typename MuT<MU>::T;
+    const KB* __restrict__ kv = static_cast<const KB*>(kv_);
+    const MT* __restrict__ mu = static_cast<const MT*>(mu_);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t groups = channels / 64;
+    const int64_t vp = blockIdx.x / groups;                   // (plane, sigma block) pair
+    const int64_t p = vp / nb;
+    const int64_t t_lo = (vp - p * nb) * block;
+    const int64_t len = tokens - t_lo < block ? tokens - t_lo : block;
+    const int64_t d = (blockIdx.x % groups) * 64 + lane;
+    const int64_t splits = gridDim.y, s = blockIdx.y;
+    const uint32_t j = blockIdx.z;
+    const int64_t n = planes * nb * channels;
+    // the candidate: 1 - j/32 is exact in float32
+    const float k = static_cast<float>(32u - j) * 0.03125f;
+    const float sg = fmaxf(__fmul_rn(base[vp * channels + d], k), sigma_floor);
+    const float inv24 = __frcp_rn(sg) * 16777216.0f;
+    const Model m{s_tab, prefix, nullptr};
+    const int64_t rows = reps * len;
+    const int64_t r1 = rows * (s + 1) / splits;
+    unsigned long long acc = 0;
+    for (int64_t r = rows * s / splits + wave; r < r1; r += kCalibWaves) {
+        const int64_t rep = r / len, t = r - rep * len;
+        const int64_t off = ((rep * planes + p) * tokens + t_lo + t) * channels + d;
+        const uint32_t sym = order_of_bits<KV>(kv[off]);
+        const float mv = mu_value<MU>(mu[off]);
+        const uint32_t f = cdf_at<KV>(sym + 1u, mv, inv24, m) - cdf_at<KV>(sym, mv, inv24, m);
+        acc += code_len_q16(f, s_log);
+    }
+    s_sum[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        unsigned long long t = 0;
+        for (int w = 0; w < kCalibWaves; ++w) t += s_sum[w][lane];
+        part[(static_cast<int64_t>(j) * splits + s) * n + vp * channels + d] = t;
+    }
+}
+
+// One thread per (plane, sigma block, channel): the candidate with the least
+// code length; sigma_io holds the base on entry and the fitted sigma after.
+__global__ void k_rate_pick(const unsigned long long* __restrict__ part, int64_t splits, int64_t n, float sigma_floor,
+                            float* __restrict__ sigma_io) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    unsigned long long best = ~0ull;
+    uint32_t best_j = 0;
+    for (uint32_t j = 0; j < static_cast<uint32_t>(kRateSteps); ++j) {
+        unsigned long long c = 0;
+        for (int64_t s = 0; s < splits; ++s) c += part[(static_cast<int64_t>(j) * splits + s) * n + i];
+        if (c < best) {
+            best = c;
+            best_j = j;
+        }
+    }
+    const float k = static_cast<float>(32u - best_j) * 0.03125f;
+    sigma_io[i] = fmaxf(__fmul_rn(sigma_io[i], k), sigma_floor);
+}
+
+hipError_t launch_rate_fit(const void* kv, const void* mu, int kv_dtype, int mu_dtype, int64_t reps, int64_t planes,
+                           int64_t tokens, int64_t channels, int64_t block_tokens, float sigma_floor,
+                           const uint32_t* table, const uint32_t* prefix, float* sigma_io, unsigned long long* part,
+                           hipStream_t s) {
+    const int64_t blk = (block_tokens == 0 || block_tokens > tokens) ? tokens : block_tokens;
+    const int64_t nb = (tokens + blk - 1) / blk;
+    const int64_t pairs = planes * nb * (channels / 64);
+    const int64_t splits = calibrate_splits(reps, pairs, blk);
+    const dim3 grid(static_cast<uint32_t>(pairs), static_cast<uint32_t>(splits), kRateSteps), block(kCalibBlock);
+#define KVC_RATE(K, U)                                                                                          \
+    hipLaunchKernelGGL((k_rate_cost<K, U>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, blk, nb, \
+                       sigma_io, sigma_floor, table, prefix, part)
+    if (kv_dtype == kBF16 && mu_dtype == kBF16) KVC_RATE(kBF16, kBF16);
+    else if (kv_dtype == kBF16 && mu_dtype == kF32) KVC_RATE(kBF16, kF32);
+    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) KVC_RATE(kE4M3, kBF16);
+    else if (kv_dtype == kE4M3 && mu_dtype == kF32) KVC_RATE(kE4M3, kF32);
+    else return hipErrorInvalidValue;
+#undef KVC_RATE
+    const int64_t n = planes * nb * channels;
+    hipLaunchKernelGGL(k_rate_pick, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s, part, splits, n,
+                       sigma_floor, sigma_io);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // empirical marginal: histogram in value order (integer atomics, so the
 // result does not depend on order), then one workgroup turns counts + 1
 // into the scaled prefix in place.

@@ -28,6 +28,7 @@ DECODE_STAGES = 2     # side-information checksum + escape bucket table, decodin
 EXPORTS = [
     "kvc_version", "kvc_status_string", "kvc_phi_tables", "kvc_encode_sizes", "kvc_encode",
     "kvc_stream_info", "kvc_decode", "kvc_decode_paged", "kvc_calibrate_sigma", "kvc_calibrate_sigma_blocks",
+    "kvc_calibrate_sigma_rate",
     "kvc_build_marginal", "kvc_estimate_bits", "kvc_cdf_table",
 ]
 
@@ -89,6 +90,9 @@ _lib_calibrate = _sig("kvc_calibrate_sigma", ctypes.c_int,
                       [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _U64, _P])
 _lib_calibrate_blocks = _sig("kvc_calibrate_sigma_blocks", ctypes.c_int,
                              [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _U64, _P])
+_lib_calibrate_rate = _sig("kvc_calibrate_sigma_rate", ctypes.c_int,
+                           [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, _I64, ctypes.c_float, _U32, _U32, _P, _P,
+                            _P, _U64, _P])
 _lib_marginal = _sig("kvc_build_marginal", ctypes.c_int, [_P, _I32, _U64, _U32, _U32, _P, _P])
 _lib_estimate = _sig("kvc_estimate_bits", ctypes.c_int, [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _P, _U64, _P])
 _lib_cdf_table = _sig("kvc_cdf_table", ctypes.c_int, [_I32, _I32, _U32, _U32, _P, _P, _I64, _P, _P, _P])
@@ -319,6 +323,30 @@ def kvc_calibrate_sigma(kv: torch.Tensor, mu: torch.Tensor, sigma_floor: float =
         st = _lib_calibrate_blocks(_ptr(kv), _ptr(mu), _kv_dtype(kv), _mu_dtype(mu), r, g, t, d, block_tokens,
                                    sigma_floor, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "kvc_calibrate_sigma")
+    return out
+
+
+def kvc_calibrate_sigma_rate(kv: torch.Tensor, mu: torch.Tensor, prefix: torch.Tensor | None = None,
+                             weights=(9500, 300), sigma_floor: float = 2.0 ** -30, block_tokens: int = 0,
+                             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                             stream=None) -> torch.Tensor:
+    """Rate-fitted sigma: of the candidates max(floor, rms * (1 - j/32)),
+    j = 0..24, the one with the least integer code length of the held-out
+    kv [reps, planes, tokens, channels] under the mixture the data will be
+    coded with.  Shapes as kvc_calibrate_sigma."""
+    _need(kv, "kv")
+    _need(mu, "mu")
+    r, g, t, d = kv.shape
+    shape = sigma_shape(g, t, d, block_tokens)
+    n_rows = g if block_tokens == 0 else g * shape[1]
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=kv.device)
+    if workspace is None:
+        workspace = torch.empty(n_rows * d * (1024 + 12800) + 65536, dtype=torch.uint8, device=kv.device)
+    st = _lib_calibrate_rate(_ptr(kv), _ptr(mu), _kv_dtype(kv), _mu_dtype(mu), r, g, t, d, block_tokens,
+                             sigma_floor, weights[0], weights[1], _ptr(prefix), _ptr(out), _ptr(workspace),
+                             workspace.numel(), _stream(stream))
+    _check(st, "kvc_calibrate_sigma_rate")
     return out
 
 

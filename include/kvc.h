@@ -250,6 +250,32 @@ int kvc_calibrate_sigma_blocks(const void* d_kv, const void* d_mu, int32_t kv_dt
                                void* stream);
 
 /*
+ * Rate-fitted sigma ([blog] "limitations and future directions": better
+ * residual models; [blog] "engineering choice of predictor": sigma measured
+ * once on held-out data).  The RMS of kvc_calibrate_sigma_blocks is the base;
+ * one outlier in a few hundred inflates it.  For each (plane, block, channel)
+ * this call keeps, of the candidates max(sigma_floor, base * (1 - j/32)),
+ * j = 0..24 (float32 products), the one under which the held-out data cost
+ * the fewest bits in the coder's own integer model: the sum over the data
+ * of 2^16 (31 - e) - L[m] for each frequency f = C(s+1) - C(s), with e the
+ * top bit of f, m the 8 bits below it and L[m] = round(2^16 log2(1 + m/256));
+ * the first j on a tie (an integer sum: deterministic).  The mixture
+ * weights and d_prefix (NULL allowed for a single Gaussian) are the ones the
+ * data will be coded with.  sigma_floor in [2^-96, 2^96].  Output and
+ * block_tokens as kvc_calibrate_sigma_blocks.  Workspace (256-byte aligned):
+ * KVC_CALIBRATE_RATE_WORKSPACE_BYTES(planes * n_blocks, channels).  Does
+ * not synchronise.
+ */
+#define KVC_CALIBRATE_RATE_WORKSPACE_BYTES(rows, channels) \
+    ((uint64_t)(rows) * (uint64_t)(channels) * (1024u + 12800u) + 65536u)
+int kvc_calibrate_sigma_rate(const void* d_kv, const void* d_mu, int32_t kv_dtype,
+                             int32_t mu_dtype, int64_t reps, int64_t planes, int64_t tokens,
+                             int64_t channels, int64_t block_tokens, float sigma_floor,
+                             uint32_t w_narrow_bp, uint32_t w_wide_bp, const uint32_t* d_prefix,
+                             float* d_sigma_out, void* d_workspace, uint64_t workspace_bytes,
+                             void* stream);
+
+/*
  * Empirical marginal ([wiki] "mixture distribution": an empirical BF16
  * distribution catches extreme outliers).  d_samples holds n bit patterns
  * (bf16 or e4m3); writes the integer prefix d_prefix_out[b] =
