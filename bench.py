@@ -122,7 +122,7 @@ def cpu_baseline(workload, planes_per_worker: int, tokens: int):
 # ---------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------
-def prepare(workload, dev, calib_reps: int, sigma_block: int = 0):
+def prepare(workload, dev, calib_reps: int, sigma_block: int = 0, sigma_fit: str = "rms"):
     import torch
     from entropy_coding_amd import kvc
     from entropy_coding_amd import workloads as W
@@ -136,18 +136,21 @@ def prepare(workload, dev, calib_reps: int, sigma_block: int = 0):
     sigma = torch.empty(kvc.sigma_shape(G, T, D, sigma_block), dtype=torch.float32, device=dev)
     ppl = w.planes_per_layer
     t0 = time.perf_counter()
+    prefix = kvc.kvc_build_marginal(W.marginal_samples(w, device=dev), (w.w_narrow_bp, w.w_wide_bp))
     for l in range(w.layers):
         k_l, m_l = W.layer_data(w, l, device=dev)
         kv[l * ppl:(l + 1) * ppl] = k_l
         mu[l * ppl:(l + 1) * ppl] = m_l
         del k_l, m_l
         ck, cm = W.layer_calibration(w, l, reps=calib_reps, device=dev)
-        s_kvh = kvc.kvc_calibrate_sigma(ck, cm, block_tokens=sigma_block)
+        if sigma_fit == "rate":
+            s_kvh = kvc.kvc_calibrate_sigma_rate(ck, cm, prefix, (w.w_narrow_bp, w.w_wide_bp), block_tokens=sigma_block)
+        else:
+            s_kvh = kvc.kvc_calibrate_sigma(ck, cm, block_tokens=sigma_block)
         sigma[l * ppl:(l + 1) * ppl] = W.expand_sigma(w, s_kvh)
         del ck, cm
-    prefix = kvc.kvc_build_marginal(W.marginal_samples(w, device=dev), (w.w_narrow_bp, w.w_wide_bp))
     torch.cuda.synchronize()
-    log(f"[bench] generated {w.name}: {w.n_scalars} scalars, sigma from {calib_reps}x{w.calib_tokens} "
+    log(f"[bench] generated {w.name}: {w.n_scalars} scalars, sigma ({sigma_fit}) from {calib_reps}x{w.calib_tokens} "
         f"tokens per layer, in {time.perf_counter() - t0:.1f} s")
     return kv, mu, sigma, prefix
 
@@ -240,6 +243,8 @@ def main():
                     help="(per-layer workload 4) also time the host-offload reload: pinned streams, copies overlapped with decode")
     ap.add_argument("--sigma-block", type=int, default=0,
                     help="position-aware sigma: one sigma per block of this many tokens (0 = per plane)")
+    ap.add_argument("--sigma-fit", choices=["rms", "rate"], default="rms",
+                    help="sigma calibration: the RMS of the residual, or the scale fitted to the code length")
     ap.add_argument("--paged", type=int, default=0,
                     help="decode straight into a paged KV cache with pages of this many tokens (shuffled table)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -269,7 +274,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     reps = args.calib_reps if args.calib_reps is not None else w.calib_reps
-    kv, mu, sigma, prefix = prepare(w, dev, reps, args.sigma_block)
+    kv, mu, sigma, prefix = prepare(w, dev, reps, args.sigma_block, args.sigma_fit)
     n = w.n_scalars
     weights = (w.w_narrow_bp, w.w_wide_bp)
     # with sigma blocks the library's default picks a divisor of the block length
@@ -392,7 +397,7 @@ def main():
     # out (encode); words and states and mu in, KV out (decode)
     alg = float(kv_size + mu_size) * n + stream_bytes
     traffic = measured_traffic() if args.workload == 2 and tc == w.chunk_tokens and not args.paged \
-        and not args.sigma_block else {}
+        and not args.sigma_block and args.sigma_fit == "rms" else {}
 
     def roofline(kernel, avg_ms):
         a = alg / (avg_ms * 1e-3) / 1e9
@@ -419,7 +424,7 @@ def main():
         "config": {
             "workload": w.name, "shape": [w.layers, 2, w.batch, w.heads, w.tokens, w.channels],
             "scalars": n, "mixture_bp": list(weights), "chunk_tokens": tc, "sigma_block_tokens": args.sigma_block,
-            "sigma_calibration": f"{reps}x{w.calib_tokens} tokens per layer",
+            "sigma_calibration": f"{args.sigma_fit}, {reps}x{w.calib_tokens} tokens per layer",
             "mu_dtype": "bf16" if mu_size == 2 else "fp32", "calls_per_step": len(parts),
             "decode_output": f"paged, {args.paged}-token pages" if args.paged else "contiguous",
             "second_pass_copy_ms": scatter_ms,
