@@ -298,28 +298,42 @@ __device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float in
     return make_slots(s, ha, hb, m, htot);
 }
 
-// Element `lane` of a row whose base is wave-uniform: the base stays in
-// scalar registers and the lane adds a 32-bit byte offset.
+// Rows of the chunk through buffer resources: the lane's byte offset in a
+// vector register, the row's in a scalar one.
 template <typename T>
-__device__ __forceinline__ const T& row_elem(const T* __restrict__ row, uint32_t lane) {
-    return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(row) + lane * static_cast<uint32_t>(sizeof(T)));
+__device__ __forceinline__ uint32_t load_row_elem(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t row_off) {
+    if constexpr (sizeof(T) == 1) return __builtin_amdgcn_raw_buffer_load_b8(r, lane_off, row_off, 0);
+    else if constexpr (sizeof(T) == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, lane_off, row_off, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, row_off, 0);
 }
 
 template <int KV, int MU, int U>
-__device__ __forceinline__ void encode_batch(int t, PushState& st, const typename Alphabet<KV>::Bits* __restrict__ kvb,
-                                             const typename MuT<MU>::T* __restrict__ mub, uint32_t D, uint32_t lane,
+__device__ __forceinline__ void encode_batch(int t, PushState& st, __amdgpu_buffer_rsrc_t kvr,
+                                             __amdgpu_buffer_rsrc_t mur, uint32_t D, uint32_t lane,
                                              float inv24, const Model& m, uint32_t htot, uint16_t* __restrict__ slot) {
+    using KB = typename Alphabet<KV>::Bits;
+    using MT = typename MuT<MU>::T;
     uint32_t kb[U];
-    typename MuT<MU>::T mb[U];
+    float mus[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const uint64_t row = static_cast<uint64_t>(t - u) * D;
-        kb[u] = row_elem(kvb + row, lane);
-        mb[u] = row_elem(mub + row, lane);
+        const uint32_t row = static_cast<uint32_t>(t - u) * D;
+        kb[u] = load_row_elem<KB>(kvr, lane * static_cast<uint32_t>(sizeof(KB)), row * static_cast<uint32_t>(sizeof(KB)));
+        const uint32_t mr = load_row_elem<MT>(mur, lane * static_cast<uint32_t>(sizeof(MT)), row * static_cast<uint32_t>(sizeof(MT)));
+        mus[u] = MU == kBF16 ? __uint_as_float(mr << 16) : __uint_as_float(mr);
+    }
+    // a non-finite mean counts as 0 (rare: one test for the batch)
+    uint64_t odd = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) odd |= __ballot(!__builtin_isfinite(mus[u]));
+    if (odd) {
+        __asm__ volatile("");                       // a branch, not selects on every step
+#pragma unroll
+        for (int u = 0; u < U; ++u) mus[u] = __builtin_isfinite(mus[u]) ? mus[u] : 0.0f;
     }
     SymSlots y[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) y[u] = symbol_slots<KV, MU>(kb[u], mu_value<MU>(mb[u]), inv24, m, htot);
+    for (int u = 0; u < U; ++u) y[u] = symbol_slots<KV, MU>(kb[u], mus[u], inv24, m, htot);
 #pragma unroll
     for (int u = 0; u < U; ++u) rans_push(st, y[u], slot);
 }
@@ -348,10 +362,11 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
-    // wave-uniform bases; lanes index them with 32-bit offsets
+    // the chunk's rows of KV and mu as buffers (a chunk's rows span fewer than
+    // 2^31 bytes)
     const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * static_cast<int64_t>(D) + cp.k * 64;
-    const KB* __restrict__ kvb = static_cast<const KB*>(a.kv) + row0;
-    const MT* __restrict__ mub = static_cast<const MT*>(a.mu) + row0;
+    const __amdgpu_buffer_rsrc_t kvb = buffer_rsrc(static_cast<const KB*>(a.kv) + row0, cp.len * D * sizeof(KB));
+    const __amdgpu_buffer_rsrc_t mub = buffer_rsrc(static_cast<const MT*>(a.mu) + row0, cp.len * D * sizeof(MT));
     uint16_t* __restrict__ slot = a.slots + static_cast<uint64_t>(chunk) * a.slot_words;
 
     PushState st{static_cast<uint32_t>(kL), kLHi, static_cast<uint32_t>(a.slot_words)};
