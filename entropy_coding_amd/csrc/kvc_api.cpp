@@ -23,13 +23,15 @@ constexpr uint32_t kLanes = 64;
 constexpr uint32_t kVersion = 3;   // stream format version (split slot ranges, floor of z * 2^24)
 constexpr uint32_t kMaxChunkTokens = 1u << 20;
 constexpr int64_t kMaxScalars = int64_t(1) << 40;
-// decode workspace: control block, the escape bucket table (u32), the
-// mixture table and the aim table
-constexpr uint64_t kDecodeBucketOffset = 256;
-constexpr uint64_t kDecodeTableOffset = 262656;
+// decode workspace: control block, the escape slot table, the escape
+// bucket table (u32; right after the slot table, where the bf16 decoder
+// expects it), the mixture table and the aim table
+constexpr uint64_t kDecodeSlotsOffset = 256;
+constexpr uint64_t kDecodeBucketOffset = kDecodeSlotsOffset + kvc::kEscapeSlotsBytes;
+constexpr uint64_t kDecodeTableOffset = 786944;
 constexpr uint64_t kDecodeAimOffset = kDecodeTableOffset + 49408;
 static_assert(kDecodeBucketOffset + 4 * kvc::kEscapeBucketsMax <= kDecodeTableOffset &&
-                  kDecodeTableOffset + kvc::kTableBytes <= kDecodeAimOffset &&
+                  kDecodeTableOffset % 256 == 0 && kDecodeTableOffset + kvc::kTableBytes <= kDecodeAimOffset &&
                   kDecodeAimOffset + kvc::kAimBytes <= KVC_DECODE_WORKSPACE_BYTES,
               "decode workspace layout");
 
@@ -134,7 +136,7 @@ bool params_geometry(const kvc_params* p, ChunkGeom* g) {
 // directory, one word slot per chunk sized for two words per scalar, then
 // the per-call mixture table.
 struct EncodeLayout {
-    uint64_t states, chunk_words, directory, slots, table, total, slot_words, max_stream;
+    uint64_t states, chunk_words, directory, slots, table, eslots, total, slot_words, max_stream;
 };
 
 EncodeLayout encode_layout(const ChunkGeom& g) {
@@ -146,7 +148,8 @@ EncodeLayout encode_layout(const ChunkGeom& g) {
     l.directory = round_up(l.chunk_words + n * 4, 256);
     l.slots = round_up(l.directory + (n + 1) * 8, 256);
     l.table = round_up(l.slots + n * l.slot_words * 2, 256);
-    l.total = l.table + kvc::kTableBytes;
+    l.eslots = round_up(l.table + kvc::kTableBytes, 256);
+    l.total = l.eslots + kvc::kEscapeSlotsBytes;
     l.max_stream = KVC_HEADER_BYTES + 8 * (n + 1) + n * (kLanes * 8 + l.slot_words * 2);
     return l;
 }
@@ -329,6 +332,13 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     if ((e = kvc::launch_side_hash(d_sigma, sigma_words(g), prefix, prefix ? alphabet(p->kv_dtype) + 1u : 0u, ctl,
                                    s)) != hipSuccess)
         return KVC_ERR_DEVICE;
+    if ((e = kvc::launch_coder_tables(phi, tn, tw, reinterpret_cast<uint32_t*>(ws + l.table), nullptr, s)) !=
+        hipSuccess)
+        return KVC_ERR_DEVICE;
+    if (p->kv_dtype == KVC_BF16 && (e = kvc::launch_escape_slots(prefix ? prefix : phi.zero, tn + tw,
+                                                                  reinterpret_cast<uint32_t*>(ws + l.eslots), s)) !=
+                                       hipSuccess)
+        return KVC_ERR_DEVICE;
     timer.mark(1);
 
     kvc::EncodeArgs ea;
@@ -340,14 +350,12 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     ea.tn = tn;
     ea.tw = tw;
     ea.table = reinterpret_cast<const uint32_t*>(ws + l.table);
+    ea.eslots = reinterpret_cast<const uint32_t*>(ws + l.eslots);
     ea.slots = reinterpret_cast<uint16_t*>(ws + l.slots);
     ea.slot_words = l.slot_words;
     ea.states = reinterpret_cast<unsigned long long*>(ws + l.states);
     ea.chunk_words = reinterpret_cast<uint32_t*>(ws + l.chunk_words);
     ea.ctl = ctl;
-    if ((e = kvc::launch_coder_tables(phi, tn, tw, reinterpret_cast<uint32_t*>(ws + l.table), nullptr, s)) !=
-        hipSuccess)
-        return KVC_ERR_DEVICE;
     if ((e = kvc::launch_encode(ea, p->kv_dtype, p->mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(2);
 
@@ -477,6 +485,10 @@ int decode_common(const void* d_in, uint64_t in_bytes, const void* d_mu, const f
     if ((e = kvc::launch_coder_tables(phi, tn, tw, reinterpret_cast<uint32_t*>(ws + kDecodeTableOffset),
                                       reinterpret_cast<float*>(ws + kDecodeAimOffset), s)) != hipSuccess)
         return KVC_ERR_DEVICE;
+    if (p.kv_dtype == KVC_BF16 &&
+        (e = kvc::launch_escape_slots(prefix ? prefix : phi.zero, tn + tw,
+                                      reinterpret_cast<uint32_t*>(ws + kDecodeSlotsOffset), s)) != hipSuccess)
+        return KVC_ERR_DEVICE;
     timer.mark(1);
     const uint8_t* in = static_cast<const uint8_t*>(d_in);
     kvc::DecodeArgs da;
@@ -493,6 +505,7 @@ int decode_common(const void* d_in, uint64_t in_bytes, const void* d_mu, const f
     da.aim = reinterpret_cast<const float*>(ws + kDecodeAimOffset);
     da.buckets = buckets;
     da.bucket_shift = shift;
+    da.eslots = reinterpret_cast<const uint32_t*>(ws + kDecodeSlotsOffset);
     da.kv_out = d_kv_out;
     da.paged = po;
     da.ctl = ctl;

@@ -158,6 +158,8 @@ struct Model {
     const uint32_t* __restrict__ tab;      // mixture table in LDS
     const uint32_t* __restrict__ prefix;   // escape prefix (N + 1 entries; zeros without an escape part)
     const uint32_t* small;                 // e4m3 only: prefix and edges in LDS
+    const uint32_t* __restrict__ eslots;   // bf16 coders only: the escape slot table (k_escape_slots)
+    uint32_t htot;                         // T_n + T_w, where the floor-and-escape range starts
 };
 
 // Two consecutive u32 at byte offset `off` of `base` in one 8-byte read
@@ -167,13 +169,6 @@ struct alignas(4) U32Pair {
 };
 __device__ __forceinline__ U32Pair load_pair(const uint32_t* base, uint32_t off) {
     return *reinterpret_cast<const U32Pair*>(reinterpret_cast<const char*>(base) + off);
-}
-
-// prefix[s] and prefix[s + 1] (s < N)
-__device__ __forceinline__ void prefix_pair(const Model& m, uint32_t s, uint32_t& p0, uint32_t& p1) {
-    const U32Pair v = load_pair(m.prefix, s << 2);
-    p0 = v.a;
-    p1 = v.b;
 }
 
 // C(b) = b + h_fx(q(b)) + prefix[b].

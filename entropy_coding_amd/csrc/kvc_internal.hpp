@@ -61,6 +61,7 @@ struct EncodeArgs {
     const uint32_t* prefix;             // escape prefix; the zero table when there is no escape part
     uint32_t tn, tw;
     const uint32_t* table;              // the mixture table (launch_coder_tables)
+    const uint32_t* eslots;             // bf16: the escape slot table (launch_escape_slots)
     uint16_t* slots;                    // per-chunk word slots, filled from the end
     uint64_t slot_words;                // words per slot (2 per scalar, multiple of 4)
     unsigned long long* states;         // [n_chunks][64] final states
@@ -109,6 +110,8 @@ struct DecodeArgs {
     const float* aim;                   // the aim table, kAimFloats floats
     const uint32_t* buckets;            // escape bucket table (launch_escape_buckets)
     uint32_t bucket_shift;
+    const uint32_t* eslots;             // bf16: the escape slot table (launch_escape_slots),
+                                        // with the bucket table right after it
     void* kv_out;                       // contiguous output [planes][tokens][channels], or
     PagedOut paged;                     // the paged output (launch_decode with paged = true)
     Control* ctl;
@@ -151,6 +154,12 @@ hipError_t launch_check_pages(const PagedOut& p, int64_t used, Control* ctl, hip
 constexpr uint32_t kEscapeBucketsMax = 65538;
 hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_t shift, uint32_t n_entries,
                                  int kv_dtype, uint32_t* bucket, hipStream_t s);
+// Escape slot table of the bf16 alphabet, indexed by bit pattern p (s its
+// ordered index): entry p = (T_n + T_w + Q(s), Q(s + 1) - Q(s)), two u32,
+// so a coder finds the start and the count of a symbol's floor-and-escape
+// slots in one read.
+constexpr uint64_t kEscapeSlotsBytes = 65536ull * 8;
+hipError_t launch_escape_slots(const uint32_t* prefix, uint32_t htot, uint32_t* out, hipStream_t s);
 // sigma calibration: float64 partial sums per (split, plane, channel)
 struct CalibPart {
     double sum;

@@ -247,26 +247,23 @@ __device__ __forceinline__ void rans_push(PushState& st, const SymSlots& y, uint
     st.xl = (q << 31) | sl;
 }
 
-// Slots of the symbol with bit pattern kb under the mixture: ga, gb are the
-// mixture-table values at its two cell edges (in either order), s its index.
-__device__ __forceinline__ SymSlots make_slots(uint32_t s, uint32_t ga, uint32_t gb, const Model& m, uint32_t htot) {
+// Slots of a bf16 symbol under the mixture: ga, gb are the mixture-table
+// values at its two cell edges (in either order), q its escape slot table
+// entry (T_n + T_w + Q(s), Q(s + 1) - Q(s)).
+__device__ __forceinline__ SymSlots make_slots(uint32_t ga, uint32_t gb, U32Pair q) {
     const uint32_t g0 = __builtin_elementwise_min(ga, gb);
     const uint32_t fg = __builtin_elementwise_max(ga, gb) - g0;
-    uint32_t p0, p1;
-    prefix_pair(m, s, p0, p1);
     SymSlots y;
     y.g0 = g0;
     y.fg = fg;
-    y.qb = htot + s + p0 - fg;
-    y.f = fg + 1u + (p1 - p0);
+    y.qb = q.a - fg;
+    y.f = fg + q.b;
     return y;
 }
 
 template <int KV, int MU>
-__device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float inv24, const Model& m, uint32_t htot) {
+__device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float inv24, const Model& m) {
     if constexpr (KV == kBF16 && MU == kBF16) {
-        // ord(u): u ^ 0x8000 for a positive pattern, u ^ 0xFFFF for a negative one
-        const uint32_t s = (kb ^ 0x8000u) ^ (static_cast<uint32_t>(static_cast<int32_t>(kb << 16) >> 31) & 0x7FFFu);
         // both cell edges carry the value's sign; h is monotone in the
         // position, so the lower edge's h is the smaller one on either side
         uint32_t mg = kb & 0x7FFFu;
@@ -277,17 +274,17 @@ __device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float in
         const uint32_t sb = (kb & 0x8000u) << 16;
         const uint32_t ha = h_fx(z_fixed(__uint_as_float(ib | sb), mu, inv24), m.tab);
         const uint32_t hb = h_fx(z_fixed(__uint_as_float(ob | sb), mu, inv24), m.tab);
-        return make_slots(s, ha, hb, m, htot);
+        return make_slots(ha, hb, load_pair(m.eslots, kb << 3));
     }
-    const uint32_t s = order_of_bits<KV>(kb);
     if constexpr (KV == kE4M3) {
+        const uint32_t s = order_of_bits<KV>(kb);
         const uint32_t ha = h_fx(z_fixed(e4_edge(m.small, s), mu, inv24), m.tab);
         const uint32_t hb = h_fx(z_fixed(e4_edge(m.small, s + 1u), mu, inv24), m.tab);
         const uint32_t p0 = m.small[s], p1 = m.small[s + 1u];
         SymSlots y;
         y.g0 = ha;
         y.fg = hb - ha;
-        y.qb = htot + s + p0 - y.fg;
+        y.qb = m.htot + s + p0 - y.fg;
         y.f = y.fg + 1u + (p1 - p0);
         return y;
     }
@@ -295,7 +292,7 @@ __device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float in
     bf16_cell_edges(kb, lo, hi);
     const uint32_t ha = h_fx(z_fixed(lo, mu, inv24), m.tab);
     const uint32_t hb = h_fx(z_fixed(hi, mu, inv24), m.tab);
-    return make_slots(s, ha, hb, m, htot);
+    return make_slots(ha, hb, load_pair(m.eslots, kb << 3));
 }
 
 // Rows of the chunk through buffer resources: the lane's byte offset in a
@@ -310,7 +307,7 @@ __device__ __forceinline__ uint32_t load_row_elem(__amdgpu_buffer_rsrc_t r, uint
 template <int KV, int MU, int U>
 __device__ __forceinline__ void encode_batch(int t, PushState& st, __amdgpu_buffer_rsrc_t kvr,
                                              __amdgpu_buffer_rsrc_t mur, uint32_t D, uint32_t lane,
-                                             float inv24, const Model& m, uint32_t htot, uint16_t* __restrict__ slot) {
+                                             float inv24, const Model& m, uint16_t* __restrict__ slot) {
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
     uint32_t kb[U];
@@ -333,7 +330,7 @@ __device__ __forceinline__ void encode_batch(int t, PushState& st, __amdgpu_buff
     }
     SymSlots y[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) y[u] = symbol_slots<KV, MU>(kb[u], mus[u], inv24, m, htot);
+    for (int u = 0; u < U; ++u) y[u] = symbol_slots<KV, MU>(kb[u], mus[u], inv24, m);
 #pragma unroll
     for (int u = 0; u < U; ++u) rans_push(st, y[u], slot);
 }
@@ -358,7 +355,7 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
         if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
         inv24 = 16777216.0f;
     }
-    const Model m{s_tab, a.prefix, s_small};
+    const Model m{s_tab, a.prefix, s_small, a.eslots, a.tn + a.tw};
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
@@ -371,10 +368,9 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
 
     PushState st{static_cast<uint32_t>(kL), kLHi, static_cast<uint32_t>(a.slot_words)};
     int t = static_cast<int>(cp.len) - 1;
-    const uint32_t htot = a.tn + a.tw;
     for (; t >= kEncodeBatch - 1; t -= kEncodeBatch)
-        encode_batch<KV, MU, kEncodeBatch>(t, st, kvb, mub, D, lane, inv24, m, htot, slot);
-    for (; t >= 0; --t) encode_batch<KV, MU, 1>(t, st, kvb, mub, D, lane, inv24, m, htot, slot);
+        encode_batch<KV, MU, kEncodeBatch>(t, st, kvb, mub, D, lane, inv24, m, slot);
+    for (; t >= 0; --t) encode_batch<KV, MU, 1>(t, st, kvb, mub, D, lane, inv24, m, slot);
 
     a.states[chunk * 64 + lane] = (static_cast<unsigned long long>(st.xh) << 32) | st.xl;
     if (lane == 0) a.chunk_words[chunk] = static_cast<uint32_t>(a.slot_words) - st.wp;
@@ -658,11 +654,19 @@ __device__ __forceinline__ uint32_t candidate_bits(uint32_t cand) {
     else return cand;
 }
 
-// A candidate symbol with its exact CDF terms: G at both cell edges, and
-// the escape prefix at s and s + 1.
+// A candidate symbol with its exact CDF terms: G at both cell edges, the
+// start of its floor-and-escape slots (T_n + T_w + Q(s)) and their count
+// (Q(s + 1) - Q(s)), where Q(b) = b + prefix[b].
 struct Cell {
-    uint32_t s, g0, g1, p0, p1;
+    uint32_t g0, g1, qa, qf;
 };
+
+// Ordered index of a candidate (bf16: pattern in the upper half).
+template <int KV>
+__device__ __forceinline__ uint32_t index_of_candidate(uint32_t cand) {
+    if constexpr (KV == kBF16) return order_of_bits<kBF16>(cand >> 16);
+    else return order_of_bits<KV>(cand);
+}
 
 // Cell of the bf16 candidate kw (pattern in the upper half).  The outer edge (away from zero) is the
 // pattern's magnitude plus half a step, the inner edge the magnitude minus
@@ -671,10 +675,10 @@ struct Cell {
 // z saturates at +-24 as for an infinite edge, sigma <= 2^96); with an fp32
 // mean it becomes infinite, as the format defines.  Inf and NaN patterns
 // reach here only from the escape lookup, and their G terms are replaced
-// by the caller (every edge of theirs is infinite).
+// by the caller (every edge of theirs is infinite).  The escape terms come
+// from the escape slot table, at the pattern's entry.
 template <int MU>
 __device__ __forceinline__ Cell eval_bf16(uint32_t kw, float mu, float inv24, const Model& m) {
-    const uint32_t neg = static_cast<uint32_t>(static_cast<int32_t>(kw) >> 31);
     const uint32_t sign = kw & 0x80000000u;
     uint32_t ob = (kw & 0xFFFF0000u) | 0x8000u;
     const uint32_t ib = __builtin_elementwise_max(__builtin_elementwise_sub_sat(ob, 0x10000u), sign);
@@ -684,20 +688,21 @@ __device__ __forceinline__ Cell eval_bf16(uint32_t kw, float mu, float inv24, co
     Cell c;
     c.g0 = __builtin_elementwise_min(ha, hb);
     c.g1 = __builtin_elementwise_max(ha, hb);
-    // ordered index: 0x8000 + m for a positive pattern, 0x7FFF - m for a negative one
-    c.s = (((kw >> 16) & 0x7FFFu) ^ neg) + 0x8000u;
-    prefix_pair(m, c.s, c.p0, c.p1);
+    const U32Pair q = load_pair(m.eslots, (kw >> 13) & 0x7FFF8u);     // 8 bytes per pattern
+    c.qa = q.a;
+    c.qf = q.b;
     return c;
 }
 
 // Cell of the e4m3 pattern kb: edges and prefix from the LDS copies.
 __device__ __forceinline__ Cell eval_e4m3(uint32_t kb, float mu, float inv24, const Model& m) {
     Cell c;
-    c.s = order_of_bits<kE4M3>(kb);
-    c.g0 = h_fx(z_fixed(e4_edge(m.small, c.s), mu, inv24), m.tab);
-    c.g1 = h_fx(z_fixed(e4_edge(m.small, c.s + 1u), mu, inv24), m.tab);
-    c.p0 = m.small[c.s];
-    c.p1 = m.small[c.s + 1u];
+    const uint32_t s = order_of_bits<kE4M3>(kb);
+    c.g0 = h_fx(z_fixed(e4_edge(m.small, s), mu, inv24), m.tab);
+    c.g1 = h_fx(z_fixed(e4_edge(m.small, s + 1u), mu, inv24), m.tab);
+    const uint32_t p0 = m.small[s], p1 = m.small[s + 1u];
+    c.qa = m.htot + s + p0;
+    c.qf = 1u + (p1 - p0);
     return c;
 }
 
@@ -827,18 +832,34 @@ hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_
     return hipGetLastError();
 }
 
+// Escape slot table: entry p of the bf16 pattern p, with s its ordered
+// index, holds T_n + T_w + Q(s) and Q(s + 1) - Q(s), Q(b) = b + prefix[b].
+// One thread per pattern; the grid covers the 65536 patterns exactly.
+__global__ void __launch_bounds__(256) k_escape_slots(const uint32_t* __restrict__ prefix, uint32_t htot,
+                                                      uint2* __restrict__ out) {
+    const uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t s = order_of_bits<kBF16>(p);
+    const uint32_t p0 = prefix[s], p1 = prefix[s + 1u];
+    out[p] = make_uint2(htot + s + p0, 1u + (p1 - p0));
+}
+
+hipError_t launch_escape_slots(const uint32_t* prefix, uint32_t htot, uint32_t* out, hipStream_t s) {
+    hipLaunchKernelGGL(k_escape_slots, dim3(65536 / 256), dim3(256), 0, s, prefix, htot, reinterpret_cast<uint2*>(out));
+    return hipGetLastError();
+}
+
 // The symbol of escape offset y within [lo, hi]: binary search for the
-// largest s with s + prefix[s] <= y.
+// largest s with Q(s) = s + prefix[s] <= y (bf16: Q(s) from the escape slot
+// table at s's pattern; e4m3: from the LDS prefix).
 template <int KV>
 __device__ __forceinline__ uint32_t escape_symbol(uint32_t lo, uint32_t hi, uint32_t y, const Model& m) {
     while (__ballot(lo < hi)) {
         if (lo < hi) {
             const uint32_t mid = (lo + hi + 1u) >> 1;
-            uint32_t pm;
-            if constexpr (KV == kBF16)
-                pm = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(m.prefix) + (mid << 2));
-            else pm = m.small[mid];
-            if (mid + pm <= y) lo = mid;
+            uint32_t qm;
+            if constexpr (KV == kBF16) qm = m.eslots[2u * bits_of_order<kBF16>(mid)] - m.htot;
+            else qm = mid + m.small[mid];
+            if (qm <= y) lo = mid;
             else hi = mid - 1u;
         }
     }
@@ -851,13 +872,17 @@ __device__ __forceinline__ uint32_t escape_symbol(uint32_t lo, uint32_t hi, uint
 // Q(b) = b + prefix[b] finishes the rest.  Indices stay in [0, N) whatever
 // the prefix holds.
 template <int KV>
-__device__ __forceinline__ uint32_t escape_candidate(bool need, uint32_t y, const uint32_t* bucket, uint32_t shift,
-                                                     const Model& m) {
+__device__ __forceinline__ uint32_t escape_candidate(bool need, uint32_t y, const uint32_t* base, uint32_t boff,
+                                                     uint32_t shift, const Model& m) {
     // entries j and j + 1 (j <= the last bucket but one) in one read; a
     // lane without `need` keeps them equal.  Entries order as their symbols.
+    // The table starts boff bytes after base; the sum stays in the vector
+    // offset, so no second scalar base is kept for it.
     uint32_t e0 = 0, e1 = 0;
     if (need) {
-        const U32Pair v = load_pair(bucket, (y >> shift) << 2);
+        uint32_t off = ((y >> shift) << 2) + boff;
+        __asm__("" : "+v"(off));
+        const U32Pair v = load_pair(base, off);
         e0 = v.a;
         e1 = v.b;
     }
@@ -961,8 +986,12 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         sg = 1.0f;
     }
     constexpr uint32_t kN = Alphabet<KV>::kSize;
-    const Model m{s_tab, a.prefix, s_small};
+    const Model m{s_tab, a.prefix, s_small, a.eslots, htot};
     const uint32_t geo = geo_offset(lane);
+    // bf16: the bucket table follows the escape slot table (one base address
+    // for both)
+    const uint32_t* bucket_base = KV == kBF16 ? a.eslots : a.buckets;
+    const uint32_t bucket_off = KV == kBF16 ? static_cast<uint32_t>(kEscapeSlotsBytes) : 0u;
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
@@ -1041,7 +1070,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         if (esc) {
             // floor-and-escape slots: the symbol comes from the lookup
             misses += __popcll(esc);
-            const uint32_t ce = escape_candidate<KV>(is_esc, target - htot, a.buckets, a.bucket_shift, m);
+            const uint32_t ce = escape_candidate<KV>(is_esc, target - htot, bucket_base, bucket_off, a.bucket_shift, m);
             if (is_esc) kb = ce;
         }
         Cell c = eval_cell<KV, MU>(kb, mu, inv24, m);
@@ -1064,8 +1093,8 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
                     }
                 }
                 const uint32_t fg = c.g1 - c.g0;
-                c.g0 = htot + c.s + c.p0 - fg;
-                c.g1 = c.g0 + fg;
+                c.g0 = c.qa - fg;
+                c.g1 = c.qa;
             }
         }
         // in the cell when target - G0 < G1 - G0 (unsigned: below G0 wraps)
@@ -1077,24 +1106,26 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
             misses += __popcll(need);
             bool hit = ((need >> lane) & 1ull) == 0ull;
             if (!hit) {
-                kb = candidate_of_index<KV>(target < c.g0 ? c.s - 1u : c.s + 1u);
+                const uint32_t s0 = index_of_candidate<KV>(kb);
+                kb = candidate_of_index<KV>(target < c.g0 ? s0 - 1u : s0 + 1u);
                 c = eval_cell<KV, MU>(kb, mu, inv24, m);
                 hit = target - c.g0 < c.g1 - c.g0;
             }
             need = __ballot(!hit);
             if (need) {
                 const bool up = target >= c.g1;
-                const uint32_t sym = coop_gauss<KV, MU>(!hit, target, mu, inv24, up, up ? c.s + 1u : 0u,
-                                                        up ? kN : c.s, up ? c.g1 : 0u, up ? htot : c.g0, m, geo, c.s);
+                const uint32_t s1 = index_of_candidate<KV>(kb);
+                const uint32_t sym = coop_gauss<KV, MU>(!hit, target, mu, inv24, up, up ? s1 + 1u : 0u,
+                                                        up ? kN : s1, up ? c.g1 : 0u, up ? htot : c.g0, m, geo, s1);
                 if (!hit) {
                     kb = candidate_of_index<KV>(sym);
                     c = eval_cell<KV, MU>(kb, mu, inv24, m);
                 }
             }
         }
-        // x = f (x >> 31) + rank, f = f_G + 1 + (prefix[s + 1] - prefix[s]);
-        // x < 2^63, so x >> 31 fits 32 bits
-        const uint32_t f = (c.g1 - c.g0) + 1u + (c.p1 - c.p0);
+        // x = f (x >> 31) + rank, f = f_G + Q(s + 1) - Q(s); x < 2^63, so
+        // x >> 31 fits 32 bits
+        const uint32_t f = (c.g1 - c.g0) + c.qf;
         // the symbol is final: store it right after this step's wait for its
         // prefix read (f is an input of the store only to hold it there).
         // The vector memory counter is in order and counts stores: a store

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libkvc.so")
 KVC_OK, KVC_ERR_INVALID, KVC_ERR_CAPACITY, KVC_ERR_CORRUPT, KVC_ERR_MISMATCH, KVC_ERR_DEVICE = 0, -1, -2, -3, -4, -5
 KVC_BF16, KVC_E4M3, KVC_F32 = 0, 1, 2
 HEADER_BYTES = 128
-DECODE_WORKSPACE_BYTES = 393216
+DECODE_WORKSPACE_BYTES = 917504
 ESTIMATE_WORKSPACE_BYTES = 256
 ENCODE_STAGES = 4     # side-information checksum, coding kernel, size scan, compaction
 DECODE_STAGES = 2     # side-information checksum + escape bucket table, decoding kernel
