@@ -1059,8 +1059,9 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
 
     // One symbol of every lane: row t of the chunk, predictor mean mu.  The
     // first step of a batch loads the means of the next batch right after
-    // its prefix read: the vector memory counter is in order, so this step's
-    // wait for the prefix does not include them and the next step's does.
+    // its escape slot table read: the vector memory counter is in order, so
+    // this step's wait for that read does not include them and the next
+    // step's does.
     auto step = [&](uint32_t t, float mu, bool first) {
         const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
         // candidate: the cell the aim lands in, with its exact CDF terms
@@ -1127,7 +1128,8 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         // x >> 31 fits 32 bits
         const uint32_t f = (c.g1 - c.g0) + c.qf;
         // the symbol is final: store it right after this step's wait for its
-        // prefix read (f is an input of the store only to hold it there).
+        // escape slot table read (f is an input of the store only to hold it
+        // there).
         // The vector memory counter is in order and counts stores: a store
         // issued before that wait would be waited for too, and one issued
         // in the next step would hold up the next wait.
