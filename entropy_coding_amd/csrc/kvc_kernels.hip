@@ -941,12 +941,15 @@ struct WordRing {
     }
 };
 
+constexpr uint32_t kPageWindow = 32;      // block-table entries a paged-decode wave keeps in LDS
+
 template <int KV, int MU, bool PAGED>
 __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(64))) k_decode(DecodeArgs a) {
     __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
     __shared__ __align__(16) float2 s_aim[kAimEntries + 1];
     __shared__ uint32_t s_ring[kDecodeBlock / 64][kRingDwords];
     __shared__ uint32_t s_small[KV == kE4M3 ? kE4Words : 1];
+    __shared__ int32_t s_pages[PAGED ? kDecodeBlock / 64 : 1][PAGED ? kPageWindow : 1];
     if constexpr (KV == kE4M3) build_e4_lds(s_small, a.prefix);      // exact prefix + edges
     copy_to_lds(s_tab, a.table, static_cast<uint32_t>(kTableBytes / 16));
     copy_to_lds(s_aim, a.aim, static_cast<uint32_t>(kAimBytes / 16));
@@ -1010,14 +1013,24 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
     // (this chunk's 64 channels of head h), a token further each step; at a
     // page boundary the next entry of the sequence's table row names the
     // page.  Every entry the call reads was checked before the launch
-    // (k_check_pages; the decode does nothing when one is bad).  Reads of
-    // the pool pointer and of table entries come back in vector registers
-    // and are moved to scalar ones, where the stores take their base address.
+    // (k_check_pages; the decode does nothing when one is bad).  The wave
+    // stages kPageWindow entries of its table row at a time in LDS, so a
+    // page boundary reads LDS rather than waiting on a global read (whose
+    // wait would also cover the row stores in flight).  Reads of the pool
+    // pointer and of table entries come back in vector registers and are
+    // moved to scalar ones, where the stores take their base address.
     uint64_t page_row = 0, page_base = 0;
-    const int32_t* page_entry = nullptr;
+    const int32_t* page_entry = nullptr;                 // the window's first entry
     uint32_t page_left = 0, tok_bytes = 0, page_bytes = 0;
+    uint32_t page_slot = 0;                              // the current page's entry in the window
+    uint32_t cols_left = 0;                              // checked entries from page_entry on
+    auto fill_window = [&]() {
+        const uint32_t n = cols_left < kPageWindow ? cols_left : kPageWindow;
+        if (static_cast<uint32_t>(lane) < n) s_pages[wave][lane] = page_entry[lane];
+        __builtin_amdgcn_wave_barrier();
+    };
     auto page_at = [&](uint32_t row) -> uint64_t {
-        const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(*page_entry));
+        const uint32_t e = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(s_pages[wave][page_slot]));
         return page_base + uint64_t(e) * page_bytes + uint64_t(row) * tok_bytes;
     };
     if constexpr (PAGED) {
@@ -1036,6 +1049,8 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         const uint32_t page_i = cp.t0 / a.paged.page_tokens;
         const uint32_t in_page = cp.t0 - page_i * a.paged.page_tokens;
         page_entry = a.paged.block_table + int64_t(b) * a.paged.max_pages + page_i;
+        cols_left = static_cast<uint32_t>((a.geom.tokens + a.paged.page_tokens - 1) / a.paged.page_tokens) - page_i;
+        fill_window();
         page_left = a.paged.page_tokens - in_page;
         page_row = page_at(in_page);
     }
@@ -1140,7 +1155,12 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
             else __asm__ volatile("global_store_byte %0, %1, %2" : : "v"(kv_lane), "v"(kb), "s"(page_row), "v"(f));
             page_row += tok_bytes;
             if (--page_left == 0 && t + 1u < cp.len) {  // the next token starts a page
-                ++page_entry;
+                if (++page_slot == kPageWindow) {        // (a checked entry follows the window)
+                    page_entry += kPageWindow;
+                    cols_left -= kPageWindow;
+                    fill_window();
+                    page_slot = 0;
+                }
                 page_left = a.paged.page_tokens;
                 page_row = page_at(0);
             }
