@@ -295,19 +295,13 @@ __device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float in
     return make_slots(ha, hb, load_pair(m.eslots, kb << 3));
 }
 
-// Cache policy of the streamed reads (KV, means, stream words: each read
-// once) and of the decoder's row stores: non-temporal, so they do not push
-// the coders' tables out of the vector L1.  (The encoder's word-slot stores
-// stay ordinary: non-temporal there made the encoder 12% slower.)
-constexpr int kStream = 2;
-
 // Rows of the chunk through buffer resources: the lane's byte offset in a
 // vector register, the row's in a scalar one.
 template <typename T>
 __device__ __forceinline__ uint32_t load_row_elem(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t row_off) {
-    if constexpr (sizeof(T) == 1) return __builtin_amdgcn_raw_buffer_load_b8(r, lane_off, row_off, kStream);
-    else if constexpr (sizeof(T) == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, lane_off, row_off, kStream);
-    else return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, row_off, kStream);
+    if constexpr (sizeof(T) == 1) return __builtin_amdgcn_raw_buffer_load_b8(r, lane_off, row_off, 0);
+    else if constexpr (sizeof(T) == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, lane_off, row_off, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, row_off, 0);
 }
 
 template <int KV, int MU, int U>
@@ -918,7 +912,7 @@ struct WordRing {
 
     __device__ __forceinline__ uint32_t load(uint32_t block, uint32_t lane) const {
         // the whole offset in the vector operand, where the range check applies
-        return __builtin_amdgcn_raw_buffer_load_b32(words, (block * 64u + lane) * 4u, 0, kStream);
+        return __builtin_amdgcn_raw_buffer_load_b32(words, (block * 64u + lane) * 4u, 0, 0);
     }
     __device__ __forceinline__ void init(uint32_t lane) {
         base = 0;
@@ -946,6 +940,14 @@ struct WordRing {
         }
     }
 };
+
+// Cache policy of the decoder's row stores (each row written once):
+// non-temporal, decode 1.6% faster on the 8B-shaped cache.  The streamed
+// reads keep the default policy: non-temporal reads gained nothing more
+// there and made the decoder 9% slower on small calls whose inputs stay in
+// the last-level cache, and non-temporal word-slot stores made the encoder
+// 12% slower.
+constexpr int kNonTemporal = 2;
 
 constexpr uint32_t kPageWindow = 32;      // block-table entries a paged-decode wave keeps in LDS
 
@@ -1070,8 +1072,8 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
     using MRaw = typename std::conditional<MU == kBF16, uint16_t, uint32_t>::type;
     auto load_mu = [&](uint32_t t) -> MRaw {
         const uint32_t roff = (t < cp.len ? t : cp.len - 1) * D * static_cast<uint32_t>(sizeof(MT));
-        if constexpr (MU == kBF16) return __builtin_amdgcn_raw_buffer_load_b16(mub, mu_lane, roff, kStream);
-        else return __builtin_amdgcn_raw_buffer_load_b32(mub, mu_lane, roff, kStream);
+        if constexpr (MU == kBF16) return __builtin_amdgcn_raw_buffer_load_b16(mub, mu_lane, roff, 0);
+        else return __builtin_amdgcn_raw_buffer_load_b32(mub, mu_lane, roff, 0);
     };
     auto mu_of = [](MRaw r) -> float {
         return MU == kBF16 ? __uint_as_float(static_cast<uint32_t>(r) << 16) : __uint_as_float(static_cast<uint32_t>(r));
@@ -1179,7 +1181,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         }
         else {
             __asm__ volatile("" : : "v"(f));
-            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(kb), outb, kv_lane, ooff, kStream);
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(kb), outb, kv_lane, ooff, kNonTemporal);
         }
         x = static_cast<unsigned long long>(f) * static_cast<uint32_t>(x >> kLog2M) + (target - c.g0);
 
