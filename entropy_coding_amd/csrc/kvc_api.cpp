@@ -23,14 +23,14 @@ constexpr uint32_t kLanes = 64;
 constexpr uint32_t kVersion = 3;   // stream format version (split slot ranges, floor of z * 2^24)
 constexpr uint32_t kMaxChunkTokens = 1u << 20;
 constexpr int64_t kMaxScalars = int64_t(1) << 40;
-// decode workspace: control block, the escape slot table, the escape
-// bucket table (u32; right after the slot table, where the bf16 decoder
-// expects it), the mixture table and the aim table
-constexpr uint64_t kDecodeSlotsOffset = 256;
-constexpr uint64_t kDecodeBucketOffset = kDecodeSlotsOffset + kvc::kEscapeSlotsBytes;
+// decode workspace: control block, the escape count table, the escape
+// bucket table (two u32 per entry; right after the count table, where the
+// bf16 decoder expects it), the mixture table and the aim table
+constexpr uint64_t kDecodeCountOffset = 256;
+constexpr uint64_t kDecodeBucketOffset = kDecodeCountOffset + kvc::kEscapeCountBytes;
 constexpr uint64_t kDecodeTableOffset = 786944;
 constexpr uint64_t kDecodeAimOffset = kDecodeTableOffset + 49408;
-static_assert(kDecodeBucketOffset + 4 * kvc::kEscapeBucketsMax <= kDecodeTableOffset &&
+static_assert(kDecodeBucketOffset + 8 * kvc::kEscapeBucketsMax <= kDecodeTableOffset &&
                   kDecodeTableOffset % 256 == 0 && kDecodeTableOffset + kvc::kTableBytes <= kDecodeAimOffset &&
                   kDecodeAimOffset + kvc::kAimBytes <= KVC_DECODE_WORKSPACE_BYTES,
               "decode workspace layout");
@@ -335,9 +335,9 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     if ((e = kvc::launch_coder_tables(phi, tn, tw, reinterpret_cast<uint32_t*>(ws + l.table), nullptr, s)) !=
         hipSuccess)
         return KVC_ERR_DEVICE;
-    if (p->kv_dtype == KVC_BF16 && (e = kvc::launch_escape_slots(prefix ? prefix : phi.zero, tn + tw,
-                                                                  reinterpret_cast<uint32_t*>(ws + l.eslots), s)) !=
-                                       hipSuccess)
+    if (p->kv_dtype == KVC_BF16 &&
+        (e = kvc::launch_escape_slots(prefix ? prefix : phi.zero, tn + tw, reinterpret_cast<uint32_t*>(ws + l.eslots),
+                                      nullptr, s)) != hipSuccess)
         return KVC_ERR_DEVICE;
     timer.mark(1);
 
@@ -486,8 +486,8 @@ int decode_common(const void* d_in, uint64_t in_bytes, const void* d_mu, const f
                                       reinterpret_cast<float*>(ws + kDecodeAimOffset), s)) != hipSuccess)
         return KVC_ERR_DEVICE;
     if (p.kv_dtype == KVC_BF16 &&
-        (e = kvc::launch_escape_slots(prefix ? prefix : phi.zero, tn + tw,
-                                      reinterpret_cast<uint32_t*>(ws + kDecodeSlotsOffset), s)) != hipSuccess)
+        (e = kvc::launch_escape_slots(prefix ? prefix : phi.zero, tn + tw, nullptr,
+                                      reinterpret_cast<uint32_t*>(ws + kDecodeCountOffset), s)) != hipSuccess)
         return KVC_ERR_DEVICE;
     timer.mark(1);
     const uint8_t* in = static_cast<const uint8_t*>(d_in);
@@ -505,7 +505,7 @@ int decode_common(const void* d_in, uint64_t in_bytes, const void* d_mu, const f
     da.aim = reinterpret_cast<const float*>(ws + kDecodeAimOffset);
     da.buckets = buckets;
     da.bucket_shift = shift;
-    da.eslots = reinterpret_cast<const uint32_t*>(ws + kDecodeSlotsOffset);
+    da.ecount = reinterpret_cast<const uint32_t*>(ws + kDecodeCountOffset);
     da.kv_out = d_kv_out;
     da.paged = po;
     da.ctl = ctl;

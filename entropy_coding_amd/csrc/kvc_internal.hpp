@@ -110,7 +110,7 @@ struct DecodeArgs {
     const float* aim;                   // the aim table, kAimFloats floats
     const uint32_t* buckets;            // escape bucket table (launch_escape_buckets)
     uint32_t bucket_shift;
-    const uint32_t* eslots;             // bf16: the escape slot table (launch_escape_slots),
+    const uint32_t* ecount;             // bf16: the escape count table (launch_escape_slots),
                                         // with the bucket table right after it
     void* kv_out;                       // contiguous output [planes][tokens][channels], or
     PagedOut paged;                     // the paged output (launch_decode with paged = true)
@@ -149,17 +149,22 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, bool p
 // Sets kFlagBadPage if a block-table entry of columns [0, used) lies outside the pool.
 hipError_t launch_check_pages(const PagedOut& p, int64_t used, Control* ctl, hipStream_t s);
 // Bucket table of Q(b) = b + prefix[b] for the decoder's floor-and-escape
-// lookup: entry j = (s_j << 16) | pattern of s_j, where s_j is the largest
-// s < n_sym with Q(s) <= j << shift (entries order as their symbols).
+// lookup, two u32 per entry: entry j = ((s_j << 16) | pattern of s_j,
+// Q(s_j)), where s_j is the largest s < n_sym with Q(s) <= j << shift
+// (entries order as their symbols).
 constexpr uint32_t kEscapeBucketsMax = 65538;
 hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_t shift, uint32_t n_entries,
                                  int kv_dtype, uint32_t* bucket, hipStream_t s);
 // Escape slot table of the bf16 alphabet, indexed by bit pattern p (s its
 // ordered index): entry p = (T_n + T_w + Q(s), Q(s + 1) - Q(s)), two u32,
-// so a coder finds the start and the count of a symbol's floor-and-escape
-// slots in one read.
+// so the encoder finds the start and the count of a symbol's
+// floor-and-escape slots in one read.  The escape count table holds the
+// count alone (one u32 per pattern) for the decoder, which needs the start
+// only for slots in the floor-and-escape range, where the bucket table
+// gives it.  Either output may be null.
 constexpr uint64_t kEscapeSlotsBytes = 65536ull * 8;
-hipError_t launch_escape_slots(const uint32_t* prefix, uint32_t htot, uint32_t* out, hipStream_t s);
+constexpr uint64_t kEscapeCountBytes = 65536ull * 4;
+hipError_t launch_escape_slots(const uint32_t* prefix, uint32_t htot, uint32_t* out, uint32_t* count, hipStream_t s);
 // sigma calibration: float64 partial sums per (split, plane, channel)
 struct CalibPart {
     double sum;

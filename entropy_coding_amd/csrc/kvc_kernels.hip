@@ -654,11 +654,11 @@ __device__ __forceinline__ uint32_t candidate_bits(uint32_t cand) {
     else return cand;
 }
 
-// A candidate symbol with its exact CDF terms: G at both cell edges, the
-// start of its floor-and-escape slots (T_n + T_w + Q(s)) and their count
-// (Q(s + 1) - Q(s)), where Q(b) = b + prefix[b].
+// A candidate symbol with its exact CDF terms: G at both cell edges and
+// the count of its floor-and-escape slots, Q(s + 1) - Q(s), where
+// Q(b) = b + prefix[b].
 struct Cell {
-    uint32_t g0, g1, qa, qf;
+    uint32_t g0, g1, qf;
 };
 
 // Ordered index of a candidate (bf16: pattern in the upper half).
@@ -675,8 +675,8 @@ __device__ __forceinline__ uint32_t index_of_candidate(uint32_t cand) {
 // z saturates at +-24 as for an infinite edge, sigma <= 2^96); with an fp32
 // mean it becomes infinite, as the format defines.  Inf and NaN patterns
 // reach here only from the escape lookup, and their G terms are replaced
-// by the caller (every edge of theirs is infinite).  The escape terms come
-// from the escape slot table, at the pattern's entry.
+// by the caller (every edge of theirs is infinite).  The escape slot count
+// comes from the escape count table, at the pattern's entry.
 template <int MU>
 __device__ __forceinline__ Cell eval_bf16(uint32_t kw, float mu, float inv24, const Model& m) {
     const uint32_t sign = kw & 0x80000000u;
@@ -688,9 +688,7 @@ __device__ __forceinline__ Cell eval_bf16(uint32_t kw, float mu, float inv24, co
     Cell c;
     c.g0 = __builtin_elementwise_min(ha, hb);
     c.g1 = __builtin_elementwise_max(ha, hb);
-    const U32Pair q = load_pair(m.eslots, (kw >> 13) & 0x7FFF8u);     // 8 bytes per pattern
-    c.qa = q.a;
-    c.qf = q.b;
+    c.qf = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(m.ecount) + ((kw >> 14) & 0x3FFFCu));
     return c;
 }
 
@@ -700,9 +698,7 @@ __device__ __forceinline__ Cell eval_e4m3(uint32_t kb, float mu, float inv24, co
     const uint32_t s = order_of_bits<kE4M3>(kb);
     c.g0 = h_fx(z_fixed(e4_edge(m.small, s), mu, inv24), m.tab);
     c.g1 = h_fx(z_fixed(e4_edge(m.small, s + 1u), mu, inv24), m.tab);
-    const uint32_t p0 = m.small[s], p1 = m.small[s + 1u];
-    c.qa = m.htot + s + p0;
-    c.qf = 1u + (p1 - p0);
+    c.qf = 1u + (m.small[s + 1u] - m.small[s]);
     return c;
 }
 
@@ -801,16 +797,16 @@ __device__ __forceinline__ uint32_t coop_gauss(bool need, uint32_t target, float
 }
 
 // Bucket table of the static part Q(b) = b + prefix[b] of the CDF: with
-// s_j the largest s < N with Q(s) <= j * 2^shift, entry j holds s_j in its
-// high 16 bits and s_j's bit pattern in its low 16 (so entries order as
-// their symbols, and an entry gives the decoder's candidate word of s_j
-// at once).  A slot y in the floor-and-escape range has its symbol in
-// [s_(y >> shift), s_((y >> shift) + 1)].  The shift is the smallest that
-// keeps the table within kEscapeBucketsMax entries.
+// s_j the largest s < N with Q(s) <= j * 2^shift, entry j holds, first,
+// s_j in its high 16 bits and s_j's bit pattern in its low 16 (so entries
+// order as their symbols, and an entry gives the decoder's candidate word
+// of s_j at once), then Q(s_j).  A slot y in the floor-and-escape range has
+// its symbol in [s_(y >> shift), s_((y >> shift) + 1)].  The shift is the
+// smallest that keeps the table within kEscapeBucketsMax entries.
 template <int KV>
 __global__ void __launch_bounds__(256) k_escape_buckets(const uint32_t* __restrict__ prefix, uint32_t n_sym,
                                                         uint32_t shift, uint32_t n_entries,
-                                                        uint32_t* __restrict__ bucket) {
+                                                        uint2* __restrict__ bucket) {
     const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= n_entries) return;
     const unsigned long long y = static_cast<unsigned long long>(j) << shift;
@@ -820,80 +816,97 @@ __global__ void __launch_bounds__(256) k_escape_buckets(const uint32_t* __restri
         if (static_cast<unsigned long long>(mid) + prefix[mid] <= y) lo = mid;
         else hi = mid - 1u;
     }
-    bucket[j] = (lo << 16) | candidate_bits<KV>(candidate_of_index<KV>(lo));
+    bucket[j] = make_uint2((lo << 16) | candidate_bits<KV>(candidate_of_index<KV>(lo)), lo + prefix[lo]);
 }
 
 hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_t shift, uint32_t n_entries,
                                  int kv_dtype, uint32_t* bucket, hipStream_t s) {
     const dim3 grid((n_entries + 255) / 256), block(256);
     if (kv_dtype == kBF16)
-        hipLaunchKernelGGL(k_escape_buckets<kBF16>, grid, block, 0, s, prefix, n_sym, shift, n_entries, bucket);
-    else hipLaunchKernelGGL(k_escape_buckets<kE4M3>, grid, block, 0, s, prefix, n_sym, shift, n_entries, bucket);
+        hipLaunchKernelGGL(k_escape_buckets<kBF16>, grid, block, 0, s, prefix, n_sym, shift, n_entries,
+                           reinterpret_cast<uint2*>(bucket));
+    else hipLaunchKernelGGL(k_escape_buckets<kE4M3>, grid, block, 0, s, prefix, n_sym, shift, n_entries,
+                            reinterpret_cast<uint2*>(bucket));
     return hipGetLastError();
 }
 
 // Escape slot table: entry p of the bf16 pattern p, with s its ordered
-// index, holds T_n + T_w + Q(s) and Q(s + 1) - Q(s), Q(b) = b + prefix[b].
-// One thread per pattern; the grid covers the 65536 patterns exactly.
+// index, holds T_n + T_w + Q(s) and Q(s + 1) - Q(s), Q(b) = b + prefix[b];
+// the escape count table holds Q(s + 1) - Q(s) alone.  Either output may be
+// null.  One thread per pattern; the grid covers the 65536 patterns exactly.
 __global__ void __launch_bounds__(256) k_escape_slots(const uint32_t* __restrict__ prefix, uint32_t htot,
-                                                      uint2* __restrict__ out) {
+                                                      uint2* __restrict__ out, uint32_t* __restrict__ count) {
     const uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;
     const uint32_t s = order_of_bits<kBF16>(p);
     const uint32_t p0 = prefix[s], p1 = prefix[s + 1u];
-    out[p] = make_uint2(htot + s + p0, 1u + (p1 - p0));
+    if (out) out[p] = make_uint2(htot + s + p0, 1u + (p1 - p0));
+    if (count) count[p] = 1u + (p1 - p0);
 }
 
-hipError_t launch_escape_slots(const uint32_t* prefix, uint32_t htot, uint32_t* out, hipStream_t s) {
-    hipLaunchKernelGGL(k_escape_slots, dim3(65536 / 256), dim3(256), 0, s, prefix, htot, reinterpret_cast<uint2*>(out));
+hipError_t launch_escape_slots(const uint32_t* prefix, uint32_t htot, uint32_t* out, uint32_t* count, hipStream_t s) {
+    hipLaunchKernelGGL(k_escape_slots, dim3(65536 / 256), dim3(256), 0, s, prefix, htot, reinterpret_cast<uint2*>(out),
+                       count);
     return hipGetLastError();
 }
 
 // The symbol of escape offset y within [lo, hi]: binary search for the
-// largest s with Q(s) = s + prefix[s] <= y (bf16: Q(s) from the escape slot
-// table at s's pattern; e4m3: from the LDS prefix).
+// largest s with Q(s) = s + prefix[s] <= y (e4m3: the LDS prefix), with
+// Q(lo) = qlo on entry; qlo leaves holding Q of the result.
 template <int KV>
-__device__ __forceinline__ uint32_t escape_symbol(uint32_t lo, uint32_t hi, uint32_t y, const Model& m) {
+__device__ __forceinline__ uint32_t escape_symbol(uint32_t lo, uint32_t hi, uint32_t y, uint32_t& qlo, const Model& m) {
     while (__ballot(lo < hi)) {
         if (lo < hi) {
             const uint32_t mid = (lo + hi + 1u) >> 1;
             uint32_t qm;
-            if constexpr (KV == kBF16) qm = m.eslots[2u * bits_of_order<kBF16>(mid)] - m.htot;
+            if constexpr (KV == kBF16) qm = mid + m.prefix[mid];
             else qm = mid + m.small[mid];
-            if (qm <= y) lo = mid;
-            else hi = mid - 1u;
+            if (qm <= y) {
+                lo = mid;
+                qlo = qm;
+            } else {
+                hi = mid - 1u;
+            }
         }
     }
     return lo;
 }
 
 // Candidate word of the floor-and-escape slot y for every lane with `need`
-// set: the bucket table narrows the symbol to [lo, hi] and, when lo = hi,
-// gives the candidate word itself; a per-lane binary search over
-// Q(b) = b + prefix[b] finishes the rest.  Indices stay in [0, N) whatever
-// the prefix holds.
+// set, and q = Q(s) of its symbol s: the bucket table narrows the symbol to
+// [lo, hi] and, when lo = hi, gives the candidate word and Q(s) at once; a
+// per-lane binary search over Q(b) = b + prefix[b] finishes the rest.
+// Indices stay in [0, N) whatever the prefix holds.
+struct EscapeHit {
+    uint32_t cand, q;
+};
+struct alignas(4) U32Quad {
+    uint32_t a, b, c, d;
+};
+
 template <int KV>
-__device__ __forceinline__ uint32_t escape_candidate(bool need, uint32_t y, const uint32_t* base, uint32_t boff,
-                                                     uint32_t shift, const Model& m) {
+__device__ __forceinline__ EscapeHit escape_candidate(bool need, uint32_t y, const uint32_t* base, uint32_t boff,
+                                                      uint32_t shift, const Model& m) {
     // entries j and j + 1 (j <= the last bucket but one) in one read; a
     // lane without `need` keeps them equal.  Entries order as their symbols.
     // The table starts boff bytes after base; the sum stays in the vector
     // offset, so no second scalar base is kept for it.
-    uint32_t e0 = 0, e1 = 0;
+    uint32_t e0 = 0, e1 = 0, q = 0;
     if (need) {
-        uint32_t off = ((y >> shift) << 2) + boff;
+        uint32_t off = ((y >> shift) << 3) + boff;
         __asm__("" : "+v"(off));
-        const U32Pair v = load_pair(base, off);
+        const U32Quad v = *reinterpret_cast<const U32Quad*>(reinterpret_cast<const char*>(base) + off);
         e0 = v.a;
-        e1 = v.b;
+        q = v.b;
+        e1 = v.c;
     }
     if (__ballot(e0 < e1)) {
         // a bucket that starts within a run of symbols: search it
         const bool search = e0 < e1;
-        const uint32_t s = escape_symbol<KV>(e0 >> 16, e1 >> 16, y, m);
+        const uint32_t s = escape_symbol<KV>(e0 >> 16, e1 >> 16, y, q, m);
         if (search) e0 = (s << 16) | candidate_bits<KV>(candidate_of_index<KV>(s));
     }
-    if constexpr (KV == kBF16) return e0 << 16;
-    else return e0 & 0xFFFFu;
+    if constexpr (KV == kBF16) return EscapeHit{e0 << 16, q};
+    else return EscapeHit{e0 & 0xFFFFu, q};
 }
 
 // Stream words of a chunk, staged through a per-wave LDS ring of two
@@ -997,12 +1010,12 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         sg = 1.0f;
     }
     constexpr uint32_t kN = Alphabet<KV>::kSize;
-    const Model m{s_tab, a.prefix, s_small, a.eslots, htot};
+    const Model m{s_tab, a.prefix, s_small, nullptr, htot, a.ecount};
     const uint32_t geo = geo_offset(lane);
-    // bf16: the bucket table follows the escape slot table (one base address
-    // for both)
-    const uint32_t* bucket_base = KV == kBF16 ? a.eslots : a.buckets;
-    const uint32_t bucket_off = KV == kBF16 ? static_cast<uint32_t>(kEscapeSlotsBytes) : 0u;
+    // bf16: the bucket table follows the escape count table (one base
+    // address for both)
+    const uint32_t* bucket_base = KV == kBF16 ? a.ecount : a.buckets;
+    const uint32_t bucket_off = KV == kBF16 ? static_cast<uint32_t>(kEscapeCountBytes) : 0u;
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
@@ -1082,7 +1095,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
 
     // One symbol of every lane: row t of the chunk, predictor mean mu.  The
     // first step of a batch loads the means of the next batch right after
-    // its escape slot table read: the vector memory counter is in order, so
+    // its escape count table read: the vector memory counter is in order, so
     // this step's wait for that read does not include them and the next
     // step's does.
     auto step = [&](uint32_t t, float mu, bool first) {
@@ -1091,11 +1104,13 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         uint32_t kb = nearest_candidate<KV>(__fmaf_rn(aim_z(target, htot, s_aim), sg, mu));
         const bool is_esc = target >= htot;
         const uint64_t esc = __ballot(is_esc);
+        uint32_t qs = 0;                                 // Q(s) of an escape lane's symbol
         if (esc) {
             // floor-and-escape slots: the symbol comes from the lookup
             misses += __popcll(esc);
-            const uint32_t ce = escape_candidate<KV>(is_esc, target - htot, bucket_base, bucket_off, a.bucket_shift, m);
-            if (is_esc) kb = ce;
+            const EscapeHit h = escape_candidate<KV>(is_esc, target - htot, bucket_base, bucket_off, a.bucket_shift, m);
+            if (is_esc) kb = h.cand;
+            qs = h.q;
         }
         Cell c = eval_cell<KV, MU>(kb, mu, inv24, m);
         if (first) {
@@ -1117,8 +1132,8 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
                     }
                 }
                 const uint32_t fg = c.g1 - c.g0;
-                c.g0 = c.qa - fg;
-                c.g1 = c.qa;
+                c.g1 = htot + qs;
+                c.g0 = c.g1 - fg;
             }
         }
         // in the cell when target - G0 < G1 - G0 (unsigned: below G0 wraps)
@@ -1151,7 +1166,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(6
         // x >> 31 fits 32 bits
         const uint32_t f = (c.g1 - c.g0) + c.qf;
         // the symbol is final: store it right after this step's wait for its
-        // escape slot table read (f is an input of the store only to hold it
+        // escape count table read (f is an input of the store only to hold it
         // there).
         // The vector memory counter is in order and counts stores: a store
         // issued before that wait would be waited for too, and one issued
