@@ -525,7 +525,7 @@ hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream
 // aim, only the cost of finding it.
 // ---------------------------------------------------------------------------
 constexpr int kDecodeBlock = 1024;
-constexpr int kDecodeBatch = 8;
+constexpr int kDecodeBatch = 12;
 
 // Aim table: z(d), the position at which the interpolated mixture table
 // reaches d, is linear between the knots d_j = 2^(j >> 6) (1 + (j & 63) / 64);
