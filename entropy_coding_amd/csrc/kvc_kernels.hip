@@ -965,7 +965,7 @@ constexpr int kNonTemporal = 2;
 constexpr uint32_t kPageWindow = 32;      // block-table entries a paged-decode wave keeps in LDS
 
 template <int KV, int MU, bool PAGED>
-__global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(64))) k_decode(DecodeArgs a) {
+__global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(80))) k_decode(DecodeArgs a) {
     __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
     __shared__ __align__(16) float2 s_aim[kAimEntries + 1];
     __shared__ uint32_t s_ring[kDecodeBlock / 64][kRingDwords];
