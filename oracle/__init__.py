@@ -23,15 +23,21 @@ Parity status of each function (what pins it other than itself):
   gauss_cum / escape_cum       -- the slot ranges tile the coder range and
                                   add up to the mixture frequencies
   encode / decode              -- round trip, exact size band, unbounded
-                                  big-integer rANS
+                                  big-integer rANS, a two-token chunk whose
+                                  payload (states, word order of every step
+                                  block, padding) is written out with Python
+                                  ints from the format's steps
   build_marginal               -- brute-force counting on tiny inputs
   calibrate_sigma              -- float64 closed form, minimum of the
                                   Gaussian cost
-  side_hash                    -- parity unpinned (an integrity checksum of
-                                  the side information; its value is a
-                                  convention of the format, not of the pages)
-  model_bits_float             -- closed form for a single Gaussian in a
-                                  constant-ulp region
+  side_hash                    -- splitmix64's published outputs for seed 0
+                                  pin the mixer; a small case summed word by
+                                  word with Python ints pins the sum
+  model_bits_float             -- closed forms for the narrow part alone and
+                                  the wide part alone (a Gaussian at 3 sigma)
+                                  in a constant-ulp region; the escape part
+                                  alone against the smoothed histogram counted
+                                  pattern by pattern
 """
 
 from .kvc_oracle import *  # noqa: F401,F403

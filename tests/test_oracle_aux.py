@@ -68,6 +68,50 @@ def test_calibrate_sigma_floor_and_f32_mu():
     assert np.all(s == np.float32(2.0 ** -30))
 
 
+# splitmix64 (Vigna): the state advances by 0x9E3779B97F4A7C15 per output
+# and each output is the finaliser of the new state; seeded with 0, the
+# generator's first three outputs are published values.
+SPLITMIX64_SEED0 = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def _mix_scalar(z: int) -> int:
+    """The splitmix64 finaliser on a Python int, reduced mod 2^64 by hand."""
+    m = (1 << 64) - 1
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & m
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & m
+    return z ^ (z >> 31)
+
+
+def test_side_hash_mixer_is_splitmix64():
+    """The oracle's mixer reproduces splitmix64's published first outputs
+    (seed 0), so a wrong shift or constant cannot pass."""
+    from oracle import kvc_oracle as K
+    golden = 0x9E3779B97F4A7C15
+    for k, want in enumerate(SPLITMIX64_SEED0, start=1):
+        state = (k * golden) % (1 << 64)
+        assert _mix_scalar(state) == want
+        with np.errstate(over="ignore"):
+            assert int(K._mix64(np.uint64(state))) == want
+
+
+def test_side_hash_small_case_by_hand():
+    """Two sigma words and a three-entry prefix, summed word by word with
+    Python ints: sum over (tag, index, word) of mix((index << 32 | word) +
+    tag * golden) mod 2^64, sigma words tag 1, prefix words tag 2."""
+    golden = 0x9E3779B97F4A7C15
+    sig = np.array([[0.5, 3.0]], dtype=np.float32)          # words 0x3F000000, 0x40400000
+    pref = np.array([0, 7, 1 << 30], dtype=np.int64)
+    m = (1 << 64) - 1
+    want = 0
+    for i, w in enumerate([0x3F000000, 0x40400000]):
+        want += _mix_scalar(((i << 32 | w) + 1 * golden) & m)
+    for i, w in enumerate([0, 7, 1 << 30]):
+        want += _mix_scalar(((i << 32 | w) + 2 * golden) & m)
+    assert O.side_hash(sig, pref) == want & m
+    assert O.side_hash(sig, None) == (_mix_scalar((0x3F000000 + golden) & m)
+                                      + _mix_scalar(((1 << 32 | 0x40400000) + golden) & m)) & m
+
+
 def test_side_hash_sensitivity():
     rng = np.random.default_rng(4)
     sig = rng.random((16, 128)).astype(np.float32)

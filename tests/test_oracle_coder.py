@@ -95,18 +95,71 @@ def test_matches_unbounded_big_integer_rans():
     assert 1 * 64 <= 8 * len(body) - big_bits - 0 <= 17 * 64 + 48
 
 
+def _bf16(x: float) -> int:
+    return int(W.to_numpy_bits(torch.tensor([x], dtype=torch.float32).to(torch.bfloat16))[0])
+
+
 def test_interleaving_order_within_a_step():
-    """Hand-check one step: with all lanes emitting, the step block must be
-    the last-emitted words in lane order, then the first-emitted ones."""
-    kv, mu, sig, samples, mu_dtype = case(planes=1, tokens=2, channels=64)
-    pref = O.build_marginal(samples, O.BF16, 9500, 300)
-    st = O.encode(kv, mu, sig, pref, O.BF16, mu_dtype, 9500, 300, 2)
-    body = O.chunk_payload(st, 0)
-    # decoding must consume exactly the words; the words after the states
-    # belong to step 0 first (decoder order)
-    out = O.decode(st, mu, sig, pref)
-    assert np.array_equal(out, kv)
-    assert len(body) % 8 == 0
+    """One chunk of 64 lanes and two tokens, its payload written out here
+    from S-8 and S-9 with Python ints.  Each lane's (mu, sigma, KV) is picked
+    so that its frequency is about 2^31 (KV = mu, tiny sigma), exactly 1 (KV
+    far from mu, tiny sigma) or in between, which makes lanes emit 0, 1 or 2
+    words in an irregular lane pattern.  Expected payload: the 64 final
+    states (u64 little-endian), then for t = 0 and t = 1 the step block:
+    the last-emitted word of every lane with count >= 1 in ascending lane
+    order, then the first-emitted word of every lane with count = 2, then
+    zero padding to 8 bytes."""
+    kinds = [[(l * 7 + t * 3) % 5 for l in range(64)] for t in range(2)]
+    # kind: (mu, sigma, kv): 0, 3 -> f about 2^31; 1, 4 -> f = 1; 2 -> f about 2^16
+    spec = {0: (1.0, 2.0 ** -30, 1.0), 1: (1.0, 2.0 ** -30, 2.0), 2: (1.0, 2.0 ** -5, 1.125),
+            3: (-3.0, 2.0 ** -30, -3.0), 4: (-3.0, 2.0 ** -30, 5.0)}
+    kv = np.zeros((1, 2, 64), dtype=np.uint16)
+    mu = np.zeros((1, 2, 64), dtype=np.uint16)
+    sig = np.zeros((1, 64), dtype=np.float32)
+    for l in range(64):
+        # sigma is per lane; a lane's two tokens share it (take the smaller kind's)
+        sig[0, l] = np.float32(min(spec[kinds[0][l]][1], spec[kinds[1][l]][1]))
+        for t in range(2):
+            m, _, x = spec[kinds[t][l]]
+            mu[0, t, l], kv[0, t, l] = _bf16(m), _bf16(x)
+    w = (10000, 0)
+    t_n, t_w, _ = O.budgets(O.BF16, *w)
+    inv = (np.float32(1) / sig).astype(np.float32)
+    s = O.order_index(kv, O.BF16)[0]
+    m32 = O.mu_to_f32(mu, O.BF16)[0]
+    g0 = O.gauss_cum(s, m32, inv, O.BF16, t_n, t_w)
+    g1 = O.gauss_cum(s + 1, m32, inv, O.BF16, t_n, t_w)
+    # S-8 lane by lane, tokens last to first; words[t][l] lists the words in
+    # emission order
+    words = [[None] * 64 for _ in range(2)]
+    states = []
+    for l in range(64):
+        x = O.L
+        for t in (1, 0):
+            fg = int(g1[t, l] - g0[t, l])
+            q = int(s[t, l])                      # Q(s) = s without an escape part
+            f = fg + 1
+            count = int((x >> 32) >= f) + int((x >> 48) >= f)
+            em = []
+            for _ in range(count):
+                em.append(x & 0xFFFF)
+                x >>= 16
+            words[t][l] = em
+            r = x % f
+            slot = int(g0[t, l]) + r if r < fg else t_n + t_w + q + (r - fg)
+            x = (x // f) * O.M + slot
+        states.append(x)
+    counts = [[len(words[t][l]) for l in range(64)] for t in range(2)]
+    assert {0, 1, 2} <= set(counts[0]) and {0, 1} <= set(counts[1])
+    body = b"".join(x.to_bytes(8, "little") for x in states)
+    for t in (0, 1):
+        block = [words[t][l][-1] for l in range(64) if counts[t][l] >= 1]
+        block += [words[t][l][0] for l in range(64) if counts[t][l] == 2]
+        body += b"".join(v.to_bytes(2, "little") for v in block)
+    body += bytes(-len(body) % 8)
+    st = O.encode(kv, mu, sig, None, O.BF16, O.BF16, *w, 2)
+    assert O.chunk_payload(st, 0) == body
+    assert np.array_equal(O.decode(st, mu, sig, None), kv)
 
 
 def test_damaged_streams_are_rejected():

@@ -113,3 +113,53 @@ def test_escape_component_is_about_11_bits(pages):
     p = c[c > 0] / c.sum()
     h = float(-(p * np.log2(p)).sum())
     assert abs(h - pages["escape_component_bits"]["value"]) < 1.0
+
+
+def test_wide_part_alone_is_a_gaussian_of_three_sigma():
+    """Weights (0, 10000) leave only the N(mu, (3 sigma)^2) part: the float
+    model must equal the single Gaussian at scale 3 sigma (3 sigma is exact
+    in float32 here), and both the discretised entropy of that Gaussian and
+    1/2 log2(2 pi e (3 sigma)^2) - log2(width) for cells narrow against it."""
+    sigma = 2.0 ** -6                      # 3 sigma = 0.046875 exactly
+    kv, mu, _ = gaussian_case(1.5, 3 * sigma, 1 << 17, seed=23)
+    sig1 = np.full((1, 64), sigma, dtype=np.float32)
+    sig3 = np.full((1, 64), 3 * sigma, dtype=np.float32)
+    wide = O.model_bits_float(kv, mu, sig1, None, O.BF16, O.BF16, 0, 10000)
+    single = O.model_bits_float(kv, mu, sig3, None, O.BF16, O.BF16, 10000, 0)
+    assert wide == single
+    from scipy.special import ndtr
+    v = 1.0 + np.arange(128) / 128.0
+    p = ndtr((v + 2.0 ** -8 - 1.5) / (3 * sigma)) - ndtr((v - 2.0 ** -8 - 1.5) / (3 * sigma))
+    p = p[p > 0]
+    exact = float(-(p * np.log2(p)).sum())
+    closed = 0.5 * math.log2(2 * math.pi * math.e * (3 * sigma) ** 2) - math.log2(2.0 ** -7)
+    se = 1.1 / math.sqrt(kv.size)
+    assert abs(wide - exact) < 4.5 * se
+    assert abs(exact - closed) < 0.005
+    # the integer model of the same weights agrees with the float model
+    assert abs(O.model_bits_int(kv, mu, sig1, None, O.BF16, O.BF16, 0, 10000) - wide) < 1e-3
+
+
+def test_escape_part_alone_is_the_smoothed_histogram():
+    """Weights (0, 0) leave only the escape part: every scalar costs
+    -log2 p_hat(x).  Against the +1-smoothed histogram counted here pattern
+    by pattern, p(x) = (1 + #{samples equal to x}) / (N + #samples), the
+    integer prefix differs by at most one budget unit per symbol, so the mean
+    cost differs by at most log2(1 + (N + #samples) / T_e)."""
+    kv, mu, sig, samples = W.tiny_case(31, planes=2, tokens=40, channels=128)
+    kvn, mun, sgn, smn = W.to_numpy_bits(kv), W.to_numpy_bits(mu), sig.numpy(), W.to_numpy_bits(samples)
+    pref = O.build_marginal(smn, O.BF16, 0, 0)
+    got = O.model_bits_float(kvn, mun, sgn, pref, O.BF16, O.BF16, 0, 0)
+    counts = {}
+    for u in smn.ravel().tolist():
+        counts[u] = counts.get(u, 0) + 1
+    tot = 65536 + smn.size
+    bits = [-math.log2((1 + counts.get(u, 0)) / tot) for u in kvn.ravel().tolist()]
+    want = sum(bits) / len(bits)
+    t_e = O.budgets(O.BF16, 0, 0)[2]
+    assert t_e == O.M - 65536
+    assert abs(got - want) <= math.log2(1 + tot / t_e)
+    # the integer model codes (1 + dP) / M where the float model has dP / T_e
+    # (dP >= T_e / tot - 1 units): the two differ by less than that bound too
+    gi = O.model_bits_int(kvn, mun, sgn, pref, O.BF16, O.BF16, 0, 0)
+    assert abs(got - gi) <= math.log2(1 + tot / t_e)
