@@ -809,12 +809,12 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
         bits = bits_of_order(sym, kv_dtype)
         for i in range(nb):
             n_t = int(ln[i])
-            blk = bits[i, :n_t, :]
+            rows = bits[i, :n_t, :]
             if out_full is not None:
                 t0 = int(tcid[i]) * tcn
-                out_full[g[i], t0:t0 + n_t, 64 * k[i]:64 * k[i] + 64] = blk
+                out_full[g[i], t0:t0 + n_t, 64 * k[i]:64 * k[i] + 64] = rows
             else:
-                out_dict[int(cid[i])] = blk.astype(out_dict_dtype(kv_dtype))
+                out_dict[int(cid[i])] = rows.astype(out_dict_dtype(kv_dtype))
     return out_full if out_full is not None else out_dict
 
 

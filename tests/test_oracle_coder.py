@@ -207,3 +207,18 @@ def test_golden_tiny_stream_is_stable():
         pref = O.build_marginal(samples, kv_dtype, w_n, w_w)
         st = O.encode(kv, mu, sig, pref, kv_dtype, mu_dtype, w_n, w_w, tc)
         assert len(st) == size and hashlib.sha256(st).hexdigest() == digest, name
+
+
+@pytest.mark.parametrize("sigma_block", [0, 14])
+def test_batching_does_not_change_the_result(sigma_block):
+    """Encoding and decoding in batches of chunks (down to one chunk per
+    batch) gives the same stream and the same KV as one batch."""
+    kv, mu, sig, samples, mu_dtype = case(planes=2, tokens=28)
+    if sigma_block:
+        sig = np.stack([sig, sig * np.float32(0.5)], axis=1)          # [G, 2 blocks, D]
+    pref = O.build_marginal(samples, O.BF16, 9500, 300)
+    one = O.encode(kv, mu, sig, pref, O.BF16, mu_dtype, 9500, 300, 7, sigma_block_tokens=sigma_block)
+    for bc in (1, 3):
+        assert O.encode(kv, mu, sig, pref, O.BF16, mu_dtype, 9500, 300, 7, batch_chunks=bc,
+                        sigma_block_tokens=sigma_block) == one
+        assert np.array_equal(O.decode(one, mu, sig, pref, batch_chunks=bc), kv)
