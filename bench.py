@@ -67,54 +67,61 @@ def log(*a):
 # CPU oracle baseline (runs before the GPU is touched; plain fork pool)
 # ---------------------------------------------------------------------------
 def _oracle_worker(args):
-    import numpy as np
-    import oracle as O
-    kv, mu, sig, pref, tc, w = args
-    t0 = time.perf_counter()
-    st = O.encode(kv, mu, sig, pref, O.BF16, O.BF16, w[0], w[1], tc)
-    t1 = time.perf_counter()
-    out = O.decode(st, mu, sig, pref)
-    t2 = time.perf_counter()
-    assert np.array_equal(out, kv)
-    return t1 - t0, t2 - t1, len(st)
-
-
-def cpu_baseline(workload, planes_per_worker: int, tokens: int):
-    """The oracle on a bounded sample of the same workload: layer-0 planes
-    drawn with the same recipe on the CPU, split over the host cores; each
-    worker codes and decodes its planes (token chunk of `tokens`)."""
+    """One worker's share: half the planes of one layer at the workload's
+    full token count and chunk length, drawn on the host with the same
+    recipe; returns (encode s, decode s, scalars, stream bytes)."""
     import numpy as np
     import torch
     import oracle as O
     from entropy_coding_amd import workloads as W
-
-    cores = len(os.sched_getaffinity(0))
-    kv, mu = W.layer_data(workload, 0, device="cpu", tokens=tokens)
-    sig = W.layer_sigma_true(workload, 0, device="cpu")
-    samples = W.marginal_samples(workload, device="cpu")
-    w = (workload.w_narrow_bp, workload.w_wide_bp)
-    pref = O.build_marginal(W.to_numpy_bits(samples), O.BF16, *w)
-    kvn, mun, sgn = W.to_numpy_bits(kv), W.to_numpy_bits(mu), sig.numpy()
-    g_avail = kvn.shape[0]
-    jobs = []
-    for i in range(cores):
-        sel = [(i * planes_per_worker + j) % g_avail for j in range(planes_per_worker)]
-        jobs.append((kvn[sel], mun[sel], sgn[sel], pref, tokens, w))
-    n = cores * planes_per_worker * tokens * workload.channels
+    wid, layer, half, tc = args
     torch.set_num_threads(1)
+    w = W.WORKLOADS[wid]
+    kv, mu = W.layer_data(w, layer, device="cpu")
+    sig = W.layer_sigma_true(w, layer, device="cpu")
+    pref = O.build_marginal(W.to_numpy_bits(W.marginal_samples(w, device="cpu")), O.BF16,
+                            w.w_narrow_bp, w.w_wide_bp)
+    g = kv.shape[0] // 2
+    sel = slice(half * g, (half + 1) * g)
+    kvn, mun, sgn = W.to_numpy_bits(kv[sel]), W.to_numpy_bits(mu[sel]), sig[sel].numpy()
+    del kv, mu
+    t0 = time.perf_counter()
+    st = O.encode(kvn, mun, sgn, pref, O.BF16, O.BF16, w.w_narrow_bp, w.w_wide_bp, tc)
+    t1 = time.perf_counter()
+    out = O.decode(st, mun, sgn, pref)
+    t2 = time.perf_counter()
+    assert np.array_equal(out, kvn)
+    return t1 - t0, t2 - t1, kvn.size, len(st)
+
+
+def cpu_baseline(workload, workers: int = 0):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    each worker codes and decodes half the planes of one layer (32 planes of
+    4096 tokens x 128 channels, 448 chunks of the workload's chunk length,
+    coded by the oracle in one batch), one worker per host core.  The rate
+    is the sample's raw bytes over the slowest worker's encode and decode
+    time (the pool's parallel time; the host-side data generation in each
+    worker is not timed)."""
+    cores = len(os.sched_getaffinity(0))
+    n_workers = workers or cores
+    jobs = [(workload.cid, i // 2 % workload.layers, i % 2, workload.chunk_tokens) for i in range(n_workers)]
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
-    with ctx.Pool(cores) as pool:
+    with ctx.Pool(n_workers) as pool:
         res = pool.map(_oracle_worker, jobs)
     wall = time.perf_counter() - t0
+    n = sum(r[2] for r in res)
     enc = max(r[0] for r in res)
     dec = max(r[1] for r in res)
+    rt = max(r[0] + r[1] for r in res)
     raw = 2.0 * n
+    per = res[0][2] // (workload.tokens * workload.channels)
     return {
-        "value": raw / wall / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-        "sample": f"{n} scalars ({cores} workers x {planes_per_worker} planes x {tokens} tokens x "
-                  f"{workload.channels} channels of layer 0, same recipe drawn on the host); "
-                  f"encode+decode round trip, wall {wall:.2f} s",
+        "value": raw / rt / 1e9, "unit": "GB/s", "cores": n_workers, "kind": "oracle",
+        "sample": f"{n} scalars: {n_workers} workers, each {per} planes x {workload.tokens} tokens x "
+                  f"{workload.channels} channels of one layer (same recipe drawn on the host), "
+                  f"{workload.chunk_tokens}-token chunks coded in one batch; encode+decode round trip, "
+                  f"slowest worker {rt:.2f} s (pool wall {wall:.2f} s)",
         "encode_gbps": raw / enc / 1e9, "decode_gbps": raw / dec / 1e9,
     }
 
@@ -236,8 +243,7 @@ def main():
                     help="workload id: 2 = the bench line; 1 and 3 code the whole cache in one call, 4 one layer per call")
     ap.add_argument("--calib-reps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-planes-per-worker", type=int, default=8)
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-workers", type=int, default=0, help="oracle workers (0 = one per host core)")
     ap.add_argument("--chunk-tokens", type=int, default=None, help="override the workload's chunk length")
     ap.add_argument("--offload", action="store_true",
                     help="(per-layer workload 4) also time the host-offload reload: pinned streams, copies overlapped with decode")
@@ -265,7 +271,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and w.kv_dtype == W.BF16:
         log("[bench] cpu_baseline: oracle on a host sample ...")
-        cpu = cpu_baseline(w, args.cpu_planes_per_worker, args.cpu_tokens)
+        cpu = cpu_baseline(w, args.cpu_workers)
         log(f"[bench] cpu_baseline {cpu['value']:.4f} GB/s on {cpu['cores']} cores")
 
     import torch
