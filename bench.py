@@ -178,6 +178,7 @@ def offload_reload(w, kv, mu, sigma, prefix, kvc, enc, parts, dws, steps: int):
     host = torch.empty(offs[-1], dtype=torch.uint8, pin_memory=True)
     for s, o in zip(streams, offs):
         host[o:o + s.numel()].copy_(s)
+    headers = [host[o:o + 128].numpy().copy() for o in offs[:-1]]      # host copies: no device read
     del streams
     stage = [torch.empty(max(sizes), dtype=torch.uint8, device=dev) for _ in range(2)]
     out = torch.empty_like(kv, dtype=torch.int16 if kv.dtype == torch.bfloat16 else torch.uint8)
@@ -199,7 +200,8 @@ def offload_reload(w, kv, mu, sigma, prefix, kvc, enc, parts, dws, steps: int):
             if l + 1 < len(parts):
                 fetch(l + 1)          # its buffer was last read by the decode of layer l - 1, already done
             compute.wait_event(ready[l])
-            rc = kvc.kvc_decode_into(stage[l % 2][:sizes[l]], mu[sl], sigma[sl], prefix, out[sl], dws)
+            rc = kvc.kvc_decode_into(stage[l % 2][:sizes[l]], mu[sl], sigma[sl], prefix, out[sl], dws,
+                                     header=headers[l])
             if rc != kvc.KVC_OK:
                 raise kvc.KvcError(rc, "kvc_decode")
         torch.cuda.synchronize()
@@ -327,9 +329,9 @@ def main():
             ei, di = {}, {}
             st = enc(kv[sl], mu[sl], sigma[sl], prefix, info=ei)
             if paged is not None:
-                rc = kvc.kvc_decode_paged(st, mu[sl], sigma[sl], prefix, paged, dws, info=di)
+                rc = kvc.kvc_decode_paged(st, mu[sl], sigma[sl], prefix, paged, dws, info=di, header=enc.header)
             else:
-                rc = kvc.kvc_decode_into(st, mu[sl], sigma[sl], prefix, kv_out[sl], dws, info=di)
+                rc = kvc.kvc_decode_into(st, mu[sl], sigma[sl], prefix, kv_out[sl], dws, info=di, header=enc.header)
             if rc != kvc.KVC_OK:
                 raise kvc.KvcError(rc, "kvc_decode")
             e_ms = [a + b for a, b in zip(e_ms, ei["stage_ms"])]

@@ -20,7 +20,7 @@ constexpr uint32_t kLog2M = 31;
 constexpr uint32_t kLog2L = 47;
 constexpr uint32_t kWordBits = 16;
 constexpr uint32_t kLanes = 64;
-constexpr uint32_t kVersion = 3;   // stream format version (split slot ranges, floor of z * 2^24)
+constexpr uint32_t kVersion = 4;   // stream format version (split slot ranges, floor of z * 2^24, header CRC)
 constexpr uint32_t kMaxChunkTokens = 1u << 20;
 constexpr int64_t kMaxScalars = int64_t(1) << 40;
 // decode workspace: control block, the escape count table, the escape
@@ -189,9 +189,21 @@ kvc::StreamHeader make_header(const kvc_params* p, const ChunkGeom& g, uint32_t 
     return h;
 }
 
+// CRC-32 (reflected polynomial 0xEDB88320, initial value and final xor
+// 0xFFFFFFFF: the zlib / gzip / PNG checksum), bit by bit.
+uint32_t crc32(const uint8_t* b, size_t n) {
+    uint32_t c = 0xFFFFFFFFu;
+    for (size_t i = 0; i < n; ++i) {
+        c ^= b[i];
+        for (int k = 0; k < 8; ++k) c = (c >> 1) ^ ((c & 1u) ? 0xEDB88320u : 0u);
+    }
+    return ~c;
+}
+
 int parse_header(const uint8_t* b, kvc_params* p, ChunkGeom* g, uint64_t* payload, uint64_t* hash) {
     if (std::memcmp(b, "KVC1", 4) != 0 || get16(b, 4) != kVersion || get16(b, 6) != KVC_HEADER_BYTES)
         return KVC_ERR_CORRUPT;
+    if (get32(b, kvc::kHeaderCrcOffset) != crc32(b, kvc::kHeaderCrcOffset)) return KVC_ERR_CORRUPT;
     if (b[10] != kLog2M || b[11] != kLog2L || b[12] != kWordBits || b[13] != kLanes || get16(b, 14) != 0)
         return KVC_ERR_CORRUPT;
     kvc_params q;
@@ -216,7 +228,7 @@ int parse_header(const uint8_t* b, kvc_params* p, ChunkGeom* g, uint64_t* payloa
     if (q.chunk_tokens == 0 || !geometry(q.planes, q.tokens, q.channels, q.chunk_tokens, q.sigma_block_tokens, g))
         return KVC_ERR_CORRUPT;
     if (get64(b, 64) != static_cast<uint64_t>(g->n_chunks)) return KVC_ERR_CORRUPT;
-    for (int i = 92; i < KVC_HEADER_BYTES; ++i)
+    for (int i = kvc::kHeaderCrcOffset + 4; i < KVC_HEADER_BYTES; ++i)
         if (b[i]) return KVC_ERR_CORRUPT;
     *payload = get64(b, 72);
     *hash = get64(b, 80);
@@ -306,10 +318,11 @@ int kvc_encode_sizes(const kvc_params* p, uint64_t* h_max_stream_bytes, uint64_t
 
 int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const float* d_sigma,
                const uint32_t* d_prefix, void* d_out, uint64_t out_capacity, uint64_t* h_out_bytes,
-               void* d_workspace, uint64_t workspace_bytes, void* stream, kvc_encode_info* h_info) {
+               void* h_header_out, void* d_workspace, uint64_t workspace_bytes, void* stream,
+               kvc_encode_info* h_info) {
     ChunkGeom g;
-    if (!params_geometry(p, &g) || !d_kv || !d_mu || !d_sigma || !d_out || !h_out_bytes || !d_workspace)
-        return KVC_ERR_INVALID;
+    if (!params_geometry(p, &g) || !d_kv || !d_mu || !d_sigma || !d_out || !d_workspace) return KVC_ERR_INVALID;
+    if (!h_out_bytes && (h_header_out || h_info)) return KVC_ERR_INVALID;   // host outputs need the sync
     uint32_t tn, tw, te;
     if (!budgets(p->kv_dtype, p->w_narrow_bp, p->w_wide_bp, &tn, &tw, &te)) return KVC_ERR_INVALID;
     if (te && !d_prefix) return KVC_ERR_INVALID;
@@ -329,8 +342,9 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     StageTimer timer(h_info ? h_info->stage_ms : nullptr, KVC_ENCODE_STAGES, s);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(0);
-    if ((e = kvc::launch_side_hash(d_sigma, sigma_words(g), prefix, prefix ? alphabet(p->kv_dtype) + 1u : 0u, ctl,
-                                   s)) != hipSuccess)
+    const kvc::StreamHeader no_header{};
+    if ((e = kvc::launch_side_hash(d_sigma, sigma_words(g), prefix, prefix ? alphabet(p->kv_dtype) + 1u : 0u, nullptr,
+                                   no_header, ctl, s)) != hipSuccess)
         return KVC_ERR_DEVICE;
     if ((e = kvc::launch_coder_tables(phi, tn, tw, reinterpret_cast<uint32_t*>(ws + l.table), nullptr, s)) !=
         hipSuccess)
@@ -373,17 +387,37 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     ca.out = static_cast<uint8_t*>(d_out);
     ca.out_capacity = out_capacity;
     ca.ctl = ctl;
+    ca.header_copy = ws + kvc::kHeaderCopyOffset;
     const kvc::StreamHeader h = make_header(p, g, tn, tw, te);
     if ((e = kvc::launch_compact(ca, h, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(4);
-
-    Control host;
-    if ((e = hipMemcpyAsync(&host, ctl, sizeof(host), hipMemcpyDeviceToHost, s)) != hipSuccess) return KVC_ERR_DEVICE;
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) return KVC_ERR_DEVICE;
+    if (!h_out_bytes) return KVC_OK;                  // asynchronous: kvc_encode_result reads the outcome
+    const int st = kvc_encode_result(d_workspace, stream, h_out_bytes, h_header_out);
     timer.read();
-    *h_out_bytes = KVC_HEADER_BYTES + 8ull * uint64_t(g.n_chunks + 1) + host.total_payload;
+    return st;
+}
+
+int kvc_encode_result(const void* d_workspace, void* stream, uint64_t* h_out_bytes, void* h_header_out) {
+    if (!d_workspace || !h_out_bytes || !aligned(d_workspace, 256)) return KVC_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t blk[kvc::kHeaderCopyOffset + KVC_HEADER_BYTES];
+    if (hipMemcpyAsync(blk, d_workspace, sizeof(blk), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return KVC_ERR_DEVICE;
+    Control host;
+    std::memcpy(&host, blk, sizeof(host));
+    const uint8_t* head = blk + kvc::kHeaderCopyOffset;
+    // the workspace's header copy is written also when the stream did not
+    // fit, so the size it needed is known then too
+    kvc_params q;
+    ChunkGeom g;
+    uint64_t payload = 0, hash = 0;
     if (host.flags & kvc::kFlagBadSigma) return KVC_ERR_INVALID;
+    if (parse_header(head, &q, &g, &payload, &hash) != KVC_OK || payload != host.total_payload)
+        return KVC_ERR_DEVICE;
+    *h_out_bytes = KVC_HEADER_BYTES + 8ull * uint64_t(g.n_chunks + 1) + payload;
     if (host.flags & kvc::kFlagCapacity) return KVC_ERR_CAPACITY;
+    if (h_header_out) std::memcpy(h_header_out, head, KVC_HEADER_BYTES);
     return KVC_OK;
 }
 
@@ -401,37 +435,36 @@ int kvc_stream_info(const void* h_header, uint64_t header_bytes, kvc_params* h_p
 
 namespace {
 
-// kvc_decode and kvc_decode_paged: the output is d_kv_out, or the paged
-// pools when `paged` is not null.
-int decode_common(const void* d_in, uint64_t in_bytes, const void* d_mu, const float* d_sigma,
-                  const uint32_t* d_prefix, void* d_kv_out, const kvc_paged_kv* paged, void* d_workspace,
-                  uint64_t workspace_bytes, void* stream, kvc_decode_info* h_info) {
-    if (!d_in || !d_mu || !d_sigma || (!d_kv_out && !paged) || !d_workspace) return KVC_ERR_INVALID;
+// Sizes in bytes of one element of each dtype.
+uint64_t kv_size(int32_t t) { return t == KVC_BF16 ? 2u : 1u; }
+uint64_t mu_size(int32_t t) { return t == KVC_F32 ? 4u : 2u; }
+
+// kvc_decode_async and kvc_decode_paged_async: the output is d_kv_out, or
+// the paged pools when `paged` is not null.  Everything is checked on the
+// host against the header the caller holds before anything is launched;
+// the kernels compare the device stream's header with it.
+int decode_launch(const void* h_header, const void* d_in, uint64_t in_bytes, const void* d_mu, uint64_t mu_bytes,
+                  const float* d_sigma, uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
+                  void* d_kv_out, uint64_t kv_out_bytes, const kvc_paged_kv* paged, void* d_workspace,
+                  uint64_t workspace_bytes, void* stream, float* stage_ms) {
+    if (!h_header || !d_in || !d_mu || !d_sigma || (!d_kv_out && !paged) || !d_workspace) return KVC_ERR_INVALID;
     if (workspace_bytes < KVC_DECODE_WORKSPACE_BYTES) return KVC_ERR_CAPACITY;
     if (!aligned(d_in, 8) || !aligned(d_workspace, 256) || !aligned(d_sigma, 4) || !aligned(d_prefix, 4) ||
         !aligned(d_kv_out, 2) || !aligned(d_mu, 2))
         return KVC_ERR_INVALID;
     if (paged) {
         if (!paged->d_pools || !paged->d_block_table || !aligned(paged->d_pools, 8) ||
-            !aligned(paged->d_block_table, 4) || paged->reserved != 0 || paged->page_tokens < 1 ||
-            paged->batch < 1 || paged->heads < 1 || paged->batch > 0x7FFFFFFF || paged->heads > 0x7FFFFFFF ||
-            paged->num_pages < 1 || paged->num_pages > 0x7FFFFFFF || paged->max_pages < 1 ||
-            paged->max_pages > kMaxScalars || paged->batch * paged->max_pages > kMaxScalars)
+            !aligned(paged->d_block_table, 4) || paged->page_tokens < 1 || paged->batch < 1 || paged->heads < 1 ||
+            paged->batch > 0x7FFFFFFF || paged->heads > 0x7FFFFFFF || paged->num_pages < 1 ||
+            paged->num_pages > 0x7FFFFFFF || paged->max_pages < 1 || paged->max_pages > kMaxScalars ||
+            paged->batch * paged->max_pages > kMaxScalars || paged->n_pools < 1 || paged->n_pools > kMaxScalars ||
+            paged->reserved != 0)
             return KVC_ERR_INVALID;
     }
-    if (in_bytes < KVC_HEADER_BYTES) return KVC_ERR_CORRUPT;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipSuccess;
-    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
-    if (e != hipSuccess) return KVC_ERR_DEVICE;
-
-    uint8_t hb[KVC_HEADER_BYTES];
-    if ((e = hipMemcpyAsync(hb, d_in, sizeof(hb), hipMemcpyDeviceToHost, s)) != hipSuccess) return KVC_ERR_DEVICE;
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) return KVC_ERR_DEVICE;
     kvc_params p;
     ChunkGeom g;
     uint64_t payload = 0, hash = 0;
-    int st = parse_header(hb, &p, &g, &payload, &hash);
+    int st = parse_header(static_cast<const uint8_t*>(h_header), &p, &g, &payload, &hash);
     if (st != KVC_OK) return st;
     const uint64_t dir_bytes = 8ull * uint64_t(g.n_chunks + 1);
     if (in_bytes < KVC_HEADER_BYTES + dir_bytes || in_bytes - KVC_HEADER_BYTES - dir_bytes != payload)
@@ -441,16 +474,24 @@ int decode_common(const void* d_in, uint64_t in_bytes, const void* d_mu, const f
     if (te && !d_prefix) return KVC_ERR_INVALID;
     const uint32_t* prefix = te ? d_prefix : nullptr;
     if (!data_aligned(p.kv_dtype, p.mu_dtype, d_kv_out, d_mu, d_sigma, d_prefix)) return KVC_ERR_INVALID;
+    // the caller's buffers must hold what the header describes
+    const uint64_t n = uint64_t(g.planes) * uint64_t(g.tokens) * uint64_t(g.channels);
+    const uint32_t n_sym = alphabet(p.kv_dtype);
+    if (mu_bytes / mu_size(p.mu_dtype) < n || sigma_bytes / 4u < sigma_words(g)) return KVC_ERR_INVALID;
+    if (prefix && prefix_bytes / 4u < uint64_t(n_sym) + 1u) return KVC_ERR_INVALID;
+    if (!paged && kv_out_bytes / kv_size(p.kv_dtype) < n) return KVC_ERR_INVALID;
     kvc::PagedOut po{};
     if (paged) {
-        // planes ordered (layer, kv, batch, head); every token's page inside the table's rows
-        const int64_t per_layer = 2 * paged->batch * paged->heads;
-        if (g.planes % per_layer != 0) return KVC_ERR_INVALID;
+        // planes ordered (layer, kv, batch, head), one pool per (layer, kv);
+        // every token's page inside the table's rows; every pool holds
+        // num_pages pages of page_tokens rows of heads x channels elements
+        const int64_t per_kv = paged->batch * paged->heads;
+        if (g.planes % (2 * per_kv) != 0 || g.planes / per_kv != paged->n_pools) return KVC_ERR_INVALID;
         if (paged->max_pages < (g.tokens + paged->page_tokens - 1) / paged->page_tokens) return KVC_ERR_INVALID;
-        // a page's bytes fit 32 bits
-        const int64_t esize = p.kv_dtype == KVC_BF16 ? 2 : 1;
-        if (paged->heads * g.channels * esize * int64_t(paged->page_tokens) >= (int64_t(1) << 32))
-            return KVC_ERR_INVALID;
+        const uint64_t page_bytes = uint64_t(paged->heads) * uint64_t(g.channels) * kv_size(p.kv_dtype) *
+                                    uint64_t(paged->page_tokens);
+        if (page_bytes >= (uint64_t(1) << 32)) return KVC_ERR_INVALID;        // a page's bytes fit 32 bits
+        if (paged->pool_bytes / page_bytes < uint64_t(paged->num_pages)) return KVC_ERR_INVALID;
         po.pools = paged->d_pools;
         po.block_table = paged->d_block_table;
         po.max_pages = paged->max_pages;
@@ -459,21 +500,26 @@ int decode_common(const void* d_in, uint64_t in_bytes, const void* d_mu, const f
         po.heads = static_cast<uint32_t>(paged->heads);
         po.batch = static_cast<uint32_t>(paged->batch);
     }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
+    if (e != hipSuccess) return KVC_ERR_DEVICE;
 
     Control* ctl = static_cast<Control*>(d_workspace);
     // escape bucket table after the control block: the smallest shift that
     // keeps ((N + T_e - 1) >> shift) + 2 entries within the table
-    const uint32_t n_sym = alphabet(p.kv_dtype);
     const uint64_t q_total = uint64_t(n_sym) + te;
     uint32_t shift = 0;
     while (((q_total - 1) >> shift) + 2 > kvc::kEscapeBucketsMax) ++shift;
     const uint32_t n_buckets = static_cast<uint32_t>(((q_total - 1) >> shift) + 2);
     uint32_t* buckets = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d_workspace) + kDecodeBucketOffset);
-    StageTimer timer(h_info ? h_info->stage_ms : nullptr, KVC_DECODE_STAGES, s);
+    kvc::StreamHeader expect;
+    std::memcpy(expect.bytes, h_header, KVC_HEADER_BYTES);
+    StageTimer timer(stage_ms, KVC_DECODE_STAGES, s);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(0);
-    if ((e = kvc::launch_side_hash(d_sigma, sigma_words(g), prefix, prefix ? n_sym + 1u : 0u, ctl, s)) !=
-        hipSuccess)
+    if ((e = kvc::launch_side_hash(d_sigma, sigma_words(g), prefix, prefix ? n_sym + 1u : 0u,
+                                   static_cast<const uint8_t*>(d_in), expect, ctl, s)) != hipSuccess)
         return KVC_ERR_DEVICE;
     if (paged && (e = kvc::launch_check_pages(po, (g.tokens + po.page_tokens - 1) / po.page_tokens, ctl, s)) !=
                      hipSuccess)
@@ -508,15 +554,23 @@ int decode_common(const void* d_in, uint64_t in_bytes, const void* d_mu, const f
     da.ecount = reinterpret_cast<const uint32_t*>(ws + kDecodeCountOffset);
     da.kv_out = d_kv_out;
     da.paged = po;
+    da.expect_hash = hash;
     da.ctl = ctl;
     if ((e = kvc::launch_decode(da, p.kv_dtype, p.mu_dtype, paged != nullptr, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(2);
-    Control host;
-    if ((e = hipMemcpyAsync(&host, ctl, sizeof(host), hipMemcpyDeviceToHost, s)) != hipSuccess) return KVC_ERR_DEVICE;
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) return KVC_ERR_DEVICE;
-    timer.read();
-    if (h_info) h_info->fallback_symbols = host.misses;
-    if (host.side_hash != hash) return KVC_ERR_MISMATCH;
+    if (stage_ms) {
+        // stage times need the stream finished: the caller synchronises
+        // through kvc_decode_result right after
+        if (hipStreamSynchronize(s) != hipSuccess) return KVC_ERR_DEVICE;
+        timer.read();
+    }
+    return KVC_OK;
+}
+
+// Status of a decode from its control block (after the stream has finished).
+int decode_status(const Control& host) {
+    if (host.flags & kvc::kFlagHeader) return KVC_ERR_CORRUPT;
+    if (host.flags & kvc::kFlagMismatch) return KVC_ERR_MISMATCH;
     if (host.flags & (kvc::kFlagBadSigma | kvc::kFlagBadPage)) return KVC_ERR_INVALID;
     if (host.flags & kvc::kFlagCorrupt) return KVC_ERR_CORRUPT;
     return KVC_OK;
@@ -526,20 +580,48 @@ int decode_common(const void* d_in, uint64_t in_bytes, const void* d_mu, const f
 
 extern "C" {
 
-int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu, const float* d_sigma,
-               const uint32_t* d_prefix, void* d_kv_out, void* d_workspace, uint64_t workspace_bytes,
-               void* stream, kvc_decode_info* h_info) {
+int kvc_decode_async(const void* h_header, const void* d_in, uint64_t in_bytes, const void* d_mu, uint64_t mu_bytes,
+                     const float* d_sigma, uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
+                     void* d_kv_out, uint64_t kv_out_bytes, void* d_workspace, uint64_t workspace_bytes,
+                     void* stream) {
     if (!d_kv_out) return KVC_ERR_INVALID;
-    return decode_common(d_in, in_bytes, d_mu, d_sigma, d_prefix, d_kv_out, nullptr, d_workspace, workspace_bytes,
-                         stream, h_info);
+    return decode_launch(h_header, d_in, in_bytes, d_mu, mu_bytes, d_sigma, sigma_bytes, d_prefix, prefix_bytes,
+                         d_kv_out, kv_out_bytes, nullptr, d_workspace, workspace_bytes, stream, nullptr);
 }
 
-int kvc_decode_paged(const void* d_in, uint64_t in_bytes, const void* d_mu, const float* d_sigma,
-                     const uint32_t* d_prefix, const kvc_paged_kv* h_paged, void* d_workspace,
-                     uint64_t workspace_bytes, void* stream, kvc_decode_info* h_info) {
+int kvc_decode_result(const void* d_workspace, void* stream, kvc_decode_info* h_info) {
+    if (!d_workspace || !aligned(d_workspace, 256)) return KVC_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Control host;
+    if (hipMemcpyAsync(&host, d_workspace, sizeof(host), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return KVC_ERR_DEVICE;
+    if (h_info) h_info->fallback_symbols = host.misses;
+    return decode_status(host);
+}
+
+int kvc_decode(const void* h_header, const void* d_in, uint64_t in_bytes, const void* d_mu, uint64_t mu_bytes,
+               const float* d_sigma, uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
+               void* d_kv_out, uint64_t kv_out_bytes, void* d_workspace, uint64_t workspace_bytes, void* stream,
+               kvc_decode_info* h_info) {
+    if (!d_kv_out) return KVC_ERR_INVALID;
+    const int st = decode_launch(h_header, d_in, in_bytes, d_mu, mu_bytes, d_sigma, sigma_bytes, d_prefix,
+                                 prefix_bytes, d_kv_out, kv_out_bytes, nullptr, d_workspace, workspace_bytes, stream,
+                                 h_info ? h_info->stage_ms : nullptr);
+    if (st != KVC_OK) return st;
+    return kvc_decode_result(d_workspace, stream, h_info);
+}
+
+int kvc_decode_paged(const void* h_header, const void* d_in, uint64_t in_bytes, const void* d_mu, uint64_t mu_bytes,
+                     const float* d_sigma, uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
+                     const kvc_paged_kv* h_paged, void* d_workspace, uint64_t workspace_bytes, void* stream,
+                     kvc_decode_info* h_info) {
     if (!h_paged) return KVC_ERR_INVALID;
-    return decode_common(d_in, in_bytes, d_mu, d_sigma, d_prefix, nullptr, h_paged, d_workspace, workspace_bytes,
-                         stream, h_info);
+    const int st = decode_launch(h_header, d_in, in_bytes, d_mu, mu_bytes, d_sigma, sigma_bytes, d_prefix,
+                                 prefix_bytes, nullptr, 0, h_paged, d_workspace, workspace_bytes, stream,
+                                 h_info ? h_info->stage_ms : nullptr);
+    if (st != KVC_OK) return st;
+    return kvc_decode_result(d_workspace, stream, h_info);
 }
 
 int kvc_calibrate_sigma(const void* d_kv, const void* d_mu, int32_t kv_dtype, int32_t mu_dtype, int64_t reps,

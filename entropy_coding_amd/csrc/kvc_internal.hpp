@@ -14,9 +14,13 @@ enum : uint32_t {
     kFlagCorrupt = 2u,
     kFlagCapacity = 4u,
     kFlagBadPage = 8u,                  // a block-table entry outside the page pool
+    kFlagMismatch = 16u,                // decode: sigma / prefix checksum differs from the header's
+    kFlagHeader = 32u,                  // decode: the device stream's header differs from the host copy
 };
 
-// Control block at the head of every workspace (cleared by a kernel).
+// Control block at the head of every workspace (cleared by a kernel),
+// followed by a copy of the stream header (encode: written with the
+// stream; read back by kvc_encode_result).
 struct Control {
     uint32_t flags;
     uint32_t pad;
@@ -27,6 +31,8 @@ struct Control {
     unsigned long long reserved[2];
 };
 static_assert(sizeof(Control) == 64, "control block size");
+constexpr uint64_t kHeaderCopyOffset = 64;           // header copy in the workspace, after Control
+constexpr uint32_t kHeaderCrcOffset = 92;            // CRC-32 of header bytes [0, 92) at [92, 96)
 
 struct ChunkGeom {
     int64_t planes, tokens, channels;
@@ -83,6 +89,7 @@ struct CompactArgs {
     uint8_t* out;
     uint64_t out_capacity;
     Control* ctl;
+    uint8_t* header_copy;               // the workspace's copy of the header
 };
 
 // Decoded rows written straight into paged KV pools: pool (layer, kv) is
@@ -114,6 +121,7 @@ struct DecodeArgs {
                                         // with the bucket table right after it
     void* kv_out;                       // contiguous output [planes][tokens][channels], or
     PagedOut paged;                     // the paged output (launch_decode with paged = true)
+    unsigned long long expect_hash;     // the header's side-information checksum
     Control* ctl;
 };
 
@@ -139,8 +147,12 @@ hipError_t launch_clear_control(Control* ctl, hipStream_t s);
 // when `aim` is not null, the decoder's aim table (kAimBytes).
 hipError_t launch_coder_tables(const PhiTables& phi, uint32_t tn, uint32_t tw, uint32_t* table, float* aim,
                                hipStream_t s);
+// Side-information checksum into ctl->side_hash; with `head` not null (a
+// decode), also compares the device stream's first 128 bytes with the host
+// copy `expect` and raises kFlagHeader when they differ.
 hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t* prefix,
-                            uint64_t n_prefix, Control* ctl, hipStream_t s);
+                            uint64_t n_prefix, const uint8_t* head, const StreamHeader& expect, Control* ctl,
+                            hipStream_t s);
 hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);
 hipError_t launch_scan(const uint32_t* chunk_words, int64_t n_chunks,
                        unsigned long long* directory, Control* ctl, hipStream_t s);

@@ -154,7 +154,14 @@ __device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
 
 __global__ void __launch_bounds__(256) k_side_hash(const uint32_t* __restrict__ sigma_words, uint64_t n1,
                                                    const uint32_t* __restrict__ prefix, uint64_t n2,
+                                                   const uint8_t* __restrict__ head, StreamHeader expect,
                                                    Control* ctl) {
+    if (head != nullptr && blockIdx.x == 0 && threadIdx.x < kHeaderBytes / 8) {
+        unsigned long long w, e;
+        __builtin_memcpy(&w, head + 8 * threadIdx.x, 8);
+        __builtin_memcpy(&e, expect.bytes + 8 * threadIdx.x, 8);
+        if (w != e) atomicOr(&ctl->flags, kFlagHeader);
+    }
     const unsigned long long golden = 0x9E3779B97F4A7C15ull;
     unsigned long long acc = 0;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
@@ -169,14 +176,26 @@ __global__ void __launch_bounds__(256) k_side_hash(const uint32_t* __restrict__ 
 }
 
 hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t* prefix,
-                            uint64_t n_prefix, Control* ctl, hipStream_t s) {
+                            uint64_t n_prefix, const uint8_t* head, const StreamHeader& expect, Control* ctl,
+                            hipStream_t s) {
     const uint64_t n = n_sigma + n_prefix;
     uint64_t blocks = (n + 255) / 256;
     if (blocks > 512) blocks = 512;
     if (blocks == 0) blocks = 1;
     hipLaunchKernelGGL(k_side_hash, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s,
-                       reinterpret_cast<const uint32_t*>(sigma), n_sigma, prefix, n_prefix, ctl);
+                       reinterpret_cast<const uint32_t*>(sigma), n_sigma, prefix, n_prefix, head, expect, ctl);
     return hipGetLastError();
+}
+
+// CRC-32 (reflected polynomial 0xEDB88320, as zlib computes it) of the
+// header's first 92 bytes, bit by bit; one thread, once per encode.
+__device__ uint32_t header_crc32(const uint8_t* b) {
+    uint32_t c = 0xFFFFFFFFu;
+    for (uint32_t i = 0; i < kHeaderCrcOffset; ++i) {
+        c ^= b[i];
+        for (int k = 0; k < 8; ++k) c = (c >> 1) ^ ((c & 1u) ? 0xEDB88320u : 0u);
+    }
+    return ~c;
 }
 
 // ---------------------------------------------------------------------------
@@ -446,18 +465,25 @@ __global__ void __launch_bounds__(256) k_compact(CompactArgs a, StreamHeader h) 
     const unsigned long long total = a.ctl->total_payload;
     const uint64_t dir_off = kHeaderBytes;
     const uint64_t pay_off = dir_off + 8ull * static_cast<uint64_t>(n + 1);
-    if (pay_off + total > a.out_capacity) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(&a.ctl->flags, kFlagCapacity);
-        return;
-    }
+    const bool fits = pay_off + total <= a.out_capacity;
     const int tid = threadIdx.x;
-    if (blockIdx.x == 0 && tid < kHeaderBytes / 8) {
-        unsigned long long w;
-        __builtin_memcpy(&w, h.bytes + 8 * tid, 8);
-        if (tid == 72 / 8) w = total;
-        if (tid == 80 / 8) w = a.ctl->side_hash;
-        reinterpret_cast<unsigned long long*>(a.out)[tid] = w;
+    if (blockIdx.x == 0 && tid == 0) {
+        // the payload size and the side-information checksum complete the
+        // header; its CRC covers bytes [0, 92).  The workspace keeps a copy
+        // (also when the stream does not fit, for the size it needed).
+        __shared__ unsigned long long s_head[kHeaderBytes / 8];
+        for (int i = 0; i < kHeaderBytes / 8; ++i) __builtin_memcpy(&s_head[i], h.bytes + 8 * i, 8);
+        s_head[72 / 8] = total;
+        s_head[80 / 8] = a.ctl->side_hash;
+        const uint32_t crc = header_crc32(reinterpret_cast<const uint8_t*>(s_head));
+        s_head[kHeaderCrcOffset / 8] = (s_head[kHeaderCrcOffset / 8] & 0xFFFFFFFFull) | (static_cast<unsigned long long>(crc) << 32);
+        for (int i = 0; i < kHeaderBytes / 8; ++i) {
+            if (fits) reinterpret_cast<unsigned long long*>(a.out)[i] = s_head[i];
+            reinterpret_cast<unsigned long long*>(a.header_copy)[i] = s_head[i];
+        }
+        if (!fits) atomicOr(&a.ctl->flags, kFlagCapacity);
     }
+    if (!fits) return;
     unsigned long long* odir = reinterpret_cast<unsigned long long*>(a.out + dir_off);
     for (int64_t c = blockIdx.x; c < n; c += gridDim.x) {
         const unsigned long long beg = a.directory[c];
@@ -964,6 +990,28 @@ constexpr int kNonTemporal = 2;
 
 constexpr uint32_t kPageWindow = 32;      // block-table entries a paged-decode wave keeps in LDS
 
+// Store of one decoded row element: the row's byte address is wave-uniform
+// (scalar registers) and the lane's byte offset a 32-bit vector register,
+// widened next to the store so that the compiler selects the scalar-base
+// form (no 64-bit address arithmetic per store).  A bf16 candidate word
+// holds the pattern in its high half (a high-half 16-bit store).
+// Non-temporal: each row is written once.  Plain stores rather than inline
+// assembly, so that the compiler sees the address registers and covers them
+// in its hazard handling.
+template <int KV>
+__device__ __forceinline__ void store_row(uint64_t row, uint32_t lane_off, uint32_t cand) {
+    __asm__("" : "+v"(lane_off));
+    using GChar = __attribute__((address_space(1))) char;
+    GChar* p = reinterpret_cast<GChar*>(row) + lane_off;
+    if constexpr (KV == kBF16) {
+        using G16 = __attribute__((address_space(1))) uint16_t;
+        __builtin_nontemporal_store(static_cast<uint16_t>(cand >> 16), reinterpret_cast<G16*>(p));
+    } else {
+        using G8 = __attribute__((address_space(1))) uint8_t;
+        __builtin_nontemporal_store(static_cast<uint8_t>(cand), reinterpret_cast<G8*>(p));
+    }
+}
+
 template <int KV, int MU, bool PAGED>
 __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(80))) k_decode(DecodeArgs a) {
     __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
@@ -980,6 +1028,13 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(8
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (kDecodeBlock / 64) + wave;
     if (chunk >= a.geom.n_chunks) return;
+    // nothing is decoded when the stream's header is not the one the call
+    // was set up with, a block-table entry is bad (paged output), or the
+    // side information is not the encoder's (the same in every wave)
+    if ((a.ctl->flags & (kFlagHeader | kFlagBadPage)) || a.ctl->side_hash != a.expect_hash) {
+        if (chunk == 0 && lane == 0 && a.ctl->side_hash != a.expect_hash) atomicOr(&a.ctl->flags, kFlagMismatch);
+        return;
+    }
     const ChunkPos cp = chunk_pos(a.geom, chunk);
     const uint32_t D = static_cast<uint32_t>(a.geom.channels);
 
@@ -1055,7 +1110,6 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(8
         return page_base + uint64_t(e) * page_bytes + uint64_t(row) * tok_bytes;
     };
     if constexpr (PAGED) {
-        if (a.ctl->flags & kFlagBadPage) return;                // the same in every wave of the launch
         const int64_t per_kv = int64_t(a.paged.batch) * a.paged.heads;
         const int64_t lk = cp.g / per_kv;                       // layer * 2 + kv
         const uint32_t bh = static_cast<uint32_t>(cp.g - lk * per_kv);
@@ -1172,10 +1226,11 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(8
         // issued before that wait would be waited for too, and one issued
         // in the next step would hold up the next wait.
         const uint32_t ooff = t * D * static_cast<uint32_t>(sizeof(KB));
+        // f is a false input of the stored value, which holds the store there
+        uint32_t kst = kb;
+        __asm__ volatile("" : "+v"(kst) : "v"(f));
         if constexpr (PAGED) {
-            if constexpr (KV == kBF16)
-                __asm__ volatile("global_store_short_d16_hi %0, %1, %2 nt" : : "v"(kv_lane), "v"(kb), "s"(page_row), "v"(f));
-            else __asm__ volatile("global_store_byte %0, %1, %2 nt" : : "v"(kv_lane), "v"(kb), "s"(page_row), "v"(f));
+            store_row<KV>(page_row, kv_lane, kst);
             page_row += tok_bytes;
             if (--page_left == 0 && t + 1u < cp.len) {  // the next token starts a page
                 if (++page_slot == kPageWindow) {        // (a checked entry follows the window)
@@ -1187,16 +1242,10 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(8
                 page_left = a.paged.page_tokens;
                 page_row = page_at(0);
             }
-        } else if constexpr (KV == kBF16)
-        {
-            // the pattern is the high half of the candidate word: a high-half
-            // store from a scalar row address and the lane's offset
-            const uint64_t row = out_base + ooff;
-            __asm__ volatile("global_store_short_d16_hi %0, %1, %2 nt" : : "v"(kv_lane), "v"(kb), "s"(row), "v"(f));
-        }
-        else {
-            __asm__ volatile("" : : "v"(f));
-            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(kb), outb, kv_lane, ooff, kNonTemporal);
+        } else if constexpr (KV == kBF16) {
+            store_row<KV>(out_base + ooff, kv_lane, kst);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(kst), outb, kv_lane, ooff, kNonTemporal);
         }
         x = static_cast<unsigned long long>(f) * static_cast<uint32_t>(x >> kLog2M) + (target - c.g0);
 

@@ -9,6 +9,7 @@ been built (``python -m entropy_coding_amd.build``); there is no fallback.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -26,9 +27,9 @@ ENCODE_STAGES = 4     # side-information checksum, coding kernel, size scan, com
 DECODE_STAGES = 2     # side-information checksum + escape bucket table, decoding kernel
 
 EXPORTS = [
-    "kvc_version", "kvc_status_string", "kvc_phi_tables", "kvc_encode_sizes", "kvc_encode",
-    "kvc_stream_info", "kvc_decode", "kvc_decode_paged", "kvc_calibrate_sigma", "kvc_calibrate_sigma_blocks",
-    "kvc_calibrate_sigma_rate",
+    "kvc_version", "kvc_status_string", "kvc_phi_tables", "kvc_encode_sizes", "kvc_encode", "kvc_encode_result",
+    "kvc_stream_info", "kvc_decode", "kvc_decode_async", "kvc_decode_result", "kvc_decode_paged",
+    "kvc_calibrate_sigma", "kvc_calibrate_sigma_blocks", "kvc_calibrate_sigma_rate",
     "kvc_build_marginal", "kvc_estimate_bits", "kvc_cdf_table",
 ]
 
@@ -49,6 +50,7 @@ class kvc_params(ctypes.Structure):
 class kvc_paged_kv(ctypes.Structure):
     _fields_ = [
         ("d_pools", ctypes.c_void_p), ("d_block_table", ctypes.c_void_p),
+        ("n_pools", ctypes.c_int64), ("pool_bytes", ctypes.c_uint64),
         ("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("max_pages", ctypes.c_int64),
         ("num_pages", ctypes.c_int64), ("page_tokens", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
     ]
@@ -81,11 +83,16 @@ _lib_version = _sig("kvc_version", ctypes.c_int, [])
 _lib_status_string = _sig("kvc_status_string", ctypes.c_char_p, [ctypes.c_int])
 _lib_phi_tables = _sig("kvc_phi_tables", ctypes.c_int, [_P, _P])
 _lib_encode_sizes = _sig("kvc_encode_sizes", ctypes.c_int, [ctypes.POINTER(kvc_params), ctypes.POINTER(_U64), ctypes.POINTER(_U64)])
-_lib_encode = _sig("kvc_encode", ctypes.c_int, [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _U64, ctypes.POINTER(_U64), _P, _U64, _P, _P])
+_lib_encode = _sig("kvc_encode", ctypes.c_int,
+                   [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _U64, ctypes.POINTER(_U64), _P, _P, _U64, _P, _P])
+_lib_encode_result = _sig("kvc_encode_result", ctypes.c_int, [_P, _P, ctypes.POINTER(_U64), _P])
 _lib_stream_info = _sig("kvc_stream_info", ctypes.c_int, [_P, _U64, ctypes.POINTER(kvc_params), ctypes.POINTER(_U64)])
-_lib_decode = _sig("kvc_decode", ctypes.c_int, [_P, _U64, _P, _P, _P, _P, _P, _U64, _P, _P])
+_DECODE_ARGS = [_P, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P]
+_lib_decode = _sig("kvc_decode", ctypes.c_int, _DECODE_ARGS + [_P])
+_lib_decode_async = _sig("kvc_decode_async", ctypes.c_int, _DECODE_ARGS)
+_lib_decode_result = _sig("kvc_decode_result", ctypes.c_int, [_P, _P, _P])
 _lib_decode_paged = _sig("kvc_decode_paged", ctypes.c_int,
-                         [_P, _U64, _P, _P, _P, ctypes.POINTER(kvc_paged_kv), _P, _U64, _P, _P])
+                         [_P, _P, _U64, _P, _U64, _P, _U64, _P, _U64, ctypes.POINTER(kvc_paged_kv), _P, _U64, _P, _P])
 _lib_calibrate = _sig("kvc_calibrate_sigma", ctypes.c_int,
                       [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _U64, _P])
 _lib_calibrate_blocks = _sig("kvc_calibrate_sigma_blocks", ctypes.c_int,
@@ -117,6 +124,21 @@ def _stream(stream=None) -> int:
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _host_header(header) -> np.ndarray:
+    """A host copy of a stream header (bytes, numpy or a device tensor holding
+    at least the header) as a contiguous 128-byte array."""
+    if isinstance(header, torch.Tensor):
+        header = header[:HEADER_BYTES].cpu().numpy()
+    h = np.frombuffer(bytes(header[:HEADER_BYTES]), dtype=np.uint8).copy()
+    if h.size != HEADER_BYTES:
+        raise KvcError(KVC_ERR_CORRUPT, "stream header")
+    return h
 
 
 def _kv_dtype(t: torch.Tensor) -> int:
@@ -185,16 +207,41 @@ class Encoder:
         self.capacity = max_stream if out_capacity is None else out_capacity
         self.out = torch.empty(self.capacity, dtype=torch.uint8, device=device)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        self.header = np.zeros(HEADER_BYTES, dtype=np.uint8)     # host copy of the last stream's header
+
+    def _check_inputs(self, kv, mu, sigma):
+        p = self.p
+        n = p.planes * p.tokens * p.channels
+        if kv.numel() != n or mu.numel() != n or _kv_dtype(kv) != p.kv_dtype or _mu_dtype(mu) != p.mu_dtype:
+            raise ValueError("kv / mu do not match the encoder's parameters")
+        if sigma.numel() != math.prod(sigma_shape(p.planes, p.tokens, p.channels, p.sigma_block_tokens)):
+            raise ValueError("sigma does not match the encoder's parameters")
 
     def __call__(self, kv, mu, sigma, prefix=None, stream=None, info: dict | None = None) -> torch.Tensor:
+        self._check_inputs(kv, mu, sigma)
         n = _U64(0)
         inf = kvc_encode_info() if info is not None else None
         st = _lib_encode(ctypes.byref(self.p), _ptr(kv), _ptr(mu), _ptr(sigma), _ptr(prefix),
-                         _ptr(self.out), self.capacity, ctypes.byref(n), _ptr(self.workspace),
-                         self.workspace.numel(), _stream(stream), ctypes.byref(inf) if inf is not None else None)
+                         _ptr(self.out), self.capacity, ctypes.byref(n), self.header.ctypes.data,
+                         _ptr(self.workspace), self.workspace.numel(), _stream(stream),
+                         ctypes.byref(inf) if inf is not None else None)
         _check(st, "kvc_encode")
         if inf is not None:
             info["stage_ms"] = list(inf.stage_ms)
+        return self.out[: n.value]
+
+    def enqueue(self, kv, mu, sigma, prefix=None, stream=None):
+        """Queue an encode without waiting for it; result() gives the stream."""
+        self._check_inputs(kv, mu, sigma)
+        st = _lib_encode(ctypes.byref(self.p), _ptr(kv), _ptr(mu), _ptr(sigma), _ptr(prefix),
+                         _ptr(self.out), self.capacity, None, None, _ptr(self.workspace), self.workspace.numel(),
+                         _stream(stream), None)
+        _check(st, "kvc_encode")
+
+    def result(self, stream=None) -> torch.Tensor:
+        n = _U64(0)
+        _check(_lib_encode_result(_ptr(self.workspace), _stream(stream), ctypes.byref(n), self.header.ctypes.data),
+               "kvc_encode_result")
         return self.out[: n.value]
 
 
@@ -224,39 +271,65 @@ def kvc_stream_info(header: bytes | np.ndarray):
     return p, total.value
 
 
+def _decode_args(header, stream_bytes, mu, sigma, prefix, kv_out, workspace, stream):
+    h = _host_header(stream_bytes if header is None else header)
+    args = [h.ctypes.data, _ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _nbytes(mu), _ptr(sigma),
+            _nbytes(sigma), _ptr(prefix), _nbytes(prefix), _ptr(kv_out), _nbytes(kv_out), _ptr(workspace),
+            _nbytes(workspace), _stream(stream)]
+    return h, args
+
+
 def kvc_decode(stream_bytes: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor,
                prefix: torch.Tensor | None = None, kv_out: torch.Tensor | None = None,
-               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+               workspace: torch.Tensor | None = None, stream=None, header=None) -> torch.Tensor:
     """Decode a KVC-1 stream (uint8 device tensor) back to KV bit patterns
-    (int16 for bf16, uint8 for e4m3), shape [G, T, D]."""
+    (int16 for bf16, uint8 for e4m3), shape [G, T, D].  header: a host copy
+    of the stream's first 128 bytes; read from the device stream if None."""
     _need(stream_bytes, "stream")
     for t, nm in ((mu, "mu"), (sigma, "sigma")):
         _need(t, nm)
     if stream_bytes.numel() < HEADER_BYTES:
         raise KvcError(KVC_ERR_CORRUPT, "kvc_decode")
-    p, _ = kvc_stream_info(stream_bytes[:HEADER_BYTES].cpu().numpy().tobytes())
+    h = _host_header(stream_bytes if header is None else header)
+    p, _ = kvc_stream_info(h)
     shape = (p.planes, p.tokens, p.channels)
     if kv_out is None:
         kv_out = torch.empty(shape, dtype=torch.int16 if p.kv_dtype == KVC_BF16 else torch.uint8,
                              device=stream_bytes.device)
     if workspace is None:
         workspace = torch.empty(DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=stream_bytes.device)
-    st = _lib_decode(_ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _ptr(sigma), _ptr(prefix),
-                     _ptr(kv_out), _ptr(workspace), workspace.numel(), _stream(stream), None)
-    _check(st, "kvc_decode")
+    _, args = _decode_args(h, stream_bytes, mu, sigma, prefix, kv_out, workspace, stream)
+    _check(_lib_decode(*args, None), "kvc_decode")
     return kv_out
 
 
 def kvc_decode_into(stream_bytes, mu, sigma, prefix, kv_out, workspace, stream=None,
-                    info: dict | None = None) -> int:
-    """Decode without reading the header on the Python side; returns the
-    status instead of raising (for timing loops and error-path tests)."""
+                    info: dict | None = None, header=None) -> int:
+    """Decode into kv_out and return the status instead of raising (for
+    timing loops and error-path tests).  header: a host copy of the stream's
+    header (bytes or numpy); read from the device stream if None."""
     inf = kvc_decode_info() if info is not None else None
-    st = _lib_decode(_ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _ptr(sigma), _ptr(prefix),
-                     _ptr(kv_out), _ptr(workspace), workspace.numel(), _stream(stream),
-                     ctypes.byref(inf) if inf is not None else None)
+    try:
+        _, args = _decode_args(header, stream_bytes, mu, sigma, prefix, kv_out, workspace, stream)
+    except KvcError as e:                 # fewer bytes than a header
+        return e.status
+    st = _lib_decode(*args, ctypes.byref(inf) if inf is not None else None)
     if inf is not None:
         info["stage_ms"] = list(inf.stage_ms)
+        info["fallback_symbols"] = inf.fallback_symbols
+    return st
+
+
+def kvc_decode_async(stream_bytes, mu, sigma, prefix, kv_out, workspace, header, stream=None) -> int:
+    """Queue a decode (host checks only); kvc_decode_result gives its status."""
+    _, args = _decode_args(header, stream_bytes, mu, sigma, prefix, kv_out, workspace, stream)
+    return _lib_decode_async(*args)
+
+
+def kvc_decode_result(workspace, stream=None, info: dict | None = None) -> int:
+    inf = kvc_decode_info()
+    st = _lib_decode_result(_ptr(workspace), _stream(stream), ctypes.byref(inf))
+    if info is not None:
         info["fallback_symbols"] = inf.fallback_symbols
     return st
 
@@ -269,27 +342,42 @@ class PagedKV:
 
     def __init__(self, pools, block_table: torch.Tensor, page_tokens: int):
         pools = list(pools)
+        if not pools:
+            raise ValueError("no pools")
         for t in pools:
             _need(t, "pool")
         _need(block_table, "block_table")
         if block_table.dtype != torch.int32 or block_table.dim() != 2:
             raise ValueError("block_table must be int32 [batch, max_pages]")
+        if pools[0].dim() != 4:
+            raise ValueError("pools must be [num_pages, page_tokens, heads, channels]")
         n_pages, pt, heads, _ = pools[0].shape
-        if pt != page_tokens or any(tuple(t.shape) != tuple(pools[0].shape) for t in pools):
-            raise ValueError("pools must all be [num_pages, page_tokens, heads, channels]")
+        if pt != page_tokens or any(tuple(t.shape) != tuple(pools[0].shape) or t.dtype != pools[0].dtype
+                                    for t in pools):
+            raise ValueError("pools must all be [num_pages, page_tokens, heads, channels] of one dtype")
         self.pools = pools
         self.block_table = block_table
         self.ptrs = torch.tensor([t.data_ptr() for t in pools], dtype=torch.int64, device=block_table.device)
-        self.desc = kvc_paged_kv(self.ptrs.data_ptr(), block_table.data_ptr(), block_table.shape[0], heads,
-                                 block_table.shape[1], n_pages, page_tokens, 0)
+        self.channels = pools[0].shape[3]
+        self.dtype = pools[0].dtype
+        self.desc = kvc_paged_kv(self.ptrs.data_ptr(), block_table.data_ptr(), len(pools), _nbytes(pools[0]),
+                                 block_table.shape[0], heads, block_table.shape[1], n_pages, page_tokens, 0)
 
 
 def kvc_decode_paged(stream_bytes, mu, sigma, prefix, paged: PagedKV, workspace, stream=None,
-                     info: dict | None = None) -> int:
-    """Decode straight into a paged KV cache; returns the status."""
+                     info: dict | None = None, header=None) -> int:
+    """Decode straight into a paged KV cache; returns the status.  The pools'
+    channels and element type must be the stream's (checked here against
+    the header; the library checks the pool count and sizes)."""
+    h = _host_header(stream_bytes if header is None else header)
+    p, _ = kvc_stream_info(h)
+    esize = 2 if p.kv_dtype == KVC_BF16 else 1
+    if paged.channels != p.channels or torch.empty(0, dtype=paged.dtype).element_size() != esize:
+        return KVC_ERR_INVALID
     inf = kvc_decode_info() if info is not None else None
-    st = _lib_decode_paged(_ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _ptr(sigma), _ptr(prefix),
-                           ctypes.byref(paged.desc), _ptr(workspace), workspace.numel(), _stream(stream),
+    st = _lib_decode_paged(h.ctypes.data, _ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _nbytes(mu),
+                           _ptr(sigma), _nbytes(sigma), _ptr(prefix), _nbytes(prefix), ctypes.byref(paged.desc),
+                           _ptr(workspace), _nbytes(workspace), _stream(stream),
                            ctypes.byref(inf) if inf is not None else None)
     if inf is not None:
         info["stage_ms"] = list(inf.stage_ms)

@@ -24,7 +24,10 @@
  *     never frees caller memory; scratch comes from a caller workspace.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     All work is queued on it; calls that return a host value synchronise
- *     that stream once before returning.
+ *     that stream once before returning; the *_async calls queue the work
+ *     and return at once, their outcome read later by the *_result call
+ *     (one synchronisation), so that many calls can be queued, on one stream
+ *     or several, with no host round trip between them.
  *   - Layouts are row-major: KV and mu are [planes][tokens][channels] with
  *     channels fastest; sigma is [planes][channels] float32; the marginal
  *     prefix is uint32[N + 1] (N = 65536 for bf16, 256 for e4m3).
@@ -107,8 +110,9 @@ typedef struct kvc_params {
     int64_t channels;        /* D, a positive multiple of 64                       */
 } kvc_params;
 
-/* Stream format version written and accepted: 3 (Gaussian and floor-and-escape
-   slots in separate ranges of the coder; the CDF argument q = floor(z * 2^24)). */
+/* Stream format version written and accepted: 4 (Gaussian and floor-and-escape
+   slots in separate ranges of the coder; the CDF argument q = floor(z * 2^24);
+   the header's bytes [92, 96) hold the CRC-32 of its bytes [0, 92)). */
 int kvc_version(void);
 
 /* Human-readable name of a status code (static string). */
@@ -133,20 +137,36 @@ int kvc_encode_sizes(const kvc_params* p, uint64_t* h_max_stream_bytes,
 
 /*
  * Encoder ([wiki] "pipeline": KV_full and (mu, sigma) go into the arithmetic
- * coder, which emits the bits).  Codes d_kv (bf16 or e4m3 bit patterns) under
- * the mixture around d_mu with d_sigma and the marginal prefix d_prefix
- * (NULL allowed when w_narrow_bp + w_wide_bp == 10000).  Writes the stream
- * to d_out and its length to *h_out_bytes.  Every sigma must lie in
- * [2^-96, 2^96], else KVC_ERR_INVALID.  If the stream
- * does not fit out_capacity the call returns KVC_ERR_CAPACITY and sets
- * *h_out_bytes to the size it needed.  Synchronises `stream` once.
+ * coder, which emits the bits).  Codes d_kv (bf16 or e4m3 bit patterns,
+ * p->planes x p->tokens x p->channels of them) under the mixture around d_mu
+ * with d_sigma and the marginal prefix d_prefix (NULL allowed when
+ * w_narrow_bp + w_wide_bp == 10000); the buffers must hold what *p
+ * describes.  Writes the stream to d_out, its length to *h_out_bytes and,
+ * when h_header_out is not NULL, a host copy of its 128-byte header (what
+ * kvc_decode takes) to h_header_out.  Every sigma must lie in [2^-96, 2^96],
+ * else KVC_ERR_INVALID.  If the stream does not fit out_capacity the call
+ * returns KVC_ERR_CAPACITY and sets *h_out_bytes to the size it needed.
+ * Synchronises `stream` once.
+ * h_out_bytes == NULL makes the call asynchronous: it queues the work and
+ * returns KVC_OK (h_header_out and h_info must then be NULL);
+ * kvc_encode_result on the same workspace gives the outcome later.
  * h_info: NULL, or receives the GPU time of each stage, measured with HIP
  * events on `stream`.
  */
 int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu,
                const float* d_sigma, const uint32_t* d_prefix, void* d_out,
-               uint64_t out_capacity, uint64_t* h_out_bytes, void* d_workspace,
-               uint64_t workspace_bytes, void* stream, kvc_encode_info* h_info);
+               uint64_t out_capacity, uint64_t* h_out_bytes, void* h_header_out,
+               void* d_workspace, uint64_t workspace_bytes, void* stream,
+               kvc_encode_info* h_info);
+
+/*
+ * Outcome of the last encode queued with this workspace: synchronises
+ * `stream` once, then returns the status kvc_encode would have returned and
+ * fills *h_out_bytes (and, if not NULL, the 128-byte h_header_out) as it
+ * would have.
+ */
+int kvc_encode_result(const void* d_workspace, void* stream, uint64_t* h_out_bytes,
+                      void* h_header_out);
 
 /*
  * Parse the 128-byte stream header held in HOST memory into *h_params and
@@ -158,21 +178,50 @@ int kvc_stream_info(const void* h_header, uint64_t header_bytes, kvc_params* h_p
 
 /*
  * Decoder ([wiki] "pipeline": the bitstream plus (mu, sigma) give back
- * KV_full exactly).  d_in holds in_bytes of a KVC-1 stream; shape and
- * parameters come from its header.  d_mu, d_sigma, d_prefix must be the
- * encoder's (checked through the stream's checksum: KVC_ERR_MISMATCH).
- * Writes KV bit patterns to d_kv_out ([planes][tokens][channels]).  Returns
- * KVC_ERR_CORRUPT if the stream is malformed, truncated or damaged (every
- * lane must start from a state in [2^47, 2^63), end in the initial state
- * and consume exactly its chunk).
- * Workspace: KVC_DECODE_WORKSPACE_BYTES, 256-byte aligned.  Synchronises `stream` twice
- * (header read, status read).  h_info: NULL, or receives the stage times
- * and the number of symbols the aim did not find.
+ * KV_full exactly).  h_header is a HOST copy of the stream's first 128
+ * bytes (kvc_encode's h_header_out, or the head of a host-resident stream);
+ * shape and parameters come from it, and the call checks, before anything
+ * runs, that the header is a valid KVC-1 header (CRC included:
+ * KVC_ERR_CORRUPT), that in_bytes is the length it gives (KVC_ERR_CORRUPT),
+ * and that the caller's buffers hold what it describes (KVC_ERR_INVALID):
+ * mu_bytes >= scalars x mu element size, sigma_bytes >= 4 x sigma words,
+ * prefix_bytes >= 4 x (N + 1) when the mixture has an escape part,
+ * kv_out_bytes >= scalars x KV element size.  On the device the stream's
+ * own header must equal h_header (KVC_ERR_CORRUPT, nothing decoded).
+ * d_in holds in_bytes of a KVC-1 stream; d_mu, d_sigma, d_prefix must be
+ * the encoder's (checked through the stream's checksum: KVC_ERR_MISMATCH,
+ * nothing decoded).  Writes KV bit patterns to d_kv_out
+ * ([planes][tokens][channels]).  Returns KVC_ERR_CORRUPT if the stream is
+ * malformed, truncated or damaged (every lane must start from a state in
+ * [2^47, 2^63), end in the initial state and consume exactly its chunk).
+ * Workspace: KVC_DECODE_WORKSPACE_BYTES, 256-byte aligned.  Synchronises
+ * `stream` once (the status read).  h_info: NULL, or receives the stage
+ * times and the number of symbols the aim did not find.
  */
-int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu,
-               const float* d_sigma, const uint32_t* d_prefix, void* d_kv_out,
-               void* d_workspace, uint64_t workspace_bytes, void* stream,
-               kvc_decode_info* h_info);
+int kvc_decode(const void* h_header, const void* d_in, uint64_t in_bytes,
+               const void* d_mu, uint64_t mu_bytes, const float* d_sigma,
+               uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
+               void* d_kv_out, uint64_t kv_out_bytes, void* d_workspace,
+               uint64_t workspace_bytes, void* stream, kvc_decode_info* h_info);
+
+/*
+ * kvc_decode without its synchronisation: the host-side checks run and
+ * return their status at once; the work is queued on `stream` and its
+ * outcome is read later by kvc_decode_result on the same workspace (which
+ * must not be reused before that).
+ */
+int kvc_decode_async(const void* h_header, const void* d_in, uint64_t in_bytes,
+                     const void* d_mu, uint64_t mu_bytes, const float* d_sigma,
+                     uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
+                     void* d_kv_out, uint64_t kv_out_bytes, void* d_workspace,
+                     uint64_t workspace_bytes, void* stream);
+
+/*
+ * Outcome of the last decode queued with this workspace: synchronises
+ * `stream` once and returns the status kvc_decode would have returned;
+ * h_info (may be NULL) receives the fallback count (stage times are -1).
+ */
+int kvc_decode_result(const void* d_workspace, void* stream, kvc_decode_info* h_info);
 
 /*
  * Paged output for kvc_decode_paged: the serving engine's KV cache as page
@@ -183,15 +232,18 @@ int kvc_decode(const void* d_in, uint64_t in_bytes, const void* d_mu,
  * block_table[b * max_pages + t / page_tokens], row t % page_tokens.
  */
 typedef struct kvc_paged_kv {
-    void* const* d_pools;          /* device array of layers * 2 pool base pointers  */
+    void* const* d_pools;          /* device array of n_pools pool base pointers      */
     const int32_t* d_block_table;  /* device [batch][max_pages] physical page numbers */
+    int64_t n_pools;               /* entries of d_pools: layers * 2                  */
+    uint64_t pool_bytes;           /* bytes of every pool, >= num_pages x page_tokens
+                                      x heads x channels x KV element size           */
     int64_t batch;                 /* sequences                                       */
     int64_t heads;                 /* KV heads per pool row                           */
     int64_t max_pages;             /* row stride of the table, >= ceil(tokens /
                                       page_tokens)                                    */
     int64_t num_pages;             /* pages in every pool, < 2^31                    */
     uint32_t page_tokens;          /* tokens per page                                 */
-    uint32_t reserved;             /* must be 0                                       */
+    uint32_t reserved;             /* 0                                               */
 } kvc_paged_kv;
 
 /*
@@ -203,15 +255,17 @@ typedef struct kvc_paged_kv {
  * (host struct; its pointers are device pointers) instead of a contiguous
  * [planes][tokens][channels] array: no second pass over the KV.  Rows of
  * pages the table does not name are left untouched.  KVC_ERR_INVALID if the
- * planes are not a multiple of 2 * batch * heads, the table is too narrow,
- * a page holds 2^32 bytes or more, or (checked on the device before the
- * decode) an entry of the columns the tokens use lies outside
- * [0, num_pages): then nothing is written.
+ * planes are not n_pools x batch x heads with n_pools even, the table is
+ * too narrow, a page holds 2^32 bytes or more, pool_bytes is short of
+ * num_pages pages, or (checked on the device before the decode) an entry of
+ * the columns the tokens use lies outside [0, num_pages): then nothing is
+ * written.  Header and buffer checks as kvc_decode.
  */
-int kvc_decode_paged(const void* d_in, uint64_t in_bytes, const void* d_mu,
-                     const float* d_sigma, const uint32_t* d_prefix, const kvc_paged_kv* h_paged,
-                     void* d_workspace, uint64_t workspace_bytes, void* stream,
-                     kvc_decode_info* h_info);
+int kvc_decode_paged(const void* h_header, const void* d_in, uint64_t in_bytes,
+                     const void* d_mu, uint64_t mu_bytes, const float* d_sigma,
+                     uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
+                     const kvc_paged_kv* h_paged, void* d_workspace, uint64_t workspace_bytes,
+                     void* stream, kvc_decode_info* h_info);
 
 /*
  * Sigma calibration ([wiki] "predictor choice": per-(kv, head, channel)

@@ -41,7 +41,7 @@ __all__ = [
     "gauss_cum", "escape_cum",
     "cdf_table", "build_marginal", "calibrate_sigma", "side_hash", "encode",
     "decode", "parse_header", "model_bits_int", "model_bits_float",
-    "chunk_layout", "sigma_blocks",
+    "chunk_layout", "sigma_blocks", "crc32", "HEADER_CRC_OFFSET",
 ]
 
 # ---------------------------------------------------------------------------
@@ -57,7 +57,7 @@ LANES = 64                         # interleaved rANS lanes per chunk
 HEADER_BYTES = 128
 STATE_BYTES = 8 * LANES            # 64 final states, u64 each
 MAGIC = b"KVC1"
-VERSION = 3
+VERSION = 4
 
 
 class StreamError(ValueError):
@@ -550,14 +550,34 @@ def chunk_layout(planes: int, tokens: int, channels: int, chunk_tokens: int):
 _HEADER_FMT = "<4sHHBBBBBBHIIIIIIQQQQQQI"
 
 
+HEADER_CRC_OFFSET = 92             # CRC-32 of header bytes [0, 92) at [92, 96)
+
+
+def crc32(data: bytes) -> int:
+    """CRC-32 as used by zlib, gzip and PNG (reflected polynomial
+    0xEDB88320, initial value and final xor 0xFFFFFFFF), bit by bit from its
+    definition."""
+    c = 0xFFFFFFFF
+    for byte in data:
+        c ^= byte
+        for _ in range(8):
+            c = (c >> 1) ^ (0xEDB88320 if c & 1 else 0)
+    return c ^ 0xFFFFFFFF
+
+
 def _header(kv_dtype, mu_dtype, w_n, w_w, chunk_tokens, planes, tokens, channels,
             n_chunks, payload_bytes, shash, sigma_block_tokens=0) -> bytes:
+    """S-10: the 128-byte header.  Bytes [0, 92) hold the fields, [92, 96)
+    the CRC-32 of those 92 bytes (a damaged header is reported as such
+    instead of steering the decoder with a wrong shape), the rest zero."""
     t_n, t_w, t_e = budgets(kv_dtype, w_n, w_w)
     h = struct.pack(
         _HEADER_FMT,
         MAGIC, VERSION, HEADER_BYTES, kv_dtype, mu_dtype, LOG2_M, LOG2_L,
         WORD_BITS, LANES, 0, w_n, w_w, t_n, t_w, t_e, chunk_tokens,
         planes, tokens, channels, n_chunks, payload_bytes, shash, sigma_block_tokens)
+    assert len(h) == HEADER_CRC_OFFSET
+    h += struct.pack("<I", crc32(h))
     return h + bytes(HEADER_BYTES - len(h))
 
 
@@ -572,8 +592,10 @@ def parse_header(stream: bytes) -> dict:
     h = dict(zip(keys, f))
     if h["magic"] != MAGIC or h["version"] != VERSION or h["header_bytes"] != HEADER_BYTES:
         raise StreamError("bad magic/version")
+    if struct.unpack_from("<I", stream, HEADER_CRC_OFFSET)[0] != crc32(stream[:HEADER_CRC_OFFSET]):
+        raise StreamError("header checksum")
     if (h["log2_m"], h["log2_l"], h["word_bits"], h["lanes"]) != (LOG2_M, LOG2_L, WORD_BITS, LANES) \
-            or h["reserved"] != 0 or any(stream[struct.calcsize(_HEADER_FMT):HEADER_BYTES]):
+            or h["reserved"] != 0 or any(stream[HEADER_CRC_OFFSET + 4:HEADER_BYTES]):
         raise StreamError("unsupported coder parameters")
     if h["kv_dtype"] not in (BF16, E4M3) or h["mu_dtype"] not in (BF16, F32):
         raise StreamError("bad dtype")

@@ -103,6 +103,18 @@ def test_paged_decode_rejects_bad_descriptors(kvc, cuda):
     odd.desc.heads = heads
     odd.desc.reserved = 1
     assert kvc.kvc_decode_paged(st, mu_d, sig_d, pref, odd, ws) == kvc.KVC_ERR_INVALID
+    odd.desc.reserved = 0
+    # fewer pools than the planes need, pools shorter than num_pages pages
+    odd.desc.n_pools = 1
+    assert kvc.kvc_decode_paged(st, mu_d, sig_d, pref, odd, ws) == kvc.KVC_ERR_INVALID
+    odd.desc.n_pools = 2
+    odd.desc.pool_bytes -= 2
+    assert kvc.kvc_decode_paged(st, mu_d, sig_d, pref, odd, ws) == kvc.KVC_ERR_INVALID
+    # pools whose rows are not the stream's channels or element type
+    wide = make_pools(kvc, 2, num_pages, pt, heads, 2 * d, torch.int16, cuda, 0)
+    assert kvc.kvc_decode_paged(st, mu_d, sig_d, pref, kvc.PagedKV(wide, table, pt), ws) == kvc.KVC_ERR_INVALID
+    bytes8 = make_pools(kvc, 2, num_pages, pt, heads, d, torch.uint8, cuda, 0)
+    assert kvc.kvc_decode_paged(st, mu_d, sig_d, pref, kvc.PagedKV(bytes8, table, pt), ws) == kvc.KVC_ERR_INVALID
 
 
 def test_paged_decode_full_size(kvc, cuda):

@@ -315,3 +315,76 @@ def test_error_statuses(kvc, cuda):
     # missing prefix for a mixture
     with pytest.raises(kvc.KvcError):
         kvc.kvc_encode(kv_d, mu_d, sig_d, None, (9500, 300), 16)
+
+
+def test_decode_checks_the_header_and_the_buffers(kvc, cuda):
+    """kvc_decode takes the header from the host: it must be valid (CRC),
+    its length must be the stream's, the device stream's header must equal
+    it, and every caller buffer must hold what it describes; otherwise
+    nothing runs (or nothing is decoded) and the status says why."""
+    kv, mu, sig, samples, mu_dtype = tiny(O.BF16)
+    pref = O.build_marginal(samples, O.BF16, 9500, 300)
+    kv_d, mu_d, sig_d, pref_d = dev_bits(kv, cuda), dev_bits(mu, cuda), torch.from_numpy(sig).to(cuda), dev_prefix(pref, cuda)
+    p = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, *kv.shape, (9500, 300), 16)
+    enc = kvc.Encoder(p, cuda)
+    st = enc(kv_d, mu_d, sig_d, pref_d).clone()
+    head = enc.header.copy()
+    assert head.tobytes() == host_bytes(st)[:128]
+    ws = torch.empty(kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=cuda)
+    out = torch.empty(kv.shape, dtype=torch.int16, device=cuda)
+
+    def dec(h=head, m=mu_d, s=sig_d, pr=pref_d, o=out, stream=st):
+        o.fill_(0)
+        return kvc.kvc_decode_into(stream, m, s, pr, o, ws, header=h)
+
+    assert dec() == kvc.KVC_OK and torch.equal(out, kv_d)
+    # header fields damaged on the host copy: refused by the CRC
+    for off in (9, 48, 88):
+        bad = head.copy()
+        bad[off] ^= 1
+        assert dec(h=bad) == kvc.KVC_ERR_CORRUPT
+    # a valid header (CRC recomputed) that is not the device stream's
+    import zlib
+    other = head.copy()
+    other[80] ^= 1                                        # the side-information checksum
+    other[92:96] = np.frombuffer(zlib.crc32(other[:92].tobytes()).to_bytes(4, "little"), np.uint8)
+    assert dec(h=other) == kvc.KVC_ERR_CORRUPT
+    assert int(out.abs().sum()) == 0                      # nothing decoded
+    # buffers shorter than the header describes
+    assert dec(m=mu_d.flatten()[:-1]) == kvc.KVC_ERR_INVALID
+    assert dec(s=sig_d.flatten()[:-1]) == kvc.KVC_ERR_INVALID
+    assert dec(pr=pref_d[:-1]) == kvc.KVC_ERR_INVALID
+    assert dec(o=out.flatten()[:-1]) == kvc.KVC_ERR_INVALID
+    # a stream one word longer than its header says
+    longer = torch.cat([st, torch.zeros(8, dtype=torch.uint8, device=cuda)])
+    assert dec(stream=longer) == kvc.KVC_ERR_CORRUPT
+
+
+def test_asynchronous_calls(kvc, cuda):
+    """Encodes and decodes queued without waiting, their outcomes read
+    afterwards, give what the synchronous calls give."""
+    kv, mu, sig, samples, mu_dtype = tiny(O.BF16)
+    pref = O.build_marginal(samples, O.BF16, 9500, 300)
+    kv_d, mu_d, sig_d, pref_d = dev_bits(kv, cuda), dev_bits(mu, cuda), torch.from_numpy(sig).to(cuda), dev_prefix(pref, cuda)
+    want = kvc.kvc_encode(kv_d, mu_d, sig_d, pref_d, (9500, 300), 16)
+    p = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, *kv.shape, (9500, 300), 16)
+    encs = [kvc.Encoder(p, cuda) for _ in range(2)]
+    s2 = torch.cuda.Stream()
+    encs[0].enqueue(kv_d, mu_d, sig_d, pref_d)
+    with torch.cuda.stream(s2):
+        encs[1].enqueue(kv_d, mu_d, sig_d, pref_d, stream=s2)
+    a = encs[0].result()
+    b = encs[1].result(stream=s2)
+    assert torch.equal(a, want) and torch.equal(b, want)
+    assert encs[1].header.tobytes() == host_bytes(want)[:128]
+    ws = [torch.empty(kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=cuda) for _ in range(2)]
+    outs = [torch.empty(kv.shape, dtype=torch.int16, device=cuda) for _ in range(2)]
+    for i in range(2):
+        assert kvc.kvc_decode_async(want, mu_d, sig_d, pref_d, outs[i], ws[i], encs[0].header) == kvc.KVC_OK
+    assert kvc.kvc_decode_result(ws[0]) == kvc.KVC_OK and kvc.kvc_decode_result(ws[1]) == kvc.KVC_OK
+    assert torch.equal(outs[0], kv_d) and torch.equal(outs[1], kv_d)
+    # a damaged stream queued asynchronously reports through the result call
+    bad = want.clone()
+    bad[-9] ^= 4
+    assert kvc.kvc_decode_async(bad, mu_d, sig_d, pref_d, outs[0], ws[0], encs[0].header) == kvc.KVC_OK
+    assert kvc.kvc_decode_result(ws[0]) == kvc.KVC_ERR_CORRUPT

@@ -90,8 +90,9 @@ def test_block_sigma_errors(kvc, cuda):
     s2 = sig_d.clone()
     s2[1, 2, 77] *= 2
     assert kvc.kvc_decode_into(st, mu_d, s2, pref_d, out, ws) == kvc.KVC_ERR_MISMATCH
-    # the per-plane sigma of the same planes is not the stream's side information
-    assert kvc.kvc_decode_into(st, mu_d, torch.from_numpy(sig).to(cuda), pref_d, out, ws) == kvc.KVC_ERR_MISMATCH
+    # the per-plane sigma of the same planes is smaller than the blocks the
+    # header describes: refused before anything runs
+    assert kvc.kvc_decode_into(st, mu_d, torch.from_numpy(sig).to(cuda), pref_d, out, ws) == kvc.KVC_ERR_INVALID
 
 
 @pytest.mark.parametrize("reps,planes,tokens,channels,blk", [

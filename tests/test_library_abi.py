@@ -39,7 +39,7 @@ def test_binding_constants_match_header(kvc):
 
 
 def test_version_and_status_strings(kvc):
-    assert kvc.kvc_version() == O.VERSION == 3
+    assert kvc.kvc_version() == O.VERSION == 4
     assert kvc.kvc_status_string(0) == "ok"
     assert "corrupt" in kvc.kvc_status_string(-3)
 
@@ -146,3 +146,26 @@ def test_stream_info_rejects_damaged_headers(kvc, offset):
     with pytest.raises(kvc.KvcError) as e:
         kvc.kvc_stream_info(bytes(st))
     assert e.value.status == kvc.KVC_ERR_CORRUPT
+
+
+@pytest.mark.parametrize("offset,bit", [(9, 1), (9, 2), (48, 0), (48, 1), (64, 0), (72, 3), (80, 5), (88, 0), (88, 4)])
+def test_stream_info_rejects_single_bit_flips_that_keep_the_fields_valid(kvc, offset, bit):
+    """Flips that leave every field plausible on its own (mu dtype bf16 ->
+    f32, a token count with the same chunk count, the payload size, the side
+    checksum, the sigma block length) are caught by the header CRC."""
+    st = bytearray(oracle_stream()[:128])
+    st[offset] ^= 1 << bit
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_stream_info(bytes(st))
+    assert e.value.status == kvc.KVC_ERR_CORRUPT
+
+
+def test_stream_info_accepts_a_recomputed_crc(kvc):
+    """The library's CRC is zlib's: a field changed together with a
+    recomputed CRC parses (so the check is the CRC, not a byte compare)."""
+    import zlib
+    st = bytearray(oracle_stream()[:128])
+    st[80] ^= 0xFF                                          # the side checksum: any value is valid
+    st[92:96] = zlib.crc32(bytes(st[:92])).to_bytes(4, "little")
+    p, total = kvc.kvc_stream_info(bytes(st))
+    assert total == len(oracle_stream())

@@ -222,3 +222,31 @@ def test_batching_does_not_change_the_result(sigma_block):
         assert O.encode(kv, mu, sig, pref, O.BF16, mu_dtype, 9500, 300, 7, batch_chunks=bc,
                         sigma_block_tokens=sigma_block) == one
         assert np.array_equal(O.decode(one, mu, sig, pref, batch_chunks=bc), kv)
+
+
+def test_header_crc_is_zlib_crc32():
+    """The header checksum is CRC-32 as zlib computes it (an independent
+    implementation), over the header's first 92 bytes."""
+    import zlib
+    rng = np.random.default_rng(9)
+    for n in (0, 1, 7, 92, 300):
+        data = rng.integers(0, 256, n, dtype=np.uint8).tobytes()
+        assert O.crc32(data) == zlib.crc32(data)
+    assert O.crc32(b"123456789") == 0xCBF43926          # the standard check value
+    kv, mu, sig, samples, mu_dtype = case()
+    pref = O.build_marginal(samples, O.BF16, 9500, 300)
+    st = O.encode(kv, mu, sig, pref, O.BF16, mu_dtype, 9500, 300, 16)
+    assert int.from_bytes(st[92:96], "little") == zlib.crc32(st[:92])
+    assert not any(st[96:128])
+
+
+@pytest.mark.parametrize("offset", [9, 40, 48, 56, 72, 80, 88, 92])
+def test_damaged_header_fields_are_rejected(offset):
+    """A flipped bit in any field (a dtype, the shape, the payload size, the
+    side hash, the sigma block length) or in the checksum itself."""
+    kv, mu, sig, samples, mu_dtype = case()
+    pref = O.build_marginal(samples, O.BF16, 9500, 300)
+    st = bytearray(O.encode(kv, mu, sig, pref, O.BF16, mu_dtype, 9500, 300, 16))
+    st[offset] ^= 0x02
+    with pytest.raises(O.StreamError):
+        O.parse_header(bytes(st))
