@@ -612,6 +612,24 @@ int kvc_decode(const void* h_header, const void* d_in, uint64_t in_bytes, const 
     return kvc_decode_result(d_workspace, stream, h_info);
 }
 
+int kvc_decode_noalloc(const void* h_header, const void* d_in, uint64_t in_bytes, const void* d_mu,
+                       uint64_t mu_bytes, const float* d_sigma, uint64_t sigma_bytes, const uint32_t* d_prefix,
+                       uint64_t prefix_bytes, void* d_kv_out, uint64_t kv_out_bytes, void* stream) {
+    static_assert(kvc::kNoAllocScratchBytes >= KVC_DECODE_WORKSPACE_BYTES, "scratch holds a decode workspace");
+    if (!d_kv_out) return KVC_ERR_INVALID;
+    hipError_t e = hipSuccess;
+    void* ws = kvc::noalloc_scratch(&e);
+    if (e != hipSuccess || !ws) return KVC_ERR_DEVICE;
+    // the decoder's workspace does not grow with the stream; a layout that
+    // needed more than the scratch holds would be refused here
+    if (KVC_DECODE_WORKSPACE_BYTES > kvc::kNoAllocScratchBytes) return KVC_ERR_CAPACITY;
+    const int st = decode_launch(h_header, d_in, in_bytes, d_mu, mu_bytes, d_sigma, sigma_bytes, d_prefix,
+                                 prefix_bytes, d_kv_out, kv_out_bytes, nullptr, ws, kvc::kNoAllocScratchBytes, stream,
+                                 nullptr);
+    if (st != KVC_OK) return st;
+    return kvc_decode_result(ws, stream, nullptr);
+}
+
 int kvc_decode_paged(const void* h_header, const void* d_in, uint64_t in_bytes, const void* d_mu, uint64_t mu_bytes,
                      const float* d_sigma, uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
                      const kvc_paged_kv* h_paged, void* d_workspace, uint64_t workspace_bytes, void* stream,

@@ -137,6 +137,12 @@ struct EstimateArgs {
     Control* ctl;
 };
 
+// The allocation-free decode's scratch: a fixed device array of
+// kNoAllocScratchBytes per device; its device address (taken once per
+// device), or null with *err set.
+constexpr uint64_t kNoAllocScratchBytes = 917504;
+void* noalloc_scratch(hipError_t* err);
+
 // Phi base tables: computed once on the host, copied to each device.
 constexpr int kPhiPoints = 12289;
 PhiTables device_phi_tables(hipError_t* err);

@@ -79,6 +79,37 @@ PhiTables device_phi_tables(hipError_t* err) {
 }
 
 // ---------------------------------------------------------------------------
+// Scratch of the allocation-free decode: a fixed array in device memory
+// (each device holds its own copy while the process lives).  Host code
+// takes its device address once per device with hipGetSymbolAddress; the
+// array's name is not a device address on the host.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_dev[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+void* noalloc_scratch(hipError_t* err) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = (e != hipSuccess) ? e : hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* p = nullptr;
+        const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_err[dev] = r;
+        g_scratch_dev[dev] = (r == hipSuccess) ? p : nullptr;
+    });
+    *err = g_scratch_err[dev];
+    return g_scratch_dev[dev];
+}
+
+// ---------------------------------------------------------------------------
 // helpers
 // ---------------------------------------------------------------------------
 // H[k] = floor(T_n A[k] / 2^31) + floor(T_w B[k] / 2^31), H[12289] = H[12288].

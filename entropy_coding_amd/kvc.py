@@ -22,13 +22,15 @@ KVC_OK, KVC_ERR_INVALID, KVC_ERR_CAPACITY, KVC_ERR_CORRUPT, KVC_ERR_MISMATCH, KV
 KVC_BF16, KVC_E4M3, KVC_F32 = 0, 1, 2
 HEADER_BYTES = 128
 DECODE_WORKSPACE_BYTES = 917504
+NOALLOC_SCRATCH_BYTES = 917504
 ESTIMATE_WORKSPACE_BYTES = 256
 ENCODE_STAGES = 4     # side-information checksum, coding kernel, size scan, compaction
 DECODE_STAGES = 2     # side-information checksum + escape bucket table, decoding kernel
 
 EXPORTS = [
     "kvc_version", "kvc_status_string", "kvc_phi_tables", "kvc_encode_sizes", "kvc_encode", "kvc_encode_result",
-    "kvc_stream_info", "kvc_decode", "kvc_decode_async", "kvc_decode_result", "kvc_decode_paged",
+    "kvc_stream_info", "kvc_decode", "kvc_decode_async", "kvc_decode_result", "kvc_decode_noalloc",
+    "kvc_decode_paged",
     "kvc_calibrate_sigma", "kvc_calibrate_sigma_blocks", "kvc_calibrate_sigma_rate",
     "kvc_build_marginal", "kvc_estimate_bits", "kvc_cdf_table",
 ]
@@ -91,6 +93,7 @@ _DECODE_ARGS = [_P, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P, _U64, 
 _lib_decode = _sig("kvc_decode", ctypes.c_int, _DECODE_ARGS + [_P])
 _lib_decode_async = _sig("kvc_decode_async", ctypes.c_int, _DECODE_ARGS)
 _lib_decode_result = _sig("kvc_decode_result", ctypes.c_int, [_P, _P, _P])
+_lib_decode_noalloc = _sig("kvc_decode_noalloc", ctypes.c_int, [_P, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P])
 _lib_decode_paged = _sig("kvc_decode_paged", ctypes.c_int,
                          [_P, _P, _U64, _P, _U64, _P, _U64, _P, _U64, ctypes.POINTER(kvc_paged_kv), _P, _U64, _P, _P])
 _lib_calibrate = _sig("kvc_calibrate_sigma", ctypes.c_int,
@@ -332,6 +335,19 @@ def kvc_decode_result(workspace, stream=None, info: dict | None = None) -> int:
     if info is not None:
         info["fallback_symbols"] = inf.fallback_symbols
     return st
+
+
+def kvc_decode_noalloc(stream_bytes, mu, sigma, prefix, kv_out, stream=None, header=None) -> int:
+    """Decode into kv_out with the library's fixed device scratch (no
+    workspace, nothing allocated); returns the status.  Calls on one device
+    share the scratch and must not overlap."""
+    try:
+        h = _host_header(stream_bytes if header is None else header)
+    except KvcError as e:
+        return e.status
+    return _lib_decode_noalloc(h.ctypes.data, _ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _nbytes(mu),
+                               _ptr(sigma), _nbytes(sigma), _ptr(prefix), _nbytes(prefix), _ptr(kv_out),
+                               _nbytes(kv_out), _stream(stream))
 
 
 class PagedKV:

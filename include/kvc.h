@@ -217,6 +217,26 @@ int kvc_decode_async(const void* h_header, const void* d_in, uint64_t in_bytes,
                      uint64_t workspace_bytes, void* stream);
 
 /*
+ * kvc_decode for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument and no allocation of any kind.  Its scratch is a
+ * fixed array of KVC_NOALLOC_SCRATCH_BYTES in device memory that the
+ * library holds on every device it runs on until the process ends; the
+ * decoder's scratch does not grow with the stream, so every stream
+ * kvc_decode accepts fits (a layout needing more would be refused with
+ * KVC_ERR_CAPACITY).  Arguments, checks, output and statuses as
+ * kvc_decode; synchronises `stream` once.  Every call on one device
+ * shares that device's scratch (cleared by the call where it must start at
+ * zero): calls that overlap on one device, from several threads or on
+ * several streams, race, and the caller must serialise them.
+ */
+#define KVC_NOALLOC_SCRATCH_BYTES 917504
+int kvc_decode_noalloc(const void* h_header, const void* d_in, uint64_t in_bytes,
+                       const void* d_mu, uint64_t mu_bytes, const float* d_sigma,
+                       uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
+                       void* d_kv_out, uint64_t kv_out_bytes, void* stream);
+
+/*
  * Outcome of the last decode queued with this workspace: synchronises
  * `stream` once and returns the status kvc_decode would have returned;
  * h_info (may be NULL) receives the fallback count (stage times are -1).

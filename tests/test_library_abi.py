@@ -35,6 +35,8 @@ def test_binding_constants_match_header(kvc):
     ws = int(re.search(r"#define KVC_DECODE_WORKSPACE_BYTES (\d+)", text).group(1))
     hb = int(re.search(r"#define KVC_HEADER_BYTES (\d+)", text).group(1))
     assert kvc.DECODE_WORKSPACE_BYTES == ws and ws % 256 == 0
+    na = int(re.search(r"#define KVC_NOALLOC_SCRATCH_BYTES (\d+)", text).group(1))
+    assert kvc.NOALLOC_SCRATCH_BYTES == na and na >= ws
     assert kvc.HEADER_BYTES == hb
 
 
