@@ -41,7 +41,7 @@ __all__ = [
     "gauss_cum", "escape_cum",
     "cdf_table", "build_marginal", "calibrate_sigma", "side_hash", "encode",
     "decode", "parse_header", "model_bits_int", "model_bits_float",
-    "chunk_layout", "sigma_blocks", "crc32", "HEADER_CRC_OFFSET",
+    "chunk_layout", "sigma_blocks", "crc32", "HEADER_CRC_OFFSET", "stream_header",
 ]
 
 # ---------------------------------------------------------------------------
@@ -565,7 +565,7 @@ def crc32(data: bytes) -> int:
     return c ^ 0xFFFFFFFF
 
 
-def _header(kv_dtype, mu_dtype, w_n, w_w, chunk_tokens, planes, tokens, channels,
+def stream_header(kv_dtype, mu_dtype, w_n, w_w, chunk_tokens, planes, tokens, channels,
             n_chunks, payload_bytes, shash, sigma_block_tokens=0) -> bytes:
     """S-10: the 128-byte header.  Bytes [0, 92) hold the fields, [92, 96)
     the CRC-32 of those 92 bytes (a damaged header is reported as such
@@ -703,7 +703,7 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
     sizes = np.array([len(p) for p in payloads], dtype=np.int64)
     directory = np.concatenate([[0], np.cumsum(sizes)]).astype("<u8")
     shash = side_hash(sigma, prefix if t_e else None)
-    head = _header(kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp, chunk_tokens,
+    head = stream_header(kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp, chunk_tokens,
                    g_n, t_len, d_n, n_chunks, int(directory[-1]), shash, sigma_block_tokens)
     return head + directory.tobytes() + b"".join(payloads)
 
@@ -883,7 +883,7 @@ def wrap_chunk(payload: bytes, sigma_sub, prefix, kv_dtype, mu_dtype, w_narrow_b
     chunk cut out of a large stream on its own."""
     t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)[2]
     shash = side_hash(np.asarray(sigma_sub, dtype=np.float32).reshape(1, LANES), prefix if t_e else None)
-    head = _header(kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp, chunk_tokens, 1, tokens, LANES, 1,
+    head = stream_header(kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp, chunk_tokens, 1, tokens, LANES, 1,
                    len(payload), shash)
     directory = np.array([0, len(payload)], dtype="<u8")
     return head + directory.tobytes() + payload

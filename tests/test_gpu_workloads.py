@@ -1,9 +1,10 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times.  The GPU round trip is checked on every scalar; the oracle
-codes and decodes a sample of chunks cut from the GPU's stream (each chunk
-depends only on its own slice of KV and mu, its 64 sigmas and p_hat), and
-the smaller workload is checked byte for byte in full."""
+benchmark times: every stream byte-identical to the oracle's (the oracle
+codes every chunk, a range of planes at a time, in worker processes on the
+host cores: a chunk depends only on its own rows of KV and mu, its 64 sigmas
+and p_hat), and the GPU round trip exact on every scalar."""
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -43,61 +44,126 @@ def build_inputs(kvc, w, dev, layers=None, reps=None, sigma_block=0):
     return kv, mu, sig, prefix
 
 
-def sampled_chunk_parity(kvc, w, kv, mu, sig, prefix, stream, n_sample=6, seed=0, tc=None, sigma_block=0):
-    g_n, t_n, d_n = kv.shape
-    tc = w.chunk_tokens if tc is None else tc
-    gof, tcof, kof, lnof = O.chunk_layout(g_n, t_n, d_n, tc)
-    n_chunks = gof.size
-    rng = np.random.default_rng(seed)
-    ids = sorted(set([0, n_chunks - 1] + rng.integers(0, n_chunks, n_sample - 2).tolist()))
-    pref = prefix.cpu().numpy().astype(np.int64)
-    head = stream[:128 + 8 * (n_chunks + 1)].cpu().numpy()
-    directory = head[128:].view("<u8")
-    pay_off = 128 + 8 * (n_chunks + 1)
-    w_ = (w.w_narrow_bp, w.w_wide_bp)
-    for cid in ids:
-        g, tci, k, ln = int(gof[cid]), int(tcof[cid]), int(kof[cid]), int(lnof[cid])
-        t0 = tci * tc
-        sl = (slice(g, g + 1), slice(t0, t0 + ln), slice(64 * k, 64 * k + 64))
-        kvs = W.to_numpy_bits(kv[sl].contiguous())
-        mus = W.to_numpy_bits(mu[sl].contiguous())
-        if sigma_block:
-            sgs = sig[g:g + 1, t0 // sigma_block, 64 * k:64 * k + 64].cpu().numpy()
-        else:
-            sgs = sig[g:g + 1, 64 * k:64 * k + 64].cpu().numpy()
-        gpu_payload = stream[pay_off + int(directory[cid]):pay_off + int(directory[cid + 1])].cpu().numpy().tobytes()
-        want = O.encode_chunks(kvs, mus, sgs, pref, w.kv_dtype, w.mu_dtype, *w_, tc, [0])[0]
-        assert gpu_payload == want, f"chunk {cid} (plane {g}, tokens {t0}+{ln}, group {k}) differs"
-        back = O.decode(O.wrap_chunk(gpu_payload, sgs, pref, w.kv_dtype, w.mu_dtype, *w_, tc, ln), mus, sgs, pref)
-        assert np.array_equal(back, kvs)
-    say(f"sampled chunks {ids} of {n_chunks} identical to the oracle")
+@pytest.fixture(scope="module")
+def pool():
+    """Oracle workers on the host cores (fresh interpreters, no GPU)."""
+    from oracle import pool as P
+    with P.Pool() as p:
+        say(f"oracle pool: {p.n} workers")
+        yield p
 
 
-@pytest.mark.parametrize("wid,layers", [(2, None), (3, None), (4, [0, 63])])
-def test_full_size_round_trip_and_sampled_parity(kvc, cuda, wid, layers):
+class StreamCheck:
+    """Byte-for-byte comparison of one GPU stream with the oracle's, spread
+    over the oracle pool: planes are coded by the oracle a range at a time
+    (a chunk depends only on its own rows, its sigmas and the prefix), each
+    range's payload bytes must equal the GPU's, each range's chunk sizes the
+    GPU directory's, and the GPU header must be the one the oracle writes."""
+
+    def __init__(self, pool, w, st, kv, mu, sig, pref, tc, planes_per_task, sigma_block=0):
+        self.host = st.cpu().numpy().tobytes()
+        h = O.parse_header(self.host)
+        g_n, t_n, d_n = kv.shape
+        self.n_chunks = h["n_chunks"]
+        self.cpp = self.n_chunks // g_n                              # chunks per plane
+        self.pay = O.HEADER_BYTES + 8 * (self.n_chunks + 1)
+        self.dir = np.frombuffer(self.host, "<u8", count=self.n_chunks + 1, offset=O.HEADER_BYTES).astype(np.int64)
+        assert self.dir[0] == 0 and self.pay + self.dir[-1] == len(self.host)
+        kvn, mun = W.to_numpy_bits(kv), W.to_numpy_bits(mu)
+        sgn = sig.cpu().numpy()
+        pref = pref.cpu().numpy().astype(np.int64)
+        wts = (w.w_narrow_bp, w.w_wide_bp)
+        want_head = O.stream_header(w.kv_dtype, w.mu_dtype, *wts, tc, g_n, t_n, d_n, self.n_chunks,
+                                    int(self.dir[-1]), O.side_hash(sgn, pref), sigma_block)
+        assert self.host[:O.HEADER_BYTES] == want_head, "stream header differs from the oracle's"
+        self.jobs = []
+        for g0 in range(0, g_n, planes_per_task):
+            g1 = min(g_n, g0 + planes_per_task)
+            c0, c1 = g0 * self.cpp, g1 * self.cpp
+            expect = self.host[self.pay + self.dir[c0]:self.pay + self.dir[c1]]
+            r = pool.submit(kvn[g0:g1], mun[g0:g1], sgn[g0:g1], pref, w.kv_dtype, w.mu_dtype, *wts, tc,
+                            expect, sigma_block_tokens=sigma_block)
+            self.jobs.append((c0, c1, r))
+
+    def finish(self, timeout=600):
+        for c0, c1, r in self.jobs:
+            ok, local_dir, bad = r.get(timeout=timeout)
+            assert ok, f"chunk {c0 + bad} differs from the oracle's"
+            assert np.array_equal(local_dir, self.dir[c0:c1 + 1] - self.dir[c0]), f"chunk sizes of {c0}..{c1}"
+        return self.n_chunks
+
+
+def gpu_round_trip(kvc, st, kv, mu, sig, prefix, header):
+    out = kvc.kvc_decode(st, mu, sig, prefix, header=header)
+    assert torch.equal(out.view(kv.dtype) if kv.dtype != torch.uint8 else out, kv)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wid,planes_per_task", [(2, 32), (3, 8)])
+def test_full_size_stream_is_the_oracles(kvc, cuda, pool, wid, planes_per_task):
+    """The whole cache in one call, sigma calibrated as the benchmark does
+    (128 x 1024 held-out tokens per layer): every chunk, the directory and
+    the header byte-identical to the oracle's; the GPU round trip exact on
+    every scalar."""
     w = W.WORKLOADS[wid]
-    say(f"workload {wid}: {w.name}, layers {layers or 'all'}")
-    kv, mu, sig, prefix = build_inputs(kvc, w, cuda, layers, reps=16)
+    say(f"workload {wid}: {w.name}")
+    t0 = time.perf_counter()
+    kv, mu, sig, prefix = build_inputs(kvc, w, cuda)
     torch.cuda.synchronize()
     g, t, d = kv.shape
     p = kvc.make_params(kvc._kv_dtype(kv), kvc._mu_dtype(mu), g, t, d, (w.w_narrow_bp, w.w_wide_bp), w.chunk_tokens)
     enc = kvc.Encoder(p, cuda)
     st = enc(kv, mu, sig, prefix)
+    head = enc.header.copy()
     say(f"encoded {kv.numel()} scalars -> {st.numel()} bytes ({8.0 * st.numel() / kv.numel():.4f} bits/scalar)")
-    out = kvc.kvc_decode(st, mu, sig, prefix)
-    assert torch.equal(out.view(kv.dtype) if kv.dtype != torch.uint8 else out, kv)
-    sampled_chunk_parity(kvc, w, kv, mu, sig, prefix, st)
+    gpu_round_trip(kvc, st, kv, mu, sig, prefix, head)
     # the encoder is deterministic: a second call gives the same bytes
-    st2 = enc(kv, mu, sig, prefix)
-    assert torch.equal(st2, st)
+    assert torch.equal(enc(kv, mu, sig, prefix), st)
+    chk = StreamCheck(pool, w, st, kv, mu, sig, prefix, w.chunk_tokens, planes_per_task)
+    del kv, mu
+    n = chk.finish()
+    say(f"all {n} chunks identical to the oracle ({time.perf_counter() - t0:.1f} s)")
 
 
-def test_position_aware_sigma_full_size(kvc, cuda):
+@pytest.mark.timeout(900)
+def test_per_layer_streams_of_the_32b_shaped_cache_are_the_oracles(kvc, cuda, pool):
+    """The Qwen3-32B-shaped cache coded as the benchmark streams it, one
+    call per layer over all 64 layers, sigma from 128 x 1024 held-out tokens
+    per layer: every layer's stream byte-identical to the oracle's, every
+    layer's GPU round trip exact."""
+    w = W.WORKLOADS[4]
+    t0 = time.perf_counter()
+    ppl = w.planes_per_layer
+    prefix = kvc.kvc_build_marginal(W.marginal_samples(w, device=cuda), (w.w_narrow_bp, w.w_wide_bp))
+    p = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, ppl, w.tokens, w.channels, (w.w_narrow_bp, w.w_wide_bp),
+                        w.chunk_tokens)
+    enc = kvc.Encoder(p, cuda)
+    checks, total = [], 0
+    for l in range(w.layers):
+        kv, mu = W.layer_data(w, l, device=cuda)
+        ck, cm = W.layer_calibration(w, l, reps=w.calib_reps, device=cuda)
+        sig = W.expand_sigma(w, kvc.kvc_calibrate_sigma(ck, cm))
+        del ck, cm
+        st = enc(kv, mu, sig, prefix).clone()
+        gpu_round_trip(kvc, st, kv, mu, sig, prefix, enc.header.copy())
+        checks.append(StreamCheck(pool, w, st, kv, mu, sig, prefix, w.chunk_tokens, 4))
+        # a bounded number of layers in flight on the host
+        while len(checks) > 3:
+            total += checks.pop(0).finish()
+        if l % 16 == 15:
+            say(f"layer {l + 1}/{w.layers} coded, {total} chunks checked ({time.perf_counter() - t0:.1f} s)")
+    for c in checks:
+        total += c.finish()
+    say(f"all {w.layers} layer streams ({total} chunks) identical to the oracle ({time.perf_counter() - t0:.1f} s)")
+
+
+@pytest.mark.timeout(900)
+def test_position_aware_sigma_full_size(kvc, cuda, pool):
     """The position-varying workload at full size with one sigma per 512
     tokens, calibrated per block on the device, in the configuration the
-    benchmark times (the library's default chunk length): round trip,
-    sampled chunks against the oracle, and fewer bits than one sigma per
-    plane."""
+    benchmark times (the library's default chunk length): the whole stream
+    byte-identical to the oracle's, the round trip exact, and fewer bits than
+    one sigma per plane."""
     w = W.WORKLOADS[5]
     blk = 512
     say(f"workload 5: {w.name}, sigma blocks of {blk} tokens")
@@ -107,12 +173,11 @@ def test_position_aware_sigma_full_size(kvc, cuda):
     wts = (w.w_narrow_bp, w.w_wide_bp)
     enc = kvc.Encoder(kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, g, t, d, wts, 0, blk), cuda)
     st = enc(kv, mu, sig, prefix)
-    p, _ = kvc.kvc_stream_info(st[:128].cpu().numpy())
+    p, _ = kvc.kvc_stream_info(enc.header)
     assert p.sigma_block_tokens == blk and blk % p.chunk_tokens == 0
     say(f"encoded {kv.numel()} scalars at {p.chunk_tokens}-token chunks -> {8.0 * st.numel() / kv.numel():.4f} bits/scalar")
-    out = kvc.kvc_decode(st, mu, sig, prefix)
-    assert torch.equal(out, kv.view(torch.int16))
-    sampled_chunk_parity(kvc, w, kv, mu, sig, prefix, st, tc=p.chunk_tokens, sigma_block=blk)
+    gpu_round_trip(kvc, st, kv, mu, sig, prefix, enc.header.copy())
+    chk = StreamCheck(pool, w, st, kv, mu, sig, prefix, p.chunk_tokens, 32, sigma_block=blk)
     # one sigma per plane over the same calibration draws costs more
     _, _, sig1, _ = build_inputs(kvc, w, cuda, layers=[0], reps=8)
     ppl = w.planes_per_layer
@@ -121,21 +186,21 @@ def test_position_aware_sigma_full_size(kvc, cuda):
                                     chunk_tokens=p.chunk_tokens)[0]
     say(f"layer 0 model bits: per plane {b_plane:.4f}, per {blk}-token block {b_block:.4f}")
     assert b_block < b_plane
+    del kv, mu
+    say(f"all {chk.finish()} chunks identical to the oracle")
 
 
-def test_qwen3_0p6b_shaped_full_parity(kvc, cuda):
+@pytest.mark.timeout(900)
+def test_qwen3_0p6b_shaped_full_parity(kvc, cuda, pool):
     """The 58.7M-scalar workload byte for byte against the oracle, sigma
     calibrated on the device from 8 x 1024 held-out tokens per layer."""
     w = W.WORKLOADS[1]
     kv, mu, sig, prefix = build_inputs(kvc, w, cuda)
-    st = kvc.kvc_encode(kv, mu, sig, prefix, (w.w_narrow_bp, w.w_wide_bp), w.chunk_tokens)
-    kvn, mun, sgn = W.to_numpy_bits(kv), W.to_numpy_bits(mu), sig.cpu().numpy()
-    pref = prefix.cpu().numpy().astype(np.int64)
-    say("oracle encoding 58.7M scalars ...")
-    want = O.encode(kvn, mun, sgn, pref, O.BF16, O.BF16, w.w_narrow_bp, w.w_wide_bp, w.chunk_tokens)
-    assert st.cpu().numpy().tobytes() == want
-    out = kvc.kvc_decode(st, mu, sig, prefix)
-    assert torch.equal(out, kv.view(torch.int16))
+    p = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, *kv.shape, (w.w_narrow_bp, w.w_wide_bp), w.chunk_tokens)
+    enc = kvc.Encoder(p, cuda)
+    st = enc(kv, mu, sig, prefix)
+    gpu_round_trip(kvc, st, kv, mu, sig, prefix, enc.header.copy())
+    say(f"all {StreamCheck(pool, w, st, kv, mu, sig, prefix, w.chunk_tokens, 16).finish()} chunks identical to the oracle")
 
 
 @pytest.mark.parametrize("wts", [(9500, 300), (10000, 0)])
