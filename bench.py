@@ -323,7 +323,7 @@ def main():
         log(f"[bench] paged output: {len(pools)} pools of {num_pages} x {pt}-token pages, shuffled table")
 
     def step(stats=None):
-        e_ms, d_ms = [0.0] * 4, [0.0] * 2
+        e_ms, d_ms = [0.0] * kvc.ENCODE_STAGES, [0.0] * kvc.DECODE_STAGES
         fb, nbytes = 0, 0
         for sl in parts:
             ei, di = {}, {}
@@ -441,7 +441,7 @@ def main():
         "decode_gbps": raw / (dec_total * 1e-3) / 1e9,
         "encode_ms": enc_total, "decode_ms": dec_total,
         "encode_stage_ms": {k: mean([s[0][i] for s in stats]) for i, k in
-                            enumerate(["side_hash", "encode_kernel", "scan", "compact"])},
+                            enumerate(["side_hash_and_tables", "encode_kernel"])},
         "decode_stage_ms": {k: mean([s[1][i] for s in stats]) for i, k in enumerate(["side_hash", "decode_kernel"])},
         "bits_per_scalar": {"coded": 8.0 * stream_bytes / n, "integer_model": bits_int, "float_model": bits_float},
         "stream_bytes": stream_bytes,

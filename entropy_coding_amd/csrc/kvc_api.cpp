@@ -132,21 +132,21 @@ bool params_geometry(const kvc_params* p, ChunkGeom* g) {
     return geometry(p->planes, p->tokens, p->channels, tc, p->sigma_block_tokens, g);
 }
 
-// Workspace of the encoder: control block, final states, word counts,
-// directory, one word slot per chunk sized for two words per scalar, then
-// the per-call mixture table.
+// Workspace of the encoder: control block (and the header copy), the
+// look-back entries of the chunk sizes, one word slot per chunk sized for
+// two words per scalar (the worst case), then the per-call mixture and
+// escape slot tables.  A slot is written and read back by its chunk's wave
+// alone, never reused within a call.
 struct EncodeLayout {
-    uint64_t states, chunk_words, directory, slots, table, eslots, total, slot_words, max_stream;
+    uint64_t status, slots, table, eslots, total, slot_words, max_stream;
 };
 
 EncodeLayout encode_layout(const ChunkGeom& g) {
     EncodeLayout l;
     const uint64_t n = static_cast<uint64_t>(g.n_chunks);
     l.slot_words = round_up(2ull * kLanes * g.chunk_tokens, 4);
-    l.states = 256;
-    l.chunk_words = round_up(l.states + n * kLanes * 8, 256);
-    l.directory = round_up(l.chunk_words + n * 4, 256);
-    l.slots = round_up(l.directory + (n + 1) * 8, 256);
+    l.status = 256;
+    l.slots = round_up(l.status + n * 8, 256);
     l.table = round_up(l.slots + n * l.slot_words * 2, 256);
     l.eslots = round_up(l.table + kvc::kTableBytes, 256);
     l.total = l.eslots + kvc::kEscapeSlotsBytes;
@@ -353,7 +353,6 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
         (e = kvc::launch_escape_slots(prefix ? prefix : phi.zero, tn + tw, reinterpret_cast<uint32_t*>(ws + l.eslots),
                                       nullptr, s)) != hipSuccess)
         return KVC_ERR_DEVICE;
-    timer.mark(1);
 
     kvc::EncodeArgs ea;
     ea.geom = g;
@@ -367,30 +366,16 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     ea.eslots = reinterpret_cast<const uint32_t*>(ws + l.eslots);
     ea.slots = reinterpret_cast<uint16_t*>(ws + l.slots);
     ea.slot_words = l.slot_words;
-    ea.states = reinterpret_cast<unsigned long long*>(ws + l.states);
-    ea.chunk_words = reinterpret_cast<uint32_t*>(ws + l.chunk_words);
+    ea.status = reinterpret_cast<unsigned long long*>(ws + l.status);
+    ea.out = static_cast<uint8_t*>(d_out);
+    ea.out_capacity = out_capacity;
+    ea.header = make_header(p, g, tn, tw, te);
+    ea.header_copy = ws + kvc::kHeaderCopyOffset;
     ea.ctl = ctl;
+    if ((e = kvc::launch_zero(ea.status, uint64_t(g.n_chunks), s)) != hipSuccess) return KVC_ERR_DEVICE;
+    timer.mark(1);
     if ((e = kvc::launch_encode(ea, p->kv_dtype, p->mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(2);
-
-    unsigned long long* dir = reinterpret_cast<unsigned long long*>(ws + l.directory);
-    if ((e = kvc::launch_scan(ea.chunk_words, g.n_chunks, dir, ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
-    timer.mark(3);
-
-    kvc::CompactArgs ca;
-    ca.geom = g;
-    ca.slots = ea.slots;
-    ca.slot_words = l.slot_words;
-    ca.states = ea.states;
-    ca.chunk_words = ea.chunk_words;
-    ca.directory = dir;
-    ca.out = static_cast<uint8_t*>(d_out);
-    ca.out_capacity = out_capacity;
-    ca.ctl = ctl;
-    ca.header_copy = ws + kvc::kHeaderCopyOffset;
-    const kvc::StreamHeader h = make_header(p, g, tn, tw, te);
-    if ((e = kvc::launch_compact(ca, h, s)) != hipSuccess) return KVC_ERR_DEVICE;
-    timer.mark(4);
     if (!h_out_bytes) return KVC_OK;                  // asynchronous: kvc_encode_result reads the outcome
     const int st = kvc_encode_result(d_workspace, stream, h_out_bytes, h_header_out);
     timer.read();
@@ -412,6 +397,7 @@ int kvc_encode_result(const void* d_workspace, void* stream, uint64_t* h_out_byt
     kvc_params q;
     ChunkGeom g;
     uint64_t payload = 0, hash = 0;
+    if (host.flags & kvc::kFlagStall) return KVC_ERR_DEVICE;
     if (host.flags & kvc::kFlagBadSigma) return KVC_ERR_INVALID;
     if (parse_header(head, &q, &g, &payload, &hash) != KVC_OK || payload != host.total_payload)
         return KVC_ERR_DEVICE;

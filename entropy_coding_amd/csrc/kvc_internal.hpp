@@ -16,6 +16,7 @@ enum : uint32_t {
     kFlagBadPage = 8u,                  // a block-table entry outside the page pool
     kFlagMismatch = 16u,                // decode: sigma / prefix checksum differs from the header's
     kFlagHeader = 32u,                  // decode: the device stream's header differs from the host copy
+    kFlagStall = 64u,                   // encode: a chunk size was not published in time (never expected)
 };
 
 // Control block at the head of every workspace (cleared by a kernel),
@@ -59,6 +60,10 @@ constexpr uint64_t kTableBytes = 4ull * kTableWordsPadded;
 constexpr uint32_t kAimFloats = 2 * 1986;          // 1985 pairs and a zero pair
 constexpr uint64_t kAimBytes = 4ull * kAimFloats;
 
+struct StreamHeader {
+    uint8_t bytes[128];
+};
+
 struct EncodeArgs {
     ChunkGeom geom;
     const void* kv;
@@ -70,27 +75,15 @@ struct EncodeArgs {
     const uint32_t* eslots;             // bf16: the escape slot table (launch_escape_slots)
     uint16_t* slots;                    // per-chunk word slots, filled from the end
     uint64_t slot_words;                // words per slot (2 per scalar, multiple of 4)
-    unsigned long long* states;         // [n_chunks][64] final states
-    uint32_t* chunk_words;              // [n_chunks] words used
-    Control* ctl;
-};
-
-struct StreamHeader {
-    uint8_t bytes[128];
-};
-
-struct CompactArgs {
-    ChunkGeom geom;
-    const uint16_t* slots;
-    uint64_t slot_words;
-    const unsigned long long* states;
-    const uint32_t* chunk_words;
-    const unsigned long long* directory;   // [n_chunks + 1] payload offsets
-    uint8_t* out;
+    unsigned long long* status;         // [n_chunks] chunk sizes for the look-back, zeroed
+    uint8_t* out;                       // the stream
     uint64_t out_capacity;
+    StreamHeader header;                // the stream header but for payload size, checksum and CRC
+    uint8_t* header_copy;               // the workspace's copy of the finished header
     Control* ctl;
-    uint8_t* header_copy;               // the workspace's copy of the header
 };
+
+
 
 // Decoded rows written straight into paged KV pools: pool (layer, kv) is
 // [num_pages][page_tokens][heads][channels]; plane g = ((layer * 2 + kv) *
@@ -160,9 +153,8 @@ hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t
                             uint64_t n_prefix, const uint8_t* head, const StreamHeader& expect, Control* ctl,
                             hipStream_t s);
 hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);
-hipError_t launch_scan(const uint32_t* chunk_words, int64_t n_chunks,
-                       unsigned long long* directory, Control* ctl, hipStream_t s);
-hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream_t s);
+// Zeroes n 8-byte words (a kernel, so that the call can be captured in a graph).
+hipError_t launch_zero(unsigned long long* p, uint64_t n, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, bool paged, hipStream_t s);
 // Sets kFlagBadPage if a block-table entry of columns [0, used) lies outside the pool.
 hipError_t launch_check_pages(const PagedOut& p, int64_t used, Control* ctl, hipStream_t s);

@@ -218,16 +218,6 @@ hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t
     return hipGetLastError();
 }
 
-// CRC-32 (reflected polynomial 0xEDB88320, as zlib computes it) of the
-// header's first 92 bytes, bit by bit; one thread, once per encode.
-__device__ uint32_t header_crc32(const uint8_t* b) {
-    uint32_t c = 0xFFFFFFFFu;
-    for (uint32_t i = 0; i < kHeaderCrcOffset; ++i) {
-        c ^= b[i];
-        for (int k = 0; k < 8; ++k) c = (c >> 1) ^ ((c & 1u) ? 0xEDB88320u : 0u);
-    }
-    return ~c;
-}
 
 // ---------------------------------------------------------------------------
 // e4m3: the 257 cell edges and the 257-entry escape prefix fit in LDS, so the
@@ -385,10 +375,150 @@ __device__ __forceinline__ void encode_batch(int t, PushState& st, __amdgpu_buff
     for (int u = 0; u < U; ++u) rans_push(st, y[u], slot);
 }
 
+// ---------------------------------------------------------------------------
+// stream layout helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned long long chunk_bytes(uint32_t words) {
+    return (static_cast<unsigned long long>(kStateBytes) + 2ull * words + 7ull) & ~7ull;
+}
+
+__device__ __forceinline__ unsigned long long wave_inclusive_scan(unsigned long long v) {
+    const int lane = threadIdx.x & 63;
+    for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long u = __shfl_up(v, off, 64);
+        if (lane >= off) v += u;
+    }
+    return v;
+}
+
+// Exclusive prefix of the chunk sizes in chunk order, by decoupled look-back:
+// status[c] is 0 until chunk c publishes, then kAggregate | its own size,
+// then kInclusive | the sum of the sizes of chunks 0..c.  A chunk publishes
+// its size, then reads the 64 entries before it at a time (lane i the
+// entry i + 1 back): the nearest inclusive entry and the sizes up to it give
+// its prefix; an entry not yet published between them is waited for.
+// Workgroups start in index order, so every chunk waited for is running or
+// done, and each publishes before it waits: every wait ends.  A wait longer
+// than kLookBackSpins polls (far beyond any launch) raises kFlagStall and
+// counts the entry as 0, so the kernel ends whatever happens.  The entries
+// are read and written with device-scope atomics: chunks on different XCDs
+// see each other's entries through memory, not their L2s.
+constexpr unsigned long long kAggregate = 1ull << 62, kInclusive = 2ull << 62, kStatusValue = kAggregate - 1;
+constexpr uint32_t kLookBackSpins = 1u << 18;      // polls of up to 16 x 512 cycles (about 1 s): far beyond any launch
+
+__device__ __forceinline__ unsigned long long look_back(unsigned long long* status, int64_t chunk,
+                                                        unsigned long long size, Control* ctl) {
+    const int lane = threadIdx.x & 63;
+    if (chunk == 0) {
+        if (lane == 0) __hip_atomic_store(&status[0], kInclusive | size, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return 0;
+    }
+    if (lane == 0) __hip_atomic_store(&status[chunk], kAggregate | size, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long acc = 0;
+    int64_t base = chunk - 1;
+    uint32_t spins = 0;                              // polls so far; at the cap, no more waiting
+    for (;;) {
+        const int64_t idx = base - lane;
+        // before chunk 0: an inclusive prefix of 0
+        unsigned long long v =
+            idx >= 0 ? __hip_atomic_load(&status[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kInclusive;
+        uint64_t waiting = __ballot((v >> 62) == 0ull);
+        uint64_t inclusive = __ballot((v >> 62) == 2ull);
+        // lanes up to and including the nearest inclusive entry
+        uint64_t upto = inclusive ? (inclusive ^ (inclusive - 1ull)) : ~0ull;
+        if ((waiting & upto) && spins < kLookBackSpins) {
+            // one entry still being coded: poll it alone (lane 0), backing off,
+            // then read the window again
+            const int j = __builtin_ctzll(waiting & upto);
+            const unsigned long long* e = &status[base - j];
+            uint32_t nap = 1;
+            for (;;) {
+                if (++spins >= kLookBackSpins) {
+                    if (lane == 0) atomicOr(&ctl->flags, kFlagStall);
+                    break;
+                }
+                for (uint32_t k = 0; k < nap; ++k) __builtin_amdgcn_s_sleep(8);
+                nap = nap < 16u ? 2u * nap : 16u;
+                unsigned long long w = 0;
+                if (lane == 0) w = __hip_atomic_load(e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(w >> 62)) != 0u) break;
+            }
+            continue;
+        }
+        const unsigned long long mine = ((upto >> lane) & 1ull) ? (v & kStatusValue) : 0ull;
+        acc += wave_sum_u64(mine);
+        if (inclusive) break;
+        base -= 64;
+    }
+    if (lane == 0)
+        __hip_atomic_store(&status[chunk], kInclusive | (acc + size), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return acc;
+}
+
+// CRC-32 (reflected polynomial 0xEDB88320, as zlib computes it) of the
+// header's first 92 bytes, bit by bit; one lane, once per encode.
+__device__ uint32_t header_crc32(const uint8_t* b) {
+    uint32_t c = 0xFFFFFFFFu;
+    for (uint32_t i = 0; i < kHeaderCrcOffset; ++i) {
+        c ^= b[i];
+        for (int k = 0; k < 8; ++k) c = (c >> 1) ^ ((c & 1u) ? 0xEDB88320u : 0u);
+    }
+    return ~c;
+}
+
+// A chunk's nw words from its slot to their place in the stream, by one
+// wave: the words start at src (4-byte aligned) or, when `odd`, half a dword
+// after it; out_dw dwords are written (a multiple of 2), the words past nw
+// as zeros.  Each lane moves 16 bytes per step and issues the loads of
+// kCopyBatch steps before their stores, so that few round trips to memory
+// sit on the wave's path (the slot is long out of L2 by the end of the
+// chunk).  Reads may run up to 4 dwords past the slot into the workspace's
+// next region; those words are past nw and masked.
+constexpr int kCopyBatch = 4;
+
+__device__ __forceinline__ void copy_words(const uint32_t* __restrict__ src, bool odd, uint32_t nw,
+                                           uint32_t* __restrict__ dst, uint32_t out_dw) {
+    const uint32_t lane = threadIdx.x & 63u;
+    for (uint32_t base = 0; base < out_dw; base += 256u * kCopyBatch) {
+        uint4 a[kCopyBatch];
+        uint32_t e[kCopyBatch];
+#pragma unroll
+        for (int b = 0; b < kCopyBatch; ++b) {
+            const uint32_t j = base + 256u * b + 4u * lane;          // first output dword of this step
+            if (j < out_dw) {
+                a[b] = *reinterpret_cast<const uint4*>(src + j);
+                e[b] = src[j + 4];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kCopyBatch; ++b) {
+            const uint32_t j = base + 256u * b + 4u * lane;
+            if (j >= out_dw) continue;
+            uint32_t o[4] = {a[b].x, a[b].y, a[b].z, a[b].w};
+            if (odd) {
+                o[0] = __builtin_amdgcn_alignbit(a[b].y, a[b].x, 16);
+                o[1] = __builtin_amdgcn_alignbit(a[b].z, a[b].y, 16);
+                o[2] = __builtin_amdgcn_alignbit(a[b].w, a[b].z, 16);
+                o[3] = __builtin_amdgcn_alignbit(e[b], a[b].w, 16);
+            }
+            // words past nw are padding
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t wi = 2u * (j + q);                    // first word of dword q
+                if (wi >= nw) o[q] = 0u;
+                else if (wi + 1 >= nw) o[q] &= 0xFFFFu;
+            }
+            if (j + 4 <= out_dw) *reinterpret_cast<uint4*>(dst + j) = make_uint4(o[0], o[1], o[2], o[3]);
+            else *reinterpret_cast<uint2*>(dst + j) = make_uint2(o[0], o[1]);
+        }
+    }
+}
+
 template <int KV, int MU>
 __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
     __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
     __shared__ uint32_t s_small[KV == kE4M3 ? kE4Words : 1];
+    __shared__ unsigned long long s_head[kHeaderBytes / 8];        // the last chunk's header
     if constexpr (KV == kE4M3) build_e4_lds(s_small, a.prefix);
     copy_to_lds(s_tab, a.table, static_cast<uint32_t>(kTableBytes / 16));
 
@@ -422,8 +552,46 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
         encode_batch<KV, MU, kEncodeBatch>(t, st, kvb, mub, D, lane, inv24, m, slot);
     for (; t >= 0; --t) encode_batch<KV, MU, 1>(t, st, kvb, mub, D, lane, inv24, m, slot);
 
-    a.states[chunk * 64 + lane] = (static_cast<unsigned long long>(st.xh) << 32) | st.xl;
-    if (lane == 0) a.chunk_words[chunk] = static_cast<uint32_t>(a.slot_words) - st.wp;
+    // the chunk's place in the stream: the sizes of the chunks before it
+    const uint32_t nw = static_cast<uint32_t>(a.slot_words) - st.wp;
+    const unsigned long long size = chunk_bytes(nw);
+    const unsigned long long beg = look_back(a.status, chunk, size, a.ctl);
+    const uint64_t n = static_cast<uint64_t>(a.geom.n_chunks);
+    const uint64_t pay_off = kHeaderBytes + 8ull * (n + 1);
+    const bool dir_fits = pay_off <= a.out_capacity;
+    if (pay_off + beg + size <= a.out_capacity) {
+        // the 64 final states, then the words from the slot (this wave's own
+        // stores: wait for them before reading them back in other lanes),
+        // zero padded to 8 bytes
+        uint8_t* dst = a.out + pay_off + beg;
+        reinterpret_cast<unsigned long long*>(dst)[lane] = (static_cast<unsigned long long>(st.xh) << 32) | st.xl;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        copy_words(reinterpret_cast<const uint32_t*>(slot) + (st.wp >> 1), (st.wp & 1u) != 0, nw,
+                   reinterpret_cast<uint32_t*>(dst + kStateBytes), static_cast<uint32_t>((size - kStateBytes) / 4));
+    } else if (lane == 0) {
+        atomicOr(&a.ctl->flags, kFlagCapacity);
+    }
+    unsigned long long* dir = reinterpret_cast<unsigned long long*>(a.out + kHeaderBytes);
+    if (lane == 0 && dir_fits) dir[chunk] = beg;
+    if (static_cast<uint64_t>(chunk) + 1 == n && lane == 0) {
+        // the last chunk knows the payload size: directory end, header (with
+        // the side-information checksum of the kernel before and its CRC),
+        // and the workspace's copy of the header (also when the stream does
+        // not fit, for the size it needed)
+        const unsigned long long total = beg + size;
+        a.ctl->total_payload = total;
+        if (dir_fits) dir[n] = total;
+        for (int i = 0; i < kHeaderBytes / 8; ++i) __builtin_memcpy(&s_head[i], a.header.bytes + 8 * i, 8);
+        s_head[72 / 8] = total;
+        s_head[80 / 8] = a.ctl->side_hash;
+        const uint32_t crc = header_crc32(reinterpret_cast<const uint8_t*>(s_head));
+        s_head[kHeaderCrcOffset / 8] =
+            (s_head[kHeaderCrcOffset / 8] & 0xFFFFFFFFull) | (static_cast<unsigned long long>(crc) << 32);
+        for (int i = 0; i < kHeaderBytes / 8; ++i) {
+            if (a.out_capacity >= static_cast<uint64_t>(kHeaderBytes)) reinterpret_cast<unsigned long long*>(a.out)[i] = s_head[i];
+            reinterpret_cast<unsigned long long*>(a.header_copy)[i] = s_head[i];
+        }
+    }
 }
 
 hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s) {
@@ -435,130 +603,6 @@ hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStr
     else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_encode<kE4M3, kBF16>), grid, block, 0, s, a);
     else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_encode<kE4M3, kF32>), grid, block, 0, s, a);
     else return hipErrorInvalidValue;
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// stream compaction: exclusive scan of chunk sizes (one workgroup, wave
-// scans), then one workgroup per chunk copies states and words to the
-// chunk's final offset with 8-byte stores.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ unsigned long long chunk_bytes(uint32_t words) {
-    return (static_cast<unsigned long long>(kStateBytes) + 2ull * words + 7ull) & ~7ull;
-}
-
-__device__ __forceinline__ unsigned long long wave_inclusive_scan(unsigned long long v) {
-    const int lane = threadIdx.x & 63;
-    for (int off = 1; off < 64; off <<= 1) {
-        const unsigned long long u = __shfl_up(v, off, 64);
-        if (lane >= off) v += u;
-    }
-    return v;
-}
-
-__global__ void __launch_bounds__(1024) k_scan(const uint32_t* __restrict__ words, int64_t n,
-                                               unsigned long long* __restrict__ dir, Control* ctl) {
-    __shared__ unsigned long long s_wave[16];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t per = (n + 1023) / 1024;
-    const int64_t lo = tid * per;
-    const int64_t hi = (lo + per < n) ? lo + per : n;
-    unsigned long long local = 0;
-    for (int64_t i = lo; i < hi; ++i) local += chunk_bytes(words[i]);
-    const unsigned long long inc = wave_inclusive_scan(local);
-    if (lane == 63) s_wave[wave] = inc;
-    __syncthreads();
-    if (wave == 0) {
-        unsigned long long w = (lane < 16) ? s_wave[lane] : 0ull;
-        const unsigned long long wi = wave_inclusive_scan(w);
-        if (lane < 16) s_wave[lane] = wi - w;      // exclusive over waves
-    }
-    __syncthreads();
-    unsigned long long run = s_wave[wave] + inc - local;
-    for (int64_t i = lo; i < hi; ++i) {
-        dir[i] = run;
-        run += chunk_bytes(words[i]);
-    }
-    if (tid == 1023) {
-        dir[n] = run;
-        ctl->total_payload = run;
-    }
-}
-
-hipError_t launch_scan(const uint32_t* chunk_words, int64_t n_chunks, unsigned long long* directory,
-                       Control* ctl, hipStream_t s) {
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, chunk_words, n_chunks, directory, ctl);
-    return hipGetLastError();
-}
-
-__global__ void __launch_bounds__(256) k_compact(CompactArgs a, StreamHeader h) {
-    const int64_t n = a.geom.n_chunks;
-    const unsigned long long total = a.ctl->total_payload;
-    const uint64_t dir_off = kHeaderBytes;
-    const uint64_t pay_off = dir_off + 8ull * static_cast<uint64_t>(n + 1);
-    const bool fits = pay_off + total <= a.out_capacity;
-    const int tid = threadIdx.x;
-    if (blockIdx.x == 0 && tid == 0) {
-        // the payload size and the side-information checksum complete the
-        // header; its CRC covers bytes [0, 92).  The workspace keeps a copy
-        // (also when the stream does not fit, for the size it needed).
-        __shared__ unsigned long long s_head[kHeaderBytes / 8];
-        for (int i = 0; i < kHeaderBytes / 8; ++i) __builtin_memcpy(&s_head[i], h.bytes + 8 * i, 8);
-        s_head[72 / 8] = total;
-        s_head[80 / 8] = a.ctl->side_hash;
-        const uint32_t crc = header_crc32(reinterpret_cast<const uint8_t*>(s_head));
-        s_head[kHeaderCrcOffset / 8] = (s_head[kHeaderCrcOffset / 8] & 0xFFFFFFFFull) | (static_cast<unsigned long long>(crc) << 32);
-        for (int i = 0; i < kHeaderBytes / 8; ++i) {
-            if (fits) reinterpret_cast<unsigned long long*>(a.out)[i] = s_head[i];
-            reinterpret_cast<unsigned long long*>(a.header_copy)[i] = s_head[i];
-        }
-        if (!fits) atomicOr(&a.ctl->flags, kFlagCapacity);
-    }
-    if (!fits) return;
-    unsigned long long* odir = reinterpret_cast<unsigned long long*>(a.out + dir_off);
-    for (int64_t c = blockIdx.x; c < n; c += gridDim.x) {
-        const unsigned long long beg = a.directory[c];
-        if (tid == 0) {
-            odir[c] = beg;
-            if (c == n - 1) odir[n] = total;
-        }
-        uint8_t* dst = a.out + pay_off + beg;
-        if (tid < 64) reinterpret_cast<unsigned long long*>(dst)[tid] = a.states[c * 64 + tid];
-        // words [w0, w0 + nw) of the slot -> dst + 512, zero padded to 8 bytes;
-        // the slot is 8-byte aligned, so read aligned dwords and realign by
-        // half a dword when w0 is odd
-        const uint32_t nw = a.chunk_words[c];
-        const uint64_t w0 = a.slot_words - nw;
-        const uint32_t* src32 = reinterpret_cast<const uint32_t*>(a.slots + static_cast<uint64_t>(c) * a.slot_words);
-        const uint32_t s_dw = static_cast<uint32_t>(w0 >> 1);                    // first source dword
-        const bool odd = (w0 & 1) != 0;
-        const uint32_t out_dw = static_cast<uint32_t>((chunk_bytes(nw) - kStateBytes) / 4);   // multiple of 2
-        const uint32_t src_end_dw = static_cast<uint32_t>(a.slot_words >> 1);   // exclusive
-        uint32_t* d32 = reinterpret_cast<uint32_t*>(dst + kStateBytes);
-        for (uint32_t i = 2 * tid; i < out_dw; i += 2 * blockDim.x) {
-            uint32_t v[3];
-#pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                const uint32_t sd = s_dw + i + j;
-                v[j] = sd < src_end_dw ? src32[sd] : 0u;
-            }
-            uint32_t o0 = odd ? __builtin_amdgcn_alignbit(v[1], v[0], 16) : v[0];
-            uint32_t o1 = odd ? __builtin_amdgcn_alignbit(v[2], v[1], 16) : v[1];
-            // words past nw are padding
-            const uint32_t wi = 2 * i;                     // first word of o0
-            if (wi + 0 >= nw) o0 = 0u;
-            else if (wi + 1 >= nw) o0 &= 0xFFFFu;
-            if (wi + 2 >= nw) o1 = 0u;
-            else if (wi + 3 >= nw) o1 &= 0xFFFFu;
-            *reinterpret_cast<uint2*>(d32 + i) = make_uint2(o0, o1);
-        }
-    }
-}
-
-hipError_t launch_compact(const CompactArgs& a, const StreamHeader& h, hipStream_t s) {
-    int64_t blocks = a.geom.n_chunks;
-    if (blocks > 65535) blocks = 65535;
-    hipLaunchKernelGGL(k_compact, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, a, h);
     return hipGetLastError();
 }
 
@@ -1688,6 +1732,18 @@ __global__ void __launch_bounds__(THREADS) k_marginal_prefix(uint32_t* __restric
         run += c[j];
     }
     if (tid == THREADS - 1) hist[N] = te;
+}
+
+__global__ void k_zero_u64(unsigned long long* __restrict__ p, uint64_t n) {
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0ull;
+}
+
+hipError_t launch_zero(unsigned long long* p, uint64_t n, hipStream_t s) {
+    uint64_t blocks = (n + 255) / 256;
+    blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
+    hipLaunchKernelGGL(k_zero_u64, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_marginal(const void* samples, int dtype, uint64_t n, uint32_t te, uint32_t* prefix_out,

@@ -24,7 +24,7 @@ HEADER_BYTES = 128
 DECODE_WORKSPACE_BYTES = 917504
 NOALLOC_SCRATCH_BYTES = 917504
 ESTIMATE_WORKSPACE_BYTES = 256
-ENCODE_STAGES = 4     # side-information checksum, coding kernel, size scan, compaction
+ENCODE_STAGES = 2     # side-information checksum + per-call tables, coding kernel (with the stream's layout)
 DECODE_STAGES = 2     # side-information checksum + escape bucket table, decoding kernel
 
 EXPORTS = [
@@ -59,7 +59,7 @@ class kvc_paged_kv(ctypes.Structure):
 
 
 class kvc_encode_info(ctypes.Structure):
-    _fields_ = [("stage_ms", ctypes.c_float * 4)]
+    _fields_ = [("stage_ms", ctypes.c_float * ENCODE_STAGES)]
 
 
 class kvc_decode_info(ctypes.Structure):

@@ -59,14 +59,15 @@ enum { KVC_BF16 = 0, KVC_E4M3 = 1, KVC_F32 = 2 };   /* E4M3 = OCP float8 e4m3fn 
 #define KVC_HEADER_BYTES 128
 #define KVC_DECODE_WORKSPACE_BYTES 917504   /* control block, escape tables, coder tables */
 #define KVC_ESTIMATE_WORKSPACE_BYTES 256
-#define KVC_ENCODE_STAGES 4
+#define KVC_ENCODE_STAGES 2
 #define KVC_DECODE_STAGES 2
 
 /* Optional per-call measurements (pass NULL to skip; costs a few events). */
 typedef struct kvc_encode_info {
     float stage_ms[KVC_ENCODE_STAGES];  /* GPU time of: side-information checksum
-                                           and per-call tables, coding kernel,
-                                           size scan, compaction                  */
+                                           and per-call tables, coding kernel
+                                           (which also places every chunk at its
+                                           final offset)                          */
 } kvc_encode_info;
 
 typedef struct kvc_decode_info {

@@ -59,7 +59,8 @@ def test_encode_sizes(kvc):
     max_stream, ws = kvc.kvc_encode_sizes(p)
     n_chunks = w.planes * 4 * 2
     assert max_stream == 128 + 8 * (n_chunks + 1) + n_chunks * (512 + 2 * 2 * 64 * 1024)
-    assert ws >= n_chunks * (512 + 4 + 8 + 4 * 64 * 1024)
+    # a look-back entry and a worst-case word slot (two words per scalar) per chunk
+    assert n_chunks * (8 + 4 * 64 * 1024) <= ws <= n_chunks * (8 + 4 * 64 * 1024) + (1 << 20)
     for bad in [dict(channels=96), dict(planes=0), dict(tokens=0), dict(sigma_block_tokens=30, chunk_tokens=20),
                 dict(sigma_block_tokens=1, chunk_tokens=0, planes=1 << 30, tokens=1 << 10), dict(kv_dtype=2),
                 dict(mu_dtype=1), dict(w_narrow_bp=9000, w_wide_bp=1001), dict(chunk_tokens=1 << 21),
