@@ -129,7 +129,7 @@ def cpu_baseline(workload, workers: int = 0):
 # ---------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------
-def prepare(workload, dev, calib_reps: int, sigma_block: int = 0, sigma_fit: str = "rms"):
+def prepare(workload, dev, calib_reps: int, sigma_block: int = 0, sigma_fit: str = "rms", narrow_dof: int = 0):
     import torch
     from entropy_coding_amd import kvc
     from entropy_coding_amd import workloads as W
@@ -151,7 +151,8 @@ def prepare(workload, dev, calib_reps: int, sigma_block: int = 0, sigma_fit: str
         del k_l, m_l
         ck, cm = W.layer_calibration(w, l, reps=calib_reps, device=dev)
         if sigma_fit == "rate":
-            s_kvh = kvc.kvc_calibrate_sigma_rate(ck, cm, prefix, (w.w_narrow_bp, w.w_wide_bp), block_tokens=sigma_block)
+            s_kvh = kvc.kvc_calibrate_sigma_rate(ck, cm, prefix, (w.w_narrow_bp, w.w_wide_bp), block_tokens=sigma_block,
+                                                 narrow_dof=narrow_dof)
         else:
             s_kvh = kvc.kvc_calibrate_sigma(ck, cm, block_tokens=sigma_block)
         sigma[l * ppl:(l + 1) * ppl] = W.expand_sigma(w, s_kvh)
@@ -253,6 +254,8 @@ def main():
                     help="position-aware sigma: one sigma per block of this many tokens (0 = per plane)")
     ap.add_argument("--sigma-fit", choices=["rms", "rate"], default="rms",
                     help="sigma calibration: the RMS of the residual, or the scale fitted to the code length")
+    ap.add_argument("--narrow-dof", type=int, default=0,
+                    help="narrow part of the mixture: 0 = the pages' Gaussian, nu = Student's t with nu degrees of freedom")
     ap.add_argument("--paged", type=int, default=0,
                     help="decode straight into a paged KV cache with pages of this many tokens (shuffled table)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -282,7 +285,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     reps = args.calib_reps if args.calib_reps is not None else w.calib_reps
-    kv, mu, sigma, prefix = prepare(w, dev, reps, args.sigma_block, args.sigma_fit)
+    kv, mu, sigma, prefix = prepare(w, dev, reps, args.sigma_block, args.sigma_fit, args.narrow_dof)
     n = w.n_scalars
     weights = (w.w_narrow_bp, w.w_wide_bp)
     # with sigma blocks the library's default picks a divisor of the block length
@@ -295,7 +298,7 @@ def main():
     parts = ([slice(l * w.planes_per_layer, (l + 1) * w.planes_per_layer) for l in range(w.layers)]
              if per_layer else [slice(0, w.planes)])
     g_part = parts[0].stop - parts[0].start
-    p = kvc.make_params(kv_code, mu_code, g_part, w.tokens, w.channels, weights, tc, args.sigma_block)
+    p = kvc.make_params(kv_code, mu_code, g_part, w.tokens, w.channels, weights, tc, args.sigma_block, args.narrow_dof)
     enc = kvc.Encoder(p, dev)
     if tc == 0:
         tc = kvc.kvc_stream_info(enc(kv[parts[0]], mu[parts[0]], sigma[parts[0]], prefix)[:128].cpu().numpy())[0] \
@@ -387,7 +390,7 @@ def main():
     bits_int, bits_float = 0.0, 0.0
     for sl in parts:
         bi, bf = kvc.kvc_estimate_bits(kv[sl], mu[sl], sigma[sl], prefix, weights,
-                                       sigma_block_tokens=args.sigma_block, chunk_tokens=tc)
+                                       sigma_block_tokens=args.sigma_block, chunk_tokens=tc, narrow_dof=args.narrow_dof)
         frac = (sl.stop - sl.start) / w.planes
         bits_int += bi * frac
         bits_float += bf * frac
@@ -405,7 +408,7 @@ def main():
     # out (encode); words and states and mu in, KV out (decode)
     alg = float(kv_size + mu_size) * n + stream_bytes
     traffic = measured_traffic() if args.workload == 2 and tc == w.chunk_tokens and not args.paged \
-        and not args.sigma_block and args.sigma_fit == "rms" else {}
+        and not args.sigma_block and args.sigma_fit == "rms" and not args.narrow_dof else {}
 
     def roofline(kernel, avg_ms):
         a = alg / (avg_ms * 1e-3) / 1e9
@@ -433,6 +436,7 @@ def main():
             "workload": w.name, "shape": [w.layers, 2, w.batch, w.heads, w.tokens, w.channels],
             "scalars": n, "mixture_bp": list(weights), "chunk_tokens": tc, "sigma_block_tokens": args.sigma_block,
             "sigma_calibration": f"{args.sigma_fit}, {reps}x{w.calib_tokens} tokens per layer",
+            "narrow_part": "gaussian" if args.narrow_dof == 0 else f"student-t, {args.narrow_dof} dof",
             "mu_dtype": "bf16" if mu_size == 2 else "fp32", "calls_per_step": len(parts),
             "decode_output": f"paged, {args.paged}-token pages" if args.paged else "contiguous",
             "second_pass_copy_ms": scatter_ms,

@@ -127,6 +127,7 @@ uint32_t default_chunk_tokens(int64_t planes, int64_t tokens, int64_t channels, 
 
 bool params_geometry(const kvc_params* p, ChunkGeom* g) {
     if (!p || !kv_dtype_ok(p->kv_dtype) || !mu_dtype_ok(p->mu_dtype)) return false;
+    if (p->narrow_dof > uint32_t(kvc::kNarrowDofMax) || p->reserved != 0) return false;
     uint32_t tc = p->chunk_tokens;
     if (tc == 0) tc = default_chunk_tokens(p->planes, p->tokens, p->channels, p->sigma_block_tokens);
     return geometry(p->planes, p->tokens, p->channels, tc, p->sigma_block_tokens, g);
@@ -175,6 +176,7 @@ kvc::StreamHeader make_header(const kvc_params* p, const ChunkGeom& g, uint32_t 
     h.bytes[11] = kLog2L;
     h.bytes[12] = kWordBits;
     h.bytes[13] = kLanes;
+    h.bytes[14] = static_cast<uint8_t>(p->narrow_dof);
     put32(h.bytes, 16, p->w_narrow_bp);
     put32(h.bytes, 20, p->w_wide_bp);
     put32(h.bytes, 24, tn);
@@ -204,7 +206,8 @@ int parse_header(const uint8_t* b, kvc_params* p, ChunkGeom* g, uint64_t* payloa
     if (std::memcmp(b, "KVC1", 4) != 0 || get16(b, 4) != kVersion || get16(b, 6) != KVC_HEADER_BYTES)
         return KVC_ERR_CORRUPT;
     if (get32(b, kvc::kHeaderCrcOffset) != crc32(b, kvc::kHeaderCrcOffset)) return KVC_ERR_CORRUPT;
-    if (b[10] != kLog2M || b[11] != kLog2L || b[12] != kWordBits || b[13] != kLanes || get16(b, 14) != 0)
+    if (b[10] != kLog2M || b[11] != kLog2L || b[12] != kWordBits || b[13] != kLanes ||
+        b[14] > kvc::kNarrowDofMax || b[15] != 0)
         return KVC_ERR_CORRUPT;
     kvc_params q;
     std::memset(&q, 0, sizeof(q));
@@ -217,6 +220,7 @@ int parse_header(const uint8_t* b, kvc_params* p, ChunkGeom* g, uint64_t* payloa
     q.tokens = static_cast<int64_t>(get64(b, 48));
     q.channels = static_cast<int64_t>(get64(b, 56));
     q.sigma_block_tokens = get32(b, 88);
+    q.narrow_dof = b[14];
     uint32_t tn, tw, te;
     if (!kv_dtype_ok(q.kv_dtype) || !mu_dtype_ok(q.mu_dtype) ||
         !budgets(q.kv_dtype, q.w_narrow_bp, q.w_wide_bp, &tn, &tw, &te))
@@ -305,6 +309,12 @@ int kvc_phi_tables(uint32_t* h_narrow, uint32_t* h_wide) {
     return KVC_OK;
 }
 
+int kvc_narrow_table(uint32_t narrow_dof, uint32_t* h_out) {
+    if (!h_out || narrow_dof > uint32_t(kvc::kNarrowDofMax)) return KVC_ERR_INVALID;
+    kvc::host_narrow_table(narrow_dof, h_out);
+    return KVC_OK;
+}
+
 int kvc_encode_sizes(const kvc_params* p, uint64_t* h_max_stream_bytes, uint64_t* h_workspace_bytes) {
     ChunkGeom g;
     if (!params_geometry(p, &g)) return KVC_ERR_INVALID;
@@ -333,7 +343,7 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     if (workspace_bytes < l.total) return KVC_ERR_CAPACITY;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e, p->narrow_dof);
     if (e != hipSuccess) return KVC_ERR_DEVICE;
 
     uint8_t* ws = static_cast<uint8_t*>(d_workspace);
@@ -488,7 +498,7 @@ int decode_launch(const void* h_header, const void* d_in, uint64_t in_bytes, con
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e, p.narrow_dof);
     if (e != hipSuccess) return KVC_ERR_DEVICE;
 
     Control* ctl = static_cast<Control*>(d_workspace);
@@ -662,11 +672,12 @@ int kvc_calibrate_sigma_blocks(const void* d_kv, const void* d_mu, int32_t kv_dt
 
 int kvc_calibrate_sigma_rate(const void* d_kv, const void* d_mu, int32_t kv_dtype, int32_t mu_dtype, int64_t reps,
                              int64_t planes, int64_t tokens, int64_t channels, int64_t block_tokens, float sigma_floor,
-                             uint32_t w_narrow_bp, uint32_t w_wide_bp, const uint32_t* d_prefix, float* d_sigma_out,
-                             void* d_workspace, uint64_t workspace_bytes, void* stream) {
+                             uint32_t w_narrow_bp, uint32_t w_wide_bp, uint32_t narrow_dof, const uint32_t* d_prefix,
+                             float* d_sigma_out, void* d_workspace, uint64_t workspace_bytes, void* stream) {
     uint32_t tn, tw, te;
     if (!budgets(kv_dtype, w_narrow_bp, w_wide_bp, &tn, &tw, &te) || (te && !d_prefix) || !aligned(d_prefix, 4))
         return KVC_ERR_INVALID;
+    if (narrow_dof > uint32_t(kvc::kNarrowDofMax)) return KVC_ERR_INVALID;
     // every candidate sigma must be a valid sigma of the format
     if (!(sigma_floor >= 0x1p-96f) || !(sigma_floor <= 0x1p96f)) return KVC_ERR_INVALID;
     if (block_tokens < 0 || tokens < 1 || planes < 1 || channels < 64) return KVC_ERR_INVALID;
@@ -683,7 +694,7 @@ int kvc_calibrate_sigma_rate(const void* d_kv, const void* d_mu, int32_t kv_dtyp
     if (st != KVC_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e, narrow_dof);
     if (e != hipSuccess) return KVC_ERR_DEVICE;
     uint8_t* ws = static_cast<uint8_t*>(d_workspace);
     auto* part = reinterpret_cast<unsigned long long*>(ws + rms_bytes);
@@ -718,7 +729,7 @@ int kvc_estimate_bits(const kvc_params* p, const void* d_kv, const void* d_mu, c
     if (te && !d_prefix) return KVC_ERR_INVALID;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e, p->narrow_dof);
     if (e != hipSuccess) return KVC_ERR_DEVICE;
     Control* ctl = static_cast<Control*>(d_workspace);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
@@ -733,6 +744,7 @@ int kvc_estimate_bits(const kvc_params* p, const void* d_kv, const void* d_mu, c
     a.te = te;
     a.w_narrow_bp = p->w_narrow_bp;
     a.w_wide_bp = p->w_wide_bp;
+    a.narrow_dof = p->narrow_dof;
     a.phi = phi;
     a.ctl = ctl;
     if ((e = kvc::launch_estimate(a, p->kv_dtype, p->mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
@@ -745,17 +757,19 @@ int kvc_estimate_bits(const kvc_params* p, const void* d_kv, const void* d_mu, c
     return KVC_OK;
 }
 
-int kvc_cdf_table(int32_t kv_dtype, int32_t mu_dtype, uint32_t w_narrow_bp, uint32_t w_wide_bp, const void* d_mu,
-                  const float* d_sigma, int64_t pairs, const uint32_t* d_prefix, uint32_t* d_out, void* stream) {
+int kvc_cdf_table(int32_t kv_dtype, int32_t mu_dtype, uint32_t w_narrow_bp, uint32_t w_wide_bp, uint32_t narrow_dof,
+                  const void* d_mu, const float* d_sigma, int64_t pairs, const uint32_t* d_prefix, uint32_t* d_out,
+                  void* stream) {
     uint32_t tn, tw, te;
     if (!mu_dtype_ok(mu_dtype) || !budgets(kv_dtype, w_narrow_bp, w_wide_bp, &tn, &tw, &te)) return KVC_ERR_INVALID;
+    if (narrow_dof > uint32_t(kvc::kNarrowDofMax)) return KVC_ERR_INVALID;
     if (pairs < 1 || pairs > (int64_t(1) << 24) || !d_mu || !d_sigma || !d_out) return KVC_ERR_INVALID;
     if (te && !d_prefix) return KVC_ERR_INVALID;
     if (!data_aligned(kv_dtype, mu_dtype, nullptr, d_mu, d_sigma, d_prefix) || !aligned(d_out, 4))
         return KVC_ERR_INVALID;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    const kvc::PhiTables phi = kvc::device_phi_tables(&e);
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e, narrow_dof);
     if (e != hipSuccess) return KVC_ERR_DEVICE;
     // sigma is checked on the host, a block at a time
     bool ok = true;

@@ -126,6 +126,7 @@ struct EstimateArgs {
     const uint32_t* prefix;
     uint32_t tn, tw, te;
     uint32_t w_narrow_bp, w_wide_bp;
+    uint32_t narrow_dof;                // 0: Gaussian narrow part; nu: Student's t (float model)
     PhiTables phi;
     Control* ctl;
 };
@@ -140,6 +141,12 @@ void* noalloc_scratch(hipError_t* err);
 constexpr int kPhiPoints = 12289;
 PhiTables device_phi_tables(hipError_t* err);
 void host_phi_tables(uint32_t* a, uint32_t* b);   // kPhiPoints entries each
+// The narrow part's base table: Phi (narrow_dof = 0) or Student's t with
+// narrow_dof = 1..kNarrowDofMax degrees of freedom, truncated to [-24, 24]
+// and renormalised.  The device tables with `a` set to it.
+constexpr int kNarrowDofMax = 16;
+PhiTables device_phi_tables(hipError_t* err, uint32_t narrow_dof);
+void host_narrow_table(uint32_t narrow_dof, uint32_t* a);   // kPhiPoints entries
 
 hipError_t launch_clear_control(Control* ctl, hipStream_t s);
 // The mixture table for budgets (tn, tw) into `table` (kTableBytes) and,

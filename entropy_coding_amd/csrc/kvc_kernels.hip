@@ -52,6 +52,87 @@ PhiTables g_phi_dev[kMaxDevices];
 hipError_t g_phi_err[kMaxDevices];
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Student-t narrow part (optional): A[k] = round(2^31 (F(z_k) - F(-24)) /
+// (F(24) - F(-24))) for Student's t with nu = 1..16 degrees of freedom,
+// truncated to [-24, 24] scale units and renormalised there.  F comes from
+// the finite series for integer degrees of freedom (theta = atan(|z| /
+// sqrt(nu)), c = cos^2 theta; odd nu: 1/2 + (theta + sin theta cos theta
+// (1 + 2/3 c + (2 4)/(3 5) c^2 + ...)) / pi; even nu: 1/2 + sin theta / 2
+// (1 + 1/2 c + (1 3)/(2 4) c^2 + ...)), in double precision: every entry
+// lies more than 1e-5 from a rounding tie.  Built on the host and copied to
+// a device on its first call that uses it.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline double student_t_cdf(double z, int nu) {
+    const double th = atan(fabs(z) / sqrt(static_cast<double>(nu)));
+    const double c = cos(th) * cos(th);
+    double term = 1.0, acc = 0.0, f;
+    if (nu & 1) {
+        for (int k = 0; k < (nu - 1) / 2; ++k) {
+            if (k) term *= (2.0 * k) / (2.0 * k + 1.0) * c;
+            acc += term;
+        }
+        f = 0.5 + (th + sin(th) * cos(th) * acc) * 0.31830988618379067154;
+    } else {
+        for (int k = 0; k < nu / 2; ++k) {
+            if (k) term *= (2.0 * k - 1.0) / (2.0 * k) * c;
+            acc += term;
+        }
+        f = 0.5 + 0.5 * sin(th) * acc;
+    }
+    return z >= 0.0 ? f : 1.0 - f;
+}
+
+void host_narrow_table(uint32_t narrow_dof, uint32_t* a) {
+    if (narrow_dof == 0) {
+        static uint32_t wide[kTablePoints];
+        host_phi_tables(a, wide);
+        return;
+    }
+    const int nu = static_cast<int>(narrow_dof);
+    const double lo = student_t_cdf(-kTableZMax, nu);
+    const double span = 1.0 - 2.0 * lo;
+    for (int k = 0; k < kTablePoints; ++k) {
+        const double z = -24.0 + k / 256.0;
+        a[k] = static_cast<uint32_t>(std::floor(std::ldexp((student_t_cdf(z, nu) - lo) / span, 31) + 0.5));
+    }
+}
+
+__device__ uint32_t g_t_tables[kNarrowDofMax][kTablePoints];
+
+namespace {
+std::once_flag g_t_once[kMaxDevices][kNarrowDofMax];
+const uint32_t* g_t_dev[kMaxDevices][kNarrowDofMax];
+hipError_t g_t_err[kMaxDevices][kNarrowDofMax];
+}  // namespace
+
+PhiTables device_phi_tables(hipError_t* err, uint32_t narrow_dof) {
+    PhiTables t = device_phi_tables(err);
+    if (*err != hipSuccess || narrow_dof == 0) return t;
+    if (narrow_dof > static_cast<uint32_t>(kNarrowDofMax)) {
+        *err = hipErrorInvalidValue;
+        return PhiTables{nullptr, nullptr, nullptr};
+    }
+    int dev = 0;
+    (void)hipGetDevice(&dev);                                 // checked by the call above
+    const int j = static_cast<int>(narrow_dof) - 1;
+    std::call_once(g_t_once[dev][j], [dev, j, narrow_dof]() {
+        static uint32_t h[kTablePoints];                      // serialised by call_once per (device, nu)
+        static std::mutex m;
+        std::lock_guard<std::mutex> lock(m);
+        host_narrow_table(narrow_dof, h);
+        hipError_t r = hipMemcpyToSymbol(HIP_SYMBOL(g_t_tables), h, sizeof(h), sizeof(h) * j, hipMemcpyHostToDevice);
+        void* p = nullptr;
+        if (r == hipSuccess) r = hipGetSymbolAddress(&p, HIP_SYMBOL(g_t_tables));
+        g_t_err[dev][j] = r;
+        g_t_dev[dev][j] = r == hipSuccess ? static_cast<const uint32_t*>(p) + static_cast<size_t>(j) * kTablePoints
+                                          : nullptr;
+    });
+    *err = g_t_err[dev][j];
+    t.a = g_t_dev[dev][j];
+    return t;
+}
+
 PhiTables device_phi_tables(hipError_t* err) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -1774,6 +1855,17 @@ __device__ __forceinline__ double gauss_mass(double a, double b) {
     return 0.5 * (erfc(-b * k) - erfc(-a * k));
 }
 
+// F(b) - F(a) for the Student-t narrow part, truncated to [-24, 24] and
+// renormalised (as its table is), a <= b.
+__device__ __forceinline__ double t_mass(double a, double b, int nu) {
+    a = fmax(a, -static_cast<double>(kTableZMax));
+    b = fmin(b, static_cast<double>(kTableZMax));
+    if (!(a < b)) return 0.0;
+    const double span = 1.0 - 2.0 * student_t_cdf(-static_cast<double>(kTableZMax), nu);
+    const double m = a > 0.0 ? student_t_cdf(-a, nu) - student_t_cdf(-b, nu) : student_t_cdf(b, nu) - student_t_cdf(a, nu);
+    return m / span;
+}
+
 template <int KV, int MU>
 __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
     __shared__ uint32_t s_tab[kTableEntries];
@@ -1802,8 +1894,9 @@ __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
         acc_i += 31.0 - log2(static_cast<double>(c1 - c0));
         const double lo = edge<KV>(s), hi = edge<KV>(s + 1);
         const double m = mu, sd = sg;
-        double q = wn * gauss_mass((lo - m) / sd, (hi - m) / sd) +
-                   ww * gauss_mass((lo - m) / (3.0 * sd), (hi - m) / (3.0 * sd));
+        const double narrow = a.narrow_dof ? t_mass((lo - m) / sd, (hi - m) / sd, static_cast<int>(a.narrow_dof))
+                                           : gauss_mass((lo - m) / sd, (hi - m) / sd);
+        double q = wn * narrow + ww * gauss_mass((lo - m) / (3.0 * sd), (hi - m) / (3.0 * sd));
         if (a.te) q += we * static_cast<double>(a.prefix[s + 1] - a.prefix[s]) / a.te;
         const double b = -log2(q);
         acc_f += (b < 64.0) ? b : 64.0;

@@ -28,7 +28,7 @@ ENCODE_STAGES = 2     # side-information checksum + per-call tables, coding kern
 DECODE_STAGES = 2     # side-information checksum + escape bucket table, decoding kernel
 
 EXPORTS = [
-    "kvc_version", "kvc_status_string", "kvc_phi_tables", "kvc_encode_sizes", "kvc_encode", "kvc_encode_result",
+    "kvc_version", "kvc_status_string", "kvc_phi_tables", "kvc_narrow_table", "kvc_encode_sizes", "kvc_encode", "kvc_encode_result",
     "kvc_stream_info", "kvc_decode", "kvc_decode_async", "kvc_decode_result", "kvc_decode_noalloc",
     "kvc_decode_paged",
     "kvc_calibrate_sigma", "kvc_calibrate_sigma_blocks", "kvc_calibrate_sigma_rate",
@@ -45,6 +45,7 @@ class kvc_params(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32), ("mu_dtype", ctypes.c_int32),
         ("w_narrow_bp", ctypes.c_uint32), ("w_wide_bp", ctypes.c_uint32),
         ("chunk_tokens", ctypes.c_uint32), ("sigma_block_tokens", ctypes.c_uint32),
+        ("narrow_dof", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
         ("planes", ctypes.c_int64), ("tokens", ctypes.c_int64), ("channels", ctypes.c_int64),
     ]
 
@@ -84,6 +85,7 @@ def _sig(name, res, args):
 _lib_version = _sig("kvc_version", ctypes.c_int, [])
 _lib_status_string = _sig("kvc_status_string", ctypes.c_char_p, [ctypes.c_int])
 _lib_phi_tables = _sig("kvc_phi_tables", ctypes.c_int, [_P, _P])
+_lib_narrow_table = _sig("kvc_narrow_table", ctypes.c_int, [_U32, _P])
 _lib_encode_sizes = _sig("kvc_encode_sizes", ctypes.c_int, [ctypes.POINTER(kvc_params), ctypes.POINTER(_U64), ctypes.POINTER(_U64)])
 _lib_encode = _sig("kvc_encode", ctypes.c_int,
                    [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _U64, ctypes.POINTER(_U64), _P, _P, _U64, _P, _P])
@@ -101,11 +103,11 @@ _lib_calibrate = _sig("kvc_calibrate_sigma", ctypes.c_int,
 _lib_calibrate_blocks = _sig("kvc_calibrate_sigma_blocks", ctypes.c_int,
                              [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, _I64, ctypes.c_float, _P, _P, _U64, _P])
 _lib_calibrate_rate = _sig("kvc_calibrate_sigma_rate", ctypes.c_int,
-                           [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, _I64, ctypes.c_float, _U32, _U32, _P, _P,
-                            _P, _U64, _P])
+                           [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, _I64, ctypes.c_float, _U32, _U32, _U32, _P,
+                            _P, _P, _U64, _P])
 _lib_marginal = _sig("kvc_build_marginal", ctypes.c_int, [_P, _I32, _U64, _U32, _U32, _P, _P])
 _lib_estimate = _sig("kvc_estimate_bits", ctypes.c_int, [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _P, _U64, _P])
-_lib_cdf_table = _sig("kvc_cdf_table", ctypes.c_int, [_I32, _I32, _U32, _U32, _P, _P, _I64, _P, _P, _P])
+_lib_cdf_table = _sig("kvc_cdf_table", ctypes.c_int, [_I32, _I32, _U32, _U32, _U32, _P, _P, _I64, _P, _P, _P])
 
 
 class KvcError(RuntimeError):
@@ -181,10 +183,18 @@ def kvc_phi_tables():
     return a, b
 
 
+def kvc_narrow_table(narrow_dof: int = 0):
+    """The narrow part's base table (Phi, or Student's t with narrow_dof
+    degrees of freedom), computed on the host."""
+    a = np.zeros(12289, dtype=np.uint32)
+    _check(_lib_narrow_table(narrow_dof, a.ctypes.data), "kvc_narrow_table")
+    return a
+
+
 def make_params(kv_dtype, mu_dtype, planes, tokens, channels, weights=(9500, 300), chunk_tokens=0,
-                sigma_block_tokens=0) -> kvc_params:
+                sigma_block_tokens=0, narrow_dof=0) -> kvc_params:
     return kvc_params(kv_dtype, mu_dtype, weights[0], weights[1], chunk_tokens, sigma_block_tokens,
-                      planes, tokens, channels)
+                      narrow_dof, 0, planes, tokens, channels)
 
 
 def sigma_shape(planes: int, tokens: int, channels: int, sigma_block_tokens: int = 0):
@@ -250,7 +260,7 @@ class Encoder:
 
 def kvc_encode(kv: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, prefix: torch.Tensor | None = None,
                weights=(9500, 300), chunk_tokens: int = 0, stream=None,
-               sigma_block_tokens: int = 0) -> torch.Tensor:
+               sigma_block_tokens: int = 0, narrow_dof: int = 0) -> torch.Tensor:
     """Encode KV [G, T, D] under the mixture around mu with sigma [G, D] (or
     [G, ceil(T / B), D] with sigma_block_tokens = B); returns the stream as
     a uint8 device tensor."""
@@ -262,7 +272,7 @@ def kvc_encode(kv: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, prefix: 
     if tuple(mu.shape) != (g, t, d) or tuple(sigma.shape) != sigma_shape(g, t, d, sigma_block_tokens) \
             or sigma.dtype != torch.float32:
         raise ValueError("shapes: kv and mu [G, T, D], sigma [G, D] (or [G, ceil(T / B), D]) float32")
-    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens, sigma_block_tokens)
+    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens, sigma_block_tokens, narrow_dof)
     return Encoder(p, kv.device)(kv, mu, sigma, prefix, stream).clone()
 
 
@@ -433,7 +443,7 @@ def kvc_calibrate_sigma(kv: torch.Tensor, mu: torch.Tensor, sigma_floor: float =
 def kvc_calibrate_sigma_rate(kv: torch.Tensor, mu: torch.Tensor, prefix: torch.Tensor | None = None,
                              weights=(9500, 300), sigma_floor: float = 2.0 ** -30, block_tokens: int = 0,
                              out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                             stream=None) -> torch.Tensor:
+                             stream=None, narrow_dof: int = 0) -> torch.Tensor:
     """Rate-fitted sigma: of the candidates max(floor, rms * (1 - j/32)),
     j = 0..24, the one with the least integer code length of the held-out
     kv [reps, planes, tokens, channels] under the mixture the data will be
@@ -448,7 +458,7 @@ def kvc_calibrate_sigma_rate(kv: torch.Tensor, mu: torch.Tensor, prefix: torch.T
     if workspace is None:
         workspace = torch.empty(n_rows * d * (1024 + 12800) + 65536, dtype=torch.uint8, device=kv.device)
     st = _lib_calibrate_rate(_ptr(kv), _ptr(mu), _kv_dtype(kv), _mu_dtype(mu), r, g, t, d, block_tokens,
-                             sigma_floor, weights[0], weights[1], _ptr(prefix), _ptr(out), _ptr(workspace),
+                             sigma_floor, weights[0], weights[1], narrow_dof, _ptr(prefix), _ptr(out), _ptr(workspace),
                              workspace.numel(), _stream(stream))
     _check(st, "kvc_calibrate_sigma_rate")
     return out
@@ -467,10 +477,10 @@ def kvc_build_marginal(samples: torch.Tensor, weights=(9500, 300), stream=None) 
 
 
 def kvc_estimate_bits(kv, mu, sigma, prefix=None, weights=(9500, 300), stream=None, sigma_block_tokens: int = 0,
-                      chunk_tokens: int = 0):
+                      chunk_tokens: int = 0, narrow_dof: int = 0):
     """(integer-model bits/scalar, float-model bits/scalar)."""
     g, t, d = kv.shape
-    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens, sigma_block_tokens)
+    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens, sigma_block_tokens, narrow_dof)
     ws = torch.empty(ESTIMATE_WORKSPACE_BYTES, dtype=torch.uint8, device=kv.device)
     out = (ctypes.c_double * 2)()
     st = _lib_estimate(ctypes.byref(p), _ptr(kv), _ptr(mu), _ptr(sigma), _ptr(prefix), ctypes.addressof(out),
@@ -480,7 +490,7 @@ def kvc_estimate_bits(kv, mu, sigma, prefix=None, weights=(9500, 300), stream=No
 
 
 def kvc_cdf_table(kv_dtype: int, mu: torch.Tensor, sigma: torch.Tensor, prefix=None, weights=(9500, 300),
-                  stream=None) -> torch.Tensor:
+                  stream=None, narrow_dof: int = 0) -> torch.Tensor:
     """C(b) for b = 0..N for each (mu, sigma) pair; int32 storage of uint32
     values (reinterpret as uint32 on the host)."""
     _need(mu, "mu")
@@ -488,7 +498,7 @@ def kvc_cdf_table(kv_dtype: int, mu: torch.Tensor, sigma: torch.Tensor, prefix=N
     n_sym = 65536 if kv_dtype == KVC_BF16 else 256
     pairs = mu.numel()
     out = torch.empty((pairs, n_sym + 1), dtype=torch.int32, device=mu.device)
-    st = _lib_cdf_table(kv_dtype, _mu_dtype(mu), weights[0], weights[1], _ptr(mu), _ptr(sigma), pairs,
+    st = _lib_cdf_table(kv_dtype, _mu_dtype(mu), weights[0], weights[1], narrow_dof, _ptr(mu), _ptr(sigma), pairs,
                         _ptr(prefix), _ptr(out), _stream(stream))
     _check(st, "kvc_cdf_table")
     return out

@@ -106,6 +106,15 @@ typedef struct kvc_params {
                                 be a multiple of chunk_tokens unless B >=
                                 tokens (KVC_ERR_INVALID).  Recorded in the
                                 stream header.                                 */
+    uint32_t narrow_dof;     /* the narrow part's shape ([wiki] "future directions",
+                                [blog] "limitations and future directions": a
+                                better residual model): 0 = the pages'
+                                N(mu, sigma^2); nu = 1..16 = Student's t with nu
+                                degrees of freedom, location mu, scale sigma,
+                                truncated to +-24 sigma and renormalised there.
+                                The wide part and p_hat are unchanged.
+                                Recorded in the stream header.                 */
+    uint32_t reserved;       /* 0                                                  */
     int64_t planes;          /* G = layers * 2 * batch * kv_heads                  */
     int64_t tokens;          /* T                                                  */
     int64_t channels;        /* D, a positive multiple of 64                       */
@@ -127,6 +136,14 @@ const char* kvc_status_string(int status);
  * Returns KVC_ERR_INVALID for a NULL pointer.
  */
 int kvc_phi_tables(uint32_t* h_narrow /* [12289] */, uint32_t* h_wide /* [12289] */);
+
+/*
+ * The narrow part's table for narrow_dof (kvc_params): narrow_dof = 0 gives
+ * h_narrow of kvc_phi_tables; nu = 1..16 gives round(2^31 (F(z_k) - F(-24))
+ * / (F(24) - F(-24))) for Student's t with nu degrees of freedom.  Needs no
+ * GPU.  KVC_ERR_INVALID for a NULL pointer or nu > 16.
+ */
+int kvc_narrow_table(uint32_t narrow_dof, uint32_t* h_out /* [12289] */);
 
 /*
  * Sizes for kvc_encode: the largest stream the call can produce (every
@@ -335,8 +352,9 @@ int kvc_calibrate_sigma_blocks(const void* d_kv, const void* d_mu, int32_t kv_dt
  * of 2^16 (31 - e) - L[m] for each frequency f = C(s+1) - C(s), with e the
  * top bit of f, m the 8 bits below it and L[m] = round(2^16 log2(1 + m/256));
  * the first j on a tie (an integer sum: deterministic).  The mixture
- * weights and d_prefix (NULL allowed for a single Gaussian) are the ones the
- * data will be coded with.  sigma_floor in [2^-96, 2^96].  Output and
+ * weights, the narrow part (narrow_dof, as in kvc_params) and d_prefix
+ * (NULL allowed for a single Gaussian) are the ones the data will be coded
+ * with.  sigma_floor in [2^-96, 2^96].  Output and
  * block_tokens as kvc_calibrate_sigma_blocks.  Workspace (256-byte aligned):
  * KVC_CALIBRATE_RATE_WORKSPACE_BYTES(planes * n_blocks, channels).  Does
  * not synchronise.
@@ -346,9 +364,9 @@ int kvc_calibrate_sigma_blocks(const void* d_kv, const void* d_mu, int32_t kv_dt
 int kvc_calibrate_sigma_rate(const void* d_kv, const void* d_mu, int32_t kv_dtype,
                              int32_t mu_dtype, int64_t reps, int64_t planes, int64_t tokens,
                              int64_t channels, int64_t block_tokens, float sigma_floor,
-                             uint32_t w_narrow_bp, uint32_t w_wide_bp, const uint32_t* d_prefix,
-                             float* d_sigma_out, void* d_workspace, uint64_t workspace_bytes,
-                             void* stream);
+                             uint32_t w_narrow_bp, uint32_t w_wide_bp, uint32_t narrow_dof,
+                             const uint32_t* d_prefix, float* d_sigma_out, void* d_workspace,
+                             uint64_t workspace_bytes, void* stream);
 
 /*
  * Empirical marginal ([wiki] "mixture distribution": an empirical BF16
@@ -375,14 +393,15 @@ int kvc_estimate_bits(const kvc_params* p, const void* d_kv, const void* d_mu,
 
 /*
  * The shared CDF itself ([blog] "deployment parameters": encoder and decoder
- * must agree on it bit for bit).  For each of `pairs` (mu, sigma) pairs,
+ * must agree on it bit for bit), with the narrow part narrow_dof (as in
+ * kvc_params).  For each of `pairs` (mu, sigma) pairs,
  * writes C(b) for b = 0..N to d_out[pair][N + 1].  d_mu holds `pairs`
  * values of mu_dtype, d_sigma `pairs` floats.  Synchronises `stream` once
  * (to report an invalid sigma).
  */
 int kvc_cdf_table(int32_t kv_dtype, int32_t mu_dtype, uint32_t w_narrow_bp,
-                  uint32_t w_wide_bp, const void* d_mu, const float* d_sigma, int64_t pairs,
-                  const uint32_t* d_prefix, uint32_t* d_out, void* stream);
+                  uint32_t w_wide_bp, uint32_t narrow_dof, const void* d_mu, const float* d_sigma,
+                  int64_t pairs, const uint32_t* d_prefix, uint32_t* d_out, void* stream);
 
 #ifdef __cplusplus
 }

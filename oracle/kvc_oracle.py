@@ -42,6 +42,7 @@ __all__ = [
     "cdf_table", "build_marginal", "calibrate_sigma", "side_hash", "encode",
     "decode", "parse_header", "model_bits_int", "model_bits_float",
     "chunk_layout", "sigma_blocks", "crc32", "HEADER_CRC_OFFSET", "stream_header",
+    "NARROW_DOF_MAX", "student_t_cdf_mp", "narrow_table",
 ]
 
 # ---------------------------------------------------------------------------
@@ -207,13 +208,79 @@ def phi_tables():
     return np.array(a, dtype=np.int64), np.array(b, dtype=np.int64)
 
 
+# ---------------------------------------------------------------------------
+# S-13  Student-t narrow part (optional)
+# ---------------------------------------------------------------------------
+NARROW_DOF_MAX = 16
+
+
+def student_t_cdf_mp(z, nu: int):
+    """CDF of Student's t with nu degrees of freedom (integer nu >= 1) at z,
+    in mpmath at the working precision, from the finite series for integer
+    degrees of freedom: with theta = atan(|z| / sqrt(nu)) and c = cos^2 theta,
+    odd nu: 1/2 + (theta + sin theta cos theta (1 + 2/3 c + (2 4)/(3 5) c^2
+    + ... , (nu - 1)/2 terms)) / pi; even nu: 1/2 + sin theta / 2 (1 + 1/2 c +
+    (1 3)/(2 4) c^2 + ... , nu/2 terms); F(-z) = 1 - F(z)."""
+    import mpmath
+    z = mpmath.mpf(z)
+    th = mpmath.atan(abs(z) / mpmath.sqrt(nu))
+    c = mpmath.cos(th) ** 2
+    term, acc = mpmath.mpf(1), mpmath.mpf(0)
+    if nu % 2:
+        for k in range((nu - 1) // 2):
+            if k:
+                term *= mpmath.mpf(2 * k) / (2 * k + 1) * c
+            acc += term
+        f = mpmath.mpf(1) / 2 + (th + mpmath.sin(th) * mpmath.cos(th) * acc) / mpmath.pi
+    else:
+        for k in range(nu // 2):
+            if k:
+                term *= mpmath.mpf(2 * k - 1) / (2 * k) * c
+            acc += term
+        f = mpmath.mpf(1) / 2 + mpmath.sin(th) / 2 * acc
+    return f if z >= 0 else 1 - f
+
+
 @functools.lru_cache(maxsize=None)
-def mixture_table(t_n: int, t_w: int) -> np.ndarray:
-    """H[k] = floor(T_n A[k] / 2^31) + floor(T_w B[k] / 2^31): the two
-    Gaussian parts of the mixture, in integer budget units, on the z grid;
-    H[12289] repeats H[12288] so that interpolation may read one past the
-    end."""
-    a, b = phi_tables()
+def narrow_table(narrow_dof: int = 0) -> np.ndarray:
+    """Base table of the narrow part on the z grid.  narrow_dof = 0: the
+    pages' Gaussian, A of :func:`phi_tables`.  narrow_dof = nu in
+    1..NARROW_DOF_MAX: Student's t with nu degrees of freedom, location mu
+    and scale sigma, truncated to [-24, 24] scale units and renormalised
+    there, A[k] = floor(2^31 (F(z_k) - F(-24)) / (F(24) - F(-24)) + 1/2), so
+    that A[0] = 0 and A[12288] = 2^31 as for the Gaussian.
+
+    Reading ([wiki] § future directions and [blog] § limitations and future
+    directions name a better residual model without a form; the residual of
+    an FP8 predictor is long-tailed, [wiki] § mixture distribution): the
+    heavy-tailed narrow part replaces the Gaussian one inside the pages'
+    mixture; the wide Gaussian and the escape part stay.  nu -> infinity
+    gives back the Gaussian."""
+    if narrow_dof == 0:
+        return phi_tables()[0]
+    if not 1 <= narrow_dof <= NARROW_DOF_MAX:
+        raise ValueError("narrow_dof must be 0 or 1..16")
+    import mpmath
+    out = []
+    with mpmath.workdps(50):
+        lo = student_t_cdf_mp(-TABLE_Z_MAX, narrow_dof)
+        span = 1 - 2 * lo
+        two31 = mpmath.mpf(2) ** 31
+        half = mpmath.mpf(1) / 2
+        for k in range(TABLE_POINTS):
+            z = mpmath.mpf(-TABLE_Z_MAX) + mpmath.mpf(k) / TABLE_STEPS_PER_UNIT
+            out.append(int(mpmath.floor(two31 * (student_t_cdf_mp(z, narrow_dof) - lo) / span + half)))
+    return np.array(out, dtype=np.int64)
+
+
+@functools.lru_cache(maxsize=None)
+def mixture_table(t_n: int, t_w: int, narrow_dof: int = 0) -> np.ndarray:
+    """H[k] = floor(T_n A[k] / 2^31) + floor(T_w B[k] / 2^31): the narrow
+    and the wide part of the mixture, in integer budget units, on the z grid
+    (A the narrow part's table, S-13); H[12289] repeats H[12288] so that
+    interpolation may read one past the end."""
+    a = narrow_table(narrow_dof)
+    b = phi_tables()[1]
     h = ((t_n * a) >> 31) + ((t_w * b) >> 31)
     return np.concatenate([h, h[-1:]])
 
@@ -249,7 +316,7 @@ def mu_to_f32(mu, mu_dtype: int) -> np.ndarray:
     return np.where(np.isfinite(m), m, np.float32(0.0)).astype(np.float32)
 
 
-def cdf(b, mu32, inv32, dtype: int, t_n: int, t_w: int, prefix=None) -> np.ndarray:
+def cdf(b, mu32, inv32, dtype: int, t_n: int, t_w: int, prefix=None, narrow_dof: int = 0) -> np.ndarray:
     """C(b): cumulative frequency below symbol b under the mixture.
 
     S-3  d = pos(b) - mu and z' = d * (2^24/sigma), each one IEEE float32
@@ -271,15 +338,15 @@ def cdf(b, mu32, inv32, dtype: int, t_n: int, t_w: int, prefix=None) -> np.ndarr
         d = (pos - mu32).astype(np.float32)
         z24 = (d * inv24).astype(np.float32)
     q = np.floor(np.clip(z24, -qmax, qmax)).astype(np.int64)
-    g = h_fx(q, mixture_table(t_n, t_w))
+    g = h_fx(q, mixture_table(t_n, t_w, narrow_dof))
     if prefix is not None:
         g = g + np.asarray(prefix, dtype=np.int64)[b]
     return b + g
 
 
-def gauss_cum(b, mu32, inv32, dtype: int, t_n: int, t_w: int) -> np.ndarray:
-    """G(b) = h(q_b): the two Gaussian parts of C below symbol b, 0 .. T_n + T_w."""
-    return cdf(b, mu32, inv32, dtype, t_n, t_w, None) - np.asarray(b).astype(np.int64)
+def gauss_cum(b, mu32, inv32, dtype: int, t_n: int, t_w: int, narrow_dof: int = 0) -> np.ndarray:
+    """G(b) = h(q_b): the narrow and wide parts of C below symbol b, 0 .. T_n + T_w."""
+    return cdf(b, mu32, inv32, dtype, t_n, t_w, None, narrow_dof) - np.asarray(b).astype(np.int64)
 
 
 def escape_cum(b, prefix=None) -> np.ndarray:
@@ -333,7 +400,7 @@ def _check_sigma_blocks(tokens: int, chunk_tokens: int, sigma_block_tokens: int)
 
 
 def cdf_table(mu, sigma, dtype: int, mu_dtype: int, w_narrow_bp: int,
-              w_wide_bp: int, prefix=None) -> np.ndarray:
+              w_wide_bp: int, prefix=None, narrow_dof: int = 0) -> np.ndarray:
     """C(b) for every b = 0..N, for each (mu, sigma) pair: shape [P, N+1]."""
     t_n, t_w, t_e = budgets(dtype, w_narrow_bp, w_wide_bp)
     if t_e and prefix is None:
@@ -344,7 +411,7 @@ def cdf_table(mu, sigma, dtype: int, mu_dtype: int, w_narrow_bp: int,
     b = np.arange(n + 1, dtype=np.int64)
     out = np.empty((mu32.size, n + 1), dtype=np.int64)
     for i in range(mu32.size):
-        out[i] = cdf(b, mu32[i], inv[i], dtype, t_n, t_w, prefix if t_e else None)
+        out[i] = cdf(b, mu32[i], inv[i], dtype, t_n, t_w, prefix if t_e else None, narrow_dof)
     return out
 
 
@@ -451,7 +518,7 @@ def code_len_q16(f) -> np.ndarray:
 
 def calibrate_sigma_rate(kv, mu, kv_dtype: int, mu_dtype: int, sigma_floor: float, prefix,
                          w_narrow_bp: int, w_wide_bp: int, block_tokens: int = 0, base=None,
-                         return_costs: bool = False):
+                         return_costs: bool = False, narrow_dof: int = 0):
     """S-12: the sigma among sigma_j = max(floor, fp32(base * k_j)), k_j =
     1 - j/32, j = 0..24, that gives the held-out data the least integer code
     length sum(code_len_q16(f)) under the format's CDF, f = C(s+1) - C(s);
@@ -485,8 +552,8 @@ def calibrate_sigma_rate(kv, mu, kv_dtype: int, mu_dtype: int, sigma_floor: floa
         cands.append(sj)
         inv = _inv_sigma(sj)[:, tok_block, :]                 # [planes, T, D]
         for r in range(reps):
-            c0 = cdf(s[r], m32[r], inv, kv_dtype, t_n, t_w, pref)
-            c1 = cdf(s[r] + 1, m32[r], inv, kv_dtype, t_n, t_w, pref)
+            c0 = cdf(s[r], m32[r], inv, kv_dtype, t_n, t_w, pref, narrow_dof)
+            c1 = cdf(s[r] + 1, m32[r], inv, kv_dtype, t_n, t_w, pref, narrow_dof)
             cl = code_len_q16(c1 - c0)                        # [planes, T, D]
             for b in range(base3.shape[1]):
                 costs[j, :, b, :] += cl[:, b * blk:(b + 1) * blk, :].sum(axis=1)
@@ -547,7 +614,7 @@ def chunk_layout(planes: int, tokens: int, channels: int, chunk_tokens: int):
     return g, tc, k, length
 
 
-_HEADER_FMT = "<4sHHBBBBBBHIIIIIIQQQQQQI"
+_HEADER_FMT = "<4sHHBBBBBBBBIIIIIIQQQQQQI"
 
 
 HEADER_CRC_OFFSET = 92             # CRC-32 of header bytes [0, 92) at [92, 96)
@@ -566,7 +633,7 @@ def crc32(data: bytes) -> int:
 
 
 def stream_header(kv_dtype, mu_dtype, w_n, w_w, chunk_tokens, planes, tokens, channels,
-            n_chunks, payload_bytes, shash, sigma_block_tokens=0) -> bytes:
+            n_chunks, payload_bytes, shash, sigma_block_tokens=0, narrow_dof=0) -> bytes:
     """S-10: the 128-byte header.  Bytes [0, 92) hold the fields, [92, 96)
     the CRC-32 of those 92 bytes (a damaged header is reported as such
     instead of steering the decoder with a wrong shape), the rest zero."""
@@ -574,7 +641,7 @@ def stream_header(kv_dtype, mu_dtype, w_n, w_w, chunk_tokens, planes, tokens, ch
     h = struct.pack(
         _HEADER_FMT,
         MAGIC, VERSION, HEADER_BYTES, kv_dtype, mu_dtype, LOG2_M, LOG2_L,
-        WORD_BITS, LANES, 0, w_n, w_w, t_n, t_w, t_e, chunk_tokens,
+        WORD_BITS, LANES, narrow_dof, 0, w_n, w_w, t_n, t_w, t_e, chunk_tokens,
         planes, tokens, channels, n_chunks, payload_bytes, shash, sigma_block_tokens)
     assert len(h) == HEADER_CRC_OFFSET
     h += struct.pack("<I", crc32(h))
@@ -586,7 +653,7 @@ def parse_header(stream: bytes) -> dict:
         raise StreamError("stream shorter than its header")
     f = struct.unpack_from(_HEADER_FMT, stream, 0)
     keys = ["magic", "version", "header_bytes", "kv_dtype", "mu_dtype", "log2_m",
-            "log2_l", "word_bits", "lanes", "reserved", "w_narrow_bp", "w_wide_bp",
+            "log2_l", "word_bits", "lanes", "narrow_dof", "reserved", "w_narrow_bp", "w_wide_bp",
             "t_n", "t_w", "t_e", "chunk_tokens", "planes", "tokens", "channels",
             "n_chunks", "payload_bytes", "side_hash", "sigma_block_tokens"]
     h = dict(zip(keys, f))
@@ -599,6 +666,8 @@ def parse_header(stream: bytes) -> dict:
         raise StreamError("unsupported coder parameters")
     if h["kv_dtype"] not in (BF16, E4M3) or h["mu_dtype"] not in (BF16, F32):
         raise StreamError("bad dtype")
+    if h["narrow_dof"] > NARROW_DOF_MAX:
+        raise StreamError("bad narrow part")
     try:
         bud = budgets(h["kv_dtype"], h["w_narrow_bp"], h["w_wide_bp"])
     except ValueError as e:
@@ -624,7 +693,7 @@ def _roundup8(x):
 
 def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int,
            w_wide_bp: int, chunk_tokens: int, batch_chunks: int = 2048,
-           sigma_block_tokens: int = 0) -> bytes:
+           sigma_block_tokens: int = 0, narrow_dof: int = 0) -> bytes:
     """Code kv [G, T, D] (raw bit patterns) under the mixture around mu [G, T, D]
     with sigma [G, D] (or, with sigma_block_tokens = B > 0, sigma
     [G, ceil(T / B), D]: S-11); return the KVC-1 byte stream.
@@ -653,6 +722,8 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
     t_n, t_w, t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)
     if t_e and prefix is None:
         raise ValueError("mixture with an escape part needs the marginal prefix")
+    if not 0 <= narrow_dof <= NARROW_DOF_MAX:
+        raise ValueError("narrow_dof must be 0 or 1..16")
     pref = prefix if t_e else None
     mu32_all = mu_to_f32(mu, mu_dtype)
     sig3, blk = sigma_blocks(sigma, t_len, sigma_block_tokens)
@@ -677,8 +748,8 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
             tok = np.minimum(tcid * chunk_tokens + t, t_len - 1)[:, None]
             s = sym_all[g[:, None], tok, d]
             mu32 = mu32_all[g[:, None], tok, d]
-            g0 = gauss_cum(s, mu32, inv, kv_dtype, t_n, t_w)
-            fg = gauss_cum(s + 1, mu32, inv, kv_dtype, t_n, t_w) - g0
+            g0 = gauss_cum(s, mu32, inv, kv_dtype, t_n, t_w, narrow_dof)
+            fg = gauss_cum(s + 1, mu32, inv, kv_dtype, t_n, t_w, narrow_dof) - g0
             q0 = escape_cum(s, pref)
             f = fg + escape_cum(s + 1, pref) - q0
             fu = f.astype(np.uint64)
@@ -704,7 +775,7 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
     directory = np.concatenate([[0], np.cumsum(sizes)]).astype("<u8")
     shash = side_hash(sigma, prefix if t_e else None)
     head = stream_header(kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp, chunk_tokens,
-                   g_n, t_len, d_n, n_chunks, int(directory[-1]), shash, sigma_block_tokens)
+                         g_n, t_len, d_n, n_chunks, int(directory[-1]), shash, sigma_block_tokens, narrow_dof)
     return head + directory.tobytes() + b"".join(payloads)
 
 
@@ -730,6 +801,7 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
     g_n, t_len, d_n, tcn = h["planes"], h["tokens"], h["channels"], h["chunk_tokens"]
     n_chunks = h["n_chunks"]
     t_n, t_w, t_e = h["t_n"], h["t_w"], h["t_e"]
+    dof = h["narrow_dof"]
     pref = prefix if t_e else None
     if t_e and prefix is None:
         raise ValueError("stream uses an escape part; the marginal prefix is needed")
@@ -797,14 +869,14 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
             hi_q = np.full((nb, LANES), n_sym, dtype=np.int64)
             for _ in range(steps):
                 mid = (lo_g + hi_g) >> 1
-                go = gauss_cum(mid, mu32, inv, kv_dtype, t_n, t_w) <= target
+                go = gauss_cum(mid, mu32, inv, kv_dtype, t_n, t_w, dof) <= target
                 lo_g, hi_g = np.where(go, mid, lo_g), np.where(go, hi_g, mid)
                 mid = (lo_q + hi_q) >> 1
                 go = escape_cum(mid, pref) <= y
                 lo_q, hi_q = np.where(go, mid, lo_q), np.where(go, hi_q, mid)
             lo = np.where(in_g, lo_g, lo_q)
-            g0 = gauss_cum(lo, mu32, inv, kv_dtype, t_n, t_w)
-            fg = gauss_cum(lo + 1, mu32, inv, kv_dtype, t_n, t_w) - g0
+            g0 = gauss_cum(lo, mu32, inv, kv_dtype, t_n, t_w, dof)
+            fg = gauss_cum(lo + 1, mu32, inv, kv_dtype, t_n, t_w, dof) - g0
             q0 = escape_cum(lo, pref)
             f = (fg + escape_cum(lo + 1, pref) - q0).astype(np.uint64)
             r = np.where(in_g, target - g0, fg + (y - q0)).astype(np.uint64)
@@ -853,7 +925,7 @@ def chunk_payload(stream: bytes, chunk_id: int) -> bytes:
 
 
 def encode_chunks(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
-                  chunk_tokens, chunk_ids, sigma_block_tokens=0):
+                  chunk_tokens, chunk_ids, sigma_block_tokens=0, narrow_dof=0):
     """Payloads of selected chunks only (for sampled parity at full size).
 
     Each chunk depends only on its own slice of kv and mu and on the sigma
@@ -871,20 +943,20 @@ def encode_chunks(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide
         sub_mu = np.asarray(mu)[g:g + 1, t0:t0 + ln, 64 * k:64 * k + 64]
         sub_sig = sig3[g:g + 1, t0 // blk, 64 * k:64 * k + 64]
         s = encode(sub_kv, sub_mu, sub_sig, prefix, kv_dtype, mu_dtype, w_narrow_bp,
-                   w_wide_bp, chunk_tokens)
+                   w_wide_bp, chunk_tokens, narrow_dof=narrow_dof)
         out[int(cid)] = chunk_payload(s, 0)
     return out
 
 
 def wrap_chunk(payload: bytes, sigma_sub, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
-               chunk_tokens, tokens) -> bytes:
+               chunk_tokens, tokens, narrow_dof=0) -> bytes:
     """A one-chunk stream around one chunk's payload (64 channels, `tokens`
     tokens of one plane, its 64 sigmas), so that :func:`decode` can check a
     chunk cut out of a large stream on its own."""
     t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)[2]
     shash = side_hash(np.asarray(sigma_sub, dtype=np.float32).reshape(1, LANES), prefix if t_e else None)
     head = stream_header(kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp, chunk_tokens, 1, tokens, LANES, 1,
-                   len(payload), shash)
+                         len(payload), shash, 0, narrow_dof)
     directory = np.array([0, len(payload)], dtype="<u8")
     return head + directory.tobytes() + payload
 
@@ -935,7 +1007,7 @@ def sigma_per_token(sigma, tokens: int, sigma_block_tokens: int = 0) -> np.ndarr
 
 
 def model_bits_int(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
-                   sigma_block_tokens: int = 0) -> float:
+                   sigma_block_tokens: int = 0, narrow_dof: int = 0) -> float:
     """Mean of -log2(f(s) / M) over all scalars: the ideal code length of the
     integer model ([wiki] § core idea: bits = cross-entropy of q)."""
     kv = np.asarray(kv)
@@ -947,8 +1019,8 @@ def model_bits_int(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wid
     s = order_index(kv, kv_dtype)
     total = 0.0
     for g in range(g_n):
-        c0 = cdf(s[g], mu32[g], inv[g], kv_dtype, t_n, t_w, pref)
-        c1 = cdf(s[g] + 1, mu32[g], inv[g], kv_dtype, t_n, t_w, pref)
+        c0 = cdf(s[g], mu32[g], inv[g], kv_dtype, t_n, t_w, pref, narrow_dof)
+        c1 = cdf(s[g] + 1, mu32[g], inv[g], kv_dtype, t_n, t_w, pref, narrow_dof)
         total += float(np.sum(LOG2_M - np.log2((c1 - c0).astype(np.float64))))
     return total / kv.size
 
@@ -961,12 +1033,28 @@ def _ndtr_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.where(upper, ndtr(-a) - ndtr(-b), ndtr(b) - ndtr(a))
 
 
+def _stdtr_mass(a: np.ndarray, b: np.ndarray, nu: int) -> np.ndarray:
+    """F(b) - F(a) for Student's t with nu degrees of freedom truncated to
+    [-24, 24] and renormalised (S-13), a <= b; the upper-tail form when both
+    are positive.  scipy's stdtr is the CDF."""
+    from scipy.special import stdtr
+    lim = float(TABLE_Z_MAX)
+    a = np.clip(a, -lim, lim)
+    b = np.clip(b, -lim, lim)
+    span = 1.0 - 2.0 * stdtr(nu, -lim)
+    upper = a > 0
+    m = np.where(upper, stdtr(nu, -a) - stdtr(nu, -b), stdtr(nu, b) - stdtr(nu, a))
+    return m / span
+
+
 def model_bits_float(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
-                     cap_bits: float = 64.0, sigma_block_tokens: int = 0) -> float:
+                     cap_bits: float = 64.0, sigma_block_tokens: int = 0, narrow_dof: int = 0) -> float:
     """Mean -log2 q(x) of the continuous mixture over the same cells, float64.
 
     q(x) = w_n [Phi((hi-mu)/sigma) - Phi((lo-mu)/sigma)]
          + w_w [same with 3 sigma] + w_e p_hat(x),
+    (with narrow_dof = nu, the narrow part's Phi is the truncated Student-t
+    of S-13),
     with p_hat(x) = (prefix[x+1] - prefix[x]) / T_e and the weights in basis
     points ([wiki] § mixture distribution).  A per-scalar cost is capped at
     ``cap_bits`` (only reachable without an escape part)."""
@@ -987,7 +1075,8 @@ def model_bits_float(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_w
         with np.errstate(invalid="ignore"):
             a1, b1 = (lo - m) / sg, (hi - m) / sg
             a3, b3 = (lo - m) / (3 * sg), (hi - m) / (3 * sg)
-        q = wn * _ndtr_diff(a1, b1) + ww * _ndtr_diff(a3, b3)
+        narrow = _ndtr_diff(a1, b1) if narrow_dof == 0 else _stdtr_mass(a1, b1, narrow_dof)
+        q = wn * narrow + ww * _ndtr_diff(a3, b3)
         if t_e:
             p = np.asarray(prefix, dtype=np.float64)
             q = q + we * (p[s[g] + 1] - p[s[g]]) / t_e

@@ -22,9 +22,9 @@ def _encode_planes(args):
     """Code a range of planes with the oracle and compare its payload bytes
     with the expected ones; returns (equal, the range's own directory,
     index of the first differing chunk or -1)."""
-    (kv, mu, sig, pref, kv_dtype, mu_dtype, w_n, w_w, tc, sigma_block_tokens, expect, batch) = args
+    (kv, mu, sig, pref, kv_dtype, mu_dtype, w_n, w_w, tc, sigma_block_tokens, expect, batch, narrow_dof) = args
     st = K.encode(kv, mu, sig, pref, kv_dtype, mu_dtype, w_n, w_w, tc, batch_chunks=batch,
-                  sigma_block_tokens=sigma_block_tokens)
+                  sigma_block_tokens=sigma_block_tokens, narrow_dof=narrow_dof)
     h = K.parse_header(st)
     n = h["n_chunks"]
     pay = K.HEADER_BYTES + 8 * (n + 1)
@@ -53,9 +53,9 @@ class Pool:
         self._pool = mp.get_context("forkserver").Pool(self.n)
 
     def submit(self, kv, mu, sig, pref, kv_dtype, mu_dtype, w_n, w_w, tc, expect: bytes,
-               sigma_block_tokens: int = 0, batch: int = 64):
+               sigma_block_tokens: int = 0, batch: int = 64, narrow_dof: int = 0):
         return self._pool.apply_async(_encode_planes, ((kv, mu, sig, pref, kv_dtype, mu_dtype, w_n, w_w, tc,
-                                                        sigma_block_tokens, expect, batch),))
+                                                        sigma_block_tokens, expect, batch, narrow_dof),))
 
     def close(self):
         self._pool.close()

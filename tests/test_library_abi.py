@@ -172,3 +172,30 @@ def test_stream_info_accepts_a_recomputed_crc(kvc):
     st[92:96] = zlib.crc32(bytes(st[:92])).to_bytes(4, "little")
     p, total = kvc.kvc_stream_info(bytes(st))
     assert total == len(oracle_stream())
+
+
+@pytest.mark.parametrize("nu", list(range(0, 17)))
+def test_library_narrow_tables_equal_the_oracle(kvc, nu):
+    """The library's double-precision Student-t series (and libm's erfc for
+    nu = 0) round to the oracle's 50-digit tables."""
+    assert np.array_equal(kvc.kvc_narrow_table(nu).astype(np.int64), O.narrow_table(nu))
+
+
+def test_stream_info_reads_the_narrow_part(kvc):
+    kv, mu, sig, samples = W.tiny_case(7)
+    kv, mu, sig, samples = W.to_numpy_bits(kv), W.to_numpy_bits(mu), sig.numpy(), W.to_numpy_bits(samples)
+    pref = O.build_marginal(samples, O.BF16, 9500, 300)
+    st = O.encode(kv, mu, sig, pref, O.BF16, O.BF16, 9500, 300, 16, narrow_dof=5)
+    p, total = kvc.kvc_stream_info(st[:128])
+    assert p.narrow_dof == 5 and total == len(st)
+    import zlib
+    bad = bytearray(st[:128])
+    bad[14] = 17
+    bad[92:96] = zlib.crc32(bytes(bad[:92])).to_bytes(4, "little")
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_stream_info(bytes(bad))
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_narrow_table(17)
+    q = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, 4, 100, 128, narrow_dof=17)
+    with pytest.raises(kvc.KvcError):
+        kvc.kvc_encode_sizes(q)
