@@ -179,33 +179,24 @@ def offload_reload(w, kv, mu, sigma, prefix, kvc, enc, parts, dws, steps: int):
     host = torch.empty(offs[-1], dtype=torch.uint8, pin_memory=True)
     for s, o in zip(streams, offs):
         host[o:o + s.numel()].copy_(s)
-    headers = [host[o:o + 128].numpy().copy() for o in offs[:-1]]      # host copies: no device read
     del streams
-    stage = [torch.empty(max(sizes), dtype=torch.uint8, device=dev) for _ in range(2)]
     out = torch.empty_like(kv, dtype=torch.int16 if kv.dtype == torch.bfloat16 else torch.uint8)
+    layers = [host[o:o + n] for o, n in zip(offs[:-1], sizes)]
+    g = parts[0].stop - parts[0].start
+    mu_l = mu.view(len(parts), g, *mu.shape[1:])
+    sig_l = sigma.view(len(parts), g, *sigma.shape[1:])
+    out_l = out.view(len(parts), g, *out.shape[1:])
+    half = (max(sizes) + 511) // 256 * 256
+    staging = torch.empty(2 * half, dtype=torch.uint8, device=dev)
+    rws = torch.empty(len(parts) * kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     copy_stream = torch.cuda.Stream(device=dev)
-    compute = torch.cuda.current_stream(dev)
 
     def reload():
-        ready = [None] * len(parts)
-
-        def fetch(l):
-            with torch.cuda.stream(copy_stream):
-                stage[l % 2][:sizes[l]].copy_(host[offs[l]:offs[l + 1]], non_blocking=True)
-                ev = torch.cuda.Event()
-                ev.record(copy_stream)
-            ready[l] = ev
-
-        fetch(0)
-        for l, sl in enumerate(parts):
-            if l + 1 < len(parts):
-                fetch(l + 1)          # its buffer was last read by the decode of layer l - 1, already done
-            compute.wait_event(ready[l])
-            rc = kvc.kvc_decode_into(stage[l % 2][:sizes[l]], mu[sl], sigma[sl], prefix, out[sl], dws,
-                                     header=headers[l])
-            if rc != kvc.KVC_OK:
-                raise kvc.KvcError(rc, "kvc_decode")
-        torch.cuda.synchronize()
+        # the library's pipeline: H2D copies on copy_stream overlapping the
+        # decode of the layer before
+        rc, failed = kvc.kvc_reload(layers, mu_l, sig_l, prefix, out_l, staging, rws, copy_stream=copy_stream)
+        if rc != kvc.KVC_OK:
+            raise kvc.KvcError(rc, f"kvc_reload (layer {failed})")
 
     reload()
     t0 = time.perf_counter()
@@ -233,7 +224,8 @@ def offload_reload(w, kv, mu, sigma, prefix, kvc, enc, parts, dws, steps: int):
         "compressed_ms": t_comp * 1e3, "raw_copy_ms": t_raw * 1e3, "raw_copy_gbps": raw_total / t_raw / 1e9,
         "speedup_vs_raw_copy": t_raw / t_comp, "stream_bytes": offs[-1], "raw_bytes": raw_total,
         "bits_per_scalar": 8.0 * offs[-1] / w.n_scalars,
-        "pipeline": "pinned host stream -> H2D copy on its own stream, overlapped with the decode of the previous layer",
+        "pipeline": "kvc_reload: pinned host streams -> H2D copies on their own stream, each overlapping the decode "
+                    "of the layer before",
     }
 
 
@@ -254,6 +246,9 @@ def main():
                     help="position-aware sigma: one sigma per block of this many tokens (0 = per plane)")
     ap.add_argument("--sigma-fit", choices=["rms", "rate"], default="rms",
                     help="sigma calibration: the RMS of the residual, or the scale fitted to the code length")
+    ap.add_argument("--streams", type=int, default=2,
+                    help="(per-layer workload 4) HIP streams the asynchronous one-layer calls are spread over; "
+                         "1 = synchronous calls one after another")
     ap.add_argument("--narrow-dof", type=int, default=0,
                     help="narrow part of the mixture: 0 = the pages' Gaussian, nu = Student's t with nu degrees of freedom")
     ap.add_argument("--paged", type=int, default=0,
@@ -345,6 +340,54 @@ def main():
         if stats is not None:
             stats.append((e_ms, d_ms))
 
+    pipelined = per_layer and args.streams > 1 and paged is None
+    if pipelined:
+        # every layer's encode queued without waiting (one encoder per layer,
+        # its outcome read after the pass), spread over `streams` HIP streams
+        # so that two one-layer calls (half the chip each) run at once; then
+        # every decode the same way
+        encs = [enc] + [kvc.Encoder(p, dev) for _ in parts[1:]]
+        dwss = [dws] + [torch.empty(kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev) for _ in parts[1:]]
+        side = [torch.cuda.Stream(device=dev) for _ in range(args.streams)]
+        log(f"[bench] pipelined: {len(parts)} one-layer calls queued asynchronously over {len(side)} streams")
+
+        def step(stats=None):
+            main = torch.cuda.current_stream(dev)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record(main)
+            for q in side:
+                q.wait_stream(main)
+            for l, sl in enumerate(parts):
+                encs[l].enqueue(kv[sl], mu[sl], sigma[sl], prefix, stream=side[l % len(side)])
+            for q in side:
+                main.wait_stream(q)
+            ev[1].record(main)
+            sts = [encs[l].result(stream=side[l % len(side)]) for l in range(len(parts))]
+            ev[2].record(main)
+            for q in side:
+                q.wait_stream(main)
+            for l, sl in enumerate(parts):
+                rc = kvc.kvc_decode_async(sts[l], mu[sl], sigma[sl], prefix, kv_out[sl], dwss[l], encs[l].header.copy(),
+                                          stream=side[l % len(side)])
+                if rc != kvc.KVC_OK:
+                    raise kvc.KvcError(rc, "kvc_decode_async")
+            for q in side:
+                main.wait_stream(q)
+            ev[3].record(main)
+            fb = 0
+            for l in range(len(parts)):
+                di = {}
+                rc = kvc.kvc_decode_result(dwss[l], stream=side[l % len(side)], info=di)
+                if rc != kvc.KVC_OK:
+                    raise kvc.KvcError(rc, "kvc_decode_result")
+                fb += di["fallback_symbols"]
+            torch.cuda.synchronize()
+            fallback[0], stream_total[0] = fb, sum(st.numel() for st in sts)
+            if stats is not None:
+                # no per-kernel stage times for queued calls: the whole pass
+                e, d = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+                stats.append(([0.0, e], [0.0, d]))
+
     for i in range(args.warmup):
         step()
         log(f"[bench] warmup {i + 1}/{args.warmup}")
@@ -417,6 +460,12 @@ def main():
                 "frac": a / HBM_PEAK_GBPS, "traffic": t, "algorithmic_bytes": alg, "avg_ms": avg_ms}
 
     rl = {"k_encode": roofline("k_encode", enc_kernel), "k_decode": roofline("k_decode", dec_kernel)}
+    # the same algorithmic bytes over each whole call (per-call tables,
+    # checksum and launches included): what a caller of kvc_encode /
+    # kvc_decode gets
+    call_rl = {k: {"ms": ms, "achieved": alg / (ms * 1e-3) / 1e9,
+                   "frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+               for k, ms in (("encode", enc_total), ("decode", dec_total))}
     dominant = "k_decode" if dec_kernel >= enc_kernel else "k_encode"
     res = {
         "metric": "encode/decode GB/s of raw KV + bits/scalar, Qwen3-8B-shaped bf16 KV" if args.workload == 2
@@ -439,6 +488,8 @@ def main():
             "narrow_part": "gaussian" if args.narrow_dof == 0 else f"student-t, {args.narrow_dof} dof",
             "mu_dtype": "bf16" if mu_size == 2 else "fp32", "calls_per_step": len(parts),
             "decode_output": f"paged, {args.paged}-token pages" if args.paged else "contiguous",
+            "calls": (f"asynchronous, {args.streams} streams (times: whole passes)" if pipelined
+                      else "synchronous, one after another"),
             "second_pass_copy_ms": scatter_ms,
         },
         "encode_gbps": raw / (enc_total * 1e-3) / 1e9,
@@ -453,6 +504,7 @@ def main():
         "roundtrip_exact": ok,
         "roofline": rl[dominant],
         "rooflines": rl,
+        "call_rooflines": call_rl,
         "cpu_baseline": cpu,
         "pages_context": {"bits_per_scalar_qwen3_0.6B_to_32B": [6.74, 5.92],
                           "fp8_bits_per_element": [2.05, 2.59]},

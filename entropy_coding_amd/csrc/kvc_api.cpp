@@ -626,6 +626,71 @@ int kvc_decode_noalloc(const void* h_header, const void* d_in, uint64_t in_bytes
     return kvc_decode_result(ws, stream, nullptr);
 }
 
+int kvc_reload(int64_t n, const void* const* h_streams, const uint64_t* h_stream_bytes, const void* d_mu,
+               uint64_t mu_stride, const float* d_sigma, uint64_t sigma_stride, const uint32_t* d_prefix,
+               uint64_t prefix_bytes, void* d_kv_out, uint64_t kv_stride, void* d_staging, uint64_t staging_bytes,
+               void* d_workspace, uint64_t workspace_bytes, void* stream, void* copy_stream, int64_t* h_failed) {
+    if (h_failed) *h_failed = -1;
+    if (n < 1 || !h_streams || !h_stream_bytes || !d_staging || !d_workspace || !aligned(d_staging, 256) ||
+        !aligned(d_workspace, 256))
+        return KVC_ERR_INVALID;
+    if (workspace_bytes / KVC_DECODE_WORKSPACE_BYTES < uint64_t(n)) return KVC_ERR_CAPACITY;
+    // two staging halves, each 256-byte aligned; every stream must fit one
+    const uint64_t half = (staging_bytes / 2) & ~uint64_t(255);
+    for (int64_t l = 0; l < n; ++l) {
+        if (!h_streams[l] || h_stream_bytes[l] < KVC_HEADER_BYTES) return KVC_ERR_CORRUPT;
+        if (h_stream_bytes[l] > half) return KVC_ERR_CAPACITY;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(copy_stream);
+    hipEvent_t copied[2] = {}, consumed[2] = {};
+    int st = KVC_OK;
+    for (int i = 0; i < 2 && st == KVC_OK; ++i)
+        if (hipEventCreateWithFlags(&copied[i], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&consumed[i], hipEventDisableTiming) != hipSuccess)
+            st = KVC_ERR_DEVICE;
+    uint8_t* stage = static_cast<uint8_t*>(d_staging);
+    uint8_t* ws = static_cast<uint8_t*>(d_workspace);
+    int64_t queued = 0;
+    for (int64_t l = 0; l < n && st == KVC_OK; ++l) {
+        const int h = static_cast<int>(l & 1);
+        uint8_t* buf = stage + h * half;
+        // the half is free once the decode two layers back has read it
+        if (l >= 2 && hipStreamWaitEvent(cs, consumed[h], 0) != hipSuccess) { st = KVC_ERR_DEVICE; break; }
+        if (hipMemcpyAsync(buf, h_streams[l], h_stream_bytes[l], hipMemcpyHostToDevice, cs) != hipSuccess ||
+            hipEventRecord(copied[h], cs) != hipSuccess || hipStreamWaitEvent(s, copied[h], 0) != hipSuccess) {
+            st = KVC_ERR_DEVICE;
+            break;
+        }
+        const uint8_t* mu = static_cast<const uint8_t*>(d_mu) + uint64_t(l) * mu_stride;
+        const uint8_t* sg = reinterpret_cast<const uint8_t*>(d_sigma) + uint64_t(l) * sigma_stride;
+        uint8_t* out = static_cast<uint8_t*>(d_kv_out) + uint64_t(l) * kv_stride;
+        // the header is read in host memory: no device round trip
+        st = decode_launch(h_streams[l], buf, h_stream_bytes[l], mu, mu_stride, reinterpret_cast<const float*>(sg),
+                           sigma_stride, d_prefix, prefix_bytes, out, kv_stride, nullptr,
+                           ws + uint64_t(l) * KVC_DECODE_WORKSPACE_BYTES, KVC_DECODE_WORKSPACE_BYTES, stream, nullptr);
+        if (st != KVC_OK) {
+            if (h_failed) *h_failed = l;
+            break;
+        }
+        if (hipEventRecord(consumed[h], s) != hipSuccess) st = KVC_ERR_DEVICE;
+        ++queued;
+    }
+    // whatever was queued finishes before the events go and the statuses are read
+    if (hipStreamSynchronize(s) != hipSuccess || hipStreamSynchronize(cs) != hipSuccess) st = KVC_ERR_DEVICE;
+    for (int i = 0; i < 2; ++i) {
+        if (copied[i]) (void)hipEventDestroy(copied[i]);
+        if (consumed[i]) (void)hipEventDestroy(consumed[i]);
+    }
+    for (int64_t l = 0; l < queued && st == KVC_OK; ++l) {
+        const int ls = kvc_decode_result(ws + uint64_t(l) * KVC_DECODE_WORKSPACE_BYTES, stream, nullptr);
+        if (ls != KVC_OK) {
+            st = ls;
+            if (h_failed) *h_failed = l;
+        }
+    }
+    return st;
+}
+
 int kvc_decode_paged(const void* h_header, const void* d_in, uint64_t in_bytes, const void* d_mu, uint64_t mu_bytes,
                      const float* d_sigma, uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
                      const kvc_paged_kv* h_paged, void* d_workspace, uint64_t workspace_bytes, void* stream,

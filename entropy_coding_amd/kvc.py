@@ -30,7 +30,7 @@ DECODE_STAGES = 2     # side-information checksum + escape bucket table, decodin
 EXPORTS = [
     "kvc_version", "kvc_status_string", "kvc_phi_tables", "kvc_narrow_table", "kvc_encode_sizes", "kvc_encode", "kvc_encode_result",
     "kvc_stream_info", "kvc_decode", "kvc_decode_async", "kvc_decode_result", "kvc_decode_noalloc",
-    "kvc_decode_paged",
+    "kvc_decode_paged", "kvc_reload",
     "kvc_calibrate_sigma", "kvc_calibrate_sigma_blocks", "kvc_calibrate_sigma_rate",
     "kvc_build_marginal", "kvc_estimate_bits", "kvc_cdf_table",
 ]
@@ -95,6 +95,9 @@ _DECODE_ARGS = [_P, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P, _U64, 
 _lib_decode = _sig("kvc_decode", ctypes.c_int, _DECODE_ARGS + [_P])
 _lib_decode_async = _sig("kvc_decode_async", ctypes.c_int, _DECODE_ARGS)
 _lib_decode_result = _sig("kvc_decode_result", ctypes.c_int, [_P, _P, _P])
+_lib_reload = _sig("kvc_reload", ctypes.c_int,
+                   [_I64, _P, _P, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P, _P,
+                    ctypes.POINTER(_I64)])
 _lib_decode_noalloc = _sig("kvc_decode_noalloc", ctypes.c_int, [_P, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P, _U64, _P])
 _lib_decode_paged = _sig("kvc_decode_paged", ctypes.c_int,
                          [_P, _P, _U64, _P, _U64, _P, _U64, _P, _U64, ctypes.POINTER(kvc_paged_kv), _P, _U64, _P, _P])
@@ -358,6 +361,39 @@ def kvc_decode_noalloc(stream_bytes, mu, sigma, prefix, kv_out, stream=None, hea
     return _lib_decode_noalloc(h.ctypes.data, _ptr(stream_bytes), stream_bytes.numel(), _ptr(mu), _nbytes(mu),
                                _ptr(sigma), _nbytes(sigma), _ptr(prefix), _nbytes(prefix), _ptr(kv_out),
                                _nbytes(kv_out), _stream(stream))
+
+
+def kvc_reload(host_streams, mu: torch.Tensor, sigma: torch.Tensor, prefix, kv_out: torch.Tensor,
+               staging: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None,
+               copy_stream=None):
+    """Decode the per-layer streams in `host_streams` (uint8 CPU tensors,
+    pinned for asynchronous copies) into kv_out[l], with mu[l], sigma[l] and
+    the shared prefix; copies overlap the decodes (the library's pipeline).
+    Returns (status, index of the first failing layer or -1)."""
+    n = len(host_streams)
+    for t in host_streams:
+        if t.is_cuda or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("host streams must be contiguous uint8 CPU tensors")
+    for t, nm in ((mu, "mu"), (sigma, "sigma"), (kv_out, "kv_out")):
+        _need(t, nm)
+        if t.shape[0] != n:
+            raise ValueError(f"{nm} must have one entry per stream")
+    dev = kv_out.device
+    if staging is None:
+        half = max(t.numel() for t in host_streams) + 255
+        staging = torch.empty(2 * (half // 256 * 256 + 256), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty(n * DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    if copy_stream is None:
+        copy_stream = torch.cuda.Stream(device=dev)
+    ptrs = (ctypes.c_void_p * n)(*[t.data_ptr() for t in host_streams])
+    sizes = (ctypes.c_uint64 * n)(*[t.numel() for t in host_streams])
+    failed = _I64(-1)
+    st = _lib_reload(n, ptrs, sizes, _ptr(mu), _nbytes(mu) // n, _ptr(sigma), _nbytes(sigma) // n, _ptr(prefix),
+                     _nbytes(prefix), _ptr(kv_out), _nbytes(kv_out) // n, _ptr(staging), _nbytes(staging),
+                     _ptr(workspace), _nbytes(workspace), _stream(stream), copy_stream.cuda_stream,
+                     ctypes.byref(failed))
+    return st, failed.value
 
 
 class PagedKV:

@@ -255,6 +255,32 @@ int kvc_decode_noalloc(const void* h_header, const void* d_in, uint64_t in_bytes
                        void* d_kv_out, uint64_t kv_out_bytes, void* stream);
 
 /*
+ * Host-offload reload ([wiki] "use scenarios": KV offloaded from DRAM to
+ * VRAM; [blog] "application scenarios and deployment parameters": KV moved
+ * over PCIe in compressed form, decoding fast enough to keep up with the
+ * transfer).  Decodes n KVC-1 streams held in HOST memory (h_streams[l],
+ * h_stream_bytes[l] bytes; pinned memory, e.g. from hipHostMalloc, lets the
+ * copies run asynchronously) into device memory, one stream per layer: the
+ * copy of stream l + 1 to the device runs on copy_stream while stream l is
+ * decoded on `stream`, through two halves of d_staging (each 256-byte
+ * aligned, staging_bytes / 2 rounded down to 256: every stream must fit one,
+ * else KVC_ERR_CAPACITY).  Stream l decodes with the mu at d_mu + l x
+ * mu_stride, the sigma at d_sigma + l x sigma_stride bytes and the shared
+ * d_prefix, into d_kv_out + l x kv_stride; each stride is also the bytes
+ * available there, checked against the stream's header as kvc_decode checks
+ * its buffers.  Headers are read in host memory.  Workspace: n x
+ * KVC_DECODE_WORKSPACE_BYTES, 256-byte aligned (one decode workspace per
+ * layer).  Synchronises `stream` and `copy_stream` once at the end and
+ * returns the first failing layer's status (KVC_OK when all decode), its
+ * index in *h_failed (-1 if none; may be NULL).
+ */
+int kvc_reload(int64_t n, const void* const* h_streams, const uint64_t* h_stream_bytes,
+               const void* d_mu, uint64_t mu_stride, const float* d_sigma, uint64_t sigma_stride,
+               const uint32_t* d_prefix, uint64_t prefix_bytes, void* d_kv_out, uint64_t kv_stride,
+               void* d_staging, uint64_t staging_bytes, void* d_workspace, uint64_t workspace_bytes,
+               void* stream, void* copy_stream, int64_t* h_failed);
+
+/*
  * Outcome of the last decode queued with this workspace: synchronises
  * `stream` once and returns the status kvc_decode would have returned;
  * h_info (may be NULL) receives the fallback count (stage times are -1).
