@@ -349,20 +349,31 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     uint8_t* ws = static_cast<uint8_t*>(d_workspace);
     Control* ctl = reinterpret_cast<Control*>(ws);
     const uint32_t* prefix = te ? d_prefix : nullptr;
+    // the mixture table: the device's cached one, else built here
+    const uint32_t* table = nullptr;
+    const float* no_aim = nullptr;
+    if (!kvc::cached_coder_tables(tn, tw, p->narrow_dof, phi, s, &table, &no_aim, &e)) {
+        if (e != hipSuccess) return KVC_ERR_DEVICE;
+        table = reinterpret_cast<const uint32_t*>(ws + l.table);
+        if ((e = kvc::launch_coder_tables(phi, tn, tw, reinterpret_cast<uint32_t*>(ws + l.table), nullptr, s)) !=
+            hipSuccess)
+            return KVC_ERR_DEVICE;
+    }
     StageTimer timer(h_info ? h_info->stage_ms : nullptr, KVC_ENCODE_STAGES, s);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(0);
-    const kvc::StreamHeader no_header{};
-    if ((e = kvc::launch_side_hash(d_sigma, sigma_words(g), prefix, prefix ? alphabet(p->kv_dtype) + 1u : 0u, nullptr,
-                                   no_header, ctl, s)) != hipSuccess)
-        return KVC_ERR_DEVICE;
-    if ((e = kvc::launch_coder_tables(phi, tn, tw, reinterpret_cast<uint32_t*>(ws + l.table), nullptr, s)) !=
-        hipSuccess)
-        return KVC_ERR_DEVICE;
-    if (p->kv_dtype == KVC_BF16 &&
-        (e = kvc::launch_escape_slots(prefix ? prefix : phi.zero, tn + tw, reinterpret_cast<uint32_t*>(ws + l.eslots),
-                                      nullptr, s)) != hipSuccess)
-        return KVC_ERR_DEVICE;
+    kvc::PrologueArgs pa;
+    pa.sigma_words = reinterpret_cast<const uint32_t*>(d_sigma);
+    pa.n_sigma = sigma_words(g);
+    pa.prefix_words = prefix;
+    pa.n_prefix = prefix ? alphabet(p->kv_dtype) + 1u : 0u;
+    pa.prefix = prefix ? prefix : phi.zero;
+    pa.htot = tn + tw;
+    if (p->kv_dtype == KVC_BF16) pa.eslots = reinterpret_cast<uint2*>(ws + l.eslots);
+    pa.zero = reinterpret_cast<unsigned long long*>(ws + l.status);
+    pa.n_zero = uint64_t(g.n_chunks);
+    pa.ctl = ctl;
+    if ((e = kvc::launch_prologue(pa, p->kv_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
 
     kvc::EncodeArgs ea;
     ea.geom = g;
@@ -372,7 +383,7 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     ea.prefix = prefix ? prefix : phi.zero;          // kernels read a prefix unconditionally
     ea.tn = tn;
     ea.tw = tw;
-    ea.table = reinterpret_cast<const uint32_t*>(ws + l.table);
+    ea.table = table;
     ea.eslots = reinterpret_cast<const uint32_t*>(ws + l.eslots);
     ea.slots = reinterpret_cast<uint16_t*>(ws + l.slots);
     ea.slot_words = l.slot_words;
@@ -382,7 +393,6 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     ea.header = make_header(p, g, tn, tw, te);
     ea.header_copy = ws + kvc::kHeaderCopyOffset;
     ea.ctl = ctl;
-    if ((e = kvc::launch_zero(ea.status, uint64_t(g.n_chunks), s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(1);
     if ((e = kvc::launch_encode(ea, p->kv_dtype, p->mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(2);
@@ -509,28 +519,41 @@ int decode_launch(const void* h_header, const void* d_in, uint64_t in_bytes, con
     while (((q_total - 1) >> shift) + 2 > kvc::kEscapeBucketsMax) ++shift;
     const uint32_t n_buckets = static_cast<uint32_t>(((q_total - 1) >> shift) + 2);
     uint32_t* buckets = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d_workspace) + kDecodeBucketOffset);
-    kvc::StreamHeader expect;
-    std::memcpy(expect.bytes, h_header, KVC_HEADER_BYTES);
+    uint8_t* ws = static_cast<uint8_t*>(d_workspace);
+    // the mixture and aim tables: the device's cached ones, else built here
+    const uint32_t* table = nullptr;
+    const float* aim = nullptr;
+    if (!kvc::cached_coder_tables(tn, tw, p.narrow_dof, phi, s, &table, &aim, &e)) {
+        if (e != hipSuccess) return KVC_ERR_DEVICE;
+        table = reinterpret_cast<const uint32_t*>(ws + kDecodeTableOffset);
+        aim = reinterpret_cast<const float*>(ws + kDecodeAimOffset);
+        if ((e = kvc::launch_coder_tables(phi, tn, tw, reinterpret_cast<uint32_t*>(ws + kDecodeTableOffset),
+                                          reinterpret_cast<float*>(ws + kDecodeAimOffset), s)) != hipSuccess)
+            return KVC_ERR_DEVICE;
+    }
     StageTimer timer(stage_ms, KVC_DECODE_STAGES, s);
     if ((e = kvc::launch_clear_control(ctl, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(0);
-    if ((e = kvc::launch_side_hash(d_sigma, sigma_words(g), prefix, prefix ? n_sym + 1u : 0u,
-                                   static_cast<const uint8_t*>(d_in), expect, ctl, s)) != hipSuccess)
-        return KVC_ERR_DEVICE;
-    if (paged && (e = kvc::launch_check_pages(po, (g.tokens + po.page_tokens - 1) / po.page_tokens, ctl, s)) !=
-                     hipSuccess)
-        return KVC_ERR_DEVICE;
-    if ((e = kvc::launch_escape_buckets(prefix ? prefix : phi.zero, n_sym, shift, n_buckets, p.kv_dtype, buckets, s)) !=
-        hipSuccess)
-        return KVC_ERR_DEVICE;
-    uint8_t* ws = static_cast<uint8_t*>(d_workspace);
-    if ((e = kvc::launch_coder_tables(phi, tn, tw, reinterpret_cast<uint32_t*>(ws + kDecodeTableOffset),
-                                      reinterpret_cast<float*>(ws + kDecodeAimOffset), s)) != hipSuccess)
-        return KVC_ERR_DEVICE;
-    if (p.kv_dtype == KVC_BF16 &&
-        (e = kvc::launch_escape_slots(prefix ? prefix : phi.zero, tn + tw, nullptr,
-                                      reinterpret_cast<uint32_t*>(ws + kDecodeCountOffset), s)) != hipSuccess)
-        return KVC_ERR_DEVICE;
+    kvc::PrologueArgs pa;
+    pa.sigma_words = reinterpret_cast<const uint32_t*>(d_sigma);
+    pa.n_sigma = sigma_words(g);
+    pa.prefix_words = prefix;
+    pa.n_prefix = prefix ? n_sym + 1u : 0u;
+    pa.head = static_cast<const uint8_t*>(d_in);
+    std::memcpy(pa.expect.bytes, h_header, KVC_HEADER_BYTES);
+    pa.prefix = prefix ? prefix : phi.zero;
+    pa.htot = tn + tw;
+    if (p.kv_dtype == KVC_BF16) pa.ecount = reinterpret_cast<uint32_t*>(ws + kDecodeCountOffset);
+    pa.buckets = reinterpret_cast<uint2*>(buckets);
+    pa.n_sym = n_sym;
+    pa.bucket_shift = shift;
+    pa.n_buckets = n_buckets;
+    if (paged) {
+        pa.pages = po;
+        pa.pages_used = (g.tokens + po.page_tokens - 1) / po.page_tokens;
+    }
+    pa.ctl = ctl;
+    if ((e = kvc::launch_prologue(pa, p.kv_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(1);
     const uint8_t* in = static_cast<const uint8_t*>(d_in);
     kvc::DecodeArgs da;
@@ -543,8 +566,8 @@ int decode_launch(const void* h_header, const void* d_in, uint64_t in_bytes, con
     da.prefix = prefix ? prefix : phi.zero;
     da.tn = tn;
     da.tw = tw;
-    da.table = reinterpret_cast<const uint32_t*>(ws + kDecodeTableOffset);
-    da.aim = reinterpret_cast<const float*>(ws + kDecodeAimOffset);
+    da.table = table;
+    da.aim = aim;
     da.buckets = buckets;
     da.bucket_shift = shift;
     da.ecount = reinterpret_cast<const uint32_t*>(ws + kDecodeCountOffset);

@@ -158,9 +158,9 @@ struct Model {
     const uint32_t* __restrict__ tab;      // mixture table in LDS
     const uint32_t* __restrict__ prefix;   // escape prefix (N + 1 entries; zeros without an escape part)
     const uint32_t* small;                 // e4m3 only: prefix and edges in LDS
-    const uint32_t* __restrict__ eslots;   // bf16 encoder only: the escape slot table (k_escape_slots)
+    const uint32_t* __restrict__ eslots;   // bf16 encoder only: the escape slot table (k_prologue)
     uint32_t htot;                         // T_n + T_w, where the floor-and-escape range starts
-    const uint32_t* __restrict__ ecount;   // bf16 decoder only: the escape count table (k_escape_slots)
+    const uint32_t* __restrict__ ecount;   // bf16 decoder only: the escape count table (k_prologue)
 };
 
 // Two consecutive u32 at byte offset `off` of `base` in one 8-byte read

@@ -72,7 +72,7 @@ struct EncodeArgs {
     const uint32_t* prefix;             // escape prefix; the zero table when there is no escape part
     uint32_t tn, tw;
     const uint32_t* table;              // the mixture table (launch_coder_tables)
-    const uint32_t* eslots;             // bf16: the escape slot table (launch_escape_slots)
+    const uint32_t* eslots;             // bf16: the escape slot table (launch_prologue)
     uint16_t* slots;                    // per-chunk word slots, filled from the end
     uint64_t slot_words;                // words per slot (2 per scalar, multiple of 4)
     unsigned long long* status;         // [n_chunks] chunk sizes for the look-back, zeroed
@@ -82,8 +82,6 @@ struct EncodeArgs {
     uint8_t* header_copy;               // the workspace's copy of the finished header
     Control* ctl;
 };
-
-
 
 // Decoded rows written straight into paged KV pools: pool (layer, kv) is
 // [num_pages][page_tokens][heads][channels]; plane g = ((layer * 2 + kv) *
@@ -108,9 +106,9 @@ struct DecodeArgs {
     uint32_t tn, tw;
     const uint32_t* table;              // the mixture table (launch_coder_tables)
     const float* aim;                   // the aim table, kAimFloats floats
-    const uint32_t* buckets;            // escape bucket table (launch_escape_buckets)
+    const uint32_t* buckets;            // escape bucket table (launch_prologue)
     uint32_t bucket_shift;
-    const uint32_t* ecount;             // bf16: the escape count table (launch_escape_slots),
+    const uint32_t* ecount;             // bf16: the escape count table (launch_prologue),
                                         // with the bucket table right after it
     void* kv_out;                       // contiguous output [planes][tokens][channels], or
     PagedOut paged;                     // the paged output (launch_decode with paged = true)
@@ -153,25 +151,49 @@ hipError_t launch_clear_control(Control* ctl, hipStream_t s);
 // when `aim` is not null, the decoder's aim table (kAimBytes).
 hipError_t launch_coder_tables(const PhiTables& phi, uint32_t tn, uint32_t tw, uint32_t* table, float* aim,
                                hipStream_t s);
-// Side-information checksum into ctl->side_hash; with `head` not null (a
-// decode), also compares the device stream's first 128 bytes with the host
-// copy `expect` and raises kFlagHeader when they differ.
-hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t* prefix,
-                            uint64_t n_prefix, const uint8_t* head, const StreamHeader& expect, Control* ctl,
-                            hipStream_t s);
 hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);
-// Zeroes n 8-byte words (a kernel, so that the call can be captured in a graph).
-hipError_t launch_zero(unsigned long long* p, uint64_t n, hipStream_t s);
+// Per-call preparation in one launch (after launch_clear_control): the
+// side-information checksum of sigma_words and prefix_words (and, with head
+// not null, the comparison of the device stream's header with `expect`);
+// the bf16 escape slot table (eslots) and/or escape count table (ecount)
+// from `prefix`; the escape bucket table (buckets); zeroing n_zero words at
+// zero; the check of pages_used columns of a paged decode's block table.
+// Null outputs skip their part; the block counts are filled in by the launch.
+struct PrologueArgs {
+    const uint32_t* sigma_words = nullptr;
+    uint64_t n_sigma = 0;
+    const uint32_t* prefix_words = nullptr;   // the checksum's prefix words (null without an escape part)
+    uint64_t n_prefix = 0;
+    const uint8_t* head = nullptr;
+    StreamHeader expect{};
+    const uint32_t* prefix = nullptr;         // the prefix the tables read (the zero table without one)
+    uint32_t htot = 0;
+    uint2* eslots = nullptr;
+    uint32_t* ecount = nullptr;
+    uint2* buckets = nullptr;
+    uint32_t n_sym = 0, bucket_shift = 0, n_buckets = 0;
+    unsigned long long* zero = nullptr;
+    uint64_t n_zero = 0;
+    PagedOut pages{};                         // block_table null: no check
+    int64_t pages_used = 0;
+    Control* ctl = nullptr;
+    uint32_t hash_blocks = 0, slot_blocks = 0, bucket_blocks = 0, zero_blocks = 0, page_blocks = 0;
+};
+hipError_t launch_prologue(PrologueArgs a, int kv_dtype, hipStream_t s);
+// The mixture and aim tables of (tn, tw, narrow_dof) from the per-device
+// cache, built there on first use (synchronising s once); false when the
+// cache is full (then the caller builds them itself) or on an error (*err).
+bool cached_coder_tables(uint32_t tn, uint32_t tw, uint32_t narrow_dof, const PhiTables& phi, hipStream_t s,
+                         const uint32_t** table, const float** aim, hipError_t* err);
+
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, bool paged, hipStream_t s);
-// Sets kFlagBadPage if a block-table entry of columns [0, used) lies outside the pool.
-hipError_t launch_check_pages(const PagedOut& p, int64_t used, Control* ctl, hipStream_t s);
+
 // Bucket table of Q(b) = b + prefix[b] for the decoder's floor-and-escape
 // lookup, two u32 per entry: entry j = ((s_j << 16) | pattern of s_j,
 // Q(s_j)), where s_j is the largest s < n_sym with Q(s) <= j << shift
 // (entries order as their symbols).
 constexpr uint32_t kEscapeBucketsMax = 65538;
-hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_t shift, uint32_t n_entries,
-                                 int kv_dtype, uint32_t* bucket, hipStream_t s);
+
 // Escape slot table of the bf16 alphabet, indexed by bit pattern p (s its
 // ordered index): entry p = (T_n + T_w + Q(s), Q(s + 1) - Q(s)), two u32,
 // so the encoder finds the start and the count of a symbol's
@@ -181,7 +203,7 @@ hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_
 // gives it.  Either output may be null.
 constexpr uint64_t kEscapeSlotsBytes = 65536ull * 8;
 constexpr uint64_t kEscapeCountBytes = 65536ull * 4;
-hipError_t launch_escape_slots(const uint32_t* prefix, uint32_t htot, uint32_t* out, uint32_t* count, hipStream_t s);
+
 // sigma calibration: float64 partial sums per (split, plane, channel)
 struct CalibPart {
     double sum;

@@ -264,40 +264,6 @@ __device__ __forceinline__ unsigned long long mix64(unsigned long long z) {
     return z ^ (z >> 31);
 }
 
-__global__ void __launch_bounds__(256) k_side_hash(const uint32_t* __restrict__ sigma_words, uint64_t n1,
-                                                   const uint32_t* __restrict__ prefix, uint64_t n2,
-                                                   const uint8_t* __restrict__ head, StreamHeader expect,
-                                                   Control* ctl) {
-    if (head != nullptr && blockIdx.x == 0 && threadIdx.x < kHeaderBytes / 8) {
-        unsigned long long w, e;
-        __builtin_memcpy(&w, head + 8 * threadIdx.x, 8);
-        __builtin_memcpy(&e, expect.bytes + 8 * threadIdx.x, 8);
-        if (w != e) atomicOr(&ctl->flags, kFlagHeader);
-    }
-    const unsigned long long golden = 0x9E3779B97F4A7C15ull;
-    unsigned long long acc = 0;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
-    for (uint64_t j = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; j < n1 + n2; j += stride) {
-        unsigned long long i, w, tag;
-        if (j < n1) { i = j; w = sigma_words[j]; tag = 1; }
-        else { i = j - n1; w = prefix[j - n1]; tag = 2; }
-        acc += mix64(((i << 32) | w) + tag * golden);
-    }
-    acc = wave_sum_u64(acc);
-    if ((threadIdx.x & 63) == 0 && acc) atomicAdd(&ctl->side_hash, acc);
-}
-
-hipError_t launch_side_hash(const float* sigma, uint64_t n_sigma, const uint32_t* prefix,
-                            uint64_t n_prefix, const uint8_t* head, const StreamHeader& expect, Control* ctl,
-                            hipStream_t s) {
-    const uint64_t n = n_sigma + n_prefix;
-    uint64_t blocks = (n + 255) / 256;
-    if (blocks > 512) blocks = 512;
-    if (blocks == 0) blocks = 1;
-    hipLaunchKernelGGL(k_side_hash, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s,
-                       reinterpret_cast<const uint32_t*>(sigma), n_sigma, prefix, n_prefix, head, expect, ctl);
-    return hipGetLastError();
-}
 
 
 // ---------------------------------------------------------------------------
@@ -985,51 +951,11 @@ __device__ __forceinline__ uint32_t coop_gauss(bool need, uint32_t target, float
 // of s_j at once), then Q(s_j).  A slot y in the floor-and-escape range has
 // its symbol in [s_(y >> shift), s_((y >> shift) + 1)].  The shift is the
 // smallest that keeps the table within kEscapeBucketsMax entries.
-template <int KV>
-__global__ void __launch_bounds__(256) k_escape_buckets(const uint32_t* __restrict__ prefix, uint32_t n_sym,
-                                                        uint32_t shift, uint32_t n_entries,
-                                                        uint2* __restrict__ bucket) {
-    const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= n_entries) return;
-    const unsigned long long y = static_cast<unsigned long long>(j) << shift;
-    uint32_t lo = 0, hi = n_sym - 1;
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi + 1u) >> 1;
-        if (static_cast<unsigned long long>(mid) + prefix[mid] <= y) lo = mid;
-        else hi = mid - 1u;
-    }
-    bucket[j] = make_uint2((lo << 16) | candidate_bits<KV>(candidate_of_index<KV>(lo)), lo + prefix[lo]);
-}
-
-hipError_t launch_escape_buckets(const uint32_t* prefix, uint32_t n_sym, uint32_t shift, uint32_t n_entries,
-                                 int kv_dtype, uint32_t* bucket, hipStream_t s) {
-    const dim3 grid((n_entries + 255) / 256), block(256);
-    if (kv_dtype == kBF16)
-        hipLaunchKernelGGL(k_escape_buckets<kBF16>, grid, block, 0, s, prefix, n_sym, shift, n_entries,
-                           reinterpret_cast<uint2*>(bucket));
-    else hipLaunchKernelGGL(k_escape_buckets<kE4M3>, grid, block, 0, s, prefix, n_sym, shift, n_entries,
-                            reinterpret_cast<uint2*>(bucket));
-    return hipGetLastError();
-}
 
 // Escape slot table: entry p of the bf16 pattern p, with s its ordered
 // index, holds T_n + T_w + Q(s) and Q(s + 1) - Q(s), Q(b) = b + prefix[b];
 // the escape count table holds Q(s + 1) - Q(s) alone.  Either output may be
 // null.  One thread per pattern; the grid covers the 65536 patterns exactly.
-__global__ void __launch_bounds__(256) k_escape_slots(const uint32_t* __restrict__ prefix, uint32_t htot,
-                                                      uint2* __restrict__ out, uint32_t* __restrict__ count) {
-    const uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;
-    const uint32_t s = order_of_bits<kBF16>(p);
-    const uint32_t p0 = prefix[s], p1 = prefix[s + 1u];
-    if (out) out[p] = make_uint2(htot + s + p0, 1u + (p1 - p0));
-    if (count) count[p] = 1u + (p1 - p0);
-}
-
-hipError_t launch_escape_slots(const uint32_t* prefix, uint32_t htot, uint32_t* out, uint32_t* count, hipStream_t s) {
-    hipLaunchKernelGGL(k_escape_slots, dim3(65536 / 256), dim3(256), 0, s, prefix, htot, reinterpret_cast<uint2*>(out),
-                       count);
-    return hipGetLastError();
-}
 
 // The symbol of escape offset y within [lo, hi]: binary search for the
 // largest s with Q(s) = s + prefix[s] <= y (e4m3: the LDS prefix), with
@@ -1245,7 +1171,7 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(8
     // (this chunk's 64 channels of head h), a token further each step; at a
     // page boundary the next entry of the sequence's table row names the
     // page.  Every entry the call reads was checked before the launch
-    // (k_check_pages; the decode does nothing when one is bad).  The wave
+    // (by the prologue; the decode does nothing when one is bad).  The wave
     // stages kPageWindow entries of its table row at a time in LDS, so a
     // page boundary reads LDS rather than waiting on a global read (whose
     // wait would also cover the row stores in flight).  Reads of the pool
@@ -1469,21 +1395,6 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(8
 // Every block-table entry a paged decode reads (rows 0..batch-1, columns
 // 0..used-1) must name a page of the pool; one that does not sets the flag
 // the decoder reads before its first store.
-__global__ void __launch_bounds__(256) k_check_pages(const int32_t* __restrict__ table, int64_t batch,
-                                                     int64_t max_pages, int64_t used, int64_t num_pages,
-                                                     Control* __restrict__ ctl) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= batch * used) return;
-    const int32_t e = table[(i / used) * max_pages + i % used];
-    if (e < 0 || int64_t(e) >= num_pages) atomicOr(&ctl->flags, kFlagBadPage);
-}
-
-hipError_t launch_check_pages(const PagedOut& p, int64_t used, Control* ctl, hipStream_t s) {
-    const int64_t n = int64_t(p.batch) * used;
-    hipLaunchKernelGGL(k_check_pages, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s, p.block_table,
-                       int64_t(p.batch), p.max_pages, used, p.num_pages, ctl);
-    return hipGetLastError();
-}
 
 template <bool PAGED>
 hipError_t launch_decode_as(const DecodeArgs& a, int kv_dtype, int mu_dtype, dim3 grid, dim3 block, hipStream_t s) {
@@ -1815,17 +1726,6 @@ __global__ void __launch_bounds__(THREADS) k_marginal_prefix(uint32_t* __restric
     if (tid == THREADS - 1) hist[N] = te;
 }
 
-__global__ void k_zero_u64(unsigned long long* __restrict__ p, uint64_t n) {
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
-    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0ull;
-}
-
-hipError_t launch_zero(unsigned long long* p, uint64_t n, hipStream_t s) {
-    uint64_t blocks = (n + 255) / 256;
-    blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
-    hipLaunchKernelGGL(k_zero_u64, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, p, n);
-    return hipGetLastError();
-}
 
 hipError_t launch_marginal(const void* samples, int dtype, uint64_t n, uint32_t te, uint32_t* prefix_out,
                            hipStream_t s) {
@@ -1956,6 +1856,162 @@ hipError_t launch_cdf_table(int kv_dtype, int mu_dtype, uint32_t tn, uint32_t tw
     else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_cdf_table<kE4M3, kBF16>), grid, block, 0, s, mu, sigma, pairs, tn, tw, prefix, out, phi);
     else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_cdf_table<kE4M3, kF32>), grid, block, 0, s, mu, sigma, pairs, tn, tw, prefix, out, phi);
     else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace kvc
+
+namespace kvc {
+
+// ---------------------------------------------------------------------------
+// Per-device cache of the coder tables: the mixture table and the decoder's
+// aim table depend only on the budgets (T_n, T_w) and the narrow part, not
+// on the data, so each combination a process uses is built once per device
+// (a kernel and a synchronisation of the calling stream, on first use) and
+// only read afterwards.  A call whose combination finds no free slot builds
+// its tables in its own workspace as before.
+// ---------------------------------------------------------------------------
+constexpr int kTabCacheSlots = 8;
+__device__ __align__(16) uint32_t g_tab_cache[kTabCacheSlots][kTableWordsPadded];
+__device__ __align__(16) float g_aim_cache[kTabCacheSlots][kAimFloats];
+
+namespace {
+struct TabKey {
+    uint32_t tn, tw, dof;
+    bool used;
+};
+std::mutex g_tab_mutex;
+TabKey g_tab_keys[kMaxDevices][kTabCacheSlots];
+uint32_t* g_tab_dev[kMaxDevices];
+float* g_aim_dev[kMaxDevices];
+}  // namespace
+
+bool cached_coder_tables(uint32_t tn, uint32_t tw, uint32_t narrow_dof, const PhiTables& phi, hipStream_t s,
+                         const uint32_t** table, const float** aim, hipError_t* err) {
+    *err = hipSuccess;
+    int dev = 0;
+    if ((*err = hipGetDevice(&dev)) != hipSuccess) return false;
+    if (dev < 0 || dev >= kMaxDevices) return false;
+    std::lock_guard<std::mutex> lock(g_tab_mutex);
+    if (!g_tab_dev[dev]) {
+        void* pt = nullptr;
+        void* pa = nullptr;
+        if ((*err = hipGetSymbolAddress(&pt, HIP_SYMBOL(g_tab_cache))) != hipSuccess) return false;
+        if ((*err = hipGetSymbolAddress(&pa, HIP_SYMBOL(g_aim_cache))) != hipSuccess) return false;
+        g_tab_dev[dev] = static_cast<uint32_t*>(pt);
+        g_aim_dev[dev] = static_cast<float*>(pa);
+    }
+    int slot = -1;
+    for (int i = 0; i < kTabCacheSlots && slot < 0; ++i) {
+        const TabKey& k = g_tab_keys[dev][i];
+        if (k.used && k.tn == tn && k.tw == tw && k.dof == narrow_dof) slot = i;
+    }
+    if (slot < 0) {
+        for (int i = 0; i < kTabCacheSlots && slot < 0; ++i)
+            if (!g_tab_keys[dev][i].used) slot = i;
+        if (slot < 0) return false;                    // full: the caller builds its own
+        uint32_t* t = g_tab_dev[dev] + static_cast<size_t>(slot) * kTableWordsPadded;
+        float* a = g_aim_dev[dev] + static_cast<size_t>(slot) * kAimFloats;
+        if ((*err = launch_coder_tables(phi, tn, tw, t, a, s)) != hipSuccess) return false;
+        if ((*err = hipStreamSynchronize(s)) != hipSuccess) return false;
+        g_tab_keys[dev][slot] = TabKey{tn, tw, narrow_dof, true};
+    }
+    *table = g_tab_dev[dev] + static_cast<size_t>(slot) * kTableWordsPadded;
+    *aim = g_aim_dev[dev] + static_cast<size_t>(slot) * kAimFloats;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Per-call preparation in one launch: workgroups take one role each by
+// index range — the side-information checksum (with the decoder's header
+// comparison), the bf16 escape slot or count table, the escape bucket
+// table, the reset of the encoder's look-back entries, and the check of a
+// paged decode's block table.  The control block was cleared by the launch
+// before.
+// ---------------------------------------------------------------------------
+template <int KV>
+__global__ void __launch_bounds__(256) k_prologue(PrologueArgs a) {
+    uint32_t b = blockIdx.x;
+    const uint32_t tid = threadIdx.x;
+    if (b < a.hash_blocks) {
+        if (a.head != nullptr && b == 0 && tid < kHeaderBytes / 8) {
+            unsigned long long w, e;
+            __builtin_memcpy(&w, a.head + 8 * tid, 8);
+            __builtin_memcpy(&e, a.expect.bytes + 8 * tid, 8);
+            if (w != e) atomicOr(&a.ctl->flags, kFlagHeader);
+        }
+        __shared__ unsigned long long s_part[4];
+        const unsigned long long golden = 0x9E3779B97F4A7C15ull;
+        const uint64_t n1 = a.n_sigma, n = a.n_sigma + a.n_prefix;
+        const uint64_t stride = static_cast<uint64_t>(a.hash_blocks) * 256u;
+        unsigned long long acc = 0;
+        for (uint64_t j = static_cast<uint64_t>(b) * 256u + tid; j < n; j += stride) {
+            unsigned long long i, w, tag;
+            if (j < n1) { i = j; w = a.sigma_words[j]; tag = 1; }
+            else { i = j - n1; w = a.prefix_words[j - n1]; tag = 2; }
+            acc += mix64(((i << 32) | w) + tag * golden);
+        }
+        acc = wave_sum_u64(acc);
+        if ((tid & 63u) == 0) s_part[tid >> 6] = acc;
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned long long sum = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+            if (sum) atomicAdd(&a.ctl->side_hash, sum);
+        }
+        return;
+    }
+    b -= a.hash_blocks;
+    if (b < a.slot_blocks) {
+        // one thread per bf16 pattern p, s its ordered index
+        const uint32_t p = b * 256u + tid;
+        const uint32_t s = order_of_bits<kBF16>(p);
+        const uint32_t p0 = a.prefix[s], p1 = a.prefix[s + 1u];
+        if (a.eslots) a.eslots[p] = make_uint2(a.htot + s + p0, 1u + (p1 - p0));
+        if (a.ecount) a.ecount[p] = 1u + (p1 - p0);
+        return;
+    }
+    b -= a.slot_blocks;
+    if (b < a.bucket_blocks) {
+        const uint32_t j = b * 256u + tid;
+        if (j >= a.n_buckets) return;
+        const unsigned long long y = static_cast<unsigned long long>(j) << a.bucket_shift;
+        uint32_t lo = 0, hi = a.n_sym - 1;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1u) >> 1;
+            if (static_cast<unsigned long long>(mid) + a.prefix[mid] <= y) lo = mid;
+            else hi = mid - 1u;
+        }
+        a.buckets[j] = make_uint2((lo << 16) | candidate_bits<KV>(candidate_of_index<KV>(lo)), lo + a.prefix[lo]);
+        return;
+    }
+    b -= a.bucket_blocks;
+    if (b < a.zero_blocks) {
+        const uint64_t stride = static_cast<uint64_t>(a.zero_blocks) * 256u;
+        for (uint64_t i = static_cast<uint64_t>(b) * 256u + tid; i < a.n_zero; i += stride) a.zero[i] = 0ull;
+        return;
+    }
+    b -= a.zero_blocks;
+    if (b < a.page_blocks) {
+        const int64_t i = static_cast<int64_t>(b) * 256 + tid;
+        if (i >= a.pages.batch * a.pages_used) return;
+        const int32_t e = a.pages.block_table[(i / a.pages_used) * a.pages.max_pages + i % a.pages_used];
+        if (e < 0 || int64_t(e) >= a.pages.num_pages) atomicOr(&a.ctl->flags, kFlagBadPage);
+    }
+}
+
+hipError_t launch_prologue(PrologueArgs a, int kv_dtype, hipStream_t s) {
+    const uint64_t n = a.n_sigma + a.n_prefix;
+    uint64_t hb = (n + 255) / 256;
+    a.hash_blocks = static_cast<uint32_t>(hb < 1 ? 1 : (hb > 64 ? 64 : hb));
+    a.slot_blocks = (a.eslots || a.ecount) ? 65536u / 256u : 0u;
+    a.bucket_blocks = a.buckets ? (a.n_buckets + 255u) / 256u : 0u;
+    uint64_t zb = (a.n_zero + 255) / 256;
+    a.zero_blocks = a.zero ? static_cast<uint32_t>(zb < 1 ? 1 : (zb > 1024 ? 1024 : zb)) : 0u;
+    const int64_t np = a.pages.block_table ? int64_t(a.pages.batch) * a.pages_used : 0;
+    a.page_blocks = static_cast<uint32_t>((np + 255) / 256);
+    const uint32_t blocks = a.hash_blocks + a.slot_blocks + a.bucket_blocks + a.zero_blocks + a.page_blocks;
+    if (kv_dtype == kBF16) hipLaunchKernelGGL(k_prologue<kBF16>, dim3(blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_prologue<kE4M3>, dim3(blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
