@@ -496,8 +496,8 @@ def main():
         "decode_gbps": raw / (dec_total * 1e-3) / 1e9,
         "encode_ms": enc_total, "decode_ms": dec_total,
         "encode_stage_ms": {k: mean([s[0][i] for s in stats]) for i, k in
-                            enumerate(["side_hash_and_tables", "encode_kernel"])},
-        "decode_stage_ms": {k: mean([s[1][i] for s in stats]) for i, k in enumerate(["side_hash", "decode_kernel"])},
+                            enumerate(["prologue", "encode_kernel"])},
+        "decode_stage_ms": {k: mean([s[1][i] for s in stats]) for i, k in enumerate(["prologue", "decode_kernel"])},
         "bits_per_scalar": {"coded": 8.0 * stream_bytes / n, "integer_model": bits_int, "float_model": bits_float},
         "stream_bytes": stream_bytes,
         "decode_fallback_share": fallback[0] / n,
