@@ -61,5 +61,40 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+CHECKED_DIR = os.path.join(HERE, "_build", "checked")
+CHECKED_LIB = os.path.join(CHECKED_DIR, "libkvc_checked.so")
+
+
+def build_checked(verbose: bool = False) -> str:
+    """A second build for the CPU tests only: the C ABI layer compiled with
+    AddressSanitizer and UndefinedBehaviorSanitizer (g++; any finding aborts
+    the process), linked with the same device code into
+    _build/checked/libkvc_checked.so.  The host tests load it in a child
+    process that preloads the sanitizer runtime (the Python interpreter is
+    not built with it).  It is never loaded on a GPU."""
+    cc = hipcc()
+    os.makedirs(CHECKED_DIR, exist_ok=True)
+    rocm = os.path.dirname(os.path.dirname(cc))
+    kern = os.path.join(HERE, "_build", "kvc_kernels.o")     # the device code of build()
+    api = os.path.join(CHECKED_DIR, "kvc_api.o")
+    host_cxx = shutil.which("g++") or "g++"
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+    cmds = [] if os.path.exists(kern) else [[cc, *COMMON, *DEVICE, "-c", os.path.join(CSRC, "kvc_kernels.hip"), "-o", kern]]
+    cmds += [
+        [host_cxx, *[f for f in COMMON if f != "-O3"], "-O1", *san, "-D__HIP_PLATFORM_AMD__",
+         "-I" + os.path.join(rocm, "include"), "-Wall", "-Wextra", "-c", os.path.join(CSRC, "kvc_api.cpp"), "-o", api],
+        [host_cxx, "-shared", *san, kern, api, "-o", CHECKED_LIB + ".tmp", "-L" + os.path.join(rocm, "lib"),
+         "-Wl,-rpath," + os.path.join(rocm, "lib"), "-lamdhip64"],
+    ]
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        subprocess.run(cmd, check=True)
+    os.replace(CHECKED_LIB + ".tmp", CHECKED_LIB)
+    return CHECKED_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    if "--checked" in sys.argv:
+        print(build_checked(verbose=True))

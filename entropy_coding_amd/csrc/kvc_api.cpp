@@ -449,10 +449,23 @@ uint64_t mu_size(int32_t t) { return t == KVC_F32 ? 4u : 2u; }
 // the paged pools when `paged` is not null.  Everything is checked on the
 // host against the header the caller holds before anything is launched;
 // the kernels compare the device stream's header with it.
-int decode_launch(const void* h_header, const void* d_in, uint64_t in_bytes, const void* d_mu, uint64_t mu_bytes,
-                  const float* d_sigma, uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
-                  void* d_kv_out, uint64_t kv_out_bytes, const kvc_paged_kv* paged, void* d_workspace,
-                  uint64_t workspace_bytes, void* stream, float* stage_ms) {
+// What a decode call needs, from its host-side checks alone (no device call).
+struct DecodePlan {
+    kvc_params p;
+    ChunkGeom g;
+    uint64_t payload = 0, hash = 0, dir_bytes = 0;
+    uint32_t tn = 0, tw = 0, te = 0, n_sym = 0;
+    const uint32_t* prefix = nullptr;
+    kvc::PagedOut po{};
+};
+
+// Every check a decode makes before touching the device: arguments, the
+// header (CRC included), the stream's length against it, and every caller
+// buffer against what it describes.
+int decode_check(const void* h_header, const void* d_in, uint64_t in_bytes, const void* d_mu, uint64_t mu_bytes,
+                 const float* d_sigma, uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
+                 void* d_kv_out, uint64_t kv_out_bytes, const kvc_paged_kv* paged, const void* d_workspace,
+                 uint64_t workspace_bytes, DecodePlan* plan) {
     if (!h_header || !d_in || !d_mu || !d_sigma || (!d_kv_out && !paged) || !d_workspace) return KVC_ERR_INVALID;
     if (workspace_bytes < KVC_DECODE_WORKSPACE_BYTES) return KVC_ERR_CAPACITY;
     if (!aligned(d_in, 8) || !aligned(d_workspace, 256) || !aligned(d_sigma, 4) || !aligned(d_prefix, 4) ||
@@ -467,26 +480,24 @@ int decode_launch(const void* h_header, const void* d_in, uint64_t in_bytes, con
             paged->reserved != 0)
             return KVC_ERR_INVALID;
     }
-    kvc_params p;
-    ChunkGeom g;
-    uint64_t payload = 0, hash = 0;
-    int st = parse_header(static_cast<const uint8_t*>(h_header), &p, &g, &payload, &hash);
+    kvc_params& p = plan->p;
+    ChunkGeom& g = plan->g;
+    int st = parse_header(static_cast<const uint8_t*>(h_header), &p, &g, &plan->payload, &plan->hash);
     if (st != KVC_OK) return st;
-    const uint64_t dir_bytes = 8ull * uint64_t(g.n_chunks + 1);
-    if (in_bytes < KVC_HEADER_BYTES + dir_bytes || in_bytes - KVC_HEADER_BYTES - dir_bytes != payload)
+    plan->dir_bytes = 8ull * uint64_t(g.n_chunks + 1);
+    if (in_bytes < KVC_HEADER_BYTES + plan->dir_bytes || in_bytes - KVC_HEADER_BYTES - plan->dir_bytes != plan->payload)
         return KVC_ERR_CORRUPT;
-    uint32_t tn, tw, te;
-    if (!budgets(p.kv_dtype, p.w_narrow_bp, p.w_wide_bp, &tn, &tw, &te)) return KVC_ERR_CORRUPT;
-    if (te && !d_prefix) return KVC_ERR_INVALID;
-    const uint32_t* prefix = te ? d_prefix : nullptr;
+    if (!budgets(p.kv_dtype, p.w_narrow_bp, p.w_wide_bp, &plan->tn, &plan->tw, &plan->te)) return KVC_ERR_CORRUPT;
+    if (plan->te && !d_prefix) return KVC_ERR_INVALID;
+    plan->prefix = plan->te ? d_prefix : nullptr;
     if (!data_aligned(p.kv_dtype, p.mu_dtype, d_kv_out, d_mu, d_sigma, d_prefix)) return KVC_ERR_INVALID;
     // the caller's buffers must hold what the header describes
     const uint64_t n = uint64_t(g.planes) * uint64_t(g.tokens) * uint64_t(g.channels);
-    const uint32_t n_sym = alphabet(p.kv_dtype);
+    plan->n_sym = alphabet(p.kv_dtype);
     if (mu_bytes / mu_size(p.mu_dtype) < n || sigma_bytes / 4u < sigma_words(g)) return KVC_ERR_INVALID;
-    if (prefix && prefix_bytes / 4u < uint64_t(n_sym) + 1u) return KVC_ERR_INVALID;
+    if (plan->prefix && prefix_bytes / 4u < uint64_t(plan->n_sym) + 1u) return KVC_ERR_INVALID;
     if (!paged && kv_out_bytes / kv_size(p.kv_dtype) < n) return KVC_ERR_INVALID;
-    kvc::PagedOut po{};
+    kvc::PagedOut& po = plan->po;
     if (paged) {
         // planes ordered (layer, kv, batch, head), one pool per (layer, kv);
         // every token's page inside the table's rows; every pool holds
@@ -506,6 +517,23 @@ int decode_launch(const void* h_header, const void* d_in, uint64_t in_bytes, con
         po.heads = static_cast<uint32_t>(paged->heads);
         po.batch = static_cast<uint32_t>(paged->batch);
     }
+    return KVC_OK;
+}
+
+int decode_launch(const void* h_header, const void* d_in, uint64_t in_bytes, const void* d_mu, uint64_t mu_bytes,
+                  const float* d_sigma, uint64_t sigma_bytes, const uint32_t* d_prefix, uint64_t prefix_bytes,
+                  void* d_kv_out, uint64_t kv_out_bytes, const kvc_paged_kv* paged, void* d_workspace,
+                  uint64_t workspace_bytes, void* stream, float* stage_ms) {
+    DecodePlan plan;
+    int st = decode_check(h_header, d_in, in_bytes, d_mu, mu_bytes, d_sigma, sigma_bytes, d_prefix, prefix_bytes,
+                          d_kv_out, kv_out_bytes, paged, d_workspace, workspace_bytes, &plan);
+    if (st != KVC_OK) return st;
+    const kvc_params& p = plan.p;
+    const ChunkGeom& g = plan.g;
+    const uint32_t tn = plan.tn, tw = plan.tw, te = plan.te, n_sym = plan.n_sym;
+    const uint32_t* prefix = plan.prefix;
+    const uint64_t dir_bytes = plan.dir_bytes, payload = plan.payload, hash = plan.hash;
+    const kvc::PagedOut& po = plan.po;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     const kvc::PhiTables phi = kvc::device_phi_tables(&e, p.narrow_dof);
@@ -654,15 +682,33 @@ int kvc_reload(int64_t n, const void* const* h_streams, const uint64_t* h_stream
                uint64_t prefix_bytes, void* d_kv_out, uint64_t kv_stride, void* d_staging, uint64_t staging_bytes,
                void* d_workspace, uint64_t workspace_bytes, void* stream, void* copy_stream, int64_t* h_failed) {
     if (h_failed) *h_failed = -1;
-    if (n < 1 || !h_streams || !h_stream_bytes || !d_staging || !d_workspace || !aligned(d_staging, 256) ||
-        !aligned(d_workspace, 256))
+    if (n < 1 || !h_streams || !h_stream_bytes || !d_mu || !d_sigma || !d_kv_out || !d_staging || !d_workspace ||
+        !aligned(d_staging, 256) || !aligned(d_workspace, 256))
         return KVC_ERR_INVALID;
     if (workspace_bytes / KVC_DECODE_WORKSPACE_BYTES < uint64_t(n)) return KVC_ERR_CAPACITY;
-    // two staging halves, each 256-byte aligned; every stream must fit one
+    // two staging halves, each 256-byte aligned; every stream must fit one.
+    // Every layer passes the decode's host checks (its header read in host
+    // memory, its buffers) before anything is copied or launched.
     const uint64_t half = (staging_bytes / 2) & ~uint64_t(255);
     for (int64_t l = 0; l < n; ++l) {
-        if (!h_streams[l] || h_stream_bytes[l] < KVC_HEADER_BYTES) return KVC_ERR_CORRUPT;
-        if (h_stream_bytes[l] > half) return KVC_ERR_CAPACITY;
+        int st = KVC_OK;
+        if (!h_streams[l] || h_stream_bytes[l] < KVC_HEADER_BYTES) st = KVC_ERR_CORRUPT;
+        else if (h_stream_bytes[l] > half) st = KVC_ERR_CAPACITY;
+        if (st == KVC_OK) {
+            DecodePlan plan;
+            st = decode_check(h_streams[l], static_cast<uint8_t*>(d_staging) + (l & 1) * half, h_stream_bytes[l],
+                              static_cast<const uint8_t*>(d_mu) + uint64_t(l) * mu_stride, mu_stride,
+                              reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(d_sigma) +
+                                                             uint64_t(l) * sigma_stride),
+                              sigma_stride, d_prefix, prefix_bytes,
+                              static_cast<uint8_t*>(d_kv_out) + uint64_t(l) * kv_stride, kv_stride, nullptr,
+                              static_cast<uint8_t*>(d_workspace) + uint64_t(l) * KVC_DECODE_WORKSPACE_BYTES,
+                              KVC_DECODE_WORKSPACE_BYTES, &plan);
+        }
+        if (st != KVC_OK) {
+            if (h_failed) *h_failed = l;
+            return st;
+        }
     }
     hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(copy_stream);
     hipEvent_t copied[2] = {}, consumed[2] = {};

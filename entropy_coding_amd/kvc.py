@@ -16,7 +16,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvc.so")
+# KVC_LIBRARY names another build of the same library (the CPU tests load
+# the sanitizer build this way); by default the in-tree libkvc.so.
+LIB_PATH = os.environ.get("KVC_LIBRARY") or os.path.join(_HERE, "libkvc.so")
 
 KVC_OK, KVC_ERR_INVALID, KVC_ERR_CAPACITY, KVC_ERR_CORRUPT, KVC_ERR_MISMATCH, KVC_ERR_DEVICE = 0, -1, -2, -3, -4, -5
 KVC_BF16, KVC_E4M3, KVC_F32 = 0, 1, 2

@@ -268,7 +268,8 @@ int kvc_decode_noalloc(const void* h_header, const void* d_in, uint64_t in_bytes
  * mu_stride, the sigma at d_sigma + l x sigma_stride bytes and the shared
  * d_prefix, into d_kv_out + l x kv_stride; each stride is also the bytes
  * available there, checked against the stream's header as kvc_decode checks
- * its buffers.  Headers are read in host memory.  Workspace: n x
+ * its buffers.  Every layer's header (read in host memory) and buffers
+ * pass these checks before anything is copied or launched.  Workspace: n x
  * KVC_DECODE_WORKSPACE_BYTES, 256-byte aligned (one decode workspace per
  * layer).  Synchronises `stream` and `copy_stream` once at the end and
  * returns the first failing layer's status (KVC_OK when all decode), its
