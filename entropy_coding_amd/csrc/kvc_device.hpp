@@ -195,20 +195,25 @@ __device__ __forceinline__ bool sigma_ok(float s) {
 // fits 32 bits), without a hardware divider: a float64 quotient from the
 // hardware reciprocal refined by one Newton step is within 2^-16 of x / f;
 // truncating it plus one half gives the quotient or one above it, which one
-// borrow test settles.
+// borrow test settles.  The conversions are written as the instructions
+// (the compiler's own form of the first one adds a float64 zero, and the
+// last one saturates at 2^32 - 1 by itself, which an estimate of 2^32 needs).
+// x - q0 f then lies in [-f, f), so below 2^31 in magnitude: its low 32
+// bits, read as signed, are its value.
 __device__ __forceinline__ void divmod_q32(uint32_t xh, uint32_t xl, uint32_t f, uint32_t& q, uint32_t& r) {
     const double fd = static_cast<double>(f);
     double rc = __builtin_amdgcn_rcp(fd);
     rc = __fma_rn(rc, __fma_rn(-fd, rc, 1.0), rc);
-    // xh < 2^31 (x < 2^63): a signed conversion is exact and cheaper
-    const double xd = __fma_rn(static_cast<double>(static_cast<int32_t>(xh)), 4294967296.0, static_cast<double>(xl));
-    const uint32_t q0 = static_cast<uint32_t>(__builtin_fmin(__fma_rn(xd, rc, 0.5), 4294967295.0));
-    // rem = x - q0 f lies in [-f, f): negative exactly when the high word borrows
-    const uint64_t p = static_cast<uint64_t>(q0) * f;
-    const uint64_t rem = ((static_cast<uint64_t>(xh) << 32) | xl) - p;
-    const bool neg = static_cast<int64_t>(rem) < 0;
-    q = q0 - (neg ? 1u : 0u);
-    r = static_cast<uint32_t>(rem) + (neg ? f : 0u);
+    double dh, dl;
+    __asm__("v_cvt_f64_u32 %0, %1" : "=v"(dh) : "v"(xh));
+    __asm__("v_cvt_f64_u32 %0, %1" : "=v"(dl) : "v"(xl));
+    const double est = __fma_rn(__fma_rn(dh, 4294967296.0, dl), rc, 0.5);
+    uint32_t q0;
+    __asm__("v_cvt_u32_f64 %0, %1" : "=v"(q0) : "v"(est));
+    const int32_t rem = static_cast<int32_t>(xl - q0 * f);
+    const uint32_t neg = static_cast<uint32_t>(rem >> 31);     // all ones when x - q0 f < 0
+    q = q0 + neg;
+    r = static_cast<uint32_t>(rem) + (neg & f);
 }
 
 // Both cell edges of the bf16 symbol with bit pattern u: the inner edge

@@ -2,10 +2,12 @@
 x < 2^32 f without a hardware divider), run on the CPU with exact rationals
 so that every fused multiply-add rounds once, as on the GPU: x as a double,
 a hardware reciprocal of f with a relative error up to `rcp_rel_err`, one
-Newton step, the quotient estimate plus one half truncated (so it is the
-true quotient or one above it), and a one-sided integer fix.  Checked
-against exact integer division at the extremes of f and x, with the
-reciprocal perturbed far beyond what the hardware's error can be."""
+Newton step, the quotient estimate plus one half converted with truncation
+and saturation at 2^32 - 1 (so it is the true quotient or one above it),
+then the remainder from the low 32 bits of x - q f read as signed, and a
+one-sided fix.  Checked against exact integer division at the extremes of f
+and x, with the reciprocal perturbed far beyond what the hardware's error
+can be."""
 from fractions import Fraction
 
 import numpy as np
@@ -22,12 +24,16 @@ def divmod_model(x: int, f: int, rcp_rel_err: float):
     fd = float(f)
     r = (1.0 / fd) * (1.0 + rcp_rel_err)
     r = fma(r, fma(-fd, r, 1.0), r)
-    est = min(fma(xd, r, 0.5), 4294967295.0)
-    q = int(est)                                   # truncation of a positive value
-    rem = x - q * f
-    assert -f <= rem < f                           # q is the quotient or one above it
-    if rem < 0:
-        q, rem = q - 1, rem + f
+    est = fma(xd, r, 0.5)
+    q = min(int(est), 2 ** 32 - 1)                 # truncation, saturating at 2^32 - 1
+    exact = x - q * f
+    assert -f <= exact < f                         # q is the quotient or one above it
+    low = (x - q * f) & 0xFFFFFFFF                 # the low 32 bits of x - q f, as unsigned ...
+    rem = low - 2 ** 32 if low >> 31 else low      # ... read as signed
+    assert rem == exact                            # |x - q f| < 2^31: the low word is the value
+    neg = 0xFFFFFFFF if rem < 0 else 0
+    q = (q + neg) & 0xFFFFFFFF
+    rem = (rem + (neg & f)) & 0xFFFFFFFF
     return q, rem
 
 
