@@ -438,13 +438,15 @@ def main():
         bits_int += bi * frac
         bits_float += bf * frac
 
-    def mean(xs):
-        return sum(xs) / len(xs)
+    def median(xs):
+        # of the timed calls: robust to one slow call
+        import statistics
+        return statistics.median(xs)
 
-    enc_kernel = mean([s[0][1] for s in stats])
-    enc_total = mean([sum(s[0]) for s in stats])
-    dec_kernel = mean([s[1][1] for s in stats])
-    dec_total = mean([sum(s[1]) for s in stats])
+    enc_kernel = median([s[0][1] for s in stats])
+    enc_total = median([sum(s[0]) for s in stats])
+    dec_kernel = median([s[1][1] for s in stats])
+    dec_total = median([sum(s[1]) for s in stats])
     ms_per_step = elapsed / args.steps * 1e3
     raw = float(kv_size) * n
     # algorithmic bytes of the coding kernels: KV and mu in, words and states
@@ -495,9 +497,9 @@ def main():
         "encode_gbps": raw / (enc_total * 1e-3) / 1e9,
         "decode_gbps": raw / (dec_total * 1e-3) / 1e9,
         "encode_ms": enc_total, "decode_ms": dec_total,
-        "encode_stage_ms": {k: mean([s[0][i] for s in stats]) for i, k in
+        "encode_stage_ms": {k: median([s[0][i] for s in stats]) for i, k in
                             enumerate(["prologue", "encode_kernel"])},
-        "decode_stage_ms": {k: mean([s[1][i] for s in stats]) for i, k in enumerate(["prologue", "decode_kernel"])},
+        "decode_stage_ms": {k: median([s[1][i] for s in stats]) for i, k in enumerate(["prologue", "decode_kernel"])},
         "bits_per_scalar": {"coded": 8.0 * stream_bytes / n, "integer_model": bits_int, "float_model": bits_float},
         "stream_bytes": stream_bytes,
         "decode_fallback_share": fallback[0] / n,

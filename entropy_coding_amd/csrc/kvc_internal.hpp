@@ -29,8 +29,7 @@ struct Control {
     unsigned long long total_payload;   // payload bytes of the stream
     double bits[2];                     // estimate sums (integer model, float model)
     unsigned long long misses;          // decoder: symbols found by the fallback search
-    unsigned long long next_chunk;      // encoder: the next chunk a wave takes
-    unsigned long long reserved;
+    unsigned long long reserved[2];
 };
 static_assert(sizeof(Control) == 64, "control block size");
 constexpr uint64_t kHeaderCopyOffset = 64;           // header copy in the workspace, after Control

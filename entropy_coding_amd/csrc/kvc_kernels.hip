@@ -13,7 +13,6 @@
 // theory view", "engineering choice of predictor", "deployment parameters").
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -562,63 +561,8 @@ __device__ __forceinline__ void copy_words(const uint32_t* __restrict__ src, boo
     }
 }
 
-// A chunk's words waiting to be copied to their place in the stream while
-// the wave codes its next chunk, one piece (256 dwords: 16 bytes a lane) at
-// a time, so that the copies of waves that finish their chunks together are
-// spread over the next chunk instead of running all at once.
-struct PendingCopy {
-    const uint32_t* src;              // the words' first dword in the slot (half a dword before them when odd)
-    uint32_t* dst;                    // their place in the stream, after the chunk's states
-    uint32_t nw, out_dw, pos;         // words, dwords to write (a multiple of 2), dwords written
-    bool odd;
-};
-
-__device__ __forceinline__ void copy_piece(PendingCopy& p) {
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t j = p.pos + 4u * lane;
-    if (j < p.out_dw) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p.src + j);
-        const uint32_t e = p.src[j + 4];
-        uint32_t o[4] = {a.x, a.y, a.z, a.w};
-        if (p.odd) {
-            o[0] = __builtin_amdgcn_alignbit(a.y, a.x, 16);
-            o[1] = __builtin_amdgcn_alignbit(a.z, a.y, 16);
-            o[2] = __builtin_amdgcn_alignbit(a.w, a.z, 16);
-            o[3] = __builtin_amdgcn_alignbit(e, a.w, 16);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t wi = 2u * (j + q);
-            if (wi >= p.nw) o[q] = 0u;
-            else if (wi + 1 >= p.nw) o[q] &= 0xFFFFu;
-        }
-        if (j + 4 <= p.out_dw) *reinterpret_cast<uint4*>(p.dst + j) = make_uint4(o[0], o[1], o[2], o[3]);
-        else *reinterpret_cast<uint2*>(p.dst + j) = make_uint2(o[0], o[1]);
-    }
-    p.pos += 256u;
-}
-
-// The rest of a pending copy, with several pieces' reads in flight.
-__device__ __forceinline__ void finish_copy(PendingCopy& p) {
-    if (p.pos < p.out_dw) {
-        const uint32_t done_words = 2u * p.pos;
-        copy_words(p.src + p.pos, p.odd, p.nw > done_words ? p.nw - done_words : 0u, p.dst + p.pos,
-                   p.out_dw - p.pos);
-        p.pos = p.out_dw;
-    }
-}
-
-// Waves take chunks in index order from a counter and keep taking them
-// until none is left; a chunk is placed (its offset found by the look-back,
-// its states and directory entry written) as soon as it is coded, and its
-// words are copied while the wave codes its next chunk.  Every chunk a
-// look-back waits for was taken by a running wave, which publishes its size
-// when that chunk is coded, before it waits for anything: every wait ends,
-// however many workgroups are resident.
-// (8 waves per SIMD, so at most 64 vector registers: the chunk loop around
-// the coding loop would otherwise take more and halve the resident waves.)
 template <int KV, int MU>
-__global__ void __launch_bounds__(kEncodeBlock) __attribute__((amdgpu_waves_per_eu(8))) k_encode(EncodeArgs a) {
+__global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
     __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
     __shared__ uint32_t s_small[KV == kE4M3 ? kE4Words : 1];
     __shared__ unsigned long long s_head[kHeaderBytes / 8];        // the last chunk's header
@@ -626,76 +570,62 @@ __global__ void __launch_bounds__(kEncodeBlock) __attribute__((amdgpu_waves_per_
     copy_to_lds(s_tab, a.table, static_cast<uint32_t>(kTableBytes / 16));
 
     const uint32_t lane = threadIdx.x & 63u;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * (kEncodeBlock / 64) + wave;
+    if (chunk >= a.geom.n_chunks) return;
+    const ChunkPos cp = chunk_pos(a.geom, chunk);
     const uint32_t D = static_cast<uint32_t>(a.geom.channels);
+
+    const float sigma = a.sigma[cp.srow * D + cp.k * 64 + lane];
+    float inv24 = __frcp_rn(sigma) * 16777216.0f;
+    if (__ballot(!sigma_ok(sigma))) {
+        if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
+        inv24 = 16777216.0f;
+    }
     const Model m{s_tab, a.prefix, s_small, a.eslots, a.tn + a.tw};
+
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
+    // the chunk's rows of KV and mu as buffers (a chunk's rows span fewer than
+    // 2^31 bytes)
+    const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * static_cast<int64_t>(D) + cp.k * 64;
+    const __amdgpu_buffer_rsrc_t kvb = buffer_rsrc(static_cast<const KB*>(a.kv) + row0, cp.len * D * sizeof(KB));
+    const __amdgpu_buffer_rsrc_t mub = buffer_rsrc(static_cast<const MT*>(a.mu) + row0, cp.len * D * sizeof(MT));
+    uint16_t* __restrict__ slot = a.slots + static_cast<uint64_t>(chunk) * a.slot_words;
+
+    PushState st{static_cast<uint32_t>(kL), kLHi, static_cast<uint32_t>(a.slot_words)};
+    int t = static_cast<int>(cp.len) - 1;
+    for (; t >= kEncodeBatch - 1; t -= kEncodeBatch)
+        encode_batch<KV, MU, kEncodeBatch>(t, st, kvb, mub, D, lane, inv24, m, slot);
+    for (; t >= 0; --t) encode_batch<KV, MU, 1>(t, st, kvb, mub, D, lane, inv24, m, slot);
+
+    // the chunk's place in the stream: the sizes of the chunks before it
+    const uint32_t nw = static_cast<uint32_t>(a.slot_words) - st.wp;
+    const unsigned long long size = chunk_bytes(nw);
+    const unsigned long long beg = look_back(a.status, chunk, size, a.ctl);
     const uint64_t n = static_cast<uint64_t>(a.geom.n_chunks);
     const uint64_t pay_off = kHeaderBytes + 8ull * (n + 1);
     const bool dir_fits = pay_off <= a.out_capacity;
-    unsigned long long* dir = reinterpret_cast<unsigned long long*>(a.out + kHeaderBytes);
-    PendingCopy pend{nullptr, nullptr, 0u, 0u, 0u, false};
-    unsigned long long total = ~0ull;                  // the payload size, once this wave places the last chunk
-
-    for (;;) {
-        unsigned long long taken = 0;
-        if (lane == 0) taken = atomicAdd(&a.ctl->next_chunk, 1ull);
-        const uint64_t chunk =
-            (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(taken >> 32))) << 32) |
-            static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(taken)));
-        if (chunk >= n) break;
-        const ChunkPos cp = chunk_pos(a.geom, static_cast<int64_t>(chunk));
-
-        const float sigma = a.sigma[cp.srow * D + cp.k * 64 + lane];
-        float inv24 = __frcp_rn(sigma) * 16777216.0f;
-        if (__ballot(!sigma_ok(sigma))) {
-            if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
-            inv24 = 16777216.0f;
-        }
-        // the chunk's rows of KV and mu as buffers (a chunk's rows span fewer
-        // than 2^31 bytes)
-        const int64_t row0 = (cp.g * a.geom.tokens + cp.t0) * static_cast<int64_t>(D) + cp.k * 64;
-        const __amdgpu_buffer_rsrc_t kvb = buffer_rsrc(static_cast<const KB*>(a.kv) + row0, cp.len * D * sizeof(KB));
-        const __amdgpu_buffer_rsrc_t mub = buffer_rsrc(static_cast<const MT*>(a.mu) + row0, cp.len * D * sizeof(MT));
-        uint16_t* __restrict__ slot = a.slots + chunk * a.slot_words;
-
-        PushState st{static_cast<uint32_t>(kL), kLHi, static_cast<uint32_t>(a.slot_words)};
-        int t = static_cast<int>(cp.len) - 1;
-        for (; t >= kEncodeBatch - 1; t -= kEncodeBatch) {
-            encode_batch<KV, MU, kEncodeBatch>(t, st, kvb, mub, D, lane, inv24, m, slot);
-            if (pend.pos < pend.out_dw) copy_piece(pend);            // the previous chunk's words
-        }
-        for (; t >= 0; --t) encode_batch<KV, MU, 1>(t, st, kvb, mub, D, lane, inv24, m, slot);
-        finish_copy(pend);
-
-        // the chunk's place in the stream: the sizes of the chunks before it
-        const uint32_t nw = static_cast<uint32_t>(a.slot_words) - st.wp;
-        const unsigned long long size = chunk_bytes(nw);
-        const unsigned long long lb = look_back(a.status, static_cast<int64_t>(chunk), size, a.ctl);
-        const unsigned long long beg =                       // wave-uniform: in scalar registers
-            (static_cast<unsigned long long>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(lb >> 32))) << 32) |
-            static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(lb)));
-        if (pay_off + beg + size <= a.out_capacity) {
-            // the 64 final states now, the words (this wave's own stores:
-            // waited for before any lane reads them back) during the next chunk
-            uint8_t* dst = a.out + pay_off + beg;
-            reinterpret_cast<unsigned long long*>(dst)[lane] = (static_cast<unsigned long long>(st.xh) << 32) | st.xl;
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-            pend = PendingCopy{reinterpret_cast<const uint32_t*>(slot) + (st.wp >> 1),
-                               reinterpret_cast<uint32_t*>(dst + kStateBytes), nw,
-                               static_cast<uint32_t>((size - kStateBytes) / 4), 0u, (st.wp & 1u) != 0};
-        } else if (lane == 0) {
-            atomicOr(&a.ctl->flags, kFlagCapacity);
-        }
-        if (lane == 0 && dir_fits) dir[chunk] = beg;
-        if (chunk + 1 == n) total = beg + size;
+    if (pay_off + beg + size <= a.out_capacity) {
+        // the 64 final states, then the words from the slot (this wave's own
+        // stores: wait for them before reading them back in other lanes),
+        // zero padded to 8 bytes
+        uint8_t* dst = a.out + pay_off + beg;
+        reinterpret_cast<unsigned long long*>(dst)[lane] = (static_cast<unsigned long long>(st.xh) << 32) | st.xl;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        copy_words(reinterpret_cast<const uint32_t*>(slot) + (st.wp >> 1), (st.wp & 1u) != 0, nw,
+                   reinterpret_cast<uint32_t*>(dst + kStateBytes), static_cast<uint32_t>((size - kStateBytes) / 4));
+    } else if (lane == 0) {
+        atomicOr(&a.ctl->flags, kFlagCapacity);
     }
-    finish_copy(pend);
-    if (total != ~0ull && lane == 0) {
-        // this wave placed the last chunk, so it knows the payload size:
-        // directory end, header (with the side-information checksum of the
-        // kernel before and its CRC), and the workspace's copy of the header
-        // (also when the stream does not fit, for the size it needed)
+    unsigned long long* dir = reinterpret_cast<unsigned long long*>(a.out + kHeaderBytes);
+    if (lane == 0 && dir_fits) dir[chunk] = beg;
+    if (static_cast<uint64_t>(chunk) + 1 == n && lane == 0) {
+        // the last chunk knows the payload size: directory end, header (with
+        // the side-information checksum of the kernel before and its CRC),
+        // and the workspace's copy of the header (also when the stream does
+        // not fit, for the size it needed)
+        const unsigned long long total = beg + size;
         a.ctl->total_payload = total;
         if (dir_fits) dir[n] = total;
         for (int i = 0; i < kHeaderBytes / 8; ++i) __builtin_memcpy(&s_head[i], a.header.bytes + 8 * i, 8);
@@ -711,24 +641,9 @@ __global__ void __launch_bounds__(kEncodeBlock) __attribute__((amdgpu_waves_per_
     }
 }
 
-// Compute units of the current device (cached; 0 when unknown).
-static int device_cus() {
-    static std::atomic<int> cus[kMaxDevices];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-    int c = cus[dev].load(std::memory_order_relaxed);
-    if (c == 0 && hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
-        cus[dev].store(c, std::memory_order_relaxed);
-    return c > 0 ? c : 0;
-}
-
 hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStream_t s) {
     constexpr int waves = kEncodeBlock / 64;
-    uint64_t blocks = (static_cast<uint64_t>(a.geom.n_chunks) + waves - 1) / waves;
-    // waves keep taking chunks, so a launch needs no more workgroups than a
-    // device holds at once (two of 16 waves per CU: 32 wave slots)
-    const int cus = device_cus();
-    if (cus > 0 && blocks > 2ull * static_cast<uint64_t>(cus)) blocks = 2ull * static_cast<uint64_t>(cus);
+    const uint64_t blocks = (static_cast<uint64_t>(a.geom.n_chunks) + waves - 1) / waves;
     const dim3 grid(static_cast<uint32_t>(blocks)), block(kEncodeBlock);
     if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_encode<kBF16, kBF16>), grid, block, 0, s, a);
     else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_encode<kBF16, kF32>), grid, block, 0, s, a);
