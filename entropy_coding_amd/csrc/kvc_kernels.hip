@@ -503,13 +503,24 @@ __device__ __forceinline__ unsigned long long look_back(unsigned long long* stat
 }
 
 // CRC-32 (reflected polynomial 0xEDB88320, as zlib computes it) of the
-// header's first 92 bytes, bit by bit; one lane, once per encode.
-__device__ uint32_t header_crc32(const uint8_t* b) {
-    uint32_t c = 0xFFFFFFFFu;
-    for (uint32_t i = 0; i < kHeaderCrcOffset; ++i) {
-        c ^= b[i];
-        for (int k = 0; k < 8; ++k) c = (c >> 1) ^ ((c & 1u) ? 0xEDB88320u : 0u);
+// header's first 92 bytes, once per encode, on the last chunk's path.  The
+// wave first builds the byte table in LDS (lane l: entries l, l + 64,
+// l + 128, l + 192, eight bit steps each), then one lane takes a byte per
+// table read: 92 dependent LDS reads instead of 736 dependent bit steps.
+__device__ __forceinline__ void crc_table_wave(uint32_t* t) {
+    const uint32_t lane = threadIdx.x & 63u;
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) {
+        uint32_t c = lane + 64u * k;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c = (c >> 1) ^ ((c & 1u) ? 0xEDB88320u : 0u);
+        t[lane + 64u * k] = c;
     }
+}
+
+__device__ uint32_t header_crc32(const uint8_t* b, const uint32_t* t) {
+    uint32_t c = 0xFFFFFFFFu;
+    for (uint32_t i = 0; i < kHeaderCrcOffset; ++i) c = t[(c ^ b[i]) & 0xFFu] ^ (c >> 8);
     return ~c;
 }
 
@@ -566,6 +577,7 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
     __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
     __shared__ uint32_t s_small[KV == kE4M3 ? kE4Words : 1];
     __shared__ unsigned long long s_head[kHeaderBytes / 8];        // the last chunk's header
+    __shared__ uint32_t s_crc[256];                                // the last chunk's CRC-32 table
     if constexpr (KV == kE4M3) build_e4_lds(s_small, a.prefix);
     copy_to_lds(s_tab, a.table, static_cast<uint32_t>(kTableBytes / 16));
 
@@ -620,6 +632,10 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
     }
     unsigned long long* dir = reinterpret_cast<unsigned long long*>(a.out + kHeaderBytes);
     if (lane == 0 && dir_fits) dir[chunk] = beg;
+    if (static_cast<uint64_t>(chunk) + 1 == n) {
+        crc_table_wave(s_crc);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");      // the table's stores before its reads
+    }
     if (static_cast<uint64_t>(chunk) + 1 == n && lane == 0) {
         // the last chunk knows the payload size: directory end, header (with
         // the side-information checksum of the kernel before and its CRC),
@@ -631,7 +647,7 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
         for (int i = 0; i < kHeaderBytes / 8; ++i) __builtin_memcpy(&s_head[i], a.header.bytes + 8 * i, 8);
         s_head[72 / 8] = total;
         s_head[80 / 8] = a.ctl->side_hash;
-        const uint32_t crc = header_crc32(reinterpret_cast<const uint8_t*>(s_head));
+        const uint32_t crc = header_crc32(reinterpret_cast<const uint8_t*>(s_head), s_crc);
         s_head[kHeaderCrcOffset / 8] =
             (s_head[kHeaderCrcOffset / 8] & 0xFFFFFFFFull) | (static_cast<unsigned long long>(crc) << 32);
         for (int i = 0; i < kHeaderBytes / 8; ++i) {
