@@ -348,8 +348,16 @@ __device__ __forceinline__ SymSlots make_slots(uint32_t ga, uint32_t gb, U32Pair
     return y;
 }
 
+// bf16: the escape slot table's entry of pattern kb (a global read that
+// does not depend on the model); e4m3 reads its prefix from LDS instead.
+template <int KV>
+__device__ __forceinline__ U32Pair escape_entry(uint32_t kb, const Model& m) {
+    if constexpr (KV == kBF16) return load_pair(m.eslots, kb << 3);
+    else return U32Pair{0u, 0u};
+}
+
 template <int KV, int MU>
-__device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float inv24, const Model& m) {
+__device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float inv24, const Model& m, U32Pair q) {
     if constexpr (KV == kBF16 && MU == kBF16) {
         // both cell edges carry the value's sign; h is monotone in the
         // position, so the lower edge's h is the smaller one on either side
@@ -361,7 +369,7 @@ __device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float in
         const uint32_t sb = (kb & 0x8000u) << 16;
         const uint32_t ha = h_fx(z_fixed(__uint_as_float(ib | sb), mu, inv24), m.tab);
         const uint32_t hb = h_fx(z_fixed(__uint_as_float(ob | sb), mu, inv24), m.tab);
-        return make_slots(ha, hb, load_pair(m.eslots, kb << 3));
+        return make_slots(ha, hb, q);
     }
     if constexpr (KV == kE4M3) {
         const uint32_t s = order_of_bits<KV>(kb);
@@ -379,7 +387,7 @@ __device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float in
     bf16_cell_edges(kb, lo, hi);
     const uint32_t ha = h_fx(z_fixed(lo, mu, inv24), m.tab);
     const uint32_t hb = h_fx(z_fixed(hi, mu, inv24), m.tab);
-    return make_slots(ha, hb, load_pair(m.eslots, kb << 3));
+    return make_slots(ha, hb, q);
 }
 
 // Rows of the chunk through buffer resources: the lane's byte offset in a
@@ -417,7 +425,58 @@ __device__ __forceinline__ void encode_batch(int t, PushState& st, __amdgpu_buff
     }
     SymSlots y[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) y[u] = symbol_slots<KV, MU>(kb[u], mus[u], inv24, m);
+    for (int u = 0; u < U; ++u) y[u] = symbol_slots<KV, MU>(kb[u], mus[u], inv24, m, escape_entry<KV>(kb[u], m));
+#pragma unroll
+    for (int u = 0; u < U; ++u) rans_push(st, y[u], slot);
+}
+
+// The rows of tokens t, t - 1, ..., t - U + 1 (a row before the chunk's first
+// stands in as row 0: its values are never used).
+template <int KV, int MU, int U>
+__device__ __forceinline__ void load_rows(int t, uint32_t (&kr)[U], uint32_t (&mr)[U], __amdgpu_buffer_rsrc_t kvr,
+                                          __amdgpu_buffer_rsrc_t mur, uint32_t D, uint32_t lane) {
+    using KB = typename Alphabet<KV>::Bits;
+    using MT = typename MuT<MU>::T;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t row = static_cast<uint32_t>(t - u >= 0 ? t - u : 0) * D;
+        kr[u] = load_row_elem<KB>(kvr, lane * static_cast<uint32_t>(sizeof(KB)), row * static_cast<uint32_t>(sizeof(KB)));
+        mr[u] = load_row_elem<MT>(mur, lane * static_cast<uint32_t>(sizeof(MT)), row * static_cast<uint32_t>(sizeof(MT)));
+    }
+}
+
+// A batch whose rows were read one batch ahead (kr, mr); it reads the rows
+// of the batch after it (from t_next) into the same registers.  The order of
+// the reads matters: the vector-memory counter completes in order, so this
+// batch's escape-entry reads are issued before the next batch's rows and
+// their wait does not include those HBM reads.
+template <int KV, int MU, int U>
+__device__ __forceinline__ void encode_batch_ahead(uint32_t (&kr)[U], uint32_t (&mr)[U], int t_next, PushState& st,
+                                                   __amdgpu_buffer_rsrc_t kvr, __amdgpu_buffer_rsrc_t mur,
+                                                   uint32_t D, uint32_t lane, float inv24, const Model& m,
+                                                   uint16_t* __restrict__ slot) {
+    uint32_t kb[U];
+    float mus[U];
+    U32Pair q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        kb[u] = kr[u];
+        mus[u] = MU == kBF16 ? __uint_as_float(mr[u] << 16) : __uint_as_float(mr[u]);
+        q[u] = escape_entry<KV>(kb[u], m);
+    }
+    __asm__ volatile("" : : : "memory");
+    load_rows<KV, MU, U>(t_next, kr, mr, kvr, mur, D, lane);
+    uint64_t odd = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) odd |= __ballot(!__builtin_isfinite(mus[u]));
+    if (odd) {
+        __asm__ volatile("");
+#pragma unroll
+        for (int u = 0; u < U; ++u) mus[u] = __builtin_isfinite(mus[u]) ? mus[u] : 0.0f;
+    }
+    SymSlots y[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) y[u] = symbol_slots<KV, MU>(kb[u], mus[u], inv24, m, q[u]);
 #pragma unroll
     for (int u = 0; u < U; ++u) rans_push(st, y[u], slot);
 }
@@ -607,8 +666,10 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
 
     PushState st{static_cast<uint32_t>(kL), kLHi, static_cast<uint32_t>(a.slot_words)};
     int t = static_cast<int>(cp.len) - 1;
+    uint32_t kr[kEncodeBatch], mr[kEncodeBatch];         // the next batch's rows, read a batch ahead
+    if (t >= kEncodeBatch - 1) load_rows<KV, MU, kEncodeBatch>(t, kr, mr, kvb, mub, D, lane);
     for (; t >= kEncodeBatch - 1; t -= kEncodeBatch)
-        encode_batch<KV, MU, kEncodeBatch>(t, st, kvb, mub, D, lane, inv24, m, slot);
+        encode_batch_ahead<KV, MU, kEncodeBatch>(kr, mr, t - kEncodeBatch, st, kvb, mub, D, lane, inv24, m, slot);
     for (; t >= 0; --t) encode_batch<KV, MU, 1>(t, st, kvb, mub, D, lane, inv24, m, slot);
 
     // the chunk's place in the stream: the sizes of the chunks before it
