@@ -28,6 +28,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["entropy_coding_amd/csrc/kvc_kernels.hip", "entropy_coding_amd/csrc/kvc_device.hpp",
                   "entropy_coding_amd/csrc/kvc_internal.hpp"]
 TRAFFIC_FILE = "profiles/traffic_qwen3-8b_bf16.txt"
+VALU_FILE = "profiles/valu_k_encode_k_decode_qwen3-8b_bf16.md"
+# plain-ALU peak: one wave64 vector instruction per CU per cycle
+# (4 SIMD16 units, 4 cycles each) at 2.4 GHz on 256 CUs, in lane-ops/s
+ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 
 
 def kernel_sources_sha256() -> str:
@@ -56,6 +60,24 @@ def measured_traffic():
             elif len(parts) >= 3 and parts[0] == "traffic":
                 kv = dict(p.split("=", 1) for p in parts[2:])
                 out[parts[1]] = {k: float(v) for k, v in kv.items()}
+    return out if sha == kernel_sources_sha256() else {}
+
+
+def measured_valu():
+    """VALU instructions per wave step (one token of one 64-lane chunk) of
+    each coding kernel from the committed counter summary, or {} when it is
+    missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, VALU_FILE)
+    if not os.path.exists(path):
+        return {}
+    out, sha = {}, None
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and parts[0] == "kernel_sources_sha256":
+                sha = parts[1]
+            elif len(parts) == 3 and parts[0] == "valu":
+                out[parts[1]] = float(parts[2].split("=", 1)[1])
     return out if sha == kernel_sources_sha256() else {}
 
 
@@ -462,6 +484,16 @@ def main():
                 "frac": a / HBM_PEAK_GBPS, "traffic": t, "algorithmic_bytes": alg, "avg_ms": avg_ms}
 
     rl = {"k_encode": roofline("k_encode", enc_kernel), "k_decode": roofline("k_decode", dec_kernel)}
+    # the ALU view of the same kernels (their bound): vector lane-operations
+    # per second from the counted instructions per wave step, against one
+    # wave64 instruction per CU-cycle
+    valu = measured_valu() if traffic else {}
+    alu = {}
+    for k, ms in (("k_encode", enc_kernel), ("k_decode", dec_kernel)):
+        if k in valu:
+            a = valu[k] * 64.0 * (n / 64.0) / (ms * 1e-3) / 1e12
+            alu[k] = {"bound": "alu", "kernel": k, "achieved": a, "peak": ALU_PEAK_TOPS, "unit": "T lane-ops/s",
+                      "frac": a / ALU_PEAK_TOPS, "valu_per_wave_step": valu[k]}
     # the same algorithmic bytes over each whole call (per-call tables,
     # checksum and launches included): what a caller of kvc_encode /
     # kvc_decode gets
@@ -507,6 +539,7 @@ def main():
         "roofline": rl[dominant],
         "rooflines": rl,
         "call_rooflines": call_rl,
+        "alu_rooflines": alu or None,
         "cpu_baseline": cpu,
         "pages_context": {"bits_per_scalar_qwen3_0.6B_to_32B": [6.74, 5.92],
                           "fp8_bits_per_element": [2.05, 2.59]},
