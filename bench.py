@@ -269,8 +269,10 @@ def main():
     ap.add_argument("--sigma-fit", choices=["rms", "rate"], default="rms",
                     help="sigma calibration: the RMS of the residual, or the scale fitted to the code length")
     ap.add_argument("--streams", type=int, default=2,
-                    help="(per-layer workload 4) HIP streams the asynchronous one-layer calls are spread over; "
-                         "1 = synchronous calls one after another")
+                    help="(per-layer workload 4) HIP streams the asynchronous one-layer encode calls are spread "
+                         "over; 1 = synchronous calls one after another")
+    ap.add_argument("--decode-streams", type=int, default=3,
+                    help="(per-layer workload 4) HIP streams the asynchronous one-layer decode calls are spread over")
     ap.add_argument("--narrow-dof", type=int, default=0,
                     help="narrow part of the mixture: 0 = the pages' Gaussian, nu = Student's t with nu degrees of freedom")
     ap.add_argument("--paged", type=int, default=0,
@@ -370,8 +372,10 @@ def main():
         # every decode the same way
         encs = [enc] + [kvc.Encoder(p, dev) for _ in parts[1:]]
         dwss = [dws] + [torch.empty(kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev) for _ in parts[1:]]
-        side = [torch.cuda.Stream(device=dev) for _ in range(args.streams)]
-        log(f"[bench] pipelined: {len(parts)} one-layer calls queued asynchronously over {len(side)} streams")
+        side = [torch.cuda.Stream(device=dev) for _ in range(max(args.streams, args.decode_streams))]
+        es, ds = args.streams, args.decode_streams
+        log(f"[bench] pipelined: {len(parts)} one-layer calls queued asynchronously, encode over {es} and decode "
+            f"over {ds} streams")
 
         def step(stats=None):
             main = torch.cuda.current_stream(dev)
@@ -380,17 +384,17 @@ def main():
             for q in side:
                 q.wait_stream(main)
             for l, sl in enumerate(parts):
-                encs[l].enqueue(kv[sl], mu[sl], sigma[sl], prefix, stream=side[l % len(side)])
+                encs[l].enqueue(kv[sl], mu[sl], sigma[sl], prefix, stream=side[l % es])
             for q in side:
                 main.wait_stream(q)
             ev[1].record(main)
-            sts = [encs[l].result(stream=side[l % len(side)]) for l in range(len(parts))]
+            sts = [encs[l].result(stream=side[l % es]) for l in range(len(parts))]
             ev[2].record(main)
             for q in side:
                 q.wait_stream(main)
             for l, sl in enumerate(parts):
                 rc = kvc.kvc_decode_async(sts[l], mu[sl], sigma[sl], prefix, kv_out[sl], dwss[l], encs[l].header.copy(),
-                                          stream=side[l % len(side)])
+                                          stream=side[l % ds])
                 if rc != kvc.KVC_OK:
                     raise kvc.KvcError(rc, "kvc_decode_async")
             for q in side:
@@ -399,7 +403,7 @@ def main():
             fb = 0
             for l in range(len(parts)):
                 di = {}
-                rc = kvc.kvc_decode_result(dwss[l], stream=side[l % len(side)], info=di)
+                rc = kvc.kvc_decode_result(dwss[l], stream=side[l % ds], info=di)
                 if rc != kvc.KVC_OK:
                     raise kvc.KvcError(rc, "kvc_decode_result")
                 fb += di["fallback_symbols"]
@@ -522,7 +526,8 @@ def main():
             "narrow_part": "gaussian" if args.narrow_dof == 0 else f"student-t, {args.narrow_dof} dof",
             "mu_dtype": "bf16" if mu_size == 2 else "fp32", "calls_per_step": len(parts),
             "decode_output": f"paged, {args.paged}-token pages" if args.paged else "contiguous",
-            "calls": (f"asynchronous, {args.streams} streams (times: whole passes)" if pipelined
+            "calls": (f"asynchronous, encode on {args.streams} and decode on {args.decode_streams} streams "
+                      "(times: whole passes)" if pipelined
                       else "synchronous, one after another"),
             "second_pass_copy_ms": scatter_ms,
         },
