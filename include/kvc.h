@@ -33,8 +33,14 @@
  *     prefix is uint32[N + 1] (N = 65536 for bf16, 256 for e4m3).
  *   - Every call returns a kvc_status; no exception crosses the ABI.  On an
  *     error, outputs are undefined (but never written out of bounds).
- *   - Concurrent calls on different streams are safe; the only state the
- *     library keeps is a read-only per-device table, set up on first use.
+ *   - Concurrent calls on different streams are safe (each with its own
+ *     workspace).  The state the library keeps, per device, lives in static
+ *     device arrays (no allocation): the base CDF tables, copied on first
+ *     use, and the mixture and decoder tables of every (weights, narrow
+ *     part) a process uses (up to 8), built on first use by a kernel on the
+ *     calling stream, which that first call synchronises; all of them are
+ *     only read afterwards.  kvc_decode_noalloc's scratch is the one
+ *     exception, see there.
  */
 #ifndef KVC_H
 #define KVC_H
