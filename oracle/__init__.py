@@ -38,6 +38,13 @@ Parity status of each function (what pins it other than itself):
                                   in a constant-ulp region; the escape part
                                   alone against the smoothed histogram counted
                                   pattern by pattern
+  split_budgets / h_fx_lanes   -- (per-channel split, S-14) chunks whose lanes
+                                  share one weight equal the global-weight
+                                  chunks byte for byte; each lane's final
+                                  state and word count from a one-lane rANS
+                                  written out with Python ints; code lengths
+                                  per channel
+  calibrate_split              -- a float64 brute force over the candidates
 """
 
 from .kvc_oracle import *  # noqa: F401,F403

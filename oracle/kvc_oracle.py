@@ -300,6 +300,44 @@ def h_fx(q, table) -> np.ndarray:
     return lo + (((hi - lo) * r) >> 16)
 
 
+def split_budgets(kv_dtype: int, w_narrow_bp: int, w_wide_bp: int, split):
+    """S-14: per-channel split of the Gaussian budget.  ``split`` holds, per
+    (plane, channel), the narrow part's weight w_c in basis points (0 ..
+    w_n + w_w); the escape weight stays the call's, so T_e, the prefix and the
+    floor-and-escape slots are shared by every lane.  T_n(c) = min(floor(T
+    w_c / 10^4), T_n + T_w) and T_w(c) = T_n + T_w - T_n(c): w_c = w_n gives
+    back the call's (T_n, T_w).  Returns the two int64 arrays."""
+    t_n, t_w, _ = budgets(kv_dtype, w_narrow_bp, w_wide_bp)
+    w = np.asarray(split, dtype=np.int64)
+    if np.any(w < 0) or np.any(w > w_narrow_bp + w_wide_bp):
+        raise ValueError("a channel's narrow weight must lie in [0, w_n + w_w]")
+    big_t = M - alphabet_size(kv_dtype)
+    tn = np.minimum((big_t * w) // 10000, t_n + t_w)
+    return tn, (t_n + t_w) - tn
+
+
+def h_fx_lanes(q, t_n, t_w, narrow_dof: int = 0) -> np.ndarray:
+    """h_fx with each element's own mixture table (S-14): the same S-4 table,
+    H[k] = floor(T_n A[k] / 2^31) + floor(T_w B[k] / 2^31) with
+    H[12289] = H[12288], for that element's budgets, and the same integer
+    interpolation."""
+    q = np.asarray(q).astype(np.int64)
+    if np.any(np.abs(q) > TABLE_Z_MAX << 24):
+        raise ValueError("h_fx argument out of range")
+    u = q + (TABLE_Z_MAX << 24)
+    i = u >> 16
+    r = u & 0xFFFF
+    a = narrow_table(narrow_dof)
+    b = phi_tables()[1]
+    a = np.concatenate([a, a[-1:]])
+    b = np.concatenate([b, b[-1:]])
+    tn = np.asarray(t_n, dtype=np.int64)
+    tw = np.asarray(t_w, dtype=np.int64)
+    lo = ((tn * a[i]) >> 31) + ((tw * b[i]) >> 31)
+    hi = ((tn * a[i + 1]) >> 31) + ((tw * b[i + 1]) >> 31)
+    return lo + (((hi - lo) * r) >> 16)
+
+
 # ---------------------------------------------------------------------------
 # S-3 / S-5  the mixture CDF
 # ---------------------------------------------------------------------------
@@ -316,8 +354,9 @@ def mu_to_f32(mu, mu_dtype: int) -> np.ndarray:
     return np.where(np.isfinite(m), m, np.float32(0.0)).astype(np.float32)
 
 
-def cdf(b, mu32, inv32, dtype: int, t_n: int, t_w: int, prefix=None, narrow_dof: int = 0) -> np.ndarray:
-    """C(b): cumulative frequency below symbol b under the mixture.
+def cdf(b, mu32, inv32, dtype: int, t_n, t_w, prefix=None, narrow_dof: int = 0) -> np.ndarray:
+    """C(b): cumulative frequency below symbol b under the mixture (t_n, t_w
+    the budgets, or arrays of per-element budgets broadcast with b: S-14).
 
     S-3  d = pos(b) - mu and z' = d * (2^24/sigma), each one IEEE float32
          operation, where 2^24/sigma is the float32 1/sigma times 2^24 (exact
@@ -338,13 +377,16 @@ def cdf(b, mu32, inv32, dtype: int, t_n: int, t_w: int, prefix=None, narrow_dof:
         d = (pos - mu32).astype(np.float32)
         z24 = (d * inv24).astype(np.float32)
     q = np.floor(np.clip(z24, -qmax, qmax)).astype(np.int64)
-    g = h_fx(q, mixture_table(t_n, t_w, narrow_dof))
+    if np.ndim(t_n) == 0 and np.ndim(t_w) == 0:
+        g = h_fx(q, mixture_table(t_n, t_w, narrow_dof))
+    else:                                              # per-element budgets (S-14)
+        g = h_fx_lanes(q, t_n, t_w, narrow_dof)
     if prefix is not None:
         g = g + np.asarray(prefix, dtype=np.int64)[b]
     return b + g
 
 
-def gauss_cum(b, mu32, inv32, dtype: int, t_n: int, t_w: int, narrow_dof: int = 0) -> np.ndarray:
+def gauss_cum(b, mu32, inv32, dtype: int, t_n, t_w, narrow_dof: int = 0) -> np.ndarray:
     """G(b) = h(q_b): the narrow and wide parts of C below symbol b, 0 .. T_n + T_w."""
     return cdf(b, mu32, inv32, dtype, t_n, t_w, None, narrow_dof) - np.asarray(b).astype(np.int64)
 
@@ -567,6 +609,59 @@ __all__ += ["RATE_STEPS", "log2_table_q16", "code_len_q16", "calibrate_sigma_rat
 
 
 # ---------------------------------------------------------------------------
+# S-14  per-channel split of the Gaussian budget (an optional calibration)
+# ---------------------------------------------------------------------------
+SPLIT_STEPS = 16                   # candidate narrow weights w_n + w_w - SPLIT_STEP_BP * j
+SPLIT_STEP_BP = 200
+
+
+def split_candidates(w_narrow_bp: int, w_wide_bp: int) -> np.ndarray:
+    """The narrow weights S-14 chooses from: W - 200 j for j = 0..15, W = w_n +
+    w_w, those below 0 raised to 0."""
+    w = w_narrow_bp + w_wide_bp
+    return np.maximum(w - SPLIT_STEP_BP * np.arange(SPLIT_STEPS, dtype=np.int64), 0)
+
+
+def calibrate_split(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int,
+                    w_wide_bp: int, sigma_block_tokens: int = 0, narrow_dof: int = 0,
+                    return_costs: bool = False):
+    """S-14: per (plane, channel), the narrow weight among split_candidates
+    that gives the held-out data [reps, planes, tokens, channels] the least
+    integer code length sum(code_len_q16(f)) under the format's CDF with that
+    channel's budgets (split_budgets); the first candidate on a tie.  sigma is
+    the one the stream will use (per channel, or per block with
+    sigma_block_tokens).
+
+    Reading ([wiki] § future directions and [blog] § limitations and future
+    directions ask for a better residual model; the pages' weights 0.95 /
+    0.03 are one choice for every channel, [wiki] § mixture distribution):
+    the escape weight stays the call's, so the marginal and its slots are
+    shared, and each channel moves weight between its narrow and its wide
+    Gaussian, fitted to the code length as S-12 fits sigma."""
+    kv = np.asarray(kv)
+    reps, planes, t_len, ch = kv.shape
+    t_n, t_w, t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)
+    pref = prefix if t_e else None
+    inv = _inv_sigma(sigma_per_token(sigma, t_len, sigma_block_tokens))   # [planes, T, D]
+    s = order_index(kv, kv_dtype).astype(np.int64)
+    m32 = mu_to_f32(mu, mu_dtype)
+    cands = split_candidates(w_narrow_bp, w_wide_bp)
+    costs = np.zeros((SPLIT_STEPS, planes, ch), dtype=np.int64)
+    for j, wc in enumerate(cands):
+        tn, tw = split_budgets(kv_dtype, w_narrow_bp, w_wide_bp, np.full((planes, ch), wc))
+        for r in range(reps):
+            c0 = cdf(s[r], m32[r], inv, kv_dtype, tn[:, None, :], tw[:, None, :], pref, narrow_dof)
+            c1 = cdf(s[r] + 1, m32[r], inv, kv_dtype, tn[:, None, :], tw[:, None, :], pref, narrow_dof)
+            costs[j] += code_len_q16(c1 - c0).sum(axis=1)
+    out = cands[np.argmin(costs, axis=0)].astype(np.int64)     # the first minimum
+    return (out, costs) if return_costs else out
+
+
+__all__ += ["SPLIT_STEPS", "SPLIT_STEP_BP", "split_budgets", "h_fx_lanes", "split_candidates",
+            "calibrate_split"]
+
+
+# ---------------------------------------------------------------------------
 # S-10  side-information checksum
 # ---------------------------------------------------------------------------
 _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
@@ -587,11 +682,16 @@ def _words_hash(words: np.ndarray, tag: int) -> int:
         return int(np.sum(_mix64(z), dtype=np.uint64))
 
 
-def side_hash(sigma, prefix=None) -> int:
+def side_hash(sigma, prefix=None, split=None) -> int:
     """64-bit checksum of the side information both ends must share
-    (sum mod 2^64 of mixed (index, word) pairs; sigma words tag 1, prefix
-    words tag 2).  Detects a decoder fed different sigma or p_hat."""
-    h = _words_hash(np.asarray(sigma, dtype=np.float32), 1)
+    (sum mod 2^64 of mixed (index, word) pairs; sigma words tag 1, followed
+    in the same sequence by the per-channel split's words when there is one
+    (S-14), prefix words tag 2).  Detects a decoder fed different sigma,
+    split or p_hat."""
+    words = np.ascontiguousarray(np.asarray(sigma, dtype=np.float32)).view(np.uint32).ravel()
+    if split is not None:
+        words = np.concatenate([words, np.asarray(split, dtype=np.int64).astype(np.uint32).ravel()])
+    h = _words_hash(words, 1)
     if prefix is not None:
         h += _words_hash(np.asarray(prefix, dtype=np.int64).astype(np.uint32), 2)
     return h & ((1 << 64) - 1)
@@ -633,7 +733,7 @@ def crc32(data: bytes) -> int:
 
 
 def stream_header(kv_dtype, mu_dtype, w_n, w_w, chunk_tokens, planes, tokens, channels,
-            n_chunks, payload_bytes, shash, sigma_block_tokens=0, narrow_dof=0) -> bytes:
+            n_chunks, payload_bytes, shash, sigma_block_tokens=0, narrow_dof=0, channel_split=0) -> bytes:
     """S-10: the 128-byte header.  Bytes [0, 92) hold the fields, [92, 96)
     the CRC-32 of those 92 bytes (a damaged header is reported as such
     instead of steering the decoder with a wrong shape), the rest zero."""
@@ -641,7 +741,7 @@ def stream_header(kv_dtype, mu_dtype, w_n, w_w, chunk_tokens, planes, tokens, ch
     h = struct.pack(
         _HEADER_FMT,
         MAGIC, VERSION, HEADER_BYTES, kv_dtype, mu_dtype, LOG2_M, LOG2_L,
-        WORD_BITS, LANES, narrow_dof, 0, w_n, w_w, t_n, t_w, t_e, chunk_tokens,
+        WORD_BITS, LANES, narrow_dof, channel_split, w_n, w_w, t_n, t_w, t_e, chunk_tokens,
         planes, tokens, channels, n_chunks, payload_bytes, shash, sigma_block_tokens)
     assert len(h) == HEADER_CRC_OFFSET
     h += struct.pack("<I", crc32(h))
@@ -653,7 +753,7 @@ def parse_header(stream: bytes) -> dict:
         raise StreamError("stream shorter than its header")
     f = struct.unpack_from(_HEADER_FMT, stream, 0)
     keys = ["magic", "version", "header_bytes", "kv_dtype", "mu_dtype", "log2_m",
-            "log2_l", "word_bits", "lanes", "narrow_dof", "reserved", "w_narrow_bp", "w_wide_bp",
+            "log2_l", "word_bits", "lanes", "narrow_dof", "channel_split", "w_narrow_bp", "w_wide_bp",
             "t_n", "t_w", "t_e", "chunk_tokens", "planes", "tokens", "channels",
             "n_chunks", "payload_bytes", "side_hash", "sigma_block_tokens"]
     h = dict(zip(keys, f))
@@ -662,7 +762,7 @@ def parse_header(stream: bytes) -> dict:
     if struct.unpack_from("<I", stream, HEADER_CRC_OFFSET)[0] != crc32(stream[:HEADER_CRC_OFFSET]):
         raise StreamError("header checksum")
     if (h["log2_m"], h["log2_l"], h["word_bits"], h["lanes"]) != (LOG2_M, LOG2_L, WORD_BITS, LANES) \
-            or h["reserved"] != 0 or any(stream[HEADER_CRC_OFFSET + 4:HEADER_BYTES]):
+            or h["channel_split"] > 1 or any(stream[HEADER_CRC_OFFSET + 4:HEADER_BYTES]):
         raise StreamError("unsupported coder parameters")
     if h["kv_dtype"] not in (BF16, E4M3) or h["mu_dtype"] not in (BF16, F32):
         raise StreamError("bad dtype")
@@ -693,10 +793,12 @@ def _roundup8(x):
 
 def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int,
            w_wide_bp: int, chunk_tokens: int, batch_chunks: int = 2048,
-           sigma_block_tokens: int = 0, narrow_dof: int = 0) -> bytes:
+           sigma_block_tokens: int = 0, narrow_dof: int = 0, channel_split=None) -> bytes:
     """Code kv [G, T, D] (raw bit patterns) under the mixture around mu [G, T, D]
     with sigma [G, D] (or, with sigma_block_tokens = B > 0, sigma
-    [G, ceil(T / B), D]: S-11); return the KVC-1 byte stream.
+    [G, ceil(T / B), D]: S-11) and, when ``channel_split`` [G, D] is given,
+    each channel's own split of the Gaussian budget (S-14); return the
+    KVC-1 byte stream.
 
     Per chunk and lane, tokens are coded last to first so that the decoder
     runs first to last (rANS is last-in first-out).  Before a symbol with
@@ -725,6 +827,14 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
     if not 0 <= narrow_dof <= NARROW_DOF_MAX:
         raise ValueError("narrow_dof must be 0 or 1..16")
     pref = prefix if t_e else None
+    if channel_split is not None:
+        channel_split = np.asarray(channel_split, dtype=np.int64)
+        if channel_split.shape != (g_n, d_n):
+            raise ValueError("the channel split is [planes, channels]")
+        tn_all, tw_all = split_budgets(kv_dtype, w_narrow_bp, w_wide_bp, channel_split)
+    else:
+        tn_all = np.full((g_n, d_n), t_n, dtype=np.int64)
+        tw_all = np.full((g_n, d_n), t_w, dtype=np.int64)
     mu32_all = mu_to_f32(mu, mu_dtype)
     sig3, blk = sigma_blocks(sigma, t_len, sigma_block_tokens)
     inv_all = _inv_sigma(sig3)
@@ -740,6 +850,10 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
         nb = g.size
         d = 64 * k[:, None] + lane[None, :]
         inv = inv_all[g[:, None], (tcid * chunk_tokens // blk)[:, None], d]
+        if channel_split is not None:
+            ln_b, lw_b = tn_all[g[:, None], d], tw_all[g[:, None], d]
+        else:
+            ln_b, lw_b = t_n, t_w
         x = np.full((nb, LANES), L, dtype=np.uint64)
         words = np.zeros((nb, chunk_tokens, 2, LANES), dtype=np.uint16)
         emit = np.zeros((nb, chunk_tokens, 2, LANES), dtype=bool)
@@ -748,8 +862,8 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
             tok = np.minimum(tcid * chunk_tokens + t, t_len - 1)[:, None]
             s = sym_all[g[:, None], tok, d]
             mu32 = mu32_all[g[:, None], tok, d]
-            g0 = gauss_cum(s, mu32, inv, kv_dtype, t_n, t_w, narrow_dof)
-            fg = gauss_cum(s + 1, mu32, inv, kv_dtype, t_n, t_w, narrow_dof) - g0
+            g0 = gauss_cum(s, mu32, inv, kv_dtype, ln_b, lw_b, narrow_dof)
+            fg = gauss_cum(s + 1, mu32, inv, kv_dtype, ln_b, lw_b, narrow_dof) - g0
             q0 = escape_cum(s, pref)
             f = fg + escape_cum(s + 1, pref) - q0
             fu = f.astype(np.uint64)
@@ -773,14 +887,15 @@ def encode(kv, mu, sigma, prefix, kv_dtype: int, mu_dtype: int, w_narrow_bp: int
 
     sizes = np.array([len(p) for p in payloads], dtype=np.int64)
     directory = np.concatenate([[0], np.cumsum(sizes)]).astype("<u8")
-    shash = side_hash(sigma, prefix if t_e else None)
+    shash = side_hash(sigma, prefix if t_e else None, channel_split)
     head = stream_header(kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp, chunk_tokens,
-                         g_n, t_len, d_n, n_chunks, int(directory[-1]), shash, sigma_block_tokens, narrow_dof)
+                         g_n, t_len, d_n, n_chunks, int(directory[-1]), shash, sigma_block_tokens, narrow_dof,
+                         0 if channel_split is None else 1)
     return head + directory.tobytes() + b"".join(payloads)
 
 
 def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
-           chunk_ids=None):
+           chunk_ids=None, channel_split=None):
     """Rebuild the raw KV bit patterns [G, T, D] from a KVC-1 stream.
 
     Per token step and lane: target = x mod M.  A target below T_n + T_w is
@@ -794,7 +909,8 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
     must consume exactly its payload, else the stream is corrupt.
 
     With ``chunk_ids`` only those chunks are decoded; the result is then a
-    dict {chunk id: [length, 64] bit patterns}.
+    dict {chunk id: [length, 64] bit patterns}.  A stream coded with a
+    per-channel split (S-14) needs the same split.
     """
     h = parse_header(stream)
     kv_dtype, mu_dtype = h["kv_dtype"], h["mu_dtype"]
@@ -805,7 +921,15 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
     pref = prefix if t_e else None
     if t_e and prefix is None:
         raise ValueError("stream uses an escape part; the marginal prefix is needed")
-    if side_hash(sigma, pref) != h["side_hash"]:
+    split = None
+    if h["channel_split"]:
+        if channel_split is None:
+            raise ValueError("stream uses a per-channel split; the split is needed")
+        split = np.asarray(channel_split, dtype=np.int64)
+        if split.shape != (g_n, d_n):
+            raise ValueError("the channel split is [planes, channels]")
+        tn_all, tw_all = split_budgets(kv_dtype, h["w_narrow_bp"], h["w_wide_bp"], split)
+    if side_hash(sigma, pref, split) != h["side_hash"]:
         raise StreamError("side information does not match the stream")
     dir_off = HEADER_BYTES
     pay_off = dir_off + 8 * (n_chunks + 1)
@@ -840,6 +964,7 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
         nb = cid.size
         d = 64 * k[:, None] + lane[None, :]
         inv = inv_all[g[:, None], (tcid * tcn // blk)[:, None], d]
+        ln_b, lw_b = (tn_all[g[:, None], d], tw_all[g[:, None], d]) if split is not None else (t_n, t_w)
         start_b = pay_off + directory[cid]
         size_b = directory[cid + 1] - directory[cid]
         x = np.stack([np.frombuffer(stream, dtype="<u8", count=LANES, offset=int(o)) for o in start_b]).astype(np.uint64)
@@ -869,14 +994,14 @@ def decode(stream: bytes, mu, sigma, prefix, batch_chunks: int = 2048,
             hi_q = np.full((nb, LANES), n_sym, dtype=np.int64)
             for _ in range(steps):
                 mid = (lo_g + hi_g) >> 1
-                go = gauss_cum(mid, mu32, inv, kv_dtype, t_n, t_w, dof) <= target
+                go = gauss_cum(mid, mu32, inv, kv_dtype, ln_b, lw_b, dof) <= target
                 lo_g, hi_g = np.where(go, mid, lo_g), np.where(go, hi_g, mid)
                 mid = (lo_q + hi_q) >> 1
                 go = escape_cum(mid, pref) <= y
                 lo_q, hi_q = np.where(go, mid, lo_q), np.where(go, hi_q, mid)
             lo = np.where(in_g, lo_g, lo_q)
-            g0 = gauss_cum(lo, mu32, inv, kv_dtype, t_n, t_w, dof)
-            fg = gauss_cum(lo + 1, mu32, inv, kv_dtype, t_n, t_w, dof) - g0
+            g0 = gauss_cum(lo, mu32, inv, kv_dtype, ln_b, lw_b, dof)
+            fg = gauss_cum(lo + 1, mu32, inv, kv_dtype, ln_b, lw_b, dof) - g0
             q0 = escape_cum(lo, pref)
             f = (fg + escape_cum(lo + 1, pref) - q0).astype(np.uint64)
             r = np.where(in_g, target - g0, fg + (y - q0)).astype(np.uint64)
@@ -1007,7 +1132,7 @@ def sigma_per_token(sigma, tokens: int, sigma_block_tokens: int = 0) -> np.ndarr
 
 
 def model_bits_int(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
-                   sigma_block_tokens: int = 0, narrow_dof: int = 0) -> float:
+                   sigma_block_tokens: int = 0, narrow_dof: int = 0, channel_split=None) -> float:
     """Mean of -log2(f(s) / M) over all scalars: the ideal code length of the
     integer model ([wiki] § core idea: bits = cross-entropy of q)."""
     kv = np.asarray(kv)
@@ -1018,9 +1143,12 @@ def model_bits_int(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wid
     mu32 = mu_to_f32(mu, mu_dtype)
     s = order_index(kv, kv_dtype)
     total = 0.0
+    if channel_split is not None:
+        tn_all, tw_all = split_budgets(kv_dtype, w_narrow_bp, w_wide_bp, channel_split)
     for g in range(g_n):
-        c0 = cdf(s[g], mu32[g], inv[g], kv_dtype, t_n, t_w, pref, narrow_dof)
-        c1 = cdf(s[g] + 1, mu32[g], inv[g], kv_dtype, t_n, t_w, pref, narrow_dof)
+        ln_g, lw_g = (tn_all[g][None, :], tw_all[g][None, :]) if channel_split is not None else (t_n, t_w)
+        c0 = cdf(s[g], mu32[g], inv[g], kv_dtype, ln_g, lw_g, pref, narrow_dof)
+        c1 = cdf(s[g] + 1, mu32[g], inv[g], kv_dtype, ln_g, lw_g, pref, narrow_dof)
         total += float(np.sum(LOG2_M - np.log2((c1 - c0).astype(np.float64))))
     return total / kv.size
 
@@ -1048,13 +1176,15 @@ def _stdtr_mass(a: np.ndarray, b: np.ndarray, nu: int) -> np.ndarray:
 
 
 def model_bits_float(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
-                     cap_bits: float = 64.0, sigma_block_tokens: int = 0, narrow_dof: int = 0) -> float:
+                     cap_bits: float = 64.0, sigma_block_tokens: int = 0, narrow_dof: int = 0,
+                     channel_split=None) -> float:
     """Mean -log2 q(x) of the continuous mixture over the same cells, float64.
 
     q(x) = w_n [Phi((hi-mu)/sigma) - Phi((lo-mu)/sigma)]
          + w_w [same with 3 sigma] + w_e p_hat(x),
     (with narrow_dof = nu, the narrow part's Phi is the truncated Student-t
-    of S-13),
+    of S-13; with a per-channel split, w_n and w_w are the channel's w_c and
+    w_n + w_w - w_c, S-14),
     with p_hat(x) = (prefix[x+1] - prefix[x]) / T_e and the weights in basis
     points ([wiki] § mixture distribution).  A per-scalar cost is capped at
     ``cap_bits`` (only reachable without an escape part)."""
@@ -1062,6 +1192,9 @@ def model_bits_float(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_w
     t_n, t_w, t_e = budgets(kv_dtype, w_narrow_bp, w_wide_bp)
     wn, ww = w_narrow_bp / 1e4, w_wide_bp / 1e4
     we = 1.0 - wn - ww
+    if channel_split is not None:
+        wn = np.asarray(channel_split, dtype=np.float64)[:, None, :] / 1e4 * np.ones((1, kv.shape[1], 1))
+        ww = (w_narrow_bp + w_wide_bp) / 1e4 - wn
     pos = boundary_positions(kv_dtype).astype(np.float64)
     sig = sigma_per_token(sigma, kv.shape[1], sigma_block_tokens).astype(np.float64)
     mu_all = mu_to_f32(mu, mu_dtype).astype(np.float64)
@@ -1076,7 +1209,9 @@ def model_bits_float(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_w
             a1, b1 = (lo - m) / sg, (hi - m) / sg
             a3, b3 = (lo - m) / (3 * sg), (hi - m) / (3 * sg)
         narrow = _ndtr_diff(a1, b1) if narrow_dof == 0 else _stdtr_mass(a1, b1, narrow_dof)
-        q = wn * narrow + ww * _ndtr_diff(a3, b3)
+        wn_g = wn[g] if np.ndim(wn) else wn
+        ww_g = ww[g] if np.ndim(ww) else ww
+        q = wn_g * narrow + ww_g * _ndtr_diff(a3, b3)
         if t_e:
             p = np.asarray(prefix, dtype=np.float64)
             q = q + we * (p[s[g] + 1] - p[s[g]]) / t_e
