@@ -84,6 +84,25 @@ uint64_t sigma_words(const ChunkGeom& g) {
     return uint64_t(g.planes) * uint64_t(g.sigma_blocks) * uint64_t(g.channels);
 }
 
+// Words of the side buffer: sigma, then (with a per-channel split) the
+// narrow weight of every (plane, channel).
+uint64_t side_words(const ChunkGeom& g, uint32_t channel_split) {
+    return sigma_words(g) + (channel_split ? uint64_t(g.planes) * uint64_t(g.channels) : 0u);
+}
+
+// The kernels' view of a per-channel split (no split: words null).
+kvc::SplitArgs split_args(uint32_t channel_split, const ChunkGeom& g, const float* d_side, int32_t kv_dtype,
+                          uint32_t w_narrow_bp, uint32_t w_wide_bp, const kvc::PhiTables& phi) {
+    kvc::SplitArgs a;
+    if (!channel_split) return a;
+    a.words = reinterpret_cast<const uint32_t*>(d_side) + sigma_words(g);
+    a.a = phi.a;
+    a.b = phi.b;
+    a.t_all = static_cast<uint32_t>((uint64_t(1) << kLog2M) - alphabet(kv_dtype));
+    a.w_gauss = w_narrow_bp + w_wide_bp;
+    return a;
+}
+
 // Default chunk length.  Each chunk is one wave and MI355X holds 8,192 of
 // them at once (256 CUs x 32 waves), so a call runs in rounds of 8,192
 // chunks, each round as long as one chunk.  Among the lengths
@@ -127,7 +146,7 @@ uint32_t default_chunk_tokens(int64_t planes, int64_t tokens, int64_t channels, 
 
 bool params_geometry(const kvc_params* p, ChunkGeom* g) {
     if (!p || !kv_dtype_ok(p->kv_dtype) || !mu_dtype_ok(p->mu_dtype)) return false;
-    if (p->narrow_dof > uint32_t(kvc::kNarrowDofMax) || p->reserved != 0) return false;
+    if (p->narrow_dof > uint32_t(kvc::kNarrowDofMax) || p->channel_split > 1) return false;
     uint32_t tc = p->chunk_tokens;
     if (tc == 0) tc = default_chunk_tokens(p->planes, p->tokens, p->channels, p->sigma_block_tokens);
     return geometry(p->planes, p->tokens, p->channels, tc, p->sigma_block_tokens, g);
@@ -177,6 +196,7 @@ kvc::StreamHeader make_header(const kvc_params* p, const ChunkGeom& g, uint32_t 
     h.bytes[12] = kWordBits;
     h.bytes[13] = kLanes;
     h.bytes[14] = static_cast<uint8_t>(p->narrow_dof);
+    h.bytes[15] = static_cast<uint8_t>(p->channel_split);
     put32(h.bytes, 16, p->w_narrow_bp);
     put32(h.bytes, 20, p->w_wide_bp);
     put32(h.bytes, 24, tn);
@@ -207,7 +227,7 @@ int parse_header(const uint8_t* b, kvc_params* p, ChunkGeom* g, uint64_t* payloa
         return KVC_ERR_CORRUPT;
     if (get32(b, kvc::kHeaderCrcOffset) != crc32(b, kvc::kHeaderCrcOffset)) return KVC_ERR_CORRUPT;
     if (b[10] != kLog2M || b[11] != kLog2L || b[12] != kWordBits || b[13] != kLanes ||
-        b[14] > kvc::kNarrowDofMax || b[15] != 0)
+        b[14] > kvc::kNarrowDofMax || b[15] > 1)
         return KVC_ERR_CORRUPT;
     kvc_params q;
     std::memset(&q, 0, sizeof(q));
@@ -221,6 +241,7 @@ int parse_header(const uint8_t* b, kvc_params* p, ChunkGeom* g, uint64_t* payloa
     q.channels = static_cast<int64_t>(get64(b, 56));
     q.sigma_block_tokens = get32(b, 88);
     q.narrow_dof = b[14];
+    q.channel_split = b[15];
     uint32_t tn, tw, te;
     if (!kv_dtype_ok(q.kv_dtype) || !mu_dtype_ok(q.mu_dtype) ||
         !budgets(q.kv_dtype, q.w_narrow_bp, q.w_wide_bp, &tn, &tw, &te))
@@ -364,7 +385,7 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     timer.mark(0);
     kvc::PrologueArgs pa;
     pa.sigma_words = reinterpret_cast<const uint32_t*>(d_sigma);
-    pa.n_sigma = sigma_words(g);
+    pa.n_sigma = side_words(g, p->channel_split);
     pa.prefix_words = prefix;
     pa.n_prefix = prefix ? alphabet(p->kv_dtype) + 1u : 0u;
     pa.prefix = prefix ? prefix : phi.zero;
@@ -392,6 +413,7 @@ int kvc_encode(const kvc_params* p, const void* d_kv, const void* d_mu, const fl
     ea.out_capacity = out_capacity;
     ea.header = make_header(p, g, tn, tw, te);
     ea.header_copy = ws + kvc::kHeaderCopyOffset;
+    ea.split = split_args(p->channel_split, g, d_sigma, p->kv_dtype, p->w_narrow_bp, p->w_wide_bp, phi);
     ea.ctl = ctl;
     timer.mark(1);
     if ((e = kvc::launch_encode(ea, p->kv_dtype, p->mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
@@ -494,7 +516,8 @@ int decode_check(const void* h_header, const void* d_in, uint64_t in_bytes, cons
     // the caller's buffers must hold what the header describes
     const uint64_t n = uint64_t(g.planes) * uint64_t(g.tokens) * uint64_t(g.channels);
     plan->n_sym = alphabet(p.kv_dtype);
-    if (mu_bytes / mu_size(p.mu_dtype) < n || sigma_bytes / 4u < sigma_words(g)) return KVC_ERR_INVALID;
+    if (mu_bytes / mu_size(p.mu_dtype) < n || sigma_bytes / 4u < side_words(g, p.channel_split))
+        return KVC_ERR_INVALID;
     if (plan->prefix && prefix_bytes / 4u < uint64_t(plan->n_sym) + 1u) return KVC_ERR_INVALID;
     if (!paged && kv_out_bytes / kv_size(p.kv_dtype) < n) return KVC_ERR_INVALID;
     kvc::PagedOut& po = plan->po;
@@ -564,7 +587,7 @@ int decode_launch(const void* h_header, const void* d_in, uint64_t in_bytes, con
     timer.mark(0);
     kvc::PrologueArgs pa;
     pa.sigma_words = reinterpret_cast<const uint32_t*>(d_sigma);
-    pa.n_sigma = sigma_words(g);
+    pa.n_sigma = side_words(g, p.channel_split);
     pa.prefix_words = prefix;
     pa.n_prefix = prefix ? n_sym + 1u : 0u;
     pa.head = static_cast<const uint8_t*>(d_in);
@@ -602,6 +625,7 @@ int decode_launch(const void* h_header, const void* d_in, uint64_t in_bytes, con
     da.kv_out = d_kv_out;
     da.paged = po;
     da.expect_hash = hash;
+    da.split = split_args(p.channel_split, g, d_sigma, p.kv_dtype, p.w_narrow_bp, p.w_wide_bp, phi);
     da.ctl = ctl;
     if ((e = kvc::launch_decode(da, p.kv_dtype, p.mu_dtype, paged != nullptr, s)) != hipSuccess) return KVC_ERR_DEVICE;
     timer.mark(2);
@@ -839,6 +863,40 @@ int kvc_calibrate_sigma_rate(const void* d_kv, const void* d_mu, int32_t kv_dtyp
                                        te ? d_prefix : phi.zero, d_sigma_out, part, s));
 }
 
+int kvc_calibrate_split(const void* d_kv, const void* d_mu, int32_t kv_dtype, int32_t mu_dtype, int64_t reps,
+                        int64_t planes, int64_t tokens, int64_t channels, int64_t block_tokens, const float* d_sigma,
+                        uint32_t w_narrow_bp, uint32_t w_wide_bp, uint32_t narrow_dof, const uint32_t* d_prefix,
+                        uint32_t* d_split_out, void* d_workspace, uint64_t workspace_bytes, void* stream) {
+    uint32_t tn, tw, te;
+    if (!budgets(kv_dtype, w_narrow_bp, w_wide_bp, &tn, &tw, &te) || !mu_dtype_ok(mu_dtype) || (te && !d_prefix))
+        return KVC_ERR_INVALID;
+    if (narrow_dof > uint32_t(kvc::kNarrowDofMax)) return KVC_ERR_INVALID;
+    if (!d_kv || !d_mu || !d_sigma || !d_split_out || !d_workspace) return KVC_ERR_INVALID;
+    if (!data_aligned(kv_dtype, mu_dtype, d_kv, d_mu, d_sigma, d_prefix) || !aligned(d_split_out, 4) ||
+        !aligned(d_workspace, 256))
+        return KVC_ERR_INVALID;
+    if (reps < 1 || block_tokens < 0 || tokens < 1 || planes < 1 || channels < 64 || channels % 64)
+        return KVC_ERR_INVALID;
+    if (planes > kMaxScalars / channels || reps > kMaxScalars / (planes * channels) ||
+        tokens > kMaxScalars / (reps * planes * channels))
+        return KVC_ERR_INVALID;
+    if (workspace_bytes < KVC_CALIBRATE_SPLIT_WORKSPACE_BYTES(planes, channels)) return KVC_ERR_INVALID;
+    static_assert(kvc::kSplitSteps * kvc::kCalibSplitsMax * 8 == 8192, "workspace formula");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    const kvc::PhiTables phi = kvc::device_phi_tables(&e, narrow_dof);
+    if (e != hipSuccess) return KVC_ERR_DEVICE;
+    kvc::SplitArgs sp;
+    sp.a = phi.a;
+    sp.b = phi.b;
+    sp.t_all = static_cast<uint32_t>((uint64_t(1) << kLog2M) - alphabet(kv_dtype));
+    sp.w_gauss = w_narrow_bp + w_wide_bp;
+    return finish(kvc::launch_split_fit(d_kv, d_mu, kv_dtype, mu_dtype, reps, planes, tokens, channels,
+                                        block_tokens >= tokens ? 0 : block_tokens, d_sigma, sp, tn + tw,
+                                        te ? d_prefix : phi.zero, d_split_out,
+                                        static_cast<unsigned long long*>(d_workspace), s));
+}
+
 int kvc_build_marginal(const void* d_samples, int32_t dtype, uint64_t n, uint32_t w_narrow_bp,
                        uint32_t w_wide_bp, uint32_t* d_prefix_out, void* stream) {
     uint32_t tn, tw, te;
@@ -880,11 +938,13 @@ int kvc_estimate_bits(const kvc_params* p, const void* d_kv, const void* d_mu, c
     a.w_wide_bp = p->w_wide_bp;
     a.narrow_dof = p->narrow_dof;
     a.phi = phi;
+    a.split = split_args(p->channel_split, g, d_sigma, p->kv_dtype, p->w_narrow_bp, p->w_wide_bp, phi);
     a.ctl = ctl;
     if ((e = kvc::launch_estimate(a, p->kv_dtype, p->mu_dtype, s)) != hipSuccess) return KVC_ERR_DEVICE;
     Control host;
     if ((e = hipMemcpyAsync(&host, ctl, sizeof(host), hipMemcpyDeviceToHost, s)) != hipSuccess) return KVC_ERR_DEVICE;
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return KVC_ERR_DEVICE;
+    if (host.flags & kvc::kFlagBadSigma) return KVC_ERR_INVALID;
     const double n = static_cast<double>(g.planes) * static_cast<double>(g.tokens) * static_cast<double>(g.channels);
     h_bits_out[0] = host.bits[0] / n;
     h_bits_out[1] = host.bits[1] / n;

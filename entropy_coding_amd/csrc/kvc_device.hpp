@@ -161,6 +161,83 @@ struct Model {
     const uint32_t* __restrict__ eslots;   // bf16 encoder only: the escape slot table (k_prologue)
     uint32_t htot;                         // T_n + T_w, where the floor-and-escape range starts
     const uint32_t* __restrict__ ecount;   // bf16 decoder only: the escape count table (k_prologue)
+
+    // The narrow and wide parts of the CDF at q (both Gaussian parts, 0 .. htot).
+    __device__ __forceinline__ uint32_t h(int32_t q) const { return h_fx(q, tab); }
+
+    // The model of lane L, for a search the whole wave makes for one lane
+    // (the same on every lane here).
+    __device__ __forceinline__ Model of_lane(int) const { return *this; }
+};
+
+// (a b) >> 31 for a < 2^31 and b <= 2^31 (the product is below 2^62).
+__device__ __forceinline__ uint32_t mul_shr31(uint32_t a, uint32_t b) {
+    return static_cast<uint32_t>((static_cast<uint64_t>(a) * b) >> 31);
+}
+
+// A lane's own split of the Gaussian budget: T_n(c) = min(floor(T w_c /
+// 10^4), T_n + T_w) for the narrow weight w_c in basis points (T = M - N);
+// the wide part gets the rest of T_n + T_w.
+__device__ __forceinline__ uint32_t split_narrow_budget(uint32_t w, uint32_t t_all, uint32_t htot) {
+    const uint64_t v = static_cast<uint64_t>(t_all) * w / 10000u;
+    return v < htot ? static_cast<uint32_t>(v) : htot;
+}
+
+// h_fx with the lane's own budgets: the pair table holds (A[k], B[k]), the
+// narrow and wide base tables (the last entry repeated), and the lane's
+// mixture table entry floor(tn A[k] / 2^31) + floor(tw B[k] / 2^31) is
+// formed at the two entries the interpolation reads.  tn + tw <= T, so a
+// step of the lane's table is at most a step of either base table scaled by
+// its budget share, plus 1 for the floors: below 2^22 as for h_fx.
+__device__ __forceinline__ uint32_t h_fx_split(int32_t q, const uint2* __restrict__ ab, uint32_t tn, uint32_t tw,
+                                               uint32_t& step) {
+    const uint32_t u = static_cast<uint32_t>(q + kQMax);
+    const uint32_t i = u >> 16, r = u & 0xFFFFu;
+    const uint2 p0 = ab[i], p1 = ab[i + 1];
+    const uint32_t a = mul_shr31(tn, p0.x) + mul_shr31(tw, p0.y);
+    const uint32_t c = mul_shr31(tn, p1.x) + mul_shr31(tw, p1.y);
+    const uint32_t dlt = c - a;
+    __builtin_assume(dlt < (1u << 22));
+    step = dlt;
+    return a + static_cast<uint32_t>((static_cast<uint64_t>(dlt) * r) >> 16);
+}
+
+// The model of a chunk whose lanes each split the Gaussian budget their own
+// way: tab points at the pair table in LDS, tn / tw are the lane's budgets
+// (tn + tw = htot on every lane, so the floor-and-escape range and its
+// tables are shared).
+struct SplitModel : Model {
+    uint32_t tn, tw;
+
+    __device__ __forceinline__ uint32_t h(int32_t q) const {
+        uint32_t step;
+        return h_fx_split(q, reinterpret_cast<const uint2*>(tab), tn, tw, step);
+    }
+
+    // The model of lane L on every lane: its budgets.
+    __device__ __forceinline__ SplitModel of_lane(int L) const {
+        SplitModel r = *this;
+        r.tn = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tn), L));
+        r.tw = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tw), L));
+        return r;
+    }
+
+    // The decoder's aim for target t from a z that inverts the call's own
+    // mixture table: one Newton step on this lane's table, whose slope over
+    // a grid step (1/256 in z) is the interpolation step.  Only the cost of
+    // the search depends on it.
+    __device__ __forceinline__ float aim(float z, uint32_t t) const {
+        float zq = __fmul_rn(z, 16777216.0f);
+        zq = __builtin_amdgcn_fmed3f(zq, -kQMaxF, kQMaxF);
+        int32_t q;
+        __asm__("v_cvt_flr_i32_f32 %0, %1" : "=v"(q) : "v"(zq));
+        uint32_t step;
+        const uint32_t hq = h_fx_split(q, reinterpret_cast<const uint2*>(tab), tn, tw, step);
+        const float dz = static_cast<float>(static_cast<int32_t>(t - hq)) *
+                         __builtin_amdgcn_rcpf(static_cast<float>(step) * 256.0f);
+        const float zn = step ? z + dz : z;
+        return __builtin_amdgcn_fmed3f(zn, -static_cast<float>(kTableZMax), static_cast<float>(kTableZMax));
+    }
 };
 
 // Two consecutive u32 at byte offset `off` of `base` in one 8-byte read
@@ -172,10 +249,10 @@ __device__ __forceinline__ U32Pair load_pair(const uint32_t* base, uint32_t off)
     return *reinterpret_cast<const U32Pair*>(reinterpret_cast<const char*>(base) + off);
 }
 
-// C(b) = b + h_fx(q(b)) + prefix[b].
-template <int KV>
-__device__ __forceinline__ uint32_t cdf_at(uint32_t b, float mu, float inv24, const Model& m) {
-    uint32_t g = b + h_fx(z_fixed(edge<KV>(b), mu, inv24), m.tab);
+// C(b) = b + h(q(b)) + prefix[b].
+template <int KV, class M>
+__device__ __forceinline__ uint32_t cdf_at(uint32_t b, float mu, float inv24, const M& m) {
+    uint32_t g = b + m.h(z_fixed(edge<KV>(b), mu, inv24));
     g += m.prefix[b];
     return g;
 }

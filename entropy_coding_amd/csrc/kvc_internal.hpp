@@ -64,6 +64,19 @@ struct StreamHeader {
     uint8_t bytes[128];
 };
 
+// A per-channel split of the Gaussian budget: words[g * channels + c] is
+// the narrow weight (basis points) of plane g, channel c; the kernels form
+// the pair table (A[k], B[k]) in LDS from the base tables a, b and each
+// lane's budgets from t_all = M - N and htot = T_n + T_w.  words null: the
+// call's own weights everywhere.
+struct SplitArgs {
+    const uint32_t* words = nullptr;
+    const uint32_t* a = nullptr;        // the narrow part's base table (kPhiPoints entries)
+    const uint32_t* b = nullptr;        // the wide part's base table
+    uint32_t t_all = 0;
+    uint32_t w_gauss = 0;               // w_n + w_w: the largest narrow weight accepted
+};
+
 struct EncodeArgs {
     ChunkGeom geom;
     const void* kv;
@@ -80,6 +93,7 @@ struct EncodeArgs {
     uint64_t out_capacity;
     StreamHeader header;                // the stream header but for payload size, checksum and CRC
     uint8_t* header_copy;               // the workspace's copy of the finished header
+    SplitArgs split;
     Control* ctl;
 };
 
@@ -113,6 +127,7 @@ struct DecodeArgs {
     void* kv_out;                       // contiguous output [planes][tokens][channels], or
     PagedOut paged;                     // the paged output (launch_decode with paged = true)
     unsigned long long expect_hash;     // the header's side-information checksum
+    SplitArgs split;
     Control* ctl;
 };
 
@@ -126,6 +141,7 @@ struct EstimateArgs {
     uint32_t w_narrow_bp, w_wide_bp;
     uint32_t narrow_dof;                // 0: Gaussian narrow part; nu: Student's t (float model)
     PhiTables phi;
+    SplitArgs split;
     Control* ctl;
 };
 
@@ -226,6 +242,17 @@ hipError_t launch_rate_fit(const void* kv, const void* mu, int kv_dtype, int mu_
                            int64_t tokens, int64_t channels, int64_t block_tokens, float sigma_floor,
                            const uint32_t* table, const uint32_t* prefix, float* sigma_io, unsigned long long* part,
                            hipStream_t s);
+// Per-channel split: out[plane][channel] becomes the candidate narrow
+// weight max(w_gauss - kSplitStepBp j, 0), j < kSplitSteps, with the least
+// integer code length of the held-out data under sigma (per block of
+// block_tokens tokens when not 0) and the escape prefix.  part: kSplitSteps
+// x splits x (planes x channels) u64.
+constexpr int kSplitSteps = 16;
+constexpr uint32_t kSplitStepBp = 200;
+hipError_t launch_split_fit(const void* kv, const void* mu, int kv_dtype, int mu_dtype, int64_t reps, int64_t planes,
+                            int64_t tokens, int64_t channels, int64_t block_tokens, const float* sigma,
+                            const SplitArgs& sp, uint32_t htot, const uint32_t* prefix, uint32_t* out,
+                            unsigned long long* part, hipStream_t s);
 hipError_t launch_marginal(const void* samples, int dtype, uint64_t n, uint32_t te,
                            uint32_t* prefix_out, hipStream_t s);
 hipError_t launch_estimate(const EstimateArgs& a, int kv_dtype, int mu_dtype, hipStream_t s);

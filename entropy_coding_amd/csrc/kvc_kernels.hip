@@ -213,6 +213,18 @@ __device__ __forceinline__ void copy_to_lds(void* dst, const void* __restrict__ 
     __syncthreads();
 }
 
+// The pair table of a per-lane split: (A[k], B[k]) for k = 0 .. 12291, the
+// narrow and wide base tables with their last entry repeated; ends with a
+// barrier.
+__device__ __forceinline__ void fill_pairs_lds(uint2* s_ab, const uint32_t* __restrict__ a,
+                                               const uint32_t* __restrict__ b) {
+    for (int k = threadIdx.x; k < static_cast<int>(kTableWordsPadded); k += blockDim.x) {
+        const int kk = k < kTablePoints ? k : kTablePoints - 1;
+        s_ab[k] = make_uint2(a[kk], b[kk]);
+    }
+    __syncthreads();
+}
+
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;
@@ -356,8 +368,8 @@ __device__ __forceinline__ U32Pair escape_entry(uint32_t kb, const Model& m) {
     else return U32Pair{0u, 0u};
 }
 
-template <int KV, int MU>
-__device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float inv24, const Model& m, U32Pair q) {
+template <int KV, int MU, class M>
+__device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float inv24, const M& m, U32Pair q) {
     if constexpr (KV == kBF16 && MU == kBF16) {
         // both cell edges carry the value's sign; h is monotone in the
         // position, so the lower edge's h is the smaller one on either side
@@ -367,14 +379,14 @@ __device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float in
         const uint32_t ib = __builtin_elementwise_sub_sat(ob0, 0x10000u);  // 0 for +-0
         const uint32_t ob = __builtin_elementwise_min(ob0, 0x7F800000u);
         const uint32_t sb = (kb & 0x8000u) << 16;
-        const uint32_t ha = h_fx(z_fixed(__uint_as_float(ib | sb), mu, inv24), m.tab);
-        const uint32_t hb = h_fx(z_fixed(__uint_as_float(ob | sb), mu, inv24), m.tab);
+        const uint32_t ha = m.h(z_fixed(__uint_as_float(ib | sb), mu, inv24));
+        const uint32_t hb = m.h(z_fixed(__uint_as_float(ob | sb), mu, inv24));
         return make_slots(ha, hb, q);
     }
     if constexpr (KV == kE4M3) {
         const uint32_t s = order_of_bits<KV>(kb);
-        const uint32_t ha = h_fx(z_fixed(e4_edge(m.small, s), mu, inv24), m.tab);
-        const uint32_t hb = h_fx(z_fixed(e4_edge(m.small, s + 1u), mu, inv24), m.tab);
+        const uint32_t ha = m.h(z_fixed(e4_edge(m.small, s), mu, inv24));
+        const uint32_t hb = m.h(z_fixed(e4_edge(m.small, s + 1u), mu, inv24));
         const uint32_t p0 = m.small[s], p1 = m.small[s + 1u];
         SymSlots y;
         y.g0 = ha;
@@ -385,8 +397,8 @@ __device__ __forceinline__ SymSlots symbol_slots(uint32_t kb, float mu, float in
     }
     float lo, hi;
     bf16_cell_edges(kb, lo, hi);
-    const uint32_t ha = h_fx(z_fixed(lo, mu, inv24), m.tab);
-    const uint32_t hb = h_fx(z_fixed(hi, mu, inv24), m.tab);
+    const uint32_t ha = m.h(z_fixed(lo, mu, inv24));
+    const uint32_t hb = m.h(z_fixed(hi, mu, inv24));
     return make_slots(ha, hb, q);
 }
 
@@ -399,10 +411,10 @@ __device__ __forceinline__ uint32_t load_row_elem(__amdgpu_buffer_rsrc_t r, uint
     else return __builtin_amdgcn_raw_buffer_load_b32(r, lane_off, row_off, 0);
 }
 
-template <int KV, int MU, int U>
+template <int KV, int MU, int U, class M>
 __device__ __forceinline__ void encode_batch(int t, PushState& st, __amdgpu_buffer_rsrc_t kvr,
                                              __amdgpu_buffer_rsrc_t mur, uint32_t D, uint32_t lane,
-                                             float inv24, const Model& m, uint16_t* __restrict__ slot) {
+                                             float inv24, const M& m, uint16_t* __restrict__ slot) {
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
     uint32_t kb[U];
@@ -450,10 +462,10 @@ __device__ __forceinline__ void load_rows(int t, uint32_t (&kr)[U], uint32_t (&m
 // the reads matters: the vector-memory counter completes in order, so this
 // batch's escape-entry reads are issued before the next batch's rows and
 // their wait does not include those HBM reads.
-template <int KV, int MU, int U>
+template <int KV, int MU, int U, class M>
 __device__ __forceinline__ void encode_batch_ahead(uint32_t (&kr)[U], uint32_t (&mr)[U], int t_next, PushState& st,
                                                    __amdgpu_buffer_rsrc_t kvr, __amdgpu_buffer_rsrc_t mur,
-                                                   uint32_t D, uint32_t lane, float inv24, const Model& m,
+                                                   uint32_t D, uint32_t lane, float inv24, const M& m,
                                                    uint16_t* __restrict__ slot) {
     uint32_t kb[U];
     float mus[U];
@@ -631,14 +643,17 @@ __device__ __forceinline__ void copy_words(const uint32_t* __restrict__ src, boo
     }
 }
 
-template <int KV, int MU>
+// SPLIT: every (plane, channel) has its own split of the Gaussian budget
+// (the pair table in LDS instead of the mixture table).
+template <int KV, int MU, bool SPLIT>
 __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
-    __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
+    __shared__ __align__(16) uint32_t s_tab[SPLIT ? 2 * kTableWordsPadded : kTableWordsPadded];
     __shared__ uint32_t s_small[KV == kE4M3 ? kE4Words : 1];
     __shared__ unsigned long long s_head[kHeaderBytes / 8];        // the last chunk's header
     __shared__ uint32_t s_crc[256];                                // the last chunk's CRC-32 table
     if constexpr (KV == kE4M3) build_e4_lds(s_small, a.prefix);
-    copy_to_lds(s_tab, a.table, static_cast<uint32_t>(kTableBytes / 16));
+    if constexpr (SPLIT) fill_pairs_lds(reinterpret_cast<uint2*>(s_tab), a.split.a, a.split.b);
+    else copy_to_lds(s_tab, a.table, static_cast<uint32_t>(kTableBytes / 16));
 
     const uint32_t lane = threadIdx.x & 63u;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -653,7 +668,19 @@ __global__ void __launch_bounds__(kEncodeBlock) k_encode(EncodeArgs a) {
         if (lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
         inv24 = 16777216.0f;
     }
-    const Model m{s_tab, a.prefix, s_small, a.eslots, a.tn + a.tw};
+    const Model base{s_tab, a.prefix, s_small, a.eslots, a.tn + a.tw};
+    // a weight above w_n + w_w is refused (as a bad sigma); the budget is
+    // capped meanwhile, so the chunk still codes within its slot
+    const auto m = [&]() {
+        if constexpr (SPLIT) {
+            const uint32_t w = a.split.words[cp.g * D + cp.k * 64 + lane];
+            if (__ballot(w > a.split.w_gauss) && lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
+            const uint32_t tn = split_narrow_budget(w, a.split.t_all, base.htot);
+            return SplitModel{base, tn, base.htot - tn};
+        } else {
+            return base;
+        }
+    }();
 
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
@@ -722,11 +749,18 @@ hipError_t launch_encode(const EncodeArgs& a, int kv_dtype, int mu_dtype, hipStr
     constexpr int waves = kEncodeBlock / 64;
     const uint64_t blocks = (static_cast<uint64_t>(a.geom.n_chunks) + waves - 1) / waves;
     const dim3 grid(static_cast<uint32_t>(blocks)), block(kEncodeBlock);
-    if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_encode<kBF16, kBF16>), grid, block, 0, s, a);
-    else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_encode<kBF16, kF32>), grid, block, 0, s, a);
-    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_encode<kE4M3, kBF16>), grid, block, 0, s, a);
-    else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_encode<kE4M3, kF32>), grid, block, 0, s, a);
+    const bool sp = a.split.words != nullptr;
+#define KVC_ENC(K, U)                                                                \
+    do {                                                                             \
+        if (sp) hipLaunchKernelGGL((k_encode<K, U, true>), grid, block, 0, s, a);    \
+        else hipLaunchKernelGGL((k_encode<K, U, false>), grid, block, 0, s, a);      \
+    } while (0)
+    if (kv_dtype == kBF16 && mu_dtype == kBF16) KVC_ENC(kBF16, kBF16);
+    else if (kv_dtype == kBF16 && mu_dtype == kF32) KVC_ENC(kBF16, kF32);
+    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) KVC_ENC(kE4M3, kBF16);
+    else if (kv_dtype == kE4M3 && mu_dtype == kF32) KVC_ENC(kE4M3, kF32);
     else return hipErrorInvalidValue;
+#undef KVC_ENC
     return hipGetLastError();
 }
 
@@ -902,14 +936,14 @@ __device__ __forceinline__ uint32_t index_of_candidate(uint32_t cand) {
 // reach here only from the escape lookup, and their G terms are replaced
 // by the caller (every edge of theirs is infinite).  The escape slot count
 // comes from the escape count table, at the pattern's entry.
-template <int MU>
-__device__ __forceinline__ Cell eval_bf16(uint32_t kw, float mu, float inv24, const Model& m) {
+template <int MU, class M>
+__device__ __forceinline__ Cell eval_bf16(uint32_t kw, float mu, float inv24, const M& m) {
     const uint32_t sign = kw & 0x80000000u;
     uint32_t ob = (kw & 0xFFFF0000u) | 0x8000u;
     const uint32_t ib = __builtin_elementwise_max(__builtin_elementwise_sub_sat(ob, 0x10000u), sign);
     if constexpr (MU == kF32) ob = (kw & 0x7FFF0000u) == 0x7F7F0000u ? (sign | 0x7F800000u) : ob;
-    const uint32_t ha = h_fx(z_fixed(__uint_as_float(ib), mu, inv24), m.tab);
-    const uint32_t hb = h_fx(z_fixed(__uint_as_float(ob), mu, inv24), m.tab);
+    const uint32_t ha = m.h(z_fixed(__uint_as_float(ib), mu, inv24));
+    const uint32_t hb = m.h(z_fixed(__uint_as_float(ob), mu, inv24));
     Cell c;
     c.g0 = __builtin_elementwise_min(ha, hb);
     c.g1 = __builtin_elementwise_max(ha, hb);
@@ -918,17 +952,18 @@ __device__ __forceinline__ Cell eval_bf16(uint32_t kw, float mu, float inv24, co
 }
 
 // Cell of the e4m3 pattern kb: edges and prefix from the LDS copies.
-__device__ __forceinline__ Cell eval_e4m3(uint32_t kb, float mu, float inv24, const Model& m) {
+template <class M>
+__device__ __forceinline__ Cell eval_e4m3(uint32_t kb, float mu, float inv24, const M& m) {
     Cell c;
     const uint32_t s = order_of_bits<kE4M3>(kb);
-    c.g0 = h_fx(z_fixed(e4_edge(m.small, s), mu, inv24), m.tab);
-    c.g1 = h_fx(z_fixed(e4_edge(m.small, s + 1u), mu, inv24), m.tab);
+    c.g0 = m.h(z_fixed(e4_edge(m.small, s), mu, inv24));
+    c.g1 = m.h(z_fixed(e4_edge(m.small, s + 1u), mu, inv24));
     c.qf = 1u + (m.small[s + 1u] - m.small[s]);
     return c;
 }
 
-template <int KV, int MU>
-__device__ __forceinline__ Cell eval_cell(uint32_t kb, float mu, float inv24, const Model& m) {
+template <int KV, int MU, class M>
+__device__ __forceinline__ Cell eval_cell(uint32_t kb, float mu, float inv24, const M& m) {
     if constexpr (KV == kBF16) return eval_bf16<MU>(kb, mu, inv24, m);
     else return eval_e4m3(kb, mu, inv24, m);
 }
@@ -949,10 +984,10 @@ __device__ __forceinline__ float edge_from_index_bf16(uint32_t b) {
 
 // G(b), the mixture-table term of the CDF at edge b, for the
 // wave-cooperative search (bf16 edge from the index; e4m3 edge from LDS).
-template <int KV, int MU>
-__device__ __forceinline__ uint32_t gauss_probe(uint32_t b, float mu, float inv24, const Model& m) {
-    if constexpr (KV == kBF16) return h_fx(z_fixed(edge_from_index_bf16<MU>(b), mu, inv24), m.tab);
-    else return h_fx(z_fixed(e4_edge(m.small, b), mu, inv24), m.tab);
+template <int KV, int MU, class M>
+__device__ __forceinline__ uint32_t gauss_probe(uint32_t b, float mu, float inv24, const M& m) {
+    if constexpr (KV == kBF16) return m.h(z_fixed(edge_from_index_bf16<MU>(b), mu, inv24));
+    else return m.h(z_fixed(e4_edge(m.small, b), mu, inv24));
 }
 
 // Probe offsets for the first cooperative round: 1, 2, 3, ... then growing
@@ -966,10 +1001,12 @@ __device__ __forceinline__ uint32_t geo_offset(int lane) {
 // Gaussian-range slot the aim did not bracket: the whole wave resolves
 // every lane with `need` set, one lane at a time.  [lo, hi) brackets the
 // lane's symbol with G(lo) = glo <= target < G(hi) = ghi; `up` tells which
-// end is the known near one (lo if up).  Returns s.
-template <int KV, int MU>
+// end is the known near one (lo if up).  Every lane probes with the
+// searched lane's mean, scale and model (with a per-channel split, its
+// budgets).  Returns s.
+template <int KV, int MU, class M>
 __device__ __forceinline__ uint32_t coop_gauss(bool need, uint32_t target, float mu, float inv24, bool up, uint32_t lo,
-                                               uint32_t hi, uint32_t glo, uint32_t ghi, const Model& m, uint32_t geo,
+                                               uint32_t hi, uint32_t glo, uint32_t ghi, const M& m, uint32_t geo,
                                                uint32_t s_in) {
     const int lane = threadIdx.x & 63;
     uint32_t s_out = s_in;
@@ -981,6 +1018,7 @@ __device__ __forceinline__ uint32_t coop_gauss(bool need, uint32_t target, float
         const float mL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mu), L));
         const float iL = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv24), L));
         const bool upL = __builtin_amdgcn_readlane(static_cast<int>(up), L) != 0;
+        const M mdl = m.of_lane(L);                      // lane L's budgets on every lane
         uint32_t a = __builtin_amdgcn_readlane(lo, L), b = __builtin_amdgcn_readlane(hi, L);
         uint32_t ga = __builtin_amdgcn_readlane(glo, L), gb = __builtin_amdgcn_readlane(ghi, L);
         bool first = true;
@@ -996,7 +1034,7 @@ __device__ __forceinline__ uint32_t coop_gauss(bool need, uint32_t target, float
                 p = a + ((static_cast<uint32_t>(lane + 1) * span) >> 6);
             }
             const bool valid = lane < 63 && p > a && p < b;
-            const uint32_t c = gauss_probe<KV, MU>(valid ? p : a, mL, iL, m);
+            const uint32_t c = gauss_probe<KV, MU>(valid ? p : a, mL, iL, mdl);
             const uint64_t mle = __ballot(valid && c <= t);
             const uint64_t mgt = __ballot(valid && c > t);
             // probe positions increase with the lane, except geometric probes
@@ -1171,15 +1209,19 @@ __device__ __forceinline__ void store_row(uint64_t row, uint32_t lane_off, uint3
     }
 }
 
-template <int KV, int MU, bool PAGED>
+// SPLIT: every (plane, channel) has its own split of the Gaussian budget:
+// the pair table in LDS instead of the mixture table, and one Newton step on
+// the lane's own table after the aim.
+template <int KV, int MU, bool PAGED, bool SPLIT>
 __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(80))) k_decode(DecodeArgs a) {
-    __shared__ __align__(16) uint32_t s_tab[kTableWordsPadded];
+    __shared__ __align__(16) uint32_t s_tab[SPLIT ? 2 * kTableWordsPadded : kTableWordsPadded];
     __shared__ __align__(16) float2 s_aim[kAimEntries + 1];
     __shared__ uint32_t s_ring[kDecodeBlock / 64][kRingDwords];
     __shared__ uint32_t s_small[KV == kE4M3 ? kE4Words : 1];
     __shared__ int32_t s_pages[PAGED ? kDecodeBlock / 64 : 1][PAGED ? kPageWindow : 1];
     if constexpr (KV == kE4M3) build_e4_lds(s_small, a.prefix);      // exact prefix + edges
-    copy_to_lds(s_tab, a.table, static_cast<uint32_t>(kTableBytes / 16));
+    if constexpr (SPLIT) fill_pairs_lds(reinterpret_cast<uint2*>(s_tab), a.split.a, a.split.b);
+    else copy_to_lds(s_tab, a.table, static_cast<uint32_t>(kTableBytes / 16));
     copy_to_lds(s_aim, a.aim, static_cast<uint32_t>(kAimBytes / 16));
     const uint32_t htot = a.tn + a.tw;
 
@@ -1224,7 +1266,18 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(8
         sg = 1.0f;
     }
     constexpr uint32_t kN = Alphabet<KV>::kSize;
-    const Model m{s_tab, a.prefix, s_small, nullptr, htot, a.ecount};
+    const Model plain{s_tab, a.prefix, s_small, nullptr, htot, a.ecount};
+    // (a weight the encoder would refuse cannot pass the side-information
+    // check; the capped budgets keep every lane's table within range)
+    const auto m = [&]() {
+        if constexpr (SPLIT) {
+            const uint32_t w = a.split.words[cp.g * D + cp.k * 64 + lane];
+            const uint32_t tn = split_narrow_budget(w, a.split.t_all, htot);
+            return SplitModel{plain, tn, htot - tn};
+        } else {
+            return plain;
+        }
+    }();
     const uint32_t geo = geo_offset(lane);
     // bf16: the bucket table follows the escape count table (one base
     // address for both)
@@ -1314,7 +1367,9 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(8
     auto step = [&](uint32_t t, float mu, bool first) {
         const uint32_t target = static_cast<uint32_t>(x) & (kM - 1u);
         // candidate: the cell the aim lands in, with its exact CDF terms
-        uint32_t kb = nearest_candidate<KV>(__fmaf_rn(aim_z(target, htot, s_aim), sg, mu));
+        float za = aim_z(target, htot, s_aim);
+        if constexpr (SPLIT) za = m.aim(za, target);
+        uint32_t kb = nearest_candidate<KV>(__fmaf_rn(za, sg, mu));
         const bool is_esc = target >= htot;
         const uint64_t esc = __ballot(is_esc);
         uint32_t qs = 0;                                 // Q(s) of an escape lane's symbol
@@ -1473,12 +1528,12 @@ __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(8
 // 0..used-1) must name a page of the pool; one that does not sets the flag
 // the decoder reads before its first store.
 
-template <bool PAGED>
+template <bool PAGED, bool SPLIT>
 hipError_t launch_decode_as(const DecodeArgs& a, int kv_dtype, int mu_dtype, dim3 grid, dim3 block, hipStream_t s) {
-    if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kBF16, kBF16, PAGED>), grid, block, 0, s, a);
-    else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_decode<kBF16, kF32, PAGED>), grid, block, 0, s, a);
-    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kE4M3, kBF16, PAGED>), grid, block, 0, s, a);
-    else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_decode<kE4M3, kF32, PAGED>), grid, block, 0, s, a);
+    if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kBF16, kBF16, PAGED, SPLIT>), grid, block, 0, s, a);
+    else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_decode<kBF16, kF32, PAGED, SPLIT>), grid, block, 0, s, a);
+    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_decode<kE4M3, kBF16, PAGED, SPLIT>), grid, block, 0, s, a);
+    else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_decode<kE4M3, kF32, PAGED, SPLIT>), grid, block, 0, s, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -1487,8 +1542,11 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int mu_dtype, bool p
     constexpr int waves = kDecodeBlock / 64;
     const uint64_t blocks = (static_cast<uint64_t>(a.geom.n_chunks) + waves - 1) / waves;
     const dim3 grid(static_cast<uint32_t>(blocks)), block(kDecodeBlock);
-    return paged ? launch_decode_as<true>(a, kv_dtype, mu_dtype, grid, block, s)
-                 : launch_decode_as<false>(a, kv_dtype, mu_dtype, grid, block, s);
+    if (a.split.words != nullptr)
+        return paged ? launch_decode_as<true, true>(a, kv_dtype, mu_dtype, grid, block, s)
+                     : launch_decode_as<false, true>(a, kv_dtype, mu_dtype, grid, block, s);
+    return paged ? launch_decode_as<true, false>(a, kv_dtype, mu_dtype, grid, block, s)
+                 : launch_decode_as<false, false>(a, kv_dtype, mu_dtype, grid, block, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1753,6 +1811,134 @@ hipError_t launch_rate_fit(const void* kv, const void* mu, int kv_dtype, int mu_
 }
 
 // ---------------------------------------------------------------------------
+// per-channel split: for each candidate narrow weight w_j = max(W - 200 j,
+// 0), W = w_n + w_w, j < kSplitSteps, the integer code length of the
+// held-out data with every lane's budgets split by w_j (the same sum as
+// the rate-fitted sigma); the least sum wins, the first j on a tie.  One
+// workgroup per (plane, 64-channel group) and split of the rows evaluates
+// every candidate: the two cell edges' table entries are read once per
+// scalar and combined with each candidate's budgets.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t split_candidate(uint32_t j, uint32_t w_gauss) {
+    const uint32_t d = static_cast<uint32_t>(kSplitStepBp) * j;
+    return w_gauss > d ? w_gauss - d : 0u;
+}
+
+// The lane table's interpolated value from its two pair-table entries.
+__device__ __forceinline__ uint32_t interp_pairs(uint2 p0, uint2 p1, uint32_t r, uint32_t tn, uint32_t tw) {
+    const uint32_t a = mul_shr31(tn, p0.x) + mul_shr31(tw, p0.y);
+    const uint32_t c = mul_shr31(tn, p1.x) + mul_shr31(tw, p1.y);
+    const uint32_t dlt = c - a;
+    __builtin_assume(dlt < (1u << 22));
+    return a + static_cast<uint32_t>((static_cast<uint64_t>(dlt) * r) >> 16);
+}
+
+template <int KV, int MU>
+__global__ void __launch_bounds__(kCalibBlock) k_split_cost(const void* kv_, const void* mu_, int64_t reps,
+                                                            int64_t planes, int64_t tokens, int64_t channels,
+                                                            int64_t blk, int64_t nb, const float* __restrict__ sigma,
+                                                            SplitArgs sp, uint32_t htot,
+                                                            const uint32_t* __restrict__ prefix,
+                                                            unsigned long long* __restrict__ part) {
+    __shared__ __align__(16) uint2 s_ab[kTableWordsPadded];
+    __shared__ uint32_t s_log[256];
+    __shared__ unsigned long long s_sum[kCalibWaves][64];
+    for (uint32_t i = threadIdx.x; i < 256u; i += blockDim.x)
+        s_log[i] = static_cast<uint32_t>(floor(65536.0 * log2(1.0 + i / 256.0) + 0.5));
+    fill_pairs_lds(s_ab, sp.a, sp.b);                            // and the barrier
+    using KB = typename Alphabet<KV>::Bits;
+    using MT = typename MuT<MU>::T;
+    const KB* __restrict__ kv = static_cast<const KB*>(kv_);
+    const MT* __restrict__ mu = static_cast<const MT*>(mu_);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t groups = channels / 64;
+    const int64_t p = blockIdx.x / groups;
+    const int64_t d = (blockIdx.x % groups) * 64 + lane;
+    const int64_t splits = gridDim.y, s = blockIdx.y;
+    const int64_t n = planes * channels;
+    uint32_t tn[kSplitSteps];
+#pragma unroll
+    for (int j = 0; j < kSplitSteps; ++j) tn[j] = split_narrow_budget(split_candidate(j, sp.w_gauss), sp.t_all, htot);
+    unsigned long long acc[kSplitSteps];
+#pragma unroll
+    for (int j = 0; j < kSplitSteps; ++j) acc[j] = 0;
+    const int64_t rows = reps * tokens;
+    const int64_t r1 = rows * (s + 1) / splits;
+    for (int64_t r = rows * s / splits + wave; r < r1; r += kCalibWaves) {
+        const int64_t rep = r / tokens, t = r - rep * tokens;
+        const int64_t off = ((rep * planes + p) * tokens + t) * channels + d;
+        const uint32_t sym = order_of_bits<KV>(kv[off]);
+        const float mv = mu_value<MU>(mu[off]);
+        const float inv24 = __frcp_rn(sigma[(p * nb + t / blk) * channels + d]) * 16777216.0f;
+        const uint32_t u0 = static_cast<uint32_t>(z_fixed(edge<KV>(sym), mv, inv24) + kQMax);
+        const uint32_t u1 = static_cast<uint32_t>(z_fixed(edge<KV>(sym + 1u), mv, inv24) + kQMax);
+        const uint2 a0 = s_ab[u0 >> 16], a1 = s_ab[(u0 >> 16) + 1];
+        const uint2 b0 = s_ab[u1 >> 16], b1 = s_ab[(u1 >> 16) + 1];
+        const uint32_t qf = 1u + prefix[sym + 1u] - prefix[sym];
+#pragma unroll
+        for (int j = 0; j < kSplitSteps; ++j) {
+            const uint32_t h0 = interp_pairs(a0, a1, u0 & 0xFFFFu, tn[j], htot - tn[j]);
+            const uint32_t h1 = interp_pairs(b0, b1, u1 & 0xFFFFu, tn[j], htot - tn[j]);
+            acc[j] += code_len_q16(h1 - h0 + qf, s_log);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kSplitSteps; ++j) {
+        s_sum[wave][lane] = acc[j];
+        __syncthreads();
+        if (wave == 0) {
+            unsigned long long t = 0;
+            for (int w = 0; w < kCalibWaves; ++w) t += s_sum[w][lane];
+            part[(static_cast<int64_t>(j) * splits + s) * n + p * channels + d] = t;
+        }
+        __syncthreads();
+    }
+}
+
+// One thread per (plane, channel): the candidate with the least code length.
+__global__ void k_split_pick(const unsigned long long* __restrict__ part, int64_t splits, int64_t n, uint32_t w_gauss,
+                             uint32_t* __restrict__ out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    unsigned long long best = ~0ull;
+    uint32_t best_j = 0;
+    for (uint32_t j = 0; j < static_cast<uint32_t>(kSplitSteps); ++j) {
+        unsigned long long c = 0;
+        for (int64_t s = 0; s < splits; ++s) c += part[(static_cast<int64_t>(j) * splits + s) * n + i];
+        if (c < best) {
+            best = c;
+            best_j = j;
+        }
+    }
+    out[i] = split_candidate(best_j, w_gauss);
+}
+
+hipError_t launch_split_fit(const void* kv, const void* mu, int kv_dtype, int mu_dtype, int64_t reps, int64_t planes,
+                            int64_t tokens, int64_t channels, int64_t block_tokens, const float* sigma,
+                            const SplitArgs& sp, uint32_t htot, const uint32_t* prefix, uint32_t* out,
+                            unsigned long long* part, hipStream_t s) {
+    const int64_t blk = (block_tokens == 0 || block_tokens > tokens) ? tokens : block_tokens;
+    const int64_t nb = (tokens + blk - 1) / blk;
+    const int64_t pairs = planes * (channels / 64);
+    const int64_t splits = calibrate_splits(reps, pairs, tokens);
+    const dim3 grid(static_cast<uint32_t>(pairs), static_cast<uint32_t>(splits)), block(kCalibBlock);
+#define KVC_SPLIT(K, U)                                                                                       \
+    hipLaunchKernelGGL((k_split_cost<K, U>), grid, block, 0, s, kv, mu, reps, planes, tokens, channels, blk, nb, \
+                       sigma, sp, htot, prefix, part)
+    if (kv_dtype == kBF16 && mu_dtype == kBF16) KVC_SPLIT(kBF16, kBF16);
+    else if (kv_dtype == kBF16 && mu_dtype == kF32) KVC_SPLIT(kBF16, kF32);
+    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) KVC_SPLIT(kE4M3, kBF16);
+    else if (kv_dtype == kE4M3 && mu_dtype == kF32) KVC_SPLIT(kE4M3, kF32);
+    else return hipErrorInvalidValue;
+#undef KVC_SPLIT
+    const int64_t n = planes * channels;
+    hipLaunchKernelGGL(k_split_pick, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, s, part, splits, n,
+                       sp.w_gauss, out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // empirical marginal: histogram in value order (integer atomics, so the
 // result does not depend on order), then one workgroup turns counts + 1
 // into the scaled prefix in place.
@@ -1843,20 +2029,26 @@ __device__ __forceinline__ double t_mass(double a, double b, int nu) {
     return m / span;
 }
 
-template <int KV, int MU>
+// SPLIT: each (plane, channel) with its own split of the Gaussian weight
+// (budgets from the pair table; the float model's weights w_c and
+// w_n + w_w - w_c).
+template <int KV, int MU, bool SPLIT>
 __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
-    __shared__ uint32_t s_tab[kTableEntries];
+    __shared__ __align__(16) uint32_t s_tab[SPLIT ? 2 * kTableWordsPadded : kTableEntries];
     __shared__ double s_red[2][4];
-    build_table_lds(s_tab, a.phi, a.tn, a.tw);
+    if constexpr (SPLIT) fill_pairs_lds(reinterpret_cast<uint2*>(s_tab), a.split.a, a.split.b);
+    else build_table_lds(s_tab, a.phi, a.tn, a.tw);
     using KB = typename Alphabet<KV>::Bits;
     using MT = typename MuT<MU>::T;
     const KB* __restrict__ kv = static_cast<const KB*>(a.kv);
     const MT* __restrict__ mup = static_cast<const MT*>(a.mu);
-    const Model model{s_tab, a.prefix, nullptr};
+    const Model base{s_tab, a.prefix, nullptr, nullptr, a.tn + a.tw};
     const int64_t D = a.geom.channels, T = a.geom.tokens;
     const int64_t n = a.geom.planes * T * D;
-    const double wn = a.w_narrow_bp / 1e4, ww = a.w_wide_bp / 1e4, we = 1.0 - wn - ww;
+    double wn = a.w_narrow_bp / 1e4, ww = a.w_wide_bp / 1e4;
+    const double we = 1.0 - wn - ww;
     double acc_i = 0.0, acc_f = 0.0;
+    bool bad = false;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
         const int64_t d = i % D;
@@ -1866,6 +2058,18 @@ __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
         const float inv24 = __frcp_rn(sg) * 16777216.0f;
         const float mu = mu_value<MU>(mup[i]);
         const uint32_t s = order_of_bits<KV>(kv[i]);
+        const auto model = [&]() {
+            if constexpr (SPLIT) {
+                const uint32_t w = a.split.words[g * D + d];
+                bad |= w > a.split.w_gauss;
+                wn = w / 1e4;
+                ww = a.split.w_gauss / 1e4 - wn;
+                const uint32_t tn = split_narrow_budget(w, a.split.t_all, base.htot);
+                return SplitModel{base, tn, base.htot - tn};
+            } else {
+                return base;
+            }
+        }();
         const uint32_t c0 = cdf_at<KV>(s, mu, inv24, model);
         const uint32_t c1 = cdf_at<KV>(s + 1, mu, inv24, model);
         acc_i += 31.0 - log2(static_cast<double>(c1 - c0));
@@ -1881,6 +2085,7 @@ __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
     acc_i = wave_sum_f64(acc_i);
     acc_f = wave_sum_f64(acc_f);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (__ballot(bad) && lane == 0) atomicOr(&a.ctl->flags, kFlagBadSigma);
     if (lane == 0) { s_red[0][wave] = acc_i; s_red[1][wave] = acc_f; }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1893,11 +2098,18 @@ __global__ void __launch_bounds__(256) k_estimate(EstimateArgs a) {
 
 hipError_t launch_estimate(const EstimateArgs& a, int kv_dtype, int mu_dtype, hipStream_t s) {
     const dim3 grid(1024), block(256);
-    if (kv_dtype == kBF16 && mu_dtype == kBF16) hipLaunchKernelGGL((k_estimate<kBF16, kBF16>), grid, block, 0, s, a);
-    else if (kv_dtype == kBF16 && mu_dtype == kF32) hipLaunchKernelGGL((k_estimate<kBF16, kF32>), grid, block, 0, s, a);
-    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) hipLaunchKernelGGL((k_estimate<kE4M3, kBF16>), grid, block, 0, s, a);
-    else if (kv_dtype == kE4M3 && mu_dtype == kF32) hipLaunchKernelGGL((k_estimate<kE4M3, kF32>), grid, block, 0, s, a);
+    const bool sp = a.split.words != nullptr;
+#define KVC_EST(K, U)                                                                  \
+    do {                                                                               \
+        if (sp) hipLaunchKernelGGL((k_estimate<K, U, true>), grid, block, 0, s, a);    \
+        else hipLaunchKernelGGL((k_estimate<K, U, false>), grid, block, 0, s, a);      \
+    } while (0)
+    if (kv_dtype == kBF16 && mu_dtype == kBF16) KVC_EST(kBF16, kBF16);
+    else if (kv_dtype == kBF16 && mu_dtype == kF32) KVC_EST(kBF16, kF32);
+    else if (kv_dtype == kE4M3 && mu_dtype == kBF16) KVC_EST(kE4M3, kBF16);
+    else if (kv_dtype == kE4M3 && mu_dtype == kF32) KVC_EST(kE4M3, kF32);
     else return hipErrorInvalidValue;
+#undef KVC_EST
     return hipGetLastError();
 }
 

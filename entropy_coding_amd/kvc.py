@@ -33,7 +33,7 @@ EXPORTS = [
     "kvc_version", "kvc_status_string", "kvc_phi_tables", "kvc_narrow_table", "kvc_encode_sizes", "kvc_encode", "kvc_encode_result",
     "kvc_stream_info", "kvc_decode", "kvc_decode_async", "kvc_decode_result", "kvc_decode_noalloc",
     "kvc_decode_paged", "kvc_reload",
-    "kvc_calibrate_sigma", "kvc_calibrate_sigma_blocks", "kvc_calibrate_sigma_rate",
+    "kvc_calibrate_sigma", "kvc_calibrate_sigma_blocks", "kvc_calibrate_sigma_rate", "kvc_calibrate_split",
     "kvc_build_marginal", "kvc_estimate_bits", "kvc_cdf_table",
 ]
 
@@ -47,7 +47,7 @@ class kvc_params(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32), ("mu_dtype", ctypes.c_int32),
         ("w_narrow_bp", ctypes.c_uint32), ("w_wide_bp", ctypes.c_uint32),
         ("chunk_tokens", ctypes.c_uint32), ("sigma_block_tokens", ctypes.c_uint32),
-        ("narrow_dof", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+        ("narrow_dof", ctypes.c_uint32), ("channel_split", ctypes.c_uint32),
         ("planes", ctypes.c_int64), ("tokens", ctypes.c_int64), ("channels", ctypes.c_int64),
     ]
 
@@ -110,6 +110,9 @@ _lib_calibrate_blocks = _sig("kvc_calibrate_sigma_blocks", ctypes.c_int,
 _lib_calibrate_rate = _sig("kvc_calibrate_sigma_rate", ctypes.c_int,
                            [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, _I64, ctypes.c_float, _U32, _U32, _U32, _P,
                             _P, _P, _U64, _P])
+_lib_calibrate_split = _sig("kvc_calibrate_split", ctypes.c_int,
+                            [_P, _P, _I32, _I32, _I64, _I64, _I64, _I64, _I64, _P, _U32, _U32, _U32, _P, _P, _P, _U64,
+                             _P])
 _lib_marginal = _sig("kvc_build_marginal", ctypes.c_int, [_P, _I32, _U64, _U32, _U32, _P, _P])
 _lib_estimate = _sig("kvc_estimate_bits", ctypes.c_int, [ctypes.POINTER(kvc_params), _P, _P, _P, _P, _P, _P, _U64, _P])
 _lib_cdf_table = _sig("kvc_cdf_table", ctypes.c_int, [_I32, _I32, _U32, _U32, _U32, _P, _P, _I64, _P, _P, _P])
@@ -197,9 +200,17 @@ def kvc_narrow_table(narrow_dof: int = 0):
 
 
 def make_params(kv_dtype, mu_dtype, planes, tokens, channels, weights=(9500, 300), chunk_tokens=0,
-                sigma_block_tokens=0, narrow_dof=0) -> kvc_params:
+                sigma_block_tokens=0, narrow_dof=0, channel_split=0) -> kvc_params:
     return kvc_params(kv_dtype, mu_dtype, weights[0], weights[1], chunk_tokens, sigma_block_tokens,
-                      narrow_dof, 0, planes, tokens, channels)
+                      narrow_dof, channel_split, planes, tokens, channels)
+
+
+def side_info(sigma: torch.Tensor, channel_split: torch.Tensor) -> torch.Tensor:
+    """The side buffer of a stream with per-channel weights: sigma's words,
+    then the narrow weights [G, D] (basis points) as uint32 words, in one
+    float32 device tensor (pass it wherever sigma goes)."""
+    w = channel_split.to(torch.int32).contiguous()
+    return torch.cat([sigma.reshape(-1).to(torch.float32), w.view(torch.float32).reshape(-1)])
 
 
 def sigma_shape(planes: int, tokens: int, channels: int, sigma_block_tokens: int = 0):
@@ -232,7 +243,10 @@ class Encoder:
         n = p.planes * p.tokens * p.channels
         if kv.numel() != n or mu.numel() != n or _kv_dtype(kv) != p.kv_dtype or _mu_dtype(mu) != p.mu_dtype:
             raise ValueError("kv / mu do not match the encoder's parameters")
-        if sigma.numel() != math.prod(sigma_shape(p.planes, p.tokens, p.channels, p.sigma_block_tokens)):
+        words = math.prod(sigma_shape(p.planes, p.tokens, p.channels, p.sigma_block_tokens))
+        if p.channel_split:
+            words += p.planes * p.channels                  # the narrow weights follow sigma
+        if sigma.numel() != words:
             raise ValueError("sigma does not match the encoder's parameters")
 
     def __call__(self, kv, mu, sigma, prefix=None, stream=None, info: dict | None = None) -> torch.Tensor:
@@ -265,10 +279,13 @@ class Encoder:
 
 def kvc_encode(kv: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, prefix: torch.Tensor | None = None,
                weights=(9500, 300), chunk_tokens: int = 0, stream=None,
-               sigma_block_tokens: int = 0, narrow_dof: int = 0) -> torch.Tensor:
+               sigma_block_tokens: int = 0, narrow_dof: int = 0,
+               channel_split: torch.Tensor | None = None) -> torch.Tensor:
     """Encode KV [G, T, D] under the mixture around mu with sigma [G, D] (or
-    [G, ceil(T / B), D] with sigma_block_tokens = B); returns the stream as
-    a uint8 device tensor."""
+    [G, ceil(T / B), D] with sigma_block_tokens = B) and, when channel_split
+    [G, D] is given, each channel's own narrow weight (decode then takes
+    side_info(sigma, channel_split) as its sigma); returns the stream as a
+    uint8 device tensor."""
     for t, nm in ((kv, "kv"), (mu, "mu"), (sigma, "sigma")):
         _need(t, nm)
     if prefix is not None:
@@ -277,7 +294,14 @@ def kvc_encode(kv: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, prefix: 
     if tuple(mu.shape) != (g, t, d) or tuple(sigma.shape) != sigma_shape(g, t, d, sigma_block_tokens) \
             or sigma.dtype != torch.float32:
         raise ValueError("shapes: kv and mu [G, T, D], sigma [G, D] (or [G, ceil(T / B), D]) float32")
-    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens, sigma_block_tokens, narrow_dof)
+    split = 0
+    if channel_split is not None:
+        if tuple(channel_split.shape) != (g, d):
+            raise ValueError("channel_split is [G, D]")
+        sigma = side_info(sigma, channel_split)
+        split = 1
+    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens, sigma_block_tokens, narrow_dof,
+                    split)
     return Encoder(p, kv.device)(kv, mu, sigma, prefix, stream).clone()
 
 
@@ -502,6 +526,30 @@ def kvc_calibrate_sigma_rate(kv: torch.Tensor, mu: torch.Tensor, prefix: torch.T
     return out
 
 
+def kvc_calibrate_split(kv: torch.Tensor, mu: torch.Tensor, sigma: torch.Tensor, prefix: torch.Tensor | None = None,
+                        weights=(9500, 300), block_tokens: int = 0, narrow_dof: int = 0,
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """Per-channel narrow weights: of w_j = max(w_n + w_w - 200 j, 0),
+    j = 0..15, the one with the least integer code length of the held-out
+    kv [reps, planes, tokens, channels] under sigma (the one the stream will
+    use: [G, D], or [G, ceil(T / B), D] with block_tokens = B).  Returns
+    int32 [G, D]."""
+    _need(kv, "kv")
+    _need(mu, "mu")
+    _need(sigma, "sigma")
+    r, g, t, d = kv.shape
+    if out is None:
+        out = torch.empty((g, d), dtype=torch.int32, device=kv.device)
+    if workspace is None:
+        workspace = torch.empty(g * d * 8192, dtype=torch.uint8, device=kv.device)
+    st = _lib_calibrate_split(_ptr(kv), _ptr(mu), _kv_dtype(kv), _mu_dtype(mu), r, g, t, d, block_tokens, _ptr(sigma),
+                              weights[0], weights[1], narrow_dof, _ptr(prefix), _ptr(out), _ptr(workspace),
+                              workspace.numel(), _stream(stream))
+    _check(st, "kvc_calibrate_split")
+    return out
+
+
 def kvc_build_marginal(samples: torch.Tensor, weights=(9500, 300), stream=None) -> torch.Tensor:
     """Prefix table of the +1-smoothed marginal; returned as int32 (all
     values are below 2^31) with N + 1 entries."""
@@ -515,10 +563,13 @@ def kvc_build_marginal(samples: torch.Tensor, weights=(9500, 300), stream=None) 
 
 
 def kvc_estimate_bits(kv, mu, sigma, prefix=None, weights=(9500, 300), stream=None, sigma_block_tokens: int = 0,
-                      chunk_tokens: int = 0, narrow_dof: int = 0):
+                      chunk_tokens: int = 0, narrow_dof: int = 0, channel_split: torch.Tensor | None = None):
     """(integer-model bits/scalar, float-model bits/scalar)."""
     g, t, d = kv.shape
-    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens, sigma_block_tokens, narrow_dof)
+    if channel_split is not None:
+        sigma = side_info(sigma, channel_split)
+    p = make_params(_kv_dtype(kv), _mu_dtype(mu), g, t, d, weights, chunk_tokens, sigma_block_tokens, narrow_dof,
+                    0 if channel_split is None else 1)
     ws = torch.empty(ESTIMATE_WORKSPACE_BYTES, dtype=torch.uint8, device=kv.device)
     out = (ctypes.c_double * 2)()
     st = _lib_estimate(ctypes.byref(p), _ptr(kv), _ptr(mu), _ptr(sigma), _ptr(prefix), ctypes.addressof(out),

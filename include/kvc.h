@@ -120,7 +120,25 @@ typedef struct kvc_params {
                                 truncated to +-24 sigma and renormalised there.
                                 The wide part and p_hat are unchanged.
                                 Recorded in the stream header.                 */
-    uint32_t reserved;       /* 0                                                  */
+    uint32_t channel_split;  /* per-channel mixture weights ([wiki] "future directions",
+                                [blog] "limitations and future directions": a
+                                better residual model): 0 = the call's weights on
+                                every channel; 1 = each (plane, channel) has its
+                                own narrow weight w_c in basis points, 0 ..
+                                w_narrow_bp + w_wide_bp, its wide weight
+                                w_narrow_bp + w_wide_bp - w_c (the escape weight
+                                stays the call's).  The weights are side
+                                information: the sigma buffer (d_sigma) holds
+                                the sigma words followed by planes x channels
+                                uint32 weights, [planes][channels], and every
+                                call that takes it (encode, decode, reload,
+                                estimate) reads both; sigma_bytes / strides
+                                count both.  The coder's budgets are T_n(c) =
+                                min(floor(T w_c / 10^4), T_n + T_w), T_w(c) =
+                                T_n + T_w - T_n(c) with T = 2^31 - N.  A weight
+                                above w_narrow_bp + w_wide_bp: KVC_ERR_INVALID.
+                                Recorded in the stream header; covered by the
+                                side-information checksum.                     */
     int64_t planes;          /* G = layers * 2 * batch * kv_heads                  */
     int64_t tokens;          /* T                                                  */
     int64_t channels;        /* D, a positive multiple of 64                       */
@@ -400,6 +418,33 @@ int kvc_calibrate_sigma_rate(const void* d_kv, const void* d_mu, int32_t kv_dtyp
                              uint32_t w_narrow_bp, uint32_t w_wide_bp, uint32_t narrow_dof,
                              const uint32_t* d_prefix, float* d_sigma_out, void* d_workspace,
                              uint64_t workspace_bytes, void* stream);
+
+/*
+ * Per-channel mixture weights ([wiki] "future directions" and [blog]
+ * "limitations and future directions": a better residual model; the pages'
+ * 0.95 / 0.03 split is one choice for every channel, [wiki] "mixture
+ * distribution").  For each (plane, channel), of the narrow weights
+ * w_j = max(w_narrow_bp + w_wide_bp - 200 j, 0), j = 0..15, writes to
+ * d_split_out[planes][channels] (uint32) the one under which the held-out
+ * data d_kv / d_mu ([reps][planes][tokens][channels]) cost the fewest bits
+ * in the coder's own integer model with that channel's budgets (the sum of
+ * kvc_calibrate_sigma_rate; the first j on a tie: deterministic).  d_sigma
+ * is the sigma the data will be coded with: [planes][channels], or per
+ * block of block_tokens tokens [planes][ceil(tokens / block_tokens)]
+ * [channels] (block_tokens = 0 or >= tokens: one block); the weights,
+ * narrow_dof and d_prefix (NULL allowed for a single Gaussian) as the
+ * stream will use them.  Workspace (256-byte aligned):
+ * KVC_CALIBRATE_SPLIT_WORKSPACE_BYTES(planes, channels).  KVC_ERR_INVALID
+ * for bad shapes or arguments.  Does not synchronise.
+ */
+#define KVC_CALIBRATE_SPLIT_WORKSPACE_BYTES(planes, channels) \
+    ((uint64_t)(planes) * (uint64_t)(channels) * 8192u)
+int kvc_calibrate_split(const void* d_kv, const void* d_mu, int32_t kv_dtype, int32_t mu_dtype,
+                        int64_t reps, int64_t planes, int64_t tokens, int64_t channels,
+                        int64_t block_tokens, const float* d_sigma, uint32_t w_narrow_bp,
+                        uint32_t w_wide_bp, uint32_t narrow_dof, const uint32_t* d_prefix,
+                        uint32_t* d_split_out, void* d_workspace, uint64_t workspace_bytes,
+                        void* stream);
 
 /*
  * Empirical marginal ([wiki] "mixture distribution": an empirical BF16

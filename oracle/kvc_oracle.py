@@ -1050,12 +1050,12 @@ def chunk_payload(stream: bytes, chunk_id: int) -> bytes:
 
 
 def encode_chunks(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide_bp,
-                  chunk_tokens, chunk_ids, sigma_block_tokens=0, narrow_dof=0):
+                  chunk_tokens, chunk_ids, sigma_block_tokens=0, narrow_dof=0, channel_split=None):
     """Payloads of selected chunks only (for sampled parity at full size).
 
-    Each chunk depends only on its own slice of kv and mu and on the sigma
-    its tokens use, so it is coded by running :func:`encode` on a one-plane
-    view."""
+    Each chunk depends only on its own slice of kv and mu, on the sigma its
+    tokens use and on its channels' split (S-14), so it is coded by running
+    :func:`encode` on a one-plane view."""
     kv = np.asarray(kv)
     g_n, t_len, d_n = kv.shape
     sig3, blk = sigma_blocks(sigma, t_len, sigma_block_tokens)
@@ -1067,8 +1067,10 @@ def encode_chunks(kv, mu, sigma, prefix, kv_dtype, mu_dtype, w_narrow_bp, w_wide
         sub_kv = kv[g:g + 1, t0:t0 + ln, 64 * k:64 * k + 64]
         sub_mu = np.asarray(mu)[g:g + 1, t0:t0 + ln, 64 * k:64 * k + 64]
         sub_sig = sig3[g:g + 1, t0 // blk, 64 * k:64 * k + 64]
+        sub_split = None if channel_split is None else \
+            np.asarray(channel_split)[g:g + 1, 64 * k:64 * k + 64]
         s = encode(sub_kv, sub_mu, sub_sig, prefix, kv_dtype, mu_dtype, w_narrow_bp,
-                   w_wide_bp, chunk_tokens, narrow_dof=narrow_dof)
+                   w_wide_bp, chunk_tokens, narrow_dof=narrow_dof, channel_split=sub_split)
         out[int(cid)] = chunk_payload(s, 0)
     return out
 

@@ -78,11 +78,26 @@ def test_decode_refuses_a_damaged_header(kvc, case, offset):
 
 def test_decode_refuses_a_header_with_a_recomputed_crc_but_bad_fields(kvc, case):
     import zlib
-    for off, val in [(8, 7), (9, 1), (14, 17), (15, 1), (13, 32)]:
+    for off, val in [(8, 7), (9, 1), (14, 17), (15, 2), (13, 32)]:
         h = case["stream"][:128].copy()
         h[off] = val
         h[92:96] = np.frombuffer(zlib.crc32(h[:92].tobytes()).to_bytes(4, "little"), dtype=np.uint8)
         assert _decode(kvc, case, header=h) == kvc.KVC_ERR_CORRUPT, off
+
+
+def test_decode_of_a_split_stream_needs_the_weights_in_the_side_buffer(kvc, case):
+    """A stream with per-channel weights: the side buffer holds sigma, then
+    planes x channels weights; a buffer that holds sigma alone is refused."""
+    kv, mu, sig, samples = W.tiny_case(11, planes=2, tokens=40)
+    kvn, mun, sgn, smn = W.to_numpy_bits(kv), W.to_numpy_bits(mu), sig.numpy(), W.to_numpy_bits(samples)
+    pref = O.build_marginal(smn, O.BF16, *W_MIX)
+    split = np.full((2, 128), 9000)
+    st = O.encode(kvn, mun, sgn, pref, O.BF16, O.BF16, *W_MIX, 16, channel_split=split)
+    c = dict(case, stream=np.frombuffer(st, dtype=np.uint8).copy())
+    assert _decode(kvc, c) == kvc.KVC_ERR_INVALID                         # sigma words only
+    assert _decode(kvc, c, sigma_bytes=c["sigma_bytes"] + 4 * 256 - 4) == kvc.KVC_ERR_INVALID
+    p, total = kvc.kvc_stream_info(st[:128])
+    assert p.channel_split == 1 and total == len(st)
 
 
 def _paged(kvc, c, **kw):
@@ -154,6 +169,9 @@ def test_encode_refuses_bad_arguments_before_the_device(kvc):
     q = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, 2, 40, 128, W_MIX, 16)
     q.narrow_dof = 17
     assert enc(q=q) == kvc.KVC_ERR_INVALID
+    q = kvc.make_params(kvc.KVC_BF16, kvc.KVC_BF16, 2, 40, 128, W_MIX, 16, channel_split=2)
+    assert enc(q=q) == kvc.KVC_ERR_INVALID
+    assert kvc._lib_encode_sizes(ctypes.byref(q), None, None) == kvc.KVC_ERR_INVALID
     assert kvc._lib_encode_result(None, None, ctypes.byref(out), None) == kvc.KVC_ERR_INVALID
     assert kvc._lib_encode_result(FAKE + 8, None, ctypes.byref(out), None) == kvc.KVC_ERR_INVALID
     assert kvc._lib_decode_result(FAKE + 8, None, None) == kvc.KVC_ERR_INVALID
@@ -170,6 +188,21 @@ def test_other_calls_refuse_bad_arguments(kvc):
                                      1 << 20, None) == kvc.KVC_ERR_INVALID
     assert kvc._lib_calibrate_rate(FAKE, FAKE, kvc.KVC_BF16, kvc.KVC_BF16, 1, 1, 16, 128, 0, f, 9500, 300, 17,
                                    FAKE, FAKE, FAKE, 1 << 20, None) == kvc.KVC_ERR_INVALID
+    # per-channel split: 64-channel groups, positive sizes, known dtypes, a
+    # prefix with an escape part, a workspace of the stated size
+    ws = 2 * 128 * 8192
+
+    def split(**kw):
+        a = dict(kv=FAKE, mu=FAKE, kvd=kvc.KVC_BF16, mud=kvc.KVC_BF16, reps=1, planes=2, tokens=16, channels=128,
+                 block=0, sigma=FAKE, wn=9500, ww=300, dof=0, prefix=FAKE, out=FAKE, wsp=FAKE, ws_bytes=ws)
+        a.update(kw)
+        return kvc._lib_calibrate_split(a["kv"], a["mu"], a["kvd"], a["mud"], a["reps"], a["planes"], a["tokens"],
+                                        a["channels"], a["block"], a["sigma"], a["wn"], a["ww"], a["dof"],
+                                        a["prefix"], a["out"], a["wsp"], a["ws_bytes"], None)
+    for kw in (dict(channels=96), dict(reps=0), dict(tokens=0), dict(planes=0), dict(block=-1), dict(dof=17),
+               dict(kvd=5), dict(mud=1), dict(wn=9800, ww=300), dict(prefix=None), dict(sigma=None),
+               dict(out=None), dict(out=FAKE + 2), dict(wsp=FAKE + 64), dict(ws_bytes=ws - 1)):
+        assert split(**kw) == kvc.KVC_ERR_INVALID, kw
     # marginal: a known dtype, weights within 10000 basis points
     assert kvc._lib_marginal(FAKE, 3, 10, 9500, 300, FAKE, None) == kvc.KVC_ERR_INVALID
     assert kvc._lib_marginal(FAKE, kvc.KVC_BF16, 10, 9500, 600, FAKE, None) == kvc.KVC_ERR_INVALID
