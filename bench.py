@@ -151,7 +151,8 @@ def cpu_baseline(workload, workers: int = 0):
 # ---------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------
-def prepare(workload, dev, calib_reps: int, sigma_block: int = 0, sigma_fit: str = "rms", narrow_dof: int = 0):
+def prepare(workload, dev, calib_reps: int, sigma_block: int = 0, sigma_fit: str = "rms", narrow_dof: int = 0,
+            channel_split: bool = False):
     import torch
     from entropy_coding_amd import kvc
     from entropy_coding_amd import workloads as W
@@ -163,6 +164,7 @@ def prepare(workload, dev, calib_reps: int, sigma_block: int = 0, sigma_fit: str
     if sigma_block and w.calib_tokens < T:
         raise SystemExit("sigma blocks need calibration data over every position (calib_tokens = tokens)")
     sigma = torch.empty(kvc.sigma_shape(G, T, D, sigma_block), dtype=torch.float32, device=dev)
+    split = torch.empty((G, D), dtype=torch.int32, device=dev) if channel_split else None
     ppl = w.planes_per_layer
     t0 = time.perf_counter()
     prefix = kvc.kvc_build_marginal(W.marginal_samples(w, device=dev), (w.w_narrow_bp, w.w_wide_bp))
@@ -178,22 +180,27 @@ def prepare(workload, dev, calib_reps: int, sigma_block: int = 0, sigma_fit: str
         else:
             s_kvh = kvc.kvc_calibrate_sigma(ck, cm, block_tokens=sigma_block)
         sigma[l * ppl:(l + 1) * ppl] = W.expand_sigma(w, s_kvh)
+        if split is not None:
+            # each (kv, head, channel)'s narrow weight, fitted under that sigma
+            w_kvh = kvc.kvc_calibrate_split(ck, cm, s_kvh, prefix, (w.w_narrow_bp, w.w_wide_bp),
+                                            block_tokens=sigma_block, narrow_dof=narrow_dof)
+            split[l * ppl:(l + 1) * ppl] = W.expand_sigma(w, w_kvh)
         del ck, cm
     torch.cuda.synchronize()
     log(f"[bench] generated {w.name}: {w.n_scalars} scalars, sigma ({sigma_fit}) from {calib_reps}x{w.calib_tokens} "
-        f"tokens per layer, in {time.perf_counter() - t0:.1f} s")
-    return kv, mu, sigma, prefix
+        f"tokens per layer{', per-channel weights' if split is not None else ''}, in {time.perf_counter() - t0:.1f} s")
+    return kv, mu, sigma, prefix, split
 
 
-def offload_reload(w, kv, mu, sigma, prefix, kvc, enc, parts, dws, steps: int):
+def offload_reload(w, kv, mu, side, prefix, kvc, enc, parts, dws, steps: int):
     """Host-offload reload, one layer per call: every layer's stream sits in
     pinned host memory; the copy of layer l+1 to the device (its own stream)
     overlaps the decode of layer l.  Compared with copying the raw layers."""
     import torch
     dev = kv.device
     streams = []
-    for sl in parts:
-        streams.append(enc(kv[sl], mu[sl], sigma[sl], prefix).cpu())
+    for i, sl in enumerate(parts):
+        streams.append(enc(kv[sl], mu[sl], side[i], prefix).cpu())
     sizes = [s.numel() for s in streams]
     offs = [0]
     for n in sizes:
@@ -206,7 +213,7 @@ def offload_reload(w, kv, mu, sigma, prefix, kvc, enc, parts, dws, steps: int):
     layers = [host[o:o + n] for o, n in zip(offs[:-1], sizes)]
     g = parts[0].stop - parts[0].start
     mu_l = mu.view(len(parts), g, *mu.shape[1:])
-    sig_l = sigma.view(len(parts), g, *sigma.shape[1:])
+    sig_l = torch.stack(side)                         # each layer's side buffer (sigma, weights)
     out_l = out.view(len(parts), g, *out.shape[1:])
     half = (max(sizes) + 511) // 256 * 256
     staging = torch.empty(2 * half, dtype=torch.uint8, device=dev)
@@ -275,6 +282,8 @@ def main():
                     help="(per-layer workload 4) HIP streams the asynchronous one-layer decode calls are spread over")
     ap.add_argument("--narrow-dof", type=int, default=0,
                     help="narrow part of the mixture: 0 = the pages' Gaussian, nu = Student's t with nu degrees of freedom")
+    ap.add_argument("--channel-split", action="store_true",
+                    help="per-(plane, channel) narrow weights calibrated to the code length (kvc_calibrate_split)")
     ap.add_argument("--paged", type=int, default=0,
                     help="decode straight into a paged KV cache with pages of this many tokens (shuffled table)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -304,7 +313,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     reps = args.calib_reps if args.calib_reps is not None else w.calib_reps
-    kv, mu, sigma, prefix = prepare(w, dev, reps, args.sigma_block, args.sigma_fit, args.narrow_dof)
+    kv, mu, sigma, prefix, split = prepare(w, dev, reps, args.sigma_block, args.sigma_fit, args.narrow_dof,
+                                           args.channel_split)
     n = w.n_scalars
     weights = (w.w_narrow_bp, w.w_wide_bp)
     # with sigma blocks the library's default picks a divisor of the block length
@@ -317,10 +327,13 @@ def main():
     parts = ([slice(l * w.planes_per_layer, (l + 1) * w.planes_per_layer) for l in range(w.layers)]
              if per_layer else [slice(0, w.planes)])
     g_part = parts[0].stop - parts[0].start
-    p = kvc.make_params(kv_code, mu_code, g_part, w.tokens, w.channels, weights, tc, args.sigma_block, args.narrow_dof)
+    p = kvc.make_params(kv_code, mu_code, g_part, w.tokens, w.channels, weights, tc, args.sigma_block, args.narrow_dof,
+                        1 if split is not None else 0)
+    # the side buffer of each call: sigma, then (per-channel weights) the weights
+    side = [sigma[sl] if split is None else kvc.side_info(sigma[sl], split[sl]) for sl in parts]
     enc = kvc.Encoder(p, dev)
     if tc == 0:
-        tc = kvc.kvc_stream_info(enc(kv[parts[0]], mu[parts[0]], sigma[parts[0]], prefix)[:128].cpu().numpy())[0] \
+        tc = kvc.kvc_stream_info(enc(kv[parts[0]], mu[parts[0]], side[0], prefix)[:128].cpu().numpy())[0] \
             .chunk_tokens
     kv_out = torch.empty((w.planes, w.tokens, w.channels), dtype=torch.int16 if kv_size == 2 else torch.uint8,
                          device=dev)
@@ -347,13 +360,13 @@ def main():
     def step(stats=None):
         e_ms, d_ms = [0.0] * kvc.ENCODE_STAGES, [0.0] * kvc.DECODE_STAGES
         fb, nbytes = 0, 0
-        for sl in parts:
+        for i, sl in enumerate(parts):
             ei, di = {}, {}
-            st = enc(kv[sl], mu[sl], sigma[sl], prefix, info=ei)
+            st = enc(kv[sl], mu[sl], side[i], prefix, info=ei)
             if paged is not None:
-                rc = kvc.kvc_decode_paged(st, mu[sl], sigma[sl], prefix, paged, dws, info=di, header=enc.header)
+                rc = kvc.kvc_decode_paged(st, mu[sl], side[i], prefix, paged, dws, info=di, header=enc.header)
             else:
-                rc = kvc.kvc_decode_into(st, mu[sl], sigma[sl], prefix, kv_out[sl], dws, info=di, header=enc.header)
+                rc = kvc.kvc_decode_into(st, mu[sl], side[i], prefix, kv_out[sl], dws, info=di, header=enc.header)
             if rc != kvc.KVC_OK:
                 raise kvc.KvcError(rc, "kvc_decode")
             e_ms = [a + b for a, b in zip(e_ms, ei["stage_ms"])]
@@ -372,6 +385,7 @@ def main():
         # every decode the same way
         encs = [enc] + [kvc.Encoder(p, dev) for _ in parts[1:]]
         dwss = [dws] + [torch.empty(kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev) for _ in parts[1:]]
+        side_buf = side
         side = [torch.cuda.Stream(device=dev) for _ in range(max(args.streams, args.decode_streams))]
         es, ds = args.streams, args.decode_streams
         log(f"[bench] pipelined: {len(parts)} one-layer calls queued asynchronously, encode over {es} and decode "
@@ -384,7 +398,7 @@ def main():
             for q in side:
                 q.wait_stream(main)
             for l, sl in enumerate(parts):
-                encs[l].enqueue(kv[sl], mu[sl], sigma[sl], prefix, stream=side[l % es])
+                encs[l].enqueue(kv[sl], mu[sl], side_buf[l], prefix, stream=side[l % es])
             for q in side:
                 main.wait_stream(q)
             ev[1].record(main)
@@ -393,7 +407,7 @@ def main():
             for q in side:
                 q.wait_stream(main)
             for l, sl in enumerate(parts):
-                rc = kvc.kvc_decode_async(sts[l], mu[sl], sigma[sl], prefix, kv_out[sl], dwss[l], encs[l].header.copy(),
+                rc = kvc.kvc_decode_async(sts[l], mu[sl], side_buf[l], prefix, kv_out[sl], dwss[l], encs[l].header.copy(),
                                           stream=side[l % ds])
                 if rc != kvc.KVC_OK:
                     raise kvc.KvcError(rc, "kvc_decode_async")
@@ -459,7 +473,8 @@ def main():
     bits_int, bits_float = 0.0, 0.0
     for sl in parts:
         bi, bf = kvc.kvc_estimate_bits(kv[sl], mu[sl], sigma[sl], prefix, weights,
-                                       sigma_block_tokens=args.sigma_block, chunk_tokens=tc, narrow_dof=args.narrow_dof)
+                                       sigma_block_tokens=args.sigma_block, chunk_tokens=tc, narrow_dof=args.narrow_dof,
+                                       channel_split=None if split is None else split[sl])
         frac = (sl.stop - sl.start) / w.planes
         bits_int += bi * frac
         bits_float += bf * frac
@@ -479,7 +494,7 @@ def main():
     # out (encode); words and states and mu in, KV out (decode)
     alg = float(kv_size + mu_size) * n + stream_bytes
     traffic = measured_traffic() if args.workload == 2 and tc == w.chunk_tokens and not args.paged \
-        and not args.sigma_block and args.sigma_fit == "rms" and not args.narrow_dof else {}
+        and not args.sigma_block and args.sigma_fit == "rms" and not args.narrow_dof and not args.channel_split else {}
 
     def roofline(kernel, avg_ms):
         a = alg / (avg_ms * 1e-3) / 1e9
@@ -524,6 +539,8 @@ def main():
             "scalars": n, "mixture_bp": list(weights), "chunk_tokens": tc, "sigma_block_tokens": args.sigma_block,
             "sigma_calibration": f"{args.sigma_fit}, {reps}x{w.calib_tokens} tokens per layer",
             "narrow_part": "gaussian" if args.narrow_dof == 0 else f"student-t, {args.narrow_dof} dof",
+            "mixture_weights": "per (plane, channel), calibrated to the code length" if args.channel_split
+                               else "the call's, every channel",
             "mu_dtype": "bf16" if mu_size == 2 else "fp32", "calls_per_step": len(parts),
             "decode_output": f"paged, {args.paged}-token pages" if args.paged else "contiguous",
             "calls": (f"asynchronous, encode on {args.streams} and decode on {args.decode_streams} streams "
@@ -553,7 +570,7 @@ def main():
     if args.offload:
         if not per_layer:
             raise SystemExit("--offload is defined on the per-layer workload (4)")
-        print(json.dumps(offload_reload(w, kv, mu, sigma, prefix, kvc, enc, parts, dws, max(1, args.steps))))
+        print(json.dumps(offload_reload(w, kv, mu, side, prefix, kvc, enc, parts, dws, max(1, args.steps))))
 
 
 if __name__ == "__main__":

@@ -223,20 +223,34 @@ struct SplitModel : Model {
     }
 
     // The decoder's aim for target t from a z that inverts the call's own
-    // mixture table: one Newton step on this lane's table, whose slope over
-    // a grid step (1/256 in z) is the interpolation step.  Only the cost of
-    // the search depends on it.
+    // mixture table: two Newton steps on the logarithm of this lane's
+    // table, counted from the nearer end of the range (t, or T_n + T_w - t
+    // in the upper half), whose slope over a grid step (1/256 in z) is the
+    // interpolation step.  The tails, where the lane's wide weight decides
+    // and the call's aim is furthest off, are close to exponential in z,
+    // and the logarithm makes them close to linear.  Only the cost of the
+    // search depends on it.
     __device__ __forceinline__ float aim(float z, uint32_t t) const {
-        float zq = __fmul_rn(z, 16777216.0f);
-        zq = __builtin_amdgcn_fmed3f(zq, -kQMaxF, kQMaxF);
-        int32_t q;
-        __asm__("v_cvt_flr_i32_f32 %0, %1" : "=v"(q) : "v"(zq));
-        uint32_t step;
-        const uint32_t hq = h_fx_split(q, reinterpret_cast<const uint2*>(tab), tn, tw, step);
-        const float dz = static_cast<float>(static_cast<int32_t>(t - hq)) *
-                         __builtin_amdgcn_rcpf(static_cast<float>(step) * 256.0f);
-        const float zn = step ? z + dz : z;
-        return __builtin_amdgcn_fmed3f(zn, -static_cast<float>(kTableZMax), static_cast<float>(kTableZMax));
+        const uint32_t ht = tn + tw;
+        const bool upper = ht - t < t;
+        const float ldt = __builtin_amdgcn_logf(fmaxf(static_cast<float>(upper ? ht - t : t), 1.0f));
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            float zq = __fmul_rn(z, 16777216.0f);
+            zq = __builtin_amdgcn_fmed3f(zq, -kQMaxF, kQMaxF);
+            int32_t q;
+            __asm__("v_cvt_flr_i32_f32 %0, %1" : "=v"(q) : "v"(zq));
+            uint32_t step;
+            const uint32_t hq = h_fx_split(q, reinterpret_cast<const uint2*>(tab), tn, tw, step);
+            const float dh = fmaxf(static_cast<float>(upper ? ht - hq : hq), 1.0f);
+            // d ln D / dz = +-256 step / D (ln 2 turns log2 into ln)
+            float dz = (ldt - __builtin_amdgcn_logf(dh)) * 0.69314718f * dh *
+                       __builtin_amdgcn_rcpf(static_cast<float>(step) * 256.0f);
+            dz = upper ? -dz : dz;
+            z = step ? z + dz : z;
+            z = __builtin_amdgcn_fmed3f(z, -static_cast<float>(kTableZMax), static_cast<float>(kTableZMax));
+        }
+        return z;
     }
 };
 
