@@ -554,7 +554,13 @@ def main():
         "encode_stage_ms": {k: median([s[0][i] for s in stats]) for i, k in
                             enumerate(["prologue", "encode_kernel"])},
         "decode_stage_ms": {k: median([s[1][i] for s in stats]) for i, k in enumerate(["prologue", "decode_kernel"])},
-        "bits_per_scalar": {"coded": 8.0 * stream_bytes / n, "integer_model": bits_int, "float_model": bits_float},
+        "bits_per_scalar": {"coded": 8.0 * stream_bytes / n, "integer_model": bits_int, "float_model": bits_float,
+                            # what the stream spends beyond the model: the 64 final states of every chunk (the
+                            # price of the chunk length), the header and directory, renormalisation and padding
+                            "chunk_overhead": 8.0 * stream_bytes / n - bits_int,
+                            "header_and_directory": 8.0 * sum(
+                                128 + 8 * ((sl.stop - sl.start) * -(-w.tokens // tc) * (w.channels // 64) + 1)
+                                for sl in parts) / n},
         "stream_bytes": stream_bytes,
         "decode_fallback_share": fallback[0] / n,
         "roundtrip_exact": ok,

@@ -131,18 +131,20 @@ __device__ __forceinline__ int32_t z_fixed(float edge_pos, float mu, float inv24
     return q;
 }
 
+// floor(dlt r / 2^16) for the 16 low bits r of u: the high word of
+// dlt (r 2^16), and r 2^16 is u shifted left by 16 (one shift and one
+// multiply, exact for any dlt < 2^32).
+__device__ __forceinline__ uint32_t interp_step(uint32_t dlt, uint32_t u) {
+    return __umulhi(dlt, u << 16);
+}
+
 // Integer mixture CDF of z = q / 2^24: table step 1/256 with integer linear
-// interpolation over the 16 low bits of q.  Every step of the table is below
-// 2^22 (the largest step of round(2^31 Phi) on this grid is 3,346,562 and the
-// two weighted parts add to at most that), so the product fits the 24-bit
-// multiplier.
+// interpolation over the 16 low bits of q.
 __device__ __forceinline__ uint32_t h_fx(int32_t q, const uint32_t* __restrict__ tab) {
     const uint32_t u = static_cast<uint32_t>(q + kQMax);
-    const uint32_t i = u >> 16, r = u & 0xFFFFu;
+    const uint32_t i = u >> 16;
     const uint32_t a = tab[i], c = tab[i + 1];
-    const uint32_t dlt = c - a;
-    __builtin_assume(dlt < (1u << 22));
-    return a + static_cast<uint32_t>((static_cast<uint64_t>(dlt) * r) >> 16);
+    return a + interp_step(c - a, u);
 }
 
 // Raw buffer resource over `bytes` bytes at p (gfx9 layout: no stride,
@@ -186,20 +188,16 @@ __device__ __forceinline__ uint32_t split_narrow_budget(uint32_t w, uint32_t t_a
 // h_fx with the lane's own budgets: the pair table holds (A[k], B[k]), the
 // narrow and wide base tables (the last entry repeated), and the lane's
 // mixture table entry floor(tn A[k] / 2^31) + floor(tw B[k] / 2^31) is
-// formed at the two entries the interpolation reads.  tn + tw <= T, so a
-// step of the lane's table is at most a step of either base table scaled by
-// its budget share, plus 1 for the floors: below 2^22 as for h_fx.
+// formed at the two entries the interpolation reads.
 __device__ __forceinline__ uint32_t h_fx_split(int32_t q, const uint2* __restrict__ ab, uint32_t tn, uint32_t tw,
                                                uint32_t& step) {
     const uint32_t u = static_cast<uint32_t>(q + kQMax);
-    const uint32_t i = u >> 16, r = u & 0xFFFFu;
+    const uint32_t i = u >> 16;
     const uint2 p0 = ab[i], p1 = ab[i + 1];
     const uint32_t a = mul_shr31(tn, p0.x) + mul_shr31(tw, p0.y);
     const uint32_t c = mul_shr31(tn, p1.x) + mul_shr31(tw, p1.y);
-    const uint32_t dlt = c - a;
-    __builtin_assume(dlt < (1u << 22));
-    step = dlt;
-    return a + static_cast<uint32_t>((static_cast<uint64_t>(dlt) * r) >> 16);
+    step = c - a;
+    return a + interp_step(c - a, u);
 }
 
 // The model of a chunk whose lanes each split the Gaussian budget their own

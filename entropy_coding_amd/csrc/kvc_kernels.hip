@@ -1210,8 +1210,8 @@ __device__ __forceinline__ void store_row(uint64_t row, uint32_t lane_off, uint3
 }
 
 // SPLIT: every (plane, channel) has its own split of the Gaussian budget:
-// the pair table in LDS instead of the mixture table, and one Newton step on
-// the lane's own table after the aim.
+// the pair table in LDS instead of the mixture table, and the lane's own
+// Newton steps after the call's aim (SplitModel::aim).
 template <int KV, int MU, bool PAGED, bool SPLIT>
 __global__ void __launch_bounds__(kDecodeBlock) __attribute__((amdgpu_num_sgpr(80))) k_decode(DecodeArgs a) {
     __shared__ __align__(16) uint32_t s_tab[SPLIT ? 2 * kTableWordsPadded : kTableWordsPadded];
@@ -1824,13 +1824,12 @@ __device__ __forceinline__ uint32_t split_candidate(uint32_t j, uint32_t w_gauss
     return w_gauss > d ? w_gauss - d : 0u;
 }
 
-// The lane table's interpolated value from its two pair-table entries.
-__device__ __forceinline__ uint32_t interp_pairs(uint2 p0, uint2 p1, uint32_t r, uint32_t tn, uint32_t tw) {
+// The lane table's interpolated value from its two pair-table entries (u:
+// the table position, its 16 low bits the interpolation weight).
+__device__ __forceinline__ uint32_t interp_pairs(uint2 p0, uint2 p1, uint32_t u, uint32_t tn, uint32_t tw) {
     const uint32_t a = mul_shr31(tn, p0.x) + mul_shr31(tw, p0.y);
     const uint32_t c = mul_shr31(tn, p1.x) + mul_shr31(tw, p1.y);
-    const uint32_t dlt = c - a;
-    __builtin_assume(dlt < (1u << 22));
-    return a + static_cast<uint32_t>((static_cast<uint64_t>(dlt) * r) >> 16);
+    return a + interp_step(c - a, u);
 }
 
 template <int KV, int MU>
@@ -1878,8 +1877,8 @@ __global__ void __launch_bounds__(kCalibBlock) k_split_cost(const void* kv_, con
         const uint32_t qf = 1u + prefix[sym + 1u] - prefix[sym];
 #pragma unroll
         for (int j = 0; j < kSplitSteps; ++j) {
-            const uint32_t h0 = interp_pairs(a0, a1, u0 & 0xFFFFu, tn[j], htot - tn[j]);
-            const uint32_t h1 = interp_pairs(b0, b1, u1 & 0xFFFFu, tn[j], htot - tn[j]);
+            const uint32_t h0 = interp_pairs(a0, a1, u0, tn[j], htot - tn[j]);
+            const uint32_t h1 = interp_pairs(b0, b1, u1, tn[j], htot - tn[j]);
             acc[j] += code_len_q16(h1 - h0 + qf, s_log);
         }
     }
