@@ -880,6 +880,8 @@ int kvc_calibrate_split(const void* d_kv, const void* d_mu, int32_t kv_dtype, in
     if (planes > kMaxScalars / channels || reps > kMaxScalars / (planes * channels) ||
         tokens > kMaxScalars / (reps * planes * channels))
         return KVC_ERR_INVALID;
+    // one workgroup per (plane, 64-channel group); the workspace size formula in range
+    if (planes * (channels / 64) > 0x7FFFFFFF || planes * channels > kMaxScalars / 8192) return KVC_ERR_INVALID;
     if (workspace_bytes < KVC_CALIBRATE_SPLIT_WORKSPACE_BYTES(planes, channels)) return KVC_ERR_INVALID;
     static_assert(kvc::kSplitSteps * kvc::kCalibSplitsMax * 8 == 8192, "workspace formula");
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -201,7 +201,8 @@ def test_other_calls_refuse_bad_arguments(kvc):
                                         a["prefix"], a["out"], a["wsp"], a["ws_bytes"], None)
     for kw in (dict(channels=96), dict(reps=0), dict(tokens=0), dict(planes=0), dict(block=-1), dict(dof=17),
                dict(kvd=5), dict(mud=1), dict(wn=9800, ww=300), dict(prefix=None), dict(sigma=None),
-               dict(out=None), dict(out=FAKE + 2), dict(wsp=FAKE + 64), dict(ws_bytes=ws - 1)):
+               dict(out=None), dict(out=FAKE + 2), dict(wsp=FAKE + 64), dict(ws_bytes=ws - 1),
+               dict(planes=1 << 26, tokens=1, ws_bytes=1 << 62)):               # the workspace formula would overflow
         assert split(**kw) == kvc.KVC_ERR_INVALID, kw
     # marginal: a known dtype, weights within 10000 basis points
     assert kvc._lib_marginal(FAKE, 3, 10, 9500, 300, FAKE, None) == kvc.KVC_ERR_INVALID
