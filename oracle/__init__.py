@@ -45,6 +45,27 @@ Parity status of each function (what pins it other than itself):
                                   written out with Python ints; code lengths
                                   per channel
   calibrate_split              -- a float64 brute force over the candidates
+  sigma_blocks / calibrate_sigma with blocks (S-11)
+                               -- one block over every token and equal blocks
+                                  reproduce the per-plane payloads; per-block
+                                  closed form of the calibration
+  log2_table_q16 / code_len_q16 / calibrate_sigma_rate (S-12)
+                               -- log2 (exact at powers of two, high by less
+                                  than 0.0056 bits); a float64 brute force of
+                                  the exact code length over the candidates
+  student_t_cdf_mp / narrow_table (S-13)
+                               -- scipy's stdtr for nu = 1..16, the closed
+                                  forms for nu = 1, 2; the float model of data
+                                  drawn from the truncated t against its
+                                  closed-form entropy
+  crc32 / stream_header / parse_header
+                               -- zlib's crc32 and the standard check value;
+                                  every damaged field refused
+  model_bits_int               -- the coded size: payload minus the model's
+                                  bits within the coder's bounds per lane
+  scatter_to_pages             -- plain loops over every (plane, token)
+  published bits/scalar of the pages (6.74..5.92, 2.05-2.59)
+                               -- parity unpinned: needs Qwen3 weights and C4
 """
 
 from .kvc_oracle import *  # noqa: F401,F403
