@@ -385,8 +385,7 @@ def main():
         # every decode the same way
         encs = [enc] + [kvc.Encoder(p, dev) for _ in parts[1:]]
         dwss = [dws] + [torch.empty(kvc.DECODE_WORKSPACE_BYTES, dtype=torch.uint8, device=dev) for _ in parts[1:]]
-        side_buf = side
-        side = [torch.cuda.Stream(device=dev) for _ in range(max(args.streams, args.decode_streams))]
+        qs = [torch.cuda.Stream(device=dev) for _ in range(max(args.streams, args.decode_streams))]
         es, ds = args.streams, args.decode_streams
         log(f"[bench] pipelined: {len(parts)} one-layer calls queued asynchronously, encode over {es} and decode "
             f"over {ds} streams")
@@ -395,29 +394,29 @@ def main():
             main = torch.cuda.current_stream(dev)
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             ev[0].record(main)
-            for q in side:
+            for q in qs:
                 q.wait_stream(main)
             for l, sl in enumerate(parts):
-                encs[l].enqueue(kv[sl], mu[sl], side_buf[l], prefix, stream=side[l % es])
-            for q in side:
+                encs[l].enqueue(kv[sl], mu[sl], side[l], prefix, stream=qs[l % es])
+            for q in qs:
                 main.wait_stream(q)
             ev[1].record(main)
-            sts = [encs[l].result(stream=side[l % es]) for l in range(len(parts))]
+            sts = [encs[l].result(stream=qs[l % es]) for l in range(len(parts))]
             ev[2].record(main)
-            for q in side:
+            for q in qs:
                 q.wait_stream(main)
             for l, sl in enumerate(parts):
-                rc = kvc.kvc_decode_async(sts[l], mu[sl], side_buf[l], prefix, kv_out[sl], dwss[l], encs[l].header.copy(),
-                                          stream=side[l % ds])
+                rc = kvc.kvc_decode_async(sts[l], mu[sl], side[l], prefix, kv_out[sl], dwss[l], encs[l].header.copy(),
+                                          stream=qs[l % ds])
                 if rc != kvc.KVC_OK:
                     raise kvc.KvcError(rc, "kvc_decode_async")
-            for q in side:
+            for q in qs:
                 main.wait_stream(q)
             ev[3].record(main)
             fb = 0
             for l in range(len(parts)):
                 di = {}
-                rc = kvc.kvc_decode_result(dwss[l], stream=side[l % ds], info=di)
+                rc = kvc.kvc_decode_result(dwss[l], stream=qs[l % ds], info=di)
                 if rc != kvc.KVC_OK:
                     raise kvc.KvcError(rc, "kvc_decode_result")
                 fb += di["fallback_symbols"]
