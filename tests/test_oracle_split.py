@@ -73,26 +73,27 @@ def test_chunks_with_one_weight_equal_the_global_weight_chunks(kv_dtype, sigma_b
     assert np.array_equal(O.decode(st, mu, sig, pref, channel_split=split), kv)
 
 
-def test_each_lane_codes_under_its_own_weight():
+@pytest.mark.parametrize("kv_dtype", [O.BF16, O.E4M3])
+def test_each_lane_codes_under_its_own_weight(kv_dtype):
     """Each lane's final state and word count, from a one-lane rANS written
     out here with Python ints (S-8: emit while x >> 32 >= f, then
     x = (x // f) M + slot, slot = G(s) + r in the Gaussian range or T_n + T_w
     + Q(s) + r - f_G in the escape range) over that lane's own global-weight
     model."""
-    kv, mu, sig, samples, mu_dtype = case(planes=1, tokens=30, channels=64)
-    pref = O.build_marginal(samples, O.BF16, W_N, W_W)
+    kv, mu, sig, samples, mu_dtype = case(kv_dtype, planes=1, tokens=30, channels=64)
+    pref = O.build_marginal(samples, kv_dtype, W_N, W_W)
     split = (625 * ((np.arange(64) * 5) % 16)).astype(np.int64)[None, :]     # 0 .. 9375 across lanes
-    st = O.encode(kv, mu, sig, pref, O.BF16, mu_dtype, W_N, W_W, 30, channel_split=split)
-    s = O.order_index(kv, O.BF16)
-    m = O.mu_to_f32(mu, O.BF16)
+    st = O.encode(kv, mu, sig, pref, kv_dtype, mu_dtype, W_N, W_W, 30, channel_split=split)
+    s = O.order_index(kv, kv_dtype)
+    m = O.mu_to_f32(mu, mu_dtype)
     inv = (np.float32(1) / sig).astype(np.float32)
     states, n_words = [], 0
     for lane in range(64):
         v = int(split[0, lane])
-        t_n, t_w, _ = O.budgets(O.BF16, v, W_ALL - v)
+        t_n, t_w, _ = O.budgets(kv_dtype, v, W_ALL - v)
         sl = s[0, :, lane]
-        g0 = O.gauss_cum(sl, m[0, :, lane], inv[0, lane], O.BF16, t_n, t_w)
-        g1 = O.gauss_cum(sl + 1, m[0, :, lane], inv[0, lane], O.BF16, t_n, t_w)
+        g0 = O.gauss_cum(sl, m[0, :, lane], inv[0, lane], kv_dtype, t_n, t_w)
+        g1 = O.gauss_cum(sl + 1, m[0, :, lane], inv[0, lane], kv_dtype, t_n, t_w)
         x = O.L
         for t in range(29, -1, -1):
             fg = int(g1[t] - g0[t])
@@ -109,6 +110,7 @@ def test_each_lane_codes_under_its_own_weight():
     assert list(np.frombuffer(body[:O.STATE_BYTES], dtype="<u8")) == states
     assert len(body) == O.STATE_BYTES + -(-2 * n_words // 8) * 8
     assert np.array_equal(O.decode(st, mu, sig, pref, channel_split=split), kv)
+    assert all(_exact(kv_dtype, v) for v in range(0, W_ALL + 1, 625))      # the global models are exact
 
 
 def test_code_length_is_the_sum_over_channels():
