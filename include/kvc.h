@@ -226,7 +226,9 @@ int kvc_stream_info(const void* h_header, uint64_t header_bytes, kvc_params* h_p
  * runs, that the header is a valid KVC-1 header (CRC included:
  * KVC_ERR_CORRUPT), that in_bytes is the length it gives (KVC_ERR_CORRUPT),
  * and that the caller's buffers hold what it describes (KVC_ERR_INVALID):
- * mu_bytes >= scalars x mu element size, sigma_bytes >= 4 x sigma words,
+ * mu_bytes >= scalars x mu element size, sigma_bytes >= 4 x sigma words
+ * (with per-channel weights, channel_split in the header: 4 x (sigma words
+ * + planes x channels), the weights following sigma in d_sigma),
  * prefix_bytes >= 4 x (N + 1) when the mixture has an escape part,
  * kv_out_bytes >= scalars x KV element size.  On the device the stream's
  * own header must equal h_header (KVC_ERR_CORRUPT, nothing decoded).
@@ -462,7 +464,9 @@ int kvc_build_marginal(const void* d_samples, int32_t dtype, uint64_t n,
  * Bits per scalar ([wiki] "core idea": the rate is the cross-entropy of the
  * model).  h_bits_out[0] = mean of -log2(f/2^31) under the integer model the
  * coder uses; h_bits_out[1] = mean -log2 q under the continuous mixture over
- * the same cells (float64, per-scalar cost capped at 64 bits).  Workspace:
+ * the same cells (float64, per-scalar cost capped at 64 bits).  With
+ * p->channel_split = 1, d_sigma carries the per-channel weights after sigma
+ * (as for kvc_encode) and each channel's weights are used.  Workspace:
  * KVC_ESTIMATE_WORKSPACE_BYTES.  Synchronises `stream` once.
  */
 int kvc_estimate_bits(const kvc_params* p, const void* d_kv, const void* d_mu,
