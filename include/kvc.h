@@ -41,6 +41,11 @@
  *     calling stream, which that first call synchronises; all of them are
  *     only read afterwards.  kvc_decode_noalloc's scratch is the one
  *     exception, see there.
+ *   - Graph capture: once a call with the same weights and narrow part has
+ *     run on the device (so its tables exist), kvc_encode without a size
+ *     pointer and kvc_decode_async only launch kernels (the control block is
+ *     cleared by a kernel, not a memset) and may be captured in a HIP graph
+ *     and replayed; their *_result calls synchronise and stay outside it.
  */
 #ifndef KVC_H
 #define KVC_H
