@@ -94,6 +94,16 @@ def test_changed_or_missing_weights_are_refused(kvc, cuda):
     assert kvc.kvc_decode_into(st, mu_d, sig_d, pref_d, out, ws) == kvc.KVC_ERR_INVALID
     assert kvc.kvc_decode_into(st, mu_d, kvc.side_info(sig_d, split), pref_d, out, ws) == kvc.KVC_OK
     assert torch.equal(out, kv_d.view(torch.int16))
+    # damaged payloads are reported, as without the weights
+    h = O.parse_header(st.cpu().numpy().tobytes())
+    pay = 128 + 8 * (h["n_chunks"] + 1)
+    rng = np.random.default_rng(4)
+    side = kvc.side_info(sig_d, split)
+    for _ in range(8):
+        bad = st.clone()
+        i = int(rng.integers(pay, st.numel()))
+        bad[i] ^= 1 << int(rng.integers(0, 8))
+        assert kvc.kvc_decode_into(bad, mu_d, side, pref_d, out, ws) == kvc.KVC_ERR_CORRUPT
     # a stream without the split decoded with a side buffer that has it: the
     # extra words are outside the checksum's range, sigma decides
     plain = kvc.kvc_encode(kv_d, mu_d, sig_d, pref_d, (9500, 300), 16)
