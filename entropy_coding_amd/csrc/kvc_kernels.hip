@@ -870,12 +870,13 @@ __device__ __forceinline__ float aim_z(uint32_t t, uint32_t htot, const float2* 
 
 // A decoder candidate is held as a word whose upper half is the bf16
 // pattern (the lower half is ignored) and, for e4m3, as the pattern itself.
-// Nearest bf16 value to x (round to nearest even), x clamped to
-// [-max, max]: the rounded float32 bits, whose upper half is the pattern.
+// Nearest bf16 value to x, x clamped to [-max, max]: half a bf16 step added
+// to the float32 bits (ties away from zero; the candidate only starts the
+// search, so the tie rule does not matter), whose upper half is the pattern.
 __device__ __forceinline__ uint32_t nearest_bf16(float x) {
     const float lim = __uint_as_float(0x7F7F0000u);
     const uint32_t u = __float_as_uint(__builtin_amdgcn_fmed3f(x, -lim, lim));
-    return u + 0x7FFFu + ((u >> 16) & 1u);
+    return u + 0x8000u;
 }
 
 // e4m3fn pattern of the value nearest x, x clamped to [-448, 448]:
